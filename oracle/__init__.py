@@ -1,0 +1,29 @@
+"""CPU fp64 oracle for structured-rotation + group quantization.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library package imports, links or
+calls this package; only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path: it is plain numpy/scipy in float64, written from the pages below.
+
+Sources (cited in every function by short key and section):
+
+* [HARP] "HARP: Hadamard-Preconditioned Adaptive Rotation Processor for
+  Extreme LLM Quantization", gist.science explainer, technical summary
+  (sections 1, 2.1, 2.2, 2.4).
+* [PolarQuant] "PolarQuant: Optimal Gaussian Weight Quantization via Hadamard
+  Rotation for LLM Compression", gist.science explainer, technical overview
+  (section 1 "background", section 2 "method").
+
+Modules:
+
+* ``transform`` -- mixed-radix stage product, dense orthogonal matrix, RHT,
+  one- and two-sided application and inverses.
+* ``quant`` -- group absmax quantizer, norm-scaled codebook quantizer,
+  decision-band accounting, LSB-first bit packing.
+* ``lloydmax`` -- Lloyd-Max centroids/thresholds for N(0, 1).
+
+Readings of points the pages leave open are stated where they are used and
+listed together in the design notes of the repository.
+"""
+
+from . import transform, quant, lloydmax  # noqa: F401
