@@ -1,0 +1,310 @@
+"""Python binding of libbrq (structured rotation + group quantization, gfx950).
+
+Argument marshalling only: every step of the rotation and quantization runs
+in the HIP kernels of ``lib/libbrq.so``; PyTorch supplies device memory and
+the current stream.  There is no CPU fallback: a missing library raises.
+
+Names follow the C ABI in ``include/brq.h`` without the ``brq_`` prefix.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libbrq.so")
+DRYRUN_LIB_PATH = os.path.join(_PKG, "lib", "libbrq_dryrun.so")
+
+F32, BF16, F16 = 0, 1, 2
+HADAMARD, SHARED, PER_GROUP = 0, 1, 2
+RIGHT, LEFT = 0, 1
+ABSMAX, CODEBOOK_NORM = 0, 1
+_MODES = {"hadamard": HADAMARD, "shared": SHARED, "per_group": PER_GROUP}
+_KINDS = {"absmax": ABSMAX, "codebook_norm": CODEBOOK_NORM}
+_SIDES = {"right": RIGHT, "left": LEFT}
+
+STATUS = {0: "BRQ_OK", 1: "BRQ_ERR_INVALID_ARGUMENT", 2: "BRQ_ERR_UNSUPPORTED",
+          3: "BRQ_ERR_ALIGNMENT", 4: "BRQ_ERR_WORKSPACE", 5: "BRQ_ERR_HIP"}
+
+EXPORTED = (
+    "brq_status_string", "brq_last_error", "brq_version", "brq_plan_create",
+    "brq_plan_destroy", "brq_plan_dim", "brq_workspace_bytes", "brq_rotate",
+    "brq_rotate_inverse", "brq_rotate_quantize_pack", "brq_dequant_unrotate",
+    "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
+    "brq_profile_read",
+)
+
+
+class BrqError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Quant(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("codebook", ctypes.c_float * 32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libbrq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m butterfly_rotation_quantization_amd.build` (no CPU fallback exists)")
+    lib = bind(ctypes.CDLL(path))
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def bind(lib):
+    """Declare the argument and result types of the C ABI on a loaded library."""
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.brq_status_string.argtypes = [i32]
+    lib.brq_status_string.restype = ctypes.c_char_p
+    lib.brq_last_error.argtypes = []
+    lib.brq_last_error.restype = ctypes.c_char_p
+    lib.brq_version.restype = i32
+    lib.brq_plan_create.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, i32, vp]
+    lib.brq_plan_create.restype = i32
+    lib.brq_plan_destroy.argtypes = [vp]
+    lib.brq_plan_destroy.restype = i32
+    lib.brq_plan_dim.argtypes = [vp]
+    lib.brq_plan_dim.restype = i32
+    lib.brq_workspace_bytes.argtypes = [vp, vp, i64, i64]
+    lib.brq_workspace_bytes.restype = sz
+    rot = [vp, i32, vp, i32, i64, vp, i32, i64, i64, i64, vp, sz, vp]
+    lib.brq_rotate.argtypes = rot
+    lib.brq_rotate.restype = i32
+    lib.brq_rotate_inverse.argtypes = rot
+    lib.brq_rotate_inverse.restype = i32
+    lib.brq_rotate_quantize_pack.argtypes = [vp, vp, vp, i32, i64, i64, i64,
+                                             ctypes.POINTER(Quant), vp, vp, vp, sz, vp]
+    lib.brq_rotate_quantize_pack.restype = i32
+    lib.brq_dequant_unrotate.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Quant), i64, i64,
+                                         vp, i32, i64, vp, sz, vp]
+    lib.brq_dequant_unrotate.restype = i32
+    lib.brq_lloyd_max_gaussian.argtypes = [i32, vp]
+    lib.brq_lloyd_max_gaussian.restype = i32
+    lib.brq_profile_enable.argtypes = [i32]
+    lib.brq_profile_enable.restype = i32
+    lib.brq_profile_reset.argtypes = []
+    lib.brq_profile_reset.restype = i32
+    lib.brq_profile_count.argtypes = []
+    lib.brq_profile_count.restype = i32
+    lib.brq_profile_read.argtypes = [i32, ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(i64)]
+    lib.brq_profile_read.restype = i32
+    return lib
+
+
+def lib():
+    return load_library()
+
+
+def check(status: int):
+    if status != 0:
+        raise BrqError(status, lib().brq_last_error().decode())
+
+
+# ---------------------------------------------------------------- plans
+
+class Plan:
+    """A device transform plan (owns the brq_plan*)."""
+
+    def __init__(self, d: int, radix: Sequence[int], mode="hadamard",
+                 blocks: Optional[Sequence[np.ndarray]] = None,
+                 signs: Optional[np.ndarray] = None):
+        L = lib()
+        mode_i = _MODES[mode] if isinstance(mode, str) else int(mode)
+        r = np.ascontiguousarray(np.asarray(radix, dtype=np.int32))
+        blk = None
+        if blocks is not None:
+            blk = np.ascontiguousarray(
+                np.concatenate([np.asarray(b, dtype=np.float32).reshape(-1) for b in blocks]))
+        sg = None if signs is None else np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+        h = ctypes.c_void_p()
+        check(L.brq_plan_create(ctypes.byref(h), int(d), len(r), r.ctypes.data,
+                                None if blk is None else blk.ctypes.data, mode_i,
+                                None if sg is None else sg.ctypes.data))
+        self._h = h
+        self.d = int(d)
+        self.radix = tuple(int(x) for x in r)
+        self.mode = mode_i
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().brq_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _h(plan: Optional[Plan]):
+    return None if plan is None else plan.handle
+
+
+# ---------------------------------------------------------------- torch marshalling
+
+def dtype_code(t) -> int:
+    import torch
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}[t.dtype]
+
+
+def _torch_dtype(code: int):
+    import torch
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[code]
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return int(t.stride(0))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def workspace_bytes(left: Optional[Plan], right: Optional[Plan], m: int, n: int) -> int:
+    return int(lib().brq_workspace_bytes(_h(left), _h(right), int(m), int(n)))
+
+
+def workspace(left, right, m, n, device="cuda"):
+    import torch
+    nb = workspace_bytes(left, right, m, n)
+    return torch.empty(max(nb, 4) // 4 + 1, dtype=torch.float32, device=device)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    return int(ws.data_ptr()), int(ws.numel() * ws.element_size())
+
+
+def rotate(plan: Plan, x, y=None, side="right", ws=None, stream=None, inverse=False):
+    """Y = X M^T (side "right", rows or d-chunks of rows) or Y = M X (side
+    "left"); inverse=True applies M^T.  Returns y."""
+    import torch
+    side_i = _SIDES[side] if isinstance(side, str) else int(side)
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(plan if side_i == LEFT else None, plan if side_i == RIGHT else None,
+                       x.shape[0], x.shape[1], x.device)
+    wp, wb = _ws_args(ws)
+    fn = lib().brq_rotate_inverse if inverse else lib().brq_rotate
+    check(fn(plan.handle, side_i, _ptr(x), dtype_code(x), _ld(x), _ptr(y), dtype_code(y), _ld(y),
+             int(x.shape[0]), int(x.shape[1]), wp, wb, _stream(stream)))
+    return y
+
+
+def rotate_inverse(plan: Plan, x, y=None, side="right", ws=None, stream=None):
+    return rotate(plan, x, y, side, ws, stream, inverse=True)
+
+
+def make_quant(bits: int, group: int, kind="absmax", codebook=None) -> Quant:
+    q = Quant()
+    q.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
+    q.bits = int(bits)
+    q.group = int(group)
+    if codebook is not None:
+        cb = np.asarray(codebook, dtype=np.float32).reshape(-1)
+        for i, v in enumerate(cb):
+            q.codebook[i] = float(v)
+    return q
+
+
+def rotate_quantize_pack(left: Optional[Plan], right: Optional[Plan], w, bits: int, group: int,
+                         kind="absmax", codebook=None, codes=None, scales=None, ws=None,
+                         stream=None):
+    """W' = M_U W M_V^T, then group quantization along rows and LSB-first
+    packing.  Returns (codes uint8 [m, n*bits/8], scales [m, n/group])."""
+    import torch
+    m, n = int(w.shape[0]), int(w.shape[1])
+    q = make_quant(bits, group, kind, codebook)
+    if codes is None:
+        codes = torch.empty((m, n * bits // 8), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        sd = torch.float32 if q.kind == ABSMAX else torch.float16
+        scales = torch.empty((m, n // group), dtype=sd, device=w.device)
+    if ws is None:
+        ws = workspace(left, right, m, n, w.device)
+    wp, wb = _ws_args(ws)
+    check(lib().brq_rotate_quantize_pack(_h(left), _h(right), _ptr(w), dtype_code(w), m, n,
+                                         _ld(w), ctypes.byref(q), _ptr(codes), _ptr(scales),
+                                         wp, wb, _stream(stream)))
+    return codes, scales
+
+
+def dequant_unrotate(left: Optional[Plan], right: Optional[Plan], codes, scales, m: int, n: int,
+                     bits: int, group: int, kind="absmax", codebook=None, out=None,
+                     out_dtype=None, ws=None, stream=None):
+    """W = M_U^T deq(codes) M_V.  Returns out [m, n]."""
+    import torch
+    q = make_quant(bits, group, kind, codebook)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=codes.device)
+    if ws is None:
+        ws = workspace(left, right, m, n, codes.device)
+    wp, wb = _ws_args(ws)
+    check(lib().brq_dequant_unrotate(_h(left), _h(right), _ptr(codes), _ptr(scales),
+                                     ctypes.byref(q), int(m), int(n), _ptr(out), dtype_code(out),
+                                     _ld(out), wp, wb, _stream(stream)))
+    return out
+
+
+def profile_enable(on: bool = True):
+    """Bracket every kernel launch of the hot calls with HIP events on its stream."""
+    check(lib().brq_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    check(lib().brq_profile_reset())
+
+
+def profile_read() -> dict:
+    """{kernel name: (total ms, launches)} since the last reset (waits for the events)."""
+    L = lib()
+    out = {}
+    for i in range(L.brq_profile_count()):
+        buf = ctypes.create_string_buffer(256)
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        check(L.brq_profile_read(i, buf, 256, ctypes.byref(ms), ctypes.byref(n)))
+        out[buf.value.decode()] = (ms.value, n.value)
+    return out
+
+
+def lloyd_max_gaussian(bits: int) -> np.ndarray:
+    """2^bits float32 Lloyd-Max centroids for N(0,1), computed by the library."""
+    out = np.zeros(1 << bits, dtype=np.float32)
+    check(lib().brq_lloyd_max_gaussian(int(bits), out.ctypes.data))
+    return out

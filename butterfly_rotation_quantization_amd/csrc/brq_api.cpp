@@ -1,0 +1,762 @@
+// C ABI of libbrq: argument validation, plans, pass planning and dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "brq_internal.h"
+#include "fused.h"
+
+struct brq_plan {
+  brq::Plan p;
+};
+
+namespace brq {
+namespace {
+
+thread_local std::string g_last_error;
+
+brq_status fail(brq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+brq_status hip_fail(hipError_t e, const char* what) {
+  return fail(BRQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool valid_dtype(int32_t t) { return t == BRQ_F32 || t == BRQ_BF16 || t == BRQ_F16; }
+
+// Tile budget of the generic pass (float32 elements held in LDS).
+constexpr int kTileFloats = 16384;
+constexpr int kMaxGroupP = 4096;
+
+// A run of consecutive stages [a, e] of one side, executed in one pass.
+struct Group {
+  int a, e;
+  int P, S;
+};
+
+std::vector<Group> side_groups(const Plan& p) {
+  std::vector<Group> out;
+  int e = p.nst - 1;
+  while (e >= 0) {
+    int a = e;
+    int P = p.radix[e];
+    while (a > 0 && (int64_t)P * p.radix[a - 1] <= kMaxGroupP &&
+           e - (a - 1) + 1 <= kMaxPassStages) {
+      --a;
+      P *= p.radix[a];
+    }
+    out.push_back(Group{a, e, P, p.stride[e]});
+    e = a - 1;
+  }
+  std::reverse(out.begin(), out.end());  // forward order: the group holding stage 0 first
+  return out;
+}
+
+int largest_divisor_at_most(int s, int cap) {
+  for (int w = std::min(s, cap); w >= 1; --w)
+    if (s % w == 0) return w;
+  return 1;
+}
+
+// Axis that carries the stages of `g` of plan `p`.
+void stage_axis(AxisDesc& x, const Plan& p, const Group& g, int64_t D, bool inverse,
+                int line_budget_floats) {
+  std::memset(&x, 0, sizeof x);
+  x.P = g.P;
+  x.S = g.S;
+  int W = largest_divisor_at_most(g.S, 16);
+  while (W > 1 && (int64_t)g.P * W > line_budget_floats) {
+    W = largest_divisor_at_most(g.S, W - 1);
+  }
+  x.W = W;
+  x.d = p.d;
+  x.nhi = p.d / (g.P * g.S);
+  x.nlo = g.S / W;
+  x.nchunk = (int)(D / p.d);
+  x.D = D;
+  x.ragged = 0;
+  x.nst = g.e - g.a + 1;
+  for (int i = 0; i < x.nst; ++i) {
+    const int t = inverse ? (g.e - i) : (g.a + i);
+    StageDesc& s = x.st[i];
+    s.b = p.radix[t];
+    s.St = p.stride[t];
+    s.ls = p.stride[t] / g.S;
+    s.mode = p.mode;
+    s.blk = p.mode == BRQ_HADAMARD ? nullptr : ((inverse ? p.blkT : p.blk) + p.blk_off[t]);
+  }
+}
+
+void free_axis(AxisDesc& x, int64_t D, int extent) {
+  std::memset(&x, 0, sizeof x);
+  x.P = extent;
+  x.S = 1;
+  x.W = 1;
+  x.d = (int)std::min<int64_t>(D, 1 << 30);
+  x.nhi = 1;
+  x.nlo = 1;
+  x.nchunk = 1;
+  x.D = D;
+  x.ragged = 1;
+}
+
+int lines_for(int64_t tile_line_floats) {
+  int64_t L = kTileFloats / std::max<int64_t>(tile_line_floats, 1);
+  if (L > 16) L = 16;
+  if (L < 1) L = 1;
+  return (int)L;
+}
+
+// Host check of everything the kernel's index arithmetic relies on; a pass
+// that fails it is never launched.
+const char* check_axis(const AxisDesc& x) {
+  if (x.P < 1 || x.W < 1 || x.S < 1) return "axis extent";
+  if (x.nst < 0 || x.nst > kMaxPassStages) return "stage count";
+  if (x.ragged) {
+    if (x.nst) return "stages on a ragged axis";
+    if (x.W != 1 || x.S != 1) return "ragged axis layout";
+    return nullptr;
+  }
+  if (x.S % x.W || x.nlo * x.W != x.S) return "lo tiling";
+  if ((int64_t)x.P * x.S * x.nhi != x.d) return "hi tiling";
+  if ((int64_t)x.nchunk * x.d != x.D) return "chunk tiling";
+  int64_t span = 1;
+  for (int i = 0; i < x.nst; ++i) {
+    const StageDesc& s = x.st[i];
+    if (s.b < 2 || s.b > 64) return "radix";
+    if (s.ls < 1 || (int64_t)s.ls * x.S != s.St) return "local stride";
+    if (x.P % ((int64_t)s.ls * s.b)) return "stage digit outside the pass";
+    if (x.d % ((int64_t)s.b * s.St)) return "stage stride";
+    if (s.mode != BRQ_HADAMARD && !s.blk) return "missing blocks";
+    span *= s.b;
+  }
+  if (x.nst && span != x.P) return "pass extent != product of its radices";
+  if (x.sign && x.sign_mod < 1) return "sign length";
+  return nullptr;
+}
+
+const char* check_pass(const PassArgs& a) {
+  for (int i = 0; i < 2; ++i)
+    if (const char* why = check_axis(a.ax[i])) return why;
+  if (!a.ax[0].ragged && a.ax[0].D != a.m) return "row axis extent";
+  if (!a.ax[1].ragged && a.ax[1].D != a.n) return "column axis extent";
+  if (a.ax[0].ragged && a.ax[0].D != a.m) return "row axis extent";
+  if (a.ax[1].ragged && a.ax[1].D != a.n) return "column axis extent";
+  const int64_t RT = (int64_t)a.ax[0].P * a.ax[0].W;
+  const int64_t CT = (int64_t)a.ax[1].P * a.ax[1].W;
+  if (RT * (CT + 1) * 4 > 96 * 1024) return "tile exceeds LDS";
+  if (a.pro == PRO_LOAD && !a.src) return "source";
+  if (a.pro == PRO_DEQUANT && (!a.in_codes || !a.in_scales)) return "dequant inputs";
+  if (a.epi == EPI_STORE && !a.dst) return "destination";
+  if (a.epi == EPI_QUANT) {
+    if (!a.codes || !a.scales) return "quant outputs";
+    if (a.group < 64 || a.group > 1024 || CT % a.group) return "quant group vs tile";
+    const AxisDesc& c = a.ax[1];
+    if (!c.ragged && !(c.S == 1 && c.W == 1)) return "quant tile columns not contiguous";
+    if (c.ragged && c.P % a.group) return "quant tile columns";
+  }
+  if (a.pro == PRO_DEQUANT || a.epi == EPI_QUANT) {
+    if (a.nlev != (1 << a.bits) || a.nlev > kMaxLevels) return "levels";
+    if (a.codes_ld * 8 != a.n * a.bits || a.scales_ld * a.group != a.n) return "code layout";
+  }
+  return nullptr;
+}
+
+// Kernel name for timing: the stages the pass applies and its prologue/epilogue.
+std::string pass_name(const PassArgs& a) {
+  std::string n = "pass";
+  if (a.pro == PRO_DEQUANT) n += " dequant";
+  const char* side[2] = {" L", " R"};
+  for (int i = 0; i < 2; ++i) {
+    const AxisDesc& x = a.ax[i];
+    if (!x.nst) continue;
+    n += side[i];
+    n += a.inverse ? "^T(" : "(";
+    for (int t = 0; t < x.nst; ++t) {
+      if (t) n += ",";
+      n += std::to_string(x.st[t].b);
+    }
+    n += ")";
+  }
+  if (a.epi == EPI_QUANT) n += " quant";
+  return n;
+}
+
+hipError_t checked_launch(const PassArgs& a, hipStream_t s, brq_status* st) {
+  if (const char* why = check_pass(a)) {
+    *st = fail(BRQ_ERR_UNSUPPORTED, "internal pass check failed: %s", why);
+    return hipErrorInvalidValue;
+  }
+  const int tok = prof_begin(pass_name(a).c_str(), s);
+  hipError_t e = launch_pass(a, s);
+  prof_end(tok, s);
+  *st = e == hipSuccess ? BRQ_OK : hip_fail(e, "pass launch");
+  return e;
+}
+
+// The pass list of a transform.  Forward: the left side's groups, then the
+// right side's (the sides commute).  Inverse: the reverse, each group's
+// stages reversed with transposed blocks.
+struct PassSpec {
+  bool has_u, has_v;
+  Group gu, gv;
+};
+
+std::vector<PassSpec> plan_passes(const Plan* U, const Plan* V) {
+  std::vector<PassSpec> out;
+  if (U)
+    for (const Group& g : side_groups(*U)) out.push_back(PassSpec{true, false, g, Group{}});
+  if (V)
+    for (const Group& g : side_groups(*V)) out.push_back(PassSpec{false, true, Group{}, g});
+  return out;
+}
+
+void build_axes(PassArgs& a, const PassSpec& ps, const Plan* U, const Plan* V, int64_t m,
+                int64_t n, bool inverse) {
+  if (ps.has_u) {
+    stage_axis(a.ax[0], *U, ps.gu, m, inverse, kTileFloats / 16);
+    const int line = a.ax[0].P * a.ax[0].W;
+    free_axis(a.ax[1], n, lines_for(line));
+  } else {
+    stage_axis(a.ax[1], *V, ps.gv, n, inverse, kTileFloats / 16);
+    const int line = a.ax[1].P * a.ax[1].W;
+    free_axis(a.ax[0], m, lines_for(line));
+  }
+}
+
+void set_signs(PassArgs& a, const Plan* U, const Plan* V) {
+  if (U && U->signs) {
+    a.ax[0].sign = U->signs;
+    a.ax[0].sign_mod = U->d;
+  }
+  if (V && V->signs) {
+    a.ax[1].sign = V->signs;
+    a.ax[1].sign_mod = V->d;
+  }
+}
+
+brq_status check_plan_device(const Plan* p) {
+  if (!p) return BRQ_OK;
+  int dev = -1;
+  hipError_t e = rt_get_device(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "plan was created on device %d, current is %d",
+                p->device, dev);
+  return BRQ_OK;
+}
+
+brq_status check_quant(const brq_quant* q, int64_t n) {
+  if (!q) return fail(BRQ_ERR_INVALID_ARGUMENT, "quantizer is NULL");
+  if (q->kind != BRQ_ABSMAX && q->kind != BRQ_CODEBOOK_NORM)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "unknown quantizer kind %d", q->kind);
+  if (q->bits < 2 || q->bits > 5) return fail(BRQ_ERR_INVALID_ARGUMENT, "bits must be 2..5");
+  if (q->group <= 0 || n % q->group)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "group %d must divide n = %lld", q->group, (long long)n);
+  if (((int64_t)q->group * q->bits) % 8)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "group*bits must be a multiple of 8");
+  if (!is_pow2(q->group) || q->group < 64 || q->group > 1024)
+    return fail(BRQ_ERR_UNSUPPORTED, "group must be a power of two in 64..1024");
+  if (q->kind == BRQ_CODEBOOK_NORM) {
+    const int L = 1 << q->bits;
+    for (int i = 0; i < L; ++i)
+      if (!std::isfinite(q->codebook[i]))
+        return fail(BRQ_ERR_INVALID_ARGUMENT, "codebook entry %d is not finite", i);
+    for (int i = 1; i < L; ++i)
+      if (!(q->codebook[i] > q->codebook[i - 1]))
+        return fail(BRQ_ERR_INVALID_ARGUMENT, "codebook must be strictly ascending");
+  }
+  return BRQ_OK;
+}
+
+void fill_quant(PassArgs& a, const brq_quant* q, int64_t n) {
+  a.qkind = q->kind;
+  a.bits = q->bits;
+  a.group = q->group;
+  a.nlev = 1 << q->bits;
+  a.h = (float)((a.nlev - 1) * 0.5);
+  a.sqrt_g = std::sqrt((float)q->group);
+  for (int i = 0; i < kMaxLevels; ++i) {
+    a.cent[i] = i < a.nlev && q->kind == BRQ_CODEBOOK_NORM ? q->codebook[i] : 0.f;
+    a.tau[i] = 0.f;
+  }
+  if (q->kind == BRQ_CODEBOOK_NORM)
+    for (int i = 0; i + 1 < a.nlev; ++i) a.tau[i] = (q->codebook[i] + q->codebook[i + 1]) * 0.5f;
+  a.codes_ld = n * q->bits / 8;
+  a.scales_ld = n / q->group;
+}
+
+// Run a forward transform (possibly none) from src into either dst or the
+// quantizer.  ws holds the float32 intermediate when there is more than one pass.
+brq_status run_forward(const Plan* U, const Plan* V, const void* src, int src_t, int64_t ld_src,
+                       int64_t m, int64_t n, void* dst, int dst_t, int64_t ld_dst,
+                       const brq_quant* q, uint8_t* codes, void* scales, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  std::vector<PassSpec> passes = plan_passes(U, V);
+  // Can the quantizer ride on the last pass?  It needs contiguous whole groups
+  // along the tile's columns: a right-side group ending at stride 1.
+  bool fuse_q = false;
+  if (q && !passes.empty()) {
+    const PassSpec& last = passes.back();
+    fuse_q = last.has_v && last.gv.S == 1 && (last.gv.P % q->group) == 0;
+  }
+  const size_t npass = passes.size() + ((q && !fuse_q) ? 1 : 0);
+  const size_t need = npass > 1 ? (size_t)m * n * sizeof(float) : 0;
+  if (need && (!ws || ws_bytes < need))
+    return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+
+  for (size_t i = 0; i < npass; ++i) {
+    PassArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.m = m;
+    a.n = n;
+    a.inverse = 0;
+    if (i < passes.size()) {
+      build_axes(a, passes[i], U, V, m, n, false);
+    } else {  // stage-free quantizer pass
+      free_axis(a.ax[0], m, 4);
+      free_axis(a.ax[1], n, std::max(q->group, 256 - 256 % q->group));
+      if (a.ax[1].P % q->group) a.ax[1].P = q->group;
+    }
+    if (i == 0) {
+      set_signs(a, U, V);
+      a.src = src;
+      a.src_t = src_t;
+      a.ld_src = ld_src;
+    } else {
+      a.src = ws;
+      a.src_t = BRQ_F32;
+      a.ld_src = n;
+    }
+    a.pro = PRO_LOAD;
+    const bool last = (i + 1 == npass);
+    if (last && q) {
+      a.epi = EPI_QUANT;
+      fill_quant(a, q, n);
+      a.codes = codes;
+      a.scales = scales;
+    } else if (last) {
+      a.epi = EPI_STORE;
+      a.dst = dst;
+      a.dst_t = dst_t;
+      a.ld_dst = ld_dst;
+    } else {
+      a.epi = EPI_STORE;
+      a.dst = ws;
+      a.dst_t = BRQ_F32;
+      a.ld_dst = n;
+    }
+    brq_status st = BRQ_OK;
+    if (checked_launch(a, s, &st) != hipSuccess) return st;
+  }
+  return BRQ_OK;
+}
+
+// Inverse: optional dequant prologue in the first pass, inverse stages in
+// reverse order, signs applied when storing the last pass.
+brq_status run_inverse(const Plan* U, const Plan* V, const void* src, int src_t, int64_t ld_src,
+                       const uint8_t* codes, const void* scales, const brq_quant* q, int64_t m,
+                       int64_t n, void* dst, int dst_t, int64_t ld_dst, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  std::vector<PassSpec> passes = plan_passes(U, V);
+  std::reverse(passes.begin(), passes.end());
+  const size_t npass = std::max<size_t>(passes.size(), 1);
+  const size_t need = npass > 1 ? (size_t)m * n * sizeof(float) : 0;
+  if (need && (!ws || ws_bytes < need))
+    return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  for (size_t i = 0; i < npass; ++i) {
+    PassArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.m = m;
+    a.n = n;
+    a.inverse = 1;
+    if (i < passes.size()) {
+      build_axes(a, passes[i], U, V, m, n, true);
+    } else {
+      free_axis(a.ax[0], m, 4);
+      free_axis(a.ax[1], n, 256);
+    }
+    if (i == 0) {
+      if (q) {
+        a.pro = PRO_DEQUANT;
+        fill_quant(a, q, n);
+        a.in_codes = codes;
+        a.in_scales = scales;
+      } else {
+        a.pro = PRO_LOAD;
+        a.src = src;
+        a.src_t = src_t;
+        a.ld_src = ld_src;
+      }
+    } else {
+      a.pro = PRO_LOAD;
+      a.src = ws;
+      a.src_t = BRQ_F32;
+      a.ld_src = n;
+    }
+    const bool last = (i + 1 == npass);
+    a.epi = EPI_STORE;
+    if (last) {
+      set_signs(a, U, V);
+      a.dst = dst;
+      a.dst_t = dst_t;
+      a.ld_dst = ld_dst;
+    } else {
+      a.dst = ws;
+      a.dst_t = BRQ_F32;
+      a.ld_dst = n;
+    }
+    brq_status st = BRQ_OK;
+    if (checked_launch(a, s, &st) != hipSuccess) return st;
+  }
+  return BRQ_OK;
+}
+
+brq_status rotate_common(const brq_plan* plan, int32_t side, int inverse, const void* x,
+                         int32_t xt, int64_t ldx, void* y, int32_t yt, int64_t ldy, int64_t rows,
+                         int64_t cols, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(BRQ_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (side != 0 && side != 1) return fail(BRQ_ERR_INVALID_ARGUMENT, "side must be 0 or 1");
+  if (!valid_dtype(xt) || !valid_dtype(yt)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (rows < 0 || cols < 0) return fail(BRQ_ERR_INVALID_ARGUMENT, "negative shape");
+  const Plan* p = &plan->p;
+  if (side == 0 && (cols == 0 || cols % p->d))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "plan d = %d must divide cols = %lld", p->d,
+                (long long)cols);
+  if (side == 1 && rows != p->d)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "left side needs rows == d (%lld vs %d)",
+                (long long)rows, p->d);
+  if (ldx < cols || ldy < cols) return fail(BRQ_ERR_INVALID_ARGUMENT, "leading dimension < cols");
+  if (rows == 0) return BRQ_OK;
+  if (!x || !y) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if (x == y && (xt != yt || ldx != ldy))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "in place needs equal dtype and leading dimension");
+  brq_status st = check_plan_device(p);
+  if (st != BRQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Plan* U = side == 1 ? p : nullptr;
+  const Plan* V = side == 0 ? p : nullptr;
+  if (!inverse && fused_rotate_supported(U, V, xt, yt, rows, cols, ldx, ldy, x, y))
+    return fused_rotate(U, V, x, xt, ldx, y, yt, ldy, rows, cols, s) == hipSuccess
+               ? BRQ_OK
+               : hip_fail(hipGetLastError(), "fused rotate launch");
+  if (!inverse)
+    return run_forward(U, V, x, xt, ldx, rows, cols, y, yt, ldy, nullptr, nullptr, nullptr, ws,
+                       ws_bytes, s);
+  return run_inverse(U, V, x, xt, ldx, nullptr, nullptr, nullptr, rows, cols, y, yt, ldy, ws,
+                     ws_bytes, s);
+}
+
+// ---------------------------------------------------------------- Lloyd-Max
+
+double npdf(double x) { return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI); }
+double upper_tail(double x) { return 0.5 * std::erfc(x / std::sqrt(2.0)); }
+
+// Residual of the centroid condition on the positive half (even level count).
+void lm_residual(const std::vector<double>& c, std::vector<double>& r) {
+  const size_t h = c.size();
+  r.resize(h);
+  for (size_t k = 0; k < h; ++k) {
+    const double a = k == 0 ? 0.0 : 0.5 * (c[k - 1] + c[k]);
+    const double b = k + 1 == h ? INFINITY : 0.5 * (c[k] + c[k + 1]);
+    const double pa = npdf(a), pb = std::isinf(b) ? 0.0 : npdf(b);
+    const double mass = upper_tail(a) - (std::isinf(b) ? 0.0 : upper_tail(b));
+    r[k] = c[k] - (pa - pb) / mass;
+  }
+}
+
+}  // namespace
+}  // namespace brq
+
+using namespace brq;
+
+extern "C" {
+
+const char* brq_status_string(brq_status s) {
+  switch (s) {
+    case BRQ_OK: return "BRQ_OK";
+    case BRQ_ERR_INVALID_ARGUMENT: return "BRQ_ERR_INVALID_ARGUMENT";
+    case BRQ_ERR_UNSUPPORTED: return "BRQ_ERR_UNSUPPORTED";
+    case BRQ_ERR_ALIGNMENT: return "BRQ_ERR_ALIGNMENT";
+    case BRQ_ERR_WORKSPACE: return "BRQ_ERR_WORKSPACE";
+    case BRQ_ERR_HIP: return "BRQ_ERR_HIP";
+  }
+  return "BRQ_UNKNOWN_STATUS";
+}
+
+const char* brq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t brq_version(void) { return 100; }
+
+brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const int32_t* radix,
+                           const float* blocks, int32_t mode, const int8_t* signs) {
+  g_last_error.clear();
+  if (!out) return fail(BRQ_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (d < 2) return fail(BRQ_ERR_INVALID_ARGUMENT, "d must be >= 2");
+  if (n_stages < 1 || n_stages > kMaxStages)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "n_stages must be 1..%d", kMaxStages);
+  if (!radix) return fail(BRQ_ERR_INVALID_ARGUMENT, "radix is NULL");
+  if (mode != BRQ_HADAMARD && mode != BRQ_SHARED && mode != BRQ_PER_GROUP)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "unknown block mode %d", mode);
+  int64_t prod = 1;
+  for (int t = 0; t < n_stages; ++t) {
+    if (radix[t] < 2) return fail(BRQ_ERR_INVALID_ARGUMENT, "radix[%d] = %d < 2", t, radix[t]);
+    prod *= radix[t];
+    if (prod > (int64_t)1 << 40) break;
+  }
+  if (prod != d)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "product of radices (%lld) != d (%d)", (long long)prod,
+                d);
+  if (d > (1 << 22)) return fail(BRQ_ERR_UNSUPPORTED, "d > 2^22");
+  for (int t = 0; t < n_stages; ++t) {
+    if (radix[t] > 64) return fail(BRQ_ERR_UNSUPPORTED, "radix[%d] = %d > 64", t, radix[t]);
+    if (mode == BRQ_HADAMARD && !is_pow2(radix[t]))
+      return fail(BRQ_ERR_UNSUPPORTED, "Hadamard radix %d is not a power of two", radix[t]);
+  }
+  if (mode != BRQ_HADAMARD && !blocks)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "blocks are required for this mode");
+  if (signs)
+    for (int i = 0; i < d; ++i)
+      if (signs[i] != 1 && signs[i] != -1)
+        return fail(BRQ_ERR_INVALID_ARGUMENT, "signs[%d] = %d is not +-1", i, (int)signs[i]);
+
+  brq_plan* h = new (std::nothrow) brq_plan;
+  if (!h) return fail(BRQ_ERR_HIP, "host allocation failed");
+  Plan& p = h->p;
+  p.d = d;
+  p.nst = n_stages;
+  p.mode = mode;
+  size_t total = 0;
+  for (int t = 0; t < n_stages; ++t) p.radix[t] = radix[t];
+  for (int t = 0; t < n_stages; ++t) {
+    int64_t s = 1;
+    for (int u = t + 1; u < n_stages; ++u) s *= radix[u];
+    p.stride[t] = (int)s;
+    p.blk_off[t] = total;
+    const size_t bb = (size_t)radix[t] * radix[t];
+    if (mode == BRQ_SHARED) total += bb;
+    else if (mode == BRQ_PER_GROUP) total += (size_t)(d / radix[t]) * bb;
+  }
+  hipError_t e = rt_get_device(&p.device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  std::vector<float> host_t;
+  if (total) {
+    e = rt_malloc((void**)&p.blk, total * sizeof(float));
+    if (e == hipSuccess) e = rt_malloc((void**)&p.blkT, total * sizeof(float));
+    if (e == hipSuccess) e = rt_copy_to_device(p.blk, blocks, total * sizeof(float));
+    if (e == hipSuccess) {
+      host_t.resize(total);
+      for (int t = 0; t < n_stages; ++t) {
+        const int b = radix[t];
+        const size_t nb = mode == BRQ_SHARED ? 1 : (size_t)(d / b);
+        for (size_t g = 0; g < nb; ++g) {
+          const float* src = blocks + p.blk_off[t] + g * b * b;
+          float* dst = host_t.data() + p.blk_off[t] + g * b * b;
+          for (int j = 0; j < b; ++j)
+            for (int k = 0; k < b; ++k) dst[k * b + j] = src[j * b + k];
+        }
+      }
+      e = rt_copy_to_device(p.blkT, host_t.data(), total * sizeof(float));
+    }
+  }
+  if (e == hipSuccess && signs) {
+    std::vector<float> sf(d);
+    for (int i = 0; i < d; ++i) sf[i] = (float)signs[i];
+    e = rt_malloc((void**)&p.signs, d * sizeof(float));
+    if (e == hipSuccess) e = rt_copy_to_device(p.signs, sf.data(), d * sizeof(float));
+  }
+  if (e == hipSuccess) e = fused_prepare(p);
+  if (e != hipSuccess) {
+    brq_status st = hip_fail(e, "plan device setup");
+    brq_plan_destroy(h);
+    return st;
+  }
+  *out = h;
+  return BRQ_OK;
+}
+
+brq_status brq_plan_destroy(brq_plan* plan) {
+  if (!plan) return BRQ_OK;
+  Plan& p = plan->p;
+  rt_free(p.blk);
+  rt_free(p.blkT);
+  rt_free(p.signs);
+  fused_release(p);
+  delete plan;
+  return BRQ_OK;
+}
+
+int32_t brq_plan_dim(const brq_plan* plan) { return plan ? plan->p.d : 0; }
+
+size_t brq_workspace_bytes(const brq_plan* left, const brq_plan* right, int64_t m, int64_t n) {
+  if (m <= 0 || n <= 0) return 0;
+  if (!left && !right) return (size_t)m * n * sizeof(float);  // stand-alone quantizer pass
+  return (size_t)m * n * sizeof(float);
+}
+
+brq_status brq_rotate(const brq_plan* plan, int32_t side, const void* x, int32_t xt, int64_t ldx,
+                      void* y, int32_t yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return rotate_common(plan, side, 0, x, xt, ldx, y, yt, ldy, rows, cols, ws, ws_bytes, stream);
+}
+
+brq_status brq_rotate_inverse(const brq_plan* plan, int32_t side, const void* x, int32_t xt,
+                              int64_t ldx, void* y, int32_t yt, int64_t ldy, int64_t rows,
+                              int64_t cols, void* ws, size_t ws_bytes, void* stream) {
+  return rotate_common(plan, side, 1, x, xt, ldx, y, yt, ldy, rows, cols, ws, ws_bytes, stream);
+}
+
+brq_status brq_rotate_quantize_pack(const brq_plan* left, const brq_plan* right, const void* w,
+                                    int32_t wt, int64_t m, int64_t n, int64_t ldw,
+                                    const brq_quant* q, uint8_t* codes, void* scales, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!valid_dtype(wt)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (m < 0 || n <= 0) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape");
+  if (ldw < n) return fail(BRQ_ERR_INVALID_ARGUMENT, "leading dimension < n");
+  brq_status st = check_quant(q, n);
+  if (st != BRQ_OK) return st;
+  const Plan* U = left ? &left->p : nullptr;
+  const Plan* V = right ? &right->p : nullptr;
+  if (U && U->d != m)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "left plan d = %d != m = %lld", U->d, (long long)m);
+  if (V && n % V->d)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "right plan d = %d does not divide n", V->d);
+  if (m == 0) return BRQ_OK;
+  if (!w || !codes || !scales) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if ((st = check_plan_device(U)) != BRQ_OK) return st;
+  if ((st = check_plan_device(V)) != BRQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused_rqp_supported(U, V, wt, m, n, ldw, w, q)) {
+    st = fused_rqp(U, V, w, wt, m, n, ldw, q, codes, scales, ws, ws_bytes, s);
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+  }
+  return run_forward(U, V, w, wt, ldw, m, n, nullptr, 0, 0, q, codes, scales, ws, ws_bytes, s);
+}
+
+brq_status brq_dequant_unrotate(const brq_plan* left, const brq_plan* right, const uint8_t* codes,
+                                const void* scales, const brq_quant* q, int64_t m, int64_t n,
+                                void* out, int32_t ot, int64_t ldo, void* ws, size_t ws_bytes,
+                                void* stream) {
+  g_last_error.clear();
+  if (!valid_dtype(ot)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (m < 0 || n <= 0) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape");
+  if (ldo < n) return fail(BRQ_ERR_INVALID_ARGUMENT, "leading dimension < n");
+  brq_status st = check_quant(q, n);
+  if (st != BRQ_OK) return st;
+  const Plan* U = left ? &left->p : nullptr;
+  const Plan* V = right ? &right->p : nullptr;
+  if (U && U->d != m)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "left plan d = %d != m = %lld", U->d, (long long)m);
+  if (V && n % V->d)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "right plan d = %d does not divide n", V->d);
+  if (m == 0) return BRQ_OK;
+  if (!codes || !scales || !out) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if ((st = check_plan_device(U)) != BRQ_OK) return st;
+  if ((st = check_plan_device(V)) != BRQ_OK) return st;
+  return run_inverse(U, V, nullptr, 0, 0, codes, scales, q, m, n, out, ot, ldo, ws, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
+brq_status brq_lloyd_max_gaussian(int32_t bits, float* centroids) {
+  g_last_error.clear();
+  if (bits < 1 || bits > 5) return fail(BRQ_ERR_INVALID_ARGUMENT, "bits must be 1..5");
+  if (!centroids) return fail(BRQ_ERR_INVALID_ARGUMENT, "centroids is NULL");
+  const int L = 1 << bits, h = L / 2;
+  // start from the conditional means of equal-mass cells of the half-normal
+  std::vector<double> c(h), r, cn(h);
+  {
+    std::vector<double> edges(h + 1);
+    edges[0] = 0.0;
+    for (int k = 1; k < h; ++k) {
+      // invert the half-normal CDF by bisection
+      const double target = (double)k / h;
+      double lo = 0, hi = 40;
+      for (int it = 0; it < 200; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        (1.0 - 2.0 * upper_tail(mid) < target ? lo : hi) = mid;
+      }
+      edges[k] = 0.5 * (lo + hi);
+    }
+    edges[h] = INFINITY;
+    for (int k = 0; k < h; ++k) {
+      const double a = edges[k], b = edges[k + 1];
+      const double mass = upper_tail(a) - (std::isinf(b) ? 0.0 : upper_tail(b));
+      c[k] = (npdf(a) - (std::isinf(b) ? 0.0 : npdf(b))) / mass;
+    }
+  }
+  // fixed-point iteration of the two optimality conditions ...
+  for (int it = 0; it < 2000; ++it) {
+    lm_residual(c, r);
+    for (int k = 0; k < h; ++k) c[k] -= r[k];
+  }
+  // ... then Newton steps with a finite-difference Jacobian
+  for (int it = 0; it < 50; ++it) {
+    lm_residual(c, r);
+    double err = 0;
+    for (double v : r) err = std::max(err, std::fabs(v));
+    if (err < 1e-14) break;
+    std::vector<double> J(h * h), rp;
+    for (int j = 0; j < h; ++j) {
+      std::vector<double> cp = c;
+      const double step = 1e-7 * std::max(1.0, std::fabs(c[j]));
+      cp[j] += step;
+      lm_residual(cp, rp);
+      for (int i = 0; i < h; ++i) J[i * h + j] = (rp[i] - r[i]) / step;
+    }
+    // solve J dx = r (Gaussian elimination with partial pivoting)
+    std::vector<double> bvec = r;
+    for (int col = 0; col < h; ++col) {
+      int piv = col;
+      for (int i = col + 1; i < h; ++i)
+        if (std::fabs(J[i * h + col]) > std::fabs(J[piv * h + col])) piv = i;
+      if (piv != col) {
+        for (int k = 0; k < h; ++k) std::swap(J[col * h + k], J[piv * h + k]);
+        std::swap(bvec[col], bvec[piv]);
+      }
+      for (int i = col + 1; i < h; ++i) {
+        const double f = J[i * h + col] / J[col * h + col];
+        for (int k = col; k < h; ++k) J[i * h + k] -= f * J[col * h + k];
+        bvec[i] -= f * bvec[col];
+      }
+    }
+    for (int i = h - 1; i >= 0; --i) {
+      double acc = bvec[i];
+      for (int k = i + 1; k < h; ++k) acc -= J[i * h + k] * cn[k];
+      cn[i] = acc / J[i * h + i];
+    }
+    for (int k = 0; k < h; ++k) c[k] -= cn[k];
+  }
+  lm_residual(c, r);
+  double err = 0;
+  for (double v : r) err = std::max(err, std::fabs(v));
+  if (!(err < 1e-12)) return fail(BRQ_ERR_UNSUPPORTED, "Lloyd-Max did not converge (%g)", err);
+  for (int k = 0; k < h; ++k) {
+    centroids[h + k] = (float)c[k];
+    centroids[h - 1 - k] = (float)-c[k];
+  }
+  return BRQ_OK;
+}
+
+}  // extern "C"

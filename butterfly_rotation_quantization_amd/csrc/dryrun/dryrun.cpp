@@ -1,0 +1,156 @@
+// Host dry run of libbrq: plans live in host memory and every kernel launch is
+// replaced by a walk over each index the kernel would touch, checked against
+// the extents of its buffers.  Built as libbrq_dryrun.so for CPU tests; it
+// never touches a GPU.  Device pointers passed to it are never dereferenced.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "brq_internal.h"
+
+namespace brq {
+
+static std::string g_violation;
+static long long g_launches = 0;
+
+static bool violation(const char* fmt, long long a, long long b) {
+  if (g_violation.empty()) {
+    char buf[256];
+    snprintf(buf, sizeof buf, fmt, a, b);
+    g_violation = buf;
+    fprintf(stderr, "[dryrun] %s\n", buf);
+  }
+  return false;
+}
+
+hipError_t rt_get_device(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+
+hipError_t rt_malloc(void** p, size_t bytes) {
+  *p = std::malloc(bytes ? bytes : 1);
+  return *p ? hipSuccess : hipErrorOutOfMemory;
+}
+
+hipError_t rt_copy_to_device(void* dst, const void* src, size_t bytes) {
+  std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+
+void rt_free(void* p) { std::free(p); }
+
+// Number of float elements of the block array one stage may address.
+static int64_t stage_block_floats(const StageDesc& st, const AxisDesc& ax) {
+  if (st.mode == BRQ_PER_GROUP) return (int64_t)(ax.d / st.b) * st.b * st.b;
+  if (st.mode == BRQ_SHARED) return (int64_t)st.b * st.b;
+  return 0;
+}
+
+static bool walk_stage(const StageDesc& st, const AxisDesc& ax, int axis, int64_t relbase,
+                       int nlines, int ldl, int64_t lds_floats) {
+  const int ngroups = (ax.P / st.b) * ax.W;
+  std::vector<int> touched((size_t)ax.P * ax.W, 0);
+  for (int gid = 0; gid < ngroups; ++gid) {
+    const TileGroup tg = tile_group(st, ax, gid);
+    for (int j = 0; j < st.b; ++j) {
+      const int e = tg.e0 + j * tg.estep;
+      if (e < 0 || e >= ax.P * ax.W) return violation("stage member %lld outside the tile (%lld)", e, ax.P * ax.W);
+      touched[e]++;
+      for (int line : {0, nlines - 1}) {
+        const int64_t a = axis ? (int64_t)line * ldl + e : (int64_t)e * ldl + line;
+        if (a < 0 || a >= lds_floats) return violation("LDS index %lld >= %lld", a, lds_floats);
+      }
+    }
+    if (st.mode == BRQ_PER_GROUP) {
+      const int64_t c = group_index(st, ax, relbase, tg);
+      const int64_t hi = (c + 1) * st.b * st.b;
+      if (c < 0 || hi > stage_block_floats(st, ax)) return violation("block group %lld of %lld", c, ax.d / st.b);
+    }
+  }
+  for (size_t e = 0; e < touched.size(); ++e)
+    if (touched[e] != 1) return violation("tile element %lld updated %lld times", (long long)e, touched[e]);
+  return true;
+}
+
+hipError_t launch_pass(const PassArgs& a, hipStream_t) {
+  ++g_launches;
+  const AxisDesc& X0 = a.ax[0];
+  const AxisDesc& X1 = a.ax[1];
+  const int64_t tr = axis_tiles(X0), tc = axis_tiles(X1);
+  const int RT = X0.P * X0.W, CT = X1.P * X1.W, ldl = CT + 1;
+  const int64_t lds_floats = (int64_t)RT * ldl;
+  std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
+  for (int64_t t = 0; t < tr * tc; ++t) {
+    const int64_t ir = t / tc, ic = t - (t / tc) * tc;
+    const AxisPos pr = axis_pos(X0, ir), pc = axis_pos(X1, ic);
+    for (int er = 0; er < RT; ++er) {
+      if (er >= pr.limit) continue;
+      const int64_t row = pr.base + axis_off(X0, er);
+      if (row < 0 || row >= a.m) return violation("row %lld outside [0, %lld)", row, a.m), hipErrorInvalidValue;
+      for (int ec = 0; ec < CT; ++ec) {
+        if (ec >= pc.limit) continue;
+        const int64_t col = pc.base + axis_off(X1, ec);
+        if (col < 0 || col >= a.n) return violation("col %lld outside [0, %lld)", col, a.n), hipErrorInvalidValue;
+        if (a.pro == PRO_LOAD && col >= a.ld_src) return violation("col %lld >= ld_src %lld", col, a.ld_src), hipErrorInvalidValue;
+        if (a.epi == EPI_STORE && col >= a.ld_dst) return violation("col %lld >= ld_dst %lld", col, a.ld_dst), hipErrorInvalidValue;
+        if (a.pro == PRO_DEQUANT && (col * a.bits) / 8 >= a.codes_ld)
+          return violation("code byte %lld >= %lld", (col * a.bits) / 8, a.codes_ld), hipErrorInvalidValue;
+        if (X1.sign && X1.sign_mod < 1) return violation("sign length %lld %lld", X1.sign_mod, 0), hipErrorInvalidValue;
+        cover[(size_t)(row * a.n + col)]++;
+      }
+    }
+    for (int s = 0; s < X0.nst; ++s)
+      if (!walk_stage(X0.st[s], X0, 0, pr.relbase, CT, ldl, lds_floats)) return hipErrorInvalidValue;
+    for (int s = 0; s < X1.nst; ++s)
+      if (!walk_stage(X1.st[s], X1, 1, pc.relbase, RT, ldl, lds_floats)) return hipErrorInvalidValue;
+    if (a.epi == EPI_QUANT) {
+      const int g = a.group, gpr = CT / g, nbytes = g * a.bits / 8;
+      if (g > 1024) return violation("group %lld > %lld", g, 1024), hipErrorInvalidValue;
+      for (int u = 0; u < RT * gpr; ++u) {
+        const int er = u / gpr, gi = u % gpr;
+        if (er >= pr.limit || (int64_t)gi * g >= pc.limit) continue;
+        const int64_t row = pr.base + er;
+        if ((pc.base + (int64_t)gi * g) % g) return violation("group start %lld not aligned to %lld", pc.base + gi * g, g), hipErrorInvalidValue;
+        const int64_t gcol = (pc.base + (int64_t)gi * g) / g;
+        const int64_t off = row * a.codes_ld + gcol * nbytes;
+        if (off < 0 || off + nbytes > a.m * a.codes_ld) return violation("codes [%lld, +%lld) outside", off, nbytes), hipErrorInvalidValue;
+        if (row * a.scales_ld + gcol >= a.m * a.scales_ld) return violation("scale %lld of %lld", row * a.scales_ld + gcol, a.m * a.scales_ld), hipErrorInvalidValue;
+        if ((int64_t)er * ldl + (int64_t)gi * g + g > lds_floats) return violation("quant LDS %lld > %lld", (int64_t)er * ldl + gi * g + g, lds_floats), hipErrorInvalidValue;
+      }
+    }
+  }
+  for (int64_t i = 0; i < a.m * a.n; ++i)
+    if (cover[(size_t)i] != 1) return violation("element %lld covered %lld times", i, cover[(size_t)i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+}  // namespace brq
+
+extern "C" {
+// Dry-run diagnostics (only in libbrq_dryrun.so).
+const char* brq_dryrun_violation(void) { return brq::g_violation.c_str(); }
+long long brq_dryrun_launches(void) { return brq::g_launches; }
+void brq_dryrun_reset(void) {
+  brq::g_violation.clear();
+  brq::g_launches = 0;
+}
+}
+
+// Kernel timing is meaningless without a device: the calls exist and report
+// no kernels.
+namespace brq {
+int prof_begin(const char*, hipStream_t) { return -1; }
+void prof_end(int, hipStream_t) {}
+}  // namespace brq
+
+extern "C" {
+brq_status brq_profile_enable(int32_t) { return BRQ_OK; }
+brq_status brq_profile_reset(void) { return BRQ_OK; }
+int32_t brq_profile_count(void) { return 0; }
+brq_status brq_profile_read(int32_t, char*, size_t, double*, int64_t*) {
+  return BRQ_ERR_INVALID_ARGUMENT;
+}
+}

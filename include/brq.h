@@ -1,0 +1,194 @@
+/*
+ * brq.h -- structured orthogonal rotation + group quantization on MI355X (gfx950).
+ *
+ * C ABI of libbrq.so.  Every data pointer passed to a hot call is a DEVICE
+ * pointer owned by the caller; the library never frees or keeps it.  Hot calls
+ * (brq_rotate*, brq_rotate_quantize_pack, brq_dequant_unrotate) are
+ * asynchronous on the caller's HIP stream (`stream` is a hipStream_t, NULL =
+ * the default stream), never allocate and never synchronise; a fault inside a
+ * kernel shows up at the caller's next synchronisation.  Launch failures are
+ * returned as BRQ_ERR_HIP.  Errors are returned, never thrown; the last
+ * error's detail text is kept per thread (brq_last_error).
+ *
+ * Sources of the operations (gist.science explainers):
+ *  [HARP] "HARP: Hadamard-Preconditioned Adaptive Rotation Processor for
+ *         Extreme LLM Quantization", technical summary sections 1, 2.1, 2.2, 2.4.
+ *  [PolarQuant] "PolarQuant: Optimal Gaussian Weight Quantization via Hadamard
+ *         Rotation for LLM Compression", technical overview sections 1 and 2.
+ */
+#ifndef BRQ_H
+#define BRQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BRQ_OK = 0,
+  BRQ_ERR_INVALID_ARGUMENT = 1, /* malformed call: shapes, NULLs, radices ...  */
+  BRQ_ERR_UNSUPPORTED = 2,      /* well-formed but outside what is implemented */
+  BRQ_ERR_ALIGNMENT = 3,        /* pointer or leading dimension misaligned     */
+  BRQ_ERR_WORKSPACE = 4,        /* workspace missing or too small              */
+  BRQ_ERR_HIP = 5               /* HIP runtime error (no device, launch, alloc)*/
+} brq_status;
+
+typedef enum { BRQ_F32 = 0, BRQ_BF16 = 1, BRQ_F16 = 2 } brq_dtype;
+
+/* How the b_t x b_t blocks of each stage are given. */
+typedef enum {
+  BRQ_HADAMARD = 0,  /* blocks = NULL; every radix a power of two; block of
+                        stage t is H_b/sqrt(b), H_b the +-1 Sylvester matrix in
+                        natural order ([HARP] 2.2, the base mixer G_b).        */
+  BRQ_SHARED = 1,    /* one [b_t][b_t] block per stage, used by every group  */
+  BRQ_PER_GROUP = 2  /* [d/b_t][b_t][b_t] per stage, one block per group c     */
+} brq_block_mode;
+
+typedef enum { BRQ_ABSMAX = 0, BRQ_CODEBOOK_NORM = 1 } brq_qkind;
+
+typedef struct brq_plan brq_plan;
+
+/* Group quantizer after the rotation.
+ *  kind ABSMAX ([PolarQuant] section 1, the linear map for values uniform on
+ *    [-alpha, alpha]): per contiguous group of `group` values along a row,
+ *    alpha = max|v|, h = (2^bits - 1)/2, code = clamp(rint(fma(v, h/alpha, h)),
+ *    0, 2^bits - 1) in float32 (rint: half to even), scales are float32 alpha
+ *    [m][n/group]; alpha = 0 gives codes 0.
+ *  kind CODEBOOK_NORM ([PolarQuant] section 2): r = ||v||_2 of the group,
+ *    z = v * (sqrt(group)/r), code = #{k : z > (c_k + c_{k+1})/2} for the
+ *    2^bits ascending float32 centroids in `codebook`; scales are float16 r
+ *    [m][n/group]; r = 0 gives codes 0.
+ *  Codes of a row form one little-endian bit stream: code k of the row sits in
+ *  stream bits [k*bits, (k+1)*bits), stream bit p = bit (p mod 8) of byte p/8.
+ *  The code array is [m][n*bits/8] bytes, rows contiguous.
+ *  bits in 2..5; group a power of two in 64..1024 dividing n. */
+typedef struct {
+  int32_t kind;       /* brq_qkind                                     */
+  int32_t bits;       /* 2..5                                          */
+  int32_t group;      /* 64, 128, 256, 512 or 1024                     */
+  float codebook[32]; /* CODEBOOK_NORM: 2^bits ascending centroids     */
+} brq_quant;
+
+/* Name of a status code (static string). */
+const char* brq_status_string(brq_status s);
+
+/* Detail text of the last error returned on this thread ("" if none). */
+const char* brq_last_error(void);
+
+/* Library ABI version (major*100 + minor). */
+int32_t brq_version(void);
+
+/*
+ * Create a transform plan for dimension d ([HARP] 2.1): a mixed-radix
+ * schedule radix[0..n_stages) with prod(radix) = d; stage t applies
+ * b_t x b_t blocks to the groups {base + k*S_t : k < b_t}, S_t =
+ * prod_{s>t} b_s (digit 0 most significant, last stage stride 1); the group
+ * index is c = (i / (b_t*S_t))*S_t + i % S_t; a group's output
+ * y[base + j*S_t] = sum_k B_{t,c}[j][k] x[base + k*S_t].
+ * The transform is M = B_{m-1} ... B_0 D with D = diag(signs) ([HARP] section
+ * 1: random signs, then the Hadamard-like stages).
+ *   blocks: host float32, layout per `mode` (stage after stage, each block
+ *           row-major [j][k]); NULL for BRQ_HADAMARD.
+ *   signs:  host int8 +-1 of length d, or NULL for all +1.
+ * The host arrays are copied; the plan owns device copies on the current HIP
+ * device, is immutable and may be used concurrently from several streams.
+ * Errors: INVALID_ARGUMENT (out == NULL, d < 2, n_stages not in 1..16,
+ * prod(radix) != d, radix < 2, blocks missing, a sign not +-1, bad mode),
+ * UNSUPPORTED (radix > 64, d > 2^22, Hadamard radix not a power of two),
+ * HIP (no device or allocation failure; nothing is leaked). */
+brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const int32_t* radix,
+                           const float* blocks, int32_t mode, const int8_t* signs);
+
+/* Free a plan and its device arrays; NULL is allowed.  The caller must make
+ * sure no queued work still uses the plan. */
+brq_status brq_plan_destroy(brq_plan* plan);
+
+/* Dimension of a plan (0 for NULL). */
+int32_t brq_plan_dim(const brq_plan* plan);
+
+/*
+ * Workspace bytes needed by brq_rotate / brq_rotate_inverse (pass left = NULL
+ * or right = NULL for one side), brq_rotate_quantize_pack and
+ * brq_dequant_unrotate for an m x n matrix.  The workspace holds the float32
+ * intermediate between passes (m*n*4 bytes when one is needed, else 0).
+ */
+size_t brq_workspace_bytes(const brq_plan* left, const brq_plan* right, int64_t m, int64_t n);
+
+/*
+ * One-sided rotation.  side 0 (RIGHT, row-contiguous): every row of
+ * x [rows][cols] (or every d-long chunk of a row when d < cols, block-diagonal)
+ * becomes M x, i.e. Y = X M^T.  side 1 (LEFT, column direction): d == rows and
+ * every column becomes M x, i.e. Y = M X.  brq_rotate_inverse applies M^T
+ * instead (the exact inverse for orthogonal blocks; [PolarQuant] section 2:
+ * the Hadamard transform is its own inverse).
+ *   x, y: device arrays of type xt / yt (F32, BF16, F16) with leading
+ *         dimensions ldx, ldy (elements, >= cols).  y may equal x only when
+ *         xt == yt and ldx == ldy.
+ *   ws:   device workspace of brq_workspace_bytes(...) bytes (may be NULL if
+ *         that is 0).
+ * Errors: INVALID_ARGUMENT (NULL pointers, d does not divide cols / d != rows,
+ * ld < cols, bad dtype or side), WORKSPACE, HIP.  rows == 0 is a no-op. */
+brq_status brq_rotate(const brq_plan* plan, int32_t side, const void* x, int32_t xt, int64_t ldx,
+                      void* y, int32_t yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
+                      size_t ws_bytes, void* stream);
+brq_status brq_rotate_inverse(const brq_plan* plan, int32_t side, const void* x, int32_t xt,
+                              int64_t ldx, void* y, int32_t yt, int64_t ldy, int64_t rows,
+                              int64_t cols, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Two-sided rotate, quantize and pack ([HARP] 2: the two-sided processor
+ * U W V^T ahead of the quantizer; [PolarQuant] 2 for the codebook kind):
+ * W' = M_U W M_V^T (left or right may be NULL: identity), then the group
+ * quantizer `q` along the rows of W'.
+ *   w:      device [m][n] of type wt, leading dimension ldw (elements).
+ *   left:   d == m; right: d divides n (block-diagonal when d < n).
+ *   codes:  device [m][n*bits/8] bytes; scales: device [m][n/group]
+ *           (float32 alpha for ABSMAX, float16 r for CODEBOOK_NORM).
+ *   ws:     device workspace, brq_workspace_bytes(left, right, m, n) bytes.
+ * Errors: INVALID_ARGUMENT (NULLs, shapes, bits/group/kind), UNSUPPORTED
+ * (group not a power of two in 64..1024), WORKSPACE, HIP. */
+brq_status brq_rotate_quantize_pack(const brq_plan* left, const brq_plan* right, const void* w,
+                                    int32_t wt, int64_t m, int64_t n, int64_t ldw,
+                                    const brq_quant* q, uint8_t* codes, void* scales, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/*
+ * Inverse of the above: unpack, dequantize (ABSMAX: v = alpha*(code/h - 1);
+ * CODEBOOK_NORM: v = r*c[code]/sqrt(group)), then W = M_U^T V M_V.
+ *   out: device [m][n] of type ot, leading dimension ldo.
+ * Errors as brq_rotate_quantize_pack. */
+brq_status brq_dequant_unrotate(const brq_plan* left, const brq_plan* right, const uint8_t* codes,
+                                const void* scales, const brq_quant* q, int64_t m, int64_t n,
+                                void* out, int32_t ot, int64_t ldo, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
+ * Host helper: the 2^bits Lloyd-Max centroids for N(0,1), ascending, rounded
+ * to float32 ([PolarQuant] section 2: MSE-optimal centroids for the standard
+ * normal, table stored in float32).  bits in 1..5; centroids has 2^bits
+ * entries.  Errors: INVALID_ARGUMENT, UNSUPPORTED (did not converge).
+ */
+brq_status brq_lloyd_max_gaussian(int32_t bits, float* centroids);
+
+/*
+ * Kernel timing (diagnostics).  While enabled, every kernel launched by the
+ * hot calls on this process is bracketed by a pair of HIP events recorded on
+ * the stream it is launched on; brq_profile_read waits for those events and
+ * returns, for the idx-th distinct kernel name (in order of first launch),
+ * the summed duration in milliseconds and the launch count since the last
+ * reset.  Enabling adds two event records per launch and nothing else.
+ * Errors: INVALID_ARGUMENT (idx out of range or NULL outputs), HIP.
+ */
+brq_status brq_profile_enable(int32_t on);
+brq_status brq_profile_reset(void);
+int32_t brq_profile_count(void);
+brq_status brq_profile_read(int32_t idx, char* name, size_t name_len, double* total_ms,
+                            int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRQ_H */

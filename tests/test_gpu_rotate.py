@@ -1,0 +1,112 @@
+"""GPU parity of the one-sided rotations against the oracle (small shapes that
+span several tiles with ragged tails)."""
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import transform as T
+from parity import check_rotation
+from gpu_util import announce, from_dev, lib_plan, method_for, orc_plan, to_dev, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+PLANS = [
+    ((2,) * 8, "hadamard"),
+    ((4, 4, 16), "per_group"),
+    ((16, 16), "shared"),
+    ((43, 16, 16), "per_group"),
+    ((3, 5, 7), "per_group"),
+    ((2,) * 12, "hadamard"),
+    ((16, 16, 16), "per_group"),
+    ((7, 16, 16, 16), "per_group"),
+    ((8, 8, 8, 5, 2), "per_group"),
+    ((64, 2), "per_group"),
+    ((2,) * 7, "hadamard"),
+]
+
+
+def _side(radix, mode, seed=7, signs=True):
+    return S.random_plan(np.random.default_rng(seed), radix, mode, with_signs=signs)
+
+
+def _input(rows, cols, dtype, seed=3):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols))
+    x[:, rng.choice(cols, size=max(1, cols // 100), replace=False)] *= 30.0
+    return S.to_storage(x, dtype)
+
+
+@pytest.mark.parametrize("radix,mode", PLANS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_right_rotate(radix, mode, dt):
+    import butterfly_rotation_quantization_amd as brq
+    side = _side(radix, mode)
+    d = side.d
+    rows = 37 if d <= 4096 else 5
+    cols = 2 * d if d <= 512 else d
+    announce(f"right rotate radix={radix} mode={mode} dt={dt} rows={rows} cols={cols}")
+    xs = _input(rows, cols, dt)
+    x = to_dev(xs, dt)
+    p = lib_plan(side)
+    y = brq.rotate(p, x, side="right")
+    ref = T.apply_right(orc_plan(side), S.storage_to_f64(xs, dt), method=method_for(d))
+    check_rotation(from_dev(y), ref, dt, f"right {radix}")
+    xi = brq.rotate_inverse(p, y.float() if dt == "f32" else y, side="right")
+    refi = T.apply_right(orc_plan(side), from_dev(y), inverse=True, method=method_for(d))
+    check_rotation(from_dev(xi), refi, dt, f"right inverse {radix}")
+
+
+@pytest.mark.parametrize("radix,mode", [p for p in PLANS if np.prod(p[0]) <= 4096])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_left_rotate(radix, mode, dt):
+    import butterfly_rotation_quantization_amd as brq
+    side = _side(radix, mode, seed=9)
+    d = side.d
+    cols = 45
+    announce(f"left rotate radix={radix} mode={mode} dt={dt} cols={cols}")
+    xs = _input(d, cols, dt, seed=4)
+    x = to_dev(xs, dt)
+    p = lib_plan(side)
+    y = brq.rotate(p, x, side="left")
+    ref = T.apply_left(orc_plan(side), S.storage_to_f64(xs, dt))
+    check_rotation(from_dev(y).T, ref.T, dt, f"left {radix}")
+    xi = brq.rotate_inverse(p, y, side="left")
+    refi = T.apply_left(orc_plan(side), from_dev(y), inverse=True)
+    check_rotation(from_dev(xi).T, refi.T, dt, f"left inverse {radix}")
+
+
+def test_mixed_dtypes_and_in_place():
+    import butterfly_rotation_quantization_amd as brq
+    torch = pytest.importorskip("torch")
+    side = _side((4, 4, 16), "per_group", seed=11)
+    xs = _input(19, 512, "bf16", seed=5)
+    x = to_dev(xs, "bf16")
+    p = lib_plan(side)
+    y = torch.empty((19, 512), dtype=torch.float32, device="cuda")
+    brq.rotate(p, x, y)
+    ref = T.apply_right(orc_plan(side), S.storage_to_f64(xs, "bf16"))
+    check_rotation(from_dev(y), ref, "f32", "bf16->f32")
+    y16 = torch.empty((19, 512), dtype=torch.float16, device="cuda")
+    brq.rotate(p, x, y16)
+    check_rotation(from_dev(y16), ref, "f16", "bf16->f16")
+    z = x.clone()
+    brq.rotate(p, z, z)  # in place, same dtype
+    check_rotation(from_dev(z), ref, "bf16", "in place")
+
+
+def test_leading_dimension_and_empty():
+    import butterfly_rotation_quantization_amd as brq
+    torch = pytest.importorskip("torch")
+    side = _side((16, 16), "per_group", seed=12)
+    xs = _input(33, 300, "f32", seed=6)
+    big = to_dev(xs, "f32")
+    x = big[:, 20:276]  # ld 300 > cols 256
+    y_big = torch.zeros((33, 290), dtype=torch.float32, device="cuda")
+    y = y_big[:, 10:266]
+    brq.rotate(lib_plan(side), x, y)
+    ref = T.apply_right(orc_plan(side), xs[:, 20:276].astype(np.float64))
+    check_rotation(from_dev(y), ref, "f32", "ld")
+    assert not y_big[:, :10].any() and not y_big[:, 266:].any()
+    e = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    brq.rotate(lib_plan(side), e, e.clone())

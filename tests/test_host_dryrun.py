@@ -1,0 +1,137 @@
+"""CPU dry run of every launch the GPU tests and the benchmark make.
+
+libbrq_dryrun.so is the same host layer (validation, pass planning, dispatch)
+built with host memory for plans and, in place of each kernel launch, a walk
+over every index the kernel would touch: global rows/columns, LDS slots, block
+and code offsets; it also checks that the tiles of each pass cover every
+matrix element exactly once.  Device pointers handed to it are never
+dereferenced, so fake addresses are used.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import butterfly_rotation_quantization_amd as brq
+import synthetic as S
+
+X, Y, WS, CODES, SCALES = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+@pytest.fixture(scope="module")
+def dl():
+    import os
+    if not os.path.exists(brq.DRYRUN_LIB_PATH):
+        pytest.fail("libbrq_dryrun.so is not built")
+    lib = brq.load_library(brq.DRYRUN_LIB_PATH)
+    lib.brq_dryrun_violation.restype = ctypes.c_char_p
+    lib.brq_dryrun_launches.restype = ctypes.c_longlong
+    return lib
+
+
+def _ok(dl, st, what):
+    msg = dl.brq_last_error().decode()
+    viol = dl.brq_dryrun_violation().decode()
+    assert st == 0 and not viol, f"{what}: status {st} {msg!r} violation {viol!r}"
+
+
+class DPlan:
+    def __init__(self, dl, side: S.SidePlan):
+        r = np.asarray(side.radix, dtype=np.int32)
+        blk = None
+        if side.blocks is not None:
+            blk = np.ascontiguousarray(np.concatenate([b.reshape(-1) for b in side.blocks]),
+                                       dtype=np.float32)
+        sg = None if side.signs is None else np.ascontiguousarray(side.signs, dtype=np.int8)
+        self.h = ctypes.c_void_p()
+        mode = {"hadamard": 0, "shared": 1, "per_group": 2}[side.mode]
+        st = dl.brq_plan_create(ctypes.byref(self.h), side.d, len(r), r.ctypes.data,
+                                None if blk is None else blk.ctypes.data, mode,
+                                None if sg is None else sg.ctypes.data)
+        _ok(dl, st, f"plan {side.radix}")
+        self.dl = dl
+
+    def __del__(self):
+        self.dl.brq_plan_destroy(self.h)
+
+
+def _rotate(dl, plan, side, rows, cols, xt=0, yt=0, inverse=False):
+    dl.brq_dryrun_reset()
+    fn = dl.brq_rotate_inverse if inverse else dl.brq_rotate
+    ws = dl.brq_workspace_bytes(plan.h if side else None, None if side else plan.h, rows, cols)
+    st = fn(plan.h, side, X, xt, cols, Y, yt, cols, rows, cols, WS, ws, None)
+    _ok(dl, st, f"rotate side={side} inverse={inverse} {rows}x{cols}")
+    assert dl.brq_dryrun_launches() >= 1
+
+
+def _rqp(dl, left, right, m, n, bits, group, kind=0):
+    q = brq.make_quant(bits, group, kind,
+                       np.linspace(-2, 2, 1 << bits) if kind == 1 else None)
+    ws = dl.brq_workspace_bytes(left.h if left else None, right.h if right else None, m, n)
+    dl.brq_dryrun_reset()
+    st = dl.brq_rotate_quantize_pack(left.h if left else None, right.h if right else None, X, 1,
+                                     m, n, n, ctypes.byref(q), CODES, SCALES, WS, ws, None)
+    _ok(dl, st, f"rqp {m}x{n} b{bits} g{group}")
+    dl.brq_dryrun_reset()
+    st = dl.brq_dequant_unrotate(left.h if left else None, right.h if right else None, CODES,
+                                 SCALES, ctypes.byref(q), m, n, Y, 0, n, WS, ws, None)
+    _ok(dl, st, f"dequant {m}x{n} b{bits} g{group}")
+
+
+ROTATE_PLANS = [
+    ((2,) * 8, "hadamard"), ((4, 4, 16), "per_group"), ((16, 16), "shared"),
+    ((43, 16, 16), "per_group"), ((3, 5, 7), "per_group"), ((2,) * 12, "hadamard"),
+    ((16, 16, 16), "per_group"), ((7, 16, 16, 16), "per_group"),
+    ((8, 8, 8, 5, 2), "per_group"), ((64, 2), "per_group"), ((2,) * 7, "hadamard"),
+    ((32, 16, 16), "per_group"), ((2,) * 16, "hadamard"),
+]
+
+
+@pytest.mark.parametrize("radix,mode", ROTATE_PLANS)
+def test_rotate_launches(dl, radix, mode):
+    side = S.random_plan(np.random.default_rng(1), radix, mode)
+    p = DPlan(dl, side)
+    d = side.d
+    for inverse in (False, True):
+        _rotate(dl, p, 0, 37 if d <= 4096 else 5, 2 * d if d <= 512 else d, inverse=inverse)
+        _rotate(dl, p, 0, 1, d, 1, 2, inverse=inverse)
+        if d <= 8192:
+            _rotate(dl, p, 1, d, 45, 2, 0, inverse=inverse)
+            _rotate(dl, p, 1, d, 1, inverse=inverse)
+
+
+def test_quant_launches_small(dl):
+    rng = np.random.default_rng(2)
+    tiny = S.tiny()
+    for name in ("rht", "harp"):
+        _rqp(dl, None, DPlan(dl, tiny[name]), 64, 256, 4, 128)
+    r = DPlan(dl, S.random_plan(rng, (4, 4, 16), "per_group"))
+    for bits in (2, 3, 4, 5):
+        for group in (64, 128, 256):
+            _rqp(dl, None, r, 45, 1024, bits, group)
+    h = DPlan(dl, S.SidePlan(128, (2,) * 7, "hadamard", None, None))
+    for bits in (2, 3, 4, 5):
+        _rqp(dl, None, h, 40, 512, bits, 128, kind=1)
+    left = DPlan(dl, S.random_plan(rng, (4, 4, 4), "per_group"))
+    right = DPlan(dl, S.random_plan(rng, (43, 16, 4), "per_group"))
+    _rqp(dl, left, right, 64, 2752, 3, 64)
+    l2 = DPlan(dl, S.random_plan(rng, (16, 8), "per_group"))
+    _rqp(dl, l2, None, 128, 320, 4, 64)
+    _rqp(dl, None, None, 128, 320, 3, 64)
+    r16 = DPlan(dl, S.random_plan(rng, (16, 16), "per_group"))
+    _rqp(dl, None, r16, 13, 512, 4, 128)
+
+
+def test_quant_launches_workload_shapes(dl):
+    """The shapes of the benchmark workload and the full-size parity cases."""
+    rng = np.random.default_rng(3)
+    u = DPlan(dl, S.random_plan(rng, (16, 16, 16), "per_group"))
+    v = DPlan(dl, S.random_plan(rng, (43, 16, 16), "per_group"))
+    _rqp(dl, u, v, 4096, 11008, 3, 128)
+    hu = DPlan(dl, S.SidePlan(4096, (2,) * 12, "hadamard", None, S.signs(rng, 4096)))
+    hv = DPlan(dl, S.SidePlan(4096, (2,) * 12, "hadamard", None, S.signs(rng, 4096)))
+    _rqp(dl, hu, hv, 4096, 4096, 4, 128)
+    _rotate(dl, hv, 0, 2048, 4096, 1, 1)
+    h = DPlan(dl, S.SidePlan(128, (2,) * 7, "hadamard", None, None))
+    _rqp(dl, None, h, 12288, 4096, 4, 128, kind=1)
