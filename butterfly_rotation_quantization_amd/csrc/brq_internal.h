@@ -25,6 +25,19 @@ struct Plan {
   float* blk = nullptr;              // blocks as given, [group][j][k] (or [j][k] shared)
   float* blkT = nullptr;             // the same blocks transposed, for the inverse
   float* signs = nullptr;            // +-1 as float, or nullptr
+  // Fast-path data (fused_prepare), for plans of the shape (b0, 16, 16):
+  // stage-0 blocks zero-padded to [groups][16*fz_nb][16*fz_nb], block
+  // pointers of stages 1 and 2, and float strides between groups (0 = one
+  // block shared by all groups).
+  int fz_ok = 0;
+  int fz_nb = 0;
+  float* fz0 = nullptr;
+  int64_t fz_gs0 = 0;
+  const float* fz1 = nullptr;
+  int64_t fz_gs1 = 0;
+  const float* fz2 = nullptr;
+  int64_t fz_gs2 = 0;
+  float* fz_had = nullptr;           // Hadamard blocks materialised for stages 1 and 2
 };
 
 // One stage applied inside a pass, along one axis of the tile.

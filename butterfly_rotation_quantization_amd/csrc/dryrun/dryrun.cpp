@@ -154,3 +154,163 @@ brq_status brq_profile_read(int32_t, char*, size_t, double*, int64_t*) {
   return BRQ_ERR_INVALID_ARGUMENT;
 }
 }
+
+// ---------------------------------------------------------------- fast path
+
+#include "fused.h"
+
+namespace brq {
+
+static bool in_range(int64_t lo, int64_t n, int64_t extent) { return lo >= 0 && lo + n <= extent; }
+
+hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
+  ++g_launches;
+  const int64_t nwg = fa_nwg(a);
+  const int nb = a.nb, bv = a.bv;
+  const int64_t ldsn = fa_lds_floats(nb, bv);
+  const int elem = a.wt == BRQ_F32 ? 4 : 2;
+  std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
+  std::vector<int> slot_in(ldsn), slot_out(ldsn);
+  for (int64_t b = 0; b < nwg; ++b) {
+    const FaTile t = fa_tile(a, b, nwg);
+    if (t.p0 < 0 || t.p0 + kFaP > 256 || t.q0 < 0 || t.q0 + kFaQC > 256 || t.chunk < 0 ||
+        t.chunk >= a.nchunk)
+      return violation("pass A tile %lld of %lld", b, nwg), hipErrorInvalidValue;
+    for (int w = 0; w < kFaWaves; ++w) {
+      const int p = t.p0 + w;
+      for (int l = 0; l < 64; ++l) {
+        const int lr = l & 15, lg = l >> 4;
+        for (int kb = 0; kb < nb; ++kb)
+          for (int nt = 0; nt < nb; ++nt)
+            if (!in_range(p * a.v0_gs + (16 * nt + lr) * (16 * nb) + 16 * kb + 4 * lg, 4, a.v0_n))
+              return violation("V_0 block read (p %lld, lane %lld)", p, l), hipErrorInvalidValue;
+      }
+    }
+    for (int q = t.q0; q < t.q0 + kFaQC; ++q) {
+      std::fill(slot_in.begin(), slot_in.end(), 0);
+      std::fill(slot_out.begin(), slot_out.end(), 0);
+      for (int it = 0; it < 16 * bv * 2; ++it) {
+        const int r0 = it / (bv * 2), rem = it % (bv * 2), c0 = rem >> 1, hh = rem & 1;
+        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 8 * hh);
+        if (row >= a.m || !in_range(col, 8, a.n) || col + 8 > a.ldw || (col * elem) % 16)
+          return violation("pass A input (%lld, %lld)", row, col), hipErrorInvalidValue;
+        if (a.su && row >= a.m) return violation("row sign %lld", row, 0), hipErrorInvalidValue;
+        if (!in_range(c0 * 256 + t.p0 + 8 * hh, 8, a.dv))
+          return violation("column sign %lld", c0 * 256 + t.p0 + 8 * hh, 0), hipErrorInvalidValue;
+        for (int e = 0; e < 8; ++e) {
+          const int s = fa_lds_in(nb, 8 * hh + e, r0, c0);
+          if (s < 0 || s >= ldsn) return violation("pass A LDS in %lld", s, ldsn), hipErrorInvalidValue;
+          slot_in[s]++;
+        }
+      }
+      for (int w = 0; w < kFaWaves; ++w)
+        for (int l = 0; l < 64; ++l) {
+          const int lr = l & 15, lg = l >> 4;
+          for (int kb = 0; kb < nb; ++kb) {
+            const int s = fa_lds_in(nb, w, lr, 16 * kb + 4 * lg);
+            if (!in_range(s, 4, ldsn) || s % 4) return violation("pass A A-read %lld", s, ldsn), hipErrorInvalidValue;
+            for (int i = 0; i < 4; ++i)
+              if (16 * kb + 4 * lg + i < bv && slot_in[s + i] != 1)
+                return violation("pass A A-read of an unwritten slot %lld", s + i, 0), hipErrorInvalidValue;
+          }
+          if (!in_range((int64_t)q * a.u0_gs + lr * 16 + 4 * lg, 4, a.u0_n))
+            return violation("U_0 block read q %lld lane %lld", q, l), hipErrorInvalidValue;
+          for (int nt = 0; nt < nb; ++nt)
+            for (int i = 0; i < 4; ++i) {
+              const int c0 = 16 * nt + 4 * lg + i;
+              if (c0 >= bv) continue;
+              const int s = fa_lds_out(bv, lr, c0, w);
+              if (s < 0 || s >= ldsn) return violation("pass A LDS out %lld", s, ldsn), hipErrorInvalidValue;
+              slot_out[s]++;
+            }
+        }
+      for (int it = 0; it < 16 * bv * (kFaP / 4); ++it) {
+        const int r0 = it / (bv * 4), rem = it % (bv * 4), c0 = rem >> 2, qd = rem & 3;
+        const int s = fa_lds_out(bv, r0, c0, 4 * qd);
+        if (!in_range(s, 4, ldsn) || s % 4) return violation("pass A store read %lld", s, 0), hipErrorInvalidValue;
+        for (int i = 0; i < 4; ++i)
+          if (slot_out[s + i] != 1) return violation("pass A output slot %lld written %lld times", s + i, slot_out[s + i]), hipErrorInvalidValue;
+        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * qd);
+        if (row >= a.m || !in_range(col, 4, a.n) || (row * a.n + col) % 4)
+          return violation("pass A store (%lld, %lld)", row, col), hipErrorInvalidValue;
+        for (int i = 0; i < 4; ++i) cover[(size_t)(row * a.n + col + i)]++;
+      }
+    }
+  }
+  for (int64_t i = 0; i < a.m * a.n; ++i)
+    if (cover[(size_t)i] != 1) return violation("pass A element %lld written %lld times", i, cover[(size_t)i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_fused_b(const FusedBArgs& a, hipStream_t) {
+  ++g_launches;
+  const int64_t nwg = fb_nwg(a);
+  std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
+  std::vector<int> slot(kFbXchFloats);
+  const int bits = a.bits, g = a.group;
+  const int fpg = g / 16, nw = fpg * 16 * bits / 32;
+  for (int64_t b = 0; b < nwg; ++b) {
+    const FbTile t = fb_tile(a, b);
+    if (t.r0 < 0 || t.r0 >= 16 || t.c0 < 0 || t.c0 >= a.bv || t.chunk < 0 || t.chunk >= a.nchunk)
+      return violation("pass B tile %lld of %lld", b, nwg), hipErrorInvalidValue;
+    for (int w = 0; w < kFbWaves; ++w)
+      for (int l = 0; l < 64; ++l) {
+        const int lr = l & 15, lg = l >> 4;
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = fb_row(t, lr, w), col = fb_col(a, t, 4 * lg + i, 0);
+          if (row >= a.m || !in_range(col, 16, a.n) || (row * a.n + col) % 4)
+            return violation("pass B load (%lld, %lld)", row, col), hipErrorInvalidValue;
+          for (int c2 = 0; c2 < 16; ++c2) cover[(size_t)(row * a.n + col + c2)]++;
+        }
+        if (!in_range((int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg, 4, a.u1_n) ||
+            !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg, 4, a.u2_n))
+          return violation("U_1/U_2 block read wave %lld lane %lld", w, l), hipErrorInvalidValue;
+        for (int c = 0; c < 16; ++c)
+          if (!in_range((int64_t)(t.c0 * 16 + c) * a.v1_gs + lr * 16 + 4 * lg, 4, a.v1_n) ||
+              !in_range((int64_t)(t.c0 * 16 + c) * a.v2_gs + lr * 16 + 4 * lg, 4, a.v2_n))
+            return violation("V_1/V_2 block read c %lld lane %lld", c, l), hipErrorInvalidValue;
+      }
+    for (int h = 0; h < 2; ++h) {
+      std::fill(slot.begin(), slot.end(), 0);
+      for (int w = 0; w < kFbWaves; ++w)
+        for (int l = 0; l < 64; ++l) {
+          const int lr = l & 15, lg = l >> 4;
+          if ((lg >> 1) != h) continue;
+          for (int c2 = 0; c2 < 16; ++c2)
+            for (int i = 0; i < 4; ++i) {
+              const int s = fb_xch(lr, 4 * lg + i - 8 * h, w, c2);
+              if (s < 0 || s >= kFbXchFloats) return violation("exchange write %lld", s, 0), hipErrorInvalidValue;
+              slot[s]++;
+            }
+        }
+      for (int s = 0; s < kFbXchFloats; ++s)
+        if (slot[s] != 1) return violation("exchange slot %lld written %lld times", s, slot[s]), hipErrorInvalidValue;
+      for (int w = 0; w < kFbWaves; ++w)
+        for (int l = 0; l < 64; ++l) {
+          const int lr = l & 15, lg = l >> 4;
+          for (int c1h = 0; c1h < 8; ++c1h) {
+            const int s = fb_xch(w, c1h, lr, 4 * lg);
+            if (!in_range(s, 4, kFbXchFloats) || s % 4) return violation("exchange read %lld", s, 0), hipErrorInvalidValue;
+            for (int i = 0; i < 4; ++i)
+              if (fb_xch(w, c1h, lr, 4 * lg + i) != s + i) return violation("exchange quad %lld", s, i), hipErrorInvalidValue;
+          }
+          if (lg != 0) continue;
+          const int64_t row = fb_row(t, w, lr);
+          for (int gi = 0; gi < 128 / g; ++gi) {
+            const int64_t col0 = fb_col(a, t, 8 * h + gi * fpg, 0);
+            if (col0 % g) return violation("group start %lld", col0, g), hipErrorInvalidValue;
+            const int64_t off = row * a.codes_ld + col0 * bits / 8;
+            if (!in_range(off, 4 * nw, a.m * a.codes_ld) || off % 4)
+              return violation("codes [%lld, +%lld)", off, 4 * nw), hipErrorInvalidValue;
+            if (!in_range(row * a.scales_ld + col0 / g, 1, a.m * a.scales_ld))
+              return violation("scale %lld", row * a.scales_ld + col0 / g, 0), hipErrorInvalidValue;
+          }
+        }
+    }
+  }
+  for (int64_t i = 0; i < a.m * a.n; ++i)
+    if (cover[(size_t)i] != 1) return violation("pass B element %lld read %lld times", i, cover[(size_t)i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+}  // namespace brq

@@ -1,28 +1,211 @@
-// Host dispatch of the fast paths (MFMA tile kernels) -- not yet enabled: every call goes through
-// the generic tile pass.
+// Host side of the two-sided fast path: plan preparation, the coverage test
+// and the launch of its two kernels.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
 #include "fused.h"
 
 namespace brq {
 
-hipError_t fused_prepare(Plan&) { return hipSuccess; }
-void fused_release(Plan&) {}
+int prof_begin(const char* name, hipStream_t s);
+void prof_end(int token, hipStream_t s);
+
+namespace {
+
+bool fused_shape(const Plan& p) {
+  return p.nst == 3 && p.radix[1] == 16 && p.radix[2] == 16 && p.radix[0] >= 2 &&
+         p.radix[0] <= 64;
+}
+
+// Sylvester Hadamard block H_b / sqrt(b), row-major, H[j][k] = (-1)^popcount(j & k).
+void hadamard_block(int b, float* out) {
+  const float s = 1.0f / std::sqrt((float)b);
+  for (int j = 0; j < b; ++j)
+    for (int k = 0; k < b; ++k) out[j * b + k] = (__builtin_popcount(j & k) & 1) ? -s : s;
+}
+
+}  // namespace
+
+hipError_t fused_prepare(Plan& p, const float* host_blocks) {
+  if (!fused_shape(p)) return hipSuccess;
+  const int b0 = p.radix[0];
+  const int nb = (b0 + 15) / 16;
+  const int np = 16 * nb;
+  const bool shared = p.mode != BRQ_PER_GROUP;
+  const int ng0 = shared ? 1 : p.d / b0;
+  std::vector<float> pad((size_t)ng0 * np * np, 0.f);
+  std::vector<float> src;
+  if (p.mode == BRQ_HADAMARD) {
+    src.resize((size_t)b0 * b0);
+    hadamard_block(b0, src.data());
+  }
+  const float* g0 = p.mode == BRQ_HADAMARD ? src.data() : host_blocks + p.blk_off[0];
+  for (int g = 0; g < ng0; ++g)
+    for (int j = 0; j < b0; ++j)
+      for (int k = 0; k < b0; ++k)
+        pad[((size_t)g * np + j) * np + k] = g0[((size_t)g * b0 + j) * b0 + k];
+  hipError_t e = rt_malloc((void**)&p.fz0, pad.size() * sizeof(float));
+  if (e == hipSuccess) e = rt_copy_to_device(p.fz0, pad.data(), pad.size() * sizeof(float));
+  if (e != hipSuccess) return e;
+  p.fz_nb = nb;
+  p.fz_gs0 = shared ? 0 : (int64_t)np * np;
+  if (p.mode == BRQ_HADAMARD) {
+    std::vector<float> h16(256);
+    hadamard_block(16, h16.data());
+    e = rt_malloc((void**)&p.fz_had, 256 * sizeof(float));
+    if (e == hipSuccess) e = rt_copy_to_device(p.fz_had, h16.data(), 256 * sizeof(float));
+    if (e != hipSuccess) return e;
+    p.fz1 = p.fz_had;
+    p.fz2 = p.fz_had;
+    p.fz_gs1 = p.fz_gs2 = 0;
+  } else {
+    p.fz1 = p.blk + p.blk_off[1];
+    p.fz2 = p.blk + p.blk_off[2];
+    p.fz_gs1 = p.fz_gs2 = shared ? 0 : 256;
+  }
+  p.fz_ok = 1;
+  return hipSuccess;
+}
+
+namespace {
+
+// Host check of what the two kernels' index arithmetic relies on.
+const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
+  if (a.bv < 2 || a.bv > 64 || a.nb != (a.bv + 15) / 16) return "V_0 radix";
+  if (a.m != 4096 || a.dv != a.bv * 256 || (int64_t)a.nchunk * a.dv != a.n) return "shape";
+  if (a.nqc * kFaQC != 256 || fa_nwg(a) % 8) return "pass A grid";
+  if (!a.w || !a.ws || !a.u0 || !a.v0) return "pass A pointers";
+  if (a.u0_gs && a.u0_n < 256 * a.u0_gs) return "U_0 extent";
+  if (a.v0_gs && a.v0_n < 256 * a.v0_gs) return "V_0 extent";
+  if (a.u0_n < 256 || a.v0_n < 256 * a.nb * a.nb) return "block extent";
+  if (b.bv != a.bv || b.nchunk != a.nchunk || b.dv != a.dv || b.m != a.m || b.n != a.n)
+    return "pass B shape";
+  if (!b.u1 || !b.u2 || !b.v1 || !b.v2 || !b.codes || !b.scales) return "pass B pointers";
+  if (b.u1_gs && b.u1_n < 256 * b.u1_gs) return "U_1 extent";
+  if (b.u2_gs && b.u2_n < 256 * b.u2_gs) return "U_2 extent";
+  if (b.v1_gs && b.v1_n < (int64_t)b.bv * 16 * b.v1_gs) return "V_1 extent";
+  if (b.v2_gs && b.v2_n < (int64_t)b.bv * 16 * b.v2_gs) return "V_2 extent";
+  if (b.group != 64 && b.group != 128) return "group";
+  if (b.bits < 2 || b.bits > 5 || b.nlev != (1 << b.bits)) return "bits";
+  if (b.codes_ld * 8 != b.n * b.bits || b.codes_ld % 4 || b.scales_ld * b.group != b.n)
+    return "code layout";
+  return nullptr;
+}
+
+}  // namespace
+
+void fused_release(Plan& p) {
+  rt_free(p.fz0);
+  rt_free(p.fz_had);
+  p.fz0 = p.fz_had = nullptr;
+  p.fz_ok = 0;
+}
 
 bool fused_rotate_supported(const Plan*, const Plan*, int, int, int64_t, int64_t, int64_t, int64_t,
                             const void*, const void*) {
   return false;
 }
+
 hipError_t fused_rotate(const Plan*, const Plan*, const void*, int, int64_t, void*, int, int64_t,
                         int64_t, int64_t, hipStream_t) {
   return hipErrorNotSupported;
 }
 
-bool fused_rqp_supported(const Plan*, const Plan*, int, int64_t, int64_t, int64_t, const void*,
-                         const brq_quant*) {
-  return false;
+// Two-sided, left (16,16,16) over all rows, right (b0,16,16) on every d-chunk
+// of a row, 16-byte aligned rows, quantizer groups of 64 or 128 columns with
+// whole 32-bit code words per group and per row.
+bool fused_rqp_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_t n, int64_t ldw,
+                         const void* w, const brq_quant* q) {
+  if (!U || !V || !U->fz_ok || !V->fz_ok) return false;
+  if (U->radix[0] != 16 || U->d != m || n % V->d) return false;
+  if (q->group != 64 && q->group != 128) return false;
+  if ((n * q->bits) % 32) return false;
+  const int elem = wt == BRQ_F32 ? 4 : 2;
+  if ((ldw * elem) % 16 || reinterpret_cast<uintptr_t>(w) % 16) return false;
+  return true;
 }
-brq_status fused_rqp(const Plan*, const Plan*, const void*, int, int64_t, int64_t, int64_t,
-                     const brq_quant*, uint8_t*, void*, void*, size_t, hipStream_t) {
-  return BRQ_ERR_UNSUPPORTED;
+
+brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_t m, int64_t n,
+                     int64_t ldw, const brq_quant* q, uint8_t* codes, void* scales, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
+  const size_t need = (size_t)m * n * sizeof(float);
+  if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16) return BRQ_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(scales) % 4)
+    return BRQ_ERR_UNSUPPORTED;
+
+  FusedAArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.w = w;
+  a.wt = wt;
+  a.ldw = ldw;
+  a.ws = static_cast<float*>(ws);
+  a.m = m;
+  a.n = n;
+  a.bv = V->radix[0];
+  a.nb = V->fz_nb;
+  a.dv = V->d;
+  a.nchunk = (int)(n / V->d);
+  a.u0 = U->mode == BRQ_HADAMARD ? nullptr : U->blk + U->blk_off[0];
+  a.u0_gs = U->mode == BRQ_PER_GROUP ? 256 : 0;
+  if (U->mode == BRQ_HADAMARD) {
+    a.u0 = U->fz0;  // H16/4 padded to 16 x 16 is the block itself
+    a.u0_gs = 0;
+  }
+  a.v0 = V->fz0;
+  a.v0_gs = V->fz_gs0;
+  a.su = U->signs;
+  a.sv = V->signs;
+  a.nqc = 256 / kFaQC;
+
+  FusedBArgs b;
+  std::memset(&b, 0, sizeof b);
+  b.ws = a.ws;
+  b.m = m;
+  b.n = n;
+  b.bv = a.bv;
+  b.nchunk = a.nchunk;
+  b.dv = a.dv;
+  b.u1 = U->fz1;
+  b.u1_gs = U->fz_gs1;
+  b.u2 = U->fz2;
+  b.u2_gs = U->fz_gs2;
+  b.v1 = V->fz1;
+  b.v1_gs = V->fz_gs1;
+  b.v2 = V->fz2;
+  b.v2_gs = V->fz_gs2;
+  b.qkind = q->kind;
+  b.bits = q->bits;
+  b.group = q->group;
+  b.nlev = 1 << q->bits;
+  b.h = (float)((b.nlev - 1) * 0.5);
+  b.sqrt_g = std::sqrt((float)q->group);
+  for (int i = 0; i + 1 < b.nlev; ++i)
+    b.tau[i] = q->kind == BRQ_CODEBOOK_NORM ? (q->codebook[i] + q->codebook[i + 1]) * 0.5f : 0.f;
+  b.codes = codes;
+  b.scales = scales;
+  b.codes_ld = n * q->bits / 8;
+  b.scales_ld = n / q->group;
+  const int64_t u16 = U->mode == BRQ_PER_GROUP ? (int64_t)(U->d / 16) * 256 : 256;
+  const int64_t v16 = V->mode == BRQ_PER_GROUP ? (int64_t)(V->d / 16) * 256 : 256;
+  a.u0_n = u16;
+  a.v0_n = (V->mode == BRQ_PER_GROUP ? (int64_t)(V->d / V->radix[0]) : 1) * 256 * a.nb * a.nb;
+  b.u1_n = b.u2_n = u16;
+  b.v1_n = b.v2_n = v16;
+  if (check_fused(a, b)) return BRQ_ERR_UNSUPPORTED;
+
+  char name[96];
+  snprintf(name, sizeof name, "fusedA U0(16) V0(%d)", a.bv);
+  int tok = prof_begin(name, s);
+  hipError_t e = launch_fused_a(a, s);
+  prof_end(tok, s);
+  if (e != hipSuccess) return BRQ_ERR_HIP;
+  snprintf(name, sizeof name, "fusedB U(16,16) V(16,16) quant b%d g%d", q->bits, q->group);
+  tok = prof_begin(name, s);
+  e = launch_fused_b(b, s);
+  prof_end(tok, s);
+  return e == hipSuccess ? BRQ_OK : BRQ_ERR_HIP;
 }
 
 }  // namespace brq

@@ -135,3 +135,25 @@ def test_quant_launches_workload_shapes(dl):
     _rotate(dl, hv, 0, 2048, 4096, 1, 1)
     h = DPlan(dl, S.SidePlan(128, (2,) * 7, "hadamard", None, None))
     _rqp(dl, None, h, 12288, 4096, 4, 128, kind=1)
+
+
+@pytest.mark.parametrize("bv,mode,chunks,bits,group,wt", [
+    (43, "per_group", 1, 3, 128, 1), (16, "per_group", 1, 4, 128, 0), (32, "shared", 1, 2, 64, 2),
+    (64, "per_group", 1, 5, 128, 1), (7, "per_group", 2, 4, 64, 1), (16, "hadamard", 1, 2, 128, 1),
+    (43, "per_group", 1, 4, 64, 0),
+])
+def test_fused_two_sided_launches(dl, bv, mode, chunks, bits, group, wt):
+    """Two-sided (16,16,16) x (bv,16,16) calls take the two-kernel fast path
+    (2 launches) and every index of both kernels stays in bounds."""
+    rng = np.random.default_rng(bv)
+    umode = "hadamard" if mode == "hadamard" else "per_group"
+    u = DPlan(dl, S.random_plan(rng, (16, 16, 16), umode))
+    v = DPlan(dl, S.random_plan(rng, (bv, 16, 16), mode))
+    m, n = 4096, bv * 256 * chunks
+    q = brq.make_quant(bits, group)
+    ws = dl.brq_workspace_bytes(u.h, v.h, m, n)
+    dl.brq_dryrun_reset()
+    st = dl.brq_rotate_quantize_pack(u.h, v.h, X, wt, m, n, n, ctypes.byref(q), CODES, SCALES,
+                                     WS, ws, None)
+    _ok(dl, st, f"fused bv={bv} {mode}")
+    assert dl.brq_dryrun_launches() == 2
