@@ -102,6 +102,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device-to-device copy of MIB MiB (3 times) before the "
+                         "steps, as the reference kernel for HBM byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path needs no "
@@ -132,6 +135,14 @@ def main(argv=None):
         brq.rotate_quantize_pack(U, V, bufs[i % N_BUFFERS], BITS, GROUP, codes=codes,
                                  scales=scales, ws=ws, stream=stream)
 
+    if a.copy_calibration:
+        nel = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -586,7 +586,7 @@ brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const in
     e = rt_malloc((void**)&p.signs, d * sizeof(float));
     if (e == hipSuccess) e = rt_copy_to_device(p.signs, sf.data(), d * sizeof(float));
   }
-  if (e == hipSuccess) e = fused_prepare(p, blocks);
+  if (e == hipSuccess) e = fused_prepare(p, blocks, signs);
   if (e != hipSuccess) {
     brq_status st = hip_fail(e, "plan device setup");
     brq_plan_destroy(h);

@@ -101,6 +101,8 @@ hipError_t launch_pass(const PassArgs& a, hipStream_t s);
 hipError_t rt_get_device(int* dev);
 hipError_t rt_malloc(void** p, size_t bytes);
 hipError_t rt_copy_to_device(void* dst, const void* src, size_t bytes);
+hipError_t rt_copy_to_host(void* dst, const void* src, size_t bytes);
+hipError_t rt_cu_count(int dev, int* cus);
 void rt_free(void* p);
 
 // Kernel timing (brq_profile_*): bracket a launch with events on its stream

@@ -40,6 +40,16 @@ hipError_t rt_copy_to_device(void* dst, const void* src, size_t bytes) {
   return hipSuccess;
 }
 
+hipError_t rt_copy_to_host(void* dst, const void* src, size_t bytes) {
+  std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+
+hipError_t rt_cu_count(int, int* cus) {
+  *cus = 256;
+  return hipSuccess;
+}
+
 void rt_free(void* p) { std::free(p); }
 
 // Number of float elements of the block array one stage may address.
@@ -169,6 +179,8 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   const int nb = a.nb, bv = a.bv;
   const int64_t ldsn = fa_lds_floats(nb, bv);
   const int elem = a.wt == BRQ_F32 ? 4 : 2;
+  const int NT = kFaWaves * 64;
+  if (16 * bv > 2 * NT) return violation("items %lld > %lld", 16 * bv, 2 * NT), hipErrorInvalidValue;
   std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
   std::vector<int> slot_in(ldsn), slot_out(ldsn);
   for (int64_t b = 0; b < nwg; ++b) {
@@ -189,16 +201,14 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
     for (int q = t.q0; q < t.q0 + kFaQC; ++q) {
       std::fill(slot_in.begin(), slot_in.end(), 0);
       std::fill(slot_out.begin(), slot_out.end(), 0);
-      for (int it = 0; it < 16 * bv * 2; ++it) {
-        const int r0 = it / (bv * 2), rem = it % (bv * 2), c0 = rem >> 1, hh = rem & 1;
-        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 8 * hh);
-        if (row >= a.m || !in_range(col, 8, a.n) || col + 8 > a.ldw || (col * elem) % 16)
+      for (int it = 0; it < 16 * bv; ++it) {
+        const int r0 = fa_div_bv(a, it), c0 = it - r0 * bv;
+        if (r0 != it / bv) return violation("division of %lld by bv %lld", it, bv), hipErrorInvalidValue;
+        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0);
+        if (row >= a.m || !in_range(col, kFaP, a.n) || col + kFaP > a.ldw || ((row * a.ldw + col) * elem) % 16)
           return violation("pass A input (%lld, %lld)", row, col), hipErrorInvalidValue;
-        if (a.su && row >= a.m) return violation("row sign %lld", row, 0), hipErrorInvalidValue;
-        if (!in_range(c0 * 256 + t.p0 + 8 * hh, 8, a.dv))
-          return violation("column sign %lld", c0 * 256 + t.p0 + 8 * hh, 0), hipErrorInvalidValue;
-        for (int e = 0; e < 8; ++e) {
-          const int s = fa_lds_in(nb, 8 * hh + e, r0, c0);
+        for (int e = 0; e < kFaP; ++e) {
+          const int s = fa_lds_in(nb, e, r0, c0);
           if (s < 0 || s >= ldsn) return violation("pass A LDS in %lld", s, ldsn), hipErrorInvalidValue;
           slot_in[s]++;
         }
@@ -225,12 +235,13 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
             }
         }
       for (int it = 0; it < 16 * bv * (kFaP / 4); ++it) {
-        const int r0 = it / (bv * 4), rem = it % (bv * 4), c0 = rem >> 2, qd = rem & 3;
-        const int s = fa_lds_out(bv, r0, c0, 4 * qd);
+        const int rc = it >> 1, h2 = it & 1;
+        const int r0 = fa_div_bv(a, rc), c0 = rc - r0 * bv;
+        const int s = fa_lds_out(bv, r0, c0, 4 * h2);
         if (!in_range(s, 4, ldsn) || s % 4) return violation("pass A store read %lld", s, 0), hipErrorInvalidValue;
         for (int i = 0; i < 4; ++i)
           if (slot_out[s + i] != 1) return violation("pass A output slot %lld written %lld times", s + i, slot_out[s + i]), hipErrorInvalidValue;
-        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * qd);
+        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * h2);
         if (row >= a.m || !in_range(col, 4, a.n) || (row * a.n + col) % 4)
           return violation("pass A store (%lld, %lld)", row, col), hipErrorInvalidValue;
         for (int i = 0; i < 4; ++i) cover[(size_t)(row * a.n + col + i)]++;
@@ -242,72 +253,94 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
-hipError_t launch_fused_b(const FusedBArgs& a, hipStream_t) {
+hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
   ++g_launches;
-  const int64_t nwg = fb_nwg(a);
+  const int64_t ntiles = fb_nwg(a);
+  if (grid < 1 || grid > ntiles) return violation("pass B grid %lld of %lld tiles", grid, ntiles), hipErrorInvalidValue;
   std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
   std::vector<int> slot(kFbXchFloats);
   const int bits = a.bits, g = a.group;
   const int fpg = g / 16, nw = fpg * 16 * bits / 32;
-  for (int64_t b = 0; b < nwg; ++b) {
-    const FbTile t = fb_tile(a, b);
-    if (t.r0 < 0 || t.r0 >= 16 || t.c0 < 0 || t.c0 >= a.bv || t.chunk < 0 || t.chunk >= a.nchunk)
-      return violation("pass B tile %lld of %lld", b, nwg), hipErrorInvalidValue;
-    for (int w = 0; w < kFbWaves; ++w)
-      for (int l = 0; l < 64; ++l) {
-        const int lr = l & 15, lg = l >> 4;
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = fb_row(t, lr, w), col = fb_col(a, t, 4 * lg + i, 0);
-          if (row >= a.m || !in_range(col, 16, a.n) || (row * a.n + col) % 4)
-            return violation("pass B load (%lld, %lld)", row, col), hipErrorInvalidValue;
-          for (int c2 = 0; c2 < 16; ++c2) cover[(size_t)(row * a.n + col + c2)]++;
-        }
-        if (!in_range((int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg, 4, a.u1_n) ||
-            !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg, 4, a.u2_n))
-          return violation("U_1/U_2 block read wave %lld lane %lld", w, l), hipErrorInvalidValue;
-        for (int c = 0; c < 16; ++c)
-          if (!in_range((int64_t)(t.c0 * 16 + c) * a.v1_gs + lr * 16 + 4 * lg, 4, a.v1_n) ||
-              !in_range((int64_t)(t.c0 * 16 + c) * a.v2_gs + lr * 16 + 4 * lg, 4, a.v2_n))
-            return violation("V_1/V_2 block read c %lld lane %lld", c, l), hipErrorInvalidValue;
+  std::vector<int> tiles_seen((size_t)ntiles, 0);
+  for (int64_t wg = 0; wg < grid; ++wg)
+    for (int64_t tile = wg; tile < ntiles; tile += grid) {  // the kernel's persistent loop
+      tiles_seen[(size_t)tile]++;
+      const FbTile t = fb_tile(a, tile);
+      if (t.r0 < 0 || t.r0 >= 16 || t.c0 < 0 || t.c0 >= a.bv || t.chunk < 0 || t.chunk >= a.nchunk)
+        return violation("pass B tile %lld of %lld", tile, ntiles), hipErrorInvalidValue;
+      // block staging into LDS
+      for (int k = 0; k < 2 * 16 * 64; ++k) {
+        const int which = k >> 10, rem = k & 1023, f = rem >> 6, qd = rem & 63;
+        const int64_t src = (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs) + 4 * qd;
+        if (!in_range(src, 4, which ? a.v2_n : a.v1_n)) return violation("V block staging %lld", src, which), hipErrorInvalidValue;
+        const int dst = (which ? kFbV2Off : kFbV1Off) + f * 256 + 4 * qd;
+        if (!in_range(dst, 4, kFbLdsFloats) || (which == 0 && dst + 4 > kFbXchFloats))
+          return violation("V block LDS slot %lld", dst, which), hipErrorInvalidValue;
       }
-    for (int h = 0; h < 2; ++h) {
-      std::fill(slot.begin(), slot.end(), 0);
       for (int w = 0; w < kFbWaves; ++w)
         for (int l = 0; l < 64; ++l) {
           const int lr = l & 15, lg = l >> 4;
-          if ((lg >> 1) != h) continue;
-          for (int c2 = 0; c2 < 16; ++c2)
-            for (int i = 0; i < 4; ++i) {
-              const int s = fb_xch(lr, 4 * lg + i - 8 * h, w, c2);
-              if (s < 0 || s >= kFbXchFloats) return violation("exchange write %lld", s, 0), hipErrorInvalidValue;
-              slot[s]++;
+          const int64_t row = fb_row(t, lr, w), col = fb_col(a, t, 4 * lg, 0);
+          for (int i = 0; i < 4; ++i)
+            for (int qd = 0; qd < 4; ++qd) {
+              const int64_t off = row * a.n + col + i * 16 + 4 * qd;
+              if (row >= a.m || !in_range(col + i * 16 + 4 * qd, 4, a.n) || off % 4)
+                return violation("pass B load (%lld, %lld)", row, col + i * 16 + 4 * qd), hipErrorInvalidValue;
+              for (int j = 0; j < 4; ++j) cover[(size_t)(off + j)]++;
             }
+          if (!in_range((int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg, 4, a.u1_n) ||
+              !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg, 4, a.u2_n))
+            return violation("U_1/U_2 block read wave %lld lane %lld", w, l), hipErrorInvalidValue;
+          for (int c = 0; c < 16; ++c) {
+            if (!in_range(kFbV1Off + c * 256 + lr * 16 + 4 * lg, 4, kFbXchFloats) ||
+                !in_range(kFbV2Off + c * 256 + lr * 16 + 4 * lg, 4, kFbLdsFloats))
+              return violation("V block LDS read %lld lane %lld", c, l), hipErrorInvalidValue;
+          }
         }
-      for (int s = 0; s < kFbXchFloats; ++s)
-        if (slot[s] != 1) return violation("exchange slot %lld written %lld times", s, slot[s]), hipErrorInvalidValue;
-      for (int w = 0; w < kFbWaves; ++w)
-        for (int l = 0; l < 64; ++l) {
-          const int lr = l & 15, lg = l >> 4;
-          for (int c1h = 0; c1h < 8; ++c1h) {
-            const int s = fb_xch(w, c1h, lr, 4 * lg);
-            if (!in_range(s, 4, kFbXchFloats) || s % 4) return violation("exchange read %lld", s, 0), hipErrorInvalidValue;
+      for (int h = 0; h < 2; ++h) {
+        std::fill(slot.begin(), slot.end(), 0);
+        for (int w = 0; w < kFbWaves; ++w)
+          for (int l = 0; l < 64; ++l) {
+            const int lr = l & 15, lg = l >> 4;
+            if ((lg >> 1) != h) continue;
             for (int i = 0; i < 4; ++i)
-              if (fb_xch(w, c1h, lr, 4 * lg + i) != s + i) return violation("exchange quad %lld", s, i), hipErrorInvalidValue;
+              for (int qd = 0; qd < 4; ++qd) {
+                const int c1h = 4 * lg + i - 8 * h;
+                const int s = fb_xch(lr, c1h, w, 4 * qd);
+                if (!in_range(s, 4, kFbXchFloats) || s % 4) return violation("exchange write %lld", s, 0), hipErrorInvalidValue;
+                for (int j = 0; j < 4; ++j) {
+                  if (fb_xch(lr, c1h, w, 4 * qd + j) != s + j) return violation("exchange write quad %lld", s, j), hipErrorInvalidValue;
+                  slot[s + j]++;
+                }
+              }
           }
-          if (lg != 0) continue;
-          const int64_t row = fb_row(t, w, lr);
-          for (int gi = 0; gi < 128 / g; ++gi) {
-            const int64_t col0 = fb_col(a, t, 8 * h + gi * fpg, 0);
-            if (col0 % g) return violation("group start %lld", col0, g), hipErrorInvalidValue;
-            const int64_t off = row * a.codes_ld + col0 * bits / 8;
-            if (!in_range(off, 4 * nw, a.m * a.codes_ld) || off % 4)
-              return violation("codes [%lld, +%lld)", off, 4 * nw), hipErrorInvalidValue;
-            if (!in_range(row * a.scales_ld + col0 / g, 1, a.m * a.scales_ld))
-              return violation("scale %lld", row * a.scales_ld + col0 / g, 0), hipErrorInvalidValue;
+        for (int s = 0; s < kFbXchFloats; ++s)
+          if (slot[s] != 1) return violation("exchange slot %lld written %lld times", s, slot[s]), hipErrorInvalidValue;
+        for (int w = 0; w < kFbWaves; ++w)
+          for (int l = 0; l < 64; ++l) {
+            const int lr = l & 15, lg = l >> 4;
+            for (int c1h = 0; c1h < 8; ++c1h) {
+              const int s = fb_xch(w, c1h, lr, 4 * lg);
+              if (!in_range(s, 4, kFbXchFloats) || s % 4) return violation("exchange read %lld", s, 0), hipErrorInvalidValue;
+              for (int i = 0; i < 4; ++i)
+                if (fb_xch(w, c1h, lr, 4 * lg + i) != s + i) return violation("exchange quad %lld", s, i), hipErrorInvalidValue;
+            }
+            if (lg != 0) continue;
+            const int64_t row = fb_row(t, w, lr);
+            for (int gi = 0; gi < 128 / g; ++gi) {
+              const int64_t col0 = fb_col(a, t, 8 * h + gi * fpg, 0);
+              if (col0 % g) return violation("group start %lld", col0, g), hipErrorInvalidValue;
+              const int64_t off = row * a.codes_ld + col0 * bits / 8;
+              if (!in_range(off, 4 * nw, a.m * a.codes_ld) || off % 4)
+                return violation("codes [%lld, +%lld)", off, 4 * nw), hipErrorInvalidValue;
+              if (!in_range(row * a.scales_ld + col0 / g, 1, a.m * a.scales_ld))
+                return violation("scale %lld", row * a.scales_ld + col0 / g, 0), hipErrorInvalidValue;
+            }
           }
-        }
+      }
     }
-  }
+  for (int64_t i = 0; i < ntiles; ++i)
+    if (tiles_seen[(size_t)i] != 1) return violation("pass B tile %lld visited %lld times", i, tiles_seen[(size_t)i]), hipErrorInvalidValue;
   for (int64_t i = 0; i < a.m * a.n; ++i)
     if (cover[(size_t)i] != 1) return violation("pass B element %lld read %lld times", i, cover[(size_t)i]), hipErrorInvalidValue;
   return hipSuccess;

@@ -18,12 +18,17 @@
 
 namespace brq {
 
-constexpr int kFaWaves = 16;           // pass A: waves per workgroup (one p each)
-constexpr int kFaP = 16;               // pass A: p values per workgroup
-constexpr int kFaQC = 8;               // pass A: q values per workgroup (looped)
+constexpr int kFaWaves = 8;            // pass A: waves per workgroup (one p each)
+constexpr int kFaP = kFaWaves;         // pass A: p values per workgroup
+constexpr int kFaQC = 16;              // pass A: q values per workgroup (looped)
 constexpr int kFbWaves = 16;           // pass B: waves per workgroup
-// pass B exchange buffer: [r1 16][c1h 8][r2 16][c2 16] floats (swizzled)
+// pass B LDS: the exchange buffer [r1 16][c1h 8][r2 16][c2 16] (swizzled),
+// whose first 16 KB hold the tile's 16 V_1 blocks during phase 1, then the
+// tile's 16 V_2 blocks.
 constexpr int kFbXchFloats = 16 * 8 * 16 * 16;
+constexpr int kFbV1Off = 0;
+constexpr int kFbV2Off = kFbXchFloats;
+constexpr int kFbLdsFloats = kFbV2Off + 16 * 256;
 
 struct FusedAArgs {
   const void* w;      // input [m][n], type wt, leading dimension ldw
@@ -35,13 +40,12 @@ struct FusedAArgs {
   int nb;             // 16-blocks spanned by bv (padded K = N = 16*nb)
   int nchunk;         // n / d_V (block-diagonal right side)
   int dv;             // d_V = bv * 256
-  const float* u0;    // U_0 blocks [256][16][16] (or one shared block)
+  const float* u0;    // U_0 blocks [256][16][16] (or one shared block), signs folded in
   int64_t u0_gs;      // float stride between groups (0 = shared)
-  const float* v0;    // V_0 blocks padded [256][16nb][16nb] (or one)
+  const float* v0;    // V_0 blocks padded [256][16nb][16nb] (or one), signs folded in
   int64_t v0_gs;
-  const float* su;    // row signs [m] or null
-  const float* sv;    // column signs [d_V] or null
   int nqc;            // q chunks: 256 / kFaQC
+  uint32_t bv_magic;  // floor(2^32 / bv) + 1: i / bv = (i * bv_magic) >> 32 for the i used
   int64_t u0_n, v0_n; // float extents of the block arrays (host checks)
 };
 
@@ -88,18 +92,26 @@ __host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
   return (int64_t)(256 / kFaP) * a.nqc * a.nchunk;
 }
 
-// LDS input slot of (p_local, r0, c0): [p 16][r0 16][16*nb + 4]
+// i / bv without a division instruction (exact for the ranges the host checks).
+__host__ __device__ inline int fa_div_bv(const FusedAArgs& a, int i) {
+  return (int)(((uint64_t)(uint32_t)i * a.bv_magic) >> 32);
+}
+
+// LDS input slot of (p_local, r0, c0): [p kFaP][r0 16][16*nb + 4]
 __host__ __device__ inline int fa_kp(int nb) { return 16 * nb + 4; }
 __host__ __device__ inline int fa_lds_in(int nb, int pl, int r0, int c0) {
   return (pl * 16 + r0) * fa_kp(nb) + c0;
 }
-// LDS output slot of (r0, c0, p_local): [r0 16][c0 bv][p 16]
+// LDS output slot of (r0, c0, p_local): [r0 16][c0 bv][p kFaP + 4].  The pad
+// spreads the accumulator writes (lanes over r0 and c0) over more banks and
+// keeps each p run 16-byte aligned for the float4 reads of the store.
+constexpr int kFaOutStride = kFaP + 4;
 __host__ __device__ inline int fa_lds_out(int bv, int r0, int c0, int pl) {
-  return (r0 * bv + c0) * kFaP + pl;
+  return (r0 * bv + c0) * kFaOutStride + pl;
 }
 __host__ __device__ inline int fa_lds_floats(int nb, int bv) {
-  const int in = 16 * 16 * fa_kp(nb);
-  const int out = 16 * bv * kFaP;
+  const int in = kFaP * 16 * fa_kp(nb);
+  const int out = 16 * bv * kFaOutStride;
   return in > out ? in : out;
 }
 // Global element (row, col) of (r0, q) x (chunk, c0, p).
@@ -143,7 +155,7 @@ __host__ __device__ inline int64_t fb_col(const FusedBArgs& a, const FbTile& t, 
 
 // ---- entry points -------------------------------------------------------------
 
-hipError_t fused_prepare(Plan& p, const float* host_blocks);
+hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_signs);
 void fused_release(Plan& p);
 
 bool fused_rotate_supported(const Plan* U, const Plan* V, int xt, int yt, int64_t rows,
@@ -158,7 +170,9 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
                      size_t ws_bytes, hipStream_t s);
 
 // Kernel launchers (fused_kernels.hip; the dry-run build walks their indices).
+// Pass B is persistent: `grid` workgroups (<= its tile count) loop over tiles
+// b, b + grid, ...
 hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t s);
-hipError_t launch_fused_b(const FusedBArgs& a, hipStream_t s);
+hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t s);
 
 }  // namespace brq

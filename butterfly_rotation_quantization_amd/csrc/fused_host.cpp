@@ -28,29 +28,39 @@ void hadamard_block(int b, float* out) {
 
 }  // namespace
 
-hipError_t fused_prepare(Plan& p, const float* host_blocks) {
+// Stage-0 blocks for the fast path: zero-padded to 16*nb, with the plan's
+// signs folded in.  M = ... B_0 D, and the members of stage-0 group c are
+// i = k*S_0 + c (S_0 = 256), so (B_0 D) restricted to group c is
+// B_{0,c} diag(s[k*256 + c]): column k of the block times that sign.
+hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_signs) {
   if (!fused_shape(p)) return hipSuccess;
   const int b0 = p.radix[0];
   const int nb = (b0 + 15) / 16;
   const int np = 16 * nb;
-  const bool shared = p.mode != BRQ_PER_GROUP;
-  const int ng0 = shared ? 1 : p.d / b0;
-  std::vector<float> pad((size_t)ng0 * np * np, 0.f);
+  const int S0 = p.stride[0];  // 256
+  const bool shared_src = p.mode != BRQ_PER_GROUP;
+  const bool per_group = !shared_src || host_signs;
+  const int ng0 = per_group ? S0 : 1;
   std::vector<float> src;
   if (p.mode == BRQ_HADAMARD) {
     src.resize((size_t)b0 * b0);
     hadamard_block(b0, src.data());
   }
   const float* g0 = p.mode == BRQ_HADAMARD ? src.data() : host_blocks + p.blk_off[0];
-  for (int g = 0; g < ng0; ++g)
+  std::vector<float> pad((size_t)ng0 * np * np, 0.f);
+  for (int g = 0; g < ng0; ++g) {
+    const float* blk = g0 + (shared_src ? 0 : (size_t)g * b0 * b0);
     for (int j = 0; j < b0; ++j)
-      for (int k = 0; k < b0; ++k)
-        pad[((size_t)g * np + j) * np + k] = g0[((size_t)g * b0 + j) * b0 + k];
+      for (int k = 0; k < b0; ++k) {
+        const float sg = host_signs ? (float)host_signs[(size_t)k * S0 + g] : 1.0f;
+        pad[((size_t)g * np + j) * np + k] = blk[j * b0 + k] * sg;
+      }
+  }
   hipError_t e = rt_malloc((void**)&p.fz0, pad.size() * sizeof(float));
   if (e == hipSuccess) e = rt_copy_to_device(p.fz0, pad.data(), pad.size() * sizeof(float));
   if (e != hipSuccess) return e;
   p.fz_nb = nb;
-  p.fz_gs0 = shared ? 0 : (int64_t)np * np;
+  p.fz_gs0 = per_group ? (int64_t)np * np : 0;
   if (p.mode == BRQ_HADAMARD) {
     std::vector<float> h16(256);
     hadamard_block(16, h16.data());
@@ -63,7 +73,7 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks) {
   } else {
     p.fz1 = p.blk + p.blk_off[1];
     p.fz2 = p.blk + p.blk_off[2];
-    p.fz_gs1 = p.fz_gs2 = shared ? 0 : 256;
+    p.fz_gs1 = p.fz_gs2 = shared_src ? 0 : 256;
   }
   p.fz_ok = 1;
   return hipSuccess;
@@ -71,11 +81,26 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks) {
 
 namespace {
 
+// Persistent pass B: one workgroup per compute unit (its LDS use allows no
+// more), capped by the tile count.
+int fused_b_grid(const FusedBArgs& b) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (rt_get_device(&dev) != hipSuccess || rt_cu_count(dev, &cus) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  const int64_t nt = fb_nwg(b);
+  return (int)(nt < cus ? nt : cus);
+}
+
 // Host check of what the two kernels' index arithmetic relies on.
 const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (a.bv < 2 || a.bv > 64 || a.nb != (a.bv + 15) / 16) return "V_0 radix";
   if (a.m != 4096 || a.dv != a.bv * 256 || (int64_t)a.nchunk * a.dv != a.n) return "shape";
   if (a.nqc * kFaQC != 256 || fa_nwg(a) % 8) return "pass A grid";
+  for (int i = 0; i < 16 * a.bv; ++i)  // the multiply-shift quotient is exact where used
+    if (fa_div_bv(a, i) != i / a.bv) return "division multiplier";
   if (!a.w || !a.ws || !a.u0 || !a.v0) return "pass A pointers";
   if (a.u0_gs && a.u0_n < 256 * a.u0_gs) return "U_0 extent";
   if (a.v0_gs && a.v0_n < 256 * a.v0_gs) return "V_0 extent";
@@ -147,17 +172,12 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.nb = V->fz_nb;
   a.dv = V->d;
   a.nchunk = (int)(n / V->d);
-  a.u0 = U->mode == BRQ_HADAMARD ? nullptr : U->blk + U->blk_off[0];
-  a.u0_gs = U->mode == BRQ_PER_GROUP ? 256 : 0;
-  if (U->mode == BRQ_HADAMARD) {
-    a.u0 = U->fz0;  // H16/4 padded to 16 x 16 is the block itself
-    a.u0_gs = 0;
-  }
+  a.u0 = U->fz0;  // radix 16: the padded layout is the 16 x 16 block itself
+  a.u0_gs = U->fz_gs0;
   a.v0 = V->fz0;
   a.v0_gs = V->fz_gs0;
-  a.su = U->signs;
-  a.sv = V->signs;
   a.nqc = 256 / kFaQC;
+  a.bv_magic = (uint32_t)((1ull << 32) / (uint64_t)a.bv + 1);
 
   FusedBArgs b;
   std::memset(&b, 0, sizeof b);
@@ -189,8 +209,8 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   b.scales_ld = n / q->group;
   const int64_t u16 = U->mode == BRQ_PER_GROUP ? (int64_t)(U->d / 16) * 256 : 256;
   const int64_t v16 = V->mode == BRQ_PER_GROUP ? (int64_t)(V->d / 16) * 256 : 256;
-  a.u0_n = u16;
-  a.v0_n = (V->mode == BRQ_PER_GROUP ? (int64_t)(V->d / V->radix[0]) : 1) * 256 * a.nb * a.nb;
+  a.u0_n = (U->fz_gs0 ? 256 : 1) * 256;
+  a.v0_n = (V->fz_gs0 ? 256 : 1) * 256 * a.nb * a.nb;
   b.u1_n = b.u2_n = u16;
   b.v1_n = b.v2_n = v16;
   if (check_fused(a, b)) return BRQ_ERR_UNSUPPORTED;
@@ -203,7 +223,7 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   if (e != hipSuccess) return BRQ_ERR_HIP;
   snprintf(name, sizeof name, "fusedB U(16,16) V(16,16) quant b%d g%d", q->bits, q->group);
   tok = prof_begin(name, s);
-  e = launch_fused_b(b, s);
+  e = launch_fused_b(b, fused_b_grid(b), s);
   prof_end(tok, s);
   return e == hipSuccess ? BRQ_OK : BRQ_ERR_HIP;
 }

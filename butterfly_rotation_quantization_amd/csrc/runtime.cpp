@@ -13,6 +13,14 @@ hipError_t rt_copy_to_device(void* dst, const void* src, size_t bytes) {
   return hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
 }
 
+hipError_t rt_copy_to_host(void* dst, const void* src, size_t bytes) {
+  return hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+}
+
+hipError_t rt_cu_count(int dev, int* cus) {
+  return hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
 void rt_free(void* p) {
   if (p) (void)hipFree(p);
 }
