@@ -50,13 +50,43 @@ def algorithmic_bytes():
 def kernel_work(name: str):
     """(bound, algorithmic amount per launch, unit, peak) of a kernel of this
     workload, from the stages its name lists: a dense b x b stage is b FMA
-    (2b flop) per element, over all M*N elements."""
+    (2b flop) per element, over all M*N elements.  The fast-path kernels
+    contract on fp32 MFMA; the generic tile pass on the fp32 vector ALU."""
     import re
     flop = 0
     for grp in re.findall(r"\(([0-9,]+)\)", name):
         for b in grp.split(","):
             flop += 2 * int(b) * M * N
+    if name.startswith("fused"):
+        return "mfma", flop / 1e12, "TFLOP/s", FP32_MFMA_PEAK_TFLOPS
     return "alu", flop / 1e12, "TFLOP/s", FP32_VECTOR_PEAK_TFLOPS
+
+
+def measured_traffic(kernel_name: str):
+    """HBM bytes per launch of `kernel_name` from the committed counter
+    summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    same counter reads for a plain copy of known size), or None when the
+    summary is missing or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_fused_harp_mlp_4096x11008.md")
+    src = os.path.join(ROOT, "butterfly_rotation_quantization_amd", "csrc", "fused_kernels.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().strip("`").split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha1") != sha:
+        return None
+    key = "fused_b" if kernel_name.startswith("fusedB") else "fused_a"
+    try:
+        fetch = float(vals[f"{key}_fetch_kib"]) * float(vals["copy_fetch_scale"])
+        write = float(vals[f"{key}_write_kib"]) * float(vals["copy_write_scale"])
+    except KeyError:
+        return None
+    return round((fetch + write) * 1024)
 
 
 def cpu_baseline(cfg, rows_sample: int):
@@ -101,7 +131,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=M)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB (3 times) before the "
                          "steps, as the reference kernel for HBM byte counters")
@@ -194,7 +224,7 @@ def main(argv=None):
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 5),
-            "traffic": None,
+            "traffic": measured_traffic(dom_name),
         },
     }
     if not a.no_cpu_baseline:
