@@ -32,6 +32,7 @@ struct Plan {
   int fz_ok = 0;
   int fz_nb = 0;
   float* fz0 = nullptr;
+  float* fz0f = nullptr;             // the same blocks in MFMA fragment order (fused.h)
   int64_t fz_gs0 = 0;
   const float* fz1 = nullptr;
   int64_t fz_gs1 = 0;

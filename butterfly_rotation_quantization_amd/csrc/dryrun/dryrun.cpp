@@ -2,6 +2,7 @@
 // replaced by a walk over each index the kernel would touch, checked against
 // the extents of its buffers.  Built as libbrq_dryrun.so for CPU tests; it
 // never touches a GPU.  Device pointers passed to it are never dereferenced.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -177,75 +178,126 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   ++g_launches;
   const int64_t nwg = fa_nwg(a);
   const int nb = a.nb, bv = a.bv;
-  const int64_t ldsn = fa_lds_floats(nb, bv);
-  const int elem = a.wt == BRQ_F32 ? 4 : 2;
-  const int NT = kFaWaves * 64;
-  if (16 * bv > 2 * NT) return violation("items %lld > %lld", 16 * bv, 2 * NT), hipErrorInvalidValue;
+  const FaGeom g = fa_geom(a.wt, nb, bv);
+  const int st = fa_steps(bv), ki = fa_ki(a.wt, st), kq = fa_kq_nt(a.wt, st);
+  const int P = g.P, ppw = g.ppw, esz = g.esz, epi = 16 / esz, ipr = g.ipr;
+  if (64 % ipr || 256 % P || 8 * ki < 16 * fa_ncb(64 / ipr, st) || 8 * kq * (256 / P) < 256)
+    return violation("pass A loop counts %lld / %lld", ki, kq), hipErrorInvalidValue;
+  if (fa_lds_bytes(g) > 160 * 1024 || g.slab_bytes % 16)
+    return violation("pass A LDS %lld bytes", fa_lds_bytes(g), 0), hipErrorInvalidValue;
+  // which input element (r0, c0, p_local) each slab byte holds, and which
+  // output (r0', c0', p_local) each float of the output area holds
+  auto code = [&](int r0, int c0, int pl) { return ((int64_t)r0 * 64 + c0) * 256 + pl; };
+  std::vector<int64_t> slab(g.slab_bytes), outa(g.out_floats);
   std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
-  std::vector<int> slot_in(ldsn), slot_out(ldsn);
   for (int64_t b = 0; b < nwg; ++b) {
     const FaTile t = fa_tile(a, b, nwg);
-    if (t.p0 < 0 || t.p0 + kFaP > 256 || t.q0 < 0 || t.q0 + kFaQC > 256 || t.chunk < 0 ||
+    if (t.p0 < 0 || t.p0 + P > 256 || t.p0 % P || t.q0 < 0 || t.q0 + kFaQC > 256 || t.chunk < 0 ||
         t.chunk >= a.nchunk)
       return violation("pass A tile %lld of %lld", b, nwg), hipErrorInvalidValue;
-    for (int w = 0; w < kFaWaves; ++w) {
-      const int p = t.p0 + w;
-      for (int l = 0; l < 64; ++l) {
-        const int lr = l & 15, lg = l >> 4;
-        for (int kb = 0; kb < nb; ++kb)
+    for (int w = 0; w < kFaWaves; ++w)
+      for (int j = 0; j < ppw; ++j)
+        for (int l = 0; l < 64; ++l)
           for (int nt = 0; nt < nb; ++nt)
-            if (!in_range(p * a.v0_gs + (16 * nt + lr) * (16 * nb) + 16 * kb + 4 * lg, 4, a.v0_n))
-              return violation("V_0 block read (p %lld, lane %lld)", p, l), hipErrorInvalidValue;
-      }
-    }
+            for (int sq = 0; 4 * sq < fa_steps(bv); ++sq) {
+              const int64_t i = (int64_t)(t.p0 + ppw * w + j) * a.v0_gs + fa_vfrag(nb, nt, l & 15, l >> 4, 4 * sq);
+              if (!in_range(i, 4, a.v0_n) || i % 4)
+                return violation("V_0 block read (p %lld, lane %lld)", t.p0 + ppw * w + j, l), hipErrorInvalidValue;
+            }
     for (int q = t.q0; q < t.q0 + kFaQC; ++q) {
-      std::fill(slot_in.begin(), slot_in.end(), 0);
-      std::fill(slot_out.begin(), slot_out.end(), 0);
-      for (int it = 0; it < 16 * bv; ++it) {
-        const int r0 = fa_div_bv(a, it), c0 = it - r0 * bv;
-        if (r0 != it / bv) return violation("division of %lld by bv %lld", it, bv), hipErrorInvalidValue;
-        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0);
-        if (row >= a.m || !in_range(col, kFaP, a.n) || col + kFaP > a.ldw || ((row * a.ldw + col) * elem) % 16)
-          return violation("pass A input (%lld, %lld)", row, col), hipErrorInvalidValue;
-        for (int e = 0; e < kFaP; ++e) {
-          const int s = fa_lds_in(nb, e, r0, c0);
-          if (s < 0 || s >= ldsn) return violation("pass A LDS in %lld", s, ldsn), hipErrorInvalidValue;
-          slot_in[s]++;
+      std::fill(slab.begin(), slab.end(), -1);
+      std::fill(outa.begin(), outa.end(), -1);
+      std::vector<uint8_t> loaded(g.items, 0);
+      for (int w = 0; w < kFaWaves; ++w)
+        for (int l = 0; l < 64; ++l) {
+          const int o = l % ipr;
+          for (int k = 0; k < ki; ++k) {
+            const FaSlot x = fa_slot(ipr, w, k, l, bv, 0);
+            const int r0 = x.r0, c0 = x.c0;
+            if (c0 < 0 || c0 >= bv) return violation("pass A load column %lld", c0, 0), hipErrorInvalidValue;
+            loaded[(size_t)((r0 * bv + c0) * ipr + o)] = 1;
+            const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + o * epi);
+            if (row >= a.m || !in_range(col, epi, a.n) || col + epi > a.ldw || ((row * a.ldw + col) * esz) % 16)
+              return violation("pass A input (%lld, %lld)", row, col), hipErrorInvalidValue;
+            // the kernel's 32-bit lane offset: (r0 * 256 * ldw + o * epi + c0 * 256) * esz
+            if ((r0 * 256 * a.ldw + o * epi + c0 * 256) * esz >= (int64_t(1) << 32))
+              return violation("pass A 32-bit input offset (%lld, %lld)", r0, c0), hipErrorInvalidValue;
+            const int off = fa_slab_item(g, r0, c0, o);
+            if (!in_range(off, 16, g.slab_bytes) || off % 8)
+              return violation("pass A slab write at byte %lld", off, 0), hipErrorInvalidValue;
+            for (int e = 0; e < epi; ++e) {
+              const int64_t c = code(r0, c0, o * epi + e);
+              for (int bb = 0; bb < esz; ++bb) {
+                int64_t& sl = slab[(size_t)(off + e * esz + bb)];
+                if (sl != -1 && sl != c) return violation("pass A slab byte %lld written twice", off + e * esz + bb, 0), hipErrorInvalidValue;
+                sl = c;
+              }
+            }
+          }
         }
-      }
+      for (int it = 0; it < g.items; ++it)
+        if (!loaded[it]) return violation("pass A item %lld not loaded", it, 0), hipErrorInvalidValue;
       for (int w = 0; w < kFaWaves; ++w)
         for (int l = 0; l < 64; ++l) {
           const int lr = l & 15, lg = l >> 4;
-          for (int kb = 0; kb < nb; ++kb) {
-            const int s = fa_lds_in(nb, w, lr, 16 * kb + 4 * lg);
-            if (!in_range(s, 4, ldsn) || s % 4) return violation("pass A A-read %lld", s, ldsn), hipErrorInvalidValue;
-            for (int i = 0; i < 4; ++i)
-              if (16 * kb + 4 * lg + i < bv && slot_in[s + i] != 1)
-                return violation("pass A A-read of an unwritten slot %lld", s + i, 0), hipErrorInvalidValue;
-          }
           if (!in_range((int64_t)q * a.u0_gs + lr * 16 + 4 * lg, 4, a.u0_n))
             return violation("U_0 block read q %lld lane %lld", q, l), hipErrorInvalidValue;
+          for (int st = 0; st < fa_steps(bv); ++st) {
+            const int c0 = std::min(4 * st + lg, bv - 1);
+            const int off = fa_slab_read(g, lr, c0, w);
+            if (!in_range(off, ppw * esz, g.slab_bytes) || off % (ppw * esz))
+              return violation("pass A slab read at byte %lld", off, 0), hipErrorInvalidValue;
+            for (int e = 0; e < ppw; ++e)
+              for (int bb = 0; bb < esz; ++bb)
+                if (slab[(size_t)(off + e * esz + bb)] != code(lr, c0, ppw * w + e))
+                  return violation("pass A slab read of the wrong element at byte %lld", off + e * esz + bb, 0), hipErrorInvalidValue;
+          }
           for (int nt = 0; nt < nb; ++nt)
             for (int i = 0; i < 4; ++i) {
               const int c0 = 16 * nt + 4 * lg + i;
               if (c0 >= bv) continue;
-              const int s = fa_lds_out(bv, lr, c0, w);
-              if (s < 0 || s >= ldsn) return violation("pass A LDS out %lld", s, ldsn), hipErrorInvalidValue;
-              slot_out[s]++;
+              const int off = fa_out(g, lr, c0, ppw * w);
+              if (!in_range(off, ppw, g.out_floats) || (off * 4) % (ppw * 4))
+                return violation("pass A output-area write %lld", off, 0), hipErrorInvalidValue;
+              for (int e = 0; e < ppw; ++e) {
+                int64_t& s = outa[(size_t)(off + e)];
+                if (s != -1) return violation("pass A output float %lld written twice", off + e, 0), hipErrorInvalidValue;
+                s = code(lr, c0, ppw * w + e);
+              }
             }
         }
-      for (int it = 0; it < 16 * bv * (kFaP / 4); ++it) {
-        const int rc = it >> 1, h2 = it & 1;
-        const int r0 = fa_div_bv(a, rc), c0 = rc - r0 * bv;
-        const int s = fa_lds_out(bv, r0, c0, 4 * h2);
-        if (!in_range(s, 4, ldsn) || s % 4) return violation("pass A store read %lld", s, 0), hipErrorInvalidValue;
-        for (int i = 0; i < 4; ++i)
-          if (slot_out[s + i] != 1) return violation("pass A output slot %lld written %lld times", s + i, slot_out[s + i]), hipErrorInvalidValue;
-        const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * h2);
-        if (row >= a.m || !in_range(col, 4, a.n) || (row * a.n + col) % 4)
-          return violation("pass A store (%lld, %lld)", row, col), hipErrorInvalidValue;
-        for (int i = 0; i < 4; ++i) cover[(size_t)(row * a.n + col + i)]++;
-      }
+      std::vector<uint8_t> stored((size_t)16 * bv * (P / 4), 0);
+      for (int w = 0; w < kFaWaves; ++w)
+        for (int l = 0; l < 64; ++l) {
+          const int pq = l % (P / 4);
+          for (int k = 0; k < kq * nb; ++k) {
+            const int nt = k / kq;
+            const FaSlot x = fa_slot(P / 4, w, k % kq, l, bv, 16 * nt);
+            const int r0 = x.r0, c0 = x.c0;
+            if (c0 < 16 * nt || c0 >= 16 * nt + 16)
+              return violation("pass A store column %lld outside tile %lld", c0, nt), hipErrorInvalidValue;
+            {
+              if (r0 >= 16 || c0 < 0 || c0 >= bv) return violation("pass A store row %lld col %lld", r0, c0), hipErrorInvalidValue;
+              const int off = fa_out(g, r0, c0, 4 * pq);
+              if (!in_range(off, 4, g.out_floats) || off % 4)
+                return violation("pass A output-area read %lld", off, 0), hipErrorInvalidValue;
+              for (int e = 0; e < 4; ++e)
+                if (outa[(size_t)(off + e)] != code(r0, c0, 4 * pq + e))
+                  return violation("pass A output-area read of the wrong value at %lld", off + e, 0), hipErrorInvalidValue;
+              const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * pq);
+              if (row >= a.m || !in_range(col, 4, a.n) || (row * a.n + col) % 4)
+                return violation("pass A store (%lld, %lld)", row, col), hipErrorInvalidValue;
+              if ((r0 * 256 * a.n + c0 * 256 + 4 * pq) * 4 >= (int64_t(1) << 32))
+                return violation("pass A 32-bit output offset (%lld, %lld)", r0, c0), hipErrorInvalidValue;
+              uint8_t& sd = stored[(size_t)((r0 * bv + c0) * (P / 4) + pq)];
+              if (!sd)  // a repeated last column stores the same value again
+                for (int e = 0; e < 4; ++e) cover[(size_t)(row * a.n + col + e)]++;
+              sd = 1;
+            }
+          }
+        }
+      for (size_t i = 0; i < stored.size(); ++i)
+        if (!stored[i]) return violation("pass A output float4 %lld not stored", (int64_t)i, 0), hipErrorInvalidValue;
     }
   }
   for (int64_t i = 0; i < a.m * a.n; ++i)

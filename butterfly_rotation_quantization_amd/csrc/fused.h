@@ -18,9 +18,8 @@
 
 namespace brq {
 
-constexpr int kFaWaves = 8;            // pass A: waves per workgroup (one p each)
-constexpr int kFaP = kFaWaves;         // pass A: p values per workgroup
-constexpr int kFaQC = 16;              // pass A: q values per workgroup (looped)
+constexpr int kFaWaves = 8;            // pass A: waves per workgroup
+constexpr int kFaQC = 8;               // pass A: q values per workgroup (looped)
 constexpr int kFbWaves = 16;           // pass B: waves per workgroup
 // pass B LDS: the exchange buffer [r1 16][c1h 8][r2 16][c2 16] (swizzled),
 // whose first 16 KB hold the tile's 16 V_1 blocks during phase 1, then the
@@ -37,14 +36,13 @@ struct FusedAArgs {
   float* ws;          // float32 intermediate [m][n], leading dimension n
   int64_t m, n;
   int bv;             // radix of V_0 (columns)
-  int nb;             // 16-blocks spanned by bv (padded K = N = 16*nb)
+  int nb;             // 16-blocks spanned by bv
   int nchunk;         // n / d_V (block-diagonal right side)
   int dv;             // d_V = bv * 256
   const float* u0;    // U_0 blocks [256][16][16] (or one shared block), signs folded in
   int64_t u0_gs;      // float stride between groups (0 = shared)
-  const float* v0;    // V_0 blocks padded [256][16nb][16nb] (or one), signs folded in
+  const float* v0f;   // V_0 blocks in fragment order [256][nb][16][4][4nb] (or one), signs folded in
   int64_t v0_gs;
-  int nqc;            // q chunks: 256 / kFaQC
   uint32_t bv_magic;  // floor(2^32 / bv) + 1: i / bv = (i * bv_magic) >> 32 for the i used
   int64_t u0_n, v0_n; // float extents of the block arrays (host checks)
 };
@@ -69,6 +67,91 @@ struct FusedBArgs {
 };
 
 // ---- pass A geometry --------------------------------------------------------
+//
+// A workgroup owns P = 8 * ppw consecutive p (ppw per wave) of one column
+// chunk and kFaQC consecutive q.  For each q it stages the input slab
+// X[r0 < 16][c0 < bv][P] through LDS (runs of P input elements, at least 64
+// bytes), each wave contracts c0 with the V_0 blocks of its own ppw p held in
+// registers, then r0 with the U_0 block of q, and the results leave through a
+// second LDS area as runs of P floats.
+//
+// V_0 as MFMA steps: step s contracts c0 = 4s + lg (lane group lg), so
+// ceil(bv / 4) steps cover the radix and the block fragment of step s and
+// output tile nt is V[16 nt + lr][4 s + lg].
+
+__host__ __device__ constexpr int fa_esz(int wt) { return wt == BRQ_F32 ? 4 : 2; }
+// p per wave: 4, or 2 where the blocks (nb = 4) or the float32 slab would not fit.
+__host__ __device__ constexpr int fa_ppw(int wt, int nb) { return (wt == BRQ_F32 || nb == 4) ? 2 : 4; }
+__host__ __device__ constexpr int fa_p(int wt, int nb) { return 8 * fa_ppw(wt, nb); }
+// 16-byte input items per run of P elements
+__host__ __device__ constexpr int fa_ipr(int wt, int nb) { return fa_p(wt, nb) * fa_esz(wt) / 16; }
+
+// MFMA steps of V_0 (4 columns c0 each) and 16-blocks spanned by the radix.
+__host__ __device__ constexpr int fa_steps(int bv) { return (bv + 3) / 4; }
+__host__ __device__ constexpr int fa_nb_of_steps(int st) { return (st + 3) / 4; }
+// Slab loads and output stores take one row r0 and 64 / lpr consecutive
+// columns c0 per wave instruction (lpr lanes per run of P elements: ipr for
+// loads, P / 4 for stores): lane l holds part l % lpr of column
+// cb * (64 / lpr) + l / lpr.  Instruction k of wave w is slot j = w + 8 k:
+// row (j % 16), column block cb = j / 16.  Columns past the radix repeat the
+// last one, so every wave issues the same fixed number of instructions.
+__host__ __device__ constexpr int fa_ncb(int runs_per_inst, int st) {
+  return (4 * st + runs_per_inst - 1) / runs_per_inst;
+}
+__host__ __device__ constexpr int fa_ki(int wt, int st) {
+  return 2 * fa_ncb(64 / fa_ipr(wt, fa_nb_of_steps(st)), st);
+}
+// Output stores of one 16-column tile nt: 16 rows x 16 columns of P / 4
+// float4s, lpr = P / 4 lanes per run, as kq_nt instructions per wave.
+__host__ __device__ constexpr int fa_kq_nt(int wt, int st) { return fa_p(wt, fa_nb_of_steps(st)) / 8; }
+struct FaSlot {
+  int r0, c0;
+};
+// c_first: first column of the range (0 for slab loads, 16 nt for the
+// stores of output tile nt).
+__host__ __device__ inline FaSlot fa_slot(int lpr, int w, int k, int lane, int bv, int c_first) {
+  const int j = w + 8 * k;
+  FaSlot x;
+  x.r0 = j % 16;
+  const int c0 = c_first + (j / 16) * (64 / lpr) + lane / lpr;
+  x.c0 = c0 < bv ? c0 : bv - 1;
+  return x;
+}
+
+struct FaGeom {
+  int P, ppw, esz, ipr;
+  int rsb;         // slab: bytes between runs (c0), P*esz + 8
+  int rowb;        // slab: bytes between r0 rows; rowb / 8 odd
+  int rowo;        // output area: floats between r0 rows; rowo / 4 odd
+  int slab_bytes;  // 16 * rowb, rounded up to 16
+  int out_floats;  // 16 * rowo
+  int items;       // 16-byte input items per q: 16 * bv * ipr
+  int quads;       // float4 outputs per q: 16 * bv * P / 4
+};
+
+// The pads make the 16 lanes of a row group (16 different r0, same c0) hit
+// distinct LDS banks on the 8-byte slab reads and the 16-byte output writes.
+__host__ __device__ inline FaGeom fa_geom(int wt, int nb, int bv) {
+  FaGeom g;
+  g.ppw = fa_ppw(wt, nb);
+  g.esz = fa_esz(wt);
+  g.P = 8 * g.ppw;
+  g.ipr = g.P * g.esz / 16;
+  g.rsb = g.P * g.esz + 8;
+  g.rowb = bv * g.rsb;
+  if (((g.rowb / 8) & 1) == 0) g.rowb += 8;
+  g.rowo = bv * g.P;
+  if (((g.rowo / 4) & 1) == 0) g.rowo += 4;
+  g.slab_bytes = (16 * g.rowb + 15) / 16 * 16;
+  g.out_floats = 16 * g.rowo;
+  g.items = 16 * bv * g.ipr;
+  g.quads = 16 * bv * g.P / 4;
+  return g;
+}
+
+__host__ __device__ inline int fa_lds_bytes(const FaGeom& g) {
+  return g.slab_bytes + g.out_floats * (int)sizeof(float);
+}
 
 // Workgroup b -> (p range, q chunk, column chunk).  Workgroups are dealt to
 // the 8 XCDs round robin (b % 8); consecutive slots of one XCD walk the p
@@ -77,19 +160,20 @@ struct FaTile {
   int p0, q0, chunk;
 };
 
+__host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
+  return (int64_t)(256 / fa_p(a.wt, a.nb)) * (256 / kFaQC) * a.nchunk;
+}
+
 __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_t nwg) {
+  const int P = fa_p(a.wt, a.nb);
   const int64_t per_xcd = nwg / 8;
   const int64_t lin = (b % 8) * per_xcd + b / 8;
   FaTile t;
-  t.p0 = (int)(lin % (256 / kFaP)) * kFaP;
-  const int64_t rest = lin / (256 / kFaP);
-  t.q0 = (int)(rest % a.nqc) * kFaQC;
-  t.chunk = (int)(rest / a.nqc);
+  t.p0 = (int)(lin % (256 / P)) * P;
+  const int64_t rest = lin / (256 / P);
+  t.q0 = (int)(rest % (256 / kFaQC)) * kFaQC;
+  t.chunk = (int)(rest / (256 / kFaQC));
   return t;
-}
-
-__host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
-  return (int64_t)(256 / kFaP) * a.nqc * a.nchunk;
 }
 
 // i / bv without a division instruction (exact for the ranges the host checks).
@@ -97,27 +181,27 @@ __host__ __device__ inline int fa_div_bv(const FusedAArgs& a, int i) {
   return (int)(((uint64_t)(uint32_t)i * a.bv_magic) >> 32);
 }
 
-// LDS input slot of (p_local, r0, c0): [p kFaP][r0 16][16*nb + 4]
-__host__ __device__ inline int fa_kp(int nb) { return 16 * nb + 4; }
-__host__ __device__ inline int fa_lds_in(int nb, int pl, int r0, int c0) {
-  return (pl * 16 + r0) * fa_kp(nb) + c0;
+// Byte offset of input item (r0, c0, o) in the slab (8-byte aligned).
+__host__ __device__ inline int fa_slab_item(const FaGeom& g, int r0, int c0, int o) {
+  return r0 * g.rowb + c0 * g.rsb + 16 * o;
 }
-// LDS output slot of (r0, c0, p_local): [r0 16][c0 bv][p kFaP + 4].  The pad
-// spreads the accumulator writes (lanes over r0 and c0) over more banks and
-// keeps each p run 16-byte aligned for the float4 reads of the store.
-constexpr int kFaOutStride = kFaP + 4;
-__host__ __device__ inline int fa_lds_out(int bv, int r0, int c0, int pl) {
-  return (r0 * bv + c0) * kFaOutStride + pl;
+// Byte offset of the ppw elements (r0, c0, [ppw*w, ppw*w + ppw)) in the slab.
+__host__ __device__ inline int fa_slab_read(const FaGeom& g, int r0, int c0, int w) {
+  return r0 * g.rowb + c0 * g.rsb + g.ppw * w * g.esz;
 }
-__host__ __device__ inline int fa_lds_floats(int nb, int bv) {
-  const int in = kFaP * 16 * fa_kp(nb);
-  const int out = 16 * bv * kFaOutStride;
-  return in > out ? in : out;
+// Float offset of output (r0', c0', p_local) in the output area.
+__host__ __device__ inline int fa_out(const FaGeom& g, int r0, int c0, int pl) {
+  return r0 * g.rowo + c0 * g.P + pl;
 }
 // Global element (row, col) of (r0, q) x (chunk, c0, p).
 __host__ __device__ inline int64_t fa_row(int r0, int q) { return (int64_t)r0 * 256 + q; }
 __host__ __device__ inline int64_t fa_col(const FusedAArgs& a, int chunk, int c0, int p) {
   return (int64_t)chunk * a.dv + (int64_t)c0 * 256 + p;
+}
+// Fragment-order V_0 block index of (group, nt, lr, lg, s): the 4 nb steps of
+// one (nt, lane) are contiguous.
+__host__ __device__ inline int64_t fa_vfrag(int nb, int nt, int lr, int lg, int s) {
+  return (((int64_t)nt * 16 + lr) * 4 + lg) * (4 * nb) + s;
 }
 
 // ---- pass B geometry --------------------------------------------------------

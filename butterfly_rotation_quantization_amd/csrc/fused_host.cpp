@@ -56,8 +56,20 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
         pad[((size_t)g * np + j) * np + k] = blk[j * b0 + k] * sg;
       }
   }
+  // the same blocks in pass A's fragment order: lane (lr, lg) of output tile
+  // nt reads the 4 nb steps V[16 nt + lr][4 s + lg] as consecutive floats
+  std::vector<float> frag(pad.size());
+  for (int g = 0; g < ng0; ++g)
+    for (int nt = 0; nt < nb; ++nt)
+      for (int lr = 0; lr < 16; ++lr)
+        for (int lg = 0; lg < 4; ++lg)
+          for (int st = 0; st < 4 * nb; ++st)
+            frag[(size_t)g * np * np + fa_vfrag(nb, nt, lr, lg, st)] =
+                pad[((size_t)g * np + 16 * nt + lr) * np + 4 * st + lg];
   hipError_t e = rt_malloc((void**)&p.fz0, pad.size() * sizeof(float));
   if (e == hipSuccess) e = rt_copy_to_device(p.fz0, pad.data(), pad.size() * sizeof(float));
+  if (e == hipSuccess) e = rt_malloc((void**)&p.fz0f, frag.size() * sizeof(float));
+  if (e == hipSuccess) e = rt_copy_to_device(p.fz0f, frag.data(), frag.size() * sizeof(float));
   if (e != hipSuccess) return e;
   p.fz_nb = nb;
   p.fz_gs0 = per_group ? (int64_t)np * np : 0;
@@ -98,10 +110,16 @@ int fused_b_grid(const FusedBArgs& b) {
 const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (a.bv < 2 || a.bv > 64 || a.nb != (a.bv + 15) / 16) return "V_0 radix";
   if (a.m != 4096 || a.dv != a.bv * 256 || (int64_t)a.nchunk * a.dv != a.n) return "shape";
-  if (a.nqc * kFaQC != 256 || fa_nwg(a) % 8) return "pass A grid";
+  if (fa_nwg(a) % 8) return "pass A grid";
   for (int i = 0; i < 16 * a.bv; ++i)  // the multiply-shift quotient is exact where used
     if (fa_div_bv(a, i) != i / a.bv) return "division multiplier";
-  if (!a.w || !a.ws || !a.u0 || !a.v0) return "pass A pointers";
+  if (fa_lds_bytes(fa_geom(a.wt, a.nb, a.bv)) > 160 * 1024) return "pass A LDS";
+  // pass A addresses a lane's input and output as 32-bit byte offsets from a
+  // per-chunk base
+  if ((int64_t)a.m * a.ldw * fa_esz(a.wt) >= (int64_t(1) << 31) ||
+      (int64_t)a.m * a.n * 4 >= (int64_t(1) << 31))
+    return "32-bit offsets";
+  if (!a.w || !a.ws || !a.u0 || !a.v0f) return "pass A pointers";
   if (a.u0_gs && a.u0_n < 256 * a.u0_gs) return "U_0 extent";
   if (a.v0_gs && a.v0_n < 256 * a.v0_gs) return "V_0 extent";
   if (a.u0_n < 256 || a.v0_n < 256 * a.nb * a.nb) return "block extent";
@@ -123,8 +141,9 @@ const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
 
 void fused_release(Plan& p) {
   rt_free(p.fz0);
+  rt_free(p.fz0f);
   rt_free(p.fz_had);
-  p.fz0 = p.fz_had = nullptr;
+  p.fz0 = p.fz0f = p.fz_had = nullptr;
   p.fz_ok = 0;
 }
 
@@ -174,9 +193,8 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.nchunk = (int)(n / V->d);
   a.u0 = U->fz0;  // radix 16: the padded layout is the 16 x 16 block itself
   a.u0_gs = U->fz_gs0;
-  a.v0 = V->fz0;
+  a.v0f = V->fz0f;
   a.v0_gs = V->fz_gs0;
-  a.nqc = 256 / kFaQC;
   a.bv_magic = (uint32_t)((1ull << 32) / (uint64_t)a.bv + 1);
 
   FusedBArgs b;

@@ -11,6 +11,8 @@
 // multiplied by its own b x b block, y_j = sum_k B[j][k] x_k; here the group
 // index is fixed per tile and the batch of the product runs over the other
 // matrix index, which shares the block.
+#include <utility>
+
 #include "fused.h"
 
 namespace brq {
@@ -35,140 +37,179 @@ __device__ __forceinline__ float cvt_f16(uint32_t w, int hi) {
 
 // ------------------------------------------------------------------ pass A
 
-// One input item: the kFaP = 8 consecutive p of one (r0, c0) segment.
-template <int WT>
-struct Raw {
-  uint32_t v[WT == BRQ_F32 ? 8 : 4];
-};
+// The ppw consecutive slab elements one lane reads per V_0 step: 8 bytes, or
+// 4 for 16-bit input with ppw = 2 (then in .x).
+template <int WT, int PPW>
+__device__ __forceinline__ uint2 fa_aread(const uint8_t* src) {
+  if constexpr (PPW * fa_esz(WT) == 8) return *reinterpret_cast<const uint2*>(src);
+  else return make_uint2(*reinterpret_cast<const uint32_t*>(src), 0u);
+}
 
-template <int WT>
-__device__ __forceinline__ void fa_load_item(const FusedAArgs& a, const FaTile& t, int q, int it,
-                                             Raw<WT>& r) {
-  const int r0 = fa_div_bv(a, it);
-  const int c0 = it - r0 * a.bv;
-  const int64_t off = fa_row(r0, q) * a.ldw + fa_col(a, t.chunk, c0, t.p0);
-  if (WT == BRQ_F32) {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.w) + off);
-    const uint4 x0 = src[0], x1 = src[1];
-    r.v[0] = x0.x; r.v[1] = x0.y; r.v[2] = x0.z; r.v[3] = x0.w;
-    r.v[4] = x1.x; r.v[5] = x1.y; r.v[6] = x1.z; r.v[7] = x1.w;
+template <int WT, int PPW>
+__device__ __forceinline__ void fa_unpack(uint2 x, float (&v)[PPW]) {
+  if constexpr (WT == BRQ_F32) {
+    static_assert(PPW == 2, "float32 slabs hold two p per wave");
+    v[0] = __uint_as_float(x.x);
+    v[1] = __uint_as_float(x.y);
+  } else if constexpr (PPW == 4) {
+    if constexpr (WT == BRQ_BF16) {
+      v[0] = cvt_bf16(x.x, 0); v[1] = cvt_bf16(x.x, 1);
+      v[2] = cvt_bf16(x.y, 0); v[3] = cvt_bf16(x.y, 1);
+    } else {
+      v[0] = cvt_f16(x.x, 0); v[1] = cvt_f16(x.x, 1);
+      v[2] = cvt_f16(x.y, 0); v[3] = cvt_f16(x.y, 1);
+    }
   } else {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.w) + off);
-    r.v[0] = x0.x; r.v[1] = x0.y; r.v[2] = x0.z; r.v[3] = x0.w;
+    if constexpr (WT == BRQ_BF16) {
+      v[0] = cvt_bf16(x.x, 0); v[1] = cvt_bf16(x.x, 1);
+    } else {
+      v[0] = cvt_f16(x.x, 0); v[1] = cvt_f16(x.x, 1);
+    }
   }
-}
-
-template <int WT>
-__device__ __forceinline__ float fa_elem(const Raw<WT>& r, int e) {
-  if (WT == BRQ_F32) return __uint_as_float(r.v[e]);
-  if (WT == BRQ_BF16) return cvt_bf16(r.v[e >> 1], e & 1);
-  return cvt_f16(r.v[e >> 1], e & 1);
-}
-
-template <int WT>
-__device__ __forceinline__ void fa_store_item(const FusedAArgs& a, int it, const Raw<WT>& r,
-                                              float* lds, int nb) {
-  const int r0 = fa_div_bv(a, it);
-  const int c0 = it - r0 * a.bv;
-#pragma unroll
-  for (int e = 0; e < kFaP; ++e) lds[fa_lds_in(nb, e, r0, c0)] = fa_elem<WT>(r, e);
 }
 
 // The signs of both sides are folded into the stage-0 blocks at plan time, so
-// the input is used as stored.
-template <int NB, int WT>
-__global__ __launch_bounds__(kFaWaves * 64, 2) void fused_a_kernel(FusedAArgs a) {
-  extern __shared__ float lds[];
-  constexpr int NT = kFaWaves * 64;
+// the input is used as stored.  Per q: slab in (barrier), V_0 and U_0 on
+// MFMA per 16-column output tile with the results into the output area
+// (barrier), output area to global; the next slab is loaded into registers
+// while the products run.  Loads and stores
+// take one column c0 per wave instruction, so a lane's address is one
+// loop-invariant register plus wave-uniform terms.
+template <int ST, int WT>
+__global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a) {
+  constexpr int NB = fa_nb_of_steps(ST);
+  constexpr int PPW = fa_ppw(WT, NB);
+  constexpr int ESZ = fa_esz(WT);
+  constexpr int P = 8 * PPW;
+  constexpr int IPR = P * ESZ / 16;
+  constexpr int KI = fa_ki(WT, ST);  // slab load instructions per wave
+  constexpr int KQ = fa_kq_nt(WT, ST);  // output store instructions per wave and 16 columns
+  extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int w = tid >> 6;  // this wave's p (local)
+  const int w = tid >> 6;
   const FaTile t = fa_tile(a, blockIdx.x, fa_nwg(a));
   const int bv = a.bv;
-  const int p = t.p0 + w;
+  const FaGeom g = fa_geom(WT, NB, bv);
+  uint8_t* slab = smem;
+  float* outa = reinterpret_cast<float*>(smem + g.slab_bytes);
 
-  // V_0 block of group p, as B fragments: bvf[kb][nt] = B[16nt + lr][16kb + 4lg + i]
-  f4 bvf[NB][NB];
-  {
-    const float* vb = a.v0 + (int64_t)p * a.v0_gs;
+  // The per-instruction lane offsets are rebuilt from an opaque copy of the
+  // lane index on every use: hoisted out of the q loop they would hold some
+  // 30 registers that the V_0 blocks need.
+  auto opaque = [](int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  uint4 raw[KI];
+  auto load_slab = [&](int q) {
+    const uint8_t* base =
+        static_cast<const uint8_t*>(a.w) + ((int64_t)q * a.ldw + fa_col(a, t.chunk, 0, t.p0)) * ESZ;
+    const int ln = opaque(lane);
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int nt = 0; nt < NB; ++nt)
-        bvf[kb][nt] = ld4(vb + (16 * nt + lr) * (16 * NB) + 16 * kb + 4 * lg);
-  }
-
-  const int items = 16 * bv;  // <= 1024: at most two per thread
-  Raw<WT> raw[2];
-  int q = t.q0;
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (tid + k * NT < items) fa_load_item<WT>(a, t, q, tid + k * NT, raw[k]);
-  // U_0 block of group q as B fragments: B[k = r0 = 4lg + i][n = r0' = lr] = U[lr][4lg + i]
-  f4 bu = ld4(a.u0 + (int64_t)q * a.u0_gs + lr * 16 + 4 * lg);
-
-  for (int qi = 0; qi < kFaQC; ++qi, ++q) {
-    __syncthreads();  // previous slice's LDS reads are done
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (tid + k * NT < items) fa_store_item<WT>(a, tid + k * NT, raw[k], lds, NB);
-    __syncthreads();
-
-    // A fragments of X_qp: A[m = r0 = lr][k = c0 = 16kb + 4lg + i]
-    f4 af[NB];
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      af[kb] = ld4(&lds[fa_lds_in(NB, w, lr, 16 * kb + 4 * lg)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (16 * kb + 4 * lg + i >= bv) af[kb][i] = 0.f;
+    for (int k = 0; k < KI; ++k) {
+      const FaSlot x = fa_slot(IPR, w, k, ln, bv, 0);
+      const uint32_t off = (uint32_t)((x.r0 * 256 * a.ldw + x.c0 * 256 + (ln % IPR) * (16 / ESZ)) * ESZ);
+      raw[k] = *reinterpret_cast<const uint4*>(base + off);
     }
-    const f4 bu_q = bu;
-    if (qi + 1 < kFaQC) {  // prefetch the next slice and its U_0 block
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        if (tid + k * NT < items) fa_load_item<WT>(a, t, q + 1, tid + k * NT, raw[k]);
-      bu = ld4(a.u0 + (int64_t)(q + 1) * a.u0_gs + lr * 16 + 4 * lg);
-    }
-    __syncthreads();  // every wave holds its fragments; the slice may be overwritten
+  };
 
-    // V_0: D[nt][m = r0][n = c0'] = sum_c0 X[r0][c0] V[c0'][c0]; the NB
-    // accumulators are independent, so their products interleave.
-    f4 d[NB];
+  // V_0 blocks of this wave's p: bvf[j][nt][s] = V[16 nt + lr][4 s + lg]
+  float bvf[PPW][NB][ST];
 #pragma unroll
-    for (int nt = 0; nt < NB; ++nt) d[nt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int nt = 0; nt < NB; ++nt) d[nt] = mfma4(af[kb][i], bvf[kb][nt][i], d[nt]);
-    // U_0 on the transpose: E[nt][m = c0'][n = r0'] = sum_r0 U[r0'][r0] D[r0][c0']
-    f4 e[NB];
-#pragma unroll
-    for (int nt = 0; nt < NB; ++nt) e[nt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int nt = 0; nt < NB; ++nt) e[nt] = mfma4(d[nt][i], bu_q[i], e[nt]);
+  for (int j = 0; j < PPW; ++j) {
+    const float* vb = a.v0f + (int64_t)(t.p0 + PPW * w + j) * a.v0_gs;
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
+      for (int sq = 0; 4 * sq < ST; ++sq) {
+        const f4 v = ld4(vb + fa_vfrag(NB, nt, lr, lg, 4 * sq));
+#pragma unroll
+        for (int e = 0; e < 4 && 4 * sq + e < ST; ++e) bvf[j][nt][4 * sq + e] = v[e];
+      }
+  }
+  int q = t.q0;
+  load_slab(q);
+  f4 bu = ld4(a.u0 + (int64_t)q * a.u0_gs + lr * 16 + 4 * lg);
+  // nothing loaded before the loop is outstanding inside it, so the products
+  // never wait on the prefetch of the next slab
+  __builtin_amdgcn_s_waitcnt(0);
+
+  for (int qi = 0; qi < kFaQC; ++qi, ++q) {
+    // the previous slab's reads ended before the previous second barrier
+    const int ls = opaque(lane);
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+      const FaSlot x = fa_slot(IPR, w, k, ls, bv, 0);
+      uint8_t* d = slab + fa_slab_item(g, x.r0, x.c0, ls % IPR);
+      *reinterpret_cast<uint2*>(d) = make_uint2(raw[k].x, raw[k].y);
+      *reinterpret_cast<uint2*>(d + 8) = make_uint2(raw[k].z, raw[k].w);
+    }
+    __syncthreads();  // slab complete
+    const f4 bq = bu;
+    uint8_t* obase = reinterpret_cast<uint8_t*>(a.ws) + ((int64_t)q * a.n + fa_col(a, t.chunk, 0, t.p0)) * 4;
+
+    const uint8_t* arow = slab + fa_slab_read(g, lr, 0, w);
+#pragma unroll
+    for (int nt = 0; nt < NB; ++nt) {
+      // V_0: D[j][m = r0][n = c0'] = sum_c0 X_j[r0][c0] V_j[c0'][c0], c0' = 16 nt + n.
+      // The slab read of step s + 1 is issued before the products of step s.
+      f4 d[PPW];
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) d[j] = f4{0.f, 0.f, 0.f, 0.f};
+      uint2 nxt = fa_aread<WT, PPW>(arow + lg * g.rsb);
+#pragma unroll
+      for (int s = 0; s < ST; ++s) {
+        const uint2 cur = nxt;
+        if (s + 1 < ST) {
+          const int c1 = 4 * (s + 1) + lg;  // only the last step can pass the radix
+          nxt = fa_aread<WT, PPW>(arow + (s + 2 < ST || c1 < bv ? c1 : bv - 1) * g.rsb);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep that read ahead of this step's products
+        const bool live = s + 1 < ST || 4 * s + lg < bv;
+        float av[PPW];
+        fa_unpack<WT, PPW>(cur, av);
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) d[j] = mfma4(live ? av[j] : 0.f, bvf[j][nt][s], d[j]);
+      }
+      // the next slab's loads queue behind the previous stores: issued after
+      // the first tile's products they no longer hold up the MFMA phase
+      if (nt == 0 && qi + 1 < kFaQC) {
+        load_slab(q + 1);
+        bu = ld4(a.u0 + (int64_t)(q + 1) * a.u0_gs + lr * 16 + 4 * lg);
+      }
+      // U_0 on the transpose: E[j][m = c0'][n = r0'] = sum_r0 U[r0'][r0] D[j][r0][c0']
+      f4 e[PPW];
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) e[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) e[j] = mfma4(d[j][i], bq[i], e[j]);
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c0 = 16 * nt + 4 * lg + i;
-        if (c0 < bv) lds[fa_lds_out(bv, lr, c0, w)] = e[nt][i];
+        if (c0 < bv) {
+          float* o = outa + fa_out(g, lr, c0, PPW * w);
+          if constexpr (PPW == 4)
+            *reinterpret_cast<f4*>(o) = f4{e[0][i], e[1][i], e[2][i], e[3][i]};
+          else
+            *reinterpret_cast<float2*>(o) = make_float2(e[0][i], e[1][i]);
+        }
       }
-    __syncthreads();
-
-    // store the slice: 16 x bv runs of kFaP floats, as float4 pairs
-    const int quads = items * (kFaP / 4);
-    for (int it = tid; it < quads; it += NT) {
-      const int rc = it >> 1, h2 = it & 1;
-      const int r0 = fa_div_bv(a, rc);
-      const int c0 = rc - r0 * bv;
-      const f4 v = ld4(&lds[fa_lds_out(bv, r0, c0, 4 * h2)]);
-      *reinterpret_cast<f4*>(a.ws + fa_row(r0, q) * a.n + fa_col(a, t.chunk, c0, t.p0 + 4 * h2)) = v;
     }
+    __syncthreads();  // output area complete; the slab may be overwritten
+
+    const int lo = opaque(lane);
+#pragma unroll
+    for (int nt = 0; nt < NB; ++nt)
+#pragma unroll
+      for (int k = 0; k < KQ; ++k) {
+        const FaSlot x = fa_slot(P / 4, w, k, lo, bv, 16 * nt);
+        const int pq = lo % (P / 4);
+        const f4 v = ld4(outa + fa_out(g, x.r0, x.c0, 4 * pq));
+        *reinterpret_cast<f4*>(obase + (uint32_t)((x.r0 * 256 * a.n + x.c0 * 256 + 4 * pq) * 4)) = v;
+      }
   }
 }
 
@@ -364,27 +405,39 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   }
 }
 
-template <int NB, int WT>
+template <int ST, int WT>
 hipError_t launch_a_t(const FusedAArgs& a, hipStream_t s) {
-  static bool attr = false;  // slices above 64 KiB of LDS need the opt-in
+  static bool attr = false;  // output areas above 64 KiB of LDS need the opt-in
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_a_kernel<NB, WT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       fa_lds_floats(NB, 16 * NB) * (int)sizeof(float));
+    int most = 0;
+    for (int bv = 4 * ST - 3; bv <= 4 * ST; ++bv) {
+      const int b = fa_lds_bytes(fa_geom(WT, fa_nb_of_steps(ST), bv));
+      most = b > most ? b : most;
+    }
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_a_kernel<ST, WT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const size_t lds = (size_t)fa_lds_floats(NB, a.bv) * sizeof(float);
-  hipLaunchKernelGGL((fused_a_kernel<NB, WT>), dim3((unsigned)fa_nwg(a)), dim3(kFaWaves * 64), lds,
+  const size_t lds = (size_t)fa_lds_bytes(fa_geom(WT, a.nb, a.bv));
+  hipLaunchKernelGGL((fused_a_kernel<ST, WT>), dim3((unsigned)fa_nwg(a)), dim3(kFaWaves * 64), lds,
                      s, a);
   return hipGetLastError();
 }
 
-template <int NB>
-hipError_t launch_a_nb(const FusedAArgs& a, hipStream_t s) {
-  if (a.wt == BRQ_F32) return launch_a_t<NB, BRQ_F32>(a, s);
-  if (a.wt == BRQ_BF16) return launch_a_t<NB, BRQ_BF16>(a, s);
-  return launch_a_t<NB, BRQ_F16>(a, s);
+template <int ST>
+hipError_t launch_a_st(const FusedAArgs& a, hipStream_t s) {
+  if (a.wt == BRQ_F32) return launch_a_t<ST, BRQ_F32>(a, s);
+  if (a.wt == BRQ_BF16) return launch_a_t<ST, BRQ_BF16>(a, s);
+  return launch_a_t<ST, BRQ_F16>(a, s);
+}
+
+template <int... STs>
+hipError_t launch_a_steps(const FusedAArgs& a, hipStream_t s, std::integer_sequence<int, STs...>) {
+  hipError_t e = hipErrorInvalidValue;
+  const int st = fa_steps(a.bv);
+  ((st == STs + 1 ? (e = launch_a_st<STs + 1>(a, s), 0) : 0), ...);
+  return e;
 }
 
 template <int BITS, int QK, int G>
@@ -417,13 +470,8 @@ hipError_t launch_b_k(const FusedBArgs& a, int grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t s) {
-  switch (a.nb) {
-    case 1: return launch_a_nb<1>(a, s);
-    case 2: return launch_a_nb<2>(a, s);
-    case 3: return launch_a_nb<3>(a, s);
-    case 4: return launch_a_nb<4>(a, s);
-  }
-  return hipErrorInvalidValue;
+  if (a.bv < 2 || a.bv > 64 || a.nb != fa_nb_of_steps(fa_steps(a.bv))) return hipErrorInvalidValue;
+  return launch_a_steps(a, s, std::make_integer_sequence<int, 16>{});
 }
 
 hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t s) {
