@@ -314,6 +314,11 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
   const int bits = a.bits, g = a.group;
   const int fpg = g / 16, nw = fpg * 16 * bits / 32;
   std::vector<int> tiles_seen((size_t)ntiles, 0);
+  {  // the V_1 row order is a permutation of the 16 rows
+    int seen = 0;
+    for (int n = 0; n < 16; ++n) seen |= 1 << fb_sigma(n);
+    if (seen != 0xffff) return violation("V_1 row order is not a permutation", 0, 0), hipErrorInvalidValue;
+  }
   for (int64_t wg = 0; wg < grid; ++wg)
     for (int64_t tile = wg; tile < ntiles; tile += grid) {  // the kernel's persistent loop
       tiles_seen[(size_t)tile]++;
@@ -332,19 +337,22 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
       for (int w = 0; w < kFbWaves; ++w)
         for (int l = 0; l < 64; ++l) {
           const int lr = l & 15, lg = l >> 4;
-          const int64_t row = fb_row(t, lr, w), col = fb_col(a, t, 4 * lg, 0);
-          for (int i = 0; i < 4; ++i)
-            for (int qd = 0; qd < 4; ++qd) {
-              const int64_t off = row * a.n + col + i * 16 + 4 * qd;
-              if (row >= a.m || !in_range(col + i * 16 + 4 * qd, 4, a.n) || off % 4)
-                return violation("pass B load (%lld, %lld)", row, col + i * 16 + 4 * qd), hipErrorInvalidValue;
-              for (int j = 0; j < 4; ++j) cover[(size_t)(off + j)]++;
-            }
+          // the two halves fb_load_half<H>: columns c1 = 4 lg + 2H + e, all c2
+          const int64_t row = fb_row(t, lr, w);
+          for (int hh = 0; hh < 2; ++hh)
+            for (int e = 0; e < 2; ++e)
+              for (int qd = 0; qd < 4; ++qd) {
+                const int64_t col = fb_col(a, t, 4 * lg + 2 * hh, 0) + e * 16 + 4 * qd;
+                const int64_t off = row * a.n + col;
+                if (row >= a.m || !in_range(col, 4, a.n) || off % 4)
+                  return violation("pass B load (%lld, %lld)", row, col), hipErrorInvalidValue;
+                for (int j = 0; j < 4; ++j) cover[(size_t)(off + j)]++;
+              }
           if (!in_range((int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg, 4, a.u1_n) ||
               !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg, 4, a.u2_n))
             return violation("U_1/U_2 block read wave %lld lane %lld", w, l), hipErrorInvalidValue;
           for (int c = 0; c < 16; ++c) {
-            if (!in_range(kFbV1Off + c * 256 + lr * 16 + 4 * lg, 4, kFbXchFloats) ||
+            if (!in_range(kFbV1Off + c * 256 + fb_sigma(lr) * 16 + 4 * lg, 4, kFbXchFloats) ||
                 !in_range(kFbV2Off + c * 256 + lr * 16 + 4 * lg, 4, kFbLdsFloats))
               return violation("V block LDS read %lld lane %lld", c, l), hipErrorInvalidValue;
           }
@@ -354,10 +362,12 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
         for (int w = 0; w < kFbWaves; ++w)
           for (int l = 0; l < 64; ++l) {
             const int lr = l & 15, lg = l >> 4;
-            if ((lg >> 1) != h) continue;
-            for (int i = 0; i < 4; ++i)
+            // registers j = 2h + e hold c1' = lg + 4 j, i.e. c1h = lg + 4 e
+            for (int e = 0; e < 2; ++e)
               for (int qd = 0; qd < 4; ++qd) {
-                const int c1h = 4 * lg + i - 8 * h;
+                const int c1h = lg + 4 * e;
+                if (fb_sigma(4 * lg + 2 * h + e) != 8 * h + c1h)
+                  return violation("phase-1 output order %lld %lld", lg, e), hipErrorInvalidValue;
                 const int s = fb_xch(lr, c1h, w, 4 * qd);
                 if (!in_range(s, 4, kFbXchFloats) || s % 4) return violation("exchange write %lld", s, 0), hipErrorInvalidValue;
                 for (int j = 0; j < 4; ++j) {

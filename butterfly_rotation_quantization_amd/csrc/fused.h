@@ -223,12 +223,23 @@ __host__ __device__ inline FbTile fb_tile(const FusedBArgs& a, int64_t b) {
   return t;
 }
 
-// Exchange slot of element (r1, c1h, r2, c2).  The XOR swizzles keep the
-// float4 reads of phase 2 (4 consecutive c2) contiguous while spreading the
-// scalar writes of phase 1 (lanes over r1 and c1h) over 8 banks instead of 1.
+// Exchange slot of element (r1, c1h, r2, c2), c1h = c1 - 8 h.  Each float4
+// holds four consecutive c2; within every 16 float4s (r1, c1h and r2 / 4
+// fixed) the quad index (r2 % 4, c2 / 4) is XORed with r1 and r2 / 4.  The 16
+// lanes of a row group then hit 16 different bank groups both on the phase-1
+// writes (lanes over r1 at fixed c1h, r2, c2 / 4) and on the phase-2 reads
+// (lanes over r2 at fixed r1, c1h, c2 / 4).
 __host__ __device__ inline int fb_xch(int r1, int c1h, int r2, int c2) {
-  return ((r1 * 8 + c1h) * 16 + (r2 ^ (c1h >> 2))) * 16 + (c2 ^ ((r1 & 3) << 2));
+  const int hi = (r1 * 8 + c1h) * 4 + (r2 >> 2);
+  const int lo = (((r2 & 3) * 4 + (c2 >> 2)) ^ (r2 >> 2) ^ r1) & 15;
+  return (hi * 16 + lo) * 4 + (c2 & 3);
 }
+
+// Row order of the V_1 products: output tile row n holds c1' = fb_sigma(n),
+// so MFMA result register j of lane group lg holds c1' = lg + 4 j and the
+// exchange half h (c1' in [8h, 8h + 8)) is registers 2h and 2h + 1 of every
+// lane.
+__host__ __device__ inline int fb_sigma(int n) { return (n >> 2) + 4 * (n & 3); }
 
 __host__ __device__ inline int64_t fb_row(const FbTile& t, int r1, int r2) {
   return (int64_t)t.r0 * 256 + r1 * 16 + r2;

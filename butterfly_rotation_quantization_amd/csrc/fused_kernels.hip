@@ -26,6 +26,14 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
 
 __device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
 
+// The value itself, hidden from the optimizer: addresses derived from it are
+// rebuilt where they are used instead of being hoisted out of a loop, where
+// they would hold registers the tiles need.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ float cvt_bf16(uint32_t w, int hi) {
   return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
 }
@@ -97,10 +105,6 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
   // The per-instruction lane offsets are rebuilt from an opaque copy of the
   // lane index on every use: hoisted out of the q loop they would hold some
   // 30 registers that the V_0 blocks need.
-  auto opaque = [](int v) {
-    asm volatile("" : "+v"(v));
-    return v;
-  };
   uint4 raw[KI];
   auto load_slab = [&](int q) {
     const uint8_t* base =
@@ -215,21 +219,32 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
 
 // ------------------------------------------------------------------ pass B
 
+// Group statistic of one lane's four values: absmax, or sum of squares for
+// the norm quantizer (reduced over the four lane groups and rooted later).
+template <int QK>
+__device__ __forceinline__ float fb_stat(float acc, const f4& v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = QK == BRQ_ABSMAX ? fmaxf(acc, fabsf(v[i])) : fmaf(v[i], v[i], acc);
+  return acc;
+}
+
+// Quantize and pack half h of the tile rows of r1.  The phase-2 results were
+// written back in place into this wave's part of the exchange buffer, where
+// slot (r1, c1h, r2, 4 lg) holds row r2's four consecutive columns
+// c1 = 8h + c1h, c2 = 4 lg .. 4 lg + 3; stat[gi] holds this lane's part of
+// group gi's statistic.  Each fragment is read back, coded and packed in turn.
 template <int BITS, int QK, int G>
 __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t, int r1, int h,
-                                            const f4 (&v)[8], int lr, int lg) {
+                                            const float* xch, const float (&stat_in)[128 / G], int lr,
+                                            int lg) {
   constexpr int NG = 128 / G;      // groups in this half
   constexpr int FPG = 8 / NG;      // 16-column fragments per group
   constexpr int LV = (1 << BITS) - 1;
+  constexpr int NW = FPG * 16 * BITS / 32;  // 32-bit code words per row and group
   const int64_t row = fb_row(t, r1, lr);
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    float stat = 0.f;
-#pragma unroll
-    for (int f = gi * FPG; f < (gi + 1) * FPG; ++f)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        stat = QK == BRQ_ABSMAX ? fmaxf(stat, fabsf(v[f][i])) : fmaf(v[f][i], v[f][i], stat);
+    float stat = stat_in[gi];
     if (QK == BRQ_ABSMAX) {
       stat = fmaxf(stat, __shfl_xor(stat, 16, 64));
       stat = fmaxf(stat, __shfl_xor(stat, 32, 64));
@@ -239,96 +254,118 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
       stat = sqrtf(stat);
     }
     const float k = stat > 0.f ? (QK == BRQ_ABSMAX ? a.h / stat : a.sqrt_g / stat) : 0.f;
-    uint32_t chunk[FPG];
+    // Packing: lane group lg assembles the words of fragments
+    // [lg * FPG / 4, (lg + 1) * FPG / 4) when they end on a word boundary
+    // (NW divisible by 4), else lane group 0 assembles all NW words.
+    constexpr bool SPLIT = NW % 4 == 0;
+    constexpr int NWL = SPLIT ? NW / 4 : NW;  // words per assembling lane
+    uint32_t words[NWL];
+#pragma unroll
+    for (int j = 0; j < NWL; ++j) words[j] = 0u;
 #pragma unroll
     for (int f = 0; f < FPG; ++f) {
+      const f4 v = ld4(&xch[fb_xch(r1, gi * FPG + f, lr, 4 * lg)]);
       uint32_t c4 = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = v[gi * FPG + f][i];
         int c = 0;
         if (stat > 0.f) {
           if (QK == BRQ_ABSMAX) {
-            c = (int)__builtin_rintf(fmaf(x, k, a.h));
+            c = (int)__builtin_rintf(fmaf(v[i], k, a.h));
             c = c < 0 ? 0 : (c > LV ? LV : c);
           } else {
-            const float z = x * k;
+            const float z = v[i] * k;
 #pragma unroll
             for (int q = 0; q < LV; ++q) c += (z > a.tau[q]) ? 1 : 0;
           }
         }
         c4 |= (uint32_t)c << (BITS * i);
       }
-      chunk[f] = c4;
+      // the row's four chunks of this fragment (4 codes each)
+      const bool mine = SPLIT ? lg == f / (FPG / 4) : lg == 0;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t ch = (uint32_t)__shfl((int)c4, lr + 16 * q4, 64);
+        const int bit = (SPLIT ? (f % (FPG / 4)) * 4 + q4 : f * 4 + q4) * 4 * BITS;
+        const int wi = bit >> 5, sh = bit & 31;
+        if (mine) {
+          words[wi] |= ch << sh;
+          if (sh + 4 * BITS > 32) words[wi + 1] |= ch >> (32 - sh);
+        }
+      }
+      // one fragment at a time: read-ahead of the others would hold registers
+      // that the prefetched tile needs
+      __builtin_amdgcn_sched_barrier(0);
     }
     const int64_t col0 = fb_col(a, t, 8 * h + gi * FPG, 0);
     const int64_t gcol = col0 / G;
-    // gather the row's 4*FPG chunks (4 codes each) in lane group 0
-    constexpr int NW = FPG * 16 * BITS / 32;
-    uint32_t words[NW];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) words[j] = 0u;
-#pragma unroll
-    for (int kk = 0; kk < FPG * 4; ++kk) {
-      const uint32_t ch = (uint32_t)__shfl((int)chunk[kk >> 2], lr + 16 * (kk & 3), 64);
-      const int bit = kk * 4 * BITS;
-      const int wi = bit >> 5, sh = bit & 31;
-      words[wi] |= ch << sh;
-      if (sh + 4 * BITS > 32) words[wi + 1] |= ch >> (32 - sh);
-    }
     if (lg == 0) {
       if (QK == BRQ_ABSMAX)
         static_cast<float*>(a.scales)[row * a.scales_ld + gcol] = stat;
       else
         static_cast<_Float16*>(a.scales)[row * a.scales_ld + gcol] = (_Float16)stat;
-      uint32_t* out = reinterpret_cast<uint32_t*>(a.codes + row * a.codes_ld + col0 * BITS / 8);
+    }
+    if (SPLIT || lg == 0) {
+      uint32_t* out = reinterpret_cast<uint32_t*>(a.codes + row * a.codes_ld + col0 * BITS / 8) +
+                      (SPLIT ? lg * NWL : 0);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) out[j] = words[j];
+      for (int j = 0; j < NWL; ++j) out[j] = words[j];
     }
   }
 }
 
-constexpr int FB_IL = 2;  // pass B: fragments whose MFMA chains interleave
+constexpr int FB_IL = 2;   // pass B phase 1: fragments whose MFMA chains interleave
+constexpr int FB_IL2 = 2;  // pass B phase 2 (its registers are shared with the prefetched tile)
 
-// Load the tile's float32 block for phase 1: x[c2][i] = element
-// (r1 = lr, c1 = 4lg + i, r2 = w, c2), in quad-major order so the first
-// fragments wait only for the first loads.
-template <int QD0, int QD1>
-__device__ __forceinline__ void fb_load_tile(const FusedBArgs& a, const FbTile& t, int w, int lr,
+// Load half H of the tile's float32 block for phase 1: x[c2][i] = element
+// (r1 = lr, c1 = 4 lg + i, r2 = w, c2) for i = 2H, 2H + 1, which is 128
+// contiguous bytes of one row per lane.
+template <int H>
+__device__ __forceinline__ void fb_load_half(const FusedBArgs& a, const FbTile& t, int w, int lr,
                                              int lg, f4 (&x)[16]) {
-  const float* src = a.ws + fb_row(t, lr, w) * a.n + fb_col(a, t, 4 * lg, 0);
+  const float* src = a.ws + fb_row(t, lr, w) * a.n + fb_col(a, t, 4 * lg + 2 * H, 0);
 #pragma unroll
-  for (int qd = QD0; qd < QD1; ++qd)
+  for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f4 v = ld4(src + i * 16 + 4 * qd);
+    for (int qd = 0; qd < 4; ++qd) {
+      const f4 v = ld4(src + e * 16 + 4 * qd);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[4 * qd + j][i] = v[j];
+      for (int j = 0; j < 4; ++j) x[4 * qd + j][2 * H + e] = v[j];
     }
 }
 
-// Persistent: workgroup b handles tiles b, b + gridDim.x, ...; the next
-// tile's data is loaded into registers while the current one finishes.
+// Persistent: workgroup b handles tiles b, b + gridDim.x, ...  Each half of
+// the exchange frees half of every lane's tile registers, and the next
+// tile's matching half is loaded into them at once, so the loads run under
+// the second phase and the quantizer of the current tile.
 template <int BITS, int QK, int G>
 __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   extern __shared__ float lds[];
   float* xch = lds;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Lane coordinates are re-derived from an opaque copy of the thread index
+  // in every phase, so nothing computed from them lives across phases: the
+  // tile and its prefetch need all but a few of the 128 registers.
+  int lr, lg;
+  auto lanes = [&]() {
+    const int l = opaque(tid) & 63;
+    lr = l & 15;
+    lg = l >> 4;
+  };
+  lanes();
   const int64_t ntiles = fb_nwg(a);
   int64_t tile = blockIdx.x;
   if (tile >= ntiles) return;
 
   f4 x[16];
   FbTile t = fb_tile(a, tile);
-  fb_load_tile<0, 2>(a, t, w, lr, lg, x);
+  fb_load_half<0>(a, t, w, lr, lg, x);
+  fb_load_half<1>(a, t, w, lr, lg, x);
   f4 bu1 = ld4(a.u1 + (int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg);
+  f4 bu2 = ld4(a.u2 + (int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg);
 
   for (;;) {
-    // fragments 0..7 were loaded ahead (with the previous tile); load 8..15
-    fb_load_tile<2, 4>(a, t, w, lr, lg, x);
-    const f4 bu2 = ld4(a.u2 + (int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg);
     __syncthreads();  // the previous tile is done with LDS
     // stage the tile's V_1 and V_2 blocks (16 each, groups c0*16 + f)
     for (int k = tid; k < 2 * 16 * 64; k += kFbWaves * 64) {
@@ -339,12 +376,15 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
     __syncthreads();
 
     // ---- phase 1: this wave owns r2 = w; fragments over (r1, c1), one per c2.
+    lanes();
+    const int v1_lane = kFbV1Off + fb_sigma(lr) * 16 + 4 * lg;
 #pragma unroll
     for (int c2q = 0; c2q < 16; c2q += FB_IL) {
       f4 d[FB_IL];
 #pragma unroll
       for (int f = 0; f < FB_IL; ++f) {
-        const f4 bv1 = ld4(&lds[kFbV1Off + (c2q + f) * 256 + lr * 16 + 4 * lg]);
+        // B[k = c1][n] = V_1[c1' = sigma(n)][c1]
+        const f4 bv1 = ld4(&lds[v1_lane + (c2q + f) * 256]);
         d[f] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[f] = mfma4(x[c2q + f][i], bv1[i], d[f]);  // V_1: c1
@@ -354,54 +394,73 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int f = 0; f < FB_IL; ++f) x[c2q + f] = mfma4(d[f][i], bu1[i], x[c2q + f]);  // U_1: r1
-      // x[c2]: element (c1' = 4lg + i, r1' = lr)
+      // x[c2][j]: element (c1' = lg + 4 j, r1' = lr)
     }
 
     // ---- phase 2: this wave owns r1 = w; fragments over (r2, c2), one per c1.
     const int64_t next = tile + gridDim.x;
+    const FbTile tn = fb_tile(a, next < ntiles ? next : tile);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      __syncthreads();
-      if ((lg >> 1) == h) {
-        // four fragments give four consecutive c2 of one c1: one 16-byte write
+      lanes();
+      const int lro = lr, lgo = lg;
+      __syncthreads();  // phase 1 (h = 0) or the first half's reads (h = 1) are done
+      // registers 2h and 2h + 1 hold c1' = lg + 8h and lg + 8h + 4; four
+      // fragments give four consecutive c2 of one c1': one 16-byte write
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f4 q4 = {x[4 * qd][i], x[4 * qd + 1][i], x[4 * qd + 2][i], x[4 * qd + 3][i]};
-            *reinterpret_cast<f4*>(&xch[fb_xch(lr, 4 * lg + i - 8 * h, w, 4 * qd)]) = q4;
-          }
+        for (int qd = 0; qd < 4; ++qd) {
+          const int j = 2 * h + e;
+          const f4 q4 = {x[4 * qd][j], x[4 * qd + 1][j], x[4 * qd + 2][j], x[4 * qd + 3][j]};
+          *reinterpret_cast<f4*>(&xch[fb_xch(lro, lgo + 4 * e, w, 4 * qd)]) = q4;
+        }
+      // after the second half every tile register is free: load the whole
+      // next tile (the last tile loads itself again, which keeps this code
+      // free of branches)
+      if (h == 1) {
+        fb_load_half<0>(a, tn, w, lro, lgo, x);
+        fb_load_half<1>(a, tn, w, lro, lgo, x);
       }
-      if (h == 1 && next < ntiles) {  // x is free: prefetch half of the next tile
-        const FbTile tn = fb_tile(a, next);
-        fb_load_tile<0, 2>(a, tn, w, lr, lg, x);
-        bu1 = ld4(a.u1 + (int64_t)(tn.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg);
-      }
       __syncthreads();
-      f4 v[8];
+      lanes();
+      // only this wave reads the slots of r1 = w, so each result goes back
+      // into the slot its input came from
+      float stat[128 / G];
 #pragma unroll
-      for (int c1q = 0; c1q < 8; c1q += FB_IL) {
-        f4 d[FB_IL];
+      for (int gi = 0; gi < 128 / G; ++gi) stat[gi] = 0.f;
 #pragma unroll
-        for (int f = 0; f < FB_IL; ++f) {
+      for (int c1q = 0; c1q < 8; c1q += FB_IL2) {
+        f4 d[FB_IL2], v[FB_IL2];
+#pragma unroll
+        for (int f = 0; f < FB_IL2; ++f) {
           const f4 av = ld4(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]);  // c2 = 4lg + i, r2 = lr
           const f4 bv2 = ld4(&lds[kFbV2Off + (8 * h + c1q + f) * 256 + lr * 16 + 4 * lg]);
           d[f] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) d[f] = mfma4(av[i], bv2[i], d[f]);  // V_2: c2
-          v[c1q + f] = f4{0.f, 0.f, 0.f, 0.f};
+          v[f] = f4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int f = 0; f < FB_IL; ++f) v[c1q + f] = mfma4(d[f][i], bu2[i], v[c1q + f]);  // U_2: r2
+          for (int f = 0; f < FB_IL2; ++f) v[f] = mfma4(d[f][i], bu2[i], v[f]);  // U_2: r2
+        // v[f]: element (row r2' = lr, column c1 = 8h + c1q + f, c2' = 4lg + i)
+#pragma unroll
+        for (int f = 0; f < FB_IL2; ++f) {
+          *reinterpret_cast<f4*>(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]) = v[f];
+          stat[(c1q + f) / (G / 16)] = fb_stat<QK>(stat[(c1q + f) / (G / 16)], v[f]);
+        }
       }
-      // v[c1h]: element (row r2' = lr, column c1 = 8h + c1h, c2' = 4lg + i)
-      fb_quantize<BITS, QK, G>(a, t, w, h, v, lr, lg);
+      lanes();
+      fb_quantize<BITS, QK, G>(a, t, w, h, xch, stat, lr, lg);
     }
     if (next >= ntiles) break;
+    lanes();
+    bu1 = ld4(a.u1 + (int64_t)(tn.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg);
+    bu2 = ld4(a.u2 + (int64_t)(tn.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg);
     tile = next;
-    t = fb_tile(a, tile);
+    t = tn;
   }
 }
 
