@@ -30,6 +30,7 @@ struct Plan {
   // pointers of stages 1 and 2, and float strides between groups (0 = one
   // block shared by all groups).
   int fz_ok = 0;
+  int fz_b0 = 0;                     // radix of the fast path's stage 0 (d = fz_b0 * 256)
   int fz_nb = 0;
   float* fz0 = nullptr;
   float* fz0f = nullptr;             // the same blocks in MFMA fragment order (fused.h)

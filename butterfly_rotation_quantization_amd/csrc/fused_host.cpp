@@ -14,9 +14,18 @@ void prof_end(int token, hipStream_t s);
 
 namespace {
 
-bool fused_shape(const Plan& p) {
-  return p.nst == 3 && p.radix[1] == 16 && p.radix[2] == 16 && p.radix[0] >= 2 &&
-         p.radix[0] <= 64;
+// Radix of stage 0 when the plan fits the fast path as (b0, 16, 16), else 0.
+// A Hadamard plan of any power-of-two radix schedule is the Sylvester matrix
+// H_d / sqrt(d) = (H_b0 / sqrt(b0)) x (H_16 / 4) x (H_16 / 4) in natural order,
+// so for d = 256 b0 it is taken as that three-stage schedule.
+int fused_b0(const Plan& p) {
+  if (p.mode == BRQ_HADAMARD) {
+    const int b0 = p.d / 256;
+    return p.d % 256 == 0 && b0 >= 2 && b0 <= 64 && (b0 & (b0 - 1)) == 0 ? b0 : 0;
+  }
+  const bool fits = p.nst == 3 && p.radix[1] == 16 && p.radix[2] == 16 && p.radix[0] >= 2 &&
+                    p.radix[0] <= 64;
+  return fits ? p.radix[0] : 0;
 }
 
 // Sylvester Hadamard block H_b / sqrt(b), row-major, H[j][k] = (-1)^popcount(j & k).
@@ -33,11 +42,11 @@ void hadamard_block(int b, float* out) {
 // i = k*S_0 + c (S_0 = 256), so (B_0 D) restricted to group c is
 // B_{0,c} diag(s[k*256 + c]): column k of the block times that sign.
 hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_signs) {
-  if (!fused_shape(p)) return hipSuccess;
-  const int b0 = p.radix[0];
+  const int b0 = fused_b0(p);
+  if (!b0) return hipSuccess;
   const int nb = (b0 + 15) / 16;
   const int np = 16 * nb;
-  const int S0 = p.stride[0];  // 256
+  const int S0 = 256;  // stride of stage 0 in the (b0, 16, 16) schedule
   const bool shared_src = p.mode != BRQ_PER_GROUP;
   const bool per_group = !shared_src || host_signs;
   const int ng0 = per_group ? S0 : 1;
@@ -71,6 +80,7 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
   if (e == hipSuccess) e = rt_malloc((void**)&p.fz0f, frag.size() * sizeof(float));
   if (e == hipSuccess) e = rt_copy_to_device(p.fz0f, frag.data(), frag.size() * sizeof(float));
   if (e != hipSuccess) return e;
+  p.fz_b0 = b0;
   p.fz_nb = nb;
   p.fz_gs0 = per_group ? (int64_t)np * np : 0;
   if (p.mode == BRQ_HADAMARD) {
@@ -145,6 +155,7 @@ void fused_release(Plan& p) {
   rt_free(p.fz_had);
   p.fz0 = p.fz0f = p.fz_had = nullptr;
   p.fz_ok = 0;
+  p.fz_b0 = 0;
 }
 
 bool fused_rotate_supported(const Plan*, const Plan*, int, int, int64_t, int64_t, int64_t, int64_t,
@@ -163,7 +174,7 @@ hipError_t fused_rotate(const Plan*, const Plan*, const void*, int, int64_t, voi
 bool fused_rqp_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_t n, int64_t ldw,
                          const void* w, const brq_quant* q) {
   if (!U || !V || !U->fz_ok || !V->fz_ok) return false;
-  if (U->radix[0] != 16 || U->d != m || n % V->d) return false;
+  if (U->fz_b0 != 16 || U->d != m || n % V->d) return false;
   if (q->group != 64 && q->group != 128) return false;
   if ((n * q->bits) % 32) return false;
   const int elem = wt == BRQ_F32 ? 4 : 2;
@@ -187,7 +198,7 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.ws = static_cast<float*>(ws);
   a.m = m;
   a.n = n;
-  a.bv = V->radix[0];
+  a.bv = V->fz_b0;
   a.nb = V->fz_nb;
   a.dv = V->d;
   a.nchunk = (int)(n / V->d);

@@ -72,7 +72,12 @@ def test_llama7b_two_sided_rht(bits):
     cfg = S.llama7b()
     w = to_dev(cfg["w"], "bf16")
     U, V = lib_plan(cfg["left"]), lib_plan(cfg["right"])
+    brq.profile_reset()
+    brq.profile_enable(True)
     codes, scales = brq.rotate_quantize_pack(U, V, w, bits, 128)
+    brq.profile_enable(False)
+    # radix-2^12 Hadamard plans take the two-kernel fast path as (16,16,16)
+    assert all(k.startswith("fused") for k in brq.profile_read()), brq.profile_read()
     Uo, Vo = orc_plan(cfg["left"]), orc_plan(cfg["right"])
     w64 = S.storage_to_f64(cfg["w"], "bf16")
     rows = sampled_rows(4096, 512, 7 + bits)
