@@ -12,6 +12,7 @@
 
 #include "brq_internal.h"
 #include "fused.h"
+#include "rowhad.h"
 
 struct brq_plan {
   brq::Plan p;
@@ -453,6 +454,10 @@ brq_status rotate_common(const brq_plan* plan, int32_t side, int inverse, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Plan* U = side == 1 ? p : nullptr;
   const Plan* V = side == 0 ? p : nullptr;
+  if (rh_rotate_supported(p, side, xt, yt, rows, cols, ldx, ldy, x, y)) {
+    st = rh_rotate(p, inverse, x, xt, ldx, y, yt, ldy, rows, cols, s);
+    return st == BRQ_OK ? st : hip_fail(hipGetLastError(), "row Hadamard launch");
+  }
   if (!inverse && fused_rotate_supported(U, V, xt, yt, rows, cols, ldx, ldy, x, y))
     return fused_rotate(U, V, x, xt, ldx, y, yt, ldy, rows, cols, s) == hipSuccess
                ? BRQ_OK
@@ -652,6 +657,11 @@ brq_status brq_rotate_quantize_pack(const brq_plan* left, const brq_plan* right,
     st = fused_rqp(U, V, w, wt, m, n, ldw, q, codes, scales, ws, ws_bytes, s);
     if (st != BRQ_ERR_UNSUPPORTED) return st;
   }
+  if (rh_quant_supported(U, V, wt, n, ldw, w, q)) {
+    st = rh_rqp(V, w, wt, m, n, ldw, q, codes, scales, s);
+    if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "row Hadamard launch");
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+  }
   return run_forward(U, V, w, wt, ldw, m, n, nullptr, 0, 0, q, codes, scales, ws, ws_bytes, s);
 }
 
@@ -675,6 +685,11 @@ brq_status brq_dequant_unrotate(const brq_plan* left, const brq_plan* right, con
   if (!codes || !scales || !out) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
   if ((st = check_plan_device(U)) != BRQ_OK) return st;
   if ((st = check_plan_device(V)) != BRQ_OK) return st;
+  if (!U && rh_plan_ok(V) && q->group <= 1024) {
+    st = rh_dequant(V, codes, scales, q, m, n, out, ot, ldo, static_cast<hipStream_t>(stream));
+    if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "row Hadamard launch");
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+  }
   return run_inverse(U, V, nullptr, 0, 0, codes, scales, q, m, n, out, ot, ldo, ws, ws_bytes,
                      static_cast<hipStream_t>(stream));
 }

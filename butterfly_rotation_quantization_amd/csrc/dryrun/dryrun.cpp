@@ -409,3 +409,119 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
 }
 
 }  // namespace brq
+
+// ---------------------------------------------------------------- row Hadamard
+
+#include "rowhad.h"
+
+namespace brq {
+
+hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
+  ++g_launches;
+  const int l2d = a.log2d, d = 1 << l2d, R = rh_rounds(l2d);
+  if (l2d < 4 || l2d > 12 || a.n % d || a.cpr != a.n / d || a.nchunks != a.rows * a.cpr)
+    return violation("row Hadamard shape (d %lld, n %lld)", d, a.n), hipErrorInvalidValue;
+  {  // the rounds' new bits partition the index bits; each round's layout is a bijection
+    unsigned done = 0;
+    for (int r = 0; r < R; ++r)
+      for (int q = 4 - rh_nnew(l2d, r); q < 4; ++q) {
+        const int bit = rh_regbit(l2d, r, q);
+        if (bit < 4 * r || bit >= l2d || ((done >> bit) & 1))
+          return violation("round %lld transforms bit %lld twice or out of range", r, bit), hipErrorInvalidValue;
+        done |= 1u << bit;
+      }
+    if (done != (l2d == 32 ? ~0u : (1u << l2d) - 1))
+      return violation("rounds leave bits untransformed", 0, 0), hipErrorInvalidValue;
+    for (int r = 0; r < R; ++r) {
+      std::vector<uint8_t> seen(d, 0);
+      for (int cu = 0; cu < d / 16; ++cu)
+        for (int j = 0; j < 16; ++j) {
+          const int e = rh_elem(l2d, r, cu, j);
+          if (e < 0 || e >= d || seen[e]++) return violation("round %lld layout is not a bijection (%lld)", r, e), hipErrorInvalidValue;
+          for (int q = 0; q < 4; ++q)
+            if (((e >> rh_regbit(l2d, r, q)) & 1) != ((j >> q) & 1))
+              return violation("register bit %lld of round %lld", q, r), hipErrorInvalidValue;
+        }
+      for (int cu = 0; cu < d / 16; ++cu)
+        for (int j = 0; j < 16; ++j)
+          if (rh_elem(l2d, 0, cu, j) != 16 * cu + j)
+            return violation("round 0 is not natural order (%lld, %lld)", cu, j), hipErrorInvalidValue;
+    }
+    std::vector<int> slot(kRhLds);
+    for (int r = 0; r < R && R > 1; ++r) {
+      std::fill(slot.begin(), slot.end(), -1);
+      for (int u = 0; u < kRhThreads; ++u) {
+        const int cw = u >> (l2d - 4), cu = u & ((1 << (l2d - 4)) - 1);
+        for (int j = 0; j < 16; ++j) {
+          const int e = rh_elem(l2d, r, cu, j);
+          const int s = rh_lds(l2d, cw, e);
+          if (s < 0 || s >= kRhLds || slot[s] != -1) return violation("LDS slot %lld written twice", s, r), hipErrorInvalidValue;
+          slot[s] = (cw << l2d) + e;
+        }
+      }
+      const int rn = r + 1 < R ? r + 1 : 0;
+      for (int u = 0; u < kRhThreads; ++u) {
+        const int cw = u >> (l2d - 4), cu = u & ((1 << (l2d - 4)) - 1);
+        for (int j = 0; j < 16; ++j) {
+          const int e = rh_elem(l2d, rn, cu, j);
+          const int s = rh_lds(l2d, cw, e);
+          if (s < 0 || s >= kRhLds || slot[s] != (cw << l2d) + e)
+            return violation("LDS read of slot %lld in round %lld", s, r), hipErrorInvalidValue;
+        }
+      }
+    }
+  }
+  const int64_t nwg = rh_nwg(a);
+  const int esz_x = a.xt == BRQ_F32 ? 4 : 2, esz_y = a.yt == BRQ_F32 ? 4 : 2;
+  std::vector<uint8_t> cover((size_t)(a.rows * a.n), 0);
+  std::vector<uint8_t> scov;
+  if (a.mode == RH_QUANT) scov.assign((size_t)(a.rows * a.scales_ld), 0);
+  const int lpg = a.mode == RH_QUANT ? a.group / 16 : 1;
+  if (a.mode == RH_QUANT && (a.group % 16 || lpg > 64 || (lpg & (lpg - 1)) || kRhTile % a.group))
+    return violation("quantizer group %lld", a.group, 0), hipErrorInvalidValue;
+  for (int64_t b = 0; b < nwg; ++b)
+    for (int u = 0; u < kRhThreads; ++u) {
+      const RhPos p = rh_pos(a, b, u);
+      if (!p.live) continue;
+      if (p.row >= a.rows || p.col0 < 0 || p.col0 + 16 > a.n || p.col0 % 16)
+        return violation("row Hadamard element (%lld, %lld)", p.row, p.col0), hipErrorInvalidValue;
+      if (p.col0 % d != 16 * p.cu) return violation("chunk position of thread %lld", u, 0), hipErrorInvalidValue;
+      if (a.mode != RH_DEQUANT) {
+        const int64_t off = p.row * a.ldx + p.col0;
+        if (p.col0 + 16 > a.ldx || (off * esz_x) % 16) return violation("row Hadamard load %lld", off, 0), hipErrorInvalidValue;
+      } else {
+        const int64_t off = p.row * a.codes_ld + p.col0 * a.bits / 8;
+        if (!in_range(off, 2 * a.bits, a.rows * a.codes_ld) || off % ((a.bits & 1) ? 2 : 4))
+          return violation("code read at %lld", off, 0), hipErrorInvalidValue;
+        if (!in_range(p.row * a.scales_ld + p.col0 / a.group, 1, a.rows * a.scales_ld))
+          return violation("scale read (%lld, %lld)", p.row, p.col0), hipErrorInvalidValue;
+      }
+      if (a.mode != RH_QUANT) {
+        const int64_t off = p.row * a.ldy + p.col0;
+        if (p.col0 + 16 > a.ldy || (off * esz_y) % 16) return violation("row Hadamard store %lld", off, 0), hipErrorInvalidValue;
+      } else {
+        const int64_t off = p.row * a.codes_ld + p.col0 * a.bits / 8;
+        if (!in_range(off, 2 * a.bits, a.rows * a.codes_ld) || off % ((a.bits & 1) ? 2 : 4))
+          return violation("code write at %lld", off, 0), hipErrorInvalidValue;
+        if (u % lpg == 0) {  // the group's lanes: same wave, same row, contiguous columns
+          if (p.col0 % a.group) return violation("group start column %lld", p.col0, 0), hipErrorInvalidValue;
+          for (int k = 1; k < lpg; ++k) {
+            const RhPos o = rh_pos(a, b, u + k);
+            if ((u + k) / 64 != u / 64 || !o.live || o.row != p.row || o.col0 != p.col0 + 16 * k)
+              return violation("group lanes of thread %lld (lane +%lld)", u, k), hipErrorInvalidValue;
+          }
+          const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
+          if (!in_range(sidx, 1, a.rows * a.scales_ld) || scov[(size_t)sidx]++)
+            return violation("scale %lld written twice or out of range", sidx, 0), hipErrorInvalidValue;
+        }
+      }
+      for (int j = 0; j < 16; ++j) cover[(size_t)(p.row * a.n + p.col0 + j)]++;
+    }
+  for (size_t i = 0; i < cover.size(); ++i)
+    if (cover[i] != 1) return violation("row Hadamard element %lld covered %lld times", (int64_t)i, cover[i]), hipErrorInvalidValue;
+  for (size_t i = 0; i < scov.size(); ++i)
+    if (scov[i] != 1) return violation("scale %lld written %lld times", (int64_t)i, scov[i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+}  // namespace brq

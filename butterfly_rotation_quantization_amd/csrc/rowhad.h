@@ -1,0 +1,136 @@
+// Row Hadamard path: right-side Hadamard plans (d = 2^k, 16 <= d <= 4096)
+// applied to every d-chunk of every row in one pass, for rotate, for
+// rotate + quantize + pack, and for dequantize + unrotate.
+//
+// A workgroup of 256 threads holds 4096 consecutive chunk elements (4096 / d
+// chunks), 16 per thread.  The fast Walsh-Hadamard transform runs in rounds:
+// in each round the 16 registers of a thread hold elements whose indices
+// differ in four (or, in the last round, fewer) bits not yet transformed, the
+// radix-2 stages on those bits are butterflies between registers, and an LDS
+// transpose brings the next four bits into the registers.  A last transpose
+// restores natural order (thread t holds elements 16 t .. 16 t + 15), which
+// makes global loads and stores contiguous and keeps quantizer groups on
+// consecutive lanes.
+//
+// The index arithmetic lives here as __host__ __device__ functions so the
+// dry run checks exactly what the GPU executes.
+#pragma once
+
+#include "brq_internal.h"
+
+namespace brq {
+
+constexpr int kRhThreads = 256;
+constexpr int kRhElems = 16;                     // per thread
+constexpr int kRhTile = kRhThreads * kRhElems;   // chunk elements per workgroup
+constexpr int kRhLds = kRhTile + kRhTile / 16;   // one LDS buffer (padded)
+
+enum RhMode { RH_ROTATE = 0, RH_QUANT = 1, RH_DEQUANT = 2 };
+
+struct RhArgs {
+  int log2d;          // chunk length d = 2^log2d
+  int mode;           // RhMode
+  int64_t rows, n;    // matrix shape, n % d == 0
+  int64_t nchunks;    // rows * cpr
+  int64_t cpr;        // chunks per row, n / d
+  const void* x;      // input [rows][ldx] of type xt (rotate, quantize)
+  int xt;
+  int64_t ldx;
+  void* y;            // output [rows][ldy] of type yt (rotate, dequantize)
+  int yt;
+  int64_t ldy;
+  const float* signs; // d signs (+-1) of the plan, or null
+  int inverse;        // apply M^T: signs after the transform instead of before
+  float scale;        // 1 / sqrt(d)
+  // quantizer (quantize epilogue, dequantize prologue)
+  int qkind, bits, group, nlev;
+  float h, sqrt_g;
+  float tau[kMaxLevels];   // decision thresholds (codebook)
+  float cent[kMaxLevels];  // centroids (codebook dequantize)
+  uint8_t* codes;
+  const uint8_t* in_codes;
+  void* scales;
+  const void* in_scales;
+  int64_t codes_ld, scales_ld;
+};
+
+__host__ __device__ constexpr int rh_rounds(int l2d) { return (l2d + 3) / 4; }
+// Bits of the element index transformed in round r: [4r, 4r + rh_nnew).
+__host__ __device__ constexpr int rh_nnew(int l2d, int r) {
+  return (4 * r + 4 < l2d ? 4 * r + 4 : l2d) - 4 * r;
+}
+// Element-index bit held by register bit q in round r: the top rh_nnew bits of
+// the register index are the round's new bits, the others the lowest bits.
+__host__ __device__ constexpr int rh_regbit(int l2d, int r, int q) {
+  return q < 4 - rh_nnew(l2d, r) ? q : 4 * r + (q - (4 - rh_nnew(l2d, r)));
+}
+// Index within its chunk of the element that thread cu of the chunk holds in
+// register j during round r; the thread index fills the remaining bits in
+// increasing order.  Round 0 is natural order: 16 cu + j.
+__host__ __device__ inline int rh_elem(int l2d, int r, int cu, int j) {
+  int i = 0;
+  unsigned used = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int p = rh_regbit(l2d, r, q);
+    i |= ((j >> q) & 1) << p;
+    used |= 1u << p;
+  }
+  int t = cu;
+  for (int p = 0; p < l2d; ++p)
+    if (!((used >> p) & 1)) {
+      i |= (t & 1) << p;
+      t >>= 1;
+    }
+  return i;
+}
+// Padded LDS slot of element i of chunk cw: one float of padding per 16 spreads
+// the strided accesses of the later rounds over the banks.
+__host__ __device__ inline int rh_lds(int l2d, int cw, int i) {
+  const int x = (cw << l2d) + i;
+  return x + (x >> 4);
+}
+
+__host__ __device__ inline int64_t rh_nwg(const RhArgs& a) {
+  const int64_t cpw = kRhTile >> a.log2d;
+  return (a.nchunks + cpw - 1) / cpw;
+}
+
+// Thread u of workgroup b: chunk cw of the workgroup, thread cu of the chunk,
+// global chunk c (live when c < nchunks), its row and the row column of the
+// thread's first element in natural order.
+struct RhPos {
+  int cw, cu;
+  int64_t c, row, col0;
+  bool live;
+};
+__host__ __device__ inline RhPos rh_pos(const RhArgs& a, int64_t b, int u) {
+  RhPos p;
+  const int tpc = 1 << (a.log2d - 4);
+  p.cw = u / tpc;
+  p.cu = u - p.cw * tpc;
+  p.c = b * (kRhTile >> a.log2d) + p.cw;
+  p.live = p.c < a.nchunks;
+  p.row = p.live ? p.c / a.cpr : 0;
+  p.col0 = p.live ? (p.c - p.row * a.cpr) * ((int64_t)1 << a.log2d) + 16 * p.cu : 0;
+  return p;
+}
+
+// Whether the row Hadamard path takes this plan.
+inline bool rh_plan_ok(const Plan* p) {
+  return p && p->mode == BRQ_HADAMARD && p->d >= 16 && p->d <= 4096 && (p->d & (p->d - 1)) == 0;
+}
+
+hipError_t launch_rowhad(const RhArgs& a, hipStream_t s);
+
+bool rh_rotate_supported(const Plan* p, int side, int xt, int yt, int64_t rows, int64_t cols,
+                         int64_t ldx, int64_t ldy, const void* x, const void* y);
+brq_status rh_rotate(const Plan* p, int inverse, const void* x, int xt, int64_t ldx, void* y,
+                     int yt, int64_t ldy, int64_t rows, int64_t cols, hipStream_t s);
+bool rh_quant_supported(const Plan* U, const Plan* V, int wt, int64_t n, int64_t ldw,
+                        const void* w, const brq_quant* q);
+brq_status rh_rqp(const Plan* V, const void* w, int wt, int64_t m, int64_t n, int64_t ldw,
+                  const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s);
+brq_status rh_dequant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q,
+                      int64_t m, int64_t n, void* out, int ot, int64_t ldo, hipStream_t s);
+
+}  // namespace brq

@@ -1,0 +1,305 @@
+// Row Hadamard kernels (see rowhad.h for the data movement).
+//
+// Transform ([RHT] randomised Hadamard transform; [HARP] technical summary
+// 2.1 with Sylvester blocks): each d-chunk x of a row becomes
+// H_d D x / sqrt(d), with D the plan's signs and H_d[i][k] = (-1)^popcount(i&k).
+// H_d is a product of radix-2 stages, one per index bit; the stage on bit p
+// maps the pair (x[i], x[i + 2^p]) (bit p of i clear) to their sum and
+// difference, and the stages commute.  The inverse is D H_d / sqrt(d).
+//
+// Quantizers ([HARP] and [PolarQuant] pages; the same formulas as the tile
+// pass): absmax codes rint(v * h / alpha + h) clamped to [0, 2^b - 1] with
+// h = (2^b - 1) / 2 and fp32 alpha = max |v| per group; the norm codebook maps
+// z = v * sqrt(g) / r to the number of thresholds below it, r the group's
+// 2-norm stored as fp16.
+#include <utility>
+
+#include "rowhad.h"
+
+namespace brq {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t to_f16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// 16 consecutive elements (16-byte aligned) as float.
+__device__ __forceinline__ void load16(const void* base, int t, int64_t off, float (&v)[16]) {
+  if (t == BRQ_F32) {
+    const f4* p = reinterpret_cast<const f4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f4 x = p[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 x = p[q];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * q + 2 * e] = t == BRQ_BF16 ? bf16_lo(w[e]) : f16_lo(w[e]);
+        v[8 * q + 2 * e + 1] = t == BRQ_BF16 ? bf16_hi(w[e]) : f16_hi(w[e]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store16(void* base, int t, int64_t off, const float (&v)[16]) {
+  if (t == BRQ_F32) {
+    f4* p = reinterpret_cast<f4*>(static_cast<float*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = f4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  } else {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = v[8 * q + 2 * e], hi = v[8 * q + 2 * e + 1];
+        w[e] = t == BRQ_BF16 ? (to_bf16(lo) | (to_bf16(hi) << 16)) : (to_f16(lo) | (to_f16(hi) << 16));
+      }
+      p[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Radix-2 stages on register bits [q0, 4): butterflies between registers
+// (q0 is a constant once the round loop is unrolled).
+__device__ __forceinline__ void butterflies(float (&v)[16], int q0) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q >= q0)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (!((j >> q) & 1)) {
+        const float a = v[j], b = v[j | (1 << q)];
+        v[j] = a + b;
+        v[j | (1 << q)] = a - b;
+      }
+}
+
+// Reduction over the lanes of one quantizer group (LPG consecutive lanes).
+template <int LPG>
+__device__ __forceinline__ float group_max(float x) {
+#pragma unroll
+  for (int m = 1; m < LPG; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+template <int LPG>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < LPG; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// The 16 codes of one thread: 2 * bits bytes at a 2 * bits-aligned offset.
+__device__ __forceinline__ void store_codes(uint8_t* p, int bits, const uint32_t (&c)[16]) {
+  uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int bit = j * bits, wi = bit >> 5, sh = bit & 31;
+    w[wi] |= c[j] << sh;
+    if (sh + bits > 32) w[wi + 1] |= c[j] >> (32 - sh);
+  }
+  if ((bits & 1) == 0) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    for (int k = 0; k < bits / 2; ++k) q[k] = w[k];
+  } else {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+    for (int k = 0; k < bits; ++k) q[k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+  }
+}
+
+__device__ __forceinline__ void load_codes(const uint8_t* p, int bits, uint32_t (&c)[16]) {
+  uint32_t w[3] = {0u, 0u, 0u};
+  if ((bits & 1) == 0) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    for (int k = 0; k < bits / 2; ++k) w[k] = q[k];
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    for (int k = 0; k < bits; ++k) w[k >> 1] |= (uint32_t)q[k] << (16 * (k & 1));
+  }
+  const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int bit = j * bits, wi = bit >> 5, sh = bit & 31;
+    uint32_t x = w[wi] >> sh;
+    if (sh + bits > 32) x |= w[wi + 1] << (32 - sh);
+    c[j] = x & mask;
+  }
+}
+
+template <int L2D, int MODE, int LPG>
+__global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
+  __shared__ float lds[2][kRhLds];
+  constexpr int R = rh_rounds(L2D);
+  const RhPos p = rh_pos(a, blockIdx.x, threadIdx.x);
+  float v[16];
+
+  // ---- prologue: load or unpack + dequantize, then the signs (forward)
+  if (MODE != RH_DEQUANT) {
+    if (p.live) load16(a.x, a.xt, p.row * a.ldx + p.col0, v);
+    else
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 0.f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    if (p.live) {
+      uint32_t c[16];
+      load_codes(a.in_codes + p.row * a.codes_ld + p.col0 * a.bits / 8, a.bits, c);
+      const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
+      if (a.qkind == BRQ_ABSMAX) {
+        const float alpha = static_cast<const float*>(a.in_scales)[sidx];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = alpha * ((float)c[j] / a.h - 1.0f);
+      } else {
+        const float r = (float)static_cast<const _Float16*>(a.in_scales)[sidx];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = r * a.cent[c[j]] / a.sqrt_g;
+      }
+    }
+  }
+  if (!a.inverse && a.signs)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] *= a.signs[16 * p.cu + j];
+
+  // ---- transform: per round, butterflies on its new bits, then an LDS
+  // transpose to the next round's layout (the last one back to natural order)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    butterflies(v, 4 - rh_nnew(L2D, r));
+    if (R > 1) {
+      float* buf = lds[r & 1];
+      const int rn = r + 1 < R ? r + 1 : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) buf[rh_lds(L2D, p.cw, rh_elem(L2D, r, p.cu, j))] = v[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = buf[rh_lds(L2D, p.cw, rh_elem(L2D, rn, p.cu, j))];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] *= a.scale;
+  if (a.inverse && a.signs)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] *= a.signs[16 * p.cu + j];
+
+  // ---- epilogue
+  if (MODE != RH_QUANT) {
+    if (p.live) store16(a.y, a.yt, p.row * a.ldy + p.col0, v);
+    return;
+  }
+  // quantizer groups of g = 16 LPG consecutive columns are LPG consecutive lanes
+  float stat = 0.f;
+  if (a.qkind == BRQ_ABSMAX) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) stat = fmaxf(stat, fabsf(v[j]));
+    stat = group_max<LPG>(stat);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) stat = fmaf(v[j], v[j], stat);
+    stat = sqrtf(group_sum<LPG>(stat));
+  }
+  if (!p.live) return;
+  const int lv = a.nlev - 1;
+  uint32_t c[16];
+  if (a.qkind == BRQ_ABSMAX) {
+    const float k = stat > 0.f ? a.h / stat : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int q = 0;
+      if (stat > 0.f) {
+        q = (int)rintf(fmaf(v[j], k, a.h));
+        q = q < 0 ? 0 : (q > lv ? lv : q);
+      }
+      c[j] = (uint32_t)q;
+    }
+  } else {
+    const float k = stat > 0.f ? a.sqrt_g / stat : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int q = 0;
+      if (stat > 0.f) {
+        const float z = v[j] * k;
+        for (int t = 0; t < lv; ++t) q += (z > a.tau[t]) ? 1 : 0;
+      }
+      c[j] = (uint32_t)q;
+    }
+  }
+  store_codes(a.codes + p.row * a.codes_ld + p.col0 * a.bits / 8, a.bits, c);
+  if ((threadIdx.x & (LPG - 1)) == 0) {
+    const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
+    if (a.qkind == BRQ_ABSMAX) static_cast<float*>(a.scales)[sidx] = stat;
+    else static_cast<_Float16*>(a.scales)[sidx] = (_Float16)stat;
+  }
+}
+
+template <int L2D, int MODE, int LPG>
+hipError_t launch_t(const RhArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((rowhad_kernel<L2D, MODE, LPG>), dim3((unsigned)rh_nwg(a)), dim3(kRhThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+template <int L2D, int MODE>
+hipError_t launch_lpg(const RhArgs& a, hipStream_t s) {
+  if (MODE != RH_QUANT) return launch_t<L2D, MODE, 1>(a, s);
+  switch (a.group) {
+    case 16: return launch_t<L2D, MODE, 1>(a, s);
+    case 32: return launch_t<L2D, MODE, 2>(a, s);
+    case 64: return launch_t<L2D, MODE, 4>(a, s);
+    case 128: return launch_t<L2D, MODE, 8>(a, s);
+    case 256: return launch_t<L2D, MODE, 16>(a, s);
+    case 512: return launch_t<L2D, MODE, 32>(a, s);
+    case 1024: return launch_t<L2D, MODE, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int L2D>
+hipError_t launch_mode(const RhArgs& a, hipStream_t s) {
+  if (a.mode == RH_ROTATE) return launch_lpg<L2D, RH_ROTATE>(a, s);
+  if (a.mode == RH_QUANT) return launch_lpg<L2D, RH_QUANT>(a, s);
+  return launch_lpg<L2D, RH_DEQUANT>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_rowhad(const RhArgs& a, hipStream_t s) {
+  switch (a.log2d) {
+    case 4: return launch_mode<4>(a, s);
+    case 5: return launch_mode<5>(a, s);
+    case 6: return launch_mode<6>(a, s);
+    case 7: return launch_mode<7>(a, s);
+    case 8: return launch_mode<8>(a, s);
+    case 9: return launch_mode<9>(a, s);
+    case 10: return launch_mode<10>(a, s);
+    case 11: return launch_mode<11>(a, s);
+    case 12: return launch_mode<12>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace brq

@@ -157,3 +157,29 @@ def test_fused_two_sided_launches(dl, bv, mode, chunks, bits, group, wt):
                                      WS, ws, None)
     _ok(dl, st, f"fused bv={bv} {mode}")
     assert dl.brq_dryrun_launches() == 2
+
+
+# The row Hadamard path: one launch per call, for every chunk length it
+# takes, with partial last workgroups, every dtype pair and group size.
+@pytest.mark.parametrize("l2d,rows,cpr", [(4, 33, 2), (5, 129, 3), (7, 50, 4), (8, 17, 2),
+                                           (10, 9, 2), (11, 6, 1), (12, 37, 1), (12, 3, 2),
+                                           (7, 12288, 32)])
+def test_rowhad_launches(dl, l2d, rows, cpr):
+    d = 1 << l2d
+    rng = np.random.default_rng(l2d)
+    p = DPlan(dl, S.SidePlan(d, (2,) * l2d, "hadamard", None, S.signs(rng, d)))
+    n = cpr * d
+    for xt, yt in ((0, 0), (1, 1), (2, 2), (1, 0), (0, 2)):
+        for inverse in (False, True):
+            dl.brq_dryrun_reset()
+            fn = dl.brq_rotate_inverse if inverse else dl.brq_rotate
+            st = fn(p.h, 0, X, xt, n, Y, yt, n, rows, n, None, 0, None)
+            _ok(dl, st, f"rowhad rotate d={d} {xt}->{yt} inverse={inverse}")
+            assert dl.brq_dryrun_launches() == 1
+    for bits in (2, 3, 4, 5):
+        for group in (64, 128, 256, 512, 1024):
+            if n % group:
+                continue
+            for kind in (0, 1):
+                _rqp(dl, None, p, rows, n, bits, group, kind)
+                assert dl.brq_dryrun_launches() == 1
