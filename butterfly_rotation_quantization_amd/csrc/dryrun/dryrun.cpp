@@ -3,6 +3,7 @@
 // the extents of its buffers.  Built as libbrq_dryrun.so for CPU tests; it
 // never touches a GPU.  Device pointers passed to it are never dereferenced.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -469,6 +470,16 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
             return violation("LDS read of slot %lld in round %lld", s, r), hipErrorInvalidValue;
         }
       }
+    }
+  }
+  if (a.mode == RH_QUANT && a.qkind == BRQ_CODEBOOK_NORM && a.bin_s != 0.f) {
+    // the codebook bins: each threshold alone in a bin strictly inside the clamp range
+    int prev = 0;
+    for (int k = 0; k + 1 < a.nlev; ++k) {
+      const int b = rh_bin(std::fma(a.tau[k], a.bin_s, a.bin_off));
+      if (b <= prev || b >= kRhBins - 1)
+        return violation("codebook threshold %lld in bin %lld", k, b), hipErrorInvalidValue;
+      prev = b;
     }
   }
   const int64_t nwg = rh_nwg(a);

@@ -24,6 +24,7 @@ constexpr int kRhThreads = 256;
 constexpr int kRhElems = 16;                     // per thread
 constexpr int kRhTile = kRhThreads * kRhElems;   // chunk elements per workgroup
 constexpr int kRhLds = kRhTile + kRhTile / 16;   // one LDS buffer (padded)
+constexpr int kRhBins = 256;                     // codebook search bins
 
 enum RhMode { RH_ROTATE = 0, RH_QUANT = 1, RH_DEQUANT = 2 };
 
@@ -47,6 +48,12 @@ struct RhArgs {
   float h, sqrt_g;
   float tau[kMaxLevels];   // decision thresholds (codebook)
   float cent[kMaxLevels];  // centroids (codebook dequantize)
+  // Codebook search by bins: u = fma(z, bin_s, bin_off) falls in bin
+  // floor(u) (clamped to [0, kRhBins)); every threshold's u lies at least
+  // 1/64 from an integer and no bin holds two, so the code is the number of
+  // thresholds of the bins below plus (z > the bin's own threshold).  The host
+  // checks this and sets bin_s = 0 when no such scaling exists.
+  float bin_s, bin_off;
   uint8_t* codes;
   const uint8_t* in_codes;
   void* scales;
@@ -88,6 +95,12 @@ __host__ __device__ inline int rh_elem(int l2d, int r, int cu, int j) {
 __host__ __device__ inline int rh_lds(int l2d, int cw, int i) {
   const int x = (cw << l2d) + i;
   return x + (x >> 4);
+}
+
+// Bin of a scaled value (the kernel's arithmetic, shared with the host check).
+__host__ __device__ inline int rh_bin(float u) {
+  const float c = u < 0.f ? 0.f : (u > (float)(kRhBins - 1) ? (float)(kRhBins - 1) : u);
+  return (int)c;
 }
 
 __host__ __device__ inline int64_t rh_nwg(const RhArgs& a) {

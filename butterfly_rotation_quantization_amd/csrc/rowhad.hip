@@ -99,60 +99,65 @@ __device__ __forceinline__ void butterflies(float (&v)[16], int q0) {
       }
 }
 
-// Reduction over the lanes of one quantizer group (LPG consecutive lanes).
-template <int LPG>
-__device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-  for (int m = 1; m < LPG; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+// Reduction over the lanes of one quantizer group (lpg consecutive lanes).
+__device__ __forceinline__ float group_max(float x, int lpg) {
+  for (int m = 1; m < lpg; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
   return x;
 }
-template <int LPG>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < LPG; m <<= 1) x += __shfl_xor(x, m, 64);
+__device__ __forceinline__ float group_sum(float x, int lpg) {
+  for (int m = 1; m < lpg; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
 }
 
-// The 16 codes of one thread: 2 * bits bytes at a 2 * bits-aligned offset.
-__device__ __forceinline__ void store_codes(uint8_t* p, int bits, const uint32_t (&c)[16]) {
+// The 16 codes of one thread: 2 * BITS bytes at a 2 * BITS-aligned offset.
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[16]) {
   uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int bit = j * bits, wi = bit >> 5, sh = bit & 31;
+    const int bit = j * BITS, wi = bit >> 5, sh = bit & 31;
     w[wi] |= c[j] << sh;
-    if (sh + bits > 32) w[wi + 1] |= c[j] >> (32 - sh);
+    if (sh + BITS > 32) w[wi + 1] |= c[j] >> (32 - sh);
   }
-  if ((bits & 1) == 0) {
+  if constexpr ((BITS & 1) == 0) {
     uint32_t* q = reinterpret_cast<uint32_t*>(p);
-    for (int k = 0; k < bits / 2; ++k) q[k] = w[k];
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k) q[k] = w[k];
   } else {
     uint16_t* q = reinterpret_cast<uint16_t*>(p);
-    for (int k = 0; k < bits; ++k) q[k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) q[k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
   }
 }
 
-__device__ __forceinline__ void load_codes(const uint8_t* p, int bits, uint32_t (&c)[16]) {
+template <int BITS>
+__device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&c)[16]) {
   uint32_t w[3] = {0u, 0u, 0u};
-  if ((bits & 1) == 0) {
+  if constexpr ((BITS & 1) == 0) {
     const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    for (int k = 0; k < bits / 2; ++k) w[k] = q[k];
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k) w[k] = q[k];
   } else {
     const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-    for (int k = 0; k < bits; ++k) w[k >> 1] |= (uint32_t)q[k] << (16 * (k & 1));
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k >> 1] |= (uint32_t)q[k] << (16 * (k & 1));
   }
-  const uint32_t mask = (1u << bits) - 1u;
+  constexpr uint32_t mask = (1u << BITS) - 1u;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int bit = j * bits, wi = bit >> 5, sh = bit & 31;
+    const int bit = j * BITS, wi = bit >> 5, sh = bit & 31;
     uint32_t x = w[wi] >> sh;
-    if (sh + bits > 32) x |= w[wi + 1] << (32 - sh);
+    if (sh + BITS > 32) x |= w[wi + 1] << (32 - sh);
     c[j] = x & mask;
   }
 }
 
-template <int L2D, int MODE, int LPG>
+// BITS: the code width of the quantize and dequantize modes (0 for rotate).
+template <int L2D, int MODE, int BITS>
 __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   __shared__ float lds[2][kRhLds];
+  __shared__ int bin_cnt[MODE == RH_QUANT ? kRhBins : 1];
+  __shared__ float bin_tau[MODE == RH_QUANT ? kRhBins : 1];
   constexpr int R = rh_rounds(L2D);
   const RhPos p = rh_pos(a, blockIdx.x, threadIdx.x);
   float v[16];
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     for (int j = 0; j < 16; ++j) v[j] = 0.f;
     if (p.live) {
       uint32_t c[16];
-      load_codes(a.in_codes + p.row * a.codes_ld + p.col0 * a.bits / 8, a.bits, c);
+      load_codes<BITS>(a.in_codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
       const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
       if (a.qkind == BRQ_ABSMAX) {
         const float alpha = static_cast<const float*>(a.in_scales)[sidx];
@@ -211,19 +216,34 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     if (p.live) store16(a.y, a.yt, p.row * a.ldy + p.col0, v);
     return;
   }
-  // quantizer groups of g = 16 LPG consecutive columns are LPG consecutive lanes
+  // quantizer groups of g = 16 lpg consecutive columns are lpg consecutive lanes
+  const int lpg = a.group / 16;
+  const bool bins = a.qkind == BRQ_CODEBOOK_NORM && a.bin_s != 0.f;
+  if (bins) {  // bin b: thresholds in lower bins, and the one in b (or +inf)
+    const int b = threadIdx.x;
+    int cnt = 0;
+    float tin = __int_as_float(0x7f800000);
+    for (int k = 0; k + 1 < a.nlev; ++k) {
+      const int bk = rh_bin(fmaf(a.tau[k], a.bin_s, a.bin_off));
+      cnt += bk < b ? 1 : 0;
+      if (bk == b) tin = a.tau[k];
+    }
+    bin_cnt[b] = cnt;
+    bin_tau[b] = tin;
+    __syncthreads();
+  }
   float stat = 0.f;
   if (a.qkind == BRQ_ABSMAX) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) stat = fmaxf(stat, fabsf(v[j]));
-    stat = group_max<LPG>(stat);
+    stat = group_max(stat, lpg);
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) stat = fmaf(v[j], v[j], stat);
-    stat = sqrtf(group_sum<LPG>(stat));
+    stat = sqrtf(group_sum(stat, lpg));
   }
   if (!p.live) return;
-  const int lv = a.nlev - 1;
+  constexpr int LV = (1 << BITS) - 1;
   uint32_t c[16];
   if (a.qkind == BRQ_ABSMAX) {
     const float k = stat > 0.f ? a.h / stat : 0.f;
@@ -232,7 +252,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
       int q = 0;
       if (stat > 0.f) {
         q = (int)rintf(fmaf(v[j], k, a.h));
-        q = q < 0 ? 0 : (q > lv ? lv : q);
+        q = q < 0 ? 0 : (q > LV ? LV : q);
       }
       c[j] = (uint32_t)q;
     }
@@ -243,46 +263,48 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
       int q = 0;
       if (stat > 0.f) {
         const float z = v[j] * k;
-        for (int t = 0; t < lv; ++t) q += (z > a.tau[t]) ? 1 : 0;
+        if (bins) {
+          const int b = rh_bin(fmaf(z, a.bin_s, a.bin_off));
+          q = bin_cnt[b] + (z > bin_tau[b] ? 1 : 0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < LV; ++t) q += (z > a.tau[t]) ? 1 : 0;
+        }
       }
       c[j] = (uint32_t)q;
     }
   }
-  store_codes(a.codes + p.row * a.codes_ld + p.col0 * a.bits / 8, a.bits, c);
-  if ((threadIdx.x & (LPG - 1)) == 0) {
+  store_codes<BITS>(a.codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
+  if ((threadIdx.x & (lpg - 1)) == 0) {
     const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
     if (a.qkind == BRQ_ABSMAX) static_cast<float*>(a.scales)[sidx] = stat;
     else static_cast<_Float16*>(a.scales)[sidx] = (_Float16)stat;
   }
 }
 
-template <int L2D, int MODE, int LPG>
+template <int L2D, int MODE, int BITS>
 hipError_t launch_t(const RhArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rowhad_kernel<L2D, MODE, LPG>), dim3((unsigned)rh_nwg(a)), dim3(kRhThreads),
+  hipLaunchKernelGGL((rowhad_kernel<L2D, MODE, BITS>), dim3((unsigned)rh_nwg(a)), dim3(kRhThreads),
                      0, s, a);
   return hipGetLastError();
 }
 
 template <int L2D, int MODE>
-hipError_t launch_lpg(const RhArgs& a, hipStream_t s) {
-  if (MODE != RH_QUANT) return launch_t<L2D, MODE, 1>(a, s);
-  switch (a.group) {
-    case 16: return launch_t<L2D, MODE, 1>(a, s);
-    case 32: return launch_t<L2D, MODE, 2>(a, s);
-    case 64: return launch_t<L2D, MODE, 4>(a, s);
-    case 128: return launch_t<L2D, MODE, 8>(a, s);
-    case 256: return launch_t<L2D, MODE, 16>(a, s);
-    case 512: return launch_t<L2D, MODE, 32>(a, s);
-    case 1024: return launch_t<L2D, MODE, 64>(a, s);
+hipError_t launch_bits(const RhArgs& a, hipStream_t s) {
+  switch (a.bits) {
+    case 2: return launch_t<L2D, MODE, 2>(a, s);
+    case 3: return launch_t<L2D, MODE, 3>(a, s);
+    case 4: return launch_t<L2D, MODE, 4>(a, s);
+    case 5: return launch_t<L2D, MODE, 5>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int L2D>
 hipError_t launch_mode(const RhArgs& a, hipStream_t s) {
-  if (a.mode == RH_ROTATE) return launch_lpg<L2D, RH_ROTATE>(a, s);
-  if (a.mode == RH_QUANT) return launch_lpg<L2D, RH_QUANT>(a, s);
-  return launch_lpg<L2D, RH_DEQUANT>(a, s);
+  if (a.mode == RH_ROTATE) return launch_t<L2D, RH_ROTATE, 0>(a, s);
+  if (a.mode == RH_QUANT) return launch_bits<L2D, RH_QUANT>(a, s);
+  return launch_bits<L2D, RH_DEQUANT>(a, s);
 }
 
 }  // namespace

@@ -52,6 +52,32 @@ void fill_quant(RhArgs& a, const brq_quant* q, int64_t n) {
     for (int i = 0; i + 1 < a.nlev; ++i) a.tau[i] = (q->codebook[i] + q->codebook[i + 1]) * 0.5f;
   a.codes_ld = n * q->bits / 8;
   a.scales_ld = n / q->group;
+  a.bin_s = a.bin_off = 0.f;
+  if (q->kind != BRQ_CODEBOOK_NORM) return;
+  // Find a scaling that puts each threshold in its own bin, away from bin
+  // edges, in the kernel's fp32 arithmetic.
+  const int nt = a.nlev - 1;
+  const float lo = a.tau[0], hi = a.tau[nt - 1];
+  for (int tries = 0; tries < 64; ++tries) {
+    const float span = hi - lo;
+    const float s = (float)(kRhBins - 8) / (span > 0.f ? span : 1.f) / (1.f + 0.03125f * tries);
+    const float off = 4.f - lo * s + 0.37f * (float)tries;
+    bool ok = true;
+    int prev = -1;
+    for (int i = 0; i < nt && ok; ++i) {
+      const float u = std::fma(a.tau[i], s, off);
+      const int b = (int)std::floor(u);
+      const float f = u - (float)b;
+      ok = b >= 1 && b < kRhBins - 1 && b > prev && f > 1.f / 64 && f < 1.f - 1.f / 64 &&
+           rh_bin(u) == b;
+      prev = b;
+    }
+    if (ok) {
+      a.bin_s = s;
+      a.bin_off = off;
+      return;
+    }
+  }
 }
 
 brq_status launch(const RhArgs& a, const char* what, hipStream_t s) {
