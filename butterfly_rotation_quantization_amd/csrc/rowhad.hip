@@ -155,7 +155,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&c)[16]) 
 // BITS: the code width of the quantize and dequantize modes (0 for rotate).
 template <int L2D, int MODE, int BITS>
 __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
-  __shared__ float lds[2][kRhLds];
+  __shared__ float lds[kRhLds];  // one buffer: more workgroups per CU beat a saved barrier
   __shared__ int bin_cnt[MODE == RH_QUANT ? kRhBins : 1];
   __shared__ float bin_tau[MODE == RH_QUANT ? kRhBins : 1];
   constexpr int R = rh_rounds(L2D);
@@ -196,13 +196,13 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   for (int r = 0; r < R; ++r) {
     butterflies(v, 4 - rh_nnew(L2D, r));
     if (R > 1) {
-      float* buf = lds[r & 1];
       const int rn = r + 1 < R ? r + 1 : 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) buf[rh_lds(L2D, p.cw, rh_elem(L2D, r, p.cu, j))] = v[j];
+      for (int j = 0; j < 16; ++j) lds[rh_lds(L2D, p.cw, rh_elem(L2D, r, p.cu, j))] = v[j];
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = buf[rh_lds(L2D, p.cw, rh_elem(L2D, rn, p.cu, j))];
+      for (int j = 0; j < 16; ++j) v[j] = lds[rh_lds(L2D, p.cw, rh_elem(L2D, rn, p.cu, j))];
+      if (r + 1 < R) __syncthreads();  // every read is done before the next round's writes
     }
   }
 #pragma unroll
