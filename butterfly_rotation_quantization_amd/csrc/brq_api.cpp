@@ -13,6 +13,7 @@
 #include "brq_internal.h"
 #include "fused.h"
 #include "rowhad.h"
+#include "stage.h"
 
 struct brq_plan {
   brq::Plan p;
@@ -462,6 +463,15 @@ brq_status rotate_common(const brq_plan* plan, int32_t side, int inverse, const 
     return fused_rotate(U, V, x, xt, ldx, y, yt, ldy, rows, cols, s) == hipSuccess
                ? BRQ_OK
                : hip_fail(hipGetLastError(), "fused rotate launch");
+  if (sp_rotate_supported(p, side, rows, cols)) {
+    hipError_t he = hipSuccess;
+    st = sp_rotate(p, side, inverse, x, xt, ldx, y, yt, ldy, rows, cols, ws, ws_bytes, s, &he);
+    if (st == BRQ_ERR_HIP) return hip_fail(he, "stage pass launch");
+    if (st == BRQ_ERR_WORKSPACE)
+      return fail(st, "workspace of %zu bytes needed, %zu given",
+                  (size_t)rows * cols * sizeof(float), ws_bytes);
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+  }
   if (!inverse)
     return run_forward(U, V, x, xt, ldx, rows, cols, y, yt, ldy, nullptr, nullptr, nullptr, ws,
                        ws_bytes, s);

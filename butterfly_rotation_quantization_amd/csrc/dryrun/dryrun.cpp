@@ -536,3 +536,130 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
 }
 
 }  // namespace brq
+
+// ---------------------------------------------------------------- stage pass
+
+#include "stage.h"
+
+namespace brq {
+
+hipError_t launch_stage(const SpArgs& a, hipStream_t) {
+  ++g_launches;
+  const int b = a.b;
+  if (b < 2 || b > 64 || a.bp < b || (a.bp & (a.bp - 1)) || a.bp > 64 || a.bs < b || a.bs % 4 ||
+      a.bs - b >= 4 || a.gw < 1 || a.gw * a.bp > kSpThreads || a.gw * a.bs > kSpLineFloats)
+    return violation("stage pass geometry (b %lld, gw %lld)", b, a.gw), hipErrorInvalidValue;
+  if (a.S < 1 || a.d % (b * a.S) || a.ngc != a.d / b || a.ngroups % a.ngc)
+    return violation("stage pass shape (d %lld, S %lld)", a.d, a.S), hipErrorInvalidValue;
+  if (a.mode == BRQ_HADAMARD ? (a.blk || (b & (b - 1))) : !a.blk)
+    return violation("stage pass blocks (mode %lld)", a.mode, 0), hipErrorInvalidValue;
+  const int64_t nchunk = a.ngroups / a.ngc;
+  const int64_t axis_len = nchunk * a.d;  // positions along the transformed axis
+  if (axis_len >= ((int64_t)1 << 31)) return violation("positions beyond 32 bits (%lld)", axis_len, 0), hipErrorInvalidValue;
+  const int64_t rows = a.side == 0 ? a.lines : axis_len;
+  const int64_t cols = a.side == 0 ? axis_len : a.lines;
+  if (a.ld_src < cols || a.ld_dst < cols)
+    return violation("stage pass leading dimension (%lld < %lld)", std::min(a.ld_src, a.ld_dst), cols), hipErrorInvalidValue;
+  const int64_t gx = sp_group_tiles(a), gy = sp_line_tiles(a);
+  if (gy > 65535 || gx >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld, %lld)", gx, gy), hipErrorInvalidValue;
+  const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
+  const int kLds = kSpLines * kSpLineFloats;
+  std::vector<uint8_t> cover((size_t)(rows * cols), 0);
+  std::vector<int> xin(kLds), yout(kLds);
+  for (int64_t bx = 0; bx < gx; ++bx)
+    for (int64_t by = 0; by < gy; ++by) {
+      const int64_t g0 = bx * a.gw, l0 = by * kSpLines;
+      const int ng = (int)std::min<int64_t>(a.ngroups - g0, a.gw);
+      const int nl = (int)std::min<int64_t>(a.lines - l0, kSpLines);
+      const int gb = a.gw * b;
+      std::fill(xin.begin(), xin.end(), 0);
+      std::fill(yout.begin(), yout.end(), 0);
+      // block rows
+      for (int u = 0; u < kSpThreads; ++u) {
+        const int g = u / a.bp, j = u - g * a.bp;
+        if (j >= b || g >= ng || a.mode == BRQ_HADAMARD) continue;
+        const int64_t r = sp_block_row(a, g0 + g, j);
+        if (r < 0 || r + b > blk_floats) return violation("block row at %lld of %lld", r, blk_floats), hipErrorInvalidValue;
+        if (a.mode == BRQ_PER_GROUP && r / (b * b) != ((g0 + g) % a.ngc))
+          return violation("block of group %lld read at %lld", g0 + g, r), hipErrorInvalidValue;
+        if (a.blk_vec && (b % 4 || r % 4 || reinterpret_cast<uintptr_t>(a.blk) % 16))
+          return violation("vector block row at %lld (b %lld)", r, b), hipErrorInvalidValue;
+      }
+      // padding
+      for (int e = 0; e < kSpLines * a.gw; ++e) {
+        const int l = e / a.gw, gg = e - l * a.gw;
+        for (int k = b; k < a.bs; ++k) {
+          const int s = sp_lds(a, l, gg, k);
+          if (s < 0 || s >= kLds) return violation("LDS pad slot %lld", s, 0), hipErrorInvalidValue;
+          xin[s] = 1;
+        }
+      }
+      // the (g, k) members each load/store thread takes, and the lines it walks
+      auto members = [&](auto&& fn) -> bool {
+        if (a.side == 0) {
+          for (int u = 0; u < kSpThreads && u < gb; ++u) {
+            int gg, k;
+            sp_member(a, u, gg, k);
+            if (gg < ng)
+              for (int l = 0; l < nl; ++l)
+                if (!fn(l, gg, k)) return false;
+          }
+        } else {
+          if (gb > kSpLines * (kSpThreads / kSpLines))
+            return violation("left-side tile of %lld members exceeds the unrolled loads", gb, 0);
+          for (int u = 0; u < kSpThreads; ++u) {
+            const int l = u % kSpLines;
+            for (int q = u / kSpLines; q < gb; q += kSpThreads / kSpLines) {
+              int gg, k;
+              sp_member(a, q, gg, k);
+              if (gg < ng && l < nl && !fn(l, gg, k)) return false;
+            }
+          }
+        }
+        return true;
+      };
+      bool ok = members([&](int l, int gg, int k) {
+        if (k < 0 || k >= b || gg < 0 || gg >= a.gw) return violation("member (%lld, %lld)", gg, k);
+        const int64_t pos = sp_pos(a, g0 + gg, k);
+        if (pos < 0 || pos >= axis_len) return violation("position %lld of %lld", pos, axis_len);
+        const int64_t off = sp_off(a, l0 + l, pos, a.ld_src);
+        const int64_t line = l0 + l;
+        if (line >= a.lines || off < 0 || off >= (a.side == 0 ? rows * a.ld_src : axis_len * a.ld_src))
+          return violation("stage pass load at %lld (line %lld)", off, line);
+        const int s = sp_lds(a, l, gg, k);
+        if (s < 0 || s >= kLds || xin[s]) return violation("LDS slot %lld loaded twice", s, 0);
+        xin[s] = 1;
+        return true;
+      });
+      if (!ok) return hipErrorInvalidValue;
+      // compute: thread (g, j) reads slots k < bs of its group for each line, writes slot j
+      for (int u = 0; u < kSpThreads; ++u) {
+        const int g = u / a.bp, j = u - g * a.bp;
+        if (j >= b || g >= ng) continue;
+        for (int l = 0; l < nl; ++l) {
+          const int base = sp_lds(a, l, g, 0);
+          if (base % 4) return violation("unaligned LDS vector read at %lld", base, 0), hipErrorInvalidValue;
+          for (int k = 0; k < a.bs; ++k)
+            if (base + k >= kLds || !xin[base + k]) return violation("LDS read of unwritten slot %lld", base + k, 0), hipErrorInvalidValue;
+          const int s = sp_lds(a, l, g, j);
+          if (yout[s]++) return violation("LDS output slot %lld written twice", s, 0), hipErrorInvalidValue;
+        }
+      }
+      ok = members([&](int l, int gg, int k) {
+        const int s = sp_lds(a, l, gg, k);
+        if (yout[s] != 1) return violation("LDS output slot %lld read before it is written", s, 0);
+        const int64_t pos = sp_pos(a, g0 + gg, k);
+        const int64_t r = a.side == 0 ? l0 + l : pos, c = a.side == 0 ? pos : l0 + l;
+        if (r >= rows || c >= cols) return violation("stage pass store (%lld, %lld)", r, c);
+        if (sp_off(a, l0 + l, pos, a.ld_dst) != r * a.ld_dst + c) return violation("store offset of (%lld, %lld)", r, c);
+        cover[(size_t)(r * cols + c)]++;
+        return true;
+      });
+      if (!ok) return hipErrorInvalidValue;
+    }
+  for (size_t i = 0; i < cover.size(); ++i)
+    if (cover[i] != 1) return violation("stage pass element %lld stored %lld times", (int64_t)i, cover[i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+}  // namespace brq

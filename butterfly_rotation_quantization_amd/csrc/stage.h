@@ -1,0 +1,118 @@
+// Stage pass: one stage of one side applied to the whole matrix in one launch.
+//
+// The multi-stage tile pass fuses several stages per tile, which needs a whole
+// group product of a line in one workgroup; with few lines (online activation
+// rotation at decode time: 1 to a few hundred rows) that leaves a handful of
+// workgroups for the whole GPU.  The stage pass instead splits the groups of
+// one stage over the workgroups, so every stage has d / b groups of
+// parallelism whatever the row count, and a plan of m stages takes m launches
+// (the intermediate stays in a float32 buffer that is updated in place).
+//
+// Stage arithmetic ([HARP] technical summary 2.1): group c = hi * S + lo of a
+// stage with radix b and stride S holds the elements hi * b * S + k * S + lo
+// (k < b) of a d-chunk, and y_j = sum_k B_c[j][k] x_k.
+//
+// A workgroup takes `gw` consecutive groups (global index over all chunks)
+// and up to kSpLines lines (rows for the right side, columns for the left).
+// Thread (g, j) keeps row j of block B_g in registers and produces output j of
+// group g for every line of the tile; the tile goes through LDS on the way in
+// and out so global loads and stores are coalesced.
+//
+// The index arithmetic lives here as __host__ __device__ functions so the dry
+// run checks exactly what the GPU executes.
+#pragma once
+
+#include "brq_internal.h"
+
+namespace brq {
+
+constexpr int kSpThreads = 256;
+constexpr int kSpLines = 32;        // lines per tile
+constexpr int kSpLineFloats = 256;  // gw * bs <= 256 floats of a line in LDS
+
+struct SpArgs {
+  int side;              // 0: right (lines are rows), 1: left (lines are columns)
+  int b;                 // radix of the stage
+  int bp;                // threads per group: b rounded up to a power of two
+  int bs;                // LDS floats per group: b rounded up to a multiple of 4
+  int gw;                // groups per tile (kSpThreads / bp)
+  int mode;              // BRQ_HADAMARD, BRQ_SHARED, BRQ_PER_GROUP
+  int64_t S;             // stride of the stage along the transformed axis
+  int64_t d;             // plan dimension
+  int64_t ngc;           // groups per chunk, d / b
+  int64_t ngroups;       // groups over all chunks
+  int64_t lines;         // rows (right side) or columns (left side)
+  const float* blk;      // blocks of the stage ([group][j][k], or one [j][k]); null: Hadamard
+  int blk_vec;           // blk 16-byte aligned and b % 4 == 0: block rows load as float4
+  float hscale;          // 1 / sqrt(b) for Hadamard blocks
+  const float* sign_in;  // signs applied when loading (first forward stage), or null
+  const float* sign_out; // signs applied when storing (last inverse stage), or null
+  const void* src;
+  int src_t;
+  int64_t ld_src;
+  void* dst;
+  int dst_t;
+  int64_t ld_dst;
+};
+
+__host__ __device__ inline int64_t sp_group_tiles(const SpArgs& a) {
+  return (a.ngroups + a.gw - 1) / a.gw;
+}
+__host__ __device__ inline int64_t sp_line_tiles(const SpArgs& a) {
+  return (a.lines + kSpLines - 1) / kSpLines;
+}
+
+// Position along the transformed axis of member k of group gid (global over
+// chunks), in 32-bit arithmetic: the host keeps every position below 2^31.
+__host__ __device__ inline int64_t sp_pos(const SpArgs& a, int64_t gid, int k) {
+  const uint32_t gi = (uint32_t)gid, ngc = (uint32_t)a.ngc, S = (uint32_t)a.S;
+  const uint32_t chunk = gi / ngc;
+  const uint32_t c = gi - chunk * ngc;
+  const uint32_t hi = c / S;
+  const uint32_t lo = c - hi * S;
+  return (int64_t)(chunk * (uint32_t)a.d + (hi * (uint32_t)a.b + (uint32_t)k) * S + lo);
+}
+
+// Float offset of row j of the block of group gid in the stage's block array
+// (per-group blocks are indexed by the group within its chunk).
+__host__ __device__ inline int64_t sp_block_row(const SpArgs& a, int64_t gid, int j) {
+  const int64_t c = a.mode == BRQ_PER_GROUP ? (int64_t)((uint32_t)gid % (uint32_t)a.ngc) : 0;
+  return (c * a.b + j) * a.b;
+}
+
+// Element offset of (line, position) in a matrix with leading dimension ld.
+__host__ __device__ inline int64_t sp_off(const SpArgs& a, int64_t line, int64_t pos, int64_t ld) {
+  return a.side == 0 ? line * ld + pos : pos * ld + line;
+}
+
+// Member (g, k) of a tile's inner index q (0 <= q < gw * b; larger q give
+// members the callers skip).  The right side's
+// load and store loops give thread q one member and walk the lines, so
+// consecutive q must be consecutive positions: k fastest when S = 1 (group
+// hi holds positions hi * b + k), group fastest otherwise (consecutive lo).
+// The left side's loops walk q with the lines fastest across threads, and any
+// order does.
+__host__ __device__ inline void sp_member(const SpArgs& a, int q, int& g, int& k) {
+  if (a.side == 1 || a.S == 1) {
+    g = q / a.b;
+    k = q - g * a.b;
+  } else {
+    k = q / a.gw;
+    g = q - k * a.gw;
+  }
+}
+
+// LDS slot of (line, group, member) in one tile buffer.
+__host__ __device__ inline int sp_lds(const SpArgs& a, int l, int g, int k) {
+  return l * kSpLineFloats + g * a.bs + k;
+}
+
+hipError_t launch_stage(const SpArgs& a, hipStream_t s);
+
+// Host side (stage_host.cpp).
+bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols);
+brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,
+                     void* y, int yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
+                     size_t ws_bytes, hipStream_t s, hipError_t* herr);
+
+}  // namespace brq

@@ -1,0 +1,141 @@
+// Host side of the stage pass (stage.h): which rotations take it, and the
+// chain of one launch per stage.
+#include <cmath>
+#include <cstdio>
+#include <cstdint>
+#include <cstring>
+
+#include "stage.h"
+
+namespace brq {
+
+namespace {
+
+// Largest line count (rows of a right-side rotation, columns of a left-side
+// one) that takes the stage pass: below it the multi-stage tile pass leaves
+// most of the GPU idle.
+constexpr int64_t kSpMaxLines = 1024;
+
+int pow2_at_least(int b) {
+  int p = 1;
+  while (p < b) p <<= 1;
+  return p;
+}
+
+// The stages to run.  A Hadamard plan is the Sylvester matrix of order d
+// whatever power-of-two radices it lists (H_{ab} = H_a (x) H_b in natural
+// order, and the normalisations multiply to 1/sqrt(d)), so it runs as
+// radix-16 stages plus one smaller remainder stage; other plans run as given.
+struct StageList {
+  int n = 0;
+  int b[kMaxStages * 4];
+  int64_t S[kMaxStages * 4];
+  int t[kMaxStages * 4];  // plan stage (-1 for the canonical Hadamard stages)
+};
+
+StageList stages_of(const Plan* p) {
+  StageList L;
+  if (p->mode == BRQ_HADAMARD) {
+    int rest = p->d;
+    int64_t S = 1;
+    int tmp_b[kMaxStages * 4];
+    int64_t tmp_S[kMaxStages * 4];
+    int k = 0;
+    while (rest > 1) {  // from the stride-1 end
+      const int b = rest >= 16 ? 16 : rest;
+      tmp_b[k] = b;
+      tmp_S[k] = S;
+      S *= b;
+      rest /= b;
+      ++k;
+    }
+    for (int i = 0; i < k; ++i) {  // stage 0 is the most significant digit
+      L.b[i] = tmp_b[k - 1 - i];
+      L.S[i] = tmp_S[k - 1 - i];
+      L.t[i] = -1;
+    }
+    L.n = k;
+    return L;
+  }
+  for (int i = 0; i < p->nst; ++i) {
+    L.b[i] = p->radix[i];
+    L.S[i] = p->stride[i];
+    L.t[i] = i;
+  }
+  L.n = p->nst;
+  return L;
+}
+
+}  // namespace
+
+bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {
+  if (!p || rows <= 0 || cols <= 0) return false;
+  const int64_t lines = side == 0 ? rows : cols;
+  const int64_t axis = side == 0 ? cols : rows;  // positions fit sp_pos's 32 bits
+  if (lines > kSpMaxLines || axis % p->d || axis > (int64_t)1 << 30) return false;
+  for (int i = 0; i < p->nst; ++i)
+    if (p->radix[i] > 64) return false;
+  return true;
+}
+
+brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,
+                     void* y, int yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
+                     size_t ws_bytes, hipStream_t s, hipError_t* herr) {
+  *herr = hipSuccess;
+  const StageList L = stages_of(p);
+  if (L.n == 0) return BRQ_ERR_UNSUPPORTED;
+  // intermediate: y itself when it is float32, else the workspace
+  void* mid = y;
+  int64_t ldm = ldy;
+  if (L.n > 1 && yt != BRQ_F32) {
+    if (!ws || ws_bytes < (size_t)rows * cols * sizeof(float)) return BRQ_ERR_WORKSPACE;
+    mid = ws;
+    ldm = cols;
+  }
+  const int64_t lines = side == 0 ? rows : cols;
+  if ((lines + kSpLines - 1) / kSpLines > 65535) return BRQ_ERR_UNSUPPORTED;
+  for (int i = 0; i < L.n; ++i) {
+    const int si = inverse ? L.n - 1 - i : i;
+    SpArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.side = side;
+    a.b = L.b[si];
+    a.bp = pow2_at_least(a.b);
+    a.bs = (a.b + 3) & ~3;
+    a.gw = kSpThreads / a.bp;
+    if (a.gw * a.bs > kSpLineFloats) a.gw = kSpLineFloats / a.bs;
+    a.mode = p->mode;
+    a.S = L.S[si];
+    a.d = p->d;
+    a.ngc = p->d / a.b;
+    a.ngroups = (side == 0 ? cols / p->d : 1) * a.ngc;
+    a.lines = lines;
+    a.hscale = 1.0f / std::sqrt((float)a.b);
+    a.blk = p->mode == BRQ_HADAMARD
+                ? nullptr
+                : (inverse ? p->blkT : p->blk) + p->blk_off[L.t[si]];
+    a.blk_vec = a.blk && a.b % 4 == 0 && reinterpret_cast<uintptr_t>(a.blk) % 16 == 0;
+    a.sign_in = (!inverse && i == 0) ? p->signs : nullptr;
+    a.sign_out = (inverse && i == L.n - 1) ? p->signs : nullptr;
+    a.src = i == 0 ? x : mid;
+    a.src_t = i == 0 ? xt : BRQ_F32;
+    a.ld_src = i == 0 ? ldx : ldm;
+    const bool last = i == L.n - 1;
+    a.dst = last ? y : mid;
+    a.dst_t = last ? yt : BRQ_F32;
+    a.ld_dst = last ? ldy : ldm;
+    char name[64];
+    snprintf(name, sizeof name, "stage %s%s(%d) S%lld", side == 0 ? "R" : "L",
+             inverse ? "^T" : "", a.b, (long long)a.S);
+    const int tok = prof_begin(name, s);
+    const hipError_t e = launch_stage(a, s);
+    prof_end(tok, s);
+    if (e != hipSuccess) {
+      *herr = e;
+      return BRQ_ERR_HIP;
+    }
+  }
+  return BRQ_OK;
+}
+
+}  // namespace brq

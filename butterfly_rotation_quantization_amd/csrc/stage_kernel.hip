@@ -1,0 +1,180 @@
+// Stage pass kernel: one stage of one side over the whole matrix (stage.h).
+#include "stage.h"
+
+namespace brq {
+namespace {
+
+__device__ __forceinline__ float sp_load(const void* p, int t, int64_t i) {
+  if (t == BRQ_F32) return static_cast<const float*>(p)[i];
+  if (t == BRQ_BF16)
+    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[i] << 16);
+  return (float)static_cast<const _Float16*>(p)[i];
+}
+
+__device__ __forceinline__ void sp_store(void* p, int t, int64_t i, float v) {
+  if (t == BRQ_F32) {
+    static_cast<float*>(p)[i] = v;
+  } else if (t == BRQ_BF16) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) u |= 0x400000u;  // keep NaN a quiet NaN
+    else u += 0x7fffu + ((u >> 16) & 1u);                   // nearest, ties to even
+    static_cast<uint16_t*>(p)[i] = (uint16_t)(u >> 16);
+  } else {
+    static_cast<_Float16*>(p)[i] = (_Float16)v;
+  }
+}
+
+template <int MAXB>
+__global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
+  __shared__ float xin[kSpLines * kSpLineFloats];
+  __shared__ float yout[kSpLines * kSpLineFloats];
+  const int u = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * a.gw;
+  const int64_t l0 = (int64_t)blockIdx.y * kSpLines;
+  const int ng = (int)(a.ngroups - g0 < a.gw ? a.ngroups - g0 : a.gw);
+  const int nl = (int)(a.lines - l0 < kSpLines ? a.lines - l0 : kSpLines);
+  const int gb = a.gw * a.b;
+
+  // ---- row j of the block of group g (zero beyond b)
+  const int g = u / a.bp;
+  const int j = u - g * a.bp;
+  const bool act = j < a.b && g < ng;
+  float w[MAXB];
+#pragma unroll
+  for (int k = 0; k < MAXB; ++k) w[k] = 0.f;
+  if (act) {
+    if (a.mode == BRQ_HADAMARD) {
+#pragma unroll
+      for (int k = 0; k < MAXB; ++k)
+        if (k < a.b) w[k] = (__popc(j & k) & 1) ? -a.hscale : a.hscale;
+    } else {
+      const float* row = a.blk + sp_block_row(a, g0 + g, j);
+      if (a.blk_vec) {  // rows 16-byte aligned, b a multiple of 4
+#pragma unroll
+        for (int k4 = 0; k4 < MAXB / 4; ++k4)
+          if (4 * k4 < a.b) {
+            const float4 q = *reinterpret_cast<const float4*>(row + 4 * k4);
+            w[4 * k4] = q.x;
+            w[4 * k4 + 1] = q.y;
+            w[4 * k4 + 2] = q.z;
+            w[4 * k4 + 3] = q.w;
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < MAXB; ++k)
+          if (k < a.b) w[k] = row[k];
+      }
+    }
+  }
+
+  // ---- tile in: zero the padding members, then the loads
+  for (int e = u; e < kSpLines * a.gw; e += kSpThreads) {
+    const int l = e / a.gw, gg = e - l * a.gw;
+    for (int k = a.b; k < a.bs; ++k) xin[sp_lds(a, l, gg, k)] = 0.f;
+  }
+  // All of a thread's loads are issued before the first LDS write, so they are
+  // in flight together.
+  float v[kSpLines];
+  if (a.side == 0) {
+    if (u < gb) {
+      int gg, k;
+      sp_member(a, u, gg, k);
+      if (gg < ng) {
+        const int64_t pos = sp_pos(a, g0 + gg, k);
+        const float sg = a.sign_in ? a.sign_in[pos % a.d] : 1.f;
+#pragma unroll
+        for (int l = 0; l < kSpLines; ++l)
+          if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, pos, a.ld_src));
+#pragma unroll
+        for (int l = 0; l < kSpLines; ++l)
+          if (l < nl) xin[sp_lds(a, l, gg, k)] = sg * v[l];
+      }
+    }
+  } else {
+    const int l = u % kSpLines;
+    constexpr int kStep = kSpThreads / kSpLines;  // q advances by 8; gb <= 256 gives <= 32 steps
+#pragma unroll
+    for (int it = 0; it < kSpLines; ++it) {
+      const int q = u / kSpLines + kStep * it;
+      int gg, k;
+      sp_member(a, q, gg, k);
+      if (q < gb && gg < ng && l < nl)
+        v[it] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, sp_pos(a, g0 + gg, k), a.ld_src));
+    }
+#pragma unroll
+    for (int it = 0; it < kSpLines; ++it) {
+      const int q = u / kSpLines + kStep * it;
+      int gg, k;
+      sp_member(a, q, gg, k);
+      if (q < gb && gg < ng && l < nl) {
+        const int64_t pos = sp_pos(a, g0 + gg, k);
+        const float sg = a.sign_in ? a.sign_in[pos % a.d] : 1.f;
+        xin[sp_lds(a, l, gg, k)] = sg * v[it];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- y_j = sum_k B[j][k] x_k for every line of the tile
+  if (act) {
+    for (int l = 0; l < nl; ++l) {
+      const float* xr = xin + sp_lds(a, l, g, 0);
+      float acc = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < MAXB / 4; ++k4) {
+        if (4 * k4 < a.bs) {
+          const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * k4);
+          acc = fmaf(w[4 * k4 + 0], xv.x, acc);
+          acc = fmaf(w[4 * k4 + 1], xv.y, acc);
+          acc = fmaf(w[4 * k4 + 2], xv.z, acc);
+          acc = fmaf(w[4 * k4 + 3], xv.w, acc);
+        }
+      }
+      yout[sp_lds(a, l, g, j)] = acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- tile out
+  if (a.side == 0) {
+    if (u < gb) {
+      int gg, k;
+      sp_member(a, u, gg, k);
+      if (gg < ng) {
+        const int64_t pos = sp_pos(a, g0 + gg, k);
+        const float sg = a.sign_out ? a.sign_out[pos % a.d] : 1.f;
+        for (int l = 0; l < nl; ++l)
+          sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * yout[sp_lds(a, l, gg, k)]);
+      }
+    }
+  } else {
+    const int l = u % kSpLines;
+    for (int q = u / kSpLines; q < gb; q += kSpThreads / kSpLines) {
+      int gg, k;
+      sp_member(a, q, gg, k);
+      if (gg < ng && l < nl) {
+        const int64_t pos = sp_pos(a, g0 + gg, k);
+        const float sg = a.sign_out ? a.sign_out[pos % a.d] : 1.f;
+        sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * yout[sp_lds(a, l, gg, k)]);
+      }
+    }
+  }
+}
+
+template <int MAXB>
+hipError_t launch_t(const SpArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)sp_group_tiles(a), (unsigned)sp_line_tiles(a));
+  hipLaunchKernelGGL((stage_kernel<MAXB>), grid, dim3(kSpThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stage(const SpArgs& a, hipStream_t s) {
+  if (a.bp <= 8) return launch_t<8>(a, s);
+  if (a.bp <= 16) return launch_t<16>(a, s);
+  if (a.bp <= 32) return launch_t<32>(a, s);
+  return launch_t<64>(a, s);
+}
+
+}  // namespace brq

@@ -171,6 +171,14 @@ def test_llama70b_decode_activations(tokens):
     xs = cfg["acts"][tokens]
     x = to_dev(xs, "f16")
     V = lib_plan(cfg["right"])
+    brq.profile_reset()
+    brq.profile_enable(True)
     y = brq.rotate(V, x)
+    names = list(brq.profile_read())
+    brq.profile_enable(False)
+    assert len(names) == 4 and all(n.startswith("stage R(") for n in names), names
     ref = T.apply_right(orc_plan(cfg["right"]), xs.astype(np.float64), method="factored")
     check_rotation(from_dev(y), ref, "f16", f"70B decode T={tokens}")
+    xi = brq.rotate_inverse(V, y)
+    refi = T.apply_right(orc_plan(cfg["right"]), from_dev(y), inverse=True, method="factored")
+    check_rotation(from_dev(xi), refi, "f16", f"70B decode inverse T={tokens}")

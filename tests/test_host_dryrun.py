@@ -183,3 +183,25 @@ def test_rowhad_launches(dl, l2d, rows, cpr):
             for kind in (0, 1):
                 _rqp(dl, None, p, rows, n, bits, group, kind)
                 assert dl.brq_dryrun_launches() == 1
+
+
+# The stage pass: one launch per stage for rotations of few lines (decode-time
+# activations on the right side, a few columns on the left side).
+@pytest.mark.parametrize("radix,mode,lines,chunks", [
+    ((7, 16, 16, 16), "per_group", 1, 1), ((7, 16, 16, 16), "per_group", 16, 1),
+    ((7, 16, 16, 16), "per_group", 256, 1), ((43, 16, 16), "per_group", 33, 2),
+    ((3, 5, 7), "shared", 70, 3), ((2,) * 13, "hadamard", 5, 1), ((64, 2), "per_group", 1024, 1),
+    ((32, 16, 16), "per_group", 9, 1),
+])
+def test_stage_pass_launches(dl, radix, mode, lines, chunks):
+    side = S.random_plan(np.random.default_rng(len(radix) + lines), radix, mode)
+    p = DPlan(dl, side)
+    d = side.d
+    nst = len(radix) if mode != "hadamard" else -(-int(np.log2(d)) // 4)
+    for inverse in (False, True):
+        for xt, yt in ((2, 2), (1, 0), (0, 1)):
+            _rotate(dl, p, 0, lines, chunks * d, xt, yt, inverse=inverse)
+            assert dl.brq_dryrun_launches() == nst
+        if d <= 8192:
+            _rotate(dl, p, 1, d, lines, 1, 1, inverse=inverse)
+            assert dl.brq_dryrun_launches() == nst
