@@ -1,27 +1,45 @@
 #!/usr/bin/env python3
 """Benchmark of the rotate + quantize hot path on one MI355X.
 
-Workload: the HARP MLP weight, 4096 x 11008 bfloat16 (0.02 * Student-t(3),
-0.5% outlier input channels x30), left plan (16,16,16) and right plan
-(43,16,16) with per-group random orthogonal blocks and random signs, then
-3-bit group-128 absmax quantization and LSB-first packing.  One step = one
-brq_rotate_quantize_pack call (W' = M_U W M_V^T, quantize, pack) on one
-resident input; four input copies rotate so the working set exceeds the
-256 MB Infinity Cache.
+Default workload (the headline line): the HARP MLP weight, 4096 x 11008
+bfloat16 (0.02 * Student-t(3), 0.5% outlier input channels x30), left plan
+(16,16,16) and right plan (43,16,16) with per-group random orthogonal blocks
+and random signs, then 3-bit group-128 absmax quantization and LSB-first
+packing.  One step = one brq_rotate_quantize_pack call (W' = M_U W M_V^T,
+quantize, pack) on one resident input; several input copies rotate so the
+working set exceeds the 256 MB Infinity Cache.
 
 Metric: algorithmic HBM GB/s = (input read once + codes + scales + plan
 arrays read once) / step time, and its fraction of the 8 TB/s peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+--workload names one of the other shapes of the hot path (each prints the
+same kind of line; "all" prints one line per workload):
 
-Prints one JSON line.  --gpus above 1 exits: this build runs on one GPU.
+  llama7b_weight   4096 x 4096 bf16, two-sided RHT d=4096, absmax g128 at
+                   2, 3 and 4 bits (one step = the three calls)
+  llama7b_act      online right-side RHT of activations 2048 x 4096 bf16
+  polar_quant      the 7 projections of a decoder block (hidden 4096, FFN
+                   12288), block-128 Walsh-Hadamard, per-block norm, 4-bit
+                   Lloyd-Max codebook (one step = 7 calls)
+  polar_dequant    dequantize + unrotate of the same 7 matrices to bf16
+  llama70b_weight  8192 x 28672 bf16, left (32,16,16) and right (7,16,16,16)
+                   per-group plans, absmax 2-bit g64
+  decode_t1/16/256 online right-side rotation of T x 28672 fp16 activations
+                   with the (7,16,16,16) plan: latency per call
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+--gpus above 1 exits: this build runs on one GPU.
 """
 
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import re
 import sys
 import time
 
@@ -29,58 +47,77 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-M, N, BITS, GROUP = 4096, 11008, 3, 128
-LEFT_RADIX, RIGHT_RADIX = (16, 16, 16), (43, 16, 16)
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3   # 256 CUs x 2.4 GHz x 256 flop/clk (packed FMA)
+# fp32 peaks: MFMA (v_mfma_f32_16x16x4f32: 256 flop/clk/CU) and vector ALU
+# (256 CUs x 64 lanes x 2 (FMA) x 2 (dual issue) x 2.4 GHz); both 157.3 TFLOP/s.
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 FP32_MFMA_PEAK_TFLOPS = 157.3
-N_BUFFERS = 4
+MALL_BYTES = 256 << 20
 
 
-def plan_bytes(d, radix, signs=True):
+def plan_bytes(d, radix, blocks=True, signs=True):
     """float32 blocks read once (d * b_t per stage) + float32 signs."""
-    return 4 * sum(d * b for b in radix) + (4 * d if signs else 0)
+    return (4 * sum(d * b for b in radix) if blocks else 0) + (4 * d if signs else 0)
 
 
-def algorithmic_bytes():
-    return (M * N * 2 + M * N * BITS // 8 + M * (N // GROUP) * 4
-            + plan_bytes(M, LEFT_RADIX) + plan_bytes(N, RIGHT_RADIX))
+def cpu_threads():
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        threads = min(threads, int(omp))
+    return threads
 
 
-def kernel_work(name: str):
-    """(bound, algorithmic amount per launch, unit, peak) of a kernel of this
-    workload, from the stages its name lists: a dense b x b stage is b FMA
-    (2b flop) per element, over all M*N elements.  The fast-path kernels
-    contract on fp32 MFMA; the generic tile pass on the fp32 vector ALU."""
-    import re
-    flop = 0
-    for grp in re.findall(r"\(([0-9,]+)\)", name):
-        for b in grp.split(","):
-            flop += 2 * int(b) * M * N
-    if name.startswith("fused"):
-        return "mfma", flop / 1e12, "TFLOP/s", FP32_MFMA_PEAK_TFLOPS
-    return "alu", flop / 1e12, "TFLOP/s", FP32_VECTOR_PEAK_TFLOPS
+def copies_for(nbytes, floor=2):
+    """Input copies that together exceed the Infinity Cache."""
+    return max(floor, math.ceil(1.25 * MALL_BYTES / max(nbytes, 1)) + 1)
 
 
-def measured_traffic(kernel_name: str):
+def stage_flops(radix, hadamard, elems):
+    """Algorithmic flops of applying one side's stages to `elems` elements: a
+    dense b x b stage is b FMA (2b flop) per element, a Hadamard stage of
+    radix b is a log2(b)-level butterfly (log2(b) add/sub per element)."""
+    if hadamard:
+        return sum(int(round(math.log2(b))) for b in radix) * elems
+    return sum(2 * b for b in radix) * elems
+
+
+def roofline_of(bytes_, flops, engine):
+    """(bound, achieved-per-second function inputs) for one kernel: the
+    resource whose time floor is larger at peak binds."""
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    peak = FP32_MFMA_PEAK_TFLOPS if engine == "mfma" else FP32_VECTOR_PEAK_TFLOPS
+    t_fl = flops / (peak * 1e12)
+    if t_hbm >= t_fl:
+        return "hbm", bytes_ / 1e9, "GB/s", HBM_PEAK_GBS
+    return ("mfma" if engine == "mfma" else "alu"), flops / 1e12, "TFLOP/s", peak
+
+
+def measured_traffic(workload: str, kernel_name: str):
     """HBM bytes per launch of `kernel_name` from the committed counter
-    summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what the
-    same counter reads for a plain copy of known size), or None when the
-    summary is missing or was taken on a different kernel source."""
+    summary of this workload (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled
+    by what the same counter reads for a plain copy of known size), or None
+    when the summary is missing or was taken on a different kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_fused_harp_mlp_4096x11008.md")
-    src = os.path.join(ROOT, "butterfly_rotation_quantization_amd", "csrc", "fused_kernels.hip")
-    if not os.path.exists(path) or not os.path.exists(src):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
         return None
-    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
     vals = {}
     for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().strip("`").split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha1") != sha:
+    h = hashlib.sha1()
+    for name in vals.get("kernel_source", "").split(","):
+        src = os.path.join(ROOT, "butterfly_rotation_quantization_amd", "csrc", name.strip())
+        if not name.strip() or not os.path.isfile(src):
+            return None
+        h.update(open(src, "rb").read())
+    if vals.get("kernel_source_sha1") != h.hexdigest():
         return None
-    key = "fused_b" if kernel_name.startswith("fusedB") else "fused_a"
+    key = vals.get(f"kernel[{kernel_name}]")
+    if key is None:
+        return None
     try:
         fetch = float(vals[f"{key}_fetch_kib"]) * float(vals["copy_fetch_scale"])
         write = float(vals[f"{key}_write_kib"]) * float(vals["copy_write_scale"])
@@ -89,82 +126,422 @@ def measured_traffic(kernel_name: str):
     return round((fetch + write) * 1024)
 
 
-def cpu_baseline(cfg, rows_sample: int):
-    """The oracle, as written, on `rows_sample` seeded rows of the workload:
-    rows of M_U (factor by factor), times W, then the dense M_V^T (formed from
-    its stages inside the timed region), group absmax and packing."""
-    import numpy as np
-    import synthetic as S
-    from oracle import quant as Q
-    from oracle import transform as T
-
-    threads = len(os.sched_getaffinity(0))
-    omp = os.environ.get("OMP_NUM_THREADS")
-    if omp and omp.isdigit():
-        threads = min(threads, int(omp))
-    left, right = cfg["left"], cfg["right"]
-    w64 = S.storage_to_f64(cfg["w"], "bf16")
-    rows = np.sort(np.random.default_rng(99).choice(M, size=rows_sample, replace=False))
-    t0 = time.perf_counter()
-    U = T.Plan(left.d, left.radix, left.mode, left.blocks, left.signs.astype(float))
-    V = T.Plan(right.d, right.radix, right.mode, right.blocks, right.signs.astype(float))
-    y = T.left_rows(U, rows) @ w64
-    y = T.apply_right(V, y, method="dense")
-    codes, _alpha = Q.absmax_quantize(y, BITS, GROUP)
-    Q.pack(codes, BITS)
-    dt = time.perf_counter() - t0
-    share = rows_sample / M
-    return {
-        "value": round(algorithmic_bytes() * share / dt / 1e9, 6),
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"{rows_sample} of {M} seeded rows of the same workload (left plan rows "
-                   f"factor by factor, dense right plan formed in the timed region, absmax, "
-                   f"pack); {dt:.1f} s"),
-    }
-
-
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=M)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="also run a plain device-to-device copy of MIB MiB (3 times) before the "
-                         "steps, as the reference kernel for HBM byte counters")
-    a = ap.parse_args(argv)
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path needs no "
-              "collectives and multi-GPU runs are out of scope here.", file=sys.stderr)
-        return 2
-
+def storage_tensor(arr, dtype, dev):
+    """A device tensor holding the bit pattern of a synthetic storage array."""
     import numpy as np
     import torch
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+    if dtype == "f16":
+        return torch.from_numpy(arr).to(dev)
+    return torch.from_numpy(arr).to(dev)
 
-    import butterfly_rotation_quantization_amd as brq
+
+def oracle_plan(side):
+    from oracle import transform as T
+    return T.Plan(side.d, side.radix, side.mode, side.blocks,
+                  None if side.signs is None else side.signs.astype(float))
+
+
+# ---------------------------------------------------------------- workloads
+
+class Workload:
+    """One shape of the hot path: device set-up, the step, the algorithmic
+    bytes and flops of each kernel it launches, and the oracle's timing."""
+    name = ""
+    metric = ""
+    unit = "GB/s"
+    higher_is_better = True
+    dtype = "f32"
+
+    def setup(self, brq, dev, stream):
+        raise NotImplementedError
+
+    def step(self, i):
+        raise NotImplementedError
+
+    def alg_bytes(self):
+        raise NotImplementedError
+
+    def kernel_cost(self, name):
+        """(algorithmic bytes, algorithmic flops, engine) of one launch."""
+        raise NotImplementedError
+
+    def value(self, ms):
+        return self.alg_bytes() / (ms * 1e-3) / 1e9
+
+    def config(self):
+        return {}
+
+    def elements(self):
+        """Matrix elements one step transforms."""
+        raise NotImplementedError
+
+    def cpu_baseline(self, budget_s):
+        return None
+
+
+def quant_bytes(m, n, bits, group, scale_bytes):
+    return m * n * bits // 8 + m * (n // group) * scale_bytes
+
+
+class TwoSidedWeight(Workload):
+    """Two-sided rotate + quantize + pack of one weight matrix."""
+    kind = "absmax"
+
+    def __init__(self, name, metric, cfg_fn, bits_list, group):
+        self.name, self.metric = name, metric
+        self.cfg_fn = cfg_fn
+        self.bits_list = tuple(bits_list)
+        self.group = group
+
+    def setup(self, brq, dev, stream):
+        import torch
+        self.brq = brq
+        self.cfg = cfg = self.cfg_fn()
+        self.M, self.N = cfg["w"].shape
+        w = storage_tensor(cfg["w"], cfg["dtype"], dev)
+        self.bufs = [w] + [w.clone() for _ in range(copies_for(w.numel() * 2) - 1)]
+        L, R = cfg["left"], cfg["right"]
+        self.U = brq.Plan(L.d, L.radix, L.mode, L.blocks, L.signs)
+        self.V = brq.Plan(R.d, R.radix, R.mode, R.blocks, R.signs)
+        self.out = {b: (torch.empty((self.M, self.N * b // 8), dtype=torch.uint8, device=dev),
+                        torch.empty((self.M, self.N // self.group), dtype=torch.float32,
+                                    device=dev)) for b in self.bits_list}
+        self.ws = brq.workspace(self.U, self.V, self.M, self.N, dev)
+        self.stream = stream
+
+    def step(self, i):
+        w = self.bufs[i % len(self.bufs)]
+        for b in self.bits_list:
+            c, s = self.out[b]
+            self.brq.rotate_quantize_pack(self.U, self.V, w, b, self.group, codes=c, scales=s,
+                                          ws=self.ws, stream=self.stream)
+
+    def elements(self):
+        return self.M * self.N * len(self.bits_list)
+
+    def _plans_bytes(self):
+        L, R = self.cfg["left"], self.cfg["right"]
+        return (plan_bytes(L.d, L.radix, L.mode != "hadamard", L.signs is not None)
+                + plan_bytes(R.d, R.radix, R.mode != "hadamard", R.signs is not None))
+
+    def alg_bytes(self):
+        M, N = self.M, self.N
+        return sum(M * N * 2 + quant_bytes(M, N, b, self.group, 4) + self._plans_bytes()
+                   for b in self.bits_list)
+
+    def kernel_cost(self, name):
+        M, N, E = self.M, self.N, self.M * self.N
+        L, R = self.cfg["left"], self.cfg["right"]
+        had = L.mode == "hadamard"
+        qb = re.search(r"quant b(\d+)", name)
+        bits = int(qb.group(1)) if qb else self.bits_list[0]
+        q_out = quant_bytes(M, N, bits, self.group, 4)
+        if name.startswith("fusedA"):
+            # U_0 and V_0 of the plans (Hadamard plans: the first four levels)
+            fl = (stage_flops((16,), True, E) * 2 if had
+                  else stage_flops((L.radix[0], R.radix[0]), False, E))
+            blk = 0 if had else 4 * (M * L.radix[0] + N * R.radix[0])
+            return E * 2 + E * 4 + blk + 4 * (M + N), fl, "mfma"
+        if name.startswith("fusedB"):
+            fl = (stage_flops((16, 16), True, E) * 2 if had
+                  else stage_flops(L.radix[1:] + R.radix[1:], False, E))
+            blk = 0 if had else 4 * (M * sum(L.radix[1:]) + N * sum(R.radix[1:]))
+            return E * 4 + q_out + blk, fl, "mfma"
+        # generic tile pass: "pass L(..) R(..) [quant]"
+        radices = []
+        for side, d, plan in (("L", M, L), ("R", N, R)):
+            m_ = re.search(side + r"\(([0-9,]+)\)", name)
+            if m_:
+                rs = tuple(int(x) for x in m_.group(1).split(","))
+                radices.append((rs, d))
+        fl = sum(stage_flops(rs, had, E) for rs, _ in radices)
+        blk = 0 if had else sum(4 * d * sum(rs) for rs, d in radices)
+        first = self._first_kernel == name
+        bytes_in = E * 2 if first else E * 4
+        bytes_out = q_out if name.endswith("quant") else E * 4
+        return bytes_in + bytes_out + blk, fl, "alu"
+
+    def config(self):
+        L, R = self.cfg["left"], self.cfg["right"]
+        return {"m": self.M, "n": self.N, "bits": list(self.bits_list), "group": self.group,
+                "left": {"d": L.d, "radix": list(L.radix), "mode": L.mode},
+                "right": {"d": R.d, "radix": list(R.radix), "mode": R.mode},
+                "input_copies": len(self.bufs)}
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on seeded rows: rows of M_U (factor by factor), times W,
+        then M_V^T (dense from its stages when d <= 11008, else factor by
+        factor), group absmax and packing."""
+        import numpy as np
+        import synthetic as S
+        from oracle import quant as Q
+        from oracle import transform as T
+        U, V = oracle_plan(self.cfg["left"]), oracle_plan(self.cfg["right"])
+        method = "dense" if V.d <= 11008 else "factored"
+        w64 = S.storage_to_f64(self.cfg["w"], self.cfg["dtype"])
+        rng = np.random.default_rng(99)
+
+        def run(k):
+            rows = np.sort(rng.choice(self.M, size=k, replace=False))
+            t0 = time.perf_counter()
+            y = T.left_rows(U, rows) @ w64
+            y = T.apply_right(V, y, method=method)
+            for b in self.bits_list:
+                codes, _alpha = Q.absmax_quantize(y, b, self.group)
+                Q.pack(codes, b)
+            return time.perf_counter() - t0
+
+        k = self._cpu_rows
+        dt = run(k)
+        share = k / self.M
+        return {
+            "value": round(self.alg_bytes() * share / dt / 1e9, 6),
+            "unit": "GB/s",
+            "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": (f"{k} of {self.M} seeded rows of the same workload (left plan rows "
+                       f"factor by factor, right plan {method}, absmax at "
+                       f"{'/'.join(map(str, self.bits_list))} bits, pack); {dt:.1f} s"),
+        }
+
+
+class RightRotate(Workload):
+    """Online right-side rotation of activations (Y = X M_V^T, same dtype)."""
+
+    def __init__(self, name, metric, side, x, dtype, latency=False):
+        self.name, self.metric = name, metric
+        self.side, self.x_host, self.xdtype = side, x, dtype
+        self.latency = latency
+        if latency:
+            self.unit, self.higher_is_better = "us", False
+
+    def setup(self, brq, dev, stream):
+        import torch
+        self.brq = brq
+        P = self.side
+        self.T, self.N = self.x_host.shape
+        x = storage_tensor(self.x_host, self.xdtype, dev)
+        # Latency runs keep one activation buffer (it comes fresh from the
+        # previous kernel) and rotate over copies of the plan, as the layers
+        # of a model would, so the plan arrays are not cache-resident.
+        xb = x.numel() * 2
+        pb = plan_bytes(P.d, P.radix, P.mode != "hadamard", P.signs is not None)
+        self.bufs = [x] + ([] if self.latency else
+                           [x.clone() for _ in range(copies_for(xb) - 1)])
+        nplans = copies_for(pb, floor=1) if self.latency and P.mode != "hadamard" else 1
+        self.plans = [brq.Plan(P.d, P.radix, P.mode, P.blocks, P.signs) for _ in range(nplans)]
+        self.y = torch.empty_like(x)
+        self.ws = brq.workspace(None, self.plans[0], self.T, self.N, dev)
+        self.stream = stream
+
+    def step(self, i):
+        self.brq.rotate(self.plans[i % len(self.plans)], self.bufs[i % len(self.bufs)], self.y,
+                        side="right", ws=self.ws, stream=self.stream)
+
+    def elements(self):
+        return self.T * self.N
+
+    def alg_bytes(self):
+        P = self.side
+        return 4 * self.T * self.N + plan_bytes(P.d, P.radix, P.mode != "hadamard",
+                                                P.signs is not None)
+
+    def value(self, ms):
+        if self.latency:
+            return ms * 1e3
+        return super().value(ms)
+
+    def kernel_cost(self, name):
+        P, E = self.side, self.T * self.N
+        had = P.mode == "hadamard"
+        m_ = re.search(r"\(([0-9,]+)\)", name)
+        rs = tuple(int(x) for x in m_.group(1).split(",")) if m_ else P.radix
+        if name.startswith("rowhad"):
+            hd = int(re.search(r"H(\d+)", name).group(1))
+            return 4 * E + 4 * P.d, int(round(math.log2(hd))) * E, "alu"
+        fl = stage_flops(rs, had, E)
+        blk = 0 if had else 4 * P.d * sum(rs)
+        first, last = self._first_kernel == name, self._last_kernel == name
+        return (2 if first else 4) * E + (2 if last else 4) * E + blk, fl, "alu"
+
+    def config(self):
+        P = self.side
+        return {"tokens": self.T, "n": self.N, "d": P.d, "radix": list(P.radix),
+                "mode": P.mode, "io_dtype": self.xdtype, "input_copies": len(self.bufs),
+                "plan_copies": len(self.plans)}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        import synthetic as S
+        from oracle import transform as T
+        V = oracle_plan(self.side)
+        x64 = S.storage_to_f64(self.x_host, self.xdtype)
+        k = min(self.T, self._cpu_rows)
+        method = "dense" if V.d <= 4096 else "factored"
+        t0 = time.perf_counter()
+        y = T.apply_right(V, x64[:k], method=method)
+        S.to_storage(y, self.xdtype)
+        dt = time.perf_counter() - t0
+        share = k / self.T
+        if self.latency:
+            val, unit = round(dt * 1e6 / share, 3), "us"
+        else:
+            val, unit = round(self.alg_bytes() * share / dt / 1e9, 6), "GB/s"
+        return {"value": val, "unit": unit, "cores": cpu_threads(), "kind": "oracle",
+                "sample": (f"{k} of {self.T} seeded rows (right plan {method}, rounded to "
+                           f"{self.xdtype}); {dt:.2f} s")}
+
+
+class PolarBlock(Workload):
+    """PolarQuant-style quantization (or dequantization) of the 7 projections
+    of one decoder block with block-128 Walsh-Hadamard and a 4-bit codebook."""
+    dequant = False
+
+    def __init__(self, name, metric, dequant):
+        self.name, self.metric, self.dequant = name, metric, dequant
+
+    def setup(self, brq, dev, stream):
+        import numpy as np
+        import torch
+        import synthetic as S
+        from oracle import lloydmax as LM
+        self.brq = brq
+        self.cfg = cfg = S.polar()
+        self.cb = LM.lloyd_max_gaussian(cfg["bits"])[0].astype(np.float32)
+        R = cfg["right"]
+        self.H = brq.Plan(R.d, R.radix, R.mode, R.blocks, R.signs)
+        self.mats = {}
+        for name, arr in cfg["mats"].items():
+            m, n = arr.shape
+            w = storage_tensor(arr, "bf16", dev)
+            codes = torch.empty((m, n * cfg["bits"] // 8), dtype=torch.uint8, device=dev)
+            scales = torch.empty((m, n // cfg["group"]), dtype=torch.float16, device=dev)
+            self.mats[name] = (w, codes, scales)
+        if self.dequant:  # codes and norms of the same matrices
+            for w, codes, scales in self.mats.values():
+                brq.rotate_quantize_pack(None, self.H, w, cfg["bits"], cfg["group"],
+                                         "codebook_norm", self.cb, codes=codes, scales=scales)
+            torch.cuda.synchronize()
+        self.stream = stream
+
+    def step(self, i):
+        b, g = self.cfg["bits"], self.cfg["group"]
+        for w, codes, scales in self.mats.values():
+            if self.dequant:
+                self.brq.dequant_unrotate(None, self.H, codes, scales, w.shape[0], w.shape[1],
+                                          b, g, "codebook_norm", self.cb, out=w,
+                                          stream=self.stream)
+            else:
+                self.brq.rotate_quantize_pack(None, self.H, w, b, g, "codebook_norm", self.cb,
+                                              codes=codes, scales=scales, stream=self.stream)
+
+    def elements(self):
+        return sum(a.size for a in self.cfg["mats"].values())
+
+    def alg_bytes(self):
+        b, g = self.cfg["bits"], self.cfg["group"]
+        return sum(a.size * 2 + quant_bytes(a.shape[0], a.shape[1], b, g, 2)
+                   for a in self.cfg["mats"].values())
+
+    def kernel_cost(self, name):
+        # every launch of the step has the same per-element cost; the profile
+        # aggregates the 7 calls, so use the mean launch
+        E = sum(a.size for a in self.cfg["mats"].values()) / 7.0
+        return self.alg_bytes() / 7.0, 7 * E, "alu"
+
+    def config(self):
+        return {"matrices": {k: list(v.shape) for k, v in self.cfg["mats"].items()},
+                "d": 128, "bits": self.cfg["bits"], "group": self.cfg["group"],
+                "quantizer": "codebook_norm (Lloyd-Max N(0,1), fp16 norms)",
+                "direction": "dequant+unrotate to bf16" if self.dequant else
+                "rotate+quantize+pack"}
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on the first `_cpu_rows` rows of every projection."""
+        import numpy as np
+        import synthetic as S
+        from oracle import quant as Q
+        from oracle import transform as T
+        H = oracle_plan(self.cfg["right"])
+        b, g = self.cfg["bits"], self.cfg["group"]
+        k = self._cpu_rows
+        dt, done = 0.0, 0
+        for arr in self.cfg["mats"].values():
+            x64 = S.storage_to_f64(arr[:k], "bf16")
+            if self.dequant:  # codes and norms first, outside the timed region
+                codes, r64 = Q.codebook_norm_quantize(T.apply_right(H, x64), self.cb, g)[:2]
+                t0 = time.perf_counter()
+                v = Q.codebook_dequant(codes, r64.astype(np.float16), self.cb, g)
+                S.to_storage(T.apply_right(H, v, inverse=True), "bf16")
+            else:
+                t0 = time.perf_counter()
+                codes = Q.codebook_norm_quantize(T.apply_right(H, x64), self.cb, g)[0]
+                Q.pack(codes, b)
+            dt += time.perf_counter() - t0
+            done += x64.size
+        share = done / sum(a.size for a in self.cfg["mats"].values())
+        return {"value": round(self.alg_bytes() * share / dt / 1e9, 6), "unit": "GB/s",
+                "cores": cpu_threads(), "kind": "oracle",
+                "sample": (f"the first {k} rows of each of the 7 projections "
+                           f"({100 * share:.0f}% of the elements; right plan dense); {dt:.2f} s")}
+
+
+def make_workload(name):
     import synthetic as S
+    if name == "harp_mlp":
+        w = TwoSidedWeight(name, "HBM GB/s & % of peak: fused 2-sided rotate+quantize, "
+                           "4096x11008 bf16", S.harp_mlp, (3,), 128)
+        w.workload = "harp_mlp_4096x11008_bf16_two_sided_(16,16,16)x(43,16,16)_absmax3_g128"
+        w._cpu_rows = 4096
+        return w
+    if name == "llama7b_weight":
+        w = TwoSidedWeight(name, "HBM GB/s: two-sided RHT d=4096 + absmax g128 at 2/3/4 bits, "
+                           "4096x4096 bf16", lambda: S.llama7b(act_tokens=1), (2, 3, 4), 128)
+        w.workload = "llama7b_weight_4096x4096_bf16_two_sided_rht4096_absmax234_g128"
+        w._cpu_rows = 4096
+        return w
+    if name == "llama70b_weight":
+        w = TwoSidedWeight(name, "HBM GB/s: two-sided HARP (32,16,16)x(7,16,16,16) + absmax2 "
+                           "g64, 8192x28672 bf16", lambda: S.llama70b(tokens=()), (2,), 64)
+        w.workload = "llama70b_weight_8192x28672_bf16_two_sided_(32,16,16)x(7,16,16,16)_absmax2_g64"
+        w._cpu_rows = 2048
+        return w
+    if name == "llama7b_act":
+        cfg = S.llama7b(rows=1)
+        w = RightRotate(name, "HBM GB/s: online right-side RHT d=4096, 2048x4096 bf16",
+                        cfg["right"], cfg["x"], "bf16")
+        w.workload = "llama7b_act_2048x4096_bf16_rht4096"
+        w._cpu_rows = 2048
+        return w
+    if name.startswith("decode_t"):
+        t = int(name[len("decode_t"):])
+        cfg = S.llama70b(rows=1, tokens=(t,))
+        w = RightRotate(name, f"latency per call: online rotation of {t}x28672 fp16 "
+                        "activations, HARP (7,16,16,16)", cfg["right"], cfg["acts"][t], "f16",
+                        latency=True)
+        w.workload = f"decode_{t}x28672_f16_(7,16,16,16)"
+        w._cpu_rows = t
+        return w
+    if name in ("polar_quant", "polar_dequant"):
+        dq = name == "polar_dequant"
+        w = PolarBlock(name, ("HBM GB/s: PolarQuant dequant+unrotate" if dq else
+                              "HBM GB/s: PolarQuant rotate+quantize+pack")
+                       + ", 7 projections (hidden 4096, FFN 12288) bf16, H128, 4-bit codebook",
+                       dq)
+        w.workload = f"{name}_7proj_4096_12288_bf16_h128_codebook4_g128"
+        w._cpu_rows = 1024
+        return w
+    raise SystemExit(f"unknown workload {name!r}")
 
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
-    cfg = S.harp_mlp()
-    w_host = torch.from_numpy(cfg["w"].view(np.int16)).view(torch.bfloat16)
-    bufs = [w_host.to(dev) for _ in range(N_BUFFERS)]
-    U = brq.Plan(cfg["left"].d, cfg["left"].radix, "per_group", cfg["left"].blocks,
-                 cfg["left"].signs)
-    V = brq.Plan(cfg["right"].d, cfg["right"].radix, "per_group", cfg["right"].blocks,
-                 cfg["right"].signs)
-    codes = torch.empty((M, N * BITS // 8), dtype=torch.uint8, device=dev)
-    scales = torch.empty((M, N // GROUP), dtype=torch.float32, device=dev)
-    ws = brq.workspace(U, V, M, N, dev)
-    stream = torch.cuda.current_stream()
 
-    def step(i):
-        brq.rotate_quantize_pack(U, V, bufs[i % N_BUFFERS], BITS, GROUP, codes=codes,
-                                 scales=scales, ws=ws, stream=stream)
+WORKLOADS = ("harp_mlp", "llama7b_weight", "llama7b_act", "polar_quant", "polar_dequant",
+             "llama70b_weight", "decode_t1", "decode_t16", "decode_t256")
 
+
+def run_workload(wl, a, brq, torch, dev, stream):
+    wl.setup(brq, dev, stream)
     if a.copy_calibration:
         nel = a.copy_calibration * (1 << 20) // 4
         src = torch.ones(nel, dtype=torch.float32, device=dev)
@@ -174,49 +551,65 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     for i in range(a.warmup):
-        step(i)
+        wl.step(i)
     torch.cuda.synchronize()
+    # Per-kernel durations come from HIP events recorded around each launch on
+    # its stream.  Latency workloads (a few microseconds per kernel) time the
+    # step without them and take the kernel durations from a second run of
+    # the same steps; the others record them inside the timed region.
+    separate = getattr(wl, "latency", False)
     brq.profile_reset()
-    brq.profile_enable(True)
+    brq.profile_enable(not separate)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(a.steps):
-        step(i)
+        wl.step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    brq.profile_enable(False)
     ms = start.elapsed_time(end) / a.steps
+    if separate:
+        brq.profile_enable(True)
+        for i in range(a.steps):
+            wl.step(i)
+        torch.cuda.synchronize()
+    brq.profile_enable(False)
     kernels = brq.profile_read()
+    names = list(kernels)
+    wl._first_kernel, wl._last_kernel = names[0], names[-1]
 
-    alg = algorithmic_bytes()
-    value = alg / (ms * 1e-3) / 1e9
+    value = wl.value(ms)
+    alg = wl.alg_bytes()
     dom_name, (dom_ms, dom_n) = max(kernels.items(), key=lambda kv: kv[1][0])
-    bound, work, unit, peak = kernel_work(dom_name)
+    kb, kf, engine = wl.kernel_cost(dom_name)
+    bound, work, unit, peak = roofline_of(kb, kf, engine)
     avg_ms = dom_ms / max(dom_n, 1)
     achieved = work / (avg_ms * 1e-3)
+    cfg = {"workload": wl.workload}
+    cfg.update(wl.config())
+    cfg.update({
+        "algorithmic_bytes": alg,
+        "hbm_gbs": round(alg / (ms * 1e-3) / 1e9, 3),
+        "hbm_peak_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+        "kernels_ms_per_step": {k: round(v[0] / a.steps, 5) for k, v in kernels.items()},
+        "launches_per_step": {k: v[1] / a.steps for k, v in kernels.items()},
+    })
+    cfg["elements_per_s"] = round(wl.elements() / (ms * 1e-3), 1)
     line = {
-        "metric": "HBM GB/s & % of peak: fused 2-sided rotate+quantize, 4096x11008 bf16",
+        "metric": wl.metric,
         "value": round(value, 3),
-        "unit": "GB/s",
+        "unit": wl.unit,
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
+        "higher_is_better": wl.higher_is_better,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": "harp_mlp_4096x11008_bf16_two_sided_(16,16,16)x(43,16,16)_absmax3_g128",
-            "m": M, "n": N, "bits": BITS, "group": GROUP,
-            "hbm_peak_frac": round(value / HBM_PEAK_GBS, 5),
-            "elements_per_s": round(M * N / (ms * 1e-3), 1),
-            "algorithmic_bytes": alg,
-            "kernels_ms_per_step": {k: round(v[0] / max(v[1], 1), 5) for k, v in kernels.items()},
-        },
+        "config": cfg,
         "roofline": {
             "bound": bound,
             "kernel": dom_name,
@@ -224,12 +617,51 @@ def main(argv=None):
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 5),
-            "traffic": measured_traffic(dom_name),
+            "traffic": measured_traffic(wl.name, dom_name),
+            "algorithmic_bytes": kb,
+            "algorithmic_flops": kf,
+            "avg_launch_ms": round(avg_ms, 5),
         },
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, a.cpu_rows)
+        line["cpu_baseline"] = wl.cpu_baseline(None)
     print(json.dumps(line), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="harp_mlp", choices=WORKLOADS + ("all",))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle sample size in rows (0: the workload's default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device-to-device copy of MIB MiB (3 times) before the "
+                         "steps, as the reference kernel for HBM byte counters")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path needs no "
+              "collectives and multi-GPU runs are out of scope here.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import butterfly_rotation_quantization_amd as brq
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    names = WORKLOADS if a.workload == "all" else (a.workload,)
+    for name in names:
+        wl = make_workload(name)
+        if a.cpu_rows:
+            wl._cpu_rows = a.cpu_rows
+        run_workload(wl, a, brq, torch, dev, stream)
+        del wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return 0
 
 
