@@ -448,6 +448,14 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
           if (rh_elem(l2d, 0, cu, j) != 16 * cu + j)
             return violation("round 0 is not natural order (%lld, %lld)", cu, j), hipErrorInvalidValue;
     }
+    // the kernel's split addressing: per-thread base + per-register constant
+    for (int r = 0; r < R; ++r)
+      for (int u = 0; u < kRhThreads; ++u) {
+        const int cw = u >> (l2d - 4), cu = u & ((1 << (l2d - 4)) - 1);
+        for (int j = 0; j < 16; ++j)
+          if (rh_lds_base(l2d, r, cw, cu) + rh_lds_off(l2d, r, j) != rh_lds(l2d, cw, rh_elem(l2d, r, cu, j)))
+            return violation("split LDS address of thread %lld, round %lld", u, r), hipErrorInvalidValue;
+      }
     std::vector<int> slot(kRhLds);
     for (int r = 0; r < R && R > 1; ++r) {
       std::fill(slot.begin(), slot.end(), -1);
@@ -479,8 +487,11 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
       const int b = rh_bin(std::fma(a.tau[k], a.bin_s, a.bin_off));
       if (b <= prev || b >= kRhBins - 1)
         return violation("codebook threshold %lld in bin %lld", k, b), hipErrorInvalidValue;
+      if (a.tbin[k] != b) return violation("threshold %lld recorded in bin %lld", k, a.tbin[k]), hipErrorInvalidValue;
       prev = b;
     }
+    if (a.nlev - 1 > kMaxLevels || a.nlev > kRhThreads)
+      return violation("codebook of %lld levels", a.nlev, 0), hipErrorInvalidValue;
   }
   const int64_t nwg = rh_nwg(a);
   const int esz_x = a.xt == BRQ_F32 ? 4 : 2, esz_y = a.yt == BRQ_F32 ? 4 : 2;

@@ -52,8 +52,10 @@ struct RhArgs {
   // floor(u) (clamped to [0, kRhBins)); every threshold's u lies at least
   // 1/64 from an integer and no bin holds two, so the code is the number of
   // thresholds of the bins below plus (z > the bin's own threshold).  The host
-  // checks this and sets bin_s = 0 when no such scaling exists.
+  // checks this, records each threshold's bin in tbin, and sets bin_s = 0
+  // when no such scaling exists.
   float bin_s, bin_off;
+  int tbin[kMaxLevels];
   uint8_t* codes;
   const uint8_t* in_codes;
   void* scales;
@@ -95,6 +97,28 @@ __host__ __device__ inline int rh_elem(int l2d, int r, int cu, int j) {
 __host__ __device__ inline int rh_lds(int l2d, int cw, int i) {
   const int x = (cw << l2d) + i;
   return x + (x >> 4);
+}
+
+// The same slot split into a per-thread base and a per-register constant.
+// The element index of register j in round r is the OR of register j's bits
+// (at positions rh_regbit) and the thread's bits (cu at the positions the
+// round leaves free, in increasing order: first [4 - nnew, 4r), then
+// [4r + nnew, l2d); the chunk cw above l2d).  The two sets of positions are
+// disjoint, so x + (x >> 4) of their OR is the sum of the same expression
+// for each part; the kernels then address LDS with immediate offsets.
+__host__ __device__ constexpr int rh_jbits(int l2d, int r, int j) {
+  int i = 0;
+  for (int q = 0; q < 4; ++q) i |= ((j >> q) & 1) << rh_regbit(l2d, r, q);
+  return i;
+}
+__host__ __device__ constexpr int rh_lds_off(int l2d, int r, int j) {
+  return rh_jbits(l2d, r, j) + (rh_jbits(l2d, r, j) >> 4);
+}
+__host__ __device__ inline int rh_lds_base(int l2d, int r, int cw, int cu) {
+  const int nn = rh_nnew(l2d, r);
+  const int A = 4 * r - 4 + nn;  // length of the first free segment
+  const int b = (cw << l2d) | ((cu & ((1 << A) - 1)) << (4 - nn)) | ((cu >> A) << (4 * r + nn));
+  return b + (b >> 4);
 }
 
 // Bin of a scaled value (the kernel's arithmetic, shared with the host check).

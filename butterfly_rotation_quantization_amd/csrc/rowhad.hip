@@ -29,11 +29,8 @@ __device__ __forceinline__ float f16_lo(uint32_t w) {
 __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
-  return u >> 16;
+__device__ __forceinline__ uint32_t to_bf16(float f) {  // nearest, ties to even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t to_f16(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
@@ -99,13 +96,25 @@ __device__ __forceinline__ void butterflies(float (&v)[16], int q0) {
       }
 }
 
-// Reduction over the lanes of one quantizer group (lpg consecutive lanes).
-__device__ __forceinline__ float group_max(float x, int lpg) {
-  for (int m = 1; m < lpg; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
+// Reduction over the lanes of one quantizer group (lpg consecutive lanes, a
+// power of two, groups aligned to lpg).  Within a row of 16 lanes the steps
+// are DPP moves: swap neighbours, swap pairs, then mirror each half row and
+// the whole row, which pairs quads and then halves; wider groups use
+// cross-row shuffles.  Every lane of a group ends with the same value (the
+// same pairwise tree as xor steps 1, 2, 4, 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float group_sum(float x, int lpg) {
-  for (int m = 1; m < lpg; m <<= 1) x += __shfl_xor(x, m, 64);
+template <bool MAX>
+__device__ __forceinline__ float group_reduce(float x, int lpg) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if (lpg > 1) x = op(x, dpp<0xb1>(x));   // quad_perm [1,0,3,2]
+  if (lpg > 2) x = op(x, dpp<0x4e>(x));   // quad_perm [2,3,0,1]
+  if (lpg > 4) x = op(x, dpp<0x141>(x));  // row_half_mirror
+  if (lpg > 8) x = op(x, dpp<0x140>(x));  // row_mirror
+  if (lpg > 16) x = op(x, __shfl_xor(x, 16, 64));
+  if (lpg > 32) x = op(x, __shfl_xor(x, 32, 64));
   return x;
 }
 
@@ -156,10 +165,28 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&c)[16]) 
 template <int L2D, int MODE, int BITS>
 __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   __shared__ float lds[kRhLds];  // one buffer: more workgroups per CU beat a saved barrier
-  __shared__ int bin_cnt[MODE == RH_QUANT ? kRhBins : 1];
-  __shared__ float bin_tau[MODE == RH_QUANT ? kRhBins : 1];
+  // quantize: codebook bins {own threshold (or +inf), thresholds below};
+  // dequantize: the level values (centroid / sqrt(g), or code / h - 1)
+  __shared__ float2 tab[MODE == RH_QUANT ? kRhBins : (MODE == RH_DEQUANT ? kMaxLevels : 1)];
   constexpr int R = rh_rounds(L2D);
+  constexpr int LV = (1 << BITS) - 1;
   const RhPos p = rh_pos(a, blockIdx.x, threadIdx.x);
+  const int lpg = a.group / 16;
+  const bool bins = MODE == RH_QUANT && a.qkind == BRQ_CODEBOOK_NORM && a.bin_s != 0.f;
+  if (MODE == RH_QUANT && bins) {  // bin b: its threshold (or +inf) and the count below
+    const int b = threadIdx.x;
+    int cnt = 0;
+    float tin = __int_as_float(0x7f800000);
+    for (int k = 0; k < LV; ++k) {
+      cnt += a.tbin[k] < b ? 1 : 0;
+      tin = a.tbin[k] == b ? a.tau[k] : tin;
+    }
+    tab[b] = make_float2(tin, (float)cnt);
+  }
+  if (MODE == RH_DEQUANT && threadIdx.x <= LV) {
+    const int c = threadIdx.x;
+    tab[c].x = a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g;
+  }
   float v[16];
 
   // ---- prologue: load or unpack + dequantize, then the signs (forward)
@@ -169,22 +196,19 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = 0.f;
   } else {
+    uint32_t c[16];
+    float scale = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    for (int j = 0; j < 16; ++j) c[j] = 0u;
     if (p.live) {
-      uint32_t c[16];
       load_codes<BITS>(a.in_codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
       const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
-      if (a.qkind == BRQ_ABSMAX) {
-        const float alpha = static_cast<const float*>(a.in_scales)[sidx];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = alpha * ((float)c[j] / a.h - 1.0f);
-      } else {
-        const float r = (float)static_cast<const _Float16*>(a.in_scales)[sidx];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = r * a.cent[c[j]] / a.sqrt_g;
-      }
+      scale = a.qkind == BRQ_ABSMAX ? static_cast<const float*>(a.in_scales)[sidx]
+                                    : (float)static_cast<const _Float16*>(a.in_scales)[sidx];
     }
+    __syncthreads();  // the level table
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = scale * tab[c[j]].x;
   }
   if (!a.inverse && a.signs)
 #pragma unroll
@@ -197,11 +221,13 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     butterflies(v, 4 - rh_nnew(L2D, r));
     if (R > 1) {
       const int rn = r + 1 < R ? r + 1 : 0;
+      float* wb = lds + rh_lds_base(L2D, r, p.cw, p.cu);
+      const float* rb = lds + rh_lds_base(L2D, rn, p.cw, p.cu);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) lds[rh_lds(L2D, p.cw, rh_elem(L2D, r, p.cu, j))] = v[j];
+      for (int j = 0; j < 16; ++j) wb[rh_lds_off(L2D, r, j)] = v[j];
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = lds[rh_lds(L2D, p.cw, rh_elem(L2D, rn, p.cu, j))];
+      for (int j = 0; j < 16; ++j) v[j] = rb[rh_lds_off(L2D, rn, j)];
       if (r + 1 < R) __syncthreads();  // every read is done before the next round's writes
     }
   }
@@ -217,63 +243,45 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     return;
   }
   // quantizer groups of g = 16 lpg consecutive columns are lpg consecutive lanes
-  const int lpg = a.group / 16;
-  const bool bins = a.qkind == BRQ_CODEBOOK_NORM && a.bin_s != 0.f;
-  if (bins) {  // bin b: thresholds in lower bins, and the one in b (or +inf)
-    const int b = threadIdx.x;
-    int cnt = 0;
-    float tin = __int_as_float(0x7f800000);
-    for (int k = 0; k + 1 < a.nlev; ++k) {
-      const int bk = rh_bin(fmaf(a.tau[k], a.bin_s, a.bin_off));
-      cnt += bk < b ? 1 : 0;
-      if (bk == b) tin = a.tau[k];
-    }
-    bin_cnt[b] = cnt;
-    bin_tau[b] = tin;
-    __syncthreads();
-  }
   float stat = 0.f;
   if (a.qkind == BRQ_ABSMAX) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) stat = fmaxf(stat, fabsf(v[j]));
-    stat = group_max(stat, lpg);
+    stat = group_reduce<true>(stat, lpg);
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) stat = fmaf(v[j], v[j], stat);
-    stat = sqrtf(group_sum(stat, lpg));
+    stat = sqrtf(group_reduce<false>(stat, lpg));
   }
+  if (R == 1 && bins) __syncthreads();  // the bin table (R > 1 passed barriers since)
   if (!p.live) return;
-  constexpr int LV = (1 << BITS) - 1;
   uint32_t c[16];
   if (a.qkind == BRQ_ABSMAX) {
     const float k = stat > 0.f ? a.h / stat : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      int q = 0;
-      if (stat > 0.f) {
-        q = (int)rintf(fmaf(v[j], k, a.h));
-        q = q < 0 ? 0 : (q > LV ? LV : q);
-      }
-      c[j] = (uint32_t)q;
+      const int q = (int)rintf(fmaf(v[j], k, a.h));
+      c[j] = (uint32_t)(q < 0 ? 0 : (q > LV ? LV : q));
     }
   } else {
     const float k = stat > 0.f ? a.sqrt_g / stat : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
+      const float z = v[j] * k;
       int q = 0;
-      if (stat > 0.f) {
-        const float z = v[j] * k;
-        if (bins) {
-          const int b = rh_bin(fmaf(z, a.bin_s, a.bin_off));
-          q = bin_cnt[b] + (z > bin_tau[b] ? 1 : 0);
-        } else {
+      if (bins) {
+        const float2 e = tab[rh_bin(fmaf(z, a.bin_s, a.bin_off))];
+        q = (int)e.y + (z > e.x ? 1 : 0);
+      } else {
 #pragma unroll
-          for (int t = 0; t < LV; ++t) q += (z > a.tau[t]) ? 1 : 0;
-        }
+        for (int t = 0; t < LV; ++t) q += (z > a.tau[t]) ? 1 : 0;
       }
       c[j] = (uint32_t)q;
     }
   }
+  if (!(stat > 0.f))  // a zero group codes as all zeros
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[j] = 0u;
   store_codes<BITS>(a.codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
   if ((threadIdx.x & (lpg - 1)) == 0) {
     const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;

@@ -75,6 +75,7 @@ void fill_quant(RhArgs& a, const brq_quant* q, int64_t n) {
     if (ok) {
       a.bin_s = s;
       a.bin_off = off;
+      for (int i = 0; i < nt; ++i) a.tbin[i] = rh_bin(std::fma(a.tau[i], s, off));
       return;
     }
   }
