@@ -140,17 +140,24 @@ struct RhPos {
   int64_t c, row, col0;
   bool live;
 };
+// Chunk indices fit 31 bits (the host checks nchunks), so the row split is a
+// 32-bit division.
 __host__ __device__ inline RhPos rh_pos(const RhArgs& a, int64_t b, int u) {
   RhPos p;
   const int tpc = 1 << (a.log2d - 4);
-  p.cw = u / tpc;
+  p.cw = u >> (a.log2d - 4);
   p.cu = u - p.cw * tpc;
   p.c = b * (kRhTile >> a.log2d) + p.cw;
   p.live = p.c < a.nchunks;
-  p.row = p.live ? p.c / a.cpr : 0;
-  p.col0 = p.live ? (p.c - p.row * a.cpr) * ((int64_t)1 << a.log2d) + 16 * p.cu : 0;
+  const uint32_t c32 = p.live ? (uint32_t)p.c : 0u, cpr = (uint32_t)a.cpr;
+  const uint32_t row = c32 / cpr;
+  p.row = row;
+  p.col0 = p.live ? (int64_t)(c32 - row * cpr) * ((int64_t)1 << a.log2d) + 16 * p.cu : 0;
   return p;
 }
+
+// Largest chunk count of one call (chunk indices stay 31-bit).
+constexpr int64_t kRhMaxChunks = ((int64_t)1 << 31) - kRhTile;
 
 // Whether the row Hadamard path takes this plan.
 inline bool rh_plan_ok(const Plan* p) {

@@ -48,14 +48,19 @@ __device__ __forceinline__ void load16(const void* base, int t, int64_t off, flo
     }
   } else {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint4 x0 = p[0], x1 = p[1];  // both loads in flight before any conversion
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if (t == BRQ_BF16) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint4 x = p[q];
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      for (int e = 0; e < 8; ++e) {
+        v[2 * e] = bf16_lo(w[e]);
+        v[2 * e + 1] = bf16_hi(w[e]);
+      }
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * q + 2 * e] = t == BRQ_BF16 ? bf16_lo(w[e]) : f16_lo(w[e]);
-        v[8 * q + 2 * e + 1] = t == BRQ_BF16 ? bf16_hi(w[e]) : f16_hi(w[e]);
+      for (int e = 0; e < 8; ++e) {
+        v[2 * e] = f16_lo(w[e]);
+        v[2 * e + 1] = f16_hi(w[e]);
       }
     }
   }
@@ -173,20 +178,24 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   const RhPos p = rh_pos(a, blockIdx.x, threadIdx.x);
   const int lpg = a.group / 16;
   const bool bins = MODE == RH_QUANT && a.qkind == BRQ_CODEBOOK_NORM && a.bin_s != 0.f;
-  if (MODE == RH_QUANT && bins) {  // bin b: its threshold (or +inf) and the count below
-    const int b = threadIdx.x;
-    int cnt = 0;
-    float tin = __int_as_float(0x7f800000);
-    for (int k = 0; k < LV; ++k) {
-      cnt += a.tbin[k] < b ? 1 : 0;
-      tin = a.tbin[k] == b ? a.tau[k] : tin;
+  // The global loads are issued first; the quantizer tables are built while
+  // they are in flight.
+  auto build_tables = [&]() {
+    if (MODE == RH_QUANT && bins) {  // bin b: its threshold (or +inf) and the count below
+      const int b = threadIdx.x;
+      int cnt = 0;
+      float tin = __int_as_float(0x7f800000);
+      for (int k = 0; k < LV; ++k) {
+        cnt += a.tbin[k] < b ? 1 : 0;
+        tin = a.tbin[k] == b ? a.tau[k] : tin;
+      }
+      tab[b] = make_float2(tin, (float)cnt);
     }
-    tab[b] = make_float2(tin, (float)cnt);
-  }
-  if (MODE == RH_DEQUANT && threadIdx.x <= LV) {
-    const int c = threadIdx.x;
-    tab[c].x = a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g;
-  }
+    if (MODE == RH_DEQUANT && threadIdx.x <= LV) {
+      const int c = threadIdx.x;
+      tab[c].x = a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g;
+    }
+  };
   float v[16];
 
   // ---- prologue: load or unpack + dequantize, then the signs (forward)
@@ -195,6 +204,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     else
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    build_tables();
   } else {
     uint32_t c[16];
     float scale = 0.f;
@@ -206,6 +216,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
       scale = a.qkind == BRQ_ABSMAX ? static_cast<const float*>(a.in_scales)[sidx]
                                     : (float)static_cast<const _Float16*>(a.in_scales)[sidx];
     }
+    build_tables();
     __syncthreads();  // the level table
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = scale * tab[c[j]].x;
@@ -265,18 +276,24 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     }
   } else {
     const float k = stat > 0.f ? a.sqrt_g / stat : 0.f;
+    // one branch for the whole thread: inside it the 16 table reads are
+    // independent and pipeline
+    if (bins) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float z = v[j] * k;
-      int q = 0;
-      if (bins) {
+      for (int j = 0; j < 16; ++j) {
+        const float z = v[j] * k;
         const float2 e = tab[rh_bin(fmaf(z, a.bin_s, a.bin_off))];
-        q = (int)e.y + (z > e.x ? 1 : 0);
-      } else {
+        c[j] = (uint32_t)((int)e.y + (z > e.x ? 1 : 0));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float z = v[j] * k;
+        int q = 0;
 #pragma unroll
         for (int t = 0; t < LV; ++t) q += (z > a.tau[t]) ? 1 : 0;
+        c[j] = (uint32_t)q;
       }
-      c[j] = (uint32_t)q;
     }
   }
   if (!(stat > 0.f))  // a zero group codes as all zeros

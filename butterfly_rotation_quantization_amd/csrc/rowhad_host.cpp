@@ -94,6 +94,7 @@ bool rh_rotate_supported(const Plan* p, int side, int xt, int yt, int64_t rows, 
                          int64_t ldx, int64_t ldy, const void* x, const void* y) {
   if (side != 0 || !rh_plan_ok(p) || cols % p->d) return false;
   if (x == y) return false;  // in place goes through the tile pass
+  if (rows * (cols / p->d) > kRhMaxChunks) return false;
   return rows > 0 && rows_aligned(x, xt, ldx) && rows_aligned(y, yt, ldy);
 }
 
@@ -117,6 +118,7 @@ brq_status rh_rotate(const Plan* p, int inverse, const void* x, int xt, int64_t 
 bool rh_quant_supported(const Plan* U, const Plan* V, int wt, int64_t n, int64_t ldw,
                         const void* w, const brq_quant* q) {
   if (U || !rh_plan_ok(V) || n % V->d) return false;
+  if (m * (n / V->d) > kRhMaxChunks) return false;
   // a quantizer group lies inside one workgroup's 4096 elements of a row
   if (q->group > 1024 || kRhTile % q->group) return false;
   return rows_aligned(w, wt, ldw);
@@ -143,7 +145,7 @@ brq_status rh_rqp(const Plan* V, const void* w, int wt, int64_t m, int64_t n, in
 brq_status rh_dequant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q,
                       int64_t m, int64_t n, void* out, int ot, int64_t ldo, hipStream_t s) {
   if (reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(scales) % 4 ||
-      !rows_aligned(out, ot, ldo))
+      !rows_aligned(out, ot, ldo) || m * (n / V->d) > kRhMaxChunks)
     return BRQ_ERR_UNSUPPORTED;
   RhArgs a;
   fill_common(a, V, m, n);
