@@ -667,7 +667,7 @@ brq_status brq_rotate_quantize_pack(const brq_plan* left, const brq_plan* right,
     st = fused_rqp(U, V, w, wt, m, n, ldw, q, codes, scales, ws, ws_bytes, s);
     if (st != BRQ_ERR_UNSUPPORTED) return st;
   }
-  if (rh_quant_supported(U, V, wt, n, ldw, w, q)) {
+  if (rh_quant_supported(U, V, wt, m, n, ldw, w, q)) {
     st = rh_rqp(V, w, wt, m, n, ldw, q, codes, scales, s);
     if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "row Hadamard launch");
     if (st != BRQ_ERR_UNSUPPORTED) return st;

@@ -399,7 +399,9 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
 
     // ---- phase 2: this wave owns r1 = w; fragments over (r2, c2), one per c1.
     const int64_t next = tile + gridDim.x;
-    const FbTile tn = fb_tile(a, next < ntiles ? next : tile);
+    // past the last tile, prefetch tile 0: every workgroup ending there reads
+    // the same block, which then comes from cache instead of HBM
+    const FbTile tn = fb_tile(a, next < ntiles ? next : 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       lanes();
@@ -416,8 +418,8 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
           *reinterpret_cast<f4*>(&xch[fb_xch(lro, lgo + 4 * e, w, 4 * qd)]) = q4;
         }
       // after the second half every tile register is free: load the whole
-      // next tile (the last tile loads itself again, which keeps this code
-      // free of branches)
+      // next tile (past the last one, tile 0, which keeps this code free of
+      // branches)
       if (h == 1) {
         fb_load_half<0>(a, tn, w, lro, lgo, x);
         fb_load_half<1>(a, tn, w, lro, lgo, x);

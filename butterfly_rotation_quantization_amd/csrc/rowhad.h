@@ -170,7 +170,7 @@ bool rh_rotate_supported(const Plan* p, int side, int xt, int yt, int64_t rows, 
                          int64_t ldx, int64_t ldy, const void* x, const void* y);
 brq_status rh_rotate(const Plan* p, int inverse, const void* x, int xt, int64_t ldx, void* y,
                      int yt, int64_t ldy, int64_t rows, int64_t cols, hipStream_t s);
-bool rh_quant_supported(const Plan* U, const Plan* V, int wt, int64_t n, int64_t ldw,
+bool rh_quant_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_t n, int64_t ldw,
                         const void* w, const brq_quant* q);
 brq_status rh_rqp(const Plan* V, const void* w, int wt, int64_t m, int64_t n, int64_t ldw,
                   const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s);

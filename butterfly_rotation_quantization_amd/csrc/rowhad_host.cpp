@@ -115,7 +115,7 @@ brq_status rh_rotate(const Plan* p, int inverse, const void* x, int xt, int64_t 
   return launch(a, name, s);
 }
 
-bool rh_quant_supported(const Plan* U, const Plan* V, int wt, int64_t n, int64_t ldw,
+bool rh_quant_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_t n, int64_t ldw,
                         const void* w, const brq_quant* q) {
   if (U || !rh_plan_ok(V) || n % V->d) return false;
   if (m * (n / V->d) > kRhMaxChunks) return false;
