@@ -249,7 +249,9 @@ class TwoSidedWeight(Workload):
                   else stage_flops(L.radix[1:] + R.radix[1:], False, E))
             blk = 0 if had else 4 * (M * sum(L.radix[1:]) + N * sum(R.radix[1:]))
             return E * 4 + q_out + blk, fl, "mfma"
-        # generic tile pass: "pass L(..) R(..) [quant]"
+        if name.startswith("rowhad quant"):  # quantizer pass over the float32 intermediate
+            return E * 4 + q_out, 0, "alu"
+        # stage pass ("stage L(b) S..") or generic tile pass ("pass L(..) R(..) [quant]")
         radices = []
         for side, d, plan in (("L", M, L), ("R", N, R)):
             m_ = re.search(side + r"\(([0-9,]+)\)", name)

@@ -35,7 +35,7 @@ EXPORTED = (
     "brq_plan_destroy", "brq_plan_dim", "brq_workspace_bytes", "brq_rotate",
     "brq_rotate_inverse", "brq_rotate_quantize_pack", "brq_dequant_unrotate",
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
-    "brq_profile_read",
+    "brq_profile_read", "brq_set_path",
 )
 
 
@@ -107,6 +107,8 @@ def bind(lib):
     lib.brq_profile_read.argtypes = [i32, ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(i64)]
     lib.brq_profile_read.restype = i32
+    lib.brq_set_path.argtypes = [i32]
+    lib.brq_set_path.restype = i32
     return lib
 
 
@@ -301,6 +303,27 @@ def profile_read() -> dict:
         check(L.brq_profile_read(i, buf, 256, ctypes.byref(ms), ctypes.byref(n)))
         out[buf.value.decode()] = (ms.value, n.value)
     return out
+
+
+PATH_AUTO, PATH_TILE = 0, 1
+
+
+def set_path(path: int):
+    """Kernel selection: PATH_AUTO (fastest kernel that takes a call) or
+    PATH_TILE (every call on the multi-stage tile pass)."""
+    check(lib().brq_set_path(int(path)))
+
+
+class tile_path:
+    """Context manager: run the enclosed calls on the tile pass."""
+
+    def __enter__(self):
+        set_path(PATH_TILE)
+        return self
+
+    def __exit__(self, *exc):
+        set_path(PATH_AUTO)
+        return False
 
 
 def lloyd_max_gaussian(bits: int) -> np.ndarray:

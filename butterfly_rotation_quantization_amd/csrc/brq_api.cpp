@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -39,6 +40,9 @@ brq_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+std::atomic<int> g_path{BRQ_PATH_AUTO};
+bool fast_paths() { return g_path.load(std::memory_order_relaxed) == BRQ_PATH_AUTO; }
 
 bool valid_dtype(int32_t t) { return t == BRQ_F32 || t == BRQ_BF16 || t == BRQ_F16; }
 
@@ -430,6 +434,71 @@ brq_status run_inverse(const Plan* U, const Plan* V, const void* src, int src_t,
   return BRQ_OK;
 }
 
+// Plans with dense blocks on either side run as stage passes into the
+// float32 workspace (left side, then right side, in place), followed by a
+// quantizer pass; the inverse is a dequantizer pass into the workspace and
+// the inverse stages.
+bool stage_sides_ok(const Plan* U, const Plan* V, int64_t m, int64_t n) {
+  if (!U && !V) return false;
+  if ((U && !sp_shape_ok(U, 1, m, n)) || (V && !sp_shape_ok(V, 0, m, n))) return false;
+  return (U && U->mode != BRQ_HADAMARD) || (V && V->mode != BRQ_HADAMARD);
+}
+
+brq_status stage_fail(brq_status st, hipError_t he, size_t need, size_t have) {
+  if (st == BRQ_ERR_HIP) return hip_fail(he, "stage pass launch");
+  if (st == BRQ_ERR_WORKSPACE)
+    return fail(st, "workspace of %zu bytes needed, %zu given", need, have);
+  return st;
+}
+
+brq_status stage_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_t m, int64_t n,
+                     int64_t ldw, const brq_quant* q, uint8_t* codes, void* scales, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
+  const size_t need = (size_t)m * n * sizeof(float);
+  if (!ws || ws_bytes < need)
+    return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hipError_t he = hipSuccess;
+  const void* src = w;
+  int src_t = wt;
+  int64_t ld = ldw;
+  for (int side = 1; side >= 0; --side) {  // left, then right
+    const Plan* p = side ? U : V;
+    if (!p) continue;
+    const brq_status st = sp_rotate(p, side, 0, src, src_t, ld, ws, BRQ_F32, n, m, n, ws,
+                                    ws_bytes, s, &he);
+    if (st != BRQ_OK) return stage_fail(st, he, need, ws_bytes);
+    src = ws;
+    src_t = BRQ_F32;
+    ld = n;
+  }
+  const brq_status st = rh_quant_only(ws, BRQ_F32, m, n, n, q, codes, scales, s);
+  if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "quantizer launch");
+  if (st != BRQ_ERR_UNSUPPORTED) return st;
+  return run_forward(nullptr, nullptr, ws, BRQ_F32, n, m, n, nullptr, 0, 0, q, codes, scales,
+                     nullptr, 0, s);
+}
+
+brq_status stage_dequant(const Plan* U, const Plan* V, const uint8_t* codes, const void* scales,
+                         const brq_quant* q, int64_t m, int64_t n, void* out, int ot, int64_t ldo,
+                         void* ws, size_t ws_bytes, hipStream_t s) {
+  const size_t need = (size_t)m * n * sizeof(float);
+  if (!ws || ws_bytes < need)
+    return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  brq_status st = run_inverse(nullptr, nullptr, nullptr, 0, 0, codes, scales, q, m, n, ws,
+                              BRQ_F32, n, nullptr, 0, s);
+  if (st != BRQ_OK) return st;
+  hipError_t he = hipSuccess;
+  for (int side = 0; side <= 1; ++side) {  // right, then left
+    const Plan* p = side ? U : V;
+    if (!p) continue;
+    const bool last = side == 1 || !U;
+    st = sp_rotate(p, side, 1, ws, BRQ_F32, n, last ? out : ws, last ? ot : BRQ_F32,
+                   last ? ldo : n, m, n, ws, ws_bytes, s, &he);
+    if (st != BRQ_OK) return stage_fail(st, he, need, ws_bytes);
+  }
+  return BRQ_OK;
+}
+
 brq_status rotate_common(const brq_plan* plan, int32_t side, int inverse, const void* x,
                          int32_t xt, int64_t ldx, void* y, int32_t yt, int64_t ldy, int64_t rows,
                          int64_t cols, void* ws, size_t ws_bytes, void* stream) {
@@ -455,22 +524,19 @@ brq_status rotate_common(const brq_plan* plan, int32_t side, int inverse, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Plan* U = side == 1 ? p : nullptr;
   const Plan* V = side == 0 ? p : nullptr;
-  if (rh_rotate_supported(p, side, xt, yt, rows, cols, ldx, ldy, x, y)) {
+  if (fast_paths() && rh_rotate_supported(p, side, xt, yt, rows, cols, ldx, ldy, x, y)) {
     st = rh_rotate(p, inverse, x, xt, ldx, y, yt, ldy, rows, cols, s);
     return st == BRQ_OK ? st : hip_fail(hipGetLastError(), "row Hadamard launch");
   }
-  if (!inverse && fused_rotate_supported(U, V, xt, yt, rows, cols, ldx, ldy, x, y))
+  if (fast_paths() && !inverse && fused_rotate_supported(U, V, xt, yt, rows, cols, ldx, ldy, x, y))
     return fused_rotate(U, V, x, xt, ldx, y, yt, ldy, rows, cols, s) == hipSuccess
                ? BRQ_OK
                : hip_fail(hipGetLastError(), "fused rotate launch");
-  if (sp_rotate_supported(p, side, rows, cols)) {
+  if (fast_paths() && sp_rotate_supported(p, side, rows, cols)) {
     hipError_t he = hipSuccess;
     st = sp_rotate(p, side, inverse, x, xt, ldx, y, yt, ldy, rows, cols, ws, ws_bytes, s, &he);
-    if (st == BRQ_ERR_HIP) return hip_fail(he, "stage pass launch");
-    if (st == BRQ_ERR_WORKSPACE)
-      return fail(st, "workspace of %zu bytes needed, %zu given",
-                  (size_t)rows * cols * sizeof(float), ws_bytes);
-    if (st != BRQ_ERR_UNSUPPORTED) return st;
+    if (st != BRQ_ERR_UNSUPPORTED)
+      return stage_fail(st, he, (size_t)rows * cols * sizeof(float), ws_bytes);
   }
   if (!inverse)
     return run_forward(U, V, x, xt, ldx, rows, cols, y, yt, ldy, nullptr, nullptr, nullptr, ws,
@@ -519,6 +585,14 @@ const char* brq_status_string(brq_status s) {
 const char* brq_last_error(void) { return g_last_error.c_str(); }
 
 int32_t brq_version(void) { return 100; }
+
+brq_status brq_set_path(int32_t path) {
+  g_last_error.clear();
+  if (path != BRQ_PATH_AUTO && path != BRQ_PATH_TILE)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+  g_path.store(path, std::memory_order_relaxed);
+  return BRQ_OK;
+}
 
 brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const int32_t* radix,
                            const float* blocks, int32_t mode, const int8_t* signs) {
@@ -663,15 +737,22 @@ brq_status brq_rotate_quantize_pack(const brq_plan* left, const brq_plan* right,
   if ((st = check_plan_device(U)) != BRQ_OK) return st;
   if ((st = check_plan_device(V)) != BRQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fused_rqp_supported(U, V, wt, m, n, ldw, w, q)) {
+  if (fast_paths() && fused_rqp_supported(U, V, wt, m, n, ldw, w, q)) {
     st = fused_rqp(U, V, w, wt, m, n, ldw, q, codes, scales, ws, ws_bytes, s);
     if (st != BRQ_ERR_UNSUPPORTED) return st;
   }
-  if (rh_quant_supported(U, V, wt, m, n, ldw, w, q)) {
+  if (fast_paths() && rh_quant_supported(U, V, wt, m, n, ldw, w, q)) {
     st = rh_rqp(V, w, wt, m, n, ldw, q, codes, scales, s);
     if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "row Hadamard launch");
     if (st != BRQ_ERR_UNSUPPORTED) return st;
   }
+  if (fast_paths() && !U && !V) {
+    st = rh_quant_only(w, wt, m, n, ldw, q, codes, scales, s);
+    if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "quantizer launch");
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+  }
+  if (fast_paths() && stage_sides_ok(U, V, m, n))
+    return stage_rqp(U, V, w, wt, m, n, ldw, q, codes, scales, ws, ws_bytes, s);
   return run_forward(U, V, w, wt, ldw, m, n, nullptr, 0, 0, q, codes, scales, ws, ws_bytes, s);
 }
 
@@ -695,11 +776,14 @@ brq_status brq_dequant_unrotate(const brq_plan* left, const brq_plan* right, con
   if (!codes || !scales || !out) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
   if ((st = check_plan_device(U)) != BRQ_OK) return st;
   if ((st = check_plan_device(V)) != BRQ_OK) return st;
-  if (!U && rh_plan_ok(V) && q->group <= 1024) {
+  if (fast_paths() && !U && rh_plan_ok(V) && q->group <= 1024) {
     st = rh_dequant(V, codes, scales, q, m, n, out, ot, ldo, static_cast<hipStream_t>(stream));
     if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "row Hadamard launch");
     if (st != BRQ_ERR_UNSUPPORTED) return st;
   }
+  if (fast_paths() && stage_sides_ok(U, V, m, n))
+    return stage_dequant(U, V, codes, scales, q, m, n, out, ot, ldo, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream));
   return run_inverse(U, V, nullptr, 0, 0, codes, scales, q, m, n, out, ot, ldo, ws, ws_bytes,
                      static_cast<hipStream_t>(stream));
 }

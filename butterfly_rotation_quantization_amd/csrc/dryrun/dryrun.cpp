@@ -421,6 +421,8 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
   ++g_launches;
   const int l2d = a.log2d, d = 1 << l2d, R = rh_rounds(l2d);
   if (a.nchunks > kRhMaxChunks) return violation("row Hadamard chunk count %lld", a.nchunks, 0), hipErrorInvalidValue;
+  if (a.identity && (a.log2d != 4 || a.signs || a.scale != 1.0f || a.mode != RH_QUANT))
+    return violation("quantize-only launch with a transform (log2 d %lld, mode %lld)", a.log2d, a.mode), hipErrorInvalidValue;
   if (l2d < 4 || l2d > 12 || a.n % d || a.cpr != a.n / d || a.nchunks != a.rows * a.cpr)
     return violation("row Hadamard shape (d %lld, n %lld)", d, a.n), hipErrorInvalidValue;
   {  // the rounds' new bits partition the index bits; each round's layout is a bijection

@@ -42,6 +42,7 @@ struct RhArgs {
   int64_t ldy;
   const float* signs; // d signs (+-1) of the plan, or null
   int inverse;        // apply M^T: signs after the transform instead of before
+  int identity;       // no transform (quantize only): d = 16, no signs, scale 1
   float scale;        // 1 / sqrt(d)
   // quantizer (quantize epilogue, dequantize prologue)
   int qkind, bits, group, nlev;
@@ -176,5 +177,10 @@ brq_status rh_rqp(const Plan* V, const void* w, int wt, int64_t m, int64_t n, in
                   const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s);
 brq_status rh_dequant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q,
                       int64_t m, int64_t n, void* out, int ot, int64_t ldo, hipStream_t s);
+// Quantize + pack with no transform (the quantizer pass after other kernels
+// have rotated into a float32 buffer); BRQ_ERR_UNSUPPORTED when the shape or
+// alignment does not fit the kernel.
+brq_status rh_quant_only(const void* w, int wt, int64_t m, int64_t n, int64_t ldw,
+                         const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s);
 
 }  // namespace brq

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   // transpose to the next round's layout (the last one back to natural order)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    butterflies(v, 4 - rh_nnew(L2D, r));
+    if (!a.identity) butterflies(v, 4 - rh_nnew(L2D, r));
     if (R > 1) {
       const int rn = r + 1 < R ? r + 1 : 0;
       float* wb = lds + rh_lds_base(L2D, r, p.cw, p.cu);
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] *= a.scale;
+  for (int j = 0; j < 16; ++j) v[j] *= a.scale;  // 1 for the identity
   if (a.inverse && a.signs)
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] *= a.signs[16 * p.cu + j];

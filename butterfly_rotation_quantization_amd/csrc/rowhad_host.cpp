@@ -142,6 +142,30 @@ brq_status rh_rqp(const Plan* V, const void* w, int wt, int64_t m, int64_t n, in
   return launch(a, name, s);
 }
 
+brq_status rh_quant_only(const void* w, int wt, int64_t m, int64_t n, int64_t ldw,
+                         const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s) {
+  if (n % 16 || q->group > 1024 || kRhTile % q->group || !rows_aligned(w, wt, ldw) ||
+      m * (n / 16) > kRhMaxChunks || reinterpret_cast<uintptr_t>(codes) % 4 ||
+      reinterpret_cast<uintptr_t>(scales) % 4)
+    return BRQ_ERR_UNSUPPORTED;
+  Plan id;  // d = 16, no blocks or signs: only the shape of the row split
+  id.d = 16;
+  RhArgs a;
+  fill_common(a, &id, m, n);
+  fill_quant(a, q, n);
+  a.mode = RH_QUANT;
+  a.identity = 1;
+  a.scale = 1.0f;
+  a.x = w;
+  a.xt = wt;
+  a.ldx = ldw;
+  a.codes = codes;
+  a.scales = scales;
+  char name[64];
+  snprintf(name, sizeof name, "rowhad quant b%d g%d", q->bits, q->group);
+  return launch(a, name, s);
+}
+
 brq_status rh_dequant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q,
                       int64_t m, int64_t n, void* out, int ot, int64_t ldo, hipStream_t s) {
   if (reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(scales) % 4 ||

@@ -93,13 +93,11 @@ __host__ __device__ inline int64_t sp_off(const SpArgs& a, int64_t line, int64_t
 // The left side's loops walk q with the lines fastest across threads, and any
 // order does.
 __host__ __device__ inline void sp_member(const SpArgs& a, int q, int& g, int& k) {
-  if (a.side == 1 || a.S == 1) {
-    g = q / a.b;
-    k = q - g * a.b;
-  } else {
-    k = q / a.gw;
-    g = q - k * a.gw;
-  }
+  const bool kfast = a.side == 1 || a.S == 1;  // selects, not branches: g and k stay in registers
+  const int div = kfast ? a.b : a.gw;
+  const int hi = q / div, lo = q - hi * div;
+  g = kfast ? hi : lo;
+  k = kfast ? lo : hi;
 }
 
 // LDS slot of (line, group, member) in one tile buffer.
@@ -109,7 +107,9 @@ __host__ __device__ inline int sp_lds(const SpArgs& a, int l, int g, int k) {
 
 hipError_t launch_stage(const SpArgs& a, hipStream_t s);
 
-// Host side (stage_host.cpp).
+// Host side (stage_host.cpp).  sp_shape_ok: the stage pass can run the plan
+// on this shape; sp_rotate_supported: it is also the faster choice.
+bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols);
 bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols);
 brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,
                      void* y, int yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,

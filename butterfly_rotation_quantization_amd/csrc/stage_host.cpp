@@ -68,14 +68,22 @@ StageList stages_of(const Plan* p) {
 
 }  // namespace
 
-bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {
+bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols) {
   if (!p || rows <= 0 || cols <= 0) return false;
   const int64_t lines = side == 0 ? rows : cols;
   const int64_t axis = side == 0 ? cols : rows;  // positions fit sp_pos's 32 bits
-  if (lines > kSpMaxLines || axis % p->d || axis > (int64_t)1 << 30) return false;
+  if (axis % p->d || axis > (int64_t)1 << 30 || (lines + kSpLines - 1) / kSpLines > 65535)
+    return false;
   for (int i = 0; i < p->nst; ++i)
     if (p->radix[i] > 64) return false;
   return true;
+}
+
+bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {
+  if (!sp_shape_ok(p, side, rows, cols)) return false;
+  // dense blocks: a block row in registers beats the tile pass's per-output
+  // block reads at any size; Hadamard plans only where the tile pass starves
+  return p->mode != BRQ_HADAMARD || (side == 0 ? rows : cols) <= kSpMaxLines;
 }
 
 brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,

@@ -26,16 +26,51 @@ __device__ __forceinline__ void sp_store(void* p, int t, int64_t i, float v) {
 
 template <int MAXB>
 __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
-  __shared__ float xin[kSpLines * kSpLineFloats];
-  __shared__ float yout[kSpLines * kSpLineFloats];
+  // one tile buffer: the outputs wait in registers until every input is read
+  __shared__ float buf[kSpLines * kSpLineFloats];
+  __shared__ int spos[kSpLineFloats];  // left side: position of tile member q
   const int u = threadIdx.x;
   const int64_t g0 = (int64_t)blockIdx.x * a.gw;
   const int64_t l0 = (int64_t)blockIdx.y * kSpLines;
   const int ng = (int)(a.ngroups - g0 < a.gw ? a.ngroups - g0 : a.gw);
   const int nl = (int)(a.lines - l0 < kSpLines ? a.lines - l0 : kSpLines);
   const int gb = a.gw * a.b;
+  constexpr int kStep = kSpThreads / kSpLines;  // left side: members per pass over the lines
 
-  // ---- row j of the block of group g (zero beyond b)
+  // ---- tile in.  Right side: thread u owns member u and walks the lines.
+  // Left side: thread u owns line u % 32 and members u / 32 + 8 it, whose
+  // positions come from a table built once per tile.
+  float v[kSpLines];
+  int mg = 0, mk = 0;
+  int64_t mpos = 0;
+  if (a.side == 0) {
+    if (u < gb) {
+      sp_member(a, u, mg, mk);
+      if (mg < ng) {
+        mpos = sp_pos(a, g0 + mg, mk);
+#pragma unroll
+        for (int l = 0; l < kSpLines; ++l)
+          if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, mpos, a.ld_src));
+      }
+    }
+  } else {
+    if (u < gb) {
+      int gg, k;
+      sp_member(a, u, gg, k);
+      spos[u] = gg < ng ? (int)sp_pos(a, g0 + gg, k) : -1;
+    }
+    __syncthreads();
+    const int l = u % kSpLines;
+#pragma unroll
+    for (int it = 0; it < kSpLines; ++it) {
+      const int q = u / kSpLines + kStep * it;
+      const int pos = q < gb ? spos[q] : -1;
+      if (pos >= 0 && l < nl) v[it] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, pos, a.ld_src));
+    }
+  }
+
+  // ---- row j of the block of group g (zero beyond b), loaded while the tile
+  // is in flight
   const int g = u / a.bp;
   const int j = u - g * a.bp;
   const bool act = j < a.b && g < ng;
@@ -67,95 +102,84 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     }
   }
 
-  // ---- tile in: zero the padding members, then the loads
+  // zero the padding members, then write the tile (signs first, forward)
   for (int e = u; e < kSpLines * a.gw; e += kSpThreads) {
     const int l = e / a.gw, gg = e - l * a.gw;
-    for (int k = a.b; k < a.bs; ++k) xin[sp_lds(a, l, gg, k)] = 0.f;
+    for (int k = a.b; k < a.bs; ++k) buf[sp_lds(a, l, gg, k)] = 0.f;
   }
-  // All of a thread's loads are issued before the first LDS write, so they are
-  // in flight together.
-  float v[kSpLines];
   if (a.side == 0) {
-    if (u < gb) {
-      int gg, k;
-      sp_member(a, u, gg, k);
-      if (gg < ng) {
-        const int64_t pos = sp_pos(a, g0 + gg, k);
-        const float sg = a.sign_in ? a.sign_in[pos % a.d] : 1.f;
+    if (u < gb && mg < ng) {
+      const float sg = a.sign_in ? a.sign_in[mpos % a.d] : 1.f;
 #pragma unroll
-        for (int l = 0; l < kSpLines; ++l)
-          if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, pos, a.ld_src));
-#pragma unroll
-        for (int l = 0; l < kSpLines; ++l)
-          if (l < nl) xin[sp_lds(a, l, gg, k)] = sg * v[l];
-      }
+      for (int l = 0; l < kSpLines; ++l)
+        if (l < nl) buf[sp_lds(a, l, mg, mk)] = sg * v[l];
     }
   } else {
     const int l = u % kSpLines;
-    constexpr int kStep = kSpThreads / kSpLines;  // q advances by 8; gb <= 256 gives <= 32 steps
 #pragma unroll
     for (int it = 0; it < kSpLines; ++it) {
       const int q = u / kSpLines + kStep * it;
-      int gg, k;
-      sp_member(a, q, gg, k);
-      if (q < gb && gg < ng && l < nl)
-        v[it] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, sp_pos(a, g0 + gg, k), a.ld_src));
-    }
-#pragma unroll
-    for (int it = 0; it < kSpLines; ++it) {
-      const int q = u / kSpLines + kStep * it;
-      int gg, k;
-      sp_member(a, q, gg, k);
-      if (q < gb && gg < ng && l < nl) {
-        const int64_t pos = sp_pos(a, g0 + gg, k);
+      const int pos = q < gb ? spos[q] : -1;
+      if (pos >= 0 && l < nl) {
+        int gg, k;
+        sp_member(a, q, gg, k);
         const float sg = a.sign_in ? a.sign_in[pos % a.d] : 1.f;
-        xin[sp_lds(a, l, gg, k)] = sg * v[it];
+        buf[sp_lds(a, l, gg, k)] = sg * v[it];
       }
     }
   }
   __syncthreads();
 
-  // ---- y_j = sum_k B[j][k] x_k for every line of the tile
+  // ---- y_j = sum_k B[j][k] x_k for every line of the tile, into registers
+  float acc[kSpLines];
   if (act) {
-    for (int l = 0; l < nl; ++l) {
-      const float* xr = xin + sp_lds(a, l, g, 0);
-      float acc = 0.f;
 #pragma unroll
-      for (int k4 = 0; k4 < MAXB / 4; ++k4) {
-        if (4 * k4 < a.bs) {
-          const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * k4);
-          acc = fmaf(w[4 * k4 + 0], xv.x, acc);
-          acc = fmaf(w[4 * k4 + 1], xv.y, acc);
-          acc = fmaf(w[4 * k4 + 2], xv.z, acc);
-          acc = fmaf(w[4 * k4 + 3], xv.w, acc);
+    for (int l = 0; l < kSpLines; ++l) {
+      if (l < nl) {
+        const float* xr = buf + sp_lds(a, l, g, 0);
+        float s = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < MAXB / 4; ++k4) {
+          if (4 * k4 < a.bs) {
+            const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * k4);
+            s = fmaf(w[4 * k4 + 0], xv.x, s);
+            s = fmaf(w[4 * k4 + 1], xv.y, s);
+            s = fmaf(w[4 * k4 + 2], xv.z, s);
+            s = fmaf(w[4 * k4 + 3], xv.w, s);
+          }
         }
+        acc[l] = s;
       }
-      yout[sp_lds(a, l, g, j)] = acc;
     }
+  }
+  __syncthreads();  // every input read
+  if (act) {
+#pragma unroll
+    for (int l = 0; l < kSpLines; ++l)
+      if (l < nl) buf[sp_lds(a, l, g, j)] = acc[l];
   }
   __syncthreads();
 
   // ---- tile out
   if (a.side == 0) {
-    if (u < gb) {
-      int gg, k;
-      sp_member(a, u, gg, k);
-      if (gg < ng) {
-        const int64_t pos = sp_pos(a, g0 + gg, k);
-        const float sg = a.sign_out ? a.sign_out[pos % a.d] : 1.f;
-        for (int l = 0; l < nl; ++l)
-          sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * yout[sp_lds(a, l, gg, k)]);
-      }
+    if (u < gb && mg < ng) {
+      const float sg = a.sign_out ? a.sign_out[mpos % a.d] : 1.f;
+#pragma unroll
+      for (int l = 0; l < kSpLines; ++l)
+        if (l < nl)
+          sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, mpos, a.ld_dst), sg * buf[sp_lds(a, l, mg, mk)]);
     }
   } else {
     const int l = u % kSpLines;
-    for (int q = u / kSpLines; q < gb; q += kSpThreads / kSpLines) {
-      int gg, k;
-      sp_member(a, q, gg, k);
-      if (gg < ng && l < nl) {
-        const int64_t pos = sp_pos(a, g0 + gg, k);
+#pragma unroll
+    for (int it = 0; it < kSpLines; ++it) {
+      const int q = u / kSpLines + kStep * it;
+      const int pos = q < gb ? spos[q] : -1;
+      if (pos >= 0 && l < nl) {
+        int gg, k;
+        sp_member(a, q, gg, k);
         const float sg = a.sign_out ? a.sign_out[pos % a.d] : 1.f;
-        sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * yout[sp_lds(a, l, gg, k)]);
+        sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * buf[sp_lds(a, l, gg, k)]);
       }
     }
   }

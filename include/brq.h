@@ -187,6 +187,19 @@ int32_t brq_profile_count(void);
 brq_status brq_profile_read(int32_t idx, char* name, size_t name_len, double* total_ms,
                             int64_t* launches);
 
+/*
+ * Kernel selection (diagnostics and tests).  BRQ_PATH_AUTO (the default)
+ * picks the fastest kernels that take a call: the fused two-sided MFMA
+ * kernels, the row Hadamard kernel, the stage pass, else the multi-stage
+ * tile pass.  BRQ_PATH_TILE sends every call to the tile pass, which takes
+ * every plan and shape, so its results can be checked and timed on shapes a
+ * faster kernel would otherwise take.  The setting is process-wide and read
+ * at each call; results agree to the tolerances of the transform, not bit
+ * for bit.  Errors: INVALID_ARGUMENT for an unknown value.
+ */
+typedef enum { BRQ_PATH_AUTO = 0, BRQ_PATH_TILE = 1 } brq_path;
+brq_status brq_set_path(int32_t path);
+
 #ifdef __cplusplus
 }
 #endif

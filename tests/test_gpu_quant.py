@@ -1,6 +1,8 @@
 """GPU parity of rotate+quantize+pack and dequant+unrotate against the oracle
 on small shapes (the Tiny workload and variations of it)."""
 
+import contextlib
+
 import numpy as np
 import pytest
 
@@ -12,6 +14,12 @@ from parity import check_absmax_scales, check_codes, check_f16_norms, check_rota
 from gpu_util import announce, from_dev, lib_plan, orc_plan, to_dev
 
 pytestmark = pytest.mark.gpu
+
+
+def kernels(path):
+    """The automatic kernel choice, or every call on the multi-stage tile pass."""
+    import butterfly_rotation_quantization_amd as brq
+    return brq.tile_path() if path == "tile" else contextlib.nullcontext()
 
 
 def run_case(w_store, dtype, left, right, bits, group, kind="absmax", codebook=None,
@@ -51,12 +59,14 @@ def run_case(w_store, dtype, left, right, bits, group, kind="absmax", codebook=N
     return info
 
 
-def test_tiny_rht_and_harp():
+@pytest.mark.parametrize("path", ["auto", "tile"])
+def test_tiny_rht_and_harp(path):
     cfg = S.tiny()
     for name in ("rht", "harp"):
-        announce(f"tiny {name}")
-        info = run_case(cfg["w"], "f32", None, cfg[name], cfg["bits"], cfg["group"],
-                        what=f"tiny {name}")
+        announce(f"tiny {name} path={path}")
+        with kernels(path):
+            info = run_case(cfg["w"], "f32", None, cfg[name], cfg["bits"], cfg["group"],
+                            what=f"tiny {name} {path}")
         print(name, info)
 
 
@@ -80,31 +90,37 @@ def test_codebook_norm(bits):
     run_case(w, "bf16", None, right, bits, 128, "codebook_norm", cb, what=f"cb{bits}")
 
 
-def test_two_sided_small():
+@pytest.mark.parametrize("path", ["auto", "tile"])
+def test_two_sided_small(path):
     rng = np.random.default_rng(50)
     left = S.random_plan(rng, (4, 4, 4), "per_group")
     right = S.random_plan(rng, (43, 16, 4), "per_group")
     w = S.to_storage(0.02 * rng.standard_t(3, size=(64, 2752)), "bf16")
-    announce("two-sided small (4,4,4) x (43,16,4)")
-    run_case(w, "bf16", left, right, 3, 64, what="two-sided")
+    announce(f"two-sided small (4,4,4) x (43,16,4) path={path}")
+    with kernels(path):
+        run_case(w, "bf16", left, right, 3, 64, what=f"two-sided {path}")
 
 
-def test_left_only_and_quant_only():
+@pytest.mark.parametrize("path", ["auto", "tile"])
+def test_left_only_and_quant_only(path):
     rng = np.random.default_rng(51)
     left = S.random_plan(rng, (16, 8), "per_group")
     w = S.to_storage(rng.standard_normal((128, 320)), "f32")
-    announce("left only")
-    run_case(w, "f32", left, None, 4, 64, what="left only")
-    announce("quant only")
-    run_case(w, "f32", None, None, 3, 64, what="quant only")
+    with kernels(path):
+        announce(f"left only path={path}")
+        run_case(w, "f32", left, None, 4, 64, what=f"left only {path}")
+        announce(f"quant only path={path}")
+        run_case(w, "f32", None, None, 3, 64, what=f"quant only {path}")
 
 
-def test_zero_groups_and_ragged_rows():
+@pytest.mark.parametrize("path", ["auto", "tile"])
+def test_zero_groups_and_ragged_rows(path):
     rng = np.random.default_rng(52)
     right = S.random_plan(rng, (16, 16), "per_group")
     x = rng.standard_normal((13, 512))
     x[3, :] = 0.0
     x[7, 256:] = 0.0
     w = S.to_storage(x, "f32")
-    announce("zero groups")
-    run_case(w, "f32", None, right, 4, 128, what="zero groups")
+    announce(f"zero groups path={path}")
+    with kernels(path):
+        run_case(w, "f32", None, right, 4, 128, what=f"zero groups {path}")

@@ -76,6 +76,33 @@ def test_left_rotate(radix, mode, dt):
     check_rotation(from_dev(xi).T, refi.T, dt, f"left inverse {radix}")
 
 
+@pytest.mark.parametrize("radix,mode", PLANS)
+def test_tile_pass_both_sides(radix, mode):
+    """The same rotations with every call on the multi-stage tile pass (the
+    kernel that takes any plan and shape)."""
+    import butterfly_rotation_quantization_amd as brq
+    side = _side(radix, mode, seed=11)
+    d = side.d
+    rows = 37 if d <= 4096 else 5
+    cols = 2 * d if d <= 512 else d
+    announce(f"tile pass radix={radix} mode={mode}")
+    xs = _input(rows, cols, "f32", seed=5)
+    p = lib_plan(side)
+    with brq.tile_path():
+        y = brq.rotate(p, to_dev(xs, "f32"), side="right")
+        xi = brq.rotate_inverse(p, y, side="right")
+    ref = T.apply_right(orc_plan(side), xs.astype(np.float64), method=method_for(d))
+    check_rotation(from_dev(y), ref, "f32", f"tile right {radix}")
+    refi = T.apply_right(orc_plan(side), from_dev(y), inverse=True, method=method_for(d))
+    check_rotation(from_dev(xi), refi, "f32", f"tile right inverse {radix}")
+    if d <= 4096:
+        xl = _input(d, 45, "f32", seed=6)
+        with brq.tile_path():
+            yl = brq.rotate(p, to_dev(xl, "f32"), side="left")
+        refl = T.apply_left(orc_plan(side), xl.astype(np.float64))
+        check_rotation(from_dev(yl).T, refl.T, "f32", f"tile left {radix}")
+
+
 def test_mixed_dtypes_and_in_place():
     import butterfly_rotation_quantization_amd as brq
     torch = pytest.importorskip("torch")

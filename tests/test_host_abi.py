@@ -137,3 +137,10 @@ def test_lloyd_max_validation(lib):
     assert lib.brq_lloyd_max_gaussian(0, buf.ctypes.data) == 1
     assert lib.brq_lloyd_max_gaussian(6, buf.ctypes.data) == 1
     assert lib.brq_lloyd_max_gaussian(3, None) == 1
+
+
+def test_path_selection(lib):
+    assert lib.brq_set_path(1) == 0
+    assert lib.brq_set_path(0) == 0
+    assert lib.brq_set_path(7) == 1  # INVALID_ARGUMENT
+    assert b"unknown path" in lib.brq_last_error()
