@@ -457,6 +457,12 @@ brq_status stage_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   const size_t need = (size_t)m * n * sizeof(float);
   if (!ws || ws_bytes < need)
     return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  // Schedules ending in (16, 16) on both sides: stage passes for the earlier
+  // stages, then pass B for the last four stages and the quantizer.
+  const bool tail = fused_tail_supported(U, V, m, n, q) &&
+                    reinterpret_cast<uintptr_t>(ws) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(codes) % 4 == 0 &&
+                    reinterpret_cast<uintptr_t>(scales) % 4 == 0;
   hipError_t he = hipSuccess;
   const void* src = w;
   int src_t = wt;
@@ -464,12 +470,19 @@ brq_status stage_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   for (int side = 1; side >= 0; --side) {  // left, then right
     const Plan* p = side ? U : V;
     if (!p) continue;
-    const brq_status st = sp_rotate(p, side, 0, src, src_t, ld, ws, BRQ_F32, n, m, n, ws,
-                                    ws_bytes, s, &he);
+    const brq_status st = sp_rotate_stages(p, side, 0, 0, tail ? p->nst - 2 : -1, src, src_t, ld,
+                                           ws, BRQ_F32, n, m, n, ws, ws_bytes, s, &he);
     if (st != BRQ_OK) return stage_fail(st, he, need, ws_bytes);
     src = ws;
     src_t = BRQ_F32;
     ld = n;
+  }
+  if (tail) {
+    const brq_status st = fused_tail_rqp(U, V, static_cast<const float*>(ws), m, n, q, codes,
+                                         scales, s);
+    if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "pass B launch");
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+    return fail(BRQ_ERR_UNSUPPORTED, "pass B rejected a shape it reported as supported");
   }
   const brq_status st = rh_quant_only(ws, BRQ_F32, m, n, n, q, codes, scales, s);
   if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "quantizer launch");

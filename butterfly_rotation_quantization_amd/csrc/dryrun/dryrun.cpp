@@ -324,7 +324,8 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
     for (int64_t tile = wg; tile < ntiles; tile += grid) {  // the kernel's persistent loop
       tiles_seen[(size_t)tile]++;
       const FbTile t = fb_tile(a, tile);
-      if (t.r0 < 0 || t.r0 >= 16 || t.c0 < 0 || t.c0 >= a.bv || t.chunk < 0 || t.chunk >= a.nchunk)
+      if (t.r0 < 0 || t.r0 >= a.nrb || a.nrb * 256 != a.m || t.c0 < 0 || t.c0 >= a.bv || t.chunk < 0 ||
+          t.chunk >= a.nchunk)
         return violation("pass B tile %lld of %lld", tile, ntiles), hipErrorInvalidValue;
       // block staging into LDS
       for (int k = 0; k < 2 * 16 * 64; ++k) {

@@ -1,5 +1,7 @@
 // Fast path for two-sided plans of the shape U = (bU, 16, 16), V = (bV, 16, 16)
-// (bU = 16, bV <= 64): two kernels on MFMA 16x16x4 float32 tiles.
+// (bU = 16, bV <= 64): two kernels on MFMA 16x16x4 float32 tiles.  Pass B also
+// serves as the tail of longer dense schedules ending in (16, 16) on both
+// sides, after stage passes have applied the earlier stages.
 //
 //  pass A: the stride-256 stages U_0 and V_0.  Rows r0*256 + q (r0 < 16) and
 //          columns c0*256 + p (c0 < bV) of one (q, p) pair form a 16 x bV
@@ -48,9 +50,10 @@ struct FusedAArgs {
 };
 
 struct FusedBArgs {
-  const float* ws;    // float32 intermediate from pass A
+  const float* ws;    // float32 intermediate from pass A (or from stage passes)
   int64_t m, n;
-  int bv;             // radix of V_0: column chunks c0 per d_V
+  int nrb;            // 256-row blocks r0: m / 256
+  int bv;             // 256-column blocks c0 per d_V (the radix of V_0 after pass A)
   int nchunk, dv;
   const float* u1; int64_t u1_gs;  // U_1 blocks [256][16][16], group r0*16 + r2
   const float* u2; int64_t u2_gs;  // U_2 blocks, group r0*16 + r1
@@ -211,13 +214,13 @@ struct FbTile {
 };
 
 __host__ __device__ inline int64_t fb_nwg(const FusedBArgs& a) {
-  return (int64_t)16 * a.bv * a.nchunk;
+  return (int64_t)a.nrb * a.bv * a.nchunk;
 }
 
 __host__ __device__ inline FbTile fb_tile(const FusedBArgs& a, int64_t b) {
   FbTile t;
-  t.r0 = (int)(b % 16);
-  const int64_t rest = b / 16;
+  t.r0 = (int)(b % a.nrb);
+  const int64_t rest = b / a.nrb;
   t.c0 = (int)(rest % a.bv);
   t.chunk = (int)(rest / a.bv);
   return t;
@@ -263,6 +266,14 @@ bool fused_rqp_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_
 brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_t m, int64_t n,
                      int64_t ldw, const brq_quant* q, uint8_t* codes, void* scales, void* ws,
                      size_t ws_bytes, hipStream_t s);
+
+// Pass B alone as the tail of a two-sided transform whose last two stages are
+// radix 16 on both sides (dense blocks, m and d_V multiples of 256): the
+// caller has applied every earlier stage into the float32 workspace `ws`;
+// pass B applies U_{m-2}, U_{m-1}, V_{m-2}, V_{m-1}, quantizes and packs.
+bool fused_tail_supported(const Plan* U, const Plan* V, int64_t m, int64_t n, const brq_quant* q);
+brq_status fused_tail_rqp(const Plan* U, const Plan* V, const float* ws, int64_t m, int64_t n,
+                          const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s);
 
 // Kernel launchers (fused_kernels.hip; the dry-run build walks their indices).
 // Pass B is persistent: `grid` workgroups (<= its tile count) loop over tiles

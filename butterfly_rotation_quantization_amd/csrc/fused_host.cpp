@@ -116,6 +116,8 @@ int fused_b_grid(const FusedBArgs& b) {
   return (int)(nt < cus ? nt : cus);
 }
 
+const char* check_b(const FusedBArgs& b);
+
 // Host check of what the two kernels' index arithmetic relies on.
 const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (a.bv < 2 || a.bv > 64 || a.nb != (a.bv + 15) / 16) return "V_0 radix";
@@ -135,9 +137,18 @@ const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (a.u0_n < 256 || a.v0_n < 256 * a.nb * a.nb) return "block extent";
   if (b.bv != a.bv || b.nchunk != a.nchunk || b.dv != a.dv || b.m != a.m || b.n != a.n)
     return "pass B shape";
-  if (!b.u1 || !b.u2 || !b.v1 || !b.v2 || !b.codes || !b.scales) return "pass B pointers";
-  if (b.u1_gs && b.u1_n < 256 * b.u1_gs) return "U_1 extent";
-  if (b.u2_gs && b.u2_n < 256 * b.u2_gs) return "U_2 extent";
+  return check_b(b);
+}
+
+// Host check of pass B alone.
+const char* check_b(const FusedBArgs& b) {
+  if (b.m < 256 || b.m % 256 || b.nrb != b.m / 256 || b.dv != b.bv * 256 || b.bv < 1 ||
+      (int64_t)b.nchunk * b.dv != b.n)
+    return "pass B shape";
+  if ((int64_t)b.m * b.n * 4 >= (int64_t(1) << 40)) return "pass B extent";
+  if (!b.ws || !b.u1 || !b.u2 || !b.v1 || !b.v2 || !b.codes || !b.scales) return "pass B pointers";
+  if (b.u1_gs && b.u1_n < (int64_t)b.nrb * 16 * b.u1_gs) return "U_1 extent";
+  if (b.u2_gs && b.u2_n < (int64_t)b.nrb * 16 * b.u2_gs) return "U_2 extent";
   if (b.v1_gs && b.v1_n < (int64_t)b.bv * 16 * b.v1_gs) return "V_1 extent";
   if (b.v2_gs && b.v2_n < (int64_t)b.bv * 16 * b.v2_gs) return "V_2 extent";
   if (b.group != 64 && b.group != 128) return "group";
@@ -145,6 +156,19 @@ const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (b.codes_ld * 8 != b.n * b.bits || b.codes_ld % 4 || b.scales_ld * b.group != b.n)
     return "code layout";
   return nullptr;
+}
+
+void fill_quant_b(FusedBArgs& b, const brq_quant* q, int64_t n) {
+  b.qkind = q->kind;
+  b.bits = q->bits;
+  b.group = q->group;
+  b.nlev = 1 << q->bits;
+  b.h = (float)((b.nlev - 1) * 0.5);
+  b.sqrt_g = std::sqrt((float)q->group);
+  for (int i = 0; i + 1 < b.nlev; ++i)
+    b.tau[i] = q->kind == BRQ_CODEBOOK_NORM ? (q->codebook[i] + q->codebook[i + 1]) * 0.5f : 0.f;
+  b.codes_ld = n * q->bits / 8;
+  b.scales_ld = n / q->group;
 }
 
 }  // namespace
@@ -213,6 +237,7 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   b.ws = a.ws;
   b.m = m;
   b.n = n;
+  b.nrb = (int)(m / 256);
   b.bv = a.bv;
   b.nchunk = a.nchunk;
   b.dv = a.dv;
@@ -224,18 +249,9 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   b.v1_gs = V->fz_gs1;
   b.v2 = V->fz2;
   b.v2_gs = V->fz_gs2;
-  b.qkind = q->kind;
-  b.bits = q->bits;
-  b.group = q->group;
-  b.nlev = 1 << q->bits;
-  b.h = (float)((b.nlev - 1) * 0.5);
-  b.sqrt_g = std::sqrt((float)q->group);
-  for (int i = 0; i + 1 < b.nlev; ++i)
-    b.tau[i] = q->kind == BRQ_CODEBOOK_NORM ? (q->codebook[i] + q->codebook[i + 1]) * 0.5f : 0.f;
+  fill_quant_b(b, q, n);
   b.codes = codes;
   b.scales = scales;
-  b.codes_ld = n * q->bits / 8;
-  b.scales_ld = n / q->group;
   const int64_t u16 = U->mode == BRQ_PER_GROUP ? (int64_t)(U->d / 16) * 256 : 256;
   const int64_t v16 = V->mode == BRQ_PER_GROUP ? (int64_t)(V->d / 16) * 256 : 256;
   a.u0_n = (U->fz_gs0 ? 256 : 1) * 256;
@@ -253,6 +269,56 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   snprintf(name, sizeof name, "fusedB U(16,16) V(16,16) quant b%d g%d", q->bits, q->group);
   tok = prof_begin(name, s);
   e = launch_fused_b(b, fused_b_grid(b), s);
+  prof_end(tok, s);
+  return e == hipSuccess ? BRQ_OK : BRQ_ERR_HIP;
+}
+
+namespace {
+// The last two stages of a dense plan are radix 16 (and the plan has more).
+bool dense_tail16(const Plan* p) {
+  return p && p->mode != BRQ_HADAMARD && p->nst >= 3 && p->radix[p->nst - 2] == 16 &&
+         p->radix[p->nst - 1] == 16 && p->d % 256 == 0;
+}
+}  // namespace
+
+bool fused_tail_supported(const Plan* U, const Plan* V, int64_t m, int64_t n, const brq_quant* q) {
+  if (!dense_tail16(U) || !dense_tail16(V) || U->d != m || n % V->d) return false;
+  if (q->group != 64 && q->group != 128) return false;
+  return (n * q->bits) % 32 == 0;
+}
+
+brq_status fused_tail_rqp(const Plan* U, const Plan* V, const float* ws, int64_t m, int64_t n,
+                          const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s) {
+  if (reinterpret_cast<uintptr_t>(ws) % 16 || reinterpret_cast<uintptr_t>(codes) % 4 ||
+      reinterpret_cast<uintptr_t>(scales) % 4)
+    return BRQ_ERR_UNSUPPORTED;
+  FusedBArgs b;
+  std::memset(&b, 0, sizeof b);
+  b.ws = ws;
+  b.m = m;
+  b.n = n;
+  b.nrb = (int)(m / 256);
+  b.bv = V->d / 256;
+  b.dv = V->d;
+  b.nchunk = (int)(n / V->d);
+  // stage t's per-group blocks: group c at c * 256 floats (shared: one block)
+  const bool ug = U->mode == BRQ_PER_GROUP, vg = V->mode == BRQ_PER_GROUP;
+  b.u1 = U->blk + U->blk_off[U->nst - 2];
+  b.u2 = U->blk + U->blk_off[U->nst - 1];
+  b.v1 = V->blk + V->blk_off[V->nst - 2];
+  b.v2 = V->blk + V->blk_off[V->nst - 1];
+  b.u1_gs = b.u2_gs = ug ? 256 : 0;
+  b.v1_gs = b.v2_gs = vg ? 256 : 0;
+  b.u1_n = b.u2_n = ug ? (int64_t)(U->d / 16) * 256 : 256;
+  b.v1_n = b.v2_n = vg ? (int64_t)(V->d / 16) * 256 : 256;
+  fill_quant_b(b, q, n);
+  b.codes = codes;
+  b.scales = scales;
+  if (check_b(b)) return BRQ_ERR_UNSUPPORTED;
+  char name[96];
+  snprintf(name, sizeof name, "fusedB U(16,16) V(16,16) quant b%d g%d", q->bits, q->group);
+  const int tok = prof_begin(name, s);
+  const hipError_t e = launch_fused_b(b, fused_b_grid(b), s);
   prof_end(tok, s);
   return e == hipSuccess ? BRQ_OK : BRQ_ERR_HIP;
 }

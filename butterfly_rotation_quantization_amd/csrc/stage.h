@@ -114,5 +114,12 @@ bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols);
 brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,
                      void* y, int yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
                      size_t ws_bytes, hipStream_t s, hipError_t* herr);
+// Stages [t_begin, t_end) of the plan only (t_end = -1: to the last), in
+// forward order (inverse: the same range, transposed, last stage first); the
+// signs go with stage 0, so a range that starts later applies none.
+brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, int t_end,
+                            const void* x, int xt, int64_t ldx, void* y, int yt, int64_t ldy,
+                            int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t s,
+                            hipError_t* herr);
 
 }  // namespace brq

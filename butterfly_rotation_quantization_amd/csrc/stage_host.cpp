@@ -89,9 +89,29 @@ bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {
 brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,
                      void* y, int yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
                      size_t ws_bytes, hipStream_t s, hipError_t* herr) {
+  return sp_rotate_stages(p, side, inverse, 0, -1, x, xt, ldx, y, yt, ldy, rows, cols, ws,
+                          ws_bytes, s, herr);
+}
+
+brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, int t_end,
+                            const void* x, int xt, int64_t ldx, void* y, int yt, int64_t ldy,
+                            int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t s,
+                            hipError_t* herr) {
   *herr = hipSuccess;
-  const StageList L = stages_of(p);
-  if (L.n == 0) return BRQ_ERR_UNSUPPORTED;
+  StageList L = stages_of(p);
+  if (t_end < 0) t_end = L.n;
+  if (t_begin < 0 || t_end > L.n || t_begin >= t_end) return BRQ_ERR_UNSUPPORTED;
+  const bool signs_here = t_begin == 0;  // the signs go with stage 0
+  {  // keep stages [t_begin, t_end) of the list
+    StageList R;
+    for (int i = t_begin; i < t_end; ++i) {
+      R.b[R.n] = L.b[i];
+      R.S[R.n] = L.S[i];
+      R.t[R.n] = L.t[i];
+      ++R.n;
+    }
+    L = R;
+  }
   // intermediate: y itself when it is float32, else the workspace
   void* mid = y;
   int64_t ldm = ldy;
@@ -123,8 +143,8 @@ brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt
                 ? nullptr
                 : (inverse ? p->blkT : p->blk) + p->blk_off[L.t[si]];
     a.blk_vec = a.blk && a.b % 4 == 0 && reinterpret_cast<uintptr_t>(a.blk) % 16 == 0;
-    a.sign_in = (!inverse && i == 0) ? p->signs : nullptr;
-    a.sign_out = (inverse && i == L.n - 1) ? p->signs : nullptr;
+    a.sign_in = (!inverse && i == 0 && signs_here) ? p->signs : nullptr;
+    a.sign_out = (inverse && i == L.n - 1 && signs_here) ? p->signs : nullptr;
     a.src = i == 0 ? x : mid;
     a.src_t = i == 0 ? xt : BRQ_F32;
     a.ld_src = i == 0 ? ldx : ldm;

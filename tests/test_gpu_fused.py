@@ -66,28 +66,39 @@ def test_fused_two_sided(bv, mode, chunks, bits, group, dt, kind):
 
 
 def test_fused_deterministic_and_matches_generic():
-    """Same inputs twice give identical bytes; the generic tile pass (forced
-    by an unaligned leading dimension) agrees outside the decision band."""
+    """Same inputs twice give identical bytes; the other routes for the same
+    plans agree outside the decision band: stage passes + pass B (taken for an
+    input whose rows are only 8-byte aligned) and the multi-stage tile pass."""
     import butterfly_rotation_quantization_amd as brq
     torch = pytest.importorskip("torch")
-    announce("fused determinism and generic agreement")
+    announce("fused determinism and agreement with the other routes")
     cfg = S.harp_mlp()
     U, V = lib_plan(cfg["left"]), lib_plan(cfg["right"])
     w = to_dev(cfg["w"], "bf16")
     c1, s1 = brq.rotate_quantize_pack(U, V, w, 3, 128)
     c2, s2 = brq.rotate_quantize_pack(U, V, w, 3, 128)
     assert torch.equal(c1, c2) and torch.equal(s1, s2)
-    # a copy with leading dimension n + 4 (8-byte row alignment) takes the generic path
+    a = Q.unpack(c1.cpu().numpy(), 3, 11008)
+    # a copy with leading dimension n + 4 (8-byte row alignment): pass A does
+    # not take it, so stage passes apply the first stages and pass B the rest
     wide = torch.zeros((4096, 11008 + 4), dtype=torch.bfloat16, device="cuda")
     wide[:, :11008] = w
-    brq.profile_reset()
-    brq.profile_enable(True)
-    c3, s3 = brq.rotate_quantize_pack(U, V, wide[:, :11008], 3, 128)
-    brq.profile_enable(False)
-    assert not any(k.startswith("fused") for k in brq.profile_read())
-    a = Q.unpack(c1.cpu().numpy(), 3, 11008)
-    b = Q.unpack(c3.cpu().numpy(), 3, 11008)
-    diff = a != b
-    assert diff.mean() < 1e-5, diff.sum()
-    rel = (s1 - s3).abs().max().item() / s1.abs().max().item()
-    assert rel < 1e-5
+    for route in ("stages + pass B", "tile pass"):
+        brq.profile_reset()
+        brq.profile_enable(True)
+        if route == "tile pass":
+            with brq.tile_path():
+                c3, s3 = brq.rotate_quantize_pack(U, V, w, 3, 128)
+        else:
+            c3, s3 = brq.rotate_quantize_pack(U, V, wide[:, :11008], 3, 128)
+        names = list(brq.profile_read())
+        brq.profile_enable(False)
+        if route == "tile pass":
+            assert all(k.startswith("pass") for k in names), names
+        else:
+            assert names[-1].startswith("fusedB") and all(k.startswith("stage") for k in names[:-1]), names
+        b = Q.unpack(c3.cpu().numpy(), 3, 11008)
+        diff = a != b
+        assert diff.mean() < 1e-5, (route, diff.sum())
+        rel = (s1 - s3).abs().max().item() / s1.abs().max().item()
+        assert rel < 1e-5, (route, rel)

@@ -124,3 +124,24 @@ def test_zero_groups_and_ragged_rows(path):
     announce(f"zero groups path={path}")
     with kernels(path):
         run_case(w, "f32", None, right, 4, 128, what=f"zero groups {path}")
+
+
+@pytest.mark.parametrize("bits,group", [(2, 64), (4, 128)])
+def test_stage_head_pass_b_tail(bits, group):
+    """Dense schedules ending in (16, 16) on both sides run as stage passes
+    for the earlier stages and pass B for the last four and the quantizer
+    (the 70B weight's route), here on a full matrix the oracle covers."""
+    import butterfly_rotation_quantization_amd as brq
+    rng = np.random.default_rng(60 + bits)
+    left = S.random_plan(rng, (4, 16, 16), "per_group")
+    right = S.random_plan(rng, (3, 16, 16, 16), "per_group")
+    w = S.to_storage(0.02 * rng.standard_t(3, size=(1024, 12288)), "bf16")
+    announce(f"stage head + pass B tail b{bits} g{group}")
+    brq.profile_reset()
+    brq.profile_enable(True)
+    info = run_case(w, "bf16", left, right, bits, group, what=f"tail b{bits} g{group}",
+                    method="factored")
+    names = list(brq.profile_read())
+    brq.profile_enable(False)
+    assert any(n.startswith("fusedB") for n in names), names
+    print(info)

@@ -205,3 +205,20 @@ def test_stage_pass_launches(dl, radix, mode, lines, chunks):
         if d <= 8192:
             _rotate(dl, p, 1, d, lines, 1, 1, inverse=inverse)
             assert dl.brq_dryrun_launches() == nst
+
+
+def test_stage_head_pass_b_tail_launches(dl):
+    """Dense two-sided schedules ending in (16, 16) on both sides: stage passes
+    for the earlier stages, then pass B (tiles of 256 rows over any number of
+    256-row blocks)."""
+    rng = np.random.default_rng(77)
+    u = DPlan(dl, S.random_plan(rng, (4, 16, 16), "per_group"))
+    v = DPlan(dl, S.random_plan(rng, (3, 16, 16, 16), "per_group"))
+    m, n = 1024, 12288
+    q = brq.make_quant(2, 64)
+    ws = dl.brq_workspace_bytes(u.h, v.h, m, n)
+    dl.brq_dryrun_reset()
+    st = dl.brq_rotate_quantize_pack(u.h, v.h, X, 1, m, n, n, ctypes.byref(q), CODES, SCALES,
+                                     WS, ws, None)
+    _ok(dl, st, "stage head + pass B tail")
+    assert dl.brq_dryrun_launches() == 1 + 2 + 1  # L(4), R(3), R(16) S256, pass B
