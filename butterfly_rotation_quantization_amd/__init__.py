@@ -107,8 +107,9 @@ def bind(lib):
     lib.brq_profile_read.argtypes = [i32, ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(i64)]
     lib.brq_profile_read.restype = i32
-    lib.brq_set_path.argtypes = [i32]
-    lib.brq_set_path.restype = i32
+    if hasattr(lib, "brq_set_path"):  # libraries built before the path switch lack it
+        lib.brq_set_path.argtypes = [i32]
+        lib.brq_set_path.restype = i32
     return lib
 
 

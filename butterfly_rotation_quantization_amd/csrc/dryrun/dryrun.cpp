@@ -575,15 +575,22 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
   const int64_t cols = a.side == 0 ? axis_len : a.lines;
   if (a.ld_src < cols || a.ld_dst < cols)
     return violation("stage pass leading dimension (%lld < %lld)", std::min(a.ld_src, a.ld_dst), cols), hipErrorInvalidValue;
-  const int64_t gx = sp_group_tiles(a), gy = sp_line_tiles(a);
+  const int64_t gx = a.side ? sp_line_tiles(a) : sp_group_tiles(a);
+  const int64_t gy = a.side ? sp_group_tiles(a) : sp_line_tiles(a);
   if (gy > 65535 || gx >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld, %lld)", gx, gy), hipErrorInvalidValue;
   const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
   const int kLds = kSpLines * kSpLineFloats;
   std::vector<uint8_t> cover((size_t)(rows * cols), 0);
   std::vector<int> xin(kLds), yout(kLds);
+  std::vector<uint8_t> tile_seen((size_t)(sp_group_tiles(a) * sp_line_tiles(a)), 0);
   for (int64_t bx = 0; bx < gx; ++bx)
     for (int64_t by = 0; by < gy; ++by) {
-      const int64_t g0 = bx * a.gw, l0 = by * kSpLines;
+      int64_t gt, lt;
+      sp_tile_of_block(a, bx, by, gt, lt);
+      if (gt < 0 || gt >= sp_group_tiles(a) || lt < 0 || lt >= sp_line_tiles(a) ||
+          tile_seen[(size_t)(gt * sp_line_tiles(a) + lt)]++)
+        return violation("stage pass block (%lld, %lld) maps to a bad or repeated tile", bx, by), hipErrorInvalidValue;
+      const int64_t g0 = gt * a.gw, l0 = lt * kSpLines;
       const int ng = (int)std::min<int64_t>(a.ngroups - g0, a.gw);
       const int nl = (int)std::min<int64_t>(a.lines - l0, kSpLines);
       const int gb = a.gw * b;
@@ -642,6 +649,8 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
         if (line >= a.lines || off < 0 || off >= (a.side == 0 ? rows * a.ld_src : axis_len * a.ld_src))
           return violation("stage pass load at %lld (line %lld)", off, line);
         const int s = sp_lds(a, l, gg, k);
+        if (s != sp_lds(a, l, 0, 0) + sp_lds(a, 0, gg, k)) return violation("LDS slot split at %lld", s, 0);
+        if (a.side == 1 && pos >= a.d) return violation("left-side sign index %lld", pos, a.d);
         if (s < 0 || s >= kLds || xin[s]) return violation("LDS slot %lld loaded twice", s, 0);
         xin[s] = 1;
         return true;

@@ -61,6 +61,14 @@ __host__ __device__ inline int64_t sp_group_tiles(const SpArgs& a) {
 __host__ __device__ inline int64_t sp_line_tiles(const SpArgs& a) {
   return (a.lines + kSpLines - 1) / kSpLines;
 }
+// Grid: right side (group tiles, line tiles), left side (line tiles, group
+// tiles), so that consecutive workgroups cover consecutive addresses (the
+// next groups of the same rows, or the next columns of the same rows).
+__host__ __device__ inline void sp_tile_of_block(const SpArgs& a, int64_t bx, int64_t by,
+                                                 int64_t& gt, int64_t& lt) {
+  gt = a.side ? by : bx;
+  lt = a.side ? bx : by;
+}
 
 // Position along the transformed axis of member k of group gid (global over
 // chunks), in 32-bit arithmetic: the host keeps every position below 2^31.

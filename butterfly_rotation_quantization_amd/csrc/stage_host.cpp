@@ -72,8 +72,8 @@ bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols) {
   if (!p || rows <= 0 || cols <= 0) return false;
   const int64_t lines = side == 0 ? rows : cols;
   const int64_t axis = side == 0 ? cols : rows;  // positions fit sp_pos's 32 bits
-  if (axis % p->d || axis > (int64_t)1 << 30 || (lines + kSpLines - 1) / kSpLines > 65535)
-    return false;
+  if (axis % p->d || axis > (int64_t)1 << 30) return false;
+  if (side == 0 && (lines + kSpLines - 1) / kSpLines > 65535) return false;  // grid y
   for (int i = 0; i < p->nst; ++i)
     if (p->radix[i] > 64) return false;
   return true;
@@ -121,7 +121,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     ldm = cols;
   }
   const int64_t lines = side == 0 ? rows : cols;
-  if ((lines + kSpLines - 1) / kSpLines > 65535) return BRQ_ERR_UNSUPPORTED;
+  if (side == 0 && (lines + kSpLines - 1) / kSpLines > 65535) return BRQ_ERR_UNSUPPORTED;
   for (int i = 0; i < L.n; ++i) {
     const int si = inverse ? L.n - 1 - i : i;
     SpArgs a;
@@ -132,6 +132,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.bs = (a.b + 3) & ~3;
     a.gw = kSpThreads / a.bp;
     if (a.gw * a.bs > kSpLineFloats) a.gw = kSpLineFloats / a.bs;
+    if (side == 1 && sp_group_tiles(a) > 65535) return BRQ_ERR_UNSUPPORTED;  // grid y
     a.mode = p->mode;
     a.S = L.S[si];
     a.d = p->d;

@@ -28,10 +28,13 @@ template <int MAXB>
 __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   // one tile buffer: the outputs wait in registers until every input is read
   __shared__ float buf[kSpLines * kSpLineFloats];
-  __shared__ int spos[kSpLineFloats];  // left side: position of tile member q
+  __shared__ int spos[kSpLineFloats];   // left side: position of tile member q (-1: none)
+  __shared__ int sslot[kSpLineFloats];  // left side: its LDS offset within a line
   const int u = threadIdx.x;
-  const int64_t g0 = (int64_t)blockIdx.x * a.gw;
-  const int64_t l0 = (int64_t)blockIdx.y * kSpLines;
+  int64_t gt, lt;
+  sp_tile_of_block(a, blockIdx.x, blockIdx.y, gt, lt);
+  const int64_t g0 = gt * a.gw;
+  const int64_t l0 = lt * kSpLines;
   const int ng = (int)(a.ngroups - g0 < a.gw ? a.ngroups - g0 : a.gw);
   const int nl = (int)(a.lines - l0 < kSpLines ? a.lines - l0 : kSpLines);
   const int gb = a.gw * a.b;
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
       int gg, k;
       sp_member(a, u, gg, k);
       spos[u] = gg < ng ? (int)sp_pos(a, g0 + gg, k) : -1;
+      sslot[u] = sp_lds(a, 0, gg, k);
     }
     __syncthreads();
     const int l = u % kSpLines;
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   }
   if (a.side == 0) {
     if (u < gb && mg < ng) {
-      const float sg = a.sign_in ? a.sign_in[mpos % a.d] : 1.f;
+      const float sg = a.sign_in ? a.sign_in[(uint32_t)mpos % (uint32_t)a.d] : 1.f;
 #pragma unroll
       for (int l = 0; l < kSpLines; ++l)
         if (l < nl) buf[sp_lds(a, l, mg, mk)] = sg * v[l];
@@ -120,11 +124,9 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     for (int it = 0; it < kSpLines; ++it) {
       const int q = u / kSpLines + kStep * it;
       const int pos = q < gb ? spos[q] : -1;
-      if (pos >= 0 && l < nl) {
-        int gg, k;
-        sp_member(a, q, gg, k);
-        const float sg = a.sign_in ? a.sign_in[pos % a.d] : 1.f;
-        buf[sp_lds(a, l, gg, k)] = sg * v[it];
+      if (pos >= 0 && l < nl) {  // left side: one chunk, so the position is the sign index
+        const float sg = a.sign_in ? a.sign_in[pos] : 1.f;
+        buf[sp_lds(a, l, 0, 0) + sslot[q]] = sg * v[it];
       }
     }
   }
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   // ---- tile out
   if (a.side == 0) {
     if (u < gb && mg < ng) {
-      const float sg = a.sign_out ? a.sign_out[mpos % a.d] : 1.f;
+      const float sg = a.sign_out ? a.sign_out[(uint32_t)mpos % (uint32_t)a.d] : 1.f;
 #pragma unroll
       for (int l = 0; l < kSpLines; ++l)
         if (l < nl)
@@ -176,10 +178,8 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
       const int q = u / kSpLines + kStep * it;
       const int pos = q < gb ? spos[q] : -1;
       if (pos >= 0 && l < nl) {
-        int gg, k;
-        sp_member(a, q, gg, k);
-        const float sg = a.sign_out ? a.sign_out[pos % a.d] : 1.f;
-        sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * buf[sp_lds(a, l, gg, k)]);
+        const float sg = a.sign_out ? a.sign_out[pos] : 1.f;
+        sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, pos, a.ld_dst), sg * buf[sp_lds(a, l, 0, 0) + sslot[q]]);
       }
     }
   }
@@ -187,7 +187,8 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
 
 template <int MAXB>
 hipError_t launch_t(const SpArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)sp_group_tiles(a), (unsigned)sp_line_tiles(a));
+  const dim3 grid = a.side ? dim3((unsigned)sp_line_tiles(a), (unsigned)sp_group_tiles(a))
+                           : dim3((unsigned)sp_group_tiles(a), (unsigned)sp_line_tiles(a));
   hipLaunchKernelGGL((stage_kernel<MAXB>), grid, dim3(kSpThreads), 0, s, a);
   return hipGetLastError();
 }
