@@ -132,13 +132,24 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.bs = (a.b + 3) & ~3;
     a.gw = kSpThreads / a.bp;
     if (a.gw * a.bs > kSpLineFloats) a.gw = kSpLineFloats / a.bs;
-    if (side == 1 && sp_group_tiles(a) > 65535) return BRQ_ERR_UNSUPPORTED;  // grid y
+    // a forward right-side pair (16, S = 16) then (16, 1) runs in one launch:
+    // the tile is one block of 256 consecutive positions
+    const bool pair = !inverse && side == 0 && i + 1 < L.n && L.b[si] == 16 &&
+                      L.b[si + 1] == 16 && L.S[si] == 16 && L.S[si + 1] == 1 &&
+                      (p->mode == BRQ_HADAMARD ||
+                       reinterpret_cast<uintptr_t>(p->blk + p->blk_off[L.t[si + 1]]) % 16 == 0);
+    if (pair) {
+      a.gw = (int)L.S[si];
+      a.b2 = L.b[si + 1];
+      a.blk2 = p->mode == BRQ_HADAMARD ? nullptr : p->blk + p->blk_off[L.t[si + 1]];
+    }
     a.mode = p->mode;
     a.S = L.S[si];
     a.d = p->d;
     a.ngc = p->d / a.b;
     a.ngroups = (side == 0 ? cols / p->d : 1) * a.ngc;
     a.lines = lines;
+    if (side == 1 && sp_group_tiles(a) > 65535) return BRQ_ERR_UNSUPPORTED;  // grid y
     a.hscale = 1.0f / std::sqrt((float)a.b);
     a.blk = p->mode == BRQ_HADAMARD
                 ? nullptr
@@ -149,13 +160,16 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.src = i == 0 ? x : mid;
     a.src_t = i == 0 ? xt : BRQ_F32;
     a.ld_src = i == 0 ? ldx : ldm;
-    const bool last = i == L.n - 1;
+    const bool last = i + (pair ? 1 : 0) == L.n - 1;
     a.dst = last ? y : mid;
     a.dst_t = last ? yt : BRQ_F32;
     a.ld_dst = last ? ldy : ldm;
     char name[64];
-    snprintf(name, sizeof name, "stage %s%s(%d) S%lld", side == 0 ? "R" : "L",
-             inverse ? "^T" : "", a.b, (long long)a.S);
+    if (pair)
+      snprintf(name, sizeof name, "stage R(%d,%d) S%lld", a.b, a.b2, (long long)a.S);
+    else
+      snprintf(name, sizeof name, "stage %s%s(%d) S%lld", side == 0 ? "R" : "L",
+               inverse ? "^T" : "", a.b, (long long)a.S);
     const int tok = prof_begin(name, s);
     const hipError_t e = launch_stage(a, s);
     prof_end(tok, s);
@@ -163,6 +177,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
       *herr = e;
       return BRQ_ERR_HIP;
     }
+    if (pair) ++i;  // the second stage of the pair is done
   }
   return BRQ_OK;
 }

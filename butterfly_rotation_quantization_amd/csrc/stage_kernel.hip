@@ -155,12 +155,54 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     }
   }
   __syncthreads();  // every input read
-  if (act) {
+  if (act) {  // a pair's first stage leaves its outputs in position order
 #pragma unroll
     for (int l = 0; l < kSpLines; ++l)
-      if (l < nl) buf[sp_lds(a, l, g, j)] = acc[l];
+      if (l < nl) buf[a.b2 ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j)] = acc[l];
   }
   __syncthreads();
+
+  // ---- the optional second stage (radix 16, stride 1) on the same tile: its
+  // group g2 is positions 16 g2 .. 16 g2 + 15, consecutive slots (g2, k2)
+  if (a.b2) {
+    const int g2 = u >> 4, j2 = u & 15;
+    float w2[16];
+    if (a.mode == BRQ_HADAMARD) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w2[k] = (__popc(j2 & k) & 1) ? -0.25f : 0.25f;
+    } else {
+      const float* row = a.blk2 + sp_block_row2(a, g0, g2, j2);
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const float4 q = *reinterpret_cast<const float4*>(row + 4 * k4);
+        w2[4 * k4] = q.x;
+        w2[4 * k4 + 1] = q.y;
+        w2[4 * k4 + 2] = q.z;
+        w2[4 * k4 + 3] = q.w;
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < kSpLines; ++l) {
+      if (l < nl) {
+        const float* xr = buf + sp_lds(a, l, g2, 0);
+        float s2 = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * k4);
+          s2 = fmaf(w2[4 * k4 + 0], xv.x, s2);
+          s2 = fmaf(w2[4 * k4 + 1], xv.y, s2);
+          s2 = fmaf(w2[4 * k4 + 2], xv.z, s2);
+          s2 = fmaf(w2[4 * k4 + 3], xv.w, s2);
+        }
+        acc[l] = s2;
+      }
+    }
+    __syncthreads();  // every first-stage output read
+#pragma unroll
+    for (int l = 0; l < kSpLines; ++l)
+      if (l < nl) buf[sp_lds(a, l, j2, g2)] = acc[l];
+    __syncthreads();
+  }
 
   // ---- tile out
   if (a.side == 0) {
