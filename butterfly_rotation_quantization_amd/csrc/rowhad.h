@@ -57,12 +57,17 @@ struct RhArgs {
   // when no such scaling exists.
   float bin_s, bin_off;
   int tbin[kMaxLevels];
+  // The bin table itself, built on the host: bin b holds {its threshold or
+  // +inf, the number of thresholds in lower bins}.
+  float2 bintab[kRhBins];
   uint8_t* codes;
   const uint8_t* in_codes;
   void* scales;
   const void* in_scales;
   int64_t codes_ld, scales_ld;
 };
+
+static_assert(sizeof(RhArgs) <= 4096, "kernel arguments are limited to 4 KB");
 
 __host__ __device__ constexpr int rh_rounds(int l2d) { return (l2d + 3) / 4; }
 // Bits of the element index transformed in round r: [4r, 4r + rh_nnew).

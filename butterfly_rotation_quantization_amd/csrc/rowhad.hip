@@ -181,16 +181,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   // The global loads are issued first; the quantizer tables are built while
   // they are in flight.
   auto build_tables = [&]() {
-    if (MODE == RH_QUANT && bins) {  // bin b: its threshold (or +inf) and the count below
-      const int b = threadIdx.x;
-      int cnt = 0;
-      float tin = __int_as_float(0x7f800000);
-      for (int k = 0; k < LV; ++k) {
-        cnt += a.tbin[k] < b ? 1 : 0;
-        tin = a.tbin[k] == b ? a.tau[k] : tin;
-      }
-      tab[b] = make_float2(tin, (float)cnt);
-    }
+    if (MODE == RH_QUANT && bins) tab[threadIdx.x] = a.bintab[threadIdx.x];  // built on the host
     if (MODE == RH_DEQUANT && threadIdx.x <= LV) {
       const int c = threadIdx.x;
       tab[c].x = a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g;

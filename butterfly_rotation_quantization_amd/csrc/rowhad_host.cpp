@@ -76,6 +76,15 @@ void fill_quant(RhArgs& a, const brq_quant* q, int64_t n) {
       a.bin_s = s;
       a.bin_off = off;
       for (int i = 0; i < nt; ++i) a.tbin[i] = rh_bin(std::fma(a.tau[i], s, off));
+      for (int b = 0; b < kRhBins; ++b) {
+        float tin = INFINITY;
+        int cnt = 0;
+        for (int i = 0; i < nt; ++i) {
+          cnt += a.tbin[i] < b ? 1 : 0;
+          if (a.tbin[i] == b) tin = a.tau[i];
+        }
+        a.bintab[b] = make_float2(tin, (float)cnt);
+      }
       return;
     }
   }
