@@ -581,7 +581,7 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
   const int64_t gy = a.side ? sp_group_tiles(a) : sp_line_tiles(a);
   if (gy > 65535 || gx >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld, %lld)", gx, gy), hipErrorInvalidValue;
   const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
-  const int kLds = kSpLines * kSpLineFloats;
+  const int kLds = a.side ? kSpBufFloats : kSpLines * kSpLineFloats;
   std::vector<uint8_t> cover((size_t)(rows * cols), 0);
   std::vector<int> xin(kLds), yout(kLds);
   std::vector<uint8_t> tile_seen((size_t)(sp_group_tiles(a) * sp_line_tiles(a)), 0);
@@ -662,11 +662,21 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
       for (int u = 0; u < kSpThreads; ++u) {
         const int g = u / a.bp, j = u - g * a.bp;
         if (j >= b || g >= ng) continue;
+        if (a.side == 1)  // float4 over lines 4 l4 .. 4 l4 + 3 (those past nl are discarded)
+          for (int l4 = 0; 4 * l4 < nl; ++l4)
+            for (int k = 0; k < b; ++k) {
+              const int base = sp_lds(a, 4 * l4, g, k);
+              if (base % 4 || base + 4 > kLds) return violation("left-side LDS vector read at %lld", base, 0), hipErrorInvalidValue;
+              for (int i = 0; i < 4 && 4 * l4 + i < nl; ++i)
+                if (!xin[base + i]) return violation("LDS read of unwritten slot %lld", base + i, 0), hipErrorInvalidValue;
+            }
         for (int l = 0; l < nl; ++l) {
           const int base = sp_lds(a, l, g, 0);
-          if (base % 4) return violation("unaligned LDS vector read at %lld", base, 0), hipErrorInvalidValue;
-          for (int k = 0; k < a.bs; ++k)
-            if (base + k >= kLds || !xin[base + k]) return violation("LDS read of unwritten slot %lld", base + k, 0), hipErrorInvalidValue;
+          if (a.side == 0) {
+            if (base % 4) return violation("unaligned LDS vector read at %lld", base, 0), hipErrorInvalidValue;
+            for (int k = 0; k < a.bs; ++k)
+              if (base + k >= kLds || !xin[base + k]) return violation("LDS read of unwritten slot %lld", base + k, 0), hipErrorInvalidValue;
+          }
           const int s = a.b2 ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j);
           if (yout[s]++) return violation("LDS output slot %lld written twice", s, 0), hipErrorInvalidValue;
         }

@@ -124,9 +124,15 @@ __host__ __device__ inline void sp_member(const SpArgs& a, int q, int& g, int& k
   k = kfast ? lo : hi;
 }
 
-// LDS slot of (line, group, member) in one tile buffer.
+// LDS slot of (line, group, member) in one tile buffer.  Right side: line
+// major, so the lanes of a load or store (one member each) are consecutive
+// slots.  Left side: member major with lines fastest (kSpLinePad floats per
+// member), because there the lanes of a load or store span the lines; the
+// products then read four lines per float4.
+constexpr int kSpLinePad = kSpLines + 4;
+constexpr int kSpBufFloats = kSpLineFloats * kSpLinePad;  // the larger of the two layouts
 __host__ __device__ inline int sp_lds(const SpArgs& a, int l, int g, int k) {
-  return l * kSpLineFloats + g * a.bs + k;
+  return a.side == 0 ? l * kSpLineFloats + g * a.bs + k : (g * a.bs + k) * kSpLinePad + l;
 }
 
 hipError_t launch_stage(const SpArgs& a, hipStream_t s);

@@ -24,12 +24,12 @@ __device__ __forceinline__ void sp_store(void* p, int t, int64_t i, float v) {
   }
 }
 
-template <int MAXB>
+template <int MAXB, int SIDE>
 __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   // one tile buffer: the outputs wait in registers until every input is read
-  __shared__ float buf[kSpLines * kSpLineFloats];
+  __shared__ __align__(16) float buf[SIDE ? kSpBufFloats : kSpLines * kSpLineFloats];
   __shared__ int spos[kSpLineFloats];   // left side: position of tile member q (-1: none)
-  __shared__ int sslot[kSpLineFloats];  // left side: its LDS offset within a line
+  __shared__ int sslot[kSpLineFloats];  // left side: its LDS slot at line 0 (+ l for line l)
   const int u = threadIdx.x;
   int64_t gt, lt;
   sp_tile_of_block(a, blockIdx.x, blockIdx.y, gt, lt);
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
 
   // ---- y_j = sum_k B[j][k] x_k for every line of the tile, into registers
   float acc[kSpLines];
-  if (act) {
+  if (act && SIDE == 0) {  // members consecutive: four members per float4
 #pragma unroll
     for (int l = 0; l < kSpLines; ++l) {
       if (l < nl) {
@@ -151,6 +151,27 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
           }
         }
         acc[l] = s;
+      }
+    }
+  } else if (act) {  // lines consecutive: four lines per float4
+#pragma unroll
+    for (int l4 = 0; l4 < kSpLines / 4; ++l4) {
+      if (4 * l4 < nl) {
+        float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < MAXB; ++k) {
+          if (k < a.b) {
+            const float4 xv = *reinterpret_cast<const float4*>(buf + sp_lds(a, 4 * l4, g, k));
+            s4.x = fmaf(w[k], xv.x, s4.x);
+            s4.y = fmaf(w[k], xv.y, s4.y);
+            s4.z = fmaf(w[k], xv.z, s4.z);
+            s4.w = fmaf(w[k], xv.w, s4.w);
+          }
+        }
+        acc[4 * l4] = s4.x;
+        acc[4 * l4 + 1] = s4.y;
+        acc[4 * l4 + 2] = s4.z;
+        acc[4 * l4 + 3] = s4.w;
       }
     }
   }
@@ -229,9 +250,13 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
 
 template <int MAXB>
 hipError_t launch_t(const SpArgs& a, hipStream_t s) {
-  const dim3 grid = a.side ? dim3((unsigned)sp_line_tiles(a), (unsigned)sp_group_tiles(a))
-                           : dim3((unsigned)sp_group_tiles(a), (unsigned)sp_line_tiles(a));
-  hipLaunchKernelGGL((stage_kernel<MAXB>), grid, dim3(kSpThreads), 0, s, a);
+  if (a.side) {
+    const dim3 grid((unsigned)sp_line_tiles(a), (unsigned)sp_group_tiles(a));
+    hipLaunchKernelGGL((stage_kernel<MAXB, 1>), grid, dim3(kSpThreads), 0, s, a);
+  } else {
+    const dim3 grid((unsigned)sp_group_tiles(a), (unsigned)sp_line_tiles(a));
+    hipLaunchKernelGGL((stage_kernel<MAXB, 0>), grid, dim3(kSpThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
