@@ -16,6 +16,7 @@ namespace brq {
 
 static std::string g_violation;
 static long long g_launches = 0;
+static long long g_rows_launches = 0;  // of those, left-side stages by whole rows
 
 static bool violation(const char* fmt, long long a, long long b) {
   if (g_violation.empty()) {
@@ -145,9 +146,11 @@ extern "C" {
 // Dry-run diagnostics (only in libbrq_dryrun.so).
 const char* brq_dryrun_violation(void) { return brq::g_violation.c_str(); }
 long long brq_dryrun_launches(void) { return brq::g_launches; }
+long long brq_dryrun_rows_launches(void) { return brq::g_rows_launches; }
 void brq_dryrun_reset(void) {
   brq::g_violation.clear();
   brq::g_launches = 0;
+  brq::g_rows_launches = 0;
 }
 }
 
@@ -715,6 +718,53 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
     }
   for (size_t i = 0; i < cover.size(); ++i)
     if (cover[i] != 1) return violation("stage pass element %lld stored %lld times", (int64_t)i, cover[i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_stage_rows(const SpArgs& a, hipStream_t) {
+  ++g_launches;
+  ++g_rows_launches;
+  const int b = a.b;
+  if (!sr_supported(a)) return violation("rows kernel launched for an unsupported stage (b %lld)", b, 0), hipErrorInvalidValue;
+  if (a.S < 1 || a.d % (b * a.S) || a.ngc != a.d / b || a.ngroups != a.ngc)
+    return violation("rows kernel shape (d %lld, S %lld)", a.d, a.S), hipErrorInvalidValue;
+  const int vec = sr_vec(b);
+  const int64_t rows = a.d, cols = a.lines;
+  if (a.ld_src < cols || a.ld_dst < cols)
+    return violation("rows kernel leading dimension (%lld < %lld)", std::min(a.ld_src, a.ld_dst), cols), hipErrorInvalidValue;
+  const int64_t nct = sr_col_tiles(a), nblk = nct * a.ngroups;
+  if (nblk >= ((int64_t)1 << 31) || nct * kSrThreads * vec < cols)
+    return violation("rows kernel grid (%lld blocks, %lld column tiles)", nblk, nct), hipErrorInvalidValue;
+  const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
+  std::vector<uint8_t> loaded((size_t)(rows * cols), 0), stored((size_t)(rows * cols), 0);
+  for (int64_t bid = 0; bid < nblk; ++bid) {
+    uint32_t gid, ct;
+    sr_tile_of_block((uint32_t)bid, (uint32_t)nct, gid, ct);
+    if (gid >= a.ngroups || ct >= nct) return violation("rows kernel block %lld maps to group %lld", bid, gid), hipErrorInvalidValue;
+    if (a.mode != BRQ_HADAMARD) {
+      const int64_t r = sp_block_row(a, gid, 0);
+      if (r < 0 || r + (int64_t)b * b > blk_floats) return violation("rows kernel block at %lld of %lld", r, blk_floats), hipErrorInvalidValue;
+      if (a.mode == BRQ_PER_GROUP && r != (int64_t)gid * b * b) return violation("block of group %lld read at %lld", gid, r), hipErrorInvalidValue;
+    }
+    for (int t = 0; t < kSrThreads; ++t) {
+      const int64_t c0 = sr_col(ct, t, vec);
+      if (c0 >= cols) continue;
+      if (c0 + vec > cols || c0 % vec) return violation("rows kernel vector at column %lld", c0, 0), hipErrorInvalidValue;
+      for (int k = 0; k < b; ++k) {
+        const int64_t row = sp_pos(a, gid, k);
+        if (row < 0 || row >= rows) return violation("rows kernel row %lld of %lld", row, rows), hipErrorInvalidValue;
+        if (row != ((int64_t)gid / a.S) * b * a.S + (int64_t)k * a.S + gid % a.S)
+          return violation("member %lld of group %lld at the wrong row", k, gid), hipErrorInvalidValue;
+        for (int v = 0; v < vec && c0 + v < cols; ++v) {
+          const int64_t e = row * cols + c0 + v;
+          if (loaded[(size_t)e]++) return violation("rows kernel loads (%lld, %lld) twice", row, c0 + v), hipErrorInvalidValue;
+          if (stored[(size_t)e]++) return violation("rows kernel stores (%lld, %lld) twice", row, c0 + v), hipErrorInvalidValue;
+        }
+      }
+    }
+  }
+  for (size_t i = 0; i < stored.size(); ++i)
+    if (stored[i] != 1) return violation("rows kernel element %lld stored %lld times", (int64_t)i, stored[i]), hipErrorInvalidValue;
   return hipSuccess;
 }
 

@@ -137,6 +137,38 @@ __host__ __device__ inline int sp_lds(const SpArgs& a, int l, int g, int k) {
 
 hipError_t launch_stage(const SpArgs& a, hipStream_t s);
 
+// ---- Left-side stages by whole rows ------------------------------------------
+//
+// On the left side the members of a group are whole matrix rows: group
+// c = hi * S + lo maps rows hi * b * S + k * S + lo (k < b) to the same rows,
+// Y[j][:] = sum_k B_c[j][k] X[k][:].  This kernel gives a workgroup one group
+// and kSrThreads * vec consecutive columns; thread t owns vec columns and keeps
+// its b x vec inputs in registers, so every load and store is a contiguous
+// run of a row and no LDS is needed.  All threads of a workgroup share one
+// block, whose entries are therefore uniform and come through the scalar
+// cache.  Radices 2 .. 64 that are powers of two take it (Hadamard blocks up
+// to 16, the canonical radices); the pointers, leading dimensions and column
+// count must allow vec-element accesses, and one side must be float32.
+constexpr int kSrThreads = 256;
+__host__ __device__ constexpr int sr_vec(int b) { return b <= 16 ? 4 : (b >= 64 ? 1 : 64 / b); }
+__host__ __device__ inline int64_t sr_col_tiles(const SpArgs& a) {
+  const int64_t w = (int64_t)kSrThreads * sr_vec(a.b);
+  return (a.lines + w - 1) / w;
+}
+// Group and column tile of workgroup bid; column tiles run fastest, so
+// consecutive workgroups read consecutive runs of the same rows.
+__host__ __device__ inline void sr_tile_of_block(uint32_t bid, uint32_t nct, uint32_t& gid,
+                                                 uint32_t& ct) {
+  gid = bid / nct;
+  ct = bid - gid * nct;
+}
+// First column of thread t in column tile ct.
+__host__ __device__ inline int64_t sr_col(uint32_t ct, int t, int vec) {
+  return ((int64_t)ct * kSrThreads + t) * vec;
+}
+bool sr_supported(const SpArgs& a);
+hipError_t launch_stage_rows(const SpArgs& a, hipStream_t s);
+
 // Host side (stage_host.cpp).  sp_shape_ok: the stage pass can run the plan
 // on this shape; sp_rotate_supported: it is also the faster choice.
 bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols);

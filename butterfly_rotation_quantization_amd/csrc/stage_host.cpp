@@ -79,6 +79,19 @@ bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols) {
   return true;
 }
 
+bool sr_supported(const SpArgs& a) {
+  if (a.side != 1 || a.b2 || a.b < 2 || a.b > 64 || (a.b & (a.b - 1))) return false;
+  if (a.mode == BRQ_HADAMARD ? a.b > 16 : !a.blk) return false;
+  if (a.src_t != BRQ_F32 && a.dst_t != BRQ_F32) return false;
+  if (a.ngroups != a.ngc || a.d >= ((int64_t)1 << 31)) return false;  // one chunk: the rows
+  const int vec = sr_vec(a.b);
+  const int in_bytes = a.src_t == BRQ_F32 ? 4 : 2, out_bytes = a.dst_t == BRQ_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(a.src) % (vec * in_bytes) ||
+      reinterpret_cast<uintptr_t>(a.dst) % (vec * out_bytes) || a.ld_src % vec || a.ld_dst % vec || a.lines % vec)
+    return false;
+  return sr_col_tiles(a) * a.ngroups < ((int64_t)1 << 31);
+}
+
 bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {
   if (!sp_shape_ok(p, side, rows, cols)) return false;
   // dense blocks: a block row in registers beats the tile pass's per-output
@@ -149,7 +162,6 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.ngc = p->d / a.b;
     a.ngroups = (side == 0 ? cols / p->d : 1) * a.ngc;
     a.lines = lines;
-    if (side == 1 && sp_group_tiles(a) > 65535) return BRQ_ERR_UNSUPPORTED;  // grid y
     a.hscale = 1.0f / std::sqrt((float)a.b);
     a.blk = p->mode == BRQ_HADAMARD
                 ? nullptr
@@ -164,6 +176,8 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.dst = last ? y : mid;
     a.dst_t = last ? yt : BRQ_F32;
     a.ld_dst = last ? ldy : ldm;
+    const bool rows_kernel = sr_supported(a);
+    if (side == 1 && !rows_kernel && sp_group_tiles(a) > 65535) return BRQ_ERR_UNSUPPORTED;  // grid y
     char name[64];
     if (pair)
       snprintf(name, sizeof name, "stage R(%d,%d) S%lld", a.b, a.b2, (long long)a.S);
@@ -171,7 +185,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
       snprintf(name, sizeof name, "stage %s%s(%d) S%lld", side == 0 ? "R" : "L",
                inverse ? "^T" : "", a.b, (long long)a.S);
     const int tok = prof_begin(name, s);
-    const hipError_t e = launch_stage(a, s);
+    const hipError_t e = rows_kernel ? launch_stage_rows(a, s) : launch_stage(a, s);
     prof_end(tok, s);
     if (e != hipSuccess) {
       *herr = e;

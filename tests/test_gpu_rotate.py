@@ -57,13 +57,15 @@ def test_right_rotate(radix, mode, dt):
     check_rotation(from_dev(xi), refi, dt, f"right inverse {radix}")
 
 
+# 45 columns: the tile kernels; 64: left stages of power-of-two radix run by
+# whole rows (vector accesses need the column count a multiple of 4).
 @pytest.mark.parametrize("radix,mode", [p for p in PLANS if np.prod(p[0]) <= 4096])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_left_rotate(radix, mode, dt):
+@pytest.mark.parametrize("cols", [45, 64])
+def test_left_rotate(radix, mode, dt, cols):
     import butterfly_rotation_quantization_amd as brq
     side = _side(radix, mode, seed=9)
     d = side.d
-    cols = 45
     announce(f"left rotate radix={radix} mode={mode} dt={dt} cols={cols}")
     xs = _input(d, cols, dt, seed=4)
     x = to_dev(xs, dt)
@@ -137,3 +139,27 @@ def test_leading_dimension_and_empty():
     assert not y_big[:, :10].any() and not y_big[:, 266:].any()
     e = torch.empty((0, 256), dtype=torch.float32, device="cuda")
     brq.rotate(lib_plan(side), e, e.clone())
+
+
+@pytest.mark.parametrize("offset", [4, 2])
+def test_left_leading_dimension(offset):
+    """Left-side rotation of a column window of a wider matrix: an offset of
+    4 floats keeps 16-byte vector accesses (whole-row stages), 2 does not
+    (tile kernels); both must match, and the columns outside stay untouched."""
+    import butterfly_rotation_quantization_amd as brq
+    torch = pytest.importorskip("torch")
+    side = _side((32, 16, 16), "per_group", seed=13)
+    d = side.d
+    xs = _input(d, 100, "f32", seed=8)
+    big = to_dev(xs, "f32")
+    x = big[:, offset:offset + 64]
+    y_big = torch.zeros((d, 100), dtype=torch.float32, device="cuda")
+    y = y_big[:, offset:offset + 64]
+    brq.rotate(lib_plan(side), x, y, side="left")
+    ref = T.apply_left(orc_plan(side), xs[:, offset:offset + 64].astype(np.float64))
+    check_rotation(from_dev(y).T, ref.T, "f32", f"left ld offset {offset}")
+    assert not y_big[:, :offset].any() and not y_big[:, offset + 64:].any()
+    xi = torch.empty_like(y)
+    brq.rotate_inverse(lib_plan(side), y.contiguous(), xi, side="left")
+    check_rotation(from_dev(xi).T, xs[:, offset:offset + 64].astype(np.float64).T, "f32",
+                   f"left ld offset {offset} round trip")

@@ -27,6 +27,7 @@ def dl():
     lib = brq.load_library(brq.DRYRUN_LIB_PATH)
     lib.brq_dryrun_violation.restype = ctypes.c_char_p
     lib.brq_dryrun_launches.restype = ctypes.c_longlong
+    lib.brq_dryrun_rows_launches.restype = ctypes.c_longlong
     return lib
 
 
@@ -227,3 +228,24 @@ def test_stage_head_pass_b_tail_launches(dl):
                                      WS, ws, None)
     _ok(dl, st, "stage head + pass B tail")
     assert dl.brq_dryrun_launches() == 1 + 2 + 1  # L(4), R(3), R(16) S256, pass B
+
+
+# Left-side stages whose radix is a power of two up to 64 run by whole rows
+# when the column count, leading dimensions and pointers allow vector accesses
+# and one side is float32; the rest keep the tile kernel.
+@pytest.mark.parametrize("radix,mode,cols,xt,yt,rows_launches", [
+    ((32, 16, 16), "per_group", 512, 1, 1, 3),    # bf16 -> f32 -> f32 -> bf16
+    ((16, 16, 16), "per_group", 64, 0, 0, 3),
+    ((64, 2), "per_group", 8, 2, 2, 2),           # radix 64: one column per thread
+    ((2,) * 12, "hadamard", 36, 1, 1, 3),         # canonical radix-16 stages
+    ((32, 16, 16), "per_group", 6, 1, 1, 1),      # 6 columns: radix 32 takes pairs, 16 needs 4
+    ((32, 16, 16), "per_group", 9, 1, 1, 0),      # odd column count
+    ((3, 5, 7), "shared", 64, 0, 0, 0),           # radices that are not powers of two
+    ((4,), "shared", 64, 1, 1, 0),                # one stage bf16 -> bf16
+])
+def test_left_rows_kernel(dl, radix, mode, cols, xt, yt, rows_launches):
+    side = S.random_plan(np.random.default_rng(cols), radix, mode)
+    p = DPlan(dl, side)
+    for inverse in (False, True):
+        _rotate(dl, p, 1, side.d, cols, xt, yt, inverse=inverse)
+        assert dl.brq_dryrun_rows_launches() == rows_launches
