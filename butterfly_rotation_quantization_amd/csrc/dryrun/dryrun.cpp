@@ -580,21 +580,19 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
   const int64_t cols = a.side == 0 ? axis_len : a.lines;
   if (a.ld_src < cols || a.ld_dst < cols)
     return violation("stage pass leading dimension (%lld < %lld)", std::min(a.ld_src, a.ld_dst), cols), hipErrorInvalidValue;
-  const int64_t gx = a.side ? sp_line_tiles(a) : sp_group_tiles(a);
-  const int64_t gy = a.side ? sp_group_tiles(a) : sp_line_tiles(a);
-  if (gy > 65535 || gx >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld, %lld)", gx, gy), hipErrorInvalidValue;
+  const int64_t nblocks = sp_blocks(a);
+  if (nblocks >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld blocks)", nblocks, 0), hipErrorInvalidValue;
   const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
   const int kLds = a.side ? kSpBufFloats : kSpLines * kSpLineFloats;
   std::vector<uint8_t> cover((size_t)(rows * cols), 0);
   std::vector<int> xin(kLds), yout(kLds);
   std::vector<uint8_t> tile_seen((size_t)(sp_group_tiles(a) * sp_line_tiles(a)), 0);
-  for (int64_t bx = 0; bx < gx; ++bx)
-    for (int64_t by = 0; by < gy; ++by) {
+  for (int64_t bid = 0; bid < nblocks; ++bid) {
       int64_t gt, lt;
-      sp_tile_of_block(a, bx, by, gt, lt);
+      sp_tile_of_block(a, (uint32_t)bid, gt, lt);
       if (gt < 0 || gt >= sp_group_tiles(a) || lt < 0 || lt >= sp_line_tiles(a) ||
           tile_seen[(size_t)(gt * sp_line_tiles(a) + lt)]++)
-        return violation("stage pass block (%lld, %lld) maps to a bad or repeated tile", bx, by), hipErrorInvalidValue;
+        return violation("stage pass block %lld maps to a bad or repeated tile (%lld)", bid, gt), hipErrorInvalidValue;
       const int64_t g0 = gt * a.gw, l0 = lt * kSpLines;
       const int ng = (int)std::min<int64_t>(a.ngroups - g0, a.gw);
       const int nl = (int)std::min<int64_t>(a.lines - l0, kSpLines);

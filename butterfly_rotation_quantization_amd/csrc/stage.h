@@ -77,13 +77,30 @@ __host__ __device__ inline int64_t sp_group_tiles(const SpArgs& a) {
 __host__ __device__ inline int64_t sp_line_tiles(const SpArgs& a) {
   return (a.lines + kSpLines - 1) / kSpLines;
 }
-// Grid: right side (group tiles, line tiles), left side (line tiles, group
-// tiles), so that consecutive workgroups cover consecutive addresses (the
-// next groups of the same rows, or the next columns of the same rows).
-__host__ __device__ inline void sp_tile_of_block(const SpArgs& a, int64_t bx, int64_t by,
-                                                 int64_t& gt, int64_t& lt) {
-  gt = a.side ? by : bx;
-  lt = a.side ? bx : by;
+// The GPU hands workgroup i to XCD i % kXcds, and each XCD has its own L2.
+// Workgroup bid takes logical tile xcd_order(bid, n), which numbers the
+// tiles XCD by XCD, so consecutive logical tiles run on one XCD at about the
+// same time and share its L2 lines (tiles of 64-byte runs split 128-byte lines
+// with their neighbours).  A bijection of [0, n) for any n.
+constexpr uint32_t kXcds = 8;
+__host__ __device__ inline uint32_t xcd_order(uint32_t bid, uint32_t n) {
+  const uint32_t q = n / kXcds, r = n % kXcds, x = bid % kXcds, s = bid / kXcds;
+  return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+__host__ __device__ inline int64_t sp_blocks(const SpArgs& a) {
+  return sp_group_tiles(a) * sp_line_tiles(a);
+}
+// Tile of workgroup bid (a one-dimensional grid of sp_blocks workgroups).
+// Logical tiles run along the groups on the right side (the next groups of
+// the same rows) and along the lines on the left side (the next columns of
+// the same rows): consecutive addresses either way.
+__host__ __device__ inline void sp_tile_of_block(const SpArgs& a, uint32_t bid, int64_t& gt,
+                                                 int64_t& lt) {
+  const uint32_t t = xcd_order(bid, (uint32_t)sp_blocks(a));
+  const uint32_t nf = (uint32_t)(a.side ? sp_line_tiles(a) : sp_group_tiles(a));
+  const uint32_t slow = t / nf, fast = t - slow * nf;
+  gt = a.side ? slow : fast;
+  lt = a.side ? fast : slow;
 }
 
 // Position along the transformed axis of member k of group gid (global over

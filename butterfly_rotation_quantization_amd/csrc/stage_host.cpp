@@ -73,7 +73,7 @@ bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols) {
   const int64_t lines = side == 0 ? rows : cols;
   const int64_t axis = side == 0 ? cols : rows;  // positions fit sp_pos's 32 bits
   if (axis % p->d || axis > (int64_t)1 << 30) return false;
-  if (side == 0 && (lines + kSpLines - 1) / kSpLines > 65535) return false;  // grid y
+  if (((lines + kSpLines - 1) / kSpLines) * (axis / 2) >= ((int64_t)1 << 31)) return false;  // grid
   for (int i = 0; i < p->nst; ++i)
     if (p->radix[i] > 64) return false;
   return true;
@@ -134,7 +134,6 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     ldm = cols;
   }
   const int64_t lines = side == 0 ? rows : cols;
-  if (side == 0 && (lines + kSpLines - 1) / kSpLines > 65535) return BRQ_ERR_UNSUPPORTED;
   for (int i = 0; i < L.n; ++i) {
     const int si = inverse ? L.n - 1 - i : i;
     SpArgs a;
@@ -177,7 +176,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.dst_t = last ? yt : BRQ_F32;
     a.ld_dst = last ? ldy : ldm;
     const bool rows_kernel = sr_supported(a);
-    if (side == 1 && !rows_kernel && sp_group_tiles(a) > 65535) return BRQ_ERR_UNSUPPORTED;  // grid y
+    if (!rows_kernel && sp_blocks(a) >= ((int64_t)1 << 31)) return BRQ_ERR_UNSUPPORTED;  // grid
     char name[64];
     if (pair)
       snprintf(name, sizeof name, "stage R(%d,%d) S%lld", a.b, a.b2, (long long)a.S);

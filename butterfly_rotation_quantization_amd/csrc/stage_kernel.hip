@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   __shared__ int sslot[kSpLineFloats];  // left side: its LDS slot at line 0 (+ l for line l)
   const int u = threadIdx.x;
   int64_t gt, lt;
-  sp_tile_of_block(a, blockIdx.x, blockIdx.y, gt, lt);
+  sp_tile_of_block(a, blockIdx.x, gt, lt);
   const int64_t g0 = gt * a.gw;
   const int64_t l0 = lt * kSpLines;
   const int ng = (int)(a.ngroups - g0 < a.gw ? a.ngroups - g0 : a.gw);
@@ -250,13 +250,11 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
 
 template <int MAXB>
 hipError_t launch_t(const SpArgs& a, hipStream_t s) {
-  if (a.side) {
-    const dim3 grid((unsigned)sp_line_tiles(a), (unsigned)sp_group_tiles(a));
+  const dim3 grid((unsigned)sp_blocks(a));
+  if (a.side)
     hipLaunchKernelGGL((stage_kernel<MAXB, 1>), grid, dim3(kSpThreads), 0, s, a);
-  } else {
-    const dim3 grid((unsigned)sp_group_tiles(a), (unsigned)sp_line_tiles(a));
+  else
     hipLaunchKernelGGL((stage_kernel<MAXB, 0>), grid, dim3(kSpThreads), 0, s, a);
-  }
   return hipGetLastError();
 }
 
