@@ -21,9 +21,11 @@ Modules:
 * ``quant`` -- group absmax quantizer, norm-scaled codebook quantizer,
   decision-band accounting, LSB-first bit packing.
 * ``lloydmax`` -- Lloyd-Max centroids/thresholds for N(0, 1).
+* ``harp`` -- HARP blocks from int8 parameters: Givens / Cayley factor times
+  the base mixer ([HARP] sections 2.1, 2.2, 2.4).
 
 Readings of points the pages leave open are stated where they are used and
 listed together in the design notes of the repository.
 """
 
-from . import transform, quant, lloydmax  # noqa: F401
+from . import transform, quant, lloydmax, harp  # noqa: F401
