@@ -26,11 +26,14 @@ same kind of line; "all" prints one line per workload):
                    per-group plans, absmax 2-bit g64
   decode_t1/16/256 online right-side rotation of T x 28672 fp16 activations
                    with the (7,16,16,16) plan: latency per call
+  harp_build       HARP blocks built on the device from int8 parameters for
+                   the 70B schedules (left (32,16,16) d=8192, right
+                   (7,16,16,16) d=28672): latency of the seven launches
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
 
---gpus above 1 exits: this build runs on one GPU.
+--gpus above 1 exits: the benchmark runs on one GPU.
 """
 
 from __future__ import annotations
@@ -52,6 +55,7 @@ HBM_PEAK_GBS = 8000.0
 # (256 CUs x 64 lanes x 2 (FMA) x 2 (dual issue) x 2.4 GHz); both 157.3 TFLOP/s.
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 FP32_MFMA_PEAK_TFLOPS = 157.3
+FP64_VECTOR_PEAK_TFLOPS = 78.6
 MALL_BYTES = 256 << 20
 
 
@@ -86,7 +90,8 @@ def roofline_of(bytes_, flops, engine):
     """(bound, achieved-per-second function inputs) for one kernel: the
     resource whose time floor is larger at peak binds."""
     t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
-    peak = FP32_MFMA_PEAK_TFLOPS if engine == "mfma" else FP32_VECTOR_PEAK_TFLOPS
+    peak = {"mfma": FP32_MFMA_PEAK_TFLOPS, "alu64": FP64_VECTOR_PEAK_TFLOPS}.get(
+        engine, FP32_VECTOR_PEAK_TFLOPS)
     t_fl = flops / (peak * 1e12)
     if t_hbm >= t_fl:
         return "hbm", bytes_ / 1e9, "GB/s", HBM_PEAK_GBS
@@ -490,6 +495,80 @@ class PolarBlock(Workload):
                            f"({100 * share:.0f}% of the elements; right plan dense); {dt:.2f} s")}
 
 
+class HarpBuild(Workload):
+    """HARP blocks built on the device from int8 parameters (brq_harp_blocks):
+    every stage of a left and a right schedule, one launch per stage."""
+    unit, higher_is_better, dtype = "us", False, "f64"
+
+    def __init__(self, name, metric, sides):
+        self.name, self.metric = name, metric
+        self.sides = sides  # [(d, radix)]
+
+    def setup(self, brq, dev, stream):
+        import numpy as np
+        import torch
+        import synthetic as S
+        self.brq, self.stream = brq, stream
+        rng = S.streams(7000, 1)[0]
+        self.jobs = []
+        for d, radix in self.sides:
+            for b in radix:
+                ng = d // b
+                npar = 1 if b == 2 else b * (b - 1) // 2
+                q = rng.integers(-127, 128, size=(ng, npar)).astype(np.int8)
+                base = None if b & (b - 1) == 0 else S.random_orthogonal(rng, b).astype(np.float32)
+                self.jobs.append((b, q, base,
+                                  torch.from_numpy(q).to(dev),
+                                  None if base is None else torch.from_numpy(base).to(dev),
+                                  torch.empty((ng, b, b), dtype=torch.float32, device=dev)))
+
+    def step(self, i):
+        for b, _, _, q, base, out in self.jobs:
+            self.brq.harp_blocks(b, q, 0.004, base, out, stream=self.stream)
+
+    def value(self, ms):
+        return ms * 1e3
+
+    def elements(self):
+        return sum(out.numel() for *_, out in self.jobs)
+
+    @staticmethod
+    def _cost(b, ng):
+        npar = 1 if b == 2 else b * (b - 1) // 2
+        # Gauss-Jordan on [I - A | I + A] (b pivots x 2b columns x b rows, an
+        # FMA each) and the product Q G (b^3 FMA): 6 b^3 flop per block
+        flops = 6 * b ** 3 if b > 2 else 16  # Givens: Q G only
+        return ng * (npar + 4 * b * b), ng * flops
+
+    def alg_bytes(self):
+        return sum(self._cost(b, out.shape[0])[0] + (0 if base is None else 4 * b * b)
+                   for b, _, _, _, base, out in self.jobs)
+
+    def kernel_cost(self, name):
+        b = int(re.search(r"b(\d+)$", name).group(1))
+        costs = [self._cost(bb, out.shape[0]) for bb, *_, out in self.jobs if bb == b]
+        n = len(costs)
+        return (sum(c[0] for c in costs) // n, sum(c[1] for c in costs) // n, "alu64")
+
+    def config(self):
+        return {"schedules": [{"d": d, "radix": list(r)} for d, r in self.sides],
+                "scale": 0.004, "blocks": self.elements()}
+
+    def cpu_baseline(self, budget_s):
+        from oracle import harp as OH
+        t0 = time.perf_counter()
+        done = total = 0.0
+        for b, q, base, *_ in self.jobs:
+            k = min(q.shape[0], 64)
+            OH.stage_blocks(b, k, q[:k], 0.004, None if base is None else base.astype("float64"))
+            done += k
+            total += q.shape[0]
+        dt = time.perf_counter() - t0
+        return {"value": round(dt * 1e6 * total / done, 1), "unit": "us", "cores": cpu_threads(),
+                "kind": "oracle",
+                "sample": f"64 blocks of each stage ({int(done)} of {int(total)}); {dt:.2f} s"}
+
+
 def make_workload(name):
     import synthetic as S
     if name == "harp_mlp":
@@ -526,6 +605,12 @@ def make_workload(name):
         w.workload = f"decode_{t}x28672_f16_(7,16,16,16)"
         w._cpu_rows = t
         return w
+    if name == "harp_build":
+        w = HarpBuild(name, "latency: HARP blocks from int8 parameters (Cayley / Givens times "
+                      "the base mixer), 70B schedules U (32,16,16) d=8192 + V (7,16,16,16) "
+                      "d=28672", [(8192, (32, 16, 16)), (28672, (7, 16, 16, 16))])
+        w.workload = "harp_build_70b_U(32,16,16)_d8192_V(7,16,16,16)_d28672_int8"
+        return w
     if name in ("polar_quant", "polar_dequant"):
         dq = name == "polar_dequant"
         w = PolarBlock(name, ("HBM GB/s: PolarQuant dequant+unrotate" if dq else
@@ -539,7 +624,7 @@ def make_workload(name):
 
 
 WORKLOADS = ("harp_mlp", "llama7b_weight", "llama7b_act", "polar_quant", "polar_dequant",
-             "llama70b_weight", "decode_t1", "decode_t16", "decode_t256")
+             "llama70b_weight", "decode_t1", "decode_t16", "decode_t256", "harp_build")
 
 
 def run_workload(wl, a, brq, torch, dev, stream):

@@ -35,7 +35,7 @@ EXPORTED = (
     "brq_plan_destroy", "brq_plan_dim", "brq_workspace_bytes", "brq_rotate",
     "brq_rotate_inverse", "brq_rotate_quantize_pack", "brq_dequant_unrotate",
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
-    "brq_profile_read", "brq_set_path",
+    "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_plan_create_harp",
 )
 
 
@@ -107,6 +107,11 @@ def bind(lib):
     lib.brq_profile_read.argtypes = [i32, ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(i64)]
     lib.brq_profile_read.restype = i32
+    if hasattr(lib, "brq_harp_blocks"):
+        lib.brq_harp_blocks.argtypes = [i32, i64, vp, ctypes.c_float, vp, vp, vp]
+        lib.brq_harp_blocks.restype = i32
+        lib.brq_plan_create_harp.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, vp, vp, vp]
+        lib.brq_plan_create_harp.restype = i32
     if hasattr(lib, "brq_set_path"):  # libraries built before the path switch lack it
         lib.brq_set_path.argtypes = [i32]
         lib.brq_set_path.restype = i32
@@ -146,6 +151,34 @@ class Plan:
         self.d = int(d)
         self.radix = tuple(int(x) for x in r)
         self.mode = mode_i
+
+    @classmethod
+    def from_harp(cls, d: int, radix: Sequence[int], theta_q: np.ndarray, scales: Sequence[float],
+                  bases: Optional[Sequence[Optional[np.ndarray]]] = None,
+                  signs: Optional[np.ndarray] = None) -> "Plan":
+        """A per-group plan whose blocks the device builds from int8 HARP
+        parameters (brq_plan_create_harp).  bases[t] is G of stage t; None
+        for all stages means Sylvester everywhere."""
+        L = lib()
+        r = np.ascontiguousarray(np.asarray(radix, dtype=np.int32))
+        th = np.ascontiguousarray(np.asarray(theta_q, dtype=np.int8).reshape(-1))
+        sc = np.ascontiguousarray(np.asarray(scales, dtype=np.float32))
+        bs = None
+        if bases is not None:
+            bs = np.ascontiguousarray(np.concatenate(
+                [np.asarray(g, dtype=np.float32).reshape(-1) for g in bases]))
+        sg = None if signs is None else np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+        h = ctypes.c_void_p()
+        check(L.brq_plan_create_harp(ctypes.byref(h), int(d), len(r), r.ctypes.data,
+                                     th.ctypes.data if th.size else None, sc.ctypes.data,
+                                     None if bs is None else bs.ctypes.data,
+                                     None if sg is None else sg.ctypes.data))
+        self = cls.__new__(cls)
+        self._h = h
+        self.d = int(d)
+        self.radix = tuple(int(x) for x in r)
+        self.mode = _MODES["per_group"]
+        return self
 
     @property
     def handle(self):
@@ -210,6 +243,19 @@ def _ws_args(ws):
     if ws is None:
         return None, 0
     return int(ws.data_ptr()), int(ws.numel() * ws.element_size())
+
+
+def harp_blocks(b: int, theta_q, scale: float, base=None, out=None, stream=None):
+    """Blocks Q(theta) G of one stage from device int8 parameters theta_q
+    [ngroups, np] (brq_harp_blocks); base is a device float32 [b, b] G or
+    None (Sylvester).  Returns out, a device float32 [ngroups, b, b]."""
+    import torch
+    ng = theta_q.shape[0]
+    if out is None:
+        out = torch.empty((ng, b, b), dtype=torch.float32, device=theta_q.device)
+    check(lib().brq_harp_blocks(int(b), int(ng), _ptr(theta_q), float(scale),
+                                None if base is None else _ptr(base), _ptr(out), _stream(stream)))
+    return out
 
 
 def rotate(plan: Plan, x, y=None, side="right", ws=None, stream=None, inverse=False):

@@ -14,6 +14,7 @@
 #include "brq_internal.h"
 #include "fused.h"
 #include "rowhad.h"
+#include "harp.h"
 #include "stage.h"
 
 struct brq_plan {
@@ -696,6 +697,91 @@ brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const in
   }
   *out = h;
   return BRQ_OK;
+}
+
+brq_status brq_harp_blocks(int32_t b, int64_t ngroups, const int8_t* theta_q, float scale,
+                           const float* base, float* blocks, void* stream) {
+  g_last_error.clear();
+  if (b < 2 || b > 64) return fail(BRQ_ERR_INVALID_ARGUMENT, "radix %d is not in 2..64", b);
+  if (ngroups < 0 || ngroups >= ((int64_t)1 << 31))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "ngroups %lld is not in 0..2^31-1", (long long)ngroups);
+  if (!base && !is_pow2(b))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "radix %d needs a base mixer (not a power of two)", b);
+  if (!std::isfinite(scale)) return fail(BRQ_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (ngroups == 0) return BRQ_OK;
+  if (!theta_q || !blocks) return fail(BRQ_ERR_INVALID_ARGUMENT, "theta_q or blocks is NULL");
+  HarpArgs a;
+  a.b = b;
+  a.np = harp_params(b);
+  a.ngroups = ngroups;
+  a.theta = theta_q;
+  a.scale = scale;
+  a.base = base;
+  a.out = blocks;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char name[48];
+  snprintf(name, sizeof name, "harp blocks %s b%d", b == 2 ? "Givens" : "Cayley", b);
+  const int tok = prof_begin(name, s);
+  const hipError_t e = launch_harp(a, s);
+  prof_end(tok, s);
+  return e == hipSuccess ? BRQ_OK : hip_fail(e, "HARP block launch");
+}
+
+brq_status brq_plan_create_harp(brq_plan** out, int32_t d, int32_t n_stages, const int32_t* radix,
+                                const int8_t* theta_q, const float* scales, const float* bases,
+                                const int8_t* signs) {
+  g_last_error.clear();
+  if (!out) return fail(BRQ_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (n_stages < 1 || n_stages > kMaxStages)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "n_stages must be 1..%d", kMaxStages);
+  if (!radix || !theta_q || !scales)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "radix, theta_q or scales is NULL");
+  int64_t prod = 1, nparams = 0, nblk = 0, nbase = 0;
+  for (int t = 0; t < n_stages; ++t) {
+    if (radix[t] < 2 || radix[t] > 64)
+      return fail(BRQ_ERR_INVALID_ARGUMENT, "radix[%d] = %d is not in 2..64", t, radix[t]);
+    if (!bases && !is_pow2(radix[t]))
+      return fail(BRQ_ERR_INVALID_ARGUMENT, "radix[%d] = %d needs a base mixer", t, radix[t]);
+    prod *= radix[t];
+    if (prod > (int64_t)1 << 22) return fail(BRQ_ERR_UNSUPPORTED, "d > 2^22");
+  }
+  if (prod != d) return fail(BRQ_ERR_INVALID_ARGUMENT, "product of radices != d (%d)", d);
+  for (int t = 0; t < n_stages; ++t) {
+    const int64_t ng = d / radix[t];
+    nparams += ng * harp_params(radix[t]);
+    nblk += ng * radix[t] * radix[t];
+    nbase += (int64_t)radix[t] * radix[t];
+  }
+  // device copies of the parameters (and bases), the blocks built there, then
+  // back to the host for the ordinary plan set-up
+  int8_t* dth = nullptr;
+  float* dbase = nullptr;
+  float* dblk = nullptr;
+  std::vector<float> hblk((size_t)nblk);
+  hipError_t e = rt_malloc((void**)&dth, (size_t)nparams);
+  if (e == hipSuccess) e = rt_malloc((void**)&dblk, (size_t)nblk * sizeof(float));
+  if (e == hipSuccess && bases) e = rt_malloc((void**)&dbase, (size_t)nbase * sizeof(float));
+  if (e == hipSuccess) e = rt_copy_to_device(dth, theta_q, (size_t)nparams);
+  if (e == hipSuccess && bases) e = rt_copy_to_device(dbase, bases, (size_t)nbase * sizeof(float));
+  brq_status st = BRQ_OK;
+  int64_t poff = 0, boff = 0, goff = 0;
+  for (int t = 0; e == hipSuccess && st == BRQ_OK && t < n_stages; ++t) {
+    const int b = radix[t];
+    const int64_t ng = d / b;
+    st = brq_harp_blocks(b, ng, dth + poff, scales[t], bases ? dbase + goff : nullptr, dblk + boff,
+                         nullptr);
+    poff += ng * harp_params(b);
+    boff += ng * b * b;
+    goff += (int64_t)b * b;
+  }
+  if (e == hipSuccess && st == BRQ_OK) e = rt_copy_to_host(hblk.data(), dblk, (size_t)nblk * sizeof(float));
+  rt_free(dth);
+  rt_free(dbase);
+  rt_free(dblk);
+  if (st != BRQ_OK) return st;
+  if (e != hipSuccess) return hip_fail(e, "HARP plan set-up");
+  return brq_plan_create(out, d, n_stages, radix, hblk.data(), BRQ_PER_GROUP, signs);
 }
 
 brq_status brq_plan_destroy(brq_plan* plan) {

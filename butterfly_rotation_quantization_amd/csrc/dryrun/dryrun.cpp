@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "brq_internal.h"
+#include "harp.h"
 
 namespace brq {
 
@@ -763,6 +764,34 @@ hipError_t launch_stage_rows(const SpArgs& a, hipStream_t) {
   }
   for (size_t i = 0; i < stored.size(); ++i)
     if (stored[i] != 1) return violation("rows kernel element %lld stored %lld times", (int64_t)i, stored[i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_harp(const HarpArgs& a, hipStream_t) {
+  ++g_launches;
+  if (a.b < 2 || a.b > 64 || a.np != harp_params(a.b) || a.ngroups < 0 || a.ngroups >= ((int64_t)1 << 31))
+    return violation("HARP launch geometry (b %lld, ngroups %lld)", a.b, a.ngroups), hipErrorInvalidValue;
+  if (!a.base && (a.b & (a.b - 1))) return violation("HARP radix %lld without a base mixer", a.b, 0), hipErrorInvalidValue;
+  const int b = a.b, P = harp_pitch(b);
+  if (harp_lds_bytes(b) > 160 * 1024) return violation("HARP LDS %lld bytes", (long long)harp_lds_bytes(b), 0), hipErrorInvalidValue;
+  // one block: every parameter index in range and used once per (i < j), LDS
+  // slots within the system, outputs once each
+  std::vector<int> used(a.np, 0);
+  if (b == 2) {
+    used[0] = 1;
+  } else {
+    for (int i = 0; i < b; ++i)
+      for (int j = 0; j < b; ++j) {
+        if (i * P + b + j >= b * P) return violation("HARP LDS slot (%lld, %lld)", i, j), hipErrorInvalidValue;
+        if (i < j) {
+          const int p = harp_pidx(b, i, j);
+          if (p < 0 || p >= a.np || used[p]++) return violation("HARP parameter index %lld (b %lld)", p, b), hipErrorInvalidValue;
+        }
+      }
+  }
+  for (int p = 0; p < a.np; ++p)
+    if (used[p] != 1) return violation("HARP parameter %lld unused", p, 0), hipErrorInvalidValue;
+  if (2 * b > 2 * kHpThreads) return violation("HARP columns per lane (b %lld)", b, 0), hipErrorInvalidValue;
   return hipSuccess;
 }
 

@@ -101,6 +101,45 @@ int32_t brq_version(void);
 brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const int32_t* radix,
                            const float* blocks, int32_t mode, const int8_t* signs);
 
+/*
+ * HARP blocks from their parameters ([HARP] section 2.2: every block is
+ * B_{t,c}(theta) = Q_{t,c}(theta) G_b, Q a Givens rotation for b = 2 and the
+ * Cayley map of a skew-symmetric matrix for b > 2, G the base mixer; section
+ * 2.4: the parameters may be stored as int8).  Builds the `ngroups` b x b
+ * blocks of one stage on the device:
+ *   theta_q: device int8 [ngroups][np], np = 1 for b = 2, b(b-1)/2 above;
+ *            theta = scale * q.  b > 2: A[i][j] = theta[i*b - i*(i+1)/2 + j-i-1]
+ *            for i < j, A[j][i] = -A[i][j], Q = (I - A)^{-1} (I + A);
+ *            b = 2: Q = [[cos theta, -sin theta], [sin theta, cos theta]].
+ *   base:    device float32 G [b][b] row-major, or NULL for the normalised
+ *            Sylvester Hadamard matrix H_b / sqrt(b) (b a power of two).
+ *   blocks:  device float32 [ngroups][b][b], block rows B[j][k] as in
+ *            brq_plan_create; computed in float64, rounded once.
+ * Asynchronous on `stream`; theta_q, base and blocks are owned by the caller.
+ * Errors: INVALID_ARGUMENT (b not in 2..64, ngroups not in 0..2^31-1, NULL
+ * pointers with ngroups > 0, NULL base for a radix that is not a power of
+ * two, scale not finite), HIP.  Parameters are not range-checked (-128 is
+ * read as -128). */
+brq_status brq_harp_blocks(int32_t b, int64_t ngroups, const int8_t* theta_q, float scale,
+                           const float* base, float* blocks, void* stream);
+
+/*
+ * A per-group plan from HARP parameters: stage t's blocks are
+ * brq_harp_blocks(radix[t], d / radix[t], ...) of its parameters.
+ *   theta_q: host int8, the stages' parameters one after the other, each
+ *            stage's groups c in order (c as in brq_plan_create).
+ *   scales:  host float32 [n_stages], theta = scales[t] * q.
+ *   bases:   host float32 G blocks of all stages, [b_t][b_t] each, one after
+ *            the other; NULL for Sylvester at every stage (all radices powers
+ *            of two).  With all parameters zero the plan is the RHT.
+ *   signs:   as brq_plan_create.
+ * Builds the blocks on the current device and waits for them, then proceeds
+ * as brq_plan_create(..., BRQ_PER_GROUP, signs).  Errors: as brq_plan_create
+ * and brq_harp_blocks. */
+brq_status brq_plan_create_harp(brq_plan** out, int32_t d, int32_t n_stages, const int32_t* radix,
+                                const int8_t* theta_q, const float* scales, const float* bases,
+                                const int8_t* signs);
+
 /* Free a plan and its device arrays; NULL is allowed.  The caller must make
  * sure no queued work still uses the plan. */
 brq_status brq_plan_destroy(brq_plan* plan);

@@ -144,3 +144,37 @@ def test_path_selection(lib):
     assert lib.brq_set_path(0) == 0
     assert lib.brq_set_path(7) == 1  # INVALID_ARGUMENT
     assert b"unknown path" in lib.brq_last_error()
+
+
+@pytest.mark.parametrize("b,ng,base,scale,expect", [
+    (1, 4, False, 0.1, 1),            # radix below 2
+    (65, 4, True, 0.1, 1),            # radix above 64
+    (7, 4, False, 0.1, 1),            # not a power of two and no base mixer
+    (16, -1, False, 0.1, 1),          # negative group count
+    (16, 1 << 31, False, 0.1, 1),     # too many groups
+    (16, 4, False, float("nan"), 1),  # scale not finite
+    (16, 0, False, 0.1, 0),           # nothing to do
+])
+def test_harp_blocks_validation(lib, b, ng, base, scale, expect):
+    """Arguments are checked before any launch (fake device addresses, never
+    dereferenced on these paths)."""
+    st = lib.brq_harp_blocks(b, ng, 0x1000, ctypes.c_float(scale), 0x2000 if base else None,
+                             0x3000, None)
+    assert st == expect, (st, lib.brq_last_error().decode())
+
+
+def test_plan_create_harp_validation(lib):
+    r = np.asarray((7, 16), dtype=np.int32)
+    th = np.zeros(16 * 21 + 7 * 1, dtype=np.int8)
+    sc = np.asarray([0.1, 0.1], dtype=np.float32)
+    h = ctypes.c_void_p()
+    # radix 7 without base mixers
+    st = lib.brq_plan_create_harp(ctypes.byref(h), 112, 2, r.ctypes.data, th.ctypes.data,
+                                  sc.ctypes.data, None, None)
+    assert st == 1 and "base" in lib.brq_last_error().decode()
+    st = lib.brq_plan_create_harp(ctypes.byref(h), 100, 2, r.ctypes.data, th.ctypes.data,
+                                  sc.ctypes.data, None, None)
+    assert st == 1
+    st = lib.brq_plan_create_harp(None, 112, 2, r.ctypes.data, th.ctypes.data, sc.ctypes.data,
+                                  None, None)
+    assert st == 1

@@ -249,3 +249,36 @@ def test_left_rows_kernel(dl, radix, mode, cols, xt, yt, rows_launches):
     for inverse in (False, True):
         _rotate(dl, p, 1, side.d, cols, xt, yt, inverse=inverse)
         assert dl.brq_dryrun_rows_launches() == rows_launches
+
+
+# HARP blocks from parameters: the launch geometry, the parameter indices of
+# every (i < j) pair once each, and the LDS system, for every radix; then a
+# whole plan built that way goes through the ordinary plan set-up.
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 7, 8, 16, 32, 43, 64])
+def test_harp_blocks_walk(dl, b):
+    dl.brq_dryrun_reset()
+    base = None if b & (b - 1) == 0 else 0x2000
+    st = dl.brq_harp_blocks(b, 37, 0x1000, ctypes.c_float(0.05), base, 0x3000, None)
+    _ok(dl, st, f"harp blocks b={b}")
+    assert dl.brq_dryrun_launches() == 1
+
+
+@pytest.mark.parametrize("radix,with_base", [((32, 16, 16), False), ((7, 16, 16, 16), True),
+                                             ((2,) * 6, False), ((43, 2), True)])
+def test_plan_create_harp_walk(dl, radix, with_base):
+    import oracle.harp as OH  # parameter counts only
+    d = int(np.prod(radix))
+    th = np.zeros(OH.total_params(d, radix), dtype=np.int8)
+    sc = np.full(len(radix), 0.01, dtype=np.float32)
+    bases = None
+    if with_base:
+        bases = np.concatenate([np.eye(b, dtype=np.float32).reshape(-1) for b in radix])
+    r = np.asarray(radix, dtype=np.int32)
+    h = ctypes.c_void_p()
+    dl.brq_dryrun_reset()
+    st = dl.brq_plan_create_harp(ctypes.byref(h), d, len(r), r.ctypes.data, th.ctypes.data,
+                                 sc.ctypes.data, None if bases is None else bases.ctypes.data,
+                                 None)
+    _ok(dl, st, f"harp plan {radix}")
+    assert dl.brq_dryrun_launches() == len(radix)
+    dl.brq_plan_destroy(h)
