@@ -36,6 +36,7 @@ EXPORTED = (
     "brq_rotate_inverse", "brq_rotate_quantize_pack", "brq_dequant_unrotate",
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
     "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_plan_create_harp",
+    "brq_plan_serialize", "brq_plan_deserialize",
 )
 
 
@@ -112,6 +113,11 @@ def bind(lib):
         lib.brq_harp_blocks.restype = i32
         lib.brq_plan_create_harp.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, vp, vp, vp]
         lib.brq_plan_create_harp.restype = i32
+    if hasattr(lib, "brq_plan_serialize"):
+        lib.brq_plan_serialize.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
+        lib.brq_plan_serialize.restype = i32
+        lib.brq_plan_deserialize.argtypes = [ctypes.POINTER(vp), vp, sz]
+        lib.brq_plan_deserialize.restype = i32
     if hasattr(lib, "brq_set_path"):  # libraries built before the path switch lack it
         lib.brq_set_path.argtypes = [i32]
         lib.brq_set_path.restype = i32
@@ -178,6 +184,28 @@ class Plan:
         self.d = int(d)
         self.radix = tuple(int(x) for x in r)
         self.mode = _MODES["per_group"]
+        return self
+
+    def serialize(self) -> bytes:
+        """Byte image of the plan (brq_plan_serialize)."""
+        L = lib()
+        n = ctypes.c_size_t()
+        check(L.brq_plan_serialize(self._h, None, 0, ctypes.byref(n)))
+        buf = ctypes.create_string_buffer(n.value)
+        check(L.brq_plan_serialize(self._h, buf, n.value, ctypes.byref(n)))
+        return buf.raw[:n.value]
+
+    @classmethod
+    def deserialize(cls, image: bytes) -> "Plan":
+        """Rebuild a plan from brq_plan_serialize's image on the current device."""
+        L = lib()
+        h = ctypes.c_void_p()
+        check(L.brq_plan_deserialize(ctypes.byref(h), image, len(image)))
+        self = cls.__new__(cls)
+        self._h = h
+        self.d = int(L.brq_plan_dim(h))
+        self.radix = None
+        self.mode = None
         return self
 
     @property

@@ -19,6 +19,11 @@
 
 struct brq_plan {
   brq::Plan p;
+  std::vector<int8_t> signs;  // host copy of the signs (empty: all +1)
+  // plans made from HARP parameters keep them, so they serialise compactly
+  bool harp = false;
+  std::vector<int8_t> theta;
+  std::vector<float> scales, bases;
 };
 
 namespace brq {
@@ -689,6 +694,7 @@ brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const in
     e = rt_malloc((void**)&p.signs, d * sizeof(float));
     if (e == hipSuccess) e = rt_copy_to_device(p.signs, sf.data(), d * sizeof(float));
   }
+  if (signs) h->signs.assign(signs, signs + d);
   if (e == hipSuccess) e = fused_prepare(p, blocks, signs);
   if (e != hipSuccess) {
     brq_status st = hip_fail(e, "plan device setup");
@@ -781,7 +787,177 @@ brq_status brq_plan_create_harp(brq_plan** out, int32_t d, int32_t n_stages, con
   rt_free(dblk);
   if (st != BRQ_OK) return st;
   if (e != hipSuccess) return hip_fail(e, "HARP plan set-up");
-  return brq_plan_create(out, d, n_stages, radix, hblk.data(), BRQ_PER_GROUP, signs);
+  st = brq_plan_create(out, d, n_stages, radix, hblk.data(), BRQ_PER_GROUP, signs);
+  if (st == BRQ_OK) {
+    brq_plan* h = *out;
+    h->harp = true;
+    h->theta.assign(theta_q, theta_q + nparams);
+    h->scales.assign(scales, scales + n_stages);
+    if (bases) h->bases.assign(bases, bases + nbase);
+  }
+  return st;
+}
+
+// ---- plan serialisation ------------------------------------------------------
+//
+// Little-endian byte image: "BRQP", u32 version 1, u32 kind (0: blocks,
+// 1: HARP parameters), i32 d, i32 n_stages, i32 mode, u32 flags (bit 0 signs,
+// bit 1 base mixers), i32 radix[n_stages]; kind 0: float32 blocks in
+// brq_plan_create's layout; kind 1: float32 scales[n_stages], float32 base
+// mixers (flag 1), int8 parameters; int8 signs (flag 0); u64 FNV-1a hash of
+// every byte before it.
+
+}  // extern "C"
+
+namespace brq {
+namespace {
+
+constexpr uint32_t kSerVersion = 1;
+
+struct ByteWriter {
+  uint8_t* buf;
+  size_t cap, n = 0;
+  void put(const void* p, size_t k) {
+    if (buf && n + k <= cap) std::memcpy(buf + n, p, k);
+    n += k;
+  }
+  template <typename T> void val(T v) { put(&v, sizeof v); }
+};
+
+uint64_t fnv1a(const uint8_t* p, size_t n) {
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+size_t plan_block_floats(const Plan& p) {
+  size_t total = 0;
+  for (int t = 0; t < p.nst; ++t) {
+    const size_t bb = (size_t)p.radix[t] * p.radix[t];
+    if (p.mode == BRQ_SHARED) total += bb;
+    else if (p.mode == BRQ_PER_GROUP) total += (size_t)(p.d / p.radix[t]) * bb;
+  }
+  return total;
+}
+
+}  // namespace
+}  // namespace brq
+
+extern "C" {
+
+brq_status brq_plan_serialize(const brq_plan* plan, void* buf, size_t cap, size_t* size) {
+  g_last_error.clear();
+  if (!plan || !size) return fail(BRQ_ERR_INVALID_ARGUMENT, "plan or size is NULL");
+  const Plan& p = plan->p;
+  std::vector<float> blocks;
+  if (!plan->harp && p.blk) {  // fetch the blocks only when writing
+    if (buf) {
+      blocks.resize(plan_block_floats(p));
+      const hipError_t e = rt_copy_to_host(blocks.data(), p.blk, blocks.size() * sizeof(float));
+      if (e != hipSuccess) return hip_fail(e, "plan block copy");
+    }
+  }
+  const uint32_t flags = (plan->signs.empty() ? 0u : 1u) | (plan->bases.empty() ? 0u : 2u);
+  ByteWriter w{static_cast<uint8_t*>(buf), cap};
+  w.put("BRQP", 4);
+  w.val<uint32_t>(kSerVersion);
+  w.val<uint32_t>(plan->harp ? 1u : 0u);
+  w.val<int32_t>(p.d);
+  w.val<int32_t>(p.nst);
+  w.val<int32_t>(p.mode);
+  w.val<uint32_t>(flags);
+  w.put(p.radix, sizeof(int32_t) * p.nst);
+  if (plan->harp) {
+    w.put(plan->scales.data(), sizeof(float) * plan->scales.size());
+    w.put(plan->bases.data(), sizeof(float) * plan->bases.size());
+    w.put(plan->theta.data(), plan->theta.size());
+  } else if (buf) {
+    w.put(blocks.data(), sizeof(float) * blocks.size());
+  } else {
+    w.n += sizeof(float) * plan_block_floats(p);
+  }
+  w.put(plan->signs.data(), plan->signs.size());
+  const size_t body = w.n;
+  w.n += sizeof(uint64_t);
+  *size = w.n;
+  if (!buf) return BRQ_OK;
+  if (cap < w.n) return fail(BRQ_ERR_INVALID_ARGUMENT, "buffer of %zu bytes < %zu", cap, w.n);
+  const uint64_t h = fnv1a(static_cast<uint8_t*>(buf), body);
+  std::memcpy(static_cast<uint8_t*>(buf) + body, &h, sizeof h);
+  return BRQ_OK;
+}
+
+brq_status brq_plan_deserialize(brq_plan** out, const void* buf, size_t size) {
+  g_last_error.clear();
+  if (!out || !buf) return fail(BRQ_ERR_INVALID_ARGUMENT, "out or buf is NULL");
+  *out = nullptr;
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  size_t at = 0;
+  auto take = [&](void* dst, size_t k) {
+    if (at + k > size) return false;
+    std::memcpy(dst, b + at, k);
+    at += k;
+    return true;
+  };
+  char magic[4];
+  uint32_t version = 0, kind = 0, flags = 0;
+  int32_t d = 0, nst = 0, mode = 0;
+  if (size < 8 + sizeof(uint64_t)) return fail(BRQ_ERR_INVALID_ARGUMENT, "image too short");
+  uint64_t h_stored;
+  std::memcpy(&h_stored, b + size - sizeof h_stored, sizeof h_stored);
+  if (fnv1a(b, size - sizeof h_stored) != h_stored)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "image hash mismatch (corrupt or truncated)");
+  size -= sizeof h_stored;
+  if (!take(magic, 4) || std::memcmp(magic, "BRQP", 4))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "not a plan image");
+  if (!take(&version, 4) || version != kSerVersion)
+    return fail(BRQ_ERR_UNSUPPORTED, "plan image version %u", version);
+  if (!take(&kind, 4) || !take(&d, 4) || !take(&nst, 4) || !take(&mode, 4) || !take(&flags, 4) ||
+      kind > 1 || nst < 1 || nst > kMaxStages)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "malformed plan header");
+  int32_t radix[kMaxStages];
+  if (!take(radix, sizeof(int32_t) * nst)) return fail(BRQ_ERR_INVALID_ARGUMENT, "truncated radices");
+  int64_t prod = 1, nparams = 0, nbase = 0, nblk = 0;
+  for (int t = 0; t < nst; ++t) {
+    if (radix[t] < 2 || radix[t] > 64) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad radix %d", radix[t]);
+    prod *= radix[t];
+    if (prod > ((int64_t)1 << 22)) return fail(BRQ_ERR_INVALID_ARGUMENT, "d too large");
+  }
+  if (prod != d) return fail(BRQ_ERR_INVALID_ARGUMENT, "radices do not multiply to d");
+  for (int t = 0; t < nst; ++t) {
+    const int64_t bb = (int64_t)radix[t] * radix[t];
+    nparams += (d / radix[t]) * harp_params(radix[t]);
+    nbase += bb;
+    nblk += mode == BRQ_SHARED ? bb : mode == BRQ_PER_GROUP ? (d / radix[t]) * bb : 0;
+  }
+  std::vector<float> scales, bases, blocks;
+  std::vector<int8_t> theta, signs;
+  if (kind == 1) {
+    scales.resize(nst);
+    if (!take(scales.data(), sizeof(float) * nst)) return fail(BRQ_ERR_INVALID_ARGUMENT, "truncated scales");
+    if (flags & 2u) {
+      bases.resize(nbase);
+      if (!take(bases.data(), sizeof(float) * nbase)) return fail(BRQ_ERR_INVALID_ARGUMENT, "truncated bases");
+    }
+    theta.resize(nparams);
+    if (!take(theta.data(), nparams)) return fail(BRQ_ERR_INVALID_ARGUMENT, "truncated parameters");
+  } else if (nblk) {
+    blocks.resize(nblk);
+    if (!take(blocks.data(), sizeof(float) * nblk)) return fail(BRQ_ERR_INVALID_ARGUMENT, "truncated blocks");
+  }
+  if (flags & 1u) {
+    signs.resize(d);
+    if (!take(signs.data(), d)) return fail(BRQ_ERR_INVALID_ARGUMENT, "truncated signs");
+  }
+  if (at != size) return fail(BRQ_ERR_INVALID_ARGUMENT, "%zu trailing bytes", size - at);
+  const int8_t* sg = signs.empty() ? nullptr : signs.data();
+  if (kind == 1)
+    return brq_plan_create_harp(out, d, nst, radix, theta.data(), scales.data(),
+                                bases.empty() ? nullptr : bases.data(), sg);
+  return brq_plan_create(out, d, nst, radix, blocks.empty() ? nullptr : blocks.data(), mode, sg);
 }
 
 brq_status brq_plan_destroy(brq_plan* plan) {

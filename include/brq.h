@@ -140,6 +140,22 @@ brq_status brq_plan_create_harp(brq_plan** out, int32_t d, int32_t n_stages, con
                                 const int8_t* theta_q, const float* scales, const float* bases,
                                 const int8_t* signs);
 
+/*
+ * Plan serialisation.  brq_plan_serialize writes a byte image of the plan:
+ * a plan made by brq_plan_create_harp as its int8 parameters, scales and base
+ * mixers ([HARP] section 2.4: int8 parameter storage), any other plan as its
+ * float32 blocks; then the signs; then a 64-bit hash of the image.  With
+ * buf == NULL it only sets *size; otherwise cap must be at least that size.
+ * The blocks are read back from the device (the call waits for them).
+ * brq_plan_deserialize rebuilds the plan on the current device (as
+ * brq_plan_create or brq_plan_create_harp would); serialising the result
+ * gives the same bytes.  Errors: INVALID_ARGUMENT (NULLs, cap too small, not
+ * an image, wrong hash, truncated or trailing bytes, a header that
+ * brq_plan_create would refuse), UNSUPPORTED (an image version other than
+ * 1), HIP. */
+brq_status brq_plan_serialize(const brq_plan* plan, void* buf, size_t cap, size_t* size);
+brq_status brq_plan_deserialize(brq_plan** out, const void* buf, size_t size);
+
 /* Free a plan and its device arrays; NULL is allowed.  The caller must make
  * sure no queued work still uses the plan. */
 brq_status brq_plan_destroy(brq_plan* plan);

@@ -142,3 +142,28 @@ def test_harp_blocks_70b_shapes():
                 ref = OH.stage_blocks(b, 1, tq[c * npar:(c + 1) * npar], 0.004,
                                       None if base is None else base.astype(np.float64))[0]
                 check_blocks(got[c], ref, f"d={d} t={t} c={c}")
+
+
+@pytest.mark.parametrize("kind", ["blocks", "harp"])
+def test_plan_image_rotates_identically(kind):
+    """A plan rebuilt from its byte image gives bit-identical rotations."""
+    import butterfly_rotation_quantization_amd as brq
+    rng = np.random.default_rng(11)
+    radix = (7, 16, 16)
+    d = int(np.prod(radix))
+    if kind == "harp":
+        tq = _theta(rng, OH.total_params(d, radix))
+        bases = [S.random_orthogonal(rng, 7).astype(np.float32), T.base_mixer(16).astype(np.float32),
+                 T.base_mixer(16).astype(np.float32)]
+        p = brq.Plan.from_harp(d, radix, tq, [0.01, 0.02, 0.03], bases, S.signs(rng, d))
+    else:
+        side = S.random_plan(rng, radix, "per_group")
+        p = brq.Plan(side.d, side.radix, side.mode, side.blocks, side.signs)
+    announce(f"plan image {kind}")
+    img = p.serialize()
+    q = brq.Plan.deserialize(img)
+    assert q.serialize() == img
+    x = to_dev(rng.standard_normal((40, 2 * d)).astype(np.float32), "f32")
+    a = brq.rotate(p, x, side="right")
+    b = brq.rotate(q, x, side="right")
+    assert bool((a == b).all())

@@ -282,3 +282,66 @@ def test_plan_create_harp_walk(dl, radix, with_base):
     _ok(dl, st, f"harp plan {radix}")
     assert dl.brq_dryrun_launches() == len(radix)
     dl.brq_plan_destroy(h)
+
+
+# Plan images: serialise, deserialise, serialise again gives the same bytes
+# (host memory stands in for the device here); damaged images are refused.
+def _image(dl, h):
+    n = ctypes.c_size_t()
+    assert dl.brq_plan_serialize(h, None, 0, ctypes.byref(n)) == 0
+    buf = ctypes.create_string_buffer(n.value)
+    assert dl.brq_plan_serialize(h, buf, n.value, ctypes.byref(n)) == 0
+    return buf.raw[:n.value]
+
+
+@pytest.mark.parametrize("radix,mode", [((2,) * 6, "hadamard"), ((4, 16), "shared"),
+                                        ((7, 16, 16), "per_group"), ((3, 5, 7), "per_group")])
+def test_plan_image_round_trip(dl, radix, mode):
+    p = DPlan(dl, S.random_plan(np.random.default_rng(3), radix, mode))
+    img = _image(dl, p.h)
+    assert img[:4] == b"BRQP"
+    h2 = ctypes.c_void_p()
+    _ok(dl, dl.brq_plan_deserialize(ctypes.byref(h2), img, len(img)), "deserialize")
+    assert _image(dl, h2) == img
+    dl.brq_plan_destroy(h2)
+
+
+def test_harp_plan_image_holds_the_int8_parameters(dl):
+    import oracle.harp as OH  # parameter counts only
+    radix, d = (7, 16, 16, 16), 28672
+    rng = np.random.default_rng(4)
+    th = rng.integers(-127, 128, size=OH.total_params(d, radix)).astype(np.int8)
+    sc = np.asarray([0.004, 0.003, 0.002, 0.001], dtype=np.float32)
+    bases = np.concatenate([np.eye(b, dtype=np.float32).reshape(-1) for b in radix])
+    sg = S.signs(rng, d)
+    r = np.asarray(radix, dtype=np.int32)
+    h = ctypes.c_void_p()
+    _ok(dl, dl.brq_plan_create_harp(ctypes.byref(h), d, 4, r.ctypes.data, th.ctypes.data,
+                                    sc.ctypes.data, bases.ctypes.data, sg.ctypes.data), "harp plan")
+    img = _image(dl, h)
+    # header 28 + radices 16 + scales 16 + bases + parameters + signs + hash 8
+    assert len(img) == 28 + 16 + 16 + 4 * bases.size + th.size + d + 8
+    assert img.find(th.tobytes()) > 0
+    h2 = ctypes.c_void_p()
+    _ok(dl, dl.brq_plan_deserialize(ctypes.byref(h2), img, len(img)), "deserialize harp")
+    assert _image(dl, h2) == img
+    # int8 parameters are 8.6x smaller than the float32 blocks they make
+    nblk = sum((d // b) * b * b for b in radix)
+    assert 4 * nblk / th.size > 8
+    dl.brq_plan_destroy(h2)
+    dl.brq_plan_destroy(h)
+
+
+def test_plan_image_damage_is_refused(dl):
+    p = DPlan(dl, S.random_plan(np.random.default_rng(5), (4, 16), "per_group"))
+    img = bytearray(_image(dl, p.h))
+    h = ctypes.c_void_p()
+    for bad in (bytes(img[:-1]), bytes(img[:20]), b"XXXX" + bytes(img[4:])):
+        assert dl.brq_plan_deserialize(ctypes.byref(h), bad, len(bad)) == 1
+    flipped = bytearray(img)
+    flipped[100] ^= 1
+    assert dl.brq_plan_deserialize(ctypes.byref(h), bytes(flipped), len(flipped)) == 1
+    assert b"hash" in dl.brq_last_error()
+    n = ctypes.c_size_t()
+    small = ctypes.create_string_buffer(16)
+    assert dl.brq_plan_serialize(p.h, small, 16, ctypes.byref(n)) == 1
