@@ -23,9 +23,11 @@ Modules:
 * ``lloydmax`` -- Lloyd-Max centroids/thresholds for N(0, 1).
 * ``harp`` -- HARP blocks from int8 parameters: Givens / Cayley factor times
   the base mixer ([HARP] sections 2.1, 2.2, 2.4).
+* ``chain`` -- PolarQuant's downstream chain: restore, then absmax INT4
+  ([PolarQuant] section 3).
 
 Readings of points the pages leave open are stated where they are used and
 listed together in the design notes of the repository.
 """
 
-from . import transform, quant, lloydmax, harp  # noqa: F401
+from . import transform, quant, lloydmax, harp, chain  # noqa: F401
