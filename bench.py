@@ -26,6 +26,9 @@ same kind of line; "all" prints one line per workload):
                    per-group plans, absmax 2-bit g64
   decode_t1/16/256 online right-side rotation of T x 28672 fp16 activations
                    with the (7,16,16,16) plan: latency per call
+  polar_requant    PolarQuant's downstream chain on the same 7 matrices: Q5
+                   codes restored and quantized again with absmax INT4 g128
+                   in one pass (one step = 7 calls)
   harp_build       HARP blocks built on the device from int8 parameters for
                    the 70B schedules (left (32,16,16) d=8192, right
                    (7,16,16,16) d=28672): latency of the seven launches
@@ -495,6 +498,82 @@ class PolarBlock(Workload):
                            f"({100 * share:.0f}% of the elements; right plan dense); {dt:.2f} s")}
 
 
+class PolarRequant(Workload):
+    """PolarQuant's downstream chain on the 7 projections: Q5 codes and fp16
+    norms (block-128 Walsh-Hadamard, 5-bit Lloyd-Max) restored and quantized
+    again with absmax INT4, group 128, in one pass (brq_requant)."""
+    bits_in, bits_out, g_out = 5, 4, 128
+
+    def __init__(self, name, metric):
+        self.name, self.metric = name, metric
+
+    def setup(self, brq, dev, stream):
+        import numpy as np
+        import torch
+        import synthetic as S
+        from oracle import lloydmax as LM
+        self.brq, self.stream = brq, stream
+        self.cfg = cfg = S.polar()
+        self.g_in = cfg["group"]
+        self.cb = LM.lloyd_max_gaussian(self.bits_in)[0].astype(np.float32)
+        R = cfg["right"]
+        self.H = brq.Plan(R.d, R.radix, R.mode, R.blocks, R.signs)
+        self.mats = []
+        for arr in cfg["mats"].values():
+            m, n = arr.shape
+            w = storage_tensor(arr, "bf16", dev)
+            codes, norms = brq.rotate_quantize_pack(None, self.H, w, self.bits_in, self.g_in,
+                                                    "codebook_norm", self.cb)
+            del w
+            out = torch.empty((m, n * self.bits_out // 8), dtype=torch.uint8, device=dev)
+            sc = torch.empty((m, n // self.g_out), dtype=torch.float32, device=dev)
+            self.mats.append((m, n, codes, norms, out, sc))
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        for m, n, codes, norms, out, sc in self.mats:
+            self.brq.requant(self.H, codes, norms, m, n, self.bits_in, self.g_in, self.bits_out,
+                             self.g_out, codebook=self.cb, codes_out=out, scales_out=sc,
+                             stream=self.stream)
+
+    def elements(self):
+        return sum(m * n for m, n, *_ in self.mats)
+
+    def alg_bytes(self):
+        return sum(quant_bytes(m, n, self.bits_in, self.g_in, 2) +
+                   quant_bytes(m, n, self.bits_out, self.g_out, 4) for m, n, *_ in self.mats)
+
+    def kernel_cost(self, name):
+        E = self.elements() / 7.0
+        return self.alg_bytes() / 7.0, 7 * E, "alu"
+
+    def config(self):
+        return {"matrices": {k: list(v.shape) for k, v in self.cfg["mats"].items()}, "d": 128,
+                "in": f"codebook_norm {self.bits_in}-bit g{self.g_in} (Lloyd-Max N(0,1), fp16 norms)",
+                "out": f"absmax {self.bits_out}-bit g{self.g_out} (float32 scales)"}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        from oracle import chain as C
+        from oracle import quant as Q
+        H = oracle_plan(self.cfg["right"])
+        k = self._cpu_rows
+        dt, done = 0.0, 0
+        for m, n, codes, norms, *_ in self.mats:
+            ci = Q.unpack(codes[:k].cpu().numpy(), self.bits_in, n)
+            r16 = norms[:k].cpu().numpy()
+            t0 = time.perf_counter()
+            c, a, _ = C.requant(ci, r16, self.cb, self.g_in, H, self.bits_out, self.g_out)
+            Q.pack(c, self.bits_out)
+            dt += time.perf_counter() - t0
+            done += k * n
+        share = done / self.elements()
+        return {"value": round(self.alg_bytes() * share / dt / 1e9, 6), "unit": "GB/s",
+                "cores": cpu_threads(), "kind": "oracle",
+                "sample": (f"the first {k} rows of each of the 7 projections "
+                           f"({100 * share:.0f}% of the elements); {dt:.2f} s")}
+
+
 class HarpBuild(Workload):
     """HARP blocks built on the device from int8 parameters (brq_harp_blocks):
     every stage of a left and a right schedule, one launch per stage."""
@@ -605,6 +684,12 @@ def make_workload(name):
         w.workload = f"decode_{t}x28672_f16_(7,16,16,16)"
         w._cpu_rows = t
         return w
+    if name == "polar_requant":
+        w = PolarRequant(name, "HBM GB/s: PolarQuant Q5 -> restore -> absmax INT4 g128 in one "
+                         "pass, 7 projections (hidden 4096, FFN 12288)")
+        w.workload = "polar_requant_7proj_4096_12288_q5_h128_to_absmax4_g128"
+        w._cpu_rows = 512
+        return w
     if name == "harp_build":
         w = HarpBuild(name, "latency: HARP blocks from int8 parameters (Cayley / Givens times "
                       "the base mixer), 70B schedules U (32,16,16) d=8192 + V (7,16,16,16) "
@@ -624,7 +709,8 @@ def make_workload(name):
 
 
 WORKLOADS = ("harp_mlp", "llama7b_weight", "llama7b_act", "polar_quant", "polar_dequant",
-             "llama70b_weight", "decode_t1", "decode_t16", "decode_t256", "harp_build")
+             "llama70b_weight", "decode_t1", "decode_t16", "decode_t256", "harp_build",
+             "polar_requant")
 
 
 def run_workload(wl, a, brq, torch, dev, stream):

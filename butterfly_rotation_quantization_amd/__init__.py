@@ -36,7 +36,7 @@ EXPORTED = (
     "brq_rotate_inverse", "brq_rotate_quantize_pack", "brq_dequant_unrotate",
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
     "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_plan_create_harp",
-    "brq_plan_serialize", "brq_plan_deserialize",
+    "brq_plan_serialize", "brq_plan_deserialize", "brq_requant_workspace_bytes", "brq_requant",
 )
 
 
@@ -64,6 +64,15 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(
             f"{path} is missing: build it with "
             "`python -m butterfly_rotation_quantization_amd.build` (no CPU fallback exists)")
+    # PyTorch ships its own HIP runtime.  Loading it first makes libbrq.so bind
+    # to that same runtime (same soname): one runtime per process, and tensors
+    # and streams from PyTorch are valid in the library.  Loaded the other way
+    # round, PyTorch would find the system runtime already in place and see no
+    # GPU.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = bind(ctypes.CDLL(path))
     if path == LIB_PATH:
         _lib = lib
@@ -113,6 +122,13 @@ def bind(lib):
         lib.brq_harp_blocks.restype = i32
         lib.brq_plan_create_harp.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, vp, vp, vp]
         lib.brq_plan_create_harp.restype = i32
+    if hasattr(lib, "brq_requant"):
+        lib.brq_requant_workspace_bytes.argtypes = [vp, ctypes.POINTER(Quant), ctypes.POINTER(Quant),
+                                                    i64, i64]
+        lib.brq_requant_workspace_bytes.restype = sz
+        lib.brq_requant.argtypes = [vp, vp, vp, ctypes.POINTER(Quant), i64, i64,
+                                    ctypes.POINTER(Quant), vp, vp, vp, sz, vp]
+        lib.brq_requant.restype = i32
     if hasattr(lib, "brq_plan_serialize"):
         lib.brq_plan_serialize.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
         lib.brq_plan_serialize.restype = i32
@@ -356,6 +372,30 @@ def dequant_unrotate(left: Optional[Plan], right: Optional[Plan], codes, scales,
                                      ctypes.byref(q), int(m), int(n), _ptr(out), dtype_code(out),
                                      _ld(out), wp, wb, _stream(stream)))
     return out
+
+
+def requant(right: Optional[Plan], codes, scales, m: int, n: int, bits_in: int, group_in: int,
+            bits_out: int, group_out: int, kind_in="codebook_norm", codebook=None,
+            codes_out=None, scales_out=None, ws=None, stream=None):
+    """Restore (dequantize + inverse right plan), then absmax-quantize the
+    restored rows at bits_out / group_out (brq_requant).  Returns
+    (codes_out uint8 [m, n*bits_out/8], scales_out float32 [m, n/group_out])."""
+    import torch
+    L = lib()
+    qi = make_quant(bits_in, group_in, kind_in, codebook)
+    qo = make_quant(bits_out, group_out, "absmax")
+    dev = codes.device
+    if codes_out is None:
+        codes_out = torch.empty((m, n * bits_out // 8), dtype=torch.uint8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty((m, n // group_out), dtype=torch.float32, device=dev)
+    if ws is None:
+        nb = L.brq_requant_workspace_bytes(_h(right), ctypes.byref(qi), ctypes.byref(qo), int(m), int(n))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev) if nb else None
+    wp, wb = _ws_args(ws)
+    check(L.brq_requant(_h(right), _ptr(codes), _ptr(scales), ctypes.byref(qi), int(m), int(n),
+                        ctypes.byref(qo), _ptr(codes_out), _ptr(scales_out), wp, wb, _stream(stream)))
+    return codes_out, scales_out
 
 
 def profile_enable(on: bool = True):

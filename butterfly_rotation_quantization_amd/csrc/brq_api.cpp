@@ -1063,6 +1063,59 @@ brq_status brq_dequant_unrotate(const brq_plan* left, const brq_plan* right, con
                      static_cast<hipStream_t>(stream));
 }
 
+// The fused re-quantizer takes the call (no workspace needed).
+static bool requant_fused(const brq_plan* right, const brq_quant* q_in, const brq_quant* q_out,
+                          int64_t m, int64_t n) {
+  const Plan* V = right ? &right->p : nullptr;
+  return fast_paths() && V && rh_plan_ok(V) && V->d >= 64 && V->d <= 256 && n % V->d == 0 &&
+         q_out->kind == BRQ_ABSMAX && q_out->group <= 1024 && q_in->group <= 1024 &&
+         m * (n / V->d) <= kRhMaxChunks;
+}
+
+size_t brq_requant_workspace_bytes(const brq_plan* right, const brq_quant* q_in,
+                                   const brq_quant* q_out, int64_t m, int64_t n) {
+  if (m <= 0 || n <= 0 || !q_in || !q_out) return 0;
+  if (requant_fused(right, q_in, q_out, m, n)) return 0;
+  return 2 * (size_t)m * n * sizeof(float);
+}
+
+brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* scales,
+                       const brq_quant* q_in, int64_t m, int64_t n, const brq_quant* q_out,
+                       uint8_t* codes_out, void* scales_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  if (m < 0 || n <= 0) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape");
+  brq_status st = check_quant(q_in, n);
+  if (st != BRQ_OK) return st;
+  if ((st = check_quant(q_out, n)) != BRQ_OK) return st;
+  if (q_out->kind != BRQ_ABSMAX)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "the downstream quantizer is absmax");
+  const Plan* V = right ? &right->p : nullptr;
+  if (V && n % V->d)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "right plan d = %d does not divide n", V->d);
+  if (m == 0) return BRQ_OK;
+  if (!codes || !scales || !codes_out || !scales_out)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if ((st = check_plan_device(V)) != BRQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (requant_fused(right, q_in, q_out, m, n)) {
+    st = rh_requant(V, codes, scales, q_in, m, n, q_out, codes_out, scales_out, s);
+    if (st == BRQ_ERR_HIP) return hip_fail(hipGetLastError(), "re-quantizer launch");
+    if (st != BRQ_ERR_UNSUPPORTED) return st;
+  }
+  // composed: restore into the workspace, then the quantizer on its own
+  const size_t half = (size_t)m * n * sizeof(float);
+  if (!ws || ws_bytes < 2 * half)
+    return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes < %zu", ws_bytes, 2 * half);
+  float* restored = static_cast<float*>(ws);
+  void* inner = static_cast<char*>(ws) + half;
+  st = brq_dequant_unrotate(nullptr, right, codes, scales, q_in, m, n, restored, BRQ_F32, n, inner,
+                            half, stream);
+  if (st != BRQ_OK) return st;
+  return brq_rotate_quantize_pack(nullptr, nullptr, restored, BRQ_F32, m, n, n, q_out, codes_out,
+                                  scales_out, inner, half, stream);
+}
+
 brq_status brq_lloyd_max_gaussian(int32_t bits, float* centroids) {
   g_last_error.clear();
   if (bits < 1 || bits > 5) return fail(BRQ_ERR_INVALID_ARGUMENT, "bits must be 1..5");

@@ -505,12 +505,24 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
   }
   const int64_t nwg = rh_nwg(a);
   const int esz_x = a.xt == BRQ_F32 ? 4 : 2, esz_y = a.yt == BRQ_F32 ? 4 : 2;
+  const bool deq = a.mode == RH_DEQUANT || a.mode == RH_REQUANT;
+  const bool qout = a.mode == RH_QUANT || a.mode == RH_REQUANT;
+  if (a.mode == RH_REQUANT && (l2d < 6 || l2d > 8 || a.bits2 < 2 || a.bits2 > 5 || !a.inverse ||
+                               a.h2 != (float)(((1 << a.bits2) - 1) * 0.5)))
+    return violation("re-quantizer launch (log2 d %lld, bits %lld)", l2d, a.bits2), hipErrorInvalidValue;
+  // the output quantizer's width, group and row strides
+  const int obits = a.mode == RH_REQUANT ? a.bits2 : a.bits;
+  const int ogroup = a.mode == RH_REQUANT ? a.group2 : a.group;
+  const int64_t ocodes_ld = a.mode == RH_REQUANT ? a.codes_ld2 : a.codes_ld;
+  const int64_t oscales_ld = a.mode == RH_REQUANT ? a.scales_ld2 : a.scales_ld;
   std::vector<uint8_t> cover((size_t)(a.rows * a.n), 0);
   std::vector<uint8_t> scov;
-  if (a.mode == RH_QUANT) scov.assign((size_t)(a.rows * a.scales_ld), 0);
-  const int lpg = a.mode == RH_QUANT ? a.group / 16 : 1;
-  if (a.mode == RH_QUANT && (a.group % 16 || lpg > 64 || (lpg & (lpg - 1)) || kRhTile % a.group))
-    return violation("quantizer group %lld", a.group, 0), hipErrorInvalidValue;
+  if (qout) scov.assign((size_t)(a.rows * oscales_ld), 0);
+  const int lpg = qout ? ogroup / 16 : 1;
+  if (qout && (ogroup % 16 || lpg > 64 || (lpg & (lpg - 1)) || kRhTile % ogroup))
+    return violation("quantizer group %lld", ogroup, 0), hipErrorInvalidValue;
+  if (deq && (a.group % 16 || a.group < 16))
+    return violation("dequantizer group %lld", a.group, 0), hipErrorInvalidValue;
   for (int64_t b = 0; b < nwg; ++b)
     for (int u = 0; u < kRhThreads; ++u) {
       const RhPos p = rh_pos(a, b, u);
@@ -518,7 +530,7 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
       if (p.row >= a.rows || p.col0 < 0 || p.col0 + 16 > a.n || p.col0 % 16)
         return violation("row Hadamard element (%lld, %lld)", p.row, p.col0), hipErrorInvalidValue;
       if (p.col0 % d != 16 * p.cu) return violation("chunk position of thread %lld", u, 0), hipErrorInvalidValue;
-      if (a.mode != RH_DEQUANT) {
+      if (!deq) {
         const int64_t off = p.row * a.ldx + p.col0;
         if (p.col0 + 16 > a.ldx || (off * esz_x) % 16) return violation("row Hadamard load %lld", off, 0), hipErrorInvalidValue;
       } else {
@@ -528,22 +540,22 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
         if (!in_range(p.row * a.scales_ld + p.col0 / a.group, 1, a.rows * a.scales_ld))
           return violation("scale read (%lld, %lld)", p.row, p.col0), hipErrorInvalidValue;
       }
-      if (a.mode != RH_QUANT) {
+      if (!qout) {
         const int64_t off = p.row * a.ldy + p.col0;
         if (p.col0 + 16 > a.ldy || (off * esz_y) % 16) return violation("row Hadamard store %lld", off, 0), hipErrorInvalidValue;
       } else {
-        const int64_t off = p.row * a.codes_ld + p.col0 * a.bits / 8;
-        if (!in_range(off, 2 * a.bits, a.rows * a.codes_ld) || off % ((a.bits & 1) ? 2 : 4))
+        const int64_t off = p.row * ocodes_ld + p.col0 * obits / 8;
+        if (!in_range(off, 2 * obits, a.rows * ocodes_ld) || off % ((obits & 1) ? 2 : 4))
           return violation("code write at %lld", off, 0), hipErrorInvalidValue;
         if (u % lpg == 0) {  // the group's lanes: same wave, same row, contiguous columns
-          if (p.col0 % a.group) return violation("group start column %lld", p.col0, 0), hipErrorInvalidValue;
+          if (p.col0 % ogroup) return violation("group start column %lld", p.col0, 0), hipErrorInvalidValue;
           for (int k = 1; k < lpg; ++k) {
             const RhPos o = rh_pos(a, b, u + k);
             if ((u + k) / 64 != u / 64 || !o.live || o.row != p.row || o.col0 != p.col0 + 16 * k)
               return violation("group lanes of thread %lld (lane +%lld)", u, k), hipErrorInvalidValue;
           }
-          const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
-          if (!in_range(sidx, 1, a.rows * a.scales_ld) || scov[(size_t)sidx]++)
+          const int64_t sidx = p.row * oscales_ld + p.col0 / ogroup;
+          if (!in_range(sidx, 1, a.rows * oscales_ld) || scov[(size_t)sidx]++)
             return violation("scale %lld written twice or out of range", sidx, 0), hipErrorInvalidValue;
         }
       }

@@ -26,7 +26,9 @@ constexpr int kRhTile = kRhThreads * kRhElems;   // chunk elements per workgroup
 constexpr int kRhLds = kRhTile + kRhTile / 16;   // one LDS buffer (padded)
 constexpr int kRhBins = 256;                     // codebook search bins
 
-enum RhMode { RH_ROTATE = 0, RH_QUANT = 1, RH_DEQUANT = 2 };
+// RH_REQUANT: dequantize, inverse transform, then quantize again with the
+// second quantizer (absmax, bits2, group2) -- PolarQuant's downstream chain.
+enum RhMode { RH_ROTATE = 0, RH_QUANT = 1, RH_DEQUANT = 2, RH_REQUANT = 3 };
 
 struct RhArgs {
   int log2d;          // chunk length d = 2^log2d
@@ -65,6 +67,10 @@ struct RhArgs {
   void* scales;
   const void* in_scales;
   int64_t codes_ld, scales_ld;
+  // second quantizer (RH_REQUANT): absmax, output codes and float32 scales
+  int bits2, group2;
+  float h2;
+  int64_t codes_ld2, scales_ld2;
 };
 
 static_assert(sizeof(RhArgs) <= 4096, "kernel arguments are limited to 4 KB");
@@ -182,6 +188,12 @@ brq_status rh_rqp(const Plan* V, const void* w, int wt, int64_t m, int64_t n, in
                   const brq_quant* q, uint8_t* codes, void* scales, hipStream_t s);
 brq_status rh_dequant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q,
                       int64_t m, int64_t n, void* out, int ot, int64_t ldo, hipStream_t s);
+// Dequantize with q_in, inverse transform, quantize + pack with q_out (absmax)
+// in one pass; BRQ_ERR_UNSUPPORTED when the plan, shape or alignment does not
+// fit the kernel.
+brq_status rh_requant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q_in,
+                      int64_t m, int64_t n, const brq_quant* q_out, uint8_t* codes_out,
+                      void* scales_out, hipStream_t s);
 // Quantize + pack with no transform (the quantizer pass after other kernels
 // have rotated into a float32 buffer); BRQ_ERR_UNSUPPORTED when the shape or
 // alignment does not fit the kernel.

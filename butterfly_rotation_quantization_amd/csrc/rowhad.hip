@@ -166,23 +166,26 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&c)[16]) 
   }
 }
 
-// BITS: the code width of the quantize and dequantize modes (0 for rotate).
-template <int L2D, int MODE, int BITS>
+// BITS: the code width of the quantize and dequantize modes (0 for rotate);
+// BITS2: the re-quantizer's code width (RH_REQUANT only).
+template <int L2D, int MODE, int BITS, int BITS2>
 __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   __shared__ float lds[kRhLds];  // one buffer: more workgroups per CU beat a saved barrier
   // quantize: codebook bins {own threshold (or +inf), thresholds below};
   // dequantize: the level values (centroid / sqrt(g), or code / h - 1)
-  __shared__ float2 tab[MODE == RH_QUANT ? kRhBins : (MODE == RH_DEQUANT ? kMaxLevels : 1)];
+  constexpr bool DEQ = MODE == RH_DEQUANT || MODE == RH_REQUANT;  // codes in
+  constexpr bool QOUT = MODE == RH_QUANT || MODE == RH_REQUANT;    // codes out
+  __shared__ float2 tab[MODE == RH_QUANT ? kRhBins : (DEQ ? kMaxLevels : 1)];
   constexpr int R = rh_rounds(L2D);
   constexpr int LV = (1 << BITS) - 1;
   const RhPos p = rh_pos(a, blockIdx.x, threadIdx.x);
-  const int lpg = a.group / 16;
+  const int lpg = (MODE == RH_REQUANT ? a.group2 : a.group) / 16;  // lanes per output group
   const bool bins = MODE == RH_QUANT && a.qkind == BRQ_CODEBOOK_NORM && a.bin_s != 0.f;
   // The global loads are issued first; the quantizer tables are built while
   // they are in flight.
   auto build_tables = [&]() {
     if (MODE == RH_QUANT && bins) tab[threadIdx.x] = a.bintab[threadIdx.x];  // built on the host
-    if (MODE == RH_DEQUANT && threadIdx.x <= LV) {
+    if (DEQ && threadIdx.x <= LV) {
       const int c = threadIdx.x;
       tab[c].x = a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g;
     }
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   float v[16];
 
   // ---- prologue: load or unpack + dequantize, then the signs (forward)
-  if (MODE != RH_DEQUANT) {
+  if (!DEQ) {
     if (p.live) load16(a.x, a.xt, p.row * a.ldx + p.col0, v);
     else
 #pragma unroll
@@ -240,13 +243,21 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     for (int j = 0; j < 16; ++j) v[j] *= a.signs[16 * p.cu + j];
 
   // ---- epilogue
-  if (MODE != RH_QUANT) {
+  if (!QOUT) {
     if (p.live) store16(a.y, a.yt, p.row * a.ldy + p.col0, v);
     return;
   }
+  // the quantizer of the output: the call's own, or the re-quantizer (absmax)
+  constexpr int QB = MODE == RH_REQUANT ? BITS2 : BITS;
+  constexpr int LVQ = (1 << QB) - 1;
+  const int qkind = MODE == RH_REQUANT ? (int)BRQ_ABSMAX : a.qkind;
+  const float qh = MODE == RH_REQUANT ? a.h2 : a.h;
+  const int qgroup = MODE == RH_REQUANT ? a.group2 : a.group;
+  uint8_t* const qcodes = a.codes + p.row * (MODE == RH_REQUANT ? a.codes_ld2 : a.codes_ld) + p.col0 * QB / 8;
+  const int64_t qsidx = p.row * (MODE == RH_REQUANT ? a.scales_ld2 : a.scales_ld) + p.col0 / qgroup;
   // quantizer groups of g = 16 lpg consecutive columns are lpg consecutive lanes
   float stat = 0.f;
-  if (a.qkind == BRQ_ABSMAX) {
+  if (qkind == BRQ_ABSMAX) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) stat = fmaxf(stat, fabsf(v[j]));
     stat = group_reduce<true>(stat, lpg);
@@ -258,14 +269,14 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   if (R == 1 && bins) __syncthreads();  // the bin table (R > 1 passed barriers since)
   if (!p.live) return;
   uint32_t c[16];
-  if (a.qkind == BRQ_ABSMAX) {
-    const float k = stat > 0.f ? a.h / stat : 0.f;
+  if (qkind == BRQ_ABSMAX) {
+    const float k = stat > 0.f ? qh / stat : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int q = (int)rintf(fmaf(v[j], k, a.h));
-      c[j] = (uint32_t)(q < 0 ? 0 : (q > LV ? LV : q));
+      const int q = (int)rintf(fmaf(v[j], k, qh));
+      c[j] = (uint32_t)(q < 0 ? 0 : (q > LVQ ? LVQ : q));
     }
-  } else {
+  } else if (MODE == RH_QUANT) {
     const float k = stat > 0.f ? a.sqrt_g / stat : 0.f;
     // one branch for the whole thread: inside it the 16 table reads are
     // independent and pipeline
@@ -290,19 +301,44 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   if (!(stat > 0.f))  // a zero group codes as all zeros
 #pragma unroll
     for (int j = 0; j < 16; ++j) c[j] = 0u;
-  store_codes<BITS>(a.codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
+  store_codes<QB>(qcodes, c);
   if ((threadIdx.x & (lpg - 1)) == 0) {
-    const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
-    if (a.qkind == BRQ_ABSMAX) static_cast<float*>(a.scales)[sidx] = stat;
-    else static_cast<_Float16*>(a.scales)[sidx] = (_Float16)stat;
+    if (qkind == BRQ_ABSMAX) static_cast<float*>(a.scales)[qsidx] = stat;
+    else static_cast<_Float16*>(a.scales)[qsidx] = (_Float16)stat;
   }
 }
 
-template <int L2D, int MODE, int BITS>
+template <int L2D, int MODE, int BITS, int BITS2 = 0>
 hipError_t launch_t(const RhArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((rowhad_kernel<L2D, MODE, BITS>), dim3((unsigned)rh_nwg(a)), dim3(kRhThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((rowhad_kernel<L2D, MODE, BITS, BITS2>), dim3((unsigned)rh_nwg(a)),
+                     dim3(kRhThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// The re-quantizer: output widths 2..5 for input widths 2..5, chunks of
+// 64..256 (PolarQuant's blocks are 128).
+template <int L2D, int BITS>
+hipError_t launch_requant_out(const RhArgs& a, hipStream_t s) {
+  switch (a.bits2) {
+    case 2: return launch_t<L2D, RH_REQUANT, BITS, 2>(a, s);
+    case 3: return launch_t<L2D, RH_REQUANT, BITS, 3>(a, s);
+    case 4: return launch_t<L2D, RH_REQUANT, BITS, 4>(a, s);
+    case 5: return launch_t<L2D, RH_REQUANT, BITS, 5>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int L2D>
+hipError_t launch_requant(const RhArgs& a, hipStream_t s) {
+  if constexpr (L2D >= 6 && L2D <= 8) {
+    switch (a.bits) {
+      case 2: return launch_requant_out<L2D, 2>(a, s);
+      case 3: return launch_requant_out<L2D, 3>(a, s);
+      case 4: return launch_requant_out<L2D, 4>(a, s);
+      case 5: return launch_requant_out<L2D, 5>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int L2D, int MODE>
@@ -320,6 +356,7 @@ template <int L2D>
 hipError_t launch_mode(const RhArgs& a, hipStream_t s) {
   if (a.mode == RH_ROTATE) return launch_t<L2D, RH_ROTATE, 0>(a, s);
   if (a.mode == RH_QUANT) return launch_bits<L2D, RH_QUANT>(a, s);
+  if (a.mode == RH_REQUANT) return launch_requant<L2D>(a, s);
   return launch_bits<L2D, RH_DEQUANT>(a, s);
 }
 

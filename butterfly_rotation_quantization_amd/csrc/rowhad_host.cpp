@@ -1,6 +1,7 @@
 // Host side of the row Hadamard path: which calls it takes, argument set-up
 // and launch.
 #include <cmath>
+#include <cstdio>
 #include <cstdint>
 #include <cstring>
 
@@ -192,6 +193,34 @@ brq_status rh_dequant(const Plan* V, const uint8_t* codes, const void* scales, c
   a.ldy = ldo;
   char name[64];
   snprintf(name, sizeof name, "rowhad dequant R^T(H%d) b%d g%d", V->d, q->bits, q->group);
+  return launch(a, name, s);
+}
+
+brq_status rh_requant(const Plan* V, const uint8_t* codes, const void* scales, const brq_quant* q_in,
+                      int64_t m, int64_t n, const brq_quant* q_out, uint8_t* codes_out,
+                      void* scales_out, hipStream_t s) {
+  if (!rh_plan_ok(V) || V->d < 64 || V->d > 256 || n % V->d || q_out->kind != BRQ_ABSMAX ||
+      q_out->group > 1024 || kRhTile % q_out->group || m * (n / V->d) > kRhMaxChunks ||
+      reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(scales) % 4 ||
+      reinterpret_cast<uintptr_t>(codes_out) % 4 || reinterpret_cast<uintptr_t>(scales_out) % 4)
+    return BRQ_ERR_UNSUPPORTED;
+  RhArgs a;
+  fill_common(a, V, m, n);
+  fill_quant(a, q_in, n);
+  a.mode = RH_REQUANT;
+  a.inverse = 1;
+  a.in_codes = codes;
+  a.in_scales = scales;
+  a.bits2 = q_out->bits;
+  a.group2 = q_out->group;
+  a.h2 = (float)(((1 << q_out->bits) - 1) * 0.5);
+  a.codes_ld2 = n * q_out->bits / 8;
+  a.scales_ld2 = n / q_out->group;
+  a.codes = codes_out;
+  a.scales = scales_out;
+  char name[80];
+  snprintf(name, sizeof name, "rowhad requant R^T(H%d) b%d g%d -> absmax b%d g%d", V->d, q_in->bits,
+           q_in->group, q_out->bits, q_out->group);
   return launch(a, name, s);
 }
 

@@ -220,6 +220,28 @@ brq_status brq_dequant_unrotate(const brq_plan* left, const brq_plan* right, con
                                 void* stream);
 
 /*
+ * PolarQuant's downstream chain ([PolarQuant] section 3: weights quantized
+ * by PolarQuant, restored, then quantized again with absmax INT4 do better
+ * than absmax INT4 alone): unpack and dequantize `codes`/`scales` with q_in,
+ * undo the right-side plan (W = V' M_V, as brq_dequant_unrotate with no left
+ * plan), then quantize and pack the restored rows with q_out, which must be
+ * ABSMAX.  The restored weights reach the second quantizer in float32.
+ *   codes, scales:         device inputs as brq_rotate_quantize_pack wrote them.
+ *   codes_out, scales_out: device [m][n*q_out.bits/8] bytes, float32 [m][n/q_out.group].
+ *   ws: device workspace of brq_requant_workspace_bytes(...) bytes: 0 when one
+ *       fused pass takes the call (a right Hadamard plan with d = 64..256,
+ *       q_in.group and q_out.group at most 1024), else 2*m*n*4 for the
+ *       restored matrix and the steps' own workspace.
+ * Errors: INVALID_ARGUMENT (NULLs, shapes, either quantizer, q_out not
+ * ABSMAX), UNSUPPORTED, WORKSPACE, HIP. */
+size_t brq_requant_workspace_bytes(const brq_plan* right, const brq_quant* q_in,
+                                   const brq_quant* q_out, int64_t m, int64_t n);
+brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* scales,
+                       const brq_quant* q_in, int64_t m, int64_t n, const brq_quant* q_out,
+                       uint8_t* codes_out, void* scales_out, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
  * Host helper: the 2^bits Lloyd-Max centroids for N(0,1), ascending, rounded
  * to float32 ([PolarQuant] section 2: MSE-optimal centroids for the standard
  * normal, table stored in float32).  bits in 1..5; centroids has 2^bits

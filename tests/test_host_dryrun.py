@@ -345,3 +345,27 @@ def test_plan_image_damage_is_refused(dl):
     n = ctypes.c_size_t()
     small = ctypes.create_string_buffer(16)
     assert dl.brq_plan_serialize(p.h, small, 16, ctypes.byref(n)) == 1
+
+
+# PolarQuant's downstream chain: one fused pass for right Hadamard plans with
+# d = 64..256, else dequantize + unrotate into the workspace and quantize.
+@pytest.mark.parametrize("d,m,n,bits_in,bits_out,g_out,fused", [
+    (128, 64, 4096, 5, 4, 128, True), (128, 5, 12288, 4, 4, 64, True),
+    (256, 3, 1024, 5, 2, 1024, True), (64, 7, 192, 3, 5, 64, True),
+    (512, 4, 1024, 5, 4, 128, False), (4096, 2, 4096, 5, 4, 128, False),
+])
+def test_requant_walk(dl, d, m, n, bits_in, bits_out, g_out, fused):
+    p = DPlan(dl, S.random_plan(np.random.default_rng(d), (2,) * int(np.log2(d)), "hadamard", False))
+    qi = brq.make_quant(bits_in, min(d, 1024), 1, np.linspace(-2.5, 2.5, 1 << bits_in))
+    qo = brq.make_quant(bits_out, g_out, 0)
+    nb = dl.brq_requant_workspace_bytes(p.h, ctypes.byref(qi), ctypes.byref(qo), m, n)
+    assert nb == (0 if fused else 2 * m * n * 4)
+    dl.brq_dryrun_reset()
+    st = dl.brq_requant(p.h, CODES, SCALES, ctypes.byref(qi), m, n, ctypes.byref(qo), X, Y,
+                        WS, nb, None)
+    _ok(dl, st, f"requant d={d}")
+    assert dl.brq_dryrun_launches() == (1 if fused else 2)
+    # the downstream quantizer must be absmax
+    qc = brq.make_quant(bits_out, g_out, 1, np.linspace(-2, 2, 1 << bits_out))
+    assert dl.brq_requant(p.h, CODES, SCALES, ctypes.byref(qi), m, n, ctypes.byref(qc), X, Y,
+                          WS, nb, None) == 1
