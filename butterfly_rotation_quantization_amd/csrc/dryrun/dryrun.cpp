@@ -18,6 +18,7 @@ namespace brq {
 static std::string g_violation;
 static long long g_launches = 0;
 static long long g_rows_launches = 0;  // of those, left-side stages by whole rows
+static long long g_lanes_launches = 0;  // right-side stages with groups in lanes
 
 static bool violation(const char* fmt, long long a, long long b) {
   if (g_violation.empty()) {
@@ -148,10 +149,12 @@ extern "C" {
 const char* brq_dryrun_violation(void) { return brq::g_violation.c_str(); }
 long long brq_dryrun_launches(void) { return brq::g_launches; }
 long long brq_dryrun_rows_launches(void) { return brq::g_rows_launches; }
+long long brq_dryrun_lanes_launches(void) { return brq::g_lanes_launches; }
 void brq_dryrun_reset(void) {
   brq::g_violation.clear();
   brq::g_launches = 0;
   brq::g_rows_launches = 0;
+  brq::g_lanes_launches = 0;
 }
 }
 
@@ -804,6 +807,56 @@ hipError_t launch_harp(const HarpArgs& a, hipStream_t) {
   for (int p = 0; p < a.np; ++p)
     if (used[p] != 1) return violation("HARP parameter %lld unused", p, 0), hipErrorInvalidValue;
   if (2 * b > 2 * kHpThreads) return violation("HARP columns per lane (b %lld)", b, 0), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
+  ++g_launches;
+  ++g_lanes_launches;
+  const int b = a.b;
+  if (!sl_supported(a) || rows_per != sl_rows_per(a) || rows_per % 4 || rows_per < 4)
+    return violation("lanes kernel launched for an unsupported stage (b %lld, rows %lld)", b, rows_per), hipErrorInvalidValue;
+  if (a.S < 1 || a.d % (b * a.S) || a.ngc != a.d / b || a.ngroups % a.ngc)
+    return violation("lanes kernel shape (d %lld, S %lld)", a.d, a.S), hipErrorInvalidValue;
+  const int64_t nchunk = a.ngroups / a.ngc, axis = nchunk * a.d, rows = a.lines;
+  if (axis >= ((int64_t)1 << 31)) return violation("positions beyond 32 bits (%lld)", axis, 0), hipErrorInvalidValue;
+  if (a.ld_src < axis || a.ld_dst < axis)
+    return violation("lanes kernel leading dimension (%lld < %lld)", std::min(a.ld_src, a.ld_dst), axis), hipErrorInvalidValue;
+  const SlGeom g = sl_geom(a, rows_per);
+  const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
+  std::vector<uint8_t> cover((size_t)(rows * axis), 0);
+  for (int64_t bid = 0; bid < g.lo_tiles * g.row_tiles; ++bid) {
+    const int64_t t = bid % g.lo_tiles, rt = bid / g.lo_tiles;
+    // the tile's 64 groups: one chunk, one hi, consecutive lo
+    const int64_t g0 = sl_group(t, 0);
+    if (g0 / a.ngc != (g0 + kSlLanes - 1) / a.ngc || ((g0 % a.ngc) / a.S) != (((g0 + kSlLanes - 1) % a.ngc) / a.S))
+      return violation("lane tile %lld spans chunks or strides", t, 0), hipErrorInvalidValue;
+    if (a.mode == BRQ_PER_GROUP) {
+      const int64_t base = sp_block_row(a, g0, 0);
+      if (base < 0 || base + (int64_t)kSlLanes * b * b > blk_floats)
+        return violation("lane tile blocks at %lld of %lld", base, blk_floats), hipErrorInvalidValue;
+      for (int l = 0; l < kSlLanes; ++l)
+        if (sp_block_row(a, sl_group(t, l), 0) != base + (int64_t)l * b * b)
+          return violation("blocks of lane %lld are not contiguous", l, 0), hipErrorInvalidValue;
+    }
+    for (int l = 0; l < kSlLanes; ++l) {
+      const int64_t gid = sl_group(t, l);
+      const int64_t pos0 = sp_pos(a, gid, 0);
+      for (int k = 0; k < b; ++k) {
+        const int64_t pos = pos0 + (int64_t)k * a.S;
+        if (pos != sp_pos(a, gid, k) || pos < 0 || pos >= axis)
+          return violation("lane member position %lld (k %lld)", pos, k), hipErrorInvalidValue;
+        if ((uint32_t)(pos0 % a.d) + (uint32_t)(k * a.S) >= (uint32_t)a.d)
+          return violation("lane sign index beyond d (%lld)", pos, 0), hipErrorInvalidValue;
+        for (int w = 0; w < kSlThreads / kSlLanes; ++w)
+          for (int64_t r = rt * rows_per + w; r < std::min(rt * rows_per + rows_per, rows); r += 4)
+            if (cover[(size_t)(r * axis + pos)]++)
+              return violation("lanes kernel element (%lld, %lld) twice", r, pos), hipErrorInvalidValue;
+      }
+    }
+  }
+  for (size_t i = 0; i < cover.size(); ++i)
+    if (cover[i] != 1) return violation("lanes kernel element %lld covered %lld times", (int64_t)i, cover[i]), hipErrorInvalidValue;
   return hipSuccess;
 }
 

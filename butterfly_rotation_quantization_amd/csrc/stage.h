@@ -186,6 +186,38 @@ __host__ __device__ inline int64_t sr_col(uint32_t ct, int t, int vec) {
 bool sr_supported(const SpArgs& a);
 hipError_t launch_stage_rows(const SpArgs& a, hipStream_t s);
 
+// ---- Right-side stages of radix <= 8 by groups in lanes ------------------------
+//
+// With b <= 8 a whole block (b^2 <= 64 floats) fits in registers, so a lane
+// can own one group: lane l of a workgroup takes group c = hi * S + lo0 + l
+// of one chunk, keeps B_c and its signs in registers, and walks rows.  The
+// groups of a workgroup are 64 consecutive lo, so each member k is a
+// 256-byte run of a row (64 consecutive positions) and every load and store
+// is coalesced; the four waves take every fourth row of the workgroup's row
+// range.  The blocks of the workgroup's 64 groups are contiguous in the
+// block array and pass through LDS once.  S must be a multiple of 64, and
+// at least 8 rows (below, the tile kernel spreads wider).
+constexpr int kSlThreads = 256;
+constexpr int kSlLanes = 64;   // groups per workgroup
+struct SlGeom {
+  int64_t lo_tiles;  // workgroups along the groups: nchunk * (d / (b S)) * S / 64
+  int64_t row_tiles; // workgroups along the rows
+  int rows_per;      // rows per workgroup (a multiple of 4)
+};
+__host__ __device__ inline SlGeom sl_geom(const SpArgs& a, int rows_per) {
+  SlGeom g;
+  g.lo_tiles = a.ngroups / kSlLanes;
+  g.rows_per = rows_per;
+  g.row_tiles = (a.lines + rows_per - 1) / rows_per;
+  return g;
+}
+// Group (global over chunks) of lane l of lo tile t: the tile's 64 groups are
+// consecutive group indices.
+__host__ __device__ inline int64_t sl_group(int64_t t, int l) { return t * kSlLanes + l; }
+bool sl_supported(const SpArgs& a);
+int sl_rows_per(const SpArgs& a);
+hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t s);
+
 // Host side (stage_host.cpp).  sp_shape_ok: the stage pass can run the plan
 // on this shape; sp_rotate_supported: it is also the faster choice.
 bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols);

@@ -92,6 +92,26 @@ bool sr_supported(const SpArgs& a) {
   return sr_col_tiles(a) * a.ngroups < ((int64_t)1 << 31);
 }
 
+bool sl_supported(const SpArgs& a) {
+  // below 8 rows a workgroup has idle waves and the tile kernel's wider
+  // spread of workgroups is faster
+  if (a.side != 0 || a.b2 || a.b < 2 || a.b > 8 || a.S % kSlLanes || a.ngroups % kSlLanes ||
+      a.lines < 8)
+    return false;
+  if (a.mode != BRQ_HADAMARD && !a.blk) return false;
+  const SlGeom g = sl_geom(a, sl_rows_per(a));
+  return g.lo_tiles * g.row_tiles < ((int64_t)1 << 31);
+}
+
+// Rows per workgroup: as many as keep at least 2048 workgroups (four waves
+// take every fourth row, so a multiple of 4, at most 64).
+int sl_rows_per(const SpArgs& a) {
+  const int64_t lo_tiles = a.ngroups / kSlLanes;
+  int rpw = 16;
+  while (rpw > 1 && lo_tiles * ((a.lines + 4 * rpw - 1) / (4 * rpw)) < 2048) rpw /= 2;
+  return 4 * rpw;
+}
+
 bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {
   if (!sp_shape_ok(p, side, rows, cols)) return false;
   // dense blocks: a block row in registers beats the tile pass's per-output
@@ -176,7 +196,8 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.dst_t = last ? yt : BRQ_F32;
     a.ld_dst = last ? ldy : ldm;
     const bool rows_kernel = sr_supported(a);
-    if (!rows_kernel && sp_blocks(a) >= ((int64_t)1 << 31)) return BRQ_ERR_UNSUPPORTED;  // grid
+    const bool lanes_kernel = !rows_kernel && sl_supported(a);
+    if (!rows_kernel && !lanes_kernel && sp_blocks(a) >= ((int64_t)1 << 31)) return BRQ_ERR_UNSUPPORTED;  // grid
     char name[64];
     if (pair)
       snprintf(name, sizeof name, "stage R(%d,%d) S%lld", a.b, a.b2, (long long)a.S);
@@ -184,7 +205,9 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
       snprintf(name, sizeof name, "stage %s%s(%d) S%lld", side == 0 ? "R" : "L",
                inverse ? "^T" : "", a.b, (long long)a.S);
     const int tok = prof_begin(name, s);
-    const hipError_t e = rows_kernel ? launch_stage_rows(a, s) : launch_stage(a, s);
+    const hipError_t e = rows_kernel    ? launch_stage_rows(a, s)
+                         : lanes_kernel ? launch_stage_lanes(a, sl_rows_per(a), s)
+                                        : launch_stage(a, s);
     prof_end(tok, s);
     if (e != hipSuccess) {
       *herr = e;

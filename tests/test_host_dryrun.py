@@ -28,6 +28,7 @@ def dl():
     lib.brq_dryrun_violation.restype = ctypes.c_char_p
     lib.brq_dryrun_launches.restype = ctypes.c_longlong
     lib.brq_dryrun_rows_launches.restype = ctypes.c_longlong
+    lib.brq_dryrun_lanes_launches.restype = ctypes.c_longlong
     return lib
 
 
@@ -369,3 +370,22 @@ def test_requant_walk(dl, d, m, n, bits_in, bits_out, g_out, fused):
     qc = brq.make_quant(bits_out, g_out, 1, np.linspace(-2, 2, 1 << bits_out))
     assert dl.brq_requant(p.h, CODES, SCALES, ctypes.byref(qi), m, n, ctypes.byref(qc), X, Y,
                           WS, nb, None) == 1
+
+
+# Right-side stages of radix <= 8 whose stride is a multiple of 64 keep one
+# group per lane (its block in registers); the rest keep the tile kernel.
+@pytest.mark.parametrize("radix,mode,rows,chunks,lanes", [
+    ((7, 16, 16, 16), "per_group", 512, 1, 1),    # the 70B right schedule: stage 0
+    ((7, 16, 16, 16), "per_group", 1, 1, 0),      # decode T = 1: the tile kernel
+    ((7, 16, 16, 16), "per_group", 16, 1, 1),     # decode T = 16
+    ((7, 16, 16), "shared", 37, 2, 1),            # block-diagonal, shared block
+    ((8, 8, 8, 5, 2), "per_group", 9, 1, 1),      # S = 640 at stage 0; 80 and 10 are not
+    ((2, 4, 64), "per_group", 33, 3, 2),          # S = 256 and 64
+    ((43, 16, 16), "per_group", 9, 1, 0),         # radix above 8
+])
+def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
+    side = S.random_plan(np.random.default_rng(rows), radix, mode)
+    p = DPlan(dl, side)
+    for inverse in (False, True):
+        _rotate(dl, p, 0, rows, chunks * side.d, 2, 2, inverse=inverse)
+        assert dl.brq_dryrun_lanes_launches() == lanes
