@@ -814,7 +814,7 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
   ++g_launches;
   ++g_lanes_launches;
   const int b = a.b;
-  if (!sl_supported(a) || rows_per != sl_rows_per(a) || rows_per % 4 || rows_per < 4)
+  if (!sl_supported(a) || rows_per != sl_rows_per(a) || (b <= 8 && (rows_per % 4 || rows_per < 4)))
     return violation("lanes kernel launched for an unsupported stage (b %lld, rows %lld)", b, rows_per), hipErrorInvalidValue;
   if (a.S < 1 || a.d % (b * a.S) || a.ngc != a.d / b || a.ngroups % a.ngc)
     return violation("lanes kernel shape (d %lld, S %lld)", a.d, a.S), hipErrorInvalidValue;
@@ -848,10 +848,18 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
           return violation("lane member position %lld (k %lld)", pos, k), hipErrorInvalidValue;
         if ((uint32_t)(pos0 % a.d) + (uint32_t)(k * a.S) >= (uint32_t)a.d)
           return violation("lane sign index beyond d (%lld)", pos, 0), hipErrorInvalidValue;
-        for (int w = 0; w < kSlThreads / kSlLanes; ++w)
-          for (int64_t r = rt * rows_per + w; r < std::min(rt * rows_per + rows_per, rows); r += 4)
+        // radix <= 8: wave w stores every output of rows w, w + 4, ...;
+        // radix 16: wave k / 4 stores output k of every row
+        for (int w = 0; w < kSlThreads / kSlLanes; ++w) {
+          if (b == 16 && w != k / 4) continue;
+          const int step = b == 16 ? 1 : 4;
+          for (int64_t r = rt * rows_per + (b == 16 ? 0 : w); r < std::min(rt * rows_per + rows_per, rows); r += step)
             if (cover[(size_t)(r * axis + pos)]++)
               return violation("lanes kernel element (%lld, %lld) twice", r, pos), hipErrorInvalidValue;
+        }
+        if (b == 16 && a.mode != BRQ_HADAMARD &&
+            (sp_block_row(a, gid, 4 * (k / 4)) % 4 || reinterpret_cast<uintptr_t>(a.blk) % 16))
+          return violation("radix-16 block rows of group %lld not 16-byte aligned", gid, 0), hipErrorInvalidValue;
       }
     }
   }

@@ -196,7 +196,8 @@ hipError_t launch_stage_rows(const SpArgs& a, hipStream_t s);
 // is coalesced; the four waves take every fourth row of the workgroup's row
 // range.  The blocks of the workgroup's 64 groups are contiguous in the
 // block array and pass through LDS once.  S must be a multiple of 64, and
-// at least 8 rows (below, the tile kernel spreads wider).
+// at least 8 rows (below, the tile kernel spreads wider).  Radix 16 takes
+// the same path with a quarter of each block per wave (stage_lanes.hip).
 constexpr int kSlThreads = 256;
 constexpr int kSlLanes = 64;   // groups per workgroup
 struct SlGeom {

@@ -95,21 +95,27 @@ bool sr_supported(const SpArgs& a) {
 bool sl_supported(const SpArgs& a) {
   // below 8 rows a workgroup has idle waves and the tile kernel's wider
   // spread of workgroups is faster
-  if (a.side != 0 || a.b2 || a.b < 2 || a.b > 8 || a.S % kSlLanes || a.ngroups % kSlLanes ||
-      a.lines < 8)
+  if (a.side != 0 || a.b2 || a.b < 2 || (a.b > 8 && a.b != 16) || a.S % kSlLanes ||
+      a.ngroups % kSlLanes || a.lines < 8)
     return false;
   if (a.mode != BRQ_HADAMARD && !a.blk) return false;
+  if (a.b == 16 && a.mode != BRQ_HADAMARD && !a.blk_vec) return false;  // float4 block rows
+  // radix 16: each workgroup reads its 64 blocks (64 KB), which pays off for
+  // a few rows (latency) or many (the blocks amortised over 32 rows and more);
+  // in between the tile kernel moves less (measured: 31 vs 44 us at 256 rows)
+  if (a.b == 16 && a.lines > 32 && a.lines < 4096) return false;
   const SlGeom g = sl_geom(a, sl_rows_per(a));
   return g.lo_tiles * g.row_tiles < ((int64_t)1 << 31);
 }
 
-// Rows per workgroup: as many as keep at least 2048 workgroups (four waves
-// take every fourth row, so a multiple of 4, at most 64).
+// Rows per workgroup: as many as keep at least 2048 workgroups, at most 64
+// (radix <= 8: the four waves take every fourth row, so a multiple of 4).
 int sl_rows_per(const SpArgs& a) {
   const int64_t lo_tiles = a.ngroups / kSlLanes;
-  int rpw = 16;
-  while (rpw > 1 && lo_tiles * ((a.lines + 4 * rpw - 1) / (4 * rpw)) < 2048) rpw /= 2;
-  return 4 * rpw;
+  const int minr = a.b == 16 ? 1 : 4;
+  int r = 64;
+  while (r > minr && lo_tiles * ((a.lines + r - 1) / r) < 2048) r /= 2;
+  return r;
 }
 
 bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols) {

@@ -98,6 +98,92 @@ __device__ __forceinline__ void sl_body(const SpArgs& a, int rows_per, float* bl
   }
 }
 
+// Radix 16: a block is 256 floats, so wave w keeps rows 4w .. 4w + 3 of its
+// lane's block (64 floats) and makes those four outputs for every row of the
+// workgroup's range; the four waves read the same inputs (from cache after
+// the first).  In place, a wave's outputs are other waves' inputs, so the
+// waves meet at a barrier between the reads and the writes of each row pair.
+template <typename TI, typename TO>
+__device__ __forceinline__ void sl_body16(const SpArgs& a, int rows_per) {
+  constexpr int B = 16, JW = 4;
+  using SI = typename Elem<TI>::S;
+  using SO = typename Elem<TO>::S;
+  const SI* src = static_cast<const SI*>(a.src);
+  SO* dst = static_cast<SO*>(a.dst);
+  const int l = threadIdx.x & (kSlLanes - 1), w = threadIdx.x / kSlLanes;
+  const uint32_t lo_tiles = (uint32_t)(a.ngroups / kSlLanes);
+  const uint32_t t = blockIdx.x % lo_tiles, rt = blockIdx.x / lo_tiles;
+  const int64_t gid = sl_group(t, l);
+  const int64_t pos0 = sp_pos(a, gid, 0);
+  const int64_t S = a.S;
+  const uint32_t ip0 = (uint32_t)pos0 % (uint32_t)a.d;
+  float wq[JW][B];
+  if (a.mode == BRQ_HADAMARD) {
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+      for (int k = 0; k < B; ++k) wq[jj][k] = (__popc((JW * w + jj) & k) & 1) ? -a.hscale : a.hscale;
+  } else {
+    const float* row = a.blk + sp_block_row(a, gid, JW * w);
+#pragma unroll
+    for (int q = 0; q < JW * B / 4; ++q) {  // 16-byte aligned: the host checks blk_vec
+      const float4 v = *reinterpret_cast<const float4*>(row + 4 * q);
+      wq[q / 4][4 * (q % 4)] = v.x;
+      wq[q / 4][4 * (q % 4) + 1] = v.y;
+      wq[q / 4][4 * (q % 4) + 2] = v.z;
+      wq[q / 4][4 * (q % 4) + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      if (a.sign_in) wq[jj][k] *= a.sign_in[ip0 + (uint32_t)(k * S)];
+      if (a.sign_out) wq[jj][k] *= a.sign_out[ip0 + (uint32_t)((JW * w + jj) * S)];
+    }
+  const bool in_place = a.src == a.dst;
+  const int64_t rb = (int64_t)rt * rows_per;
+  const int64_t rend = rb + rows_per < a.lines ? rb + rows_per : a.lines;
+  for (int64_t r = rb; r < rend; r += 2) {  // the same trip count for every wave
+    const bool two = r + 1 < rend;
+    const SI* s0 = src + r * a.ld_src;
+    const SI* s1 = src + (two ? r + 1 : r) * a.ld_src;
+    float x0[B], x1[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      x0[k] = Elem<TI>::in(s0[pos0 + k * S]);
+      x1[k] = Elem<TI>::in(s1[pos0 + k * S]);
+    }
+    if (in_place) __syncthreads();  // every wave has read both rows
+    SO* d0 = dst + r * a.ld_dst;
+    SO* d1 = dst + (r + 1) * a.ld_dst;
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        y0 = fmaf(wq[jj][k], x0[k], y0);
+        y1 = fmaf(wq[jj][k], x1[k], y1);
+      }
+      d0[pos0 + (JW * w + jj) * S] = Elem<TO>::out(y0);
+      if (two) d1[pos0 + (JW * w + jj) * S] = Elem<TO>::out(y1);
+    }
+  }
+}
+
+template <typename TI>
+__device__ __forceinline__ void sl_out16(const SpArgs& a, int rows_per) {
+  if (a.dst_t == BRQ_F32) sl_body16<TI, float>(a, rows_per);
+  else if (a.dst_t == BRQ_BF16) sl_body16<TI, Bf16>(a, rows_per);
+  else sl_body16<TI, _Float16>(a, rows_per);
+}
+
+__global__ __launch_bounds__(kSlThreads) void stage_lanes16_kernel(SpArgs a, int rows_per) {
+  if (a.src_t == BRQ_F32) sl_out16<float>(a, rows_per);
+  else if (a.src_t == BRQ_BF16) sl_out16<Bf16>(a, rows_per);
+  else sl_out16<_Float16>(a, rows_per);
+}
+
 template <int B, typename TI>
 __device__ __forceinline__ void sl_out(const SpArgs& a, int rows_per, float* blds) {
   if (a.dst_t == BRQ_F32) sl_body<B, TI, float>(a, rows_per, blds);
@@ -132,6 +218,12 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t s) {
     case 6: return launch_t<6>(a, rows_per, s);
     case 7: return launch_t<7>(a, rows_per, s);
     case 8: return launch_t<8>(a, rows_per, s);
+    case 16: {
+      const SlGeom g = sl_geom(a, rows_per);
+      hipLaunchKernelGGL(stage_lanes16_kernel, dim3((unsigned)(g.lo_tiles * g.row_tiles)),
+                         dim3(kSlThreads), 0, s, a, rows_per);
+      return hipGetLastError();
+    }
     default: return hipErrorInvalidValue;
   }
 }

@@ -163,3 +163,25 @@ def test_left_leading_dimension(offset):
     brq.rotate_inverse(lib_plan(side), y.contiguous(), xi, side="left")
     check_rotation(from_dev(xi).T, xs[:, offset:offset + 64].astype(np.float64).T, "f32",
                    f"left ld offset {offset} round trip")
+
+
+@pytest.mark.parametrize("radix,mode,rows", [((2, 16, 64), "per_group", 16),
+                                             ((2, 16, 64), "per_group", 4096),
+                                             ((7, 16, 16, 16), "per_group", 24),
+                                             ((7, 16, 16, 16), "per_group", 64),
+                                             ((4, 16, 64), "hadamard", 40)])
+def test_right_stages_in_place(radix, mode, rows):
+    """float32 in and out: every stage after the first updates the output in
+    place, so a stage whose waves share rows must not write before all have
+    read (radix 16 with groups in lanes)."""
+    import butterfly_rotation_quantization_amd as brq
+    side = _side(radix, mode, seed=21)
+    d = side.d
+    announce(f"right in place radix={radix} rows={rows}")
+    xs = _input(rows, d, "f32", seed=9)
+    p = lib_plan(side)
+    y = brq.rotate(p, to_dev(xs, "f32"), side="right")
+    ref = T.apply_right(orc_plan(side), xs.astype(np.float64), method=method_for(d))
+    check_rotation(from_dev(y), ref, "f32", f"in place {radix}")
+    xi = brq.rotate_inverse(p, y, side="right")
+    check_rotation(from_dev(xi), xs.astype(np.float64), "f32", f"in place inverse {radix}")

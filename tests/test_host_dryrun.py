@@ -375,13 +375,16 @@ def test_requant_walk(dl, d, m, n, bits_in, bits_out, g_out, fused):
 # Right-side stages of radix <= 8 whose stride is a multiple of 64 keep one
 # group per lane (its block in registers); the rest keep the tile kernel.
 @pytest.mark.parametrize("radix,mode,rows,chunks,lanes", [
-    ((7, 16, 16, 16), "per_group", 512, 1, 1),    # the 70B right schedule: stage 0
+    ((7, 16, 16, 16), "per_group", 4096, 1, 2),   # the 70B right schedule: stages 0, 1
     ((7, 16, 16, 16), "per_group", 1, 1, 0),      # decode T = 1: the tile kernel
-    ((7, 16, 16, 16), "per_group", 16, 1, 1),     # decode T = 16
+    ((7, 16, 16, 16), "per_group", 16, 1, 2),     # decode T = 16
     ((7, 16, 16), "shared", 37, 2, 1),            # block-diagonal, shared block
     ((8, 8, 8, 5, 2), "per_group", 9, 1, 1),      # S = 640 at stage 0; 80 and 10 are not
     ((2, 4, 64), "per_group", 33, 3, 2),          # S = 256 and 64
-    ((43, 16, 16), "per_group", 9, 1, 0),         # radix above 8
+    ((43, 16, 16), "per_group", 9, 1, 0),         # radix 43; radix 16 at strides 16 and 1
+    ((7, 16, 16, 16), "shared", 64, 1, 1),        # radix 7 (radix 16: block rows not 16-byte aligned)
+    ((7, 16, 16, 16), "per_group", 256, 1, 1),    # radix 16 only for <= 32 or >= 4096 rows
+    ((2, 16, 64), "shared", 12, 2, 2),            # radix 2 (S = 1024) and 16 (S = 64)
 ])
 def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
     side = S.random_plan(np.random.default_rng(rows), radix, mode)
