@@ -25,9 +25,11 @@ Modules:
   the base mixer ([HARP] sections 2.1, 2.2, 2.4).
 * ``chain`` -- PolarQuant's downstream chain: restore, then absmax INT4
   ([PolarQuant] section 3).
+* ``linear`` -- the quantized linear layer at decode: rotate the activations,
+  multiply by the quantized rotated weight, unrotate the output ([HARP] 2).
 
 Readings of points the pages leave open are stated where they are used and
 listed together in the design notes of the repository.
 """
 
-from . import transform, quant, lloydmax, harp, chain  # noqa: F401
+from . import transform, quant, lloydmax, harp, chain, linear  # noqa: F401
