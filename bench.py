@@ -29,6 +29,10 @@ same kind of line; "all" prints one line per workload):
   polar_requant    PolarQuant's downstream chain on the same 7 matrices: Q5
                    codes restored and quantized again with absmax INT4 g128
                    in one pass (one step = 7 calls)
+  qlinear_t1/16/256 the quantized 70B down projection at decode: T x 28672
+                   f16 activations rotated (7,16,16,16), times the 2-bit g64
+                   weight 8192 x 28672, the output rotated back (32,16,16):
+                   latency per call
   harp_build       HARP blocks built on the device from int8 parameters for
                    the 70B schedules (left (32,16,16) d=8192, right
                    (7,16,16,16) d=28672): latency of the seven launches
@@ -42,6 +46,7 @@ same kind of line; "all" prints one line per workload):
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -59,6 +64,7 @@ HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 FP32_MFMA_PEAK_TFLOPS = 157.3
 FP64_VECTOR_PEAK_TFLOPS = 78.6
+F16_MFMA_PEAK_TFLOPS = 2500.0  # dense f16 / bf16 MFMA
 MALL_BYTES = 256 << 20
 
 
@@ -93,12 +99,12 @@ def roofline_of(bytes_, flops, engine):
     """(bound, achieved-per-second function inputs) for one kernel: the
     resource whose time floor is larger at peak binds."""
     t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
-    peak = {"mfma": FP32_MFMA_PEAK_TFLOPS, "alu64": FP64_VECTOR_PEAK_TFLOPS}.get(
-        engine, FP32_VECTOR_PEAK_TFLOPS)
+    peak = {"mfma": FP32_MFMA_PEAK_TFLOPS, "alu64": FP64_VECTOR_PEAK_TFLOPS,
+            "mfma16": F16_MFMA_PEAK_TFLOPS}.get(engine, FP32_VECTOR_PEAK_TFLOPS)
     t_fl = flops / (peak * 1e12)
     if t_hbm >= t_fl:
         return "hbm", bytes_ / 1e9, "GB/s", HBM_PEAK_GBS
-    return ("mfma" if engine == "mfma" else "alu"), flops / 1e12, "TFLOP/s", peak
+    return ("mfma" if engine.startswith("mfma") else "alu"), flops / 1e12, "TFLOP/s", peak
 
 
 def measured_traffic(workload: str, kernel_name: str):
@@ -574,6 +580,99 @@ class PolarRequant(Workload):
                            f"({100 * share:.0f}% of the elements); {dt:.2f} s")}
 
 
+class DecodeLinear(Workload):
+    """The quantized down projection of a 70B decoder layer at decode
+    (brq_qlinear): T tokens x 28672 f16 activations rotated with the right plan
+    (7,16,16,16), times the 2-bit g64 absmax weight 8192 x 28672 (dequantized
+    in the product's prologue), the output rotated back with the left plan
+    (32,16,16)."""
+    unit, higher_is_better, dtype = "us", False, "f16"
+    m, n, bits, group = 8192, 28672, 2, 64
+
+    def __init__(self, name, metric, tokens):
+        self.name, self.metric, self.T = name, metric, tokens
+
+    def setup(self, brq, dev, stream):
+        import numpy as np
+        import torch
+        import synthetic as S
+        self.brq, self.stream = brq, stream
+        cfg = S.llama70b(rows=1, tokens=(self.T,))
+        self.Ls, self.Rs = cfg["left"], cfg["right"]
+        rng = S.streams(7100, 1)[0]
+        m, n, b = self.m, self.n, self.bits
+        # the weight: seeded codes and scales (any W' has this form)
+        self.codes_h = rng.integers(0, 256, size=(m, n * b // 8), dtype=np.int64).astype(np.uint8)
+        self.alpha_h = ((0.5 + rng.random((m, n // self.group))) * 0.05).astype(np.float32)
+        self.x_h = cfg["acts"][self.T]
+        self.U = brq.Plan(self.Ls.d, self.Ls.radix, self.Ls.mode, self.Ls.blocks, self.Ls.signs)
+        self.V = brq.Plan(self.Rs.d, self.Rs.radix, self.Rs.mode, self.Rs.blocks, self.Rs.signs)
+        # several weight copies so that the step streams the weight from HBM
+        wb = self.codes_h.nbytes + self.alpha_h.nbytes
+        self.ws_copies = [(torch.from_numpy(self.codes_h).to(dev), torch.from_numpy(self.alpha_h).to(dev))
+                          for _ in range(copies_for(wb))]
+        self.x = torch.from_numpy(self.x_h).to(dev)
+        self.y = torch.empty((self.T, m), dtype=torch.float16, device=dev)
+        q = brq.make_quant(b, self.group, "absmax")
+        nb = brq.lib().brq_qlinear_workspace_bytes(self.U.handle, self.V.handle, ctypes.byref(q),
+                                                   self.T, m, n)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.latency = True
+
+    def step(self, i):
+        codes, alpha = self.ws_copies[i % len(self.ws_copies)]
+        self.brq.qlinear(self.U, self.V, self.x, codes, alpha, self.m, self.n, self.bits,
+                         self.group, y=self.y, ws=self.ws, stream=self.stream)
+
+    def value(self, ms):
+        return ms * 1e3
+
+    def elements(self):
+        return self.m * self.n
+
+    def alg_bytes(self):
+        m, n, T_ = self.m, self.n, self.T
+        return (quant_bytes(m, n, self.bits, self.group, 4) + 2 * T_ * n + 2 * T_ * m +
+                plan_bytes(self.Rs.d, self.Rs.radix) + plan_bytes(self.Ls.d, self.Ls.radix))
+
+    def kernel_cost(self, name):
+        m, n, T_ = self.m, self.n, self.T
+        if name.startswith("qlinear b"):
+            return (quant_bytes(m, n, self.bits, self.group, 4) + 2 * T_ * n,
+                    2 * T_ * m * n, "mfma16")
+        if name.startswith("qlinear reduce"):
+            return 8 * T_ * m, T_ * m, "alu"
+        # the rotations' stage passes
+        d = self.Rs.d if name.startswith("stage R(") else self.Ls.d  # R^T: the output's
+        b = int(re.search(r"\((\d+)", name).group(1))
+        return 8 * T_ * d + 4 * d * b, 2 * b * T_ * d, "alu"
+
+    def config(self):
+        return {"tokens": self.T, "m": self.m, "n": self.n, "bits": self.bits, "group": self.group,
+                "left": {"d": self.Ls.d, "radix": list(self.Ls.radix)},
+                "right": {"d": self.Rs.d, "radix": list(self.Rs.radix)},
+                "weight_copies": len(self.ws_copies)}
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        import synthetic as S
+        from oracle import linear as OL
+        from oracle import quant as Q
+        Uo, Vo = oracle_plan(self.Ls), oracle_plan(self.Rs)
+        rows = 256  # output rows of the weight in the sample
+        t0 = time.perf_counter()
+        xt = OL.rotate_acts(Vo, S.storage_to_f64(self.x_h, "f16"))
+        w = OL.weight(Q.unpack(self.codes_h[:rows], self.bits, self.n), self.alpha_h[:rows].astype(np.float64),
+                      self.bits, self.group)
+        z = xt @ w.T
+        dt = time.perf_counter() - t0
+        share = rows / self.m
+        return {"value": round(dt * 1e6 / share, 1), "unit": "us", "cores": cpu_threads(),
+                "kind": "oracle",
+                "sample": (f"rotation of the {self.T} tokens and {rows} of the {self.m} weight rows "
+                           f"(scaled by {1 / share:.0f}); the output rotation left out; {dt:.2f} s")}
+
+
 class HarpBuild(Workload):
     """HARP blocks built on the device from int8 parameters (brq_harp_blocks):
     every stage of a left and a right schedule, one launch per stage."""
@@ -684,6 +783,12 @@ def make_workload(name):
         w.workload = f"decode_{t}x28672_f16_(7,16,16,16)"
         w._cpu_rows = t
         return w
+    if name.startswith("qlinear_t"):
+        t = int(name[len("qlinear_t"):])
+        w = DecodeLinear(name, f"latency per call: quantized 70B down projection at decode, {t} "
+                         "tokens (rotate, 2-bit g64 product, unrotate)", t)
+        w.workload = f"qlinear_{t}x28672_f16_w8192x28672_absmax2_g64_(32,16,16)x(7,16,16,16)"
+        return w
     if name == "polar_requant":
         w = PolarRequant(name, "HBM GB/s: PolarQuant Q5 -> restore -> absmax INT4 g128 in one "
                          "pass, 7 projections (hidden 4096, FFN 12288)")
@@ -710,7 +815,7 @@ def make_workload(name):
 
 WORKLOADS = ("harp_mlp", "llama7b_weight", "llama7b_act", "polar_quant", "polar_dequant",
              "llama70b_weight", "decode_t1", "decode_t16", "decode_t256", "harp_build",
-             "polar_requant")
+             "polar_requant", "qlinear_t1", "qlinear_t16", "qlinear_t256")
 
 
 def run_workload(wl, a, brq, torch, dev, stream):

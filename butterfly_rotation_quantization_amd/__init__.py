@@ -37,6 +37,7 @@ EXPORTED = (
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
     "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_plan_create_harp",
     "brq_plan_serialize", "brq_plan_deserialize", "brq_requant_workspace_bytes", "brq_requant",
+    "brq_qlinear_workspace_bytes", "brq_qlinear",
 )
 
 
@@ -129,6 +130,12 @@ def bind(lib):
         lib.brq_requant.argtypes = [vp, vp, vp, ctypes.POINTER(Quant), i64, i64,
                                     ctypes.POINTER(Quant), vp, vp, vp, sz, vp]
         lib.brq_requant.restype = i32
+    if hasattr(lib, "brq_qlinear"):
+        lib.brq_qlinear_workspace_bytes.argtypes = [vp, vp, ctypes.POINTER(Quant), i64, i64, i64]
+        lib.brq_qlinear_workspace_bytes.restype = sz
+        lib.brq_qlinear.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, ctypes.POINTER(Quant), i64,
+                                    i64, vp, i32, i64, vp, sz, vp]
+        lib.brq_qlinear.restype = i32
     if hasattr(lib, "brq_plan_serialize"):
         lib.brq_plan_serialize.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
         lib.brq_plan_serialize.restype = i32
@@ -396,6 +403,27 @@ def requant(right: Optional[Plan], codes, scales, m: int, n: int, bits_in: int, 
     check(L.brq_requant(_h(right), _ptr(codes), _ptr(scales), ctypes.byref(qi), int(m), int(n),
                         ctypes.byref(qo), _ptr(codes_out), _ptr(scales_out), wp, wb, _stream(stream)))
     return codes_out, scales_out
+
+
+def qlinear(left: Optional[Plan], right: Optional[Plan], x, codes, scales, m: int, n: int,
+            bits: int, group: int, y=None, out_dtype=None, ws=None, stream=None):
+    """Y = X W^T for the weight W = M_U^T W' M_V stored as the absmax codes and
+    scales of W' (brq_qlinear): rotate X, the quantized product, unrotate.
+    x [T, n] f16/bf16.  Returns y [T, m]."""
+    import torch
+    L = lib()
+    T = int(x.shape[0])
+    q = make_quant(bits, group, "absmax")
+    if y is None:
+        y = torch.empty((T, m), dtype=out_dtype or x.dtype, device=x.device)
+    if ws is None:
+        nb = L.brq_qlinear_workspace_bytes(_h(left), _h(right), ctypes.byref(q), T, int(m), int(n))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
+    wp, wb = _ws_args(ws)
+    check(L.brq_qlinear(_h(left), _h(right), _ptr(x), dtype_code(x), _ld(x), T, _ptr(codes),
+                        _ptr(scales), ctypes.byref(q), int(m), int(n), _ptr(y), dtype_code(y),
+                        _ld(y), wp, wb, _stream(stream)))
+    return y
 
 
 def profile_enable(on: bool = True):

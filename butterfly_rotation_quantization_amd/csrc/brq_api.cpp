@@ -15,6 +15,7 @@
 #include "fused.h"
 #include "rowhad.h"
 #include "harp.h"
+#include "qlinear.h"
 #include "stage.h"
 
 struct brq_plan {
@@ -1114,6 +1115,139 @@ brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* 
   if (st != BRQ_OK) return st;
   return brq_rotate_quantize_pack(nullptr, nullptr, restored, BRQ_F32, m, n, n, q_out, codes_out,
                                   scales_out, inner, half, stream);
+}
+
+// ---- quantized linear layer at decode ----------------------------------------
+
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Split the input index so that a few tokens still give about 1024 workgroups.
+int ql_splits(int64_t T, int64_t m, int64_t n, int group) {
+  const int64_t base = (m / kQlOut) * ((T + kQlTok - 1) / kQlTok);
+  int64_t s = (1024 + base - 1) / base;
+  const int64_t ng = n / group;
+  if (s > ng) s = ng;
+  if (s > 64) s = 64;
+  return (int)(s < 1 ? 1 : s);
+}
+
+struct QlLayout {
+  size_t xt_off, part_off, z_off, rot_off, total, rot_bytes;
+  int splits;
+  int64_t kc;
+};
+
+QlLayout ql_layout(const Plan* U, const Plan* V, const brq_quant* q, int64_t T, int64_t m,
+                   int64_t n) {
+  QlLayout L;
+  L.splits = ql_splits(T, m, n, q->group);
+  const int64_t ng = n / q->group;
+  L.kc = ((ng + L.splits - 1) / L.splits) * q->group;
+  L.splits = (int)((n + L.kc - 1) / L.kc);
+  size_t at = 0;
+  L.xt_off = at;
+  if (V) at += align256((size_t)T * n * 2);
+  L.part_off = at;
+  at += align256((size_t)L.splits * T * m * sizeof(float));
+  L.z_off = at;
+  if (U) at += align256((size_t)T * m * sizeof(float));
+  L.rot_off = at;
+  // the rotations' own float32 intermediate (X~ written in a 16-bit type,
+  // Y in the caller's type)
+  const size_t rin = V ? (size_t)T * n * sizeof(float) : 0;
+  const size_t rout = U ? (size_t)T * m * sizeof(float) : 0;
+  L.rot_bytes = rin > rout ? rin : rout;
+  L.total = at + L.rot_bytes;
+  return L;
+}
+
+}  // namespace
+
+size_t brq_qlinear_workspace_bytes(const brq_plan* left, const brq_plan* right,
+                                   const brq_quant* q, int64_t T, int64_t m, int64_t n) {
+  if (!q || T <= 0 || m <= 0 || n <= 0 || q->group <= 0 || n % q->group) return 0;
+  return ql_layout(left ? &left->p : nullptr, right ? &right->p : nullptr, q, T, m, n).total;
+}
+
+brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* x, int32_t xt,
+                       int64_t ldx, int64_t T, const uint8_t* codes, const void* scales,
+                       const brq_quant* q, int64_t m, int64_t n, void* y, int32_t yt, int64_t ldy,
+                       void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (xt != BRQ_F16 && xt != BRQ_BF16)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "activations must be f16 or bf16");
+  if (!valid_dtype(yt)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad output dtype");
+  if (T < 0 || m <= 0 || n <= 0 || ldx < n || ldy < m)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape or leading dimension");
+  brq_status st = check_quant(q, n);
+  if (st != BRQ_OK) return st;
+  if (q->kind != BRQ_ABSMAX) return fail(BRQ_ERR_INVALID_ARGUMENT, "the weight must be absmax-quantized");
+  const Plan* U = left ? &left->p : nullptr;
+  const Plan* V = right ? &right->p : nullptr;
+  if (U && U->d != m) return fail(BRQ_ERR_INVALID_ARGUMENT, "left plan d = %d != m", U->d);
+  if (V && n % V->d) return fail(BRQ_ERR_INVALID_ARGUMENT, "right plan d = %d does not divide n", V->d);
+  if (m % kQlOut) return fail(BRQ_ERR_UNSUPPORTED, "m must be a multiple of %d", kQlOut);
+  if (T == 0) return BRQ_OK;
+  if (!x || !codes || !scales || !y) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(scales) % 4)
+    return fail(BRQ_ERR_ALIGNMENT, "codes and scales must be 4-byte aligned");
+  if (!V && (reinterpret_cast<uintptr_t>(x) % 16 || ldx % 8))
+    return fail(BRQ_ERR_ALIGNMENT, "activations need 16-byte aligned rows without a right plan");
+  if ((st = check_plan_device(U)) != BRQ_OK) return st;
+  if ((st = check_plan_device(V)) != BRQ_OK) return st;
+  const QlLayout L = ql_layout(U, V, q, T, m, n);
+  if (!ws || ws_bytes < L.total)
+    return fail(BRQ_ERR_WORKSPACE, "workspace of %zu bytes < %zu", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1. X~ = X M_V^T, in the activation type
+  const void* xr = x;
+  int64_t ldxr = ldx;
+  if (V) {
+    st = brq_rotate(right, 0, x, xt, ldx, w + L.xt_off, xt, n, T, n, w + L.rot_off, L.rot_bytes,
+                    stream);
+    if (st != BRQ_OK) return st;
+    xr = w + L.xt_off;
+    ldxr = n;
+  }
+  // 2. the product, split over the input index
+  QlArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.x = xr;
+  a.xt = xt;
+  a.ldx = ldxr;
+  a.T = T;
+  a.m = m;
+  a.n = n;
+  a.codes = codes;
+  a.scales = static_cast<const float*>(scales);
+  a.bits = q->bits;
+  a.group = q->group;
+  a.codes_ld = n * q->bits / 8;
+  a.scales_ld = n / q->group;
+  a.splits = L.splits;
+  a.kc = L.kc;
+  a.part = reinterpret_cast<float*>(w + L.part_off);
+  char name[48];
+  snprintf(name, sizeof name, "qlinear b%d g%d", q->bits, q->group);
+  int tok = prof_begin(name, s);
+  hipError_t e = launch_qlinear(a, s);
+  prof_end(tok, s);
+  if (e != hipSuccess) return hip_fail(e, "quantized linear launch");
+  // 3. sum the parts, then Y = Z M_U (rows z -> M_U^T z)
+  void* zout = U ? static_cast<void*>(w + L.z_off) : y;
+  const int zt = U ? (int)BRQ_F32 : yt;
+  const int64_t ldz = U ? m : ldy;
+  tok = prof_begin("qlinear reduce", s);
+  e = launch_ql_reduce(a.part, L.splits, T, m, zout, zt, ldz, s);
+  prof_end(tok, s);
+  if (e != hipSuccess) return hip_fail(e, "quantized linear reduce launch");
+  if (U)
+    return brq_rotate_inverse(left, 0, zout, BRQ_F32, m, y, yt, ldy, T, m, w + L.rot_off,
+                              L.rot_bytes, stream);
+  return BRQ_OK;
 }
 
 brq_status brq_lloyd_max_gaussian(int32_t bits, float* centroids) {

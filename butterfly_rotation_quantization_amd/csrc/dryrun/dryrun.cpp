@@ -12,6 +12,7 @@
 
 #include "brq_internal.h"
 #include "harp.h"
+#include "qlinear.h"
 
 namespace brq {
 
@@ -865,6 +866,58 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
   }
   for (size_t i = 0; i < cover.size(); ++i)
     if (cover[i] != 1) return violation("lanes kernel element %lld covered %lld times", (int64_t)i, cover[i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
+  ++g_launches;
+  if (a.bits < 2 || a.bits > 5 || a.group % 32 || a.group < 32 || a.n % a.group || a.m % kQlOut ||
+      a.kc % a.group || a.kc <= 0 || a.splits < 1 || (a.splits - 1) * a.kc >= a.n || a.splits * a.kc < a.n)
+    return violation("quantized linear geometry (splits %lld, kc %lld)", a.splits, a.kc), hipErrorInvalidValue;
+  if (a.ldx < a.n || a.ldx % 8 || reinterpret_cast<uintptr_t>(a.x) % 16)
+    return violation("activation rows not 16-byte vectors (ld %lld)", a.ldx, 0), hipErrorInvalidValue;
+  if (a.codes_ld != a.n * a.bits / 8 || a.scales_ld != a.n / a.group)
+    return violation("code or scale row length %lld", a.codes_ld, 0), hipErrorInvalidValue;
+  const int64_t nb = ql_blocks(a);
+  if (nb >= ((int64_t)1 << 31)) return violation("quantized linear grid %lld", nb, 0), hipErrorInvalidValue;
+  std::vector<uint8_t> cover((size_t)(a.splits * a.T * a.m), 0);
+  for (int64_t bid = 0; bid < nb; ++bid) {
+    const QlTile t = ql_tile(a, bid);
+    if (t.ct >= ql_ctiles(a) || t.tt >= ql_ttiles(a) || t.split >= a.splits)
+      return violation("quantized linear block %lld", bid, 0), hipErrorInvalidValue;
+    const int64_t kb = t.split * a.kc, ke = std::min(kb + a.kc, a.n);
+    for (int w = 0; w < 4; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+        const int64_t o = t.ct * kQlOut + 16 * w + lr, tok = t.tt * kQlTok + lr;
+        if (o >= a.m) return violation("weight row %lld", o, 0), hipErrorInvalidValue;
+        for (int64_t g0 = kb; g0 < ke; g0 += a.group) {
+          if (g0 / a.group >= a.scales_ld) return violation("scale column %lld", g0 / a.group, 0), hipErrorInvalidValue;
+          for (int64_t k = g0 + 8 * lg; k < g0 + a.group; k += 32) {
+            if (k + 8 > a.n) return violation("input columns %lld", k, 0), hipErrorInvalidValue;
+            const int64_t off = ql_code_off(a, o, k);
+            if (off < 0 || off + a.bits > a.m * a.codes_ld || (a.bits == 2 && off % 2) || (a.bits == 4 && off % 4))
+              return violation("code read at %lld", off, 0), hipErrorInvalidValue;
+            if (tok < a.T && (tok * a.ldx + k) % 8) return violation("activation vector at %lld", tok * a.ldx + k, 0), hipErrorInvalidValue;
+          }
+        }
+        for (int i = 0; i < 4; ++i) {
+          const int64_t tk = t.tt * kQlTok + 4 * lg + i;
+          if (tk < a.T && cover[(size_t)((t.split * a.T + tk) * a.m + o)]++)
+            return violation("partial (%lld, %lld) written twice", tk, o), hipErrorInvalidValue;
+        }
+      }
+  }
+  for (size_t i = 0; i < cover.size(); ++i)
+    if (cover[i] != 1) return violation("partial %lld written %lld times", (int64_t)i, cover[i]), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_ql_reduce(const float*, int splits, int64_t T, int64_t m, void*, int ot,
+                            int64_t ldo, hipStream_t) {
+  ++g_launches;
+  if (splits < 1 || T < 1 || m < 1 || ldo < m || (ot != BRQ_F32 && ot != BRQ_F16 && ot != BRQ_BF16))
+    return violation("reduce geometry (splits %lld, ld %lld)", splits, ldo), hipErrorInvalidValue;
   return hipSuccess;
 }
 

@@ -1,0 +1,70 @@
+// Quantized linear layer at decode: Z = X~ W'^T, the weight given as absmax
+// codes and float32 scales (the output of rotate_quantize_pack).
+//
+// Dequantization happens in the product's prologue.  A b-bit code c stands
+// for alpha (2c - L) / L with L = 2^b - 1, and 2c - L is an integer of at
+// most 5 bits, exact in f16 and bf16; so the MFMA products (activation times
+// integer) are exact, each quantizer group's partial sum is formed in
+// float32 by v_mfma_f32_16x16x32_{f16,bf16}, and then scaled by alpha / L.
+//
+// A workgroup is four waves over 64 outputs (16 each) and 16 tokens; wave w
+// owns the 16 x 16 output tile of outputs o0 + 16 w.  The reduction over the
+// input index is split into `splits` parts of kc (a multiple of the group)
+// so that a few tokens still fill the GPU; the parts go to a float32 buffer
+// [splits][T][m] and a second kernel sums them (in a fixed order).
+//
+// The index arithmetic lives here as __host__ __device__ functions so the
+// host dry run checks exactly what the GPU executes.
+#pragma once
+
+#include "brq_internal.h"
+
+namespace brq {
+
+constexpr int kQlThreads = 256;
+constexpr int kQlOut = 64;  // outputs per workgroup
+constexpr int kQlTok = 16;  // tokens per workgroup
+
+struct QlArgs {
+  const void* x;        // X~ [T][ldx], f16 or bf16 (xt)
+  int xt;
+  int64_t ldx;
+  int64_t T, m, n;
+  const uint8_t* codes; // [m][codes_ld]: row o's codes, LSB-first
+  const float* scales;  // [m][scales_ld] absmax alpha
+  int bits, group;
+  int64_t codes_ld, scales_ld;
+  int splits;
+  int64_t kc;           // input columns per split (a multiple of group)
+  float* part;          // [splits][T][m]
+};
+
+struct QlTile {
+  int64_t ct, tt, split;
+};
+__host__ __device__ inline int64_t ql_ctiles(const QlArgs& a) { return a.m / kQlOut; }
+__host__ __device__ inline int64_t ql_ttiles(const QlArgs& a) { return (a.T + kQlTok - 1) / kQlTok; }
+__host__ __device__ inline int64_t ql_blocks(const QlArgs& a) {
+  return ql_ctiles(a) * ql_ttiles(a) * a.splits;
+}
+// Output tiles run fastest: consecutive workgroups read consecutive weight rows.
+__host__ __device__ inline QlTile ql_tile(const QlArgs& a, int64_t bid) {
+  QlTile t;
+  const int64_t nc = ql_ctiles(a), nt = ql_ttiles(a);
+  t.ct = bid % nc;
+  const int64_t r = bid / nc;
+  t.tt = r % nt;
+  t.split = r / nt;
+  return t;
+}
+// Byte offset of the codes of row o, inputs k .. k + 7 (k a multiple of 8).
+__host__ __device__ inline int64_t ql_code_off(const QlArgs& a, int64_t o, int64_t k) {
+  return o * a.codes_ld + k * a.bits / 8;
+}
+
+hipError_t launch_qlinear(const QlArgs& a, hipStream_t s);
+// Z[t][o] = sum over splits of part[s][t][o], into out (type ot, leading dimension ldo).
+hipError_t launch_ql_reduce(const float* part, int splits, int64_t T, int64_t m, void* out, int ot,
+                            int64_t ldo, hipStream_t s);
+
+}  // namespace brq

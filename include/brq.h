@@ -242,6 +242,32 @@ brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* 
                        void* stream);
 
 /*
+ * The quantized linear layer at decode ([HARP] section 2: W' = M_U W M_V^T is
+ * what gets quantized; at inference the activations are rotated online,
+ * section 2.4): with W = M_U^T W' M_V, Y = X W^T is computed as
+ *   X~ = X M_V^T (brq_rotate, right side, in the activation type),
+ *   Z  = X~ W'^T with W' the absmax codes/scales of brq_rotate_quantize_pack,
+ *        dequantized in the product's prologue (integer levels 2c - L on the
+ *        MFMA units, each group's partial sum scaled by alpha / L in float32),
+ *   Y  = Z M_U (every row z becomes M_U^T z; brq_rotate_inverse, right side).
+ * left or right may be NULL (identity).
+ *   x:      device [T][ldx] activations, xt F16 or BF16 (16-byte aligned rows
+ *           when right is NULL).
+ *   codes, scales: device, as brq_rotate_quantize_pack wrote them for an
+ *           [m][n] weight (4-byte aligned); q: that call's quantizer (ABSMAX).
+ *   y:      device [T][ldy] of type yt.
+ *   ws:     device workspace of brq_qlinear_workspace_bytes(...) bytes.
+ * m must be a multiple of 64.  Asynchronous on `stream`.  Errors:
+ * INVALID_ARGUMENT (dtypes, shapes, NULLs, q not ABSMAX), UNSUPPORTED (m),
+ * ALIGNMENT, WORKSPACE, HIP. */
+size_t brq_qlinear_workspace_bytes(const brq_plan* left, const brq_plan* right, const brq_quant* q,
+                                   int64_t T, int64_t m, int64_t n);
+brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* x, int32_t xt,
+                       int64_t ldx, int64_t T, const uint8_t* codes, const void* scales,
+                       const brq_quant* q, int64_t m, int64_t n, void* y, int32_t yt, int64_t ldy,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Host helper: the 2^bits Lloyd-Max centroids for N(0,1), ascending, rounded
  * to float32 ([PolarQuant] section 2: MSE-optimal centroids for the standard
  * normal, table stored in float32).  bits in 1..5; centroids has 2^bits

@@ -392,3 +392,32 @@ def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
     for inverse in (False, True):
         _rotate(dl, p, 0, rows, chunks * side.d, 2, 2, inverse=inverse)
         assert dl.brq_dryrun_lanes_launches() == lanes
+
+
+# The quantized linear layer: rotation passes, the split product and its
+# reduction, and the output rotation.
+@pytest.mark.parametrize("T,m,n,bits,group,sides", [
+    (1, 512, 4096, 2, 64, "both"), (16, 512, 4096, 3, 128, "both"), (40, 256, 1024, 4, 64, "right"),
+    (5, 128, 2048, 5, 256, "left"), (3, 64, 512, 2, 64, "none"),
+])
+def test_qlinear_walk(dl, T, m, n, bits, group, sides):
+    left = DPlan(dl, S.random_plan(np.random.default_rng(m), (m // 16, 16), "per_group")) \
+        if sides in ("both", "left") else None
+    right = DPlan(dl, S.random_plan(np.random.default_rng(n), (n // 64, 4, 16), "per_group")) \
+        if sides in ("both", "right") else None
+    q = brq.make_quant(bits, group, 0)
+    lh, rh = (left.h if left else None), (right.h if right else None)
+    nb = dl.brq_qlinear_workspace_bytes(lh, rh, ctypes.byref(q), T, m, n)
+    assert nb > 0
+    dl.brq_dryrun_reset()
+    st = dl.brq_qlinear(lh, rh, X, 2, n, T, CODES, SCALES, ctypes.byref(q), m, n, Y, 2, m, WS, nb, None)
+    _ok(dl, st, f"qlinear T={T} {sides}")
+    assert dl.brq_dryrun_launches() >= 2  # the product and its reduction, plus the rotations
+    # too small a workspace, a codebook weight and bf32 activations are refused
+    assert dl.brq_qlinear(lh, rh, X, 2, n, T, CODES, SCALES, ctypes.byref(q), m, n, Y, 2, m, WS,
+                          nb - 1, None) == 4
+    qc = brq.make_quant(bits, group, 1, np.linspace(-2, 2, 1 << bits))
+    assert dl.brq_qlinear(lh, rh, X, 2, n, T, CODES, SCALES, ctypes.byref(qc), m, n, Y, 2, m, WS,
+                          nb, None) == 1
+    assert dl.brq_qlinear(lh, rh, X, 0, n, T, CODES, SCALES, ctypes.byref(q), m, n, Y, 2, m, WS,
+                          nb, None) == 1
