@@ -1123,10 +1123,11 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Split the input index so that a few tokens still give about 1024 workgroups.
+// Split the input index so that a few tokens still give about 2048 workgroups.
 int ql_splits(int64_t T, int64_t m, int64_t n, int group) {
-  const int64_t base = (m / kQlOut) * ((T + kQlTok - 1) / kQlTok);
-  int64_t s = (1024 + base - 1) / base;
+  const int64_t tt = kQlTok * ql_tm(T);
+  const int64_t base = (m / (kQlOut * ql_tn(ql_tm(T)))) * ((T + tt - 1) / tt);
+  int64_t s = (2048 + base - 1) / base;
   const int64_t ng = n / group;
   if (s > ng) s = ng;
   if (s > 64) s = 64;
@@ -1184,11 +1185,13 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   brq_status st = check_quant(q, n);
   if (st != BRQ_OK) return st;
   if (q->kind != BRQ_ABSMAX) return fail(BRQ_ERR_INVALID_ARGUMENT, "the weight must be absmax-quantized");
+  if (q->group != 64 && q->group != 128) return fail(BRQ_ERR_UNSUPPORTED, "weight groups of 64 or 128");
   const Plan* U = left ? &left->p : nullptr;
   const Plan* V = right ? &right->p : nullptr;
   if (U && U->d != m) return fail(BRQ_ERR_INVALID_ARGUMENT, "left plan d = %d != m", U->d);
   if (V && n % V->d) return fail(BRQ_ERR_INVALID_ARGUMENT, "right plan d = %d does not divide n", V->d);
-  if (m % kQlOut) return fail(BRQ_ERR_UNSUPPORTED, "m must be a multiple of %d", kQlOut);
+  if (m % (kQlOut * ql_tn(ql_tm(T))))
+    return fail(BRQ_ERR_UNSUPPORTED, "m must be a multiple of %d", kQlOut * ql_tn(ql_tm(T)));
   if (T == 0) return BRQ_OK;
   if (!x || !codes || !scales || !y) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
   if (reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(scales) % 4)
@@ -1229,6 +1232,7 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   a.scales_ld = n / q->group;
   a.splits = L.splits;
   a.kc = L.kc;
+  a.tm = ql_tm(T);
   a.part = reinterpret_cast<float*>(w + L.part_off);
   char name[48];
   snprintf(name, sizeof name, "qlinear b%d g%d", q->bits, q->group);

@@ -871,8 +871,10 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   ++g_launches;
-  if (a.bits < 2 || a.bits > 5 || a.group % 32 || a.group < 32 || a.n % a.group || a.m % kQlOut ||
-      a.kc % a.group || a.kc <= 0 || a.splits < 1 || (a.splits - 1) * a.kc >= a.n || a.splits * a.kc < a.n)
+  const int TN = ql_tn(a.tm);
+  if (a.bits < 2 || a.bits > 5 || (a.group != 64 && a.group != 128) || a.n % a.group || a.m % (kQlOut * TN) ||
+      a.kc % a.group || a.kc <= 0 || a.splits < 1 || (a.splits - 1) * a.kc >= a.n || a.splits * a.kc < a.n ||
+      a.tm != ql_tm(a.T))
     return violation("quantized linear geometry (splits %lld, kc %lld)", a.splits, a.kc), hipErrorInvalidValue;
   if (a.ldx < a.n || a.ldx % 8 || reinterpret_cast<uintptr_t>(a.x) % 16)
     return violation("activation rows not 16-byte vectors (ld %lld)", a.ldx, 0), hipErrorInvalidValue;
@@ -880,6 +882,7 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
     return violation("code or scale row length %lld", a.codes_ld, 0), hipErrorInvalidValue;
   const int64_t nb = ql_blocks(a);
   if (nb >= ((int64_t)1 << 31)) return violation("quantized linear grid %lld", nb, 0), hipErrorInvalidValue;
+  const int NC = a.group / 4, NB = NC * a.bits / 8;
   std::vector<uint8_t> cover((size_t)(a.splits * a.T * a.m), 0);
   for (int64_t bid = 0; bid < nb; ++bid) {
     const QlTile t = ql_tile(a, bid);
@@ -889,23 +892,33 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
     for (int w = 0; w < 4; ++w)
       for (int lane = 0; lane < 64; ++lane) {
         const int lr = lane & 15, lg = lane >> 4;
-        const int64_t o = t.ct * kQlOut + 16 * w + lr, tok = t.tt * kQlTok + lr;
-        if (o >= a.m) return violation("weight row %lld", o, 0), hipErrorInvalidValue;
+        const int64_t ob = t.ct * ((int64_t)kQlOut * TN) + (int64_t)16 * TN * w + lr;
+        for (int tn = 0; tn < TN; ++tn)
+          if (ob + 16 * tn >= a.m) return violation("weight row %lld", ob + 16 * tn, 0), hipErrorInvalidValue;
         for (int64_t g0 = kb; g0 < ke; g0 += a.group) {
           if (g0 / a.group >= a.scales_ld) return violation("scale column %lld", g0 / a.group, 0), hipErrorInvalidValue;
-          for (int64_t k = g0 + 8 * lg; k < g0 + a.group; k += 32) {
-            if (k + 8 > a.n) return violation("input columns %lld", k, 0), hipErrorInvalidValue;
-            const int64_t off = ql_code_off(a, o, k);
-            if (off < 0 || off + a.bits > a.m * a.codes_ld || (a.bits == 2 && off % 2) || (a.bits == 4 && off % 4))
-              return violation("code read at %lld", off, 0), hipErrorInvalidValue;
-            if (tok < a.T && (tok * a.ldx + k) % 8) return violation("activation vector at %lld", tok * a.ldx + k, 0), hipErrorInvalidValue;
+          // the lane's code chunks: NB bytes, 4-byte words when NB % 4 == 0, else 16-bit pieces
+          for (int tn = 0; tn < TN; ++tn) {
+            const int64_t off = ql_code_off(a, ob + 16 * tn, g0 + (int64_t)lg * NC);
+            if (off < 0 || off + NB > a.m * a.codes_ld || off % (NB % 4 == 0 ? 4 : 2))
+              return violation("code chunk at %lld", off, 0), hipErrorInvalidValue;
+          }
+          for (int st = 0; st < NC / 8; ++st) {
+            const int64_t k = g0 + (int64_t)lg * NC + 8 * st;
+            if (k + 8 > ke) return violation("input columns %lld", k, 0), hipErrorInvalidValue;
+            for (int tm = 0; tm < a.tm; ++tm) {
+              const int64_t tok = (t.tt * a.tm + tm) * kQlTok + lr;
+              if (tok < a.T && (tok * a.ldx + k) % 8) return violation("activation vector at %lld", tok * a.ldx + k, 0), hipErrorInvalidValue;
+            }
           }
         }
-        for (int i = 0; i < 4; ++i) {
-          const int64_t tk = t.tt * kQlTok + 4 * lg + i;
-          if (tk < a.T && cover[(size_t)((t.split * a.T + tk) * a.m + o)]++)
-            return violation("partial (%lld, %lld) written twice", tk, o), hipErrorInvalidValue;
-        }
+        for (int tm = 0; tm < a.tm; ++tm)
+          for (int i = 0; i < 4; ++i) {
+            const int64_t tk = (t.tt * a.tm + tm) * kQlTok + 4 * lg + i;
+            for (int tn = 0; tn < TN; ++tn)
+              if (tk < a.T && cover[(size_t)((t.split * a.T + tk) * a.m + ob + 16 * tn)]++)
+                return violation("partial (%lld, %lld) written twice", tk, ob + 16 * tn), hipErrorInvalidValue;
+          }
       }
   }
   for (size_t i = 0; i < cover.size(); ++i)

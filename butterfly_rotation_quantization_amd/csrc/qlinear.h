@@ -7,8 +7,11 @@
 // integer) are exact, each quantizer group's partial sum is formed in
 // float32 by v_mfma_f32_16x16x32_{f16,bf16}, and then scaled by alpha / L.
 //
-// A workgroup is four waves over 64 outputs (16 each) and 16 tokens; wave w
-// owns the 16 x 16 output tile of outputs o0 + 16 w.  The reduction over the
+// A workgroup is four waves over 64 tn outputs (16 tn each) and 16 tm
+// tokens: tm = 1, tn = 4 up to 16 tokens, tm = 4, tn = 2 above.  Wave w owns
+// outputs o0 + 16 tn w .. for all the tokens; it loads each activation
+// operand once for its tn output tiles and decodes each weight code once for
+// its tm token tiles.  Groups of 64 or 128 inputs.  The reduction over the
 // input index is split into `splits` parts of kc (a multiple of the group)
 // so that a few tokens still fill the GPU; the parts go to a float32 buffer
 // [splits][T][m] and a second kernel sums them (in a fixed order).
@@ -36,14 +39,19 @@ struct QlArgs {
   int64_t codes_ld, scales_ld;
   int splits;
   int64_t kc;           // input columns per split (a multiple of group)
+  int tm;               // 16-token tiles per workgroup (1 or 4)
   float* part;          // [splits][T][m]
 };
 
 struct QlTile {
   int64_t ct, tt, split;
 };
-__host__ __device__ inline int64_t ql_ctiles(const QlArgs& a) { return a.m / kQlOut; }
-__host__ __device__ inline int64_t ql_ttiles(const QlArgs& a) { return (a.T + kQlTok - 1) / kQlTok; }
+// 16-output tiles per wave for a token tile count tm.
+__host__ __device__ inline int ql_tn(int tm) { return tm == 4 ? 2 : 4; }
+__host__ __device__ inline int64_t ql_ctiles(const QlArgs& a) { return a.m / (kQlOut * ql_tn(a.tm)); }
+__host__ __device__ inline int64_t ql_ttiles(const QlArgs& a) {
+  return (a.T + kQlTok * a.tm - 1) / (kQlTok * a.tm);
+}
 __host__ __device__ inline int64_t ql_blocks(const QlArgs& a) {
   return ql_ctiles(a) * ql_ttiles(a) * a.splits;
 }
@@ -57,10 +65,12 @@ __host__ __device__ inline QlTile ql_tile(const QlArgs& a, int64_t bid) {
   t.split = r / nt;
   return t;
 }
-// Byte offset of the codes of row o, inputs k .. k + 7 (k a multiple of 8).
+// Byte offset of the codes of row o, inputs k .. (k a multiple of 16).
 __host__ __device__ inline int64_t ql_code_off(const QlArgs& a, int64_t o, int64_t k) {
   return o * a.codes_ld + k * a.bits / 8;
 }
+// 16-token tiles per workgroup for T tokens.
+__host__ __device__ inline int ql_tm(int64_t T) { return T > kQlTok ? 4 : 1; }
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t s);
 // Z[t][o] = sum over splits of part[s][t][o], into out (type ot, leading dimension ldo).

@@ -82,7 +82,7 @@ def test_qlinear_bf16_and_f32_out():
     import butterfly_rotation_quantization_amd as brq
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(3)
-    m, n, bits, group = 128, 1024, 2, 64
+    m, n, bits, group = 256, 1024, 2, 64
     codes, alpha, x = _case(rng, 9, m, n, bits, group)
     xs = S.to_storage(x, "bf16")
     Rs = S.random_plan(rng, (4, 16, 16), "per_group")
