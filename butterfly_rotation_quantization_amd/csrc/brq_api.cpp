@@ -1144,8 +1144,11 @@ QlLayout ql_layout(const Plan* U, const Plan* V, const brq_quant* q, int64_t T, 
                    int64_t n) {
   QlLayout L;
   L.splits = ql_splits(T, m, n, q->group);
-  const int64_t ng = n / q->group;
-  L.kc = ((ng + L.splits - 1) / L.splits) * q->group;
+  // the staged kernel's splits hold whole chunks
+  const int unit = n % kQlChunk == 0 ? kQlChunk : q->group;
+  const int64_t nu = n / unit;
+  if (L.splits > nu) L.splits = (int)nu;
+  L.kc = ((nu + L.splits - 1) / L.splits) * unit;
   L.splits = (int)((n + L.kc - 1) / L.kc);
   size_t at = 0;
   L.xt_off = at;
@@ -1233,6 +1236,11 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   a.splits = L.splits;
   a.kc = L.kc;
   a.tm = ql_tm(T);
+  // staged when the chunk tiles n, the rows are 16-byte aligned and the
+  // staging fits the 64 KiB a launch takes without an attribute
+  a.staged = n % kQlChunk == 0 && reinterpret_cast<uintptr_t>(codes) % 16 == 0 &&
+                     ql_lds_bytes(q->bits, q->group, a.tm) <= 64 * 1024
+                 ? 1 : 0;
   a.part = reinterpret_cast<float*>(w + L.part_off);
   char name[48];
   snprintf(name, sizeof name, "qlinear b%d g%d", q->bits, q->group);

@@ -883,6 +883,20 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   const int64_t nb = ql_blocks(a);
   if (nb >= ((int64_t)1 << 31)) return violation("quantized linear grid %lld", nb, 0), hipErrorInvalidValue;
   const int NC = a.group / 4, NB = NC * a.bits / 8;
+  if (a.staged) {  // whole chunks per split, 16-byte rows, and the LDS the launch asks for
+    if (a.n % kQlChunk || a.kc % kQlChunk || reinterpret_cast<uintptr_t>(a.codes) % 16 || a.codes_ld % 16 ||
+        ql_lds_bytes(a.bits, a.group, a.tm) > 64 * 1024)
+      return violation("staged product geometry (kc %lld, ld %lld)", a.kc, a.codes_ld), hipErrorInvalidValue;
+    const int R = ql_rows(a.tm), CB = kQlChunk * a.bits / 8, PB = ql_code_pitch(a.bits);
+    if (PB % 16 || ((int64_t)R * PB) % 16) return violation("LDS code pitch %lld", PB, 0), hipErrorInvalidValue;
+    for (int r = 0; r < R; ++r)
+      for (int gi = 0; gi < kQlChunk / a.group; ++gi)
+        for (int lg = 0; lg < 4; ++lg) {
+          const int off = r * PB + gi * (a.group * a.bits / 8) + lg * NB;
+          if (off + NB > r * PB + CB || off % (NB % 4 == 0 ? 4 : 2))
+            return violation("LDS code word at %lld (row %lld)", off, r), hipErrorInvalidValue;
+        }
+  }
   std::vector<uint8_t> cover((size_t)(a.splits * a.T * a.m), 0);
   for (int64_t bid = 0; bid < nb; ++bid) {
     const QlTile t = ql_tile(a, bid);

@@ -40,6 +40,7 @@ struct QlArgs {
   int splits;
   int64_t kc;           // input columns per split (a multiple of group)
   int tm;               // 16-token tiles per workgroup (1 or 4)
+  int staged;           // codes and scales pass through LDS in chunks of kQlChunk inputs
   float* part;          // [splits][T][m]
 };
 
@@ -68,6 +69,18 @@ __host__ __device__ inline QlTile ql_tile(const QlArgs& a, int64_t bid) {
 // Byte offset of the codes of row o, inputs k .. (k a multiple of 16).
 __host__ __device__ inline int64_t ql_code_off(const QlArgs& a, int64_t o, int64_t k) {
   return o * a.codes_ld + k * a.bits / 8;
+}
+// Staged variant: the workgroup's weight rows move through LDS kQlChunk
+// inputs at a time with whole-line loads (each row's chunk is contiguous), so
+// every code byte leaves HBM once; the lanes then read their quarter-group
+// words from LDS.  Needs n a multiple of kQlChunk and 16-byte aligned codes.
+constexpr int kQlChunk = 512;
+// LDS row pitch of the codes: the chunk's bytes plus 16 (keeps 16-byte
+// alignment and moves successive rows by four banks).
+__host__ __device__ inline int ql_code_pitch(int bits) { return kQlChunk * bits / 8 + 16; }
+__host__ __device__ inline int ql_rows(int tm) { return kQlOut * (tm == 4 ? 2 : 4); }
+__host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int tm) {
+  return (size_t)ql_rows(tm) * ql_code_pitch(bits) + (size_t)ql_rows(tm) * (kQlChunk / group + 1) * 4;
 }
 // 16-token tiles per workgroup for T tokens.
 __host__ __device__ inline int ql_tm(int64_t T) { return T > kQlTok ? 4 : 1; }

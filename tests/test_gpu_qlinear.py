@@ -78,6 +78,26 @@ def test_qlinear_small(T_, bits, group, sides):
     _check(from_dev(y), xs, dt, Uo, Vo, codes, alpha, bits, group, dt, f"T={T_} b{bits} {sides}")
 
 
+@pytest.mark.parametrize("T_", [1, 37])
+@pytest.mark.parametrize("bits,group", [(2, 64), (3, 64), (4, 128), (5, 64)])
+@pytest.mark.parametrize("n", [1024, 3584])
+def test_qlinear_staged_chunks(T_, bits, group, n):
+    """n a multiple of the 512-input chunk: the weight rows pass through LDS
+    (when the staging fits), with one or several chunks per split and fewer
+    chunks than the split target."""
+    import butterfly_rotation_quantization_amd as brq
+    rng = np.random.default_rng(T_ * 100 + bits * 10 + n)
+    m = 512
+    codes, alpha, x = _case(rng, T_, m, n, bits, group)
+    xs = S.to_storage(x, "f16")
+    Rs = S.random_plan(rng, (n // 256, 16, 16), "per_group")
+    announce(f"qlinear staged T={T_} m={m} n={n} b{bits} g{group}")
+    y = brq.qlinear(None, lib_plan(Rs), to_dev(xs, "f16"), to_dev(codes, "u8"), to_dev(alpha, "f32"),
+                    m, n, bits, group)
+    _check(from_dev(y), xs, "f16", None, orc_plan(Rs), codes, alpha, bits, group, "f16",
+           f"staged T={T_} b{bits} n={n}")
+
+
 def test_qlinear_bf16_and_f32_out():
     import butterfly_rotation_quantization_amd as brq
     torch = pytest.importorskip("torch")

@@ -399,6 +399,7 @@ def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
 @pytest.mark.parametrize("T,m,n,bits,group,sides", [
     (1, 512, 4096, 2, 64, "both"), (16, 512, 4096, 3, 128, "both"), (40, 256, 1024, 4, 64, "right"),
     (5, 256, 2048, 5, 128, "left"), (3, 256, 512, 2, 64, "none"), (70, 128, 1024, 3, 64, "none"),
+    (9, 256, 1792, 2, 64, "none"),  # n not a multiple of the staging chunk
 ])
 def test_qlinear_walk(dl, T, m, n, bits, group, sides):
     left = DPlan(dl, S.random_plan(np.random.default_rng(m), (m // 16, 16), "per_group")) \
