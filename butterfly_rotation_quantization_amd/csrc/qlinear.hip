@@ -1,6 +1,8 @@
 // Quantized linear layer kernels (qlinear.h).
 #include "qlinear.h"
 
+#include <utility>
+
 namespace brq {
 namespace {
 
@@ -27,23 +29,193 @@ __device__ __forceinline__ void ql_chunk(const uint8_t* p, uint32_t (&wds)[(NC *
   }
 }
 
-template <int BITS, int NC>
-__device__ __forceinline__ uint32_t ql_code(const uint32_t (&wds)[(NC * BITS + 31) / 32], int i) {
-  const int bit = i * BITS, wi = bit >> 5, sh = bit & 31;
-  uint32_t v = wds[wi] >> sh;
-  if (sh + BITS > 32) v |= wds[wi + 1] << (32 - sh);
-  return v & ((1u << BITS) - 1u);
+// Decoding.  A code q of b bits stands for the weight value 2q - L (L = 2^b
+// - 1) times alpha / L.  The values are small odd integers, exact in f16 and
+// bf16; they are made with bit operations and one exact multiply-add instead
+// of integer-to-float conversions:
+//  - f16: a 16-bit half whose mantissa holds q at bit o (o >= 1, o + b <= 10)
+//    under the exponent of 1024 is the number 1024 + q 2^o; times 2^(1-o)
+//    minus (2^(11-o) + L) it is 2q - L, and every step is exact.  Two codes
+//    go into the halves of one word and one packed multiply-add finishes both.
+//  - bf16: the same in float32 (exponent of 2^23, mantissa field at bit o,
+//    1 <= o, o + b <= 23), then the upper halves of two floats are the bf16
+//    values (small integers need at most 6 significant bits).
+// The lane's codes of a group are a bit stream in words w[q] (stream bits
+// [32q, 32q + 32)); sh[q] holds stream bits [32q + 16, 32q + 48).
+
+// A two-byte window of the stream: register index (w: 0..NW-1, sh: NW..)
+// and the byte offset of the window inside it.
+struct QlWin {
+  int reg, off;
+};
+template <int NW>
+__host__ __device__ constexpr QlWin ql_win(int beta) {
+  return beta % 4 <= 2 ? QlWin{beta / 4, beta % 4} : QlWin{NW + beta / 4, 1};
+}
+
+template <int NW>
+__device__ __forceinline__ void ql_shifted(const uint32_t (&w)[NW], uint32_t (&sh)[NW]) {
+#pragma unroll
+  for (int q = 0; q < NW; ++q) sh[q] = __builtin_amdgcn_alignbit(q + 1 < NW ? w[q + 1] : 0u, w[q], 16);
+}
+
+template <int NW>
+__device__ __forceinline__ uint32_t ql_reg(const uint32_t (&w)[NW], const uint32_t (&sh)[NW], int r) {
+  return r < NW ? w[r] : sh[r - NW];
+}
+
+// f16 pair P of a lane's group: codes P (low half) and P + NC/2 (high half).
+// The two codes sit NC b / 2 bits apart, a whole number of bytes, so they
+// have the same bit offset in their windows and one byte permute brings both
+// windows into one word.
+template <int BITS, int NC, int P>
+__device__ __forceinline__ uint32_t ql_f16_pair(const uint32_t (&w)[(NC * BITS + 31) / 32],
+                                                const uint32_t (&sh)[(NC * BITS + 31) / 32]) {
+  constexpr int NW = (NC * BITS + 31) / 32, L = (1 << BITS) - 1;
+  constexpr int a = P * BITS;
+  constexpr int beta = a >= 1 ? (a - 1) / 8 : 0;  // the field starts at bit 1..8 of the window
+  constexpr int o = a - 8 * beta;
+  constexpr int betab = beta + (NC / 2) * BITS / 8;
+  constexpr QlWin wa = ql_win<NW>(beta), wb = ql_win<NW>(betab);
+  const uint32_t ra = ql_reg(w, sh, wa.reg), rb = ql_reg(w, sh, wb.reg);
+  uint32_t d;
+  if constexpr (wa.reg == wb.reg && wa.off == 0 && wb.off == 2) {
+    d = ra;
+  } else {
+    constexpr uint32_t sel = (uint32_t)wa.off | (uint32_t)(wa.off + 1) << 8 | (uint32_t)(4 + wb.off) << 16 |
+                             (uint32_t)(5 + wb.off) << 24;
+    d = __builtin_amdgcn_perm(rb, ra, sel);
+  }
+  // field to bit o2 in [1, 10 - b]: a right shift moves high-half bits into
+  // the top of the low half only (above the field); a left shift by one moves
+  // the low half's top bit below the high field
+  constexpr int o2 = o == 0 ? 1 : (o + BITS > 10 ? 10 - BITS : o);
+  if constexpr (o2 > o) d <<= (o2 - o);
+  else if constexpr (o2 < o) d >>= (o - o2);
+  constexpr uint32_t m = ((1u << BITS) - 1u) << o2;
+  const uint32_t v = (d & (m | m << 16)) | 0x64006400u;
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  constexpr _Float16 c = (_Float16)(2.0f / (float)(1 << o2));
+  constexpr _Float16 k = (_Float16)(-(float)((1 << (11 - o2)) + L));
+  const h2v r = __builtin_bit_cast(h2v, v) * h2v{c, c} + h2v{k, k};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// float32 value 2q - L of code J (its field found in w, sh or w[0] << 8).
+template <int BITS, int NC, int J>
+__device__ __forceinline__ float ql_f32_code(const uint32_t (&w)[(NC * BITS + 31) / 32],
+                                             const uint32_t (&sh)[(NC * BITS + 31) / 32], uint32_t w0s) {
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int a = J * BITS;
+  constexpr int ow = a % 32, os = (a - 16) % 32;
+  constexpr bool in_w = ow >= 1 && ow + BITS <= 23;
+  constexpr bool in_s = a >= 16 && os >= 1 && os + BITS <= 23;
+  constexpr int o = in_w ? ow : (in_s ? os : a + 8);
+  static_assert(in_w || in_s || a + 8 + BITS <= 23, "no window for the code");
+  uint32_t src;
+  if constexpr (in_w) src = w[a / 32];
+  else if constexpr (in_s) src = sh[(a - 16) / 32];
+  else src = w0s;
+  constexpr uint32_t m = ((1u << BITS) - 1u) << o;
+  const float v = __uint_as_float((src & m) | 0x4B000000u);
+  return fmaf(v, 2.0f / (float)(1 << o), -(float)((1 << (24 - o)) + L));
+}
+
+template <int BITS, int NC, int... P>
+__device__ __forceinline__ void ql_f16_pairs(const uint32_t (&w)[(NC * BITS + 31) / 32], uint32_t* out,
+                                             std::integer_sequence<int, P...>) {
+  uint32_t sh[(NC * BITS + 31) / 32];
+  ql_shifted(w, sh);
+  ((out[P] = ql_f16_pair<BITS, NC, P>(w, sh)), ...);
+}
+
+template <int BITS, int NC, int... P>
+__device__ __forceinline__ void ql_bf16_pairs(const uint32_t (&w)[(NC * BITS + 31) / 32], uint32_t* out,
+                                              std::integer_sequence<int, P...>) {
+  uint32_t sh[(NC * BITS + 31) / 32];
+  ql_shifted(w, sh);
+  const uint32_t w0s = w[0] << 8;
+  ((out[P] = __builtin_amdgcn_perm(__float_as_uint(ql_f32_code<BITS, NC, 2 * P + 1>(w, sh, w0s)),
+                                   __float_as_uint(ql_f32_code<BITS, NC, 2 * P>(w, sh, w0s)), 0x07060302u)),
+   ...);
+}
+
+// The products of one group: d[tm][tn] = sum over the group's inputs of the
+// activations times the weight values 2q - L.  Lane group lg holds the
+// inputs g0 + lg NC + [0, NC) (NC = G/4).  The order of the contraction
+// inside a group is free as long as A and B follow the same one:
+//  - f16: MFMA step s takes the pairs 4s + [0, 4) (pair p: inputs p and
+//    p + NC/2), so the activations are interleaved in registers to match;
+//  - bf16: step s takes inputs 8s .. 8s + 7 in order.
+template <int BITS, bool BF, int G, int TM, int TN>
+__device__ __forceinline__ void ql_group(f4v (&d)[TM][TN], const uint32_t (&wds)[TN][(G / 4 * BITS + 31) / 32],
+                                         const uint16_t* const (&xrow)[TM], const bool (&tok_ok)[TM], int64_t g0) {
+  constexpr int NC = G / 4;
+  using V8 = typename std::conditional<BF, b8v, h8v>::type;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) d[tm][tn] = f4v{0.f, 0.f, 0.f, 0.f};
+  uint32_t pr[TN][NC / 2];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    if constexpr (BF) ql_bf16_pairs<BITS, NC>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
+    else ql_f16_pairs<BITS, NC>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
+  }
+#pragma unroll
+  for (int sp = 0; sp < NC / 16; ++sp) {  // two MFMA steps per activation load
+    uint4 xa[TM], xb[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      if constexpr (BF) {  // inputs 16 sp .. 16 sp + 15
+        xa[tm] = tok_ok[tm] ? *reinterpret_cast<const uint4*>(xrow[tm] + g0 + 16 * sp) : make_uint4(0u, 0u, 0u, 0u);
+        xb[tm] = tok_ok[tm] ? *reinterpret_cast<const uint4*>(xrow[tm] + g0 + 16 * sp + 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+      } else {  // inputs 8 sp + [0, 8) and the same plus NC/2
+        xa[tm] = tok_ok[tm] ? *reinterpret_cast<const uint4*>(xrow[tm] + g0 + 8 * sp) : make_uint4(0u, 0u, 0u, 0u);
+        xb[tm] = tok_ok[tm] ? *reinterpret_cast<const uint4*>(xrow[tm] + g0 + 8 * sp + NC / 2)
+                            : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      V8 av[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        uint4 r;
+        if constexpr (BF) {
+          r = s2 == 0 ? xa[tm] : xb[tm];
+        } else {  // pair p = 8 sp + 4 s2 + j: (x[p], x[p + NC/2]) from word 2 s2 + j/2, half j % 2
+          const uint32_t a0 = s2 == 0 ? xa[tm].x : xa[tm].z, a1 = s2 == 0 ? xa[tm].y : xa[tm].w;
+          const uint32_t b0 = s2 == 0 ? xb[tm].x : xb[tm].z, b1 = s2 == 0 ? xb[tm].y : xb[tm].w;
+          r.x = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+          r.y = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+          r.z = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+          r.w = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+        }
+        av[tm] = __builtin_bit_cast(V8, r);
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int p0 = 8 * sp + 4 * s2;  // f16: pairs p0 .. p0 + 3; bf16: code pairs of inputs 2 p0 ..
+        const uint4 braw = make_uint4(pr[tn][p0], pr[tn][p0 + 1], pr[tn][p0 + 2], pr[tn][p0 + 3]);
+        const V8 bv = __builtin_bit_cast(V8, braw);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          if constexpr (BF) d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tm], bv, d[tm][tn], 0, 0, 0);
+          else d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[tm], bv, d[tm][tn], 0, 0, 0);
+        }
+      }
+    }
+  }
 }
 
 // G: group size (64 or 128); TM: 16-token tiles per workgroup; TN: 16-output
-// tiles per wave.  Within a group, lane group lg takes the G/4 consecutive
-// inputs g0 + lg G/4 + [0, G/4) and MFMA step s uses its inputs 8 s .. 8 s + 7
-// (the contraction order inside the group is free, A and B follow the same
-// one).  Each step loads the TM activation operands once for the TN output
-// tiles and decodes each weight operand once for the TM token tiles.
+// tiles per wave.  Each group loads the TM activation operands once for the
+// TN output tiles and decodes each weight operand once for the TM token tiles
+// (ql_group).
 template <int BITS, bool BF, int G, int TM, int TN>
 __global__ __launch_bounds__(kQlThreads) void qlinear_kernel(QlArgs a) {
-  using V8 = typename std::conditional<BF, b8v, h8v>::type;
   constexpr int L = (1 << BITS) - 1;
   constexpr int NC = G / 4;
   constexpr int NW = (NC * BITS + 31) / 32;
@@ -84,35 +256,7 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_kernel(QlArgs a) {
       sc[tn] = srow[tn][g0 / G] * invL;
     }
     f4v d[TM][TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) d[tm][tn] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < NC / 8; ++st) {
-      V8 av[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const uint4 raw = tok_ok[tm] ? *reinterpret_cast<const uint4*>(xrow[tm] + g0 + 8 * st)
-                                     : make_uint4(0u, 0u, 0u, 0u);
-        av[tm] = __builtin_bit_cast(V8, raw);
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        V8 bv;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int q = 2 * (int)ql_code<BITS, NC>(wds[tn], 8 * st + i) - L;
-          if constexpr (BF) bv[i] = (__bf16)(float)q;
-          else bv[i] = (_Float16)q;
-        }
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          if constexpr (BF) d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tm], bv, d[tm][tn], 0, 0, 0);
-          else d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[tm], bv, d[tm][tn], 0, 0, 0);
-        }
-      }
-    }
+    ql_group<BITS, BF, G, TM, TN>(d, wds, xrow, tok_ok, g0);
     // D reg i: token 4 lg + i of the tile, output lr: scale alpha(o, group) / L
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -136,7 +280,6 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_kernel(QlArgs a) {
 // The same product with the weight rows staged through LDS (qlinear.h).
 template <int BITS, bool BF, int G, int TM, int TN>
 __global__ __launch_bounds__(kQlThreads) void qlinear_staged_kernel(QlArgs a) {
-  using V8 = typename std::conditional<BF, b8v, h8v>::type;
   constexpr int L = (1 << BITS) - 1;
   constexpr int NC = G / 4;
   constexpr int NW = (NC * BITS + 31) / 32;
@@ -204,35 +347,7 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_staged_kernel(QlArgs a) {
         sc[tn] = lscales[(lrow0 + 16 * tn) * PS + gi];
       }
       f4v d[TM][TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) d[tm][tn] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < NC / 8; ++st) {
-        V8 av[TM];
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const uint4 raw = tok_ok[tm] ? *reinterpret_cast<const uint4*>(xrow[tm] + g0 + 8 * st)
-                                       : make_uint4(0u, 0u, 0u, 0u);
-          av[tm] = __builtin_bit_cast(V8, raw);
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          V8 bv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int q = 2 * (int)ql_code<BITS, NC>(wds[tn], 8 * st + i) - L;
-            if constexpr (BF) bv[i] = (__bf16)(float)q;
-            else bv[i] = (_Float16)q;
-          }
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            if constexpr (BF) d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tm], bv, d[tm][tn], 0, 0, 0);
-            else d[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[tm], bv, d[tm][tn], 0, 0, 0);
-          }
-        }
-      }
+      ql_group<BITS, BF, G, TM, TN>(d, wds, xrow, tok_ok, g0);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
