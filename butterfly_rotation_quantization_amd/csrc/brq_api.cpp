@@ -1123,10 +1123,14 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Split the input index so that a few tokens still give about 2048 workgroups.
-int ql_splits(int64_t T, int64_t m, int64_t n, int group) {
+// Split the input index so that a few tokens still fill the GPU: about 2048
+// workgroups (measured on the 70B down projection: more, shorter workgroups
+// beat fewer with longer load pipelines).  The split count does not depend
+// on the pointers, so the workspace size is known before the call.
+int ql_splits(int64_t T, int64_t m, int64_t n, int bits, int group) {
   const int64_t tt = kQlTok * ql_tm(T);
-  const int64_t base = (m / (kQlOut * ql_tn(ql_tm(T)))) * ((T + tt - 1) / tt);
+  const int kind = ql_kind(T, n, bits, group, true);
+  const int64_t base = (m / (kQlOut * ql_kind_tn(kind, ql_tm(T)))) * ((T + tt - 1) / tt);
   int64_t s = (2048 + base - 1) / base;
   const int64_t ng = n / group;
   if (s > ng) s = ng;
@@ -1143,7 +1147,7 @@ struct QlLayout {
 QlLayout ql_layout(const Plan* U, const Plan* V, const brq_quant* q, int64_t T, int64_t m,
                    int64_t n) {
   QlLayout L;
-  L.splits = ql_splits(T, m, n, q->group);
+  L.splits = ql_splits(T, m, n, q->bits, q->group);
   // the staged kernel's splits hold whole chunks
   const int unit = n % kQlChunk == 0 ? kQlChunk : q->group;
   const int64_t nu = n / unit;
@@ -1236,11 +1240,9 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   a.splits = L.splits;
   a.kc = L.kc;
   a.tm = ql_tm(T);
-  // staged when the chunk tiles n, the rows are 16-byte aligned and the
-  // staging fits the 64 KiB a launch takes without an attribute
-  a.staged = n % kQlChunk == 0 && reinterpret_cast<uintptr_t>(codes) % 16 == 0 &&
-                     ql_lds_bytes(q->bits, q->group, a.tm) <= 64 * 1024
-                 ? 1 : 0;
+  a.kind = ql_kind(T, n, q->bits, q->group, reinterpret_cast<uintptr_t>(codes) % 16 == 0);
+  a.tn = ql_kind_tn(a.kind, a.tm);
+  a.tv = (int)(T < kQlTok ? T : kQlTok);
   a.part = reinterpret_cast<float*>(w + L.part_off);
   char name[48];
   snprintf(name, sizeof name, "qlinear b%d g%d", q->bits, q->group);

@@ -871,7 +871,10 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   ++g_launches;
-  const int TN = ql_tn(a.tm);
+  const int TN = a.tn;
+  if (a.kind != ql_kind(a.T, a.n, a.bits, a.group, reinterpret_cast<uintptr_t>(a.codes) % 16 == 0) ||
+      TN != ql_kind_tn(a.kind, a.tm) || a.tv != (int)std::min<int64_t>(a.T, kQlTok))
+    return violation("quantized linear kernel choice (kind %lld, tn %lld)", a.kind, TN), hipErrorInvalidValue;
   if (a.bits < 2 || a.bits > 5 || (a.group != 64 && a.group != 128) || a.n % a.group || a.m % (kQlOut * TN) ||
       a.kc % a.group || a.kc <= 0 || a.splits < 1 || (a.splits - 1) * a.kc >= a.n || a.splits * a.kc < a.n ||
       a.tm != ql_tm(a.T))
@@ -883,11 +886,29 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   const int64_t nb = ql_blocks(a);
   if (nb >= ((int64_t)1 << 31)) return violation("quantized linear grid %lld", nb, 0), hipErrorInvalidValue;
   const int NC = a.group / 4, NB = NC * a.bits / 8;
-  if (a.staged) {  // whole chunks per split, 16-byte rows, and the LDS the launch asks for
+  if (a.kind != kQlDirect) {  // whole chunks per split, 16-byte rows, and the LDS the launch asks for
+    const int R = kQlOut * TN, CB = kQlChunk * a.bits / 8, PB = ql_code_pitch(a.bits);
+    const int tv = a.kind == kQlStream ? a.tv : 0;
     if (a.n % kQlChunk || a.kc % kQlChunk || reinterpret_cast<uintptr_t>(a.codes) % 16 || a.codes_ld % 16 ||
-        ql_lds_bytes(a.bits, a.group, a.tm) > 64 * 1024)
+        ql_lds_bytes(a.bits, a.group, R, tv) > 64 * 1024 || (a.kind == kQlStream && (a.tm != 1 || a.T > kQlTok)))
       return violation("staged product geometry (kc %lld, ld %lld)", a.kc, a.codes_ld), hipErrorInvalidValue;
-    const int R = ql_rows(a.tm), CB = kQlChunk * a.bits / 8, PB = ql_code_pitch(a.bits);
+    if (a.kind == kQlStream) {
+      // staged pieces per thread divide exactly; activation reads stay inside a token's chunk row
+      const int NG = kQlChunk / a.group;
+      if ((R * (CB / 16)) % kQlThreads || (R * NG) % kQlThreads || (kQlTok * (kQlChunk / 8)) % kQlThreads)
+        return violation("stream staging pieces (rows %lld)", R, 0), hipErrorInvalidValue;
+      const bool bf = a.xt == BRQ_BF16;
+      for (int gi = 0; gi < NG; ++gi)
+        for (int lg = 0; lg < 4; ++lg)
+          for (int sp = 0; sp < NC / 16; ++sp) {
+            const int64_t lo = gi * a.group + lg * NC + (bf ? 16 * sp : 8 * sp);
+            const int64_t hi = lo + (bf ? 8 : NC / 2) + 8;
+            if (lo < 0 || 2 * hi > 2 * kQlChunk || (2 * lo) % 16)
+              return violation("LDS activation read at %lld (group %lld)", 2 * lo, gi), hipErrorInvalidValue;
+          }
+      if ((int64_t)tv * kQlXPitch % 16 || kQlXPitch < 2 * kQlChunk)
+        return violation("LDS activation pitch %lld", kQlXPitch, 0), hipErrorInvalidValue;
+    }
     if (PB % 16 || ((int64_t)R * PB) % 16) return violation("LDS code pitch %lld", PB, 0), hipErrorInvalidValue;
     for (int r = 0; r < R; ++r)
       for (int gi = 0; gi < kQlChunk / a.group; ++gi)

@@ -40,16 +40,30 @@ struct QlArgs {
   int splits;
   int64_t kc;           // input columns per split (a multiple of group)
   int tm;               // 16-token tiles per workgroup (1 or 4)
-  int staged;           // codes and scales pass through LDS in chunks of kQlChunk inputs
+  int tn;               // 16-output tiles per wave
+  int kind;             // QlKind
+  int tv;               // kQlStream: tokens of a tile staged in LDS (min(T, 16))
   float* part;          // [splits][T][m]
 };
+
+// kQlDirect: every lane reads its codes and activations from global memory.
+// kQlStaged: the workgroup's weight rows pass through LDS one chunk of
+//   kQlChunk inputs at a time, with whole-line loads (each row's chunk is
+//   contiguous), so every code byte leaves HBM once.
+// kQlStream (up to 16 tokens): as staged, and the tile's activations go
+//   through LDS too; the next chunk's codes, scales and activations are
+//   loaded into registers while the current chunk is multiplied, so the
+//   loads stay in flight during the arithmetic (no global load is waited
+//   for inside it).
+enum QlKind { kQlDirect = 0, kQlStaged = 1, kQlStream = 2 };
+constexpr int kQlStreamTn = 2;
 
 struct QlTile {
   int64_t ct, tt, split;
 };
 // 16-output tiles per wave for a token tile count tm.
 __host__ __device__ inline int ql_tn(int tm) { return tm == 4 ? 2 : 4; }
-__host__ __device__ inline int64_t ql_ctiles(const QlArgs& a) { return a.m / (kQlOut * ql_tn(a.tm)); }
+__host__ __device__ inline int64_t ql_ctiles(const QlArgs& a) { return a.m / (kQlOut * a.tn); }
 __host__ __device__ inline int64_t ql_ttiles(const QlArgs& a) {
   return (a.T + kQlTok * a.tm - 1) / (kQlTok * a.tm);
 }
@@ -70,20 +84,31 @@ __host__ __device__ inline QlTile ql_tile(const QlArgs& a, int64_t bid) {
 __host__ __device__ inline int64_t ql_code_off(const QlArgs& a, int64_t o, int64_t k) {
   return o * a.codes_ld + k * a.bits / 8;
 }
-// Staged variant: the workgroup's weight rows move through LDS kQlChunk
-// inputs at a time with whole-line loads (each row's chunk is contiguous), so
-// every code byte leaves HBM once; the lanes then read their quarter-group
-// words from LDS.  Needs n a multiple of kQlChunk and 16-byte aligned codes.
+// The staged kinds need n a multiple of kQlChunk and 16-byte aligned codes.
 constexpr int kQlChunk = 512;
-// LDS row pitch of the codes: the chunk's bytes plus 16 (keeps 16-byte
-// alignment and moves successive rows by four banks).
+// LDS row pitches: the chunk's code bytes plus 16 (keeps 16-byte alignment
+// and moves successive rows by four banks); a token's activations plus 16.
 __host__ __device__ inline int ql_code_pitch(int bits) { return kQlChunk * bits / 8 + 16; }
-__host__ __device__ inline int ql_rows(int tm) { return kQlOut * (tm == 4 ? 2 : 4); }
-__host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int tm) {
-  return (size_t)ql_rows(tm) * ql_code_pitch(bits) + (size_t)ql_rows(tm) * (kQlChunk / group + 1) * 4;
+constexpr int kQlXPitch = 2 * kQlChunk + 16;
+// LDS of a staged launch: rows x (codes + scales of the chunk's groups), and
+// tv activation rows.
+__host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int rows, int tv) {
+  return (size_t)rows * ql_code_pitch(bits) + (size_t)rows * (kQlChunk / group + 1) * 4 +
+         (size_t)tv * kQlXPitch;
 }
 // 16-token tiles per workgroup for T tokens.
 __host__ __device__ inline int ql_tm(int64_t T) { return T > kQlTok ? 4 : 1; }
+// The kernel for a shape (codes_aligned: 16-byte aligned codes), staying
+// within the 64 KiB of LDS a launch takes without an attribute.
+__host__ __device__ inline int ql_kind(int64_t T, int64_t n, int bits, int group, bool codes_aligned) {
+  if (n % kQlChunk || !codes_aligned) return kQlDirect;
+  const int tm = ql_tm(T);
+  if (tm == 1 && ql_lds_bytes(bits, group, kQlOut * kQlStreamTn, (int)(T < kQlTok ? T : kQlTok)) <= 64 * 1024)
+    return kQlStream;
+  if (ql_lds_bytes(bits, group, kQlOut * ql_tn(tm), 0) <= 64 * 1024) return kQlStaged;
+  return kQlDirect;
+}
+__host__ __device__ inline int ql_kind_tn(int kind, int tm) { return kind == kQlStream ? kQlStreamTn : ql_tn(tm); }
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t s);
 // Z[t][o] = sum over splits of part[s][t][o], into out (type ot, leading dimension ldo).

@@ -9,6 +9,7 @@ namespace {
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 // The codes of one lane for one group: g/4 consecutive codes of its weight
 // row (inputs g0 + lg g/4 ...), gathered into 32-bit words (at most 5: 32
@@ -53,6 +54,14 @@ __host__ __device__ constexpr QlWin ql_win(int beta) {
   return beta % 4 <= 2 ? QlWin{beta / 4, beta % 4} : QlWin{NW + beta / 4, 1};
 }
 
+// (a & m) | c in one instruction (the compiler emits an and and an or when
+// both constants are literals).
+__device__ __forceinline__ uint32_t ql_and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
 template <int NW>
 __device__ __forceinline__ void ql_shifted(const uint32_t (&w)[NW], uint32_t (&sh)[NW]) {
 #pragma unroll
@@ -68,7 +77,7 @@ __device__ __forceinline__ uint32_t ql_reg(const uint32_t (&w)[NW], const uint32
 // The two codes sit NC b / 2 bits apart, a whole number of bytes, so they
 // have the same bit offset in their windows and one byte permute brings both
 // windows into one word.
-template <int BITS, int NC, int P>
+template <int BITS, int NC, int P, bool FUSE>
 __device__ __forceinline__ uint32_t ql_f16_pair(const uint32_t (&w)[(NC * BITS + 31) / 32],
                                                 const uint32_t (&sh)[(NC * BITS + 31) / 32]) {
   constexpr int NW = (NC * BITS + 31) / 32, L = (1 << BITS) - 1;
@@ -93,7 +102,7 @@ __device__ __forceinline__ uint32_t ql_f16_pair(const uint32_t (&w)[(NC * BITS +
   if constexpr (o2 > o) d <<= (o2 - o);
   else if constexpr (o2 < o) d >>= (o - o2);
   constexpr uint32_t m = ((1u << BITS) - 1u) << o2;
-  const uint32_t v = (d & (m | m << 16)) | 0x64006400u;
+  const uint32_t v = FUSE ? ql_and_or(d, m | m << 16, 0x64006400u) : (d & (m | m << 16)) | 0x64006400u;
   typedef _Float16 h2v __attribute__((ext_vector_type(2)));
   constexpr _Float16 c = (_Float16)(2.0f / (float)(1 << o2));
   constexpr _Float16 k = (_Float16)(-(float)((1 << (11 - o2)) + L));
@@ -102,7 +111,7 @@ __device__ __forceinline__ uint32_t ql_f16_pair(const uint32_t (&w)[(NC * BITS +
 }
 
 // float32 value 2q - L of code J (its field found in w, sh or w[0] << 8).
-template <int BITS, int NC, int J>
+template <int BITS, int NC, int J, bool FUSE>
 __device__ __forceinline__ float ql_f32_code(const uint32_t (&w)[(NC * BITS + 31) / 32],
                                              const uint32_t (&sh)[(NC * BITS + 31) / 32], uint32_t w0s) {
   constexpr int L = (1 << BITS) - 1;
@@ -117,26 +126,26 @@ __device__ __forceinline__ float ql_f32_code(const uint32_t (&w)[(NC * BITS + 31
   else if constexpr (in_s) src = sh[(a - 16) / 32];
   else src = w0s;
   constexpr uint32_t m = ((1u << BITS) - 1u) << o;
-  const float v = __uint_as_float((src & m) | 0x4B000000u);
+  const float v = __uint_as_float(FUSE ? ql_and_or(src, m, 0x4B000000u) : (src & m) | 0x4B000000u);
   return fmaf(v, 2.0f / (float)(1 << o), -(float)((1 << (24 - o)) + L));
 }
 
-template <int BITS, int NC, int... P>
+template <int BITS, int NC, bool FUSE, int... P>
 __device__ __forceinline__ void ql_f16_pairs(const uint32_t (&w)[(NC * BITS + 31) / 32], uint32_t* out,
                                              std::integer_sequence<int, P...>) {
   uint32_t sh[(NC * BITS + 31) / 32];
   ql_shifted(w, sh);
-  ((out[P] = ql_f16_pair<BITS, NC, P>(w, sh)), ...);
+  ((out[P] = ql_f16_pair<BITS, NC, P, FUSE>(w, sh)), ...);
 }
 
-template <int BITS, int NC, int... P>
+template <int BITS, int NC, bool FUSE, int... P>
 __device__ __forceinline__ void ql_bf16_pairs(const uint32_t (&w)[(NC * BITS + 31) / 32], uint32_t* out,
                                               std::integer_sequence<int, P...>) {
   uint32_t sh[(NC * BITS + 31) / 32];
   ql_shifted(w, sh);
   const uint32_t w0s = w[0] << 8;
-  ((out[P] = __builtin_amdgcn_perm(__float_as_uint(ql_f32_code<BITS, NC, 2 * P + 1>(w, sh, w0s)),
-                                   __float_as_uint(ql_f32_code<BITS, NC, 2 * P>(w, sh, w0s)), 0x07060302u)),
+  ((out[P] = __builtin_amdgcn_perm(__float_as_uint(ql_f32_code<BITS, NC, 2 * P + 1, FUSE>(w, sh, w0s)),
+                                   __float_as_uint(ql_f32_code<BITS, NC, 2 * P, FUSE>(w, sh, w0s)), 0x07060302u)),
    ...);
 }
 
@@ -159,8 +168,10 @@ __device__ __forceinline__ void ql_group(f4v (&d)[TM][TN], const uint32_t (&wds)
   uint32_t pr[TN][NC / 2];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    if constexpr (BF) ql_bf16_pairs<BITS, NC>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
-    else ql_f16_pairs<BITS, NC>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
+    // the fused and-or helps the one-token-tile kernels and costs the
+    // four-tile ones registers
+    if constexpr (BF) ql_bf16_pairs<BITS, NC, TM == 1>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
+    else ql_f16_pairs<BITS, NC, TM == 1>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
   }
 #pragma unroll
   for (int sp = 0; sp < NC / 16; ++sp) {  // two MFMA steps per activation load
@@ -368,6 +379,160 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_staged_kernel(QlArgs a) {
     }
 }
 
+// Staging of one chunk for the streaming kernel: R weight rows x kQlChunk
+// inputs of codes (16-byte pieces, consecutive threads along a row), their
+// scales, and the tile's tv token rows of activations.
+struct QlStage {
+  const uint8_t* codes;  // the workgroup's first row
+  int64_t codes_ld;
+  const float* scales;
+  int64_t scales_ld;
+  const uint16_t* x;     // the tile's first token
+  int64_t ldx;
+  int tv;
+};
+template <int BITS, int G, int R>
+struct QlPieces {
+  static constexpr int CB = kQlChunk * BITS / 8, NG = kQlChunk / G, XQ = kQlChunk / 8;
+  static constexpr int NCP = R * (CB / 16) / kQlThreads, NSP = R * NG / kQlThreads, NXP = kQlTok * XQ / kQlThreads;
+};
+
+template <int BITS, int G, int R>
+__device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pcod)[QlPieces<BITS, G, R>::NCP],
+                                         float (&psc)[QlPieces<BITS, G, R>::NSP],
+                                         u4v (&px)[QlPieces<BITS, G, R>::NXP]) {
+  using P = QlPieces<BITS, G, R>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < P::NCP; ++i) {
+    const int e = tid + i * kQlThreads, r = e / (P::CB / 16), q = e - r * (P::CB / 16);
+    pcod[i] = *reinterpret_cast<const u4v*>(st.codes + r * st.codes_ld + k0 * BITS / 8 + 16 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < P::NSP; ++i) {
+    const int e = tid + i * kQlThreads, r = e / P::NG, gq = e - r * P::NG;
+    psc[i] = st.scales[r * st.scales_ld + k0 / G + gq];
+  }
+#pragma unroll
+  for (int i = 0; i < P::NXP; ++i) {
+    const int e = tid + i * kQlThreads, tk = e / P::XQ, q = e - tk * P::XQ;
+    px[i] = tk < st.tv ? *reinterpret_cast<const u4v*>(st.x + tk * st.ldx + k0 + 8 * q) : u4v{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int BITS, int G, int R>
+__device__ __forceinline__ void ql_stash(int tv, float invL, uint8_t* lcodes, float* lscales, uint8_t* lx,
+                                         const u4v (&pcod)[QlPieces<BITS, G, R>::NCP],
+                                         const float (&psc)[QlPieces<BITS, G, R>::NSP],
+                                         const u4v (&px)[QlPieces<BITS, G, R>::NXP]) {
+  using P = QlPieces<BITS, G, R>;
+  constexpr int PB = P::CB + 16, PS = P::NG + 1;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < P::NCP; ++i) {
+    const int e = tid + i * kQlThreads, r = e / (P::CB / 16), q = e - r * (P::CB / 16);
+    *reinterpret_cast<u4v*>(lcodes + r * PB + 16 * q) = pcod[i];
+  }
+#pragma unroll
+  for (int i = 0; i < P::NSP; ++i) {
+    const int e = tid + i * kQlThreads, r = e / P::NG, gq = e - r * P::NG;
+    lscales[r * PS + gq] = psc[i] * invL;
+  }
+#pragma unroll
+  for (int i = 0; i < P::NXP; ++i) {
+    const int e = tid + i * kQlThreads, tk = e / P::XQ, q = e - tk * P::XQ;
+    if (tk < tv) *reinterpret_cast<u4v*>(lx + tk * kQlXPitch + 16 * q) = px[i];
+  }
+}
+
+// Up to 16 tokens with the loads of the next chunk in flight (kQlStream).
+template <int BITS, bool BF, int G, int TN, bool ONE>
+__global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int NC = G / 4;
+  constexpr int NW = (NC * BITS + 31) / 32;
+  constexpr int R = kQlOut * TN;            // weight rows of the workgroup
+  constexpr int CB = kQlChunk * BITS / 8;   // code bytes of a row per chunk
+  constexpr int PB = CB + 16;               // LDS pitch
+  constexpr int NG = kQlChunk / G;          // groups per chunk
+  constexpr int PS = NG + 1;                // scale pitch (floats)
+  constexpr int XQ = kQlChunk / 8;          // 16-byte pieces of a token's chunk
+  // pieces per thread: codes, scales, activations (the divisions are exact)
+  constexpr int NCP = R * (CB / 16) / kQlThreads;
+  constexpr int NSP = R * NG / kQlThreads;
+  constexpr int NXP = kQlTok * XQ / kQlThreads;
+  static_assert(NCP * kQlThreads == R * (CB / 16) && NSP * kQlThreads == R * NG && NXP * kQlThreads == kQlTok * XQ,
+                "staging pieces must divide among the threads");
+  extern __shared__ __align__(16) uint8_t ql_lds[];
+  uint8_t* lcodes = ql_lds;
+  float* lscales = reinterpret_cast<float*>(ql_lds + R * PB);
+  uint8_t* lx = ql_lds + R * PB + R * PS * 4;
+  const QlTile t = ql_tile(a, blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t row0 = t.ct * (int64_t)R;
+  const int lrow0 = 16 * TN * w + lr;  // + 16 tn: this lane's rows within the workgroup
+  const int64_t tok0 = t.tt * (int64_t)kQlTok;
+  const int tv = ONE ? 1 : a.tv;      // tokens tok0 .. tok0 + tv - 1 exist (tv = min(T - tok0, 16))
+  const int64_t k_beg = t.split * a.kc;
+  const int64_t k_end = k_beg + a.kc < a.n ? k_beg + a.kc : a.n;
+  const uint16_t* const xrow[1] = {reinterpret_cast<const uint16_t*>(lx + lr * kQlXPitch) + lg * NC};
+  const bool tok_ok[1] = {lr < tv};
+  const float invL = 1.0f / (float)L;
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+
+  u4v pcod[NCP];
+  float psc[NSP];
+  u4v px[NXP];
+  const QlStage st{a.codes + row0 * a.codes_ld, a.codes_ld, a.scales + row0 * a.scales_ld, a.scales_ld,
+                   xg + tok0 * a.ldx, a.ldx, tv};
+  f4v acc[1][TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) acc[0][tn] = f4v{0.f, 0.f, 0.f, 0.f};
+  ql_fetch<BITS, G, R>(st, k_beg, pcod, psc, px);  // k_end - k_beg is a positive multiple of kQlChunk
+  for (int64_t k0 = k_beg; k0 < k_end; k0 += kQlChunk) {
+    __syncthreads();  // the previous chunk's reads are done
+    ql_stash<BITS, G, R>(tv, invL, lcodes, lscales, lx, pcod, psc, px);
+    __syncthreads();
+    if (k0 + kQlChunk < k_end) ql_fetch<BITS, G, R>(st, k0 + kQlChunk, pcod, psc, px);
+#pragma unroll 2
+    for (int gi = 0; gi < NG; ++gi) {
+      uint32_t wds[TN][NW];
+      float sc[TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const uint8_t* cp = lcodes + (lrow0 + 16 * tn) * PB + gi * (G * BITS / 8) + lg * (NC * BITS / 8);
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          if constexpr ((NC * BITS / 8) % 4 == 0) {
+            wds[tn][q] = reinterpret_cast<const uint32_t*>(cp)[q];
+          } else {  // 2-byte aligned pieces
+            const uint16_t* hp = reinterpret_cast<const uint16_t*>(cp);
+            const int h0 = 2 * q;
+            wds[tn][q] = (uint32_t)hp[h0] | (h0 + 1 < NC * BITS / 16 ? (uint32_t)hp[h0 + 1] << 16 : 0u);
+          }
+        }
+        sc[tn] = lscales[(lrow0 + 16 * tn) * PS + gi];
+      }
+      f4v d[1][TN];
+      ql_group<BITS, BF, G, 1, TN>(d, wds, xrow, tok_ok, (int64_t)gi * G);
+      // D reg i holds token 4 lg + i: with one token only register 0 of lane group 0
+#pragma unroll
+      for (int i = 0; i < (ONE ? 1 : 4); ++i)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[0][tn][i] = fmaf(d[0][tn][i], sc[tn], acc[0][tn][i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tk = 4 * lg + i;
+    if (tk < tv)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        a.part[((int64_t)t.split * a.T + tok0 + tk) * a.m + row0 + lrow0 + 16 * tn] = acc[0][tn][i];
+  }
+}
+
 __global__ void ql_reduce_kernel(const float* part, int splits, int64_t T, int64_t m, void* out,
                                  int ot, int64_t ldo) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -398,8 +563,14 @@ __global__ void ql_reduce_kernel(const float* part, int splits, int64_t T, int64
 template <int BITS, bool BF, int G>
 hipError_t launch_g(const QlArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)ql_blocks(a));
-  const size_t lds = ql_lds_bytes(BITS, G, a.tm);
-  if (a.staged) {
+  if (a.kind == kQlStream) {
+    const size_t lds = ql_lds_bytes(BITS, G, kQlOut * kQlStreamTn, a.tv);
+    if (a.tv == 1)
+      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, kQlStreamTn, true>), grid, dim3(kQlThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, kQlStreamTn, false>), grid, dim3(kQlThreads), lds, s, a);
+  } else if (a.kind == kQlStaged) {
+    const size_t lds = ql_lds_bytes(BITS, G, kQlOut * a.tn, 0);
     if (a.tm == 4)
       hipLaunchKernelGGL((qlinear_staged_kernel<BITS, BF, G, 4, 2>), grid, dim3(kQlThreads), lds, s, a);
     else
