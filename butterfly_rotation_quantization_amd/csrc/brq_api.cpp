@@ -1128,9 +1128,10 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // beat fewer with longer load pipelines).  The split count does not depend
 // on the pointers, so the workspace size is known before the call.
 int ql_splits(int64_t T, int64_t m, int64_t n, int bits, int group) {
-  const int64_t tt = kQlTok * ql_tm(T);
   const int kind = ql_kind(T, n, bits, group, true);
-  const int64_t base = (m / (kQlOut * ql_kind_tn(kind, ql_tm(T)))) * ((T + tt - 1) / tt);
+  const int tm = ql_kind_tm(kind, T);
+  const int64_t tt = kQlTok * tm;
+  const int64_t base = (m / (kQlOut * ql_kind_tn(kind, tm))) * ((T + tt - 1) / tt);
   int64_t s = (2048 + base - 1) / base;
   const int64_t ng = n / group;
   if (s > ng) s = ng;
@@ -1148,7 +1149,7 @@ QlLayout ql_layout(const Plan* U, const Plan* V, const brq_quant* q, int64_t T, 
                    int64_t n) {
   QlLayout L;
   L.splits = ql_splits(T, m, n, q->bits, q->group);
-  // the staged kernel's splits hold whole chunks
+  // the streaming kernel's splits hold whole chunks
   const int unit = n % kQlChunk == 0 ? kQlChunk : q->group;
   const int64_t nu = n / unit;
   if (L.splits > nu) L.splits = (int)nu;
@@ -1239,8 +1240,8 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   a.scales_ld = n / q->group;
   a.splits = L.splits;
   a.kc = L.kc;
-  a.tm = ql_tm(T);
   a.kind = ql_kind(T, n, q->bits, q->group, reinterpret_cast<uintptr_t>(codes) % 16 == 0);
+  a.tm = ql_kind_tm(a.kind, T);
   a.tn = ql_kind_tn(a.kind, a.tm);
   a.tv = (int)(T < kQlTok ? T : kQlTok);
   a.part = reinterpret_cast<float*>(w + L.part_off);

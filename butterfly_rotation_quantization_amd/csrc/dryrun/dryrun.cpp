@@ -877,7 +877,7 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
     return violation("quantized linear kernel choice (kind %lld, tn %lld)", a.kind, TN), hipErrorInvalidValue;
   if (a.bits < 2 || a.bits > 5 || (a.group != 64 && a.group != 128) || a.n % a.group || a.m % (kQlOut * TN) ||
       a.kc % a.group || a.kc <= 0 || a.splits < 1 || (a.splits - 1) * a.kc >= a.n || a.splits * a.kc < a.n ||
-      a.tm != ql_tm(a.T))
+      a.tm != ql_kind_tm(a.kind, a.T))
     return violation("quantized linear geometry (splits %lld, kc %lld)", a.splits, a.kc), hipErrorInvalidValue;
   if (a.ldx < a.n || a.ldx % 8 || reinterpret_cast<uintptr_t>(a.x) % 16)
     return violation("activation rows not 16-byte vectors (ld %lld)", a.ldx, 0), hipErrorInvalidValue;
@@ -888,9 +888,9 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   const int NC = a.group / 4, NB = NC * a.bits / 8;
   if (a.kind != kQlDirect) {  // whole chunks per split, 16-byte rows, and the LDS the launch asks for
     const int R = kQlOut * TN, CB = kQlChunk * a.bits / 8, PB = ql_code_pitch(a.bits);
-    const int tv = a.kind == kQlStream ? a.tv : 0;
+    const int tv = a.tv;
     if (a.n % kQlChunk || a.kc % kQlChunk || reinterpret_cast<uintptr_t>(a.codes) % 16 || a.codes_ld % 16 ||
-        ql_lds_bytes(a.bits, a.group, R, tv) > 64 * 1024 || (a.kind == kQlStream && (a.tm != 1 || a.T > kQlTok)))
+        ql_lds_bytes(a.bits, a.group, R, tv) > 64 * 1024 || (a.kind == kQlStream && a.tm != 1))
       return violation("staged product geometry (kc %lld, ld %lld)", a.kc, a.codes_ld), hipErrorInvalidValue;
     if (a.kind == kQlStream) {
       // staged pieces per thread divide exactly; activation reads stay inside a token's chunk row

@@ -8,7 +8,8 @@
 // float32 by v_mfma_f32_16x16x32_{f16,bf16}, and then scaled by alpha / L.
 //
 // A workgroup is four waves over 64 tn outputs (16 tn each) and 16 tm
-// tokens: tm = 1, tn = 4 up to 16 tokens, tm = 4, tn = 2 above.  Wave w owns
+// tokens: tm = 1, tn = 4 up to 16 tokens, tm = 4, tn = 2 above (the direct
+// kernel), or tm = 1, tn = 2 (the streaming kernel).  Wave w owns
 // outputs o0 + 16 tn w .. for all the tokens; it loads each activation
 // operand once for its tn output tiles and decodes each weight code once for
 // its tm token tiles.  Groups of 64 or 128 inputs.  The reduction over the
@@ -47,15 +48,17 @@ struct QlArgs {
 };
 
 // kQlDirect: every lane reads its codes and activations from global memory.
-// kQlStaged: the workgroup's weight rows pass through LDS one chunk of
-//   kQlChunk inputs at a time, with whole-line loads (each row's chunk is
-//   contiguous), so every code byte leaves HBM once.
-// kQlStream (up to 16 tokens): as staged, and the tile's activations go
-//   through LDS too; the next chunk's codes, scales and activations are
-//   loaded into registers while the current chunk is multiplied, so the
-//   loads stay in flight during the arithmetic (no global load is waited
-//   for inside it).
-enum QlKind { kQlDirect = 0, kQlStaged = 1, kQlStream = 2 };
+// kQlStream: one 16-token tile per workgroup; the workgroup's weight rows
+//   (codes and scales) and the tile's activations pass through LDS one chunk
+//   of kQlChunk inputs at a time, with whole-line loads (each row's chunk is
+//   contiguous, so every code byte leaves HBM once per token tile), and the
+//   next chunk is loaded into registers while the current one is multiplied,
+//   so the loads stay in flight during the arithmetic (no global load is
+//   waited for inside it).  Several token tiles read the same weight block
+//   one after another (the tiles of a row block are launched together, so
+//   the re-reads hit the caches); measured, one tile per workgroup beats four
+//   at 256 tokens too, the decode work per code being the limit.
+enum QlKind { kQlDirect = 0, kQlStream = 1 };
 constexpr int kQlStreamTn = 2;
 
 struct QlTile {
@@ -84,13 +87,13 @@ __host__ __device__ inline QlTile ql_tile(const QlArgs& a, int64_t bid) {
 __host__ __device__ inline int64_t ql_code_off(const QlArgs& a, int64_t o, int64_t k) {
   return o * a.codes_ld + k * a.bits / 8;
 }
-// The staged kinds need n a multiple of kQlChunk and 16-byte aligned codes.
+// The streaming kernel needs n a multiple of kQlChunk and 16-byte aligned codes.
 constexpr int kQlChunk = 512;
 // LDS row pitches: the chunk's code bytes plus 16 (keeps 16-byte alignment
 // and moves successive rows by four banks); a token's activations plus 16.
 __host__ __device__ inline int ql_code_pitch(int bits) { return kQlChunk * bits / 8 + 16; }
 constexpr int kQlXPitch = 2 * kQlChunk + 16;
-// LDS of a staged launch: rows x (codes + scales of the chunk's groups), and
+// LDS of a streaming launch: rows x (codes + scales of the chunk's groups), and
 // tv activation rows.
 __host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int rows, int tv) {
   return (size_t)rows * ql_code_pitch(bits) + (size_t)rows * (kQlChunk / group + 1) * 4 +
@@ -99,15 +102,15 @@ __host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int rows, in
 // 16-token tiles per workgroup for T tokens.
 __host__ __device__ inline int ql_tm(int64_t T) { return T > kQlTok ? 4 : 1; }
 // The kernel for a shape (codes_aligned: 16-byte aligned codes), staying
-// within the 64 KiB of LDS a launch takes without an attribute.
+// within the 64 KiB of LDS a launch takes without an attribute (the
+// streaming kernel's staging is at most 62.75 KiB for b <= 5).
 __host__ __device__ inline int ql_kind(int64_t T, int64_t n, int bits, int group, bool codes_aligned) {
   if (n % kQlChunk || !codes_aligned) return kQlDirect;
-  const int tm = ql_tm(T);
-  if (tm == 1 && ql_lds_bytes(bits, group, kQlOut * kQlStreamTn, (int)(T < kQlTok ? T : kQlTok)) <= 64 * 1024)
+  if (ql_lds_bytes(bits, group, kQlOut * kQlStreamTn, (int)(T < kQlTok ? T : kQlTok)) <= 64 * 1024)
     return kQlStream;
-  if (ql_lds_bytes(bits, group, kQlOut * ql_tn(tm), 0) <= 64 * 1024) return kQlStaged;
   return kQlDirect;
 }
+__host__ __device__ inline int ql_kind_tm(int kind, int64_t T) { return kind == kQlStream ? 1 : ql_tm(T); }
 __host__ __device__ inline int ql_kind_tn(int kind, int tm) { return kind == kQlStream ? kQlStreamTn : ql_tn(tm); }
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t s);

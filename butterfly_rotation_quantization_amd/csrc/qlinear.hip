@@ -288,97 +288,6 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_kernel(QlArgs a) {
     }
 }
 
-// The same product with the weight rows staged through LDS (qlinear.h).
-template <int BITS, bool BF, int G, int TM, int TN>
-__global__ __launch_bounds__(kQlThreads) void qlinear_staged_kernel(QlArgs a) {
-  constexpr int L = (1 << BITS) - 1;
-  constexpr int NC = G / 4;
-  constexpr int NW = (NC * BITS + 31) / 32;
-  constexpr int R = kQlOut * TN;            // weight rows of the workgroup
-  constexpr int CB = kQlChunk * BITS / 8;   // code bytes of a row per chunk
-  constexpr int PB = CB + 16;               // LDS pitch
-  constexpr int NG = kQlChunk / G;          // groups per chunk
-  constexpr int PS = NG + 1;                // scale pitch (floats)
-  extern __shared__ __align__(16) uint8_t ql_lds[];
-  uint8_t* lcodes = ql_lds;
-  float* lscales = reinterpret_cast<float*>(ql_lds + R * PB);
-  const QlTile t = ql_tile(a, blockIdx.x);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int64_t row0 = t.ct * (int64_t)R;
-  const int lrow0 = 16 * TN * w + lr;  // + 16 tn: this lane's rows within the workgroup
-  const int64_t k_beg = t.split * a.kc;
-  const int64_t k_end = k_beg + a.kc < a.n ? k_beg + a.kc : a.n;
-  const uint16_t* xrow[TM];
-  bool tok_ok[TM];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int64_t tok = (t.tt * TM + tm) * kQlTok + lr;
-    tok_ok[tm] = tok < a.T;
-    xrow[tm] = static_cast<const uint16_t*>(a.x) + (tok_ok[tm] ? tok : 0) * a.ldx + lg * NC;
-  }
-  const float invL = 1.0f / (float)L;
-  f4v acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f4v{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t k0 = k_beg; k0 < k_end; k0 += kQlChunk) {  // k_end - k0 is a multiple of kQlChunk
-    __syncthreads();  // the previous chunk's reads are done
-    // codes: R rows x CB bytes in 16-byte pieces, consecutive threads along a row
-    for (int pc = tid; pc < R * (CB / 16); pc += kQlThreads) {
-      const int r = pc / (CB / 16), q = pc - r * (CB / 16);
-      const uint4 v = *reinterpret_cast<const uint4*>(a.codes + (row0 + r) * a.codes_ld + k0 * BITS / 8 + 16 * q);
-      *reinterpret_cast<uint4*>(lcodes + r * PB + 16 * q) = v;
-    }
-    for (int ps = tid; ps < R * NG; ps += kQlThreads) {
-      const int r = ps / NG, gq = ps - r * NG;
-      lscales[r * PS + gq] = a.scales[(row0 + r) * a.scales_ld + k0 / G + gq] * invL;
-    }
-    __syncthreads();
-#pragma unroll 2
-    for (int gi = 0; gi < NG; ++gi) {
-      const int64_t g0 = k0 + (int64_t)gi * G;
-      uint32_t wds[TN][NW];
-      float sc[TN];
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const uint8_t* cp = lcodes + (lrow0 + 16 * tn) * PB + gi * (G * BITS / 8) + lg * (NC * BITS / 8);
-#pragma unroll
-        for (int q = 0; q < NW; ++q) {
-          if constexpr ((NC * BITS / 8) % 4 == 0) {
-            wds[tn][q] = reinterpret_cast<const uint32_t*>(cp)[q];
-          } else {  // 2-byte aligned pieces
-            const uint16_t* hp = reinterpret_cast<const uint16_t*>(cp);
-            const int h0 = 2 * q;
-            wds[tn][q] = (uint32_t)hp[h0] | (h0 + 1 < NC * BITS / 16 ? (uint32_t)hp[h0 + 1] << 16 : 0u);
-          }
-        }
-        sc[tn] = lscales[(lrow0 + 16 * tn) * PS + gi];
-      }
-      f4v d[TM][TN];
-      ql_group<BITS, BF, G, TM, TN>(d, wds, xrow, tok_ok, g0);
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tm][tn][i] = fmaf(d[tm][tn][i], sc[tn], acc[tm][tn][i]);
-    }
-  }
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tk = (t.tt * TM + tm) * kQlTok + 4 * lg + i;
-      if (tk < a.T)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          a.part[((int64_t)t.split * a.T + tk) * a.m + row0 + lrow0 + 16 * tn] = acc[tm][tn][i];
-    }
-}
-
 // Staging of one chunk for the streaming kernel: R weight rows x kQlChunk
 // inputs of codes (16-byte pieces, consecutive threads along a row), their
 // scales, and the tile's tv token rows of activations.
@@ -445,7 +354,7 @@ __device__ __forceinline__ void ql_stash(int tv, float invL, uint8_t* lcodes, fl
   }
 }
 
-// Up to 16 tokens with the loads of the next chunk in flight (kQlStream).
+// One 16-token tile with the loads of the next chunk in flight (kQlStream).
 template <int BITS, bool BF, int G, int TN, bool ONE>
 __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
   constexpr int L = (1 << BITS) - 1;
@@ -473,7 +382,8 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
   const int64_t row0 = t.ct * (int64_t)R;
   const int lrow0 = 16 * TN * w + lr;  // + 16 tn: this lane's rows within the workgroup
   const int64_t tok0 = t.tt * (int64_t)kQlTok;
-  const int tv = ONE ? 1 : a.tv;      // tokens tok0 .. tok0 + tv - 1 exist (tv = min(T - tok0, 16))
+  // tokens tok0 .. tok0 + tv - 1 exist
+  const int tv = ONE ? 1 : (int)(a.T - tok0 < kQlTok ? a.T - tok0 : kQlTok);
   const int64_t k_beg = t.split * a.kc;
   const int64_t k_end = k_beg + a.kc < a.n ? k_beg + a.kc : a.n;
   const uint16_t* const xrow[1] = {reinterpret_cast<const uint16_t*>(lx + lr * kQlXPitch) + lg * NC};
@@ -569,12 +479,6 @@ hipError_t launch_g(const QlArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, kQlStreamTn, true>), grid, dim3(kQlThreads), lds, s, a);
     else
       hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, kQlStreamTn, false>), grid, dim3(kQlThreads), lds, s, a);
-  } else if (a.kind == kQlStaged) {
-    const size_t lds = ql_lds_bytes(BITS, G, kQlOut * a.tn, 0);
-    if (a.tm == 4)
-      hipLaunchKernelGGL((qlinear_staged_kernel<BITS, BF, G, 4, 2>), grid, dim3(kQlThreads), lds, s, a);
-    else
-      hipLaunchKernelGGL((qlinear_staged_kernel<BITS, BF, G, 1, 4>), grid, dim3(kQlThreads), lds, s, a);
   } else if (a.tm == 4) {
     hipLaunchKernelGGL((qlinear_kernel<BITS, BF, G, 4, 2>), grid, dim3(kQlThreads), 0, s, a);
   } else {

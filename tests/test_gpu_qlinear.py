@@ -81,7 +81,7 @@ def test_qlinear_small(T_, bits, group, sides):
 @pytest.mark.parametrize("T_", [1, 37])
 @pytest.mark.parametrize("bits,group", [(2, 64), (3, 64), (4, 128), (5, 64)])
 @pytest.mark.parametrize("n", [1024, 3584])
-def test_qlinear_staged_chunks(T_, bits, group, n):
+def test_qlinear_stream_chunks(T_, bits, group, n):
     """n a multiple of the 512-input chunk: the weight rows pass through LDS
     (when the staging fits), with one or several chunks per split and fewer
     chunks than the split target."""
@@ -91,11 +91,11 @@ def test_qlinear_staged_chunks(T_, bits, group, n):
     codes, alpha, x = _case(rng, T_, m, n, bits, group)
     xs = S.to_storage(x, "f16")
     Rs = S.random_plan(rng, (n // 256, 16, 16), "per_group")
-    announce(f"qlinear staged T={T_} m={m} n={n} b{bits} g{group}")
+    announce(f"qlinear stream T={T_} m={m} n={n} b{bits} g{group}")
     y = brq.qlinear(None, lib_plan(Rs), to_dev(xs, "f16"), to_dev(codes, "u8"), to_dev(alpha, "f32"),
                     m, n, bits, group)
     _check(from_dev(y), xs, "f16", None, orc_plan(Rs), codes, alpha, bits, group, "f16",
-           f"staged T={T_} b{bits} n={n}")
+           f"stream T={T_} b{bits} n={n}")
 
 
 def test_qlinear_bf16_and_f32_out():
@@ -111,7 +111,7 @@ def test_qlinear_bf16_and_f32_out():
     _check(from_dev(y), xs, "bf16", None, orc_plan(Rs), codes, alpha, bits, group, "f32", "bf16 in")
 
 
-@pytest.mark.parametrize("T_", [1, 16])
+@pytest.mark.parametrize("T_", [1, 16, 256])
 def test_qlinear_70b_down_proj(T_):
     """The 70B down projection: 8192 outputs, 28672 inputs, left (32,16,16),
     right (7,16,16,16), 2-bit g64, f16 activations."""
