@@ -1129,7 +1129,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // on the pointers, so the workspace size is known before the call.
 int ql_splits(int64_t T, int64_t m, int64_t n, int bits, int group) {
   const int kind = ql_kind(T, n, bits, group, true);
-  const int tm = ql_kind_tm(kind, T);
+  const int tm = ql_kind_tm(kind, T, bits, group);
   const int64_t tt = kQlTok * tm;
   const int64_t base = (m / (kQlOut * ql_kind_tn(kind, tm))) * ((T + tt - 1) / tt);
   int64_t s = (2048 + base - 1) / base;
@@ -1241,9 +1241,9 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   a.splits = L.splits;
   a.kc = L.kc;
   a.kind = ql_kind(T, n, q->bits, q->group, reinterpret_cast<uintptr_t>(codes) % 16 == 0);
-  a.tm = ql_kind_tm(a.kind, T);
+  a.tm = ql_kind_tm(a.kind, T, q->bits, q->group);
   a.tn = ql_kind_tn(a.kind, a.tm);
-  a.tv = (int)(T < kQlTok ? T : kQlTok);
+  a.tv = (int)(T < kQlTok * a.tm ? T : kQlTok * a.tm);
   a.part = reinterpret_cast<float*>(w + L.part_off);
   char name[48];
   snprintf(name, sizeof name, "qlinear b%d g%d", q->bits, q->group);

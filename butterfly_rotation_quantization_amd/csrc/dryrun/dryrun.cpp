@@ -873,11 +873,11 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   ++g_launches;
   const int TN = a.tn;
   if (a.kind != ql_kind(a.T, a.n, a.bits, a.group, reinterpret_cast<uintptr_t>(a.codes) % 16 == 0) ||
-      TN != ql_kind_tn(a.kind, a.tm) || a.tv != (int)std::min<int64_t>(a.T, kQlTok))
+      TN != ql_kind_tn(a.kind, a.tm) || a.tv != (int)std::min<int64_t>(a.T, (int64_t)kQlTok * a.tm))
     return violation("quantized linear kernel choice (kind %lld, tn %lld)", a.kind, TN), hipErrorInvalidValue;
   if (a.bits < 2 || a.bits > 5 || (a.group != 64 && a.group != 128) || a.n % a.group || a.m % (kQlOut * TN) ||
       a.kc % a.group || a.kc <= 0 || a.splits < 1 || (a.splits - 1) * a.kc >= a.n || a.splits * a.kc < a.n ||
-      a.tm != ql_kind_tm(a.kind, a.T))
+      a.tm != ql_kind_tm(a.kind, a.T, a.bits, a.group))
     return violation("quantized linear geometry (splits %lld, kc %lld)", a.splits, a.kc), hipErrorInvalidValue;
   if (a.ldx < a.n || a.ldx % 8 || reinterpret_cast<uintptr_t>(a.x) % 16)
     return violation("activation rows not 16-byte vectors (ld %lld)", a.ldx, 0), hipErrorInvalidValue;
@@ -890,12 +890,12 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
     const int R = kQlOut * TN, CB = kQlChunk * a.bits / 8, PB = ql_code_pitch(a.bits);
     const int tv = a.tv;
     if (a.n % kQlChunk || a.kc % kQlChunk || reinterpret_cast<uintptr_t>(a.codes) % 16 || a.codes_ld % 16 ||
-        ql_lds_bytes(a.bits, a.group, R, tv) > 64 * 1024 || (a.kind == kQlStream && a.tm != 1))
+        ql_lds_bytes(a.bits, a.group, R, tv) > 64 * 1024 || (a.kind == kQlStream && a.tm != 1 && a.tm != 2))
       return violation("staged product geometry (kc %lld, ld %lld)", a.kc, a.codes_ld), hipErrorInvalidValue;
     if (a.kind == kQlStream) {
       // staged pieces per thread divide exactly; activation reads stay inside a token's chunk row
       const int NG = kQlChunk / a.group;
-      if ((R * (CB / 16)) % kQlThreads || (R * NG) % kQlThreads || (kQlTok * (kQlChunk / 8)) % kQlThreads)
+      if ((R * (CB / 16)) % kQlThreads || (R * NG) % kQlThreads || (kQlTok * a.tm * (kQlChunk / 8)) % kQlThreads)
         return violation("stream staging pieces (rows %lld)", R, 0), hipErrorInvalidValue;
       const bool bf = a.xt == BRQ_BF16;
       for (int gi = 0; gi < NG; ++gi)

@@ -43,12 +43,12 @@ struct QlArgs {
   int tm;               // 16-token tiles per workgroup (1 or 4)
   int tn;               // 16-output tiles per wave
   int kind;             // QlKind
-  int tv;               // kQlStream: tokens of a tile staged in LDS (min(T, 16))
+  int tv;               // kQlStream: LDS token rows of a tile (min(T, 16 tm))
   float* part;          // [splits][T][m]
 };
 
 // kQlDirect: every lane reads its codes and activations from global memory.
-// kQlStream: one 16-token tile per workgroup; the workgroup's weight rows
+// kQlStream: one or two 16-token tiles per workgroup; the workgroup's weight rows
 //   (codes and scales) and the tile's activations pass through LDS one chunk
 //   of kQlChunk inputs at a time, with whole-line loads (each row's chunk is
 //   contiguous, so every code byte leaves HBM once per token tile), and the
@@ -56,8 +56,9 @@ struct QlArgs {
 //   so the loads stay in flight during the arithmetic (no global load is
 //   waited for inside it).  Several token tiles read the same weight block
 //   one after another (the tiles of a row block are launched together, so
-//   the re-reads hit the caches); measured, one tile per workgroup beats four
-//   at 256 tokens too, the decode work per code being the limit.
+//   most re-reads hit the caches).  The decode work per code is the limit;
+//   two tiles per workgroup (above 16 tokens, where the staging fits) halve
+//   it per token, four tiles cost too many registers.
 enum QlKind { kQlDirect = 0, kQlStream = 1 };
 constexpr int kQlStreamTn = 2;
 
@@ -110,7 +111,15 @@ __host__ __device__ inline int ql_kind(int64_t T, int64_t n, int bits, int group
     return kQlStream;
   return kQlDirect;
 }
-__host__ __device__ inline int ql_kind_tm(int kind, int64_t T) { return kind == kQlStream ? 1 : ql_tm(T); }
+// Token tiles per workgroup of the streaming kernel: two above 16 tokens when
+// the staging of 32 activation rows still fits.
+__host__ __device__ inline int ql_stream_tm(int64_t T, int bits, int group) {
+  return T > kQlTok && ql_lds_bytes(bits, group, kQlOut * kQlStreamTn, (int)(T < 2 * kQlTok ? T : 2 * kQlTok)) <= 64 * 1024
+             ? 2 : 1;
+}
+__host__ __device__ inline int ql_kind_tm(int kind, int64_t T, int bits, int group) {
+  return kind == kQlStream ? ql_stream_tm(T, bits, group) : ql_tm(T);
+}
 __host__ __device__ inline int ql_kind_tn(int kind, int tm) { return kind == kQlStream ? kQlStreamTn : ql_tn(tm); }
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t s);

@@ -168,10 +168,10 @@ __device__ __forceinline__ void ql_group(f4v (&d)[TM][TN], const uint32_t (&wds)
   uint32_t pr[TN][NC / 2];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    // the fused and-or helps the one-token-tile kernels and costs the
+    // the fused and-or helps the one- and two-tile kernels and costs the
     // four-tile ones registers
-    if constexpr (BF) ql_bf16_pairs<BITS, NC, TM == 1>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
-    else ql_f16_pairs<BITS, NC, TM == 1>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
+    if constexpr (BF) ql_bf16_pairs<BITS, NC, TM <= 2>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
+    else ql_f16_pairs<BITS, NC, TM <= 2>(wds[tn], pr[tn], std::make_integer_sequence<int, NC / 2>{});
   }
 #pragma unroll
   for (int sp = 0; sp < NC / 16; ++sp) {  // two MFMA steps per activation load
@@ -300,17 +300,18 @@ struct QlStage {
   int64_t ldx;
   int tv;
 };
-template <int BITS, int G, int R>
+template <int BITS, int G, int R, int TM>
 struct QlPieces {
   static constexpr int CB = kQlChunk * BITS / 8, NG = kQlChunk / G, XQ = kQlChunk / 8;
-  static constexpr int NCP = R * (CB / 16) / kQlThreads, NSP = R * NG / kQlThreads, NXP = kQlTok * XQ / kQlThreads;
+  static constexpr int NCP = R * (CB / 16) / kQlThreads, NSP = R * NG / kQlThreads;
+  static constexpr int NXP = kQlTok * TM * XQ / kQlThreads;
 };
 
-template <int BITS, int G, int R>
-__device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pcod)[QlPieces<BITS, G, R>::NCP],
-                                         float (&psc)[QlPieces<BITS, G, R>::NSP],
-                                         u4v (&px)[QlPieces<BITS, G, R>::NXP]) {
-  using P = QlPieces<BITS, G, R>;
+template <int BITS, int G, int R, int TM>
+__device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pcod)[QlPieces<BITS, G, R, TM>::NCP],
+                                         float (&psc)[QlPieces<BITS, G, R, TM>::NSP],
+                                         u4v (&px)[QlPieces<BITS, G, R, TM>::NXP]) {
+  using P = QlPieces<BITS, G, R, TM>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < P::NCP; ++i) {
@@ -329,12 +330,12 @@ __device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pc
   }
 }
 
-template <int BITS, int G, int R>
+template <int BITS, int G, int R, int TM>
 __device__ __forceinline__ void ql_stash(int tv, float invL, uint8_t* lcodes, float* lscales, uint8_t* lx,
-                                         const u4v (&pcod)[QlPieces<BITS, G, R>::NCP],
-                                         const float (&psc)[QlPieces<BITS, G, R>::NSP],
-                                         const u4v (&px)[QlPieces<BITS, G, R>::NXP]) {
-  using P = QlPieces<BITS, G, R>;
+                                         const u4v (&pcod)[QlPieces<BITS, G, R, TM>::NCP],
+                                         const float (&psc)[QlPieces<BITS, G, R, TM>::NSP],
+                                         const u4v (&px)[QlPieces<BITS, G, R, TM>::NXP]) {
+  using P = QlPieces<BITS, G, R, TM>;
   constexpr int PB = P::CB + 16, PS = P::NG + 1;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -354,8 +355,8 @@ __device__ __forceinline__ void ql_stash(int tv, float invL, uint8_t* lcodes, fl
   }
 }
 
-// One 16-token tile with the loads of the next chunk in flight (kQlStream).
-template <int BITS, bool BF, int G, int TN, bool ONE>
+// TM 16-token tiles with the loads of the next chunk in flight (kQlStream).
+template <int BITS, bool BF, int G, int TM, int TN, bool ONE>
 __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
   constexpr int L = (1 << BITS) - 1;
   constexpr int NC = G / 4;
@@ -369,8 +370,9 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
   // pieces per thread: codes, scales, activations (the divisions are exact)
   constexpr int NCP = R * (CB / 16) / kQlThreads;
   constexpr int NSP = R * NG / kQlThreads;
-  constexpr int NXP = kQlTok * XQ / kQlThreads;
-  static_assert(NCP * kQlThreads == R * (CB / 16) && NSP * kQlThreads == R * NG && NXP * kQlThreads == kQlTok * XQ,
+  constexpr int NXP = kQlTok * TM * XQ / kQlThreads;
+  static_assert(NCP * kQlThreads == R * (CB / 16) && NSP * kQlThreads == R * NG &&
+                    NXP * kQlThreads == kQlTok * TM * XQ,
                 "staging pieces must divide among the threads");
   extern __shared__ __align__(16) uint8_t ql_lds[];
   uint8_t* lcodes = ql_lds;
@@ -381,13 +383,18 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t row0 = t.ct * (int64_t)R;
   const int lrow0 = 16 * TN * w + lr;  // + 16 tn: this lane's rows within the workgroup
-  const int64_t tok0 = t.tt * (int64_t)kQlTok;
+  const int64_t tok0 = t.tt * (int64_t)(kQlTok * TM);
   // tokens tok0 .. tok0 + tv - 1 exist
-  const int tv = ONE ? 1 : (int)(a.T - tok0 < kQlTok ? a.T - tok0 : kQlTok);
+  const int tv = ONE ? 1 : (int)(a.T - tok0 < kQlTok * TM ? a.T - tok0 : kQlTok * TM);
   const int64_t k_beg = t.split * a.kc;
   const int64_t k_end = k_beg + a.kc < a.n ? k_beg + a.kc : a.n;
-  const uint16_t* const xrow[1] = {reinterpret_cast<const uint16_t*>(lx + lr * kQlXPitch) + lg * NC};
-  const bool tok_ok[1] = {lr < tv};
+  const uint16_t* xrow[TM];
+  bool tok_ok[TM];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    xrow[tm] = reinterpret_cast<const uint16_t*>(lx + (16 * tm + lr) * kQlXPitch) + lg * NC;
+    tok_ok[tm] = 16 * tm + lr < tv;
+  }
   const float invL = 1.0f / (float)L;
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
 
@@ -396,15 +403,17 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
   u4v px[NXP];
   const QlStage st{a.codes + row0 * a.codes_ld, a.codes_ld, a.scales + row0 * a.scales_ld, a.scales_ld,
                    xg + tok0 * a.ldx, a.ldx, tv};
-  f4v acc[1][TN];
+  f4v acc[TM][TN];
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) acc[0][tn] = f4v{0.f, 0.f, 0.f, 0.f};
-  ql_fetch<BITS, G, R>(st, k_beg, pcod, psc, px);  // k_end - k_beg is a positive multiple of kQlChunk
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f4v{0.f, 0.f, 0.f, 0.f};
+  ql_fetch<BITS, G, R, TM>(st, k_beg, pcod, psc, px);  // k_end - k_beg is a positive multiple of kQlChunk
   for (int64_t k0 = k_beg; k0 < k_end; k0 += kQlChunk) {
     __syncthreads();  // the previous chunk's reads are done
-    ql_stash<BITS, G, R>(tv, invL, lcodes, lscales, lx, pcod, psc, px);
+    ql_stash<BITS, G, R, TM>(tv, invL, lcodes, lscales, lx, pcod, psc, px);
     __syncthreads();
-    if (k0 + kQlChunk < k_end) ql_fetch<BITS, G, R>(st, k0 + kQlChunk, pcod, psc, px);
+    if (k0 + kQlChunk < k_end) ql_fetch<BITS, G, R, TM>(st, k0 + kQlChunk, pcod, psc, px);
 #pragma unroll 2
     for (int gi = 0; gi < NG; ++gi) {
       uint32_t wds[TN][NW];
@@ -424,23 +433,27 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
         }
         sc[tn] = lscales[(lrow0 + 16 * tn) * PS + gi];
       }
-      f4v d[1][TN];
-      ql_group<BITS, BF, G, 1, TN>(d, wds, xrow, tok_ok, (int64_t)gi * G);
-      // D reg i holds token 4 lg + i: with one token only register 0 of lane group 0
+      f4v d[TM][TN];
+      ql_group<BITS, BF, G, TM, TN>(d, wds, xrow, tok_ok, (int64_t)gi * G);
+      // D reg i holds token 16 tm + 4 lg + i: with one token only register 0 of lane group 0
 #pragma unroll
-      for (int i = 0; i < (ONE ? 1 : 4); ++i)
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[0][tn][i] = fmaf(d[0][tn][i], sc[tn], acc[0][tn][i]);
+        for (int i = 0; i < (ONE ? 1 : 4); ++i)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) acc[tm][tn][i] = fmaf(d[tm][tn][i], sc[tn], acc[tm][tn][i]);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tk = 4 * lg + i;
-    if (tk < tv)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        a.part[((int64_t)t.split * a.T + tok0 + tk) * a.m + row0 + lrow0 + 16 * tn] = acc[0][tn][i];
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 16 * tm + 4 * lg + i;
+      if (tk < tv)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          a.part[((int64_t)t.split * a.T + tok0 + tk) * a.m + row0 + lrow0 + 16 * tn] = acc[tm][tn][i];
+    }
 }
 
 __global__ void ql_reduce_kernel(const float* part, int splits, int64_t T, int64_t m, void* out,
@@ -475,10 +488,12 @@ hipError_t launch_g(const QlArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)ql_blocks(a));
   if (a.kind == kQlStream) {
     const size_t lds = ql_lds_bytes(BITS, G, kQlOut * kQlStreamTn, a.tv);
-    if (a.tv == 1)
-      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, kQlStreamTn, true>), grid, dim3(kQlThreads), lds, s, a);
+    if (a.tm == 2)
+      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, 2, kQlStreamTn, false>), grid, dim3(kQlThreads), lds, s, a);
+    else if (a.tv == 1)
+      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, 1, kQlStreamTn, true>), grid, dim3(kQlThreads), lds, s, a);
     else
-      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, kQlStreamTn, false>), grid, dim3(kQlThreads), lds, s, a);
+      hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, 1, kQlStreamTn, false>), grid, dim3(kQlThreads), lds, s, a);
   } else if (a.tm == 4) {
     hipLaunchKernelGGL((qlinear_kernel<BITS, BF, G, 4, 2>), grid, dim3(kQlThreads), 0, s, a);
   } else {
