@@ -695,12 +695,12 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
             for (int k = 0; k < a.bs; ++k)
               if (base + k >= kLds || !xin[base + k]) return violation("LDS read of unwritten slot %lld", base + k, 0), hipErrorInvalidValue;
           }
-          const int s = a.b2 ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j);
+          const int s = a.b2 && !a.inv2 ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j);
           if (yout[s]++) return violation("LDS output slot %lld written twice", s, 0), hipErrorInvalidValue;
         }
       }
-      if (a.b2) {  // the second stage: reads (g2, k2) (position order), writes (j2, g2)
-        if (a.side != 0 || a.gw != 16 || a.S != 16 || a.b != 16 || a.b2 != 16 || a.bs != 16 ||
+      if (a.b2) {  // the second stage: reads (g2, k2) (forward) or (k2, g2) (inverse), writes (j2, g2)
+        if (a.side != 0 || a.gw != 16 || a.S != (a.inv2 ? 1 : 16) || a.b != 16 || a.b2 != 16 || a.bs != 16 ||
             ng != a.gw || (a.mode != BRQ_HADAMARD && (!a.blk2 || reinterpret_cast<uintptr_t>(a.blk2) % 16)))
           return violation("stage pair geometry (b %lld, b2 %lld)", a.b, a.b2), hipErrorInvalidValue;
         const int64_t blk2_floats = a.mode == BRQ_PER_GROUP ? (a.d / a.b2) * a.b2 * a.b2 : (int64_t)a.b2 * a.b2;
@@ -712,9 +712,12 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
             if (r < 0 || r + a.b2 > blk2_floats) return violation("second-stage block row %lld of %lld", r, blk2_floats), hipErrorInvalidValue;
           }
           for (int l = 0; l < nl; ++l) {  // the first stage wrote (j, g) = every slot of the block
-            for (int k2 = 0; k2 < a.b2; ++k2)
-              if (yout[sp_lds(a, l, g2, k2)] != 1) return violation("second stage reads slot %lld", sp_lds(a, l, g2, k2), 0), hipErrorInvalidValue;
-            if (sp_lds(a, l, g2, 0) % 4) return violation("second stage vector read at %lld", sp_lds(a, l, g2, 0), 0), hipErrorInvalidValue;
+            for (int k2 = 0; k2 < a.b2; ++k2) {
+              const int sr = a.inv2 ? sp_lds(a, l, k2, g2) : sp_lds(a, l, g2, k2);
+              if (a.inv2 && sr != sp_lds(a, l, 0, g2) + 16 * k2) return violation("second stage column read at %lld", sr, 0), hipErrorInvalidValue;
+              if (yout[sr] != 1) return violation("second stage reads slot %lld", sr, 0), hipErrorInvalidValue;
+            }
+            if (!a.inv2 && sp_lds(a, l, g2, 0) % 4) return violation("second stage vector read at %lld", sp_lds(a, l, g2, 0), 0), hipErrorInvalidValue;
             if (yout[sp_lds(a, l, j2, g2)] != 1) return violation("second stage writes slot %lld", sp_lds(a, l, j2, g2), 0), hipErrorInvalidValue;
           }
         }

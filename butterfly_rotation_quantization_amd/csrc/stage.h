@@ -53,20 +53,28 @@ struct SpArgs {
   void* dst;
   int dst_t;
   int64_t ld_dst;
-  // Optional second stage in the same tile (right side, forward): the pair
-  // (16, S = 16), (16, 1) with gw = 16 groups, one block of 256 consecutive
-  // positions per line.  The first stage then leaves output (g, j) at slot
-  // (j, g), i.e. in position order, the second stage's group g2 reads the
-  // consecutive slots (g2, k2) and writes output (g2, j2) at slot (j2, g2),
-  // the first stage's slot of that position, where the store phase reads it.
+  // Optional second stage in the same tile (right side): the pair (16,
+  // S = 16), (16, 1) forward, or (16, 1), (16, S = 16) inverse (inv2), with
+  // gw = 16 groups, one block of 256 consecutive positions per line.
+  // Forward, the first stage leaves output (g, j) at slot (j, g), i.e. in
+  // position order, the second stage's group g2 reads the consecutive slots
+  // (g2, k2) and writes output (g2, j2) at slot (j2, g2), the first stage's
+  // slot of that position, where the store phase reads it.  Inverse, the
+  // first stage's groups are the rows of the 16 x 16 position block, so its
+  // output (g, j) stays at slot (g, j) (position order already); the second
+  // stage's group g2 is the column g2, members at slots (k2, g2), and it
+  // writes output j2 at slot (j2, g2), again that position's slot.
   int b2;             // 16, or 0 for a single stage
+  int inv2;           // the pair is the inverse one
   const float* blk2;  // its blocks ([group][j][k] over the chunk's d / b2 groups, or one)
 };
 
 // Float offset of row j2 of the second stage's block for local group g2 of
-// the tile whose first group is gid0.
+// the tile whose first group is gid0: the tile is the 256-position block hi
+// of its chunk (16 first-stage groups per tile in both pair orders), and the
+// second stage's group is hi * 16 + g2.
 __host__ __device__ inline int64_t sp_block_row2(const SpArgs& a, int64_t gid0, int g2, int j2) {
-  const int64_t hi = ((uint32_t)gid0 % (uint32_t)a.ngc) / (uint32_t)a.S;
+  const int64_t hi = ((uint32_t)gid0 % (uint32_t)a.ngc) / (uint32_t)a.gw;
   const int64_t c2 = a.mode == BRQ_PER_GROUP ? hi * a.b + g2 : 0;
   return (c2 * a.b2 + j2) * a.b2;
 }

@@ -170,16 +170,19 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.bs = (a.b + 3) & ~3;
     a.gw = kSpThreads / a.bp;
     if (a.gw * a.bs > kSpLineFloats) a.gw = kSpLineFloats / a.bs;
-    // a forward right-side pair (16, S = 16) then (16, 1) runs in one launch:
-    // the tile is one block of 256 consecutive positions
-    const bool pair = !inverse && side == 0 && i + 1 < L.n && L.b[si] == 16 &&
-                      L.b[si + 1] == 16 && L.S[si] == 16 && L.S[si + 1] == 1 &&
-                      (p->mode == BRQ_HADAMARD ||
-                       reinterpret_cast<uintptr_t>(p->blk + p->blk_off[L.t[si + 1]]) % 16 == 0);
+    // a right-side pair runs in one launch, the tile one block of 256
+    // consecutive positions: forward (16, S = 16) then (16, 1), inverse
+    // (16, 1) then (16, S = 16) (the transposed blocks)
+    const int sn = inverse ? si - 1 : si + 1;  // the next stage
+    const float* base = inverse ? p->blkT : p->blk;
+    const bool pair = side == 0 && i + 1 < L.n && L.b[si] == 16 && L.b[sn] == 16 &&
+                      L.S[si] == (inverse ? 1 : 16) && L.S[sn] == (inverse ? 16 : 1) &&
+                      (p->mode == BRQ_HADAMARD || reinterpret_cast<uintptr_t>(base + p->blk_off[L.t[sn]]) % 16 == 0);
     if (pair) {
-      a.gw = (int)L.S[si];
-      a.b2 = L.b[si + 1];
-      a.blk2 = p->mode == BRQ_HADAMARD ? nullptr : p->blk + p->blk_off[L.t[si + 1]];
+      a.gw = 16;
+      a.b2 = L.b[sn];
+      a.inv2 = inverse ? 1 : 0;
+      a.blk2 = p->mode == BRQ_HADAMARD ? nullptr : base + p->blk_off[L.t[sn]];
     }
     a.mode = p->mode;
     a.S = L.S[si];
@@ -193,7 +196,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
                 : (inverse ? p->blkT : p->blk) + p->blk_off[L.t[si]];
     a.blk_vec = a.blk && a.b % 4 == 0 && reinterpret_cast<uintptr_t>(a.blk) % 16 == 0;
     a.sign_in = (!inverse && i == 0 && signs_here) ? p->signs : nullptr;
-    a.sign_out = (inverse && i == L.n - 1 && signs_here) ? p->signs : nullptr;
+    a.sign_out = (inverse && i + (pair ? 1 : 0) == L.n - 1 && signs_here) ? p->signs : nullptr;
     a.src = i == 0 ? x : mid;
     a.src_t = i == 0 ? xt : BRQ_F32;
     a.ld_src = i == 0 ? ldx : ldm;
@@ -206,7 +209,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     if (!rows_kernel && !lanes_kernel && sp_blocks(a) >= ((int64_t)1 << 31)) return BRQ_ERR_UNSUPPORTED;  // grid
     char name[64];
     if (pair)
-      snprintf(name, sizeof name, "stage R(%d,%d) S%lld", a.b, a.b2, (long long)a.S);
+      snprintf(name, sizeof name, "stage R%s(%d,%d) S%lld", inverse ? "^T" : "", a.b, a.b2, (long long)a.S);
     else
       snprintf(name, sizeof name, "stage %s%s(%d) S%lld", side == 0 ? "R" : "L",
                inverse ? "^T" : "", a.b, (long long)a.S);

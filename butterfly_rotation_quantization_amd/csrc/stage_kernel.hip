@@ -177,9 +177,10 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   }
   __syncthreads();  // every input read
   if (act) {  // a pair's first stage leaves its outputs in position order
+    const bool swap = a.b2 && !a.inv2;
 #pragma unroll
     for (int l = 0; l < kSpLines; ++l)
-      if (l < nl) buf[a.b2 ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j)] = acc[l];
+      if (l < nl) buf[swap ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j)] = acc[l];
   }
   __syncthreads();
 
@@ -202,20 +203,33 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
         w2[4 * k4 + 3] = q.w;
       }
     }
+    if (a.inv2) {  // members of column g2: slots (k2, g2)
 #pragma unroll
-    for (int l = 0; l < kSpLines; ++l) {
-      if (l < nl) {
-        const float* xr = buf + sp_lds(a, l, g2, 0);
-        float s2 = 0.f;
+      for (int l = 0; l < kSpLines; ++l) {
+        if (l < nl) {
+          const float* xr = buf + sp_lds(a, l, 0, g2);
+          float s2 = 0.f;
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * k4);
-          s2 = fmaf(w2[4 * k4 + 0], xv.x, s2);
-          s2 = fmaf(w2[4 * k4 + 1], xv.y, s2);
-          s2 = fmaf(w2[4 * k4 + 2], xv.z, s2);
-          s2 = fmaf(w2[4 * k4 + 3], xv.w, s2);
+          for (int k = 0; k < 16; ++k) s2 = fmaf(w2[k], xr[16 * k], s2);
+          acc[l] = s2;
         }
-        acc[l] = s2;
+      }
+    } else {
+#pragma unroll
+      for (int l = 0; l < kSpLines; ++l) {
+        if (l < nl) {
+          const float* xr = buf + sp_lds(a, l, g2, 0);
+          float s2 = 0.f;
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * k4);
+            s2 = fmaf(w2[4 * k4 + 0], xv.x, s2);
+            s2 = fmaf(w2[4 * k4 + 1], xv.y, s2);
+            s2 = fmaf(w2[4 * k4 + 2], xv.z, s2);
+            s2 = fmaf(w2[4 * k4 + 3], xv.w, s2);
+          }
+          acc[l] = s2;
+        }
       }
     }
     __syncthreads();  // every first-stage output read

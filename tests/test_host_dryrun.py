@@ -203,12 +203,13 @@ def test_stage_pass_launches(dl, radix, mode, lines, chunks):
     radices = radix if mode != "hadamard" else (16,) * (nst - 1) + (d // 16 ** (nst - 1),)
     if mode == "hadamard" and d % 16 ** (nst - 1) == 0 and 16 ** nst != d:
         radices = (d // 16 ** (nst - 1),) + (16,) * (nst - 1)
-    # forward right-side rotations run a trailing (16, 16) pair as one launch
-    fwd = nst - (1 if len(radices) >= 2 and radices[-1] == 16 and radices[-2] == 16 else 0)
+    # right-side rotations run a trailing (16, 16) pair (forward) or a
+    # leading one (inverse) as one launch
+    pairs = nst - (1 if len(radices) >= 2 and radices[-1] == 16 and radices[-2] == 16 else 0)
     for inverse in (False, True):
         for xt, yt in ((2, 2), (1, 0), (0, 1)):
             _rotate(dl, p, 0, lines, chunks * d, xt, yt, inverse=inverse)
-            assert dl.brq_dryrun_launches() == (nst if inverse else fwd)
+            assert dl.brq_dryrun_launches() == pairs
         if d <= 8192:
             _rotate(dl, p, 1, d, lines, 1, 1, inverse=inverse)
             assert dl.brq_dryrun_launches() == nst
