@@ -254,12 +254,16 @@ brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* 
  *   x:      device [T][ldx] activations, xt F16 or BF16 (16-byte aligned rows
  *           when right is NULL).
  *   codes, scales: device, as brq_rotate_quantize_pack wrote them for an
- *           [m][n] weight (4-byte aligned); q: that call's quantizer (ABSMAX).
+ *           [m][n] weight (4-byte aligned); q: that call's quantizer (ABSMAX,
+ *           groups of 64 or 128).  With 16-byte aligned codes and n a
+ *           multiple of 512 the product streams the weight through LDS;
+ *           otherwise a slower kernel reads it directly (same results to
+ *           the float32 rounding of the group sums).
  *   y:      device [T][ldy] of type yt.
  *   ws:     device workspace of brq_qlinear_workspace_bytes(...) bytes.
- * m must be a multiple of 64.  Asynchronous on `stream`.  Errors:
- * INVALID_ARGUMENT (dtypes, shapes, NULLs, q not ABSMAX), UNSUPPORTED (m),
- * ALIGNMENT, WORKSPACE, HIP. */
+ * m must be a multiple of 256 for T <= 16 and of 128 above.  Asynchronous
+ * on `stream`.  Errors: INVALID_ARGUMENT (dtypes, shapes, NULLs, q not
+ * ABSMAX), UNSUPPORTED (m, group), ALIGNMENT, WORKSPACE, HIP. */
 size_t brq_qlinear_workspace_bytes(const brq_plan* left, const brq_plan* right, const brq_quant* q,
                                    int64_t T, int64_t m, int64_t n);
 brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* x, int32_t xt,
