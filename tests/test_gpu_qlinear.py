@@ -128,3 +128,33 @@ def test_qlinear_70b_down_proj(T_):
                     to_dev(alpha, "f32"), m, n, bits, group)
     _check(from_dev(y), xs, "f16", orc_plan(Ls), orc_plan(Rs), codes, alpha, bits, group, "f16",
            f"70B T={T_}")
+
+
+@pytest.mark.parametrize("T_", [1, 37])
+def test_qlinear_direct_kernel_matches_stream(T_):
+    """Codes 4 bytes off a 16-byte boundary take the direct kernel, aligned
+    codes the streaming one.  Both form each group's sum with the same MFMA
+    steps on the same operands and add a split's groups in the same order,
+    so the two outputs agree bit for bit (and the aligned one with the
+    oracle)."""
+    import butterfly_rotation_quantization_amd as brq
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(90 + T_)
+    m, n, bits, group = 512, 2048, 2, 64
+    codes, alpha, x = _case(rng, T_, m, n, bits, group)
+    xs = S.to_storage(x, "f16")
+    Ls = S.random_plan(rng, (32, 16), "per_group")
+    Rs = S.random_plan(rng, (8, 16, 16), "per_group")
+    announce(f"qlinear direct vs stream T={T_}")
+    U, V = lib_plan(Ls), lib_plan(Rs)
+    xd, sd = to_dev(xs, "f16"), to_dev(alpha, "f32")
+    aligned = to_dev(codes, "u8")
+    buf = torch.zeros(codes.size + 16, dtype=torch.uint8, device="cuda")
+    shifted = buf[4:4 + codes.size].view(m, -1)
+    shifted.copy_(aligned)
+    assert aligned.data_ptr() % 16 == 0 and shifted.data_ptr() % 16 == 4
+    y1 = brq.qlinear(U, V, xd, aligned, sd, m, n, bits, group)
+    y2 = brq.qlinear(U, V, xd, shifted, sd, m, n, bits, group)
+    assert torch.equal(y1, y2)
+    _check(from_dev(y1), xs, "f16", orc_plan(Ls), orc_plan(Rs), codes, alpha, bits, group, "f16",
+           f"direct vs stream T={T_}")
