@@ -674,8 +674,9 @@ class DecodeLinear(Workload):
 
 
 class HarpBuild(Workload):
-    """HARP blocks built on the device from int8 parameters (brq_harp_blocks):
-    every stage of a left and a right schedule, one launch per stage."""
+    """HARP blocks built on the device from int8 parameters: every stage of a
+    left and a right schedule in one brq_harp_blocks_batch call (the stages of
+    radix 3..32 share one launch, others launch alone)."""
     unit, higher_is_better, dtype = "us", False, "f64"
 
     def __init__(self, name, metric, sides):
@@ -701,8 +702,8 @@ class HarpBuild(Workload):
                                   torch.empty((ng, b, b), dtype=torch.float32, device=dev)))
 
     def step(self, i):
-        for b, _, _, q, base, out in self.jobs:
-            self.brq.harp_blocks(b, q, 0.004, base, out, stream=self.stream)
+        self.brq.harp_blocks_batch([(b, q, 0.004, base, out) for b, _, _, q, base, out in self.jobs],
+                                   stream=self.stream)
 
     def value(self, ms):
         return ms * 1e3
@@ -723,6 +724,9 @@ class HarpBuild(Workload):
                    for b, _, _, _, base, out in self.jobs)
 
     def kernel_cost(self, name):
+        if name.endswith("batch"):  # every job of radix 3..32 in the one launch
+            costs = [self._cost(bb, out.shape[0]) for bb, *_, out in self.jobs if 3 <= bb <= 32]
+            return sum(c[0] for c in costs), sum(c[1] for c in costs), "alu64"
         b = int(re.search(r"b(\d+)$", name).group(1))
         costs = [self._cost(bb, out.shape[0]) for bb, *_, out in self.jobs if bb == b]
         n = len(costs)

@@ -35,7 +35,7 @@ EXPORTED = (
     "brq_plan_destroy", "brq_plan_dim", "brq_workspace_bytes", "brq_rotate",
     "brq_rotate_inverse", "brq_rotate_quantize_pack", "brq_dequant_unrotate",
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
-    "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_plan_create_harp",
+    "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_harp_blocks_batch", "brq_plan_create_harp",
     "brq_plan_serialize", "brq_plan_deserialize", "brq_requant_workspace_bytes", "brq_requant",
     "brq_qlinear_workspace_bytes", "brq_qlinear",
 )
@@ -121,6 +121,9 @@ def bind(lib):
     if hasattr(lib, "brq_harp_blocks"):
         lib.brq_harp_blocks.argtypes = [i32, i64, vp, ctypes.c_float, vp, vp, vp]
         lib.brq_harp_blocks.restype = i32
+    if hasattr(lib, "brq_harp_blocks_batch"):
+        lib.brq_harp_blocks_batch.argtypes = [i32, ctypes.POINTER(HarpJob), vp]
+        lib.brq_harp_blocks_batch.restype = i32
         lib.brq_plan_create_harp.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, vp, vp, vp]
         lib.brq_plan_create_harp.restype = i32
     if hasattr(lib, "brq_requant"):
@@ -307,6 +310,23 @@ def harp_blocks(b: int, theta_q, scale: float, base=None, out=None, stream=None)
     check(lib().brq_harp_blocks(int(b), int(ng), _ptr(theta_q), float(scale),
                                 None if base is None else _ptr(base), _ptr(out), _stream(stream)))
     return out
+
+
+class HarpJob(ctypes.Structure):
+    """brq_harp_job: one stage's blocks for brq_harp_blocks_batch."""
+    _fields_ = [("b", ctypes.c_int32), ("ngroups", ctypes.c_int64), ("theta_q", ctypes.c_void_p),
+                ("scale", ctypes.c_float), ("base", ctypes.c_void_p), ("blocks", ctypes.c_void_p)]
+
+
+def harp_blocks_batch(jobs, stream=None):
+    """Several stages' blocks in one call (brq_harp_blocks_batch): jobs is a
+    list of (b, theta_q, scale, base or None, out) with device tensors as for
+    harp_blocks (out a device float32 [ngroups, b, b])."""
+    arr = (HarpJob * max(1, len(jobs)))()
+    for i, (b, theta_q, scale, base, out) in enumerate(jobs):
+        arr[i] = HarpJob(int(b), int(theta_q.shape[0]), _ptr(theta_q), float(scale),
+                         None if base is None else _ptr(base), _ptr(out))
+    check(lib().brq_harp_blocks_batch(len(jobs), arr, _stream(stream)))
 
 
 def rotate(plan: Plan, x, y=None, side="right", ws=None, stream=None, inverse=False):

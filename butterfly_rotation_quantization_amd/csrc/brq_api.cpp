@@ -706,6 +706,69 @@ brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const in
   return BRQ_OK;
 }
 
+namespace {
+brq_status harp_job_check(int32_t b, int64_t ngroups, const int8_t* theta_q, float scale, const float* base,
+                          const float* blocks) {
+  if (b < 2 || b > 64) return fail(BRQ_ERR_INVALID_ARGUMENT, "radix %d is not in 2..64", b);
+  if (ngroups < 0 || ngroups >= ((int64_t)1 << 31))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "ngroups %lld is not in 0..2^31-1", (long long)ngroups);
+  if (!base && !is_pow2(b))
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "radix %d needs a base mixer (not a power of two)", b);
+  if (!std::isfinite(scale)) return fail(BRQ_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (ngroups > 0 && (!theta_q || !blocks)) return fail(BRQ_ERR_INVALID_ARGUMENT, "theta_q or blocks is NULL");
+  return BRQ_OK;
+}
+}  // namespace
+
+brq_status brq_harp_blocks_batch(int32_t n_jobs, const brq_harp_job* jobs, void* stream) {
+  g_last_error.clear();
+  if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad job list");
+  for (int i = 0; i < n_jobs; ++i) {
+    const brq_harp_job& j = jobs[i];
+    const brq_status st = harp_job_check(j.b, j.ngroups, j.theta_q, j.scale, j.base, j.blocks);
+    if (st != BRQ_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // batchable jobs, largest radix first (their long eliminations start first)
+  std::vector<int> order;
+  for (int i = 0; i < n_jobs; ++i)
+    if (jobs[i].ngroups > 0) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return jobs[x].b > jobs[y].b; });
+  HarpBatch bt;
+  std::memset(&bt, 0, sizeof bt);
+  auto flush = [&]() -> brq_status {
+    if (bt.n == 0) return BRQ_OK;
+    const int tok = prof_begin("harp blocks batch", s);
+    const hipError_t e = launch_harp_batch(bt, s);
+    prof_end(tok, s);
+    std::memset(&bt, 0, sizeof bt);
+    return e == hipSuccess ? BRQ_OK : hip_fail(e, "HARP batch launch");
+  };
+  for (int i : order) {
+    const brq_harp_job& j = jobs[i];
+    if (!harp_batchable(j.b)) {
+      const brq_status st = brq_harp_blocks(j.b, j.ngroups, j.theta_q, j.scale, j.base, j.blocks, stream);
+      if (st != BRQ_OK) return st;
+      continue;
+    }
+    if (bt.n == kHpMaxJobs || bt.first[bt.n] + j.ngroups >= ((int64_t)1 << 31)) {
+      const brq_status st = flush();
+      if (st != BRQ_OK) return st;
+    }
+    HarpArgs& a = bt.job[bt.n];
+    a.b = j.b;
+    a.np = harp_params(j.b);
+    a.ngroups = j.ngroups;
+    a.theta = j.theta_q;
+    a.scale = j.scale;
+    a.base = j.base;
+    a.out = j.blocks;
+    bt.first[bt.n + 1] = bt.first[bt.n] + j.ngroups;
+    ++bt.n;
+  }
+  return flush();
+}
+
 brq_status brq_harp_blocks(int32_t b, int64_t ngroups, const int8_t* theta_q, float scale,
                            const float* base, float* blocks, void* stream) {
   g_last_error.clear();
@@ -772,15 +835,18 @@ brq_status brq_plan_create_harp(brq_plan** out, int32_t d, int32_t n_stages, con
   if (e == hipSuccess) e = rt_copy_to_device(dth, theta_q, (size_t)nparams);
   if (e == hipSuccess && bases) e = rt_copy_to_device(dbase, bases, (size_t)nbase * sizeof(float));
   brq_status st = BRQ_OK;
-  int64_t poff = 0, boff = 0, goff = 0;
-  for (int t = 0; e == hipSuccess && st == BRQ_OK && t < n_stages; ++t) {
-    const int b = radix[t];
-    const int64_t ng = d / b;
-    st = brq_harp_blocks(b, ng, dth + poff, scales[t], bases ? dbase + goff : nullptr, dblk + boff,
-                         nullptr);
-    poff += ng * harp_params(b);
-    boff += ng * b * b;
-    goff += (int64_t)b * b;
+  if (e == hipSuccess) {  // every stage in one batch
+    std::vector<brq_harp_job> jobs((size_t)n_stages);
+    int64_t poff = 0, boff = 0, goff = 0;
+    for (int t = 0; t < n_stages; ++t) {
+      const int b = radix[t];
+      const int64_t ng = d / b;
+      jobs[t] = brq_harp_job{b, ng, dth + poff, scales[t], bases ? dbase + goff : nullptr, dblk + boff};
+      poff += ng * harp_params(b);
+      boff += ng * b * b;
+      goff += (int64_t)b * b;
+    }
+    st = brq_harp_blocks_batch(n_stages, jobs.data(), nullptr);
   }
   if (e == hipSuccess && st == BRQ_OK) e = rt_copy_to_host(hblk.data(), dblk, (size_t)nblk * sizeof(float));
   rt_free(dth);

@@ -20,6 +20,7 @@ static std::string g_violation;
 static long long g_launches = 0;
 static long long g_rows_launches = 0;  // of those, left-side stages by whole rows
 static long long g_lanes_launches = 0;  // right-side stages with groups in lanes
+static long long g_harp_batches = 0;    // batched HARP block launches
 
 static bool violation(const char* fmt, long long a, long long b) {
   if (g_violation.empty()) {
@@ -150,12 +151,14 @@ extern "C" {
 const char* brq_dryrun_violation(void) { return brq::g_violation.c_str(); }
 long long brq_dryrun_launches(void) { return brq::g_launches; }
 long long brq_dryrun_rows_launches(void) { return brq::g_rows_launches; }
+long long brq_dryrun_harp_batches(void) { return brq::g_harp_batches; }
 long long brq_dryrun_lanes_launches(void) { return brq::g_lanes_launches; }
 void brq_dryrun_reset(void) {
   brq::g_violation.clear();
   brq::g_launches = 0;
   brq::g_rows_launches = 0;
   brq::g_lanes_launches = 0;
+  brq::g_harp_batches = 0;
 }
 }
 
@@ -811,6 +814,35 @@ hipError_t launch_harp(const HarpArgs& a, hipStream_t) {
   for (int p = 0; p < a.np; ++p)
     if (used[p] != 1) return violation("HARP parameter %lld unused", p, 0), hipErrorInvalidValue;
   if (2 * b > 2 * kHpThreads) return violation("HARP columns per lane (b %lld)", b, 0), hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_harp_batch(const HarpBatch& a, hipStream_t s) {
+  if (a.n < 1 || a.n > kHpMaxJobs || a.first[0] != 0)
+    return violation("HARP batch of %lld jobs", a.n, 0), hipErrorInvalidValue;
+  for (int j = 0; j < a.n; ++j) {
+    const HarpArgs& h = a.job[j];
+    if (!harp_batchable(h.b) || h.ngroups < 1 || a.first[j + 1] != a.first[j] + h.ngroups)
+      return violation("HARP batch job %lld (b %lld)", j, h.b), hipErrorInvalidValue;
+    const hipError_t e = launch_harp(h, s);  // the per-block checks
+    --g_launches;
+    if (e != hipSuccess) return e;
+    for (int k = 0; k < j; ++k) {  // outputs of distinct jobs do not overlap
+      const HarpArgs& o = a.job[k];
+      const float *lo1 = h.out, *hi1 = h.out + h.ngroups * h.b * h.b;
+      const float *lo2 = o.out, *hi2 = o.out + o.ngroups * o.b * o.b;
+      if (lo1 < hi2 && lo2 < hi1) return violation("HARP batch outputs %lld and %lld overlap", k, j), hipErrorInvalidValue;
+    }
+  }
+  if (a.first[a.n] >= ((int64_t)1 << 31)) return violation("HARP batch grid %lld", a.first[a.n], 0), hipErrorInvalidValue;
+  // every workgroup finds its job: the scan the kernel does
+  for (int64_t w : {(int64_t)0, a.first[a.n] - 1}) {
+    int j = 0;
+    while (j + 1 < a.n && w >= a.first[j + 1]) ++j;
+    if (w < a.first[j] || w >= a.first[j + 1]) return violation("HARP batch block %lld", w, 0), hipErrorInvalidValue;
+  }
+  ++g_launches;
+  ++g_harp_batches;
   return hipSuccess;
 }
 

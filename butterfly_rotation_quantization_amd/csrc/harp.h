@@ -40,4 +40,18 @@ __host__ __device__ inline size_t harp_lds_bytes(int b) {
 
 hipError_t launch_harp(const HarpArgs& a, hipStream_t s);
 
+// Several stages in one launch (3 <= b <= 32 each, the register kernel's
+// range): workgroup w builds block w - first[j] of job j, first[j] <= w <
+// first[j + 1].  The stages of a plan are independent, so one launch lets
+// the few long radix-32 eliminations overlap the many short ones instead of
+// running stage after stage.
+constexpr int kHpMaxJobs = 16;
+struct HarpBatch {
+  int n;
+  HarpArgs job[kHpMaxJobs];
+  int64_t first[kHpMaxJobs + 1];
+};
+__host__ __device__ inline bool harp_batchable(int b) { return b >= 3 && b <= 32; }
+hipError_t launch_harp_batch(const HarpBatch& a, hipStream_t s);
+
 }  // namespace brq

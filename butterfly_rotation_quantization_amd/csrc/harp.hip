@@ -74,10 +74,8 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 // pivot broadcasts column i from lane i with readlane; no LDS, no barrier
 // until Q is staged for the product.
 template <int MAXB>
-__global__ __launch_bounds__(kHpThreads) void harp_reg_kernel(HarpArgs a) {
-  __shared__ double q_lds[MAXB * (MAXB + 1)];
+__device__ __forceinline__ void harp_reg_block(const HarpArgs& a, int64_t g, double* q_lds) {
   const int b = a.b, lane = threadIdx.x;
-  const int64_t g = blockIdx.x;
   const int8_t* th = a.theta + g * a.np;
   const double sc = (double)a.scale;
   const int c = lane < MAXB ? lane : lane - MAXB;  // column within its half
@@ -120,7 +118,32 @@ __global__ __launch_bounds__(kHpThreads) void harp_reg_kernel(HarpArgs a) {
   }
 }
 
+template <int MAXB>
+__global__ __launch_bounds__(kHpThreads) void harp_reg_kernel(HarpArgs a) {
+  __shared__ double q_lds[MAXB * (MAXB + 1)];
+  harp_reg_block<MAXB>(a, blockIdx.x, q_lds);
+}
+
+__global__ __launch_bounds__(kHpThreads) void harp_batch_kernel(HarpBatch bt) {
+  __shared__ double q_lds[32 * 33];
+  const int64_t w = blockIdx.x;
+  int j = 0;
+  while (j + 1 < bt.n && w >= bt.first[j + 1]) ++j;  // uniform over the workgroup
+  const HarpArgs& a = bt.job[j];
+  const int64_t g = w - bt.first[j];
+  if (a.b <= 4) harp_reg_block<4>(a, g, q_lds);
+  else if (a.b <= 8) harp_reg_block<8>(a, g, q_lds);
+  else if (a.b <= 16) harp_reg_block<16>(a, g, q_lds);
+  else harp_reg_block<32>(a, g, q_lds);
+}
+
 }  // namespace
+
+hipError_t launch_harp_batch(const HarpBatch& a, hipStream_t s) {
+  if (a.n < 1 || a.n > kHpMaxJobs || a.first[a.n] == 0) return a.n == 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(harp_batch_kernel, dim3((unsigned)a.first[a.n]), dim3(kHpThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_harp(const HarpArgs& a, hipStream_t s) {
   if (a.ngroups == 0) return hipSuccess;

@@ -124,6 +124,27 @@ brq_status brq_harp_blocks(int32_t b, int64_t ngroups, const int8_t* theta_q, fl
                            const float* base, float* blocks, void* stream);
 
 /*
+ * Several brq_harp_blocks calls at once (the stages of a plan, [HARP]
+ * section 2.2; they are independent): job i builds jobs[i].ngroups blocks
+ * of radix jobs[i].b exactly as brq_harp_blocks(b, ngroups, theta_q, scale,
+ * base, blocks) would, bit for bit.  Jobs of radix 3..32 share launches (up
+ * to 16 jobs each), so a stage of few large blocks overlaps stages of many
+ * small ones; radix 2 and radices above 32 launch on their own.  jobs is a
+ * host array of n_jobs entries (device pointers inside, as brq_harp_blocks);
+ * outputs must not overlap.  Asynchronous on `stream`.  Errors: as
+ * brq_harp_blocks for each job (nothing is launched if one is invalid),
+ * INVALID_ARGUMENT (n_jobs < 0, jobs NULL with n_jobs > 0), HIP. */
+typedef struct brq_harp_job {
+  int32_t b;
+  int64_t ngroups;
+  const int8_t* theta_q;
+  float scale;
+  const float* base;
+  float* blocks;
+} brq_harp_job;
+brq_status brq_harp_blocks_batch(int32_t n_jobs, const brq_harp_job* jobs, void* stream);
+
+/*
  * A per-group plan from HARP parameters: stage t's blocks are
  * brq_harp_blocks(radix[t], d / radix[t], ...) of its parameters.
  *   theta_q: host int8, the stages' parameters one after the other, each

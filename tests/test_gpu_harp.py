@@ -167,3 +167,36 @@ def test_plan_image_rotates_identically(kind):
     a = brq.rotate(p, x, side="right")
     b = brq.rotate(q, x, side="right")
     assert bool((a == b).all())
+
+
+def test_harp_blocks_batch_equals_single_calls():
+    """brq_harp_blocks_batch builds every job as brq_harp_blocks does (the
+    same elimination per block), bit for bit: radices 3..32 in one launch,
+    2 and above 32 on their own, an empty job among them; sampled blocks
+    against the oracle as well."""
+    import butterfly_rotation_quantization_amd as brq
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(606)
+    spec = [(16, 1792, 0.004), (2, 37, 0.3), (32, 256, 0.002), (7, 300, 0.01), (43, 5, 0.005),
+            (64, 3, 0.003), (3, 50, 0.05), (16, 0, 0.01)]
+    announce("harp blocks batch of 8 jobs")
+    jobs, singles, refs = [], [], []
+    for b, ng, sc in spec:
+        tq = _theta(rng, ng * OH.n_params(b)).reshape(ng, OH.n_params(b))
+        base = _base(rng, b)
+        th_dev = torch.from_numpy(tq).cuda()
+        base_dev = None if base is None else torch.from_numpy(base).cuda()
+        out = torch.full((ng, b, b), float("nan"), dtype=torch.float32, device="cuda")
+        jobs.append((b, th_dev, sc, base_dev, out))
+        singles.append(brq.harp_blocks(b, th_dev, sc, base_dev))
+        refs.append((tq, base))
+    brq.harp_blocks_batch(jobs)
+    for (b, _, sc, _, out), one, (tq, base) in zip(jobs, singles, refs):
+        assert torch.equal(out, one), f"b={b}"
+        ng = out.shape[0]
+        got = from_dev(out)
+        for c in (rng.choice(ng, size=min(ng, 4), replace=False) if ng else []):
+            npar = OH.n_params(b)
+            ref = OH.stage_blocks(b, 1, tq.reshape(-1)[c * npar:(c + 1) * npar], sc,
+                                  None if base is None else base.astype(np.float64))[0]
+            check_blocks(got[c], ref, f"batch b={b} c={c}")

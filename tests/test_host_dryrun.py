@@ -282,8 +282,40 @@ def test_plan_create_harp_walk(dl, radix, with_base):
                                  sc.ctypes.data, None if bases is None else bases.ctypes.data,
                                  None)
     _ok(dl, st, f"harp plan {radix}")
-    assert dl.brq_dryrun_launches() == len(radix)
+    # the stages of radix 3..32 share one launch, the others go one by one
+    batched = [b for b in radix if 3 <= b <= 32]
+    assert dl.brq_dryrun_launches() == (1 if batched else 0) + len(radix) - len(batched)
+    assert dl.brq_dryrun_harp_batches() == (1 if batched else 0)
     dl.brq_plan_destroy(h)
+
+
+def _jobs(spec):
+    arr = (brq.HarpJob * len(spec))()
+    out = 0x100000
+    for i, (b, ng) in enumerate(spec):
+        arr[i] = brq.HarpJob(b, ng, 0x1000, 0.05, None if b & (b - 1) == 0 else 0x2000, out)
+        out += 4 * ng * b * b
+    return arr
+
+
+def test_harp_blocks_batch_walk(dl):
+    """Radix 3..32 jobs share launches of at most 16 jobs; radix 2 and above
+    32 launch alone; empty jobs launch nothing; one invalid job launches
+    nothing at all."""
+    dl.brq_dryrun_reset()
+    spec = [(16, 1792), (2, 5), (32, 256), (7, 4096), (43, 3), (16, 0), (64, 2), (3, 9)]
+    _ok(dl, dl.brq_harp_blocks_batch(len(spec), _jobs(spec), None), "batch")
+    assert dl.brq_dryrun_harp_batches() == 1
+    assert dl.brq_dryrun_launches() == 1 + 3
+    dl.brq_dryrun_reset()
+    many = [(16, 10)] * 20
+    _ok(dl, dl.brq_harp_blocks_batch(len(many), _jobs(many), None), "20 jobs")
+    assert dl.brq_dryrun_harp_batches() == 2 and dl.brq_dryrun_launches() == 2
+    dl.brq_dryrun_reset()
+    bad = _jobs([(16, 10), (7, 10)])
+    bad[1].base = None  # radix 7 without a base mixer
+    assert dl.brq_harp_blocks_batch(2, bad, None) == 1
+    assert dl.brq_dryrun_launches() == 0
 
 
 # Plan images: serialise, deserialise, serialise again gives the same bytes
