@@ -712,23 +712,28 @@ class HarpBuild(Workload):
         return sum(out.numel() for *_, out in self.jobs)
 
     @staticmethod
-    def _cost(b, ng):
+    def _cost(b, ng, sylvester):
         npar = 1 if b == 2 else b * (b - 1) // 2
         # Gauss-Jordan on [I - A | I + A] (b pivots x 2b columns x b rows, an
-        # FMA each) and the product Q G (b^3 FMA): 6 b^3 flop per block
-        flops = 6 * b ** 3 if b > 2 else 16  # Givens: Q G only
-        return ng * (npar + 4 * b * b), ng * flops
+        # FMA each: 4 b^3 flop) and the product Q G: b^3 FMA for a given G,
+        # a Walsh-Hadamard transform of each row (b^2 log2 b additions) for
+        # the Sylvester one
+        if b == 2:
+            return ng * (npar + 4 * b * b), ng * 16  # Givens: Q G only
+        prod = b * b * (b.bit_length() - 1) if sylvester else 2 * b ** 3
+        return ng * (npar + 4 * b * b), ng * (4 * b ** 3 + prod)
 
     def alg_bytes(self):
-        return sum(self._cost(b, out.shape[0])[0] + (0 if base is None else 4 * b * b)
+        return sum(self._cost(b, out.shape[0], base is None)[0] + (0 if base is None else 4 * b * b)
                    for b, _, _, _, base, out in self.jobs)
 
     def kernel_cost(self, name):
         if name.endswith("batch"):  # every job of radix 3..32 in the one launch
-            costs = [self._cost(bb, out.shape[0]) for bb, *_, out in self.jobs if 3 <= bb <= 32]
+            costs = [self._cost(bb, out.shape[0], base is None) for bb, _, _, _, base, out in self.jobs
+                     if 3 <= bb <= 32]
             return sum(c[0] for c in costs), sum(c[1] for c in costs), "alu64"
         b = int(re.search(r"b(\d+)$", name).group(1))
-        costs = [self._cost(bb, out.shape[0]) for bb, *_, out in self.jobs if bb == b]
+        costs = [self._cost(bb, out.shape[0], base is None) for bb, _, _, _, base, out in self.jobs if bb == b]
         n = len(costs)
         return (sum(c[0] for c in costs) // n, sum(c[1] for c in costs) // n, "alu64")
 

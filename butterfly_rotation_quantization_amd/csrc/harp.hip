@@ -107,6 +107,32 @@ __device__ __forceinline__ void harp_reg_block(const HarpArgs& a, int64_t g, dou
   __syncthreads();
   const double hs = 1.0 / sqrt((double)b);
   float* out = a.out + g * b * b;
+  if (!a.base && b == MAXB && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0) {
+    // Sylvester G = H_b / sqrt(b) (b a power of two, so b is MAXB): row j of
+    // Q G is the Walsh-Hadamard transform of row j of Q, b log2 b additions
+    // in registers instead of b^2 products; lane j takes row j and stores it
+    // as float4s (b^2 floats per block keep every row 16-byte aligned)
+    if (lane < MAXB) {
+      double r[MAXB];
+#pragma unroll
+      for (int q = 0; q < MAXB; ++q) r[q] = q_lds[lane * (MAXB + 1) + q];
+#pragma unroll
+      for (int h = 1; h < MAXB; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < MAXB; ++i)
+          if ((i & h) == 0) {
+            const double x = r[i], y = r[i + h];
+            r[i] = x + y;
+            r[i + h] = x - y;
+          }
+      float4* o4 = reinterpret_cast<float4*>(out + lane * MAXB);
+#pragma unroll
+      for (int k = 0; k < MAXB / 4; ++k)
+        o4[k] = make_float4((float)(r[4 * k] * hs), (float)(r[4 * k + 1] * hs), (float)(r[4 * k + 2] * hs),
+                            (float)(r[4 * k + 3] * hs));
+    }
+    return;
+  }
   for (int e = lane; e < b * b; e += kHpThreads) {
     const int j = e / b, k = e - j * b;
     double acc = 0.0;
