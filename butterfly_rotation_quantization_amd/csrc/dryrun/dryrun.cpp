@@ -21,6 +21,7 @@ static long long g_launches = 0;
 static long long g_rows_launches = 0;  // of those, left-side stages by whole rows
 static long long g_lanes_launches = 0;  // right-side stages with groups in lanes
 static long long g_harp_batches = 0;    // batched HARP block launches
+static long long g_pair2_launches = 0;  // two-stage pair launches
 
 static bool violation(const char* fmt, long long a, long long b) {
   if (g_violation.empty()) {
@@ -152,6 +153,7 @@ const char* brq_dryrun_violation(void) { return brq::g_violation.c_str(); }
 long long brq_dryrun_launches(void) { return brq::g_launches; }
 long long brq_dryrun_rows_launches(void) { return brq::g_rows_launches; }
 long long brq_dryrun_harp_batches(void) { return brq::g_harp_batches; }
+long long brq_dryrun_pair2_launches(void) { return brq::g_pair2_launches; }
 long long brq_dryrun_lanes_launches(void) { return brq::g_lanes_launches; }
 void brq_dryrun_reset(void) {
   brq::g_violation.clear();
@@ -159,6 +161,7 @@ void brq_dryrun_reset(void) {
   brq::g_rows_launches = 0;
   brq::g_lanes_launches = 0;
   brq::g_harp_batches = 0;
+  brq::g_pair2_launches = 0;
 }
 }
 
@@ -843,6 +846,47 @@ hipError_t launch_harp_batch(const HarpBatch& a, hipStream_t s) {
   }
   ++g_launches;
   ++g_harp_batches;
+  return hipSuccess;
+}
+
+hipError_t launch_stage_pair2(const P2Args& a, hipStream_t) {
+  ++g_launches;
+  ++g_pair2_launches;
+  const int n = a.bo * a.bi;
+  if (a.bo < 2 || a.bi < 2 || a.bo > 16 || a.bi > 16 || n > 256 || a.sets != 256 / n || a.sets < 1 ||
+      a.lines < 1 || a.lines > kP2Lines || a.Si < 1 || a.d % (n * a.Si))
+    return violation("stage pair geometry (bo %lld, bi %lld)", a.bo, a.bi), hipErrorInvalidValue;
+  const int64_t per_chunk = a.d / (n * a.Si) * a.Si;
+  if (a.nsets % per_chunk || a.ld_src < a.nsets / per_chunk * a.d || a.ld_dst < a.nsets / per_chunk * a.d)
+    return violation("stage pair sets %lld (chunk %lld)", a.nsets, per_chunk), hipErrorInvalidValue;
+  const int64_t cols = a.nsets / per_chunk * a.d;
+  const int64_t blk_o = a.per_group ? a.d / a.bo * a.bo * a.bo : a.bo * a.bo;
+  const int64_t blk_i = a.per_group ? a.d / a.bi * a.bi * a.bi : a.bi * a.bi;
+  std::vector<uint8_t> seen((size_t)cols, 0);
+  const int64_t nb = p2_blocks(a);
+  if (nb >= ((int64_t)1 << 31)) return violation("stage pair grid %lld", nb, 0), hipErrorInvalidValue;
+  for (int64_t blk = 0; blk < nb; ++blk)
+    for (int u = 0; u < 256; ++u) {
+      const int sl = u / n, e = u - sl * n;
+      const int64_t s = blk * a.sets + sl;
+      if (sl >= a.sets || s >= a.nsets) continue;
+      int64_t c, hi, lo;
+      p2_set(a, s, c, hi, lo);
+      const int ea = e / a.bi, eb = e - ea * a.bi, og = e / a.bo, oj = e - og * a.bo;
+      const int64_t pos = p2_pos(a, c, hi, lo, ea, eb);
+      if (pos < 0 || pos >= cols || seen[(size_t)pos]++) return violation("stage pair position %lld", pos, 0), hipErrorInvalidValue;
+      if (pos / a.d != c) return violation("stage pair chunk of %lld", pos, 0), hipErrorInvalidValue;
+      const int64_t ro = p2_row_o(a, hi, lo, og, oj), ri = p2_row_i(a, hi, lo, ea, eb);
+      if (ro < 0 || ro + a.bo > blk_o || ri < 0 || ri + a.bi > blk_i)
+        return violation("stage pair block rows %lld, %lld", ro, ri), hipErrorInvalidValue;
+      // the outer group og mixes positions (k, og), the inner group ea positions (ea, k): same chunk, hi, lo
+      for (int k = 0; k < a.bo; ++k)
+        if (p2_pos(a, c, hi, lo, k, og) / (n * a.Si) != pos / (n * a.Si)) return violation("stage pair set %lld", s, 0), hipErrorInvalidValue;
+      const int lds_max = (sl + 1) * kP2Lines * n;
+      if (lds_max > 256 * kP2Lines) return violation("stage pair LDS %lld", lds_max, 0), hipErrorInvalidValue;
+    }
+  for (size_t i = 0; i < seen.size(); ++i)
+    if (seen[i] != 1) return violation("stage pair position %lld covered %lld times", (int64_t)i, seen[i]), hipErrorInvalidValue;
   return hipSuccess;
 }
 

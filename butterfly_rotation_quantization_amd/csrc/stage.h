@@ -234,6 +234,65 @@ bool sp_rotate_supported(const Plan* p, int side, int64_t rows, int64_t cols);
 brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt, int64_t ldx,
                      void* y, int yt, int64_t ldy, int64_t rows, int64_t cols, void* ws,
                      size_t ws_bytes, hipStream_t s, hipError_t* herr);
+// ---- Two consecutive right-side stages in one launch, for few rows ----------
+//
+// Stages (b_o, S_o) and (b_i, S_i) next to each other in a schedule have
+// S_o = b_i S_i, so position hi (b_o b_i S_i) + a S_o + b S_i + lo of a chunk
+// is element (a, b) of the closed set (hi, lo): the outer stage mixes a for
+// each b, the inner one b for each a.  A workgroup takes sets = 256 / (b_o
+// b_i) consecutive lo of one hi for up to kP2Lines rows; thread (set, g, j)
+// makes output j of group g of each stage, its block rows loaded up front,
+// the set's elements in LDS between the two stages.  Forward runs the outer
+// stage first, inverse (transposed blocks) the inner one.  Used below 8 rows,
+// where the groups-in-lanes kernel does not apply (at 16 rows its two
+// launches beat this one, measured 23 against 30 us on the 70B decode).
+constexpr int kP2Lines = 7;
+struct P2Args {
+  int bo, bi;              // radices of the outer and inner stage (bo * bi <= 256, each <= 16)
+  int64_t Si;              // inner stride (outer: bo's stride bi * Si)
+  int64_t d;               // plan dimension
+  int64_t nsets;           // sets per row: (cols / d) * (d / (bo bi Si)) * Si
+  int sets;                // sets per workgroup
+  int inner_first;         // inverse order
+  int per_group;           // blocks per group (else one shared block per stage)
+  const float* blk_o;      // outer stage blocks [group][j][k] (groups hi Si bi... as in the plan)
+  const float* blk_i;
+  const float* sign_in;    // applied at load (forward, first stage of the plan), or null
+  const float* sign_out;   // applied at store (inverse, first stage of the plan), or null
+  const void* src;
+  int src_t;
+  int64_t ld_src;
+  void* dst;
+  int dst_t;
+  int64_t ld_dst;
+  int64_t lines;           // rows, at most kP2Lines
+};
+// Set s (of the row) -> chunk c, hi, lo.
+__host__ __device__ inline void p2_set(const P2Args& a, int64_t s, int64_t& c, int64_t& hi, int64_t& lo) {
+  const int64_t per_chunk = a.d / (a.bo * a.bi * a.Si) * a.Si;
+  c = s / per_chunk;
+  const int64_t r = s - c * per_chunk;
+  hi = r / a.Si;
+  lo = r - hi * a.Si;
+}
+__host__ __device__ inline int64_t p2_pos(const P2Args& a, int64_t c, int64_t hi, int64_t lo, int ao, int bi_) {
+  return c * a.d + hi * (a.bo * a.bi * a.Si) + (int64_t)ao * (a.bi * a.Si) + (int64_t)bi_ * a.Si + lo;
+}
+// Block row offsets: outer group hi (bi Si) + b Si + lo, inner group
+// (hi bo + a) Si + lo (the stages' own group numbering within the chunk).
+__host__ __device__ inline int64_t p2_row_o(const P2Args& a, int64_t hi, int64_t lo, int b, int j) {
+  const int64_t g = a.per_group ? hi * (a.bi * a.Si) + (int64_t)b * a.Si + lo : 0;
+  return (g * a.bo + j) * a.bo;
+}
+__host__ __device__ inline int64_t p2_row_i(const P2Args& a, int64_t hi, int64_t lo, int ao, int j) {
+  const int64_t g = a.per_group ? (hi * a.bo + ao) * a.Si + lo : 0;
+  return (g * a.bi + j) * a.bi;
+}
+__host__ __device__ inline int64_t p2_blocks(const P2Args& a) {
+  return (a.nsets + a.sets - 1) / a.sets;
+}
+hipError_t launch_stage_pair2(const P2Args& a, hipStream_t s);
+
 // Stages [t_begin, t_end) of the plan only (t_end = -1: to the last), in
 // forward order (inverse: the same range, transposed, last stage first); the
 // signs go with stage 0, so a range that starts later applies none.

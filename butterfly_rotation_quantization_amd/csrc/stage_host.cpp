@@ -162,6 +162,52 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
   const int64_t lines = side == 0 ? rows : cols;
   for (int i = 0; i < L.n; ++i) {
     const int si = inverse ? L.n - 1 - i : i;
+    // two consecutive right-side stages of radix <= 16 (product <= 256) for
+    // fewer than 8 rows: one launch (a trailing forward or leading inverse (16, 16)
+    // at strides 16 and 1 keeps its own pair kernel)
+    if (side == 0 && lines <= kP2Lines && p->mode != BRQ_HADAMARD && i + 1 < L.n) {
+      const int sn = inverse ? si - 1 : si + 1;
+      const int to = si < sn ? si : sn, ti = si < sn ? sn : si;  // outer (larger stride), inner
+      const bool pair16 = L.b[to] == 16 && L.b[ti] == 16 && L.S[to] == 16 && L.S[ti] == 1;
+      if (!pair16 && L.b[to] <= 16 && L.b[ti] <= 16 && L.b[to] * L.b[ti] <= 256) {
+        P2Args q;
+        std::memset(&q, 0, sizeof q);
+        q.bo = L.b[to];
+        q.bi = L.b[ti];
+        q.Si = L.S[ti];
+        q.d = p->d;
+        q.nsets = (cols / p->d) * (p->d / (q.bo * q.bi * q.Si)) * q.Si;
+        q.sets = 256 / (q.bo * q.bi);
+        q.inner_first = inverse ? 1 : 0;
+        q.per_group = p->mode == BRQ_PER_GROUP ? 1 : 0;
+        const float* base = inverse ? p->blkT : p->blk;
+        q.blk_o = base + p->blk_off[L.t[to]];
+        q.blk_i = base + p->blk_off[L.t[ti]];
+        const bool last = i + 1 == L.n - 1;
+        q.sign_in = (!inverse && i == 0 && signs_here) ? p->signs : nullptr;
+        q.sign_out = (inverse && last && signs_here) ? p->signs : nullptr;
+        q.src = i == 0 ? x : mid;
+        q.src_t = i == 0 ? xt : BRQ_F32;
+        q.ld_src = i == 0 ? ldx : ldm;
+        q.dst = last ? y : mid;
+        q.dst_t = last ? yt : BRQ_F32;
+        q.ld_dst = last ? ldy : ldm;
+        q.lines = lines;
+        if (p2_blocks(q) >= ((int64_t)1 << 31)) return BRQ_ERR_UNSUPPORTED;
+        char name[64];
+        snprintf(name, sizeof name, "stage R%s(%d,%d) S%lld", inverse ? "^T" : "", L.b[si], L.b[sn],
+                 (long long)L.S[si]);
+        const int tok = prof_begin(name, s);
+        const hipError_t e = launch_stage_pair2(q, s);
+        prof_end(tok, s);
+        if (e != hipSuccess) {
+          *herr = e;
+          return BRQ_ERR_HIP;
+        }
+        ++i;
+        continue;
+      }
+    }
     SpArgs a;
     std::memset(&a, 0, sizeof a);
     a.side = side;

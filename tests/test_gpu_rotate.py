@@ -185,3 +185,31 @@ def test_right_stages_in_place(radix, mode, rows):
     check_rotation(from_dev(y), ref, "f32", f"in place {radix}")
     xi = brq.rotate_inverse(p, y, side="right")
     check_rotation(from_dev(xi), xs.astype(np.float64), "f32", f"in place inverse {radix}")
+
+
+@pytest.mark.parametrize("radix,mode,rows,chunks", [
+    ((7, 16, 16, 16), "per_group", 1, 1), ((8, 8, 8, 5, 2), "per_group", 3, 1),
+    ((2, 16, 64), "shared", 7, 2), ((3, 5, 7), "per_group", 4, 3), ((16, 4, 16), "per_group", 2, 1),
+])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_right_stage_pairs_few_rows(radix, mode, rows, chunks, dt):
+    """Below 8 rows two consecutive stages of radix <= 16 run as one launch
+    (outer stage first forward, inner first inverse, with the signs at the
+    plan's stage 0): forward and inverse against the oracle."""
+    import butterfly_rotation_quantization_amd as brq
+    side = _side(radix, mode, seed=rows + chunks)
+    d = side.d
+    announce(f"right stage pairs radix={radix} mode={mode} rows={rows} dt={dt}")
+    xs = _input(rows, chunks * d, dt, seed=rows)
+    p = lib_plan(side)
+    brq.profile_reset()
+    brq.profile_enable(True)
+    y = brq.rotate(p, to_dev(xs, dt), side="right")
+    names = list(brq.profile_read())
+    brq.profile_enable(False)
+    assert any("," in n for n in names), names  # a pair launch ran
+    ref = T.apply_right(orc_plan(side), S.storage_to_f64(xs, dt), method=method_for(d))
+    check_rotation(from_dev(y), ref, dt, f"pairs {radix}")
+    xi = brq.rotate_inverse(p, y, side="right")
+    refi = T.apply_right(orc_plan(side), from_dev(y), inverse=True, method=method_for(d))
+    check_rotation(from_dev(xi), refi, dt, f"pairs inverse {radix}")

@@ -187,13 +187,38 @@ def test_rowhad_launches(dl, l2d, rows, cpr):
                 assert dl.brq_dryrun_launches() == 1
 
 
+def _right_launches(radices, lines, mode, inverse):
+    """Launches of a right-side stage pass: in application order, a
+    forward (16, 16) at strides 16, 1 (or its inverse) is one launch; below
+    8 rows of a dense plan, so are two consecutive stages of radix <= 16
+    with a product <= 256; every other stage is a launch of its own."""
+    n = len(radices)
+    S = [int(np.prod(radices[t + 1:])) for t in range(n)]
+    order = list(range(n))[::-1] if inverse else list(range(n))
+    i = launches = 0
+    while i < n:
+        if i + 1 < n:
+            to, ti = sorted((order[i], order[i + 1]))
+            pair16 = radices[to] == 16 and radices[ti] == 16 and S[to] == 16 and S[ti] == 1
+            pair2 = (lines < 8 and mode != "hadamard" and not pair16 and radices[to] <= 16 and
+                     radices[ti] <= 16 and radices[to] * radices[ti] <= 256)
+            if pair16 or pair2:
+                launches += 1
+                i += 2
+                continue
+        launches += 1
+        i += 1
+    return launches
+
+
 # The stage pass: one launch per stage for rotations of few lines (decode-time
 # activations on the right side, a few columns on the left side).
 @pytest.mark.parametrize("radix,mode,lines,chunks", [
     ((7, 16, 16, 16), "per_group", 1, 1), ((7, 16, 16, 16), "per_group", 16, 1),
     ((7, 16, 16, 16), "per_group", 256, 1), ((43, 16, 16), "per_group", 33, 2),
     ((3, 5, 7), "shared", 70, 3), ((2,) * 13, "hadamard", 5, 1), ((64, 2), "per_group", 1024, 1),
-    ((32, 16, 16), "per_group", 9, 1),
+    ((32, 16, 16), "per_group", 9, 1), ((8, 8, 8, 5, 2), "per_group", 3, 1), ((2, 16, 64), "shared", 7, 2),
+    ((3, 5, 7), "per_group", 4, 2),
 ])
 def test_stage_pass_launches(dl, radix, mode, lines, chunks):
     side = S.random_plan(np.random.default_rng(len(radix) + lines), radix, mode)
@@ -203,13 +228,11 @@ def test_stage_pass_launches(dl, radix, mode, lines, chunks):
     radices = radix if mode != "hadamard" else (16,) * (nst - 1) + (d // 16 ** (nst - 1),)
     if mode == "hadamard" and d % 16 ** (nst - 1) == 0 and 16 ** nst != d:
         radices = (d // 16 ** (nst - 1),) + (16,) * (nst - 1)
-    # right-side rotations run a trailing (16, 16) pair (forward) or a
-    # leading one (inverse) as one launch
-    pairs = nst - (1 if len(radices) >= 2 and radices[-1] == 16 and radices[-2] == 16 else 0)
     for inverse in (False, True):
+        want = _right_launches(radices, lines, mode, inverse)
         for xt, yt in ((2, 2), (1, 0), (0, 1)):
             _rotate(dl, p, 0, lines, chunks * d, xt, yt, inverse=inverse)
-            assert dl.brq_dryrun_launches() == pairs
+            assert dl.brq_dryrun_launches() == want
         if d <= 8192:
             _rotate(dl, p, 1, d, lines, 1, 1, inverse=inverse)
             assert dl.brq_dryrun_launches() == nst
@@ -412,12 +435,13 @@ def test_requant_walk(dl, d, m, n, bits_in, bits_out, g_out, fused):
     ((7, 16, 16, 16), "per_group", 1, 1, 0),      # decode T = 1: the tile kernel
     ((7, 16, 16, 16), "per_group", 16, 1, 2),     # decode T = 16
     ((7, 16, 16), "shared", 37, 2, 1),            # block-diagonal, shared block
-    ((8, 8, 8, 5, 2), "per_group", 9, 1, 1),      # S = 640 at stage 0; 80 and 10 are not
+    ((8, 8, 8, 5, 2), "per_group", 40, 1, 1),     # S = 640 at stage 0; 80 and 10 are not
     ((2, 4, 64), "per_group", 33, 3, 2),          # S = 256 and 64
     ((43, 16, 16), "per_group", 9, 1, 0),         # radix 43; radix 16 at strides 16 and 1
     ((7, 16, 16, 16), "shared", 64, 1, 1),        # radix 7 (radix 16: block rows not 16-byte aligned)
     ((7, 16, 16, 16), "per_group", 256, 1, 1),    # radix 16 only for <= 32 or >= 4096 rows
-    ((2, 16, 64), "shared", 12, 2, 2),            # radix 2 (S = 1024) and 16 (S = 64)
+    ((2, 16, 64), "shared", 5, 2, 0),             # below 8 rows: (2, 16) as one pair launch
+    ((2, 16, 64), "shared", 17, 2, 2),            # radix 2 (S = 1024) and 16 (S = 64)
 ])
 def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
     side = S.random_plan(np.random.default_rng(rows), radix, mode)
