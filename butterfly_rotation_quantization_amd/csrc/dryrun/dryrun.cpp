@@ -589,7 +589,8 @@ namespace brq {
 hipError_t launch_stage(const SpArgs& a, hipStream_t) {
   ++g_launches;
   const int b = a.b;
-  if (b < 2 || b > 64 || a.bp < b || (a.bp & (a.bp - 1)) || a.bp > 64 || a.bs < b || a.bs % 4 ||
+  if ((a.tile_lines != 0 && (a.side != 0 || a.tile_lines != kSpLinesFew)) ||
+      b < 2 || b > 64 || a.bp < b || (a.bp & (a.bp - 1)) || a.bp > 64 || a.bs < b || a.bs % 4 ||
       a.bs - b >= 4 || a.gw < 1 || a.gw * a.bp > kSpThreads || a.gw * a.bs > kSpLineFloats)
     return violation("stage pass geometry (b %lld, gw %lld)", b, a.gw), hipErrorInvalidValue;
   if (a.S < 1 || a.d % (b * a.S) || a.ngc != a.d / b || a.ngroups % a.ngc)
@@ -606,7 +607,8 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
   const int64_t nblocks = sp_blocks(a);
   if (nblocks >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld blocks)", nblocks, 0), hipErrorInvalidValue;
   const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
-  const int kLds = a.side ? kSpBufFloats : kSpLines * kSpLineFloats;
+  const int TL = sp_tl(a);
+  const int kLds = a.side ? kSpBufFloats : TL * kSpLineFloats;
   std::vector<uint8_t> cover((size_t)(rows * cols), 0);
   std::vector<int> xin(kLds), yout(kLds);
   std::vector<uint8_t> tile_seen((size_t)(sp_group_tiles(a) * sp_line_tiles(a)), 0);
@@ -616,9 +618,9 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
       if (gt < 0 || gt >= sp_group_tiles(a) || lt < 0 || lt >= sp_line_tiles(a) ||
           tile_seen[(size_t)(gt * sp_line_tiles(a) + lt)]++)
         return violation("stage pass block %lld maps to a bad or repeated tile (%lld)", bid, gt), hipErrorInvalidValue;
-      const int64_t g0 = gt * a.gw, l0 = lt * kSpLines;
+      const int64_t g0 = gt * a.gw, l0 = lt * TL;
       const int ng = (int)std::min<int64_t>(a.ngroups - g0, a.gw);
-      const int nl = (int)std::min<int64_t>(a.lines - l0, kSpLines);
+      const int nl = (int)std::min<int64_t>(a.lines - l0, TL);
       const int gb = a.gw * b;
       std::fill(xin.begin(), xin.end(), 0);
       std::fill(yout.begin(), yout.end(), 0);
@@ -634,7 +636,7 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
           return violation("vector block row at %lld (b %lld)", r, b), hipErrorInvalidValue;
       }
       // padding
-      for (int e = 0; e < kSpLines * a.gw; ++e) {
+      for (int e = 0; e < TL * a.gw; ++e) {
         const int l = e / a.gw, gg = e - l * a.gw;
         for (int k = b; k < a.bs; ++k) {
           const int s = sp_lds(a, l, gg, k);

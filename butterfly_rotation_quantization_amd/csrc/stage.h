@@ -66,6 +66,9 @@ struct SpArgs {
   // writes output j2 at slot (j2, g2), again that position's slot.
   int b2;             // 16, or 0 for a single stage
   int inv2;           // the pair is the inverse one
+  // right side: lines per tile, kSpLines or kSpLinesFew (few rows: more
+  // workgroups); the left side always takes kSpLines
+  int tile_lines;
   const float* blk2;  // its blocks ([group][j][k] over the chunk's d / b2 groups, or one)
 };
 
@@ -82,8 +85,12 @@ __host__ __device__ inline int64_t sp_block_row2(const SpArgs& a, int64_t gid0, 
 __host__ __device__ inline int64_t sp_group_tiles(const SpArgs& a) {
   return (a.ngroups + a.gw - 1) / a.gw;
 }
+constexpr int kSpLinesFew = 8;
+__host__ __device__ inline int sp_tl(const SpArgs& a) {
+  return a.side == 0 && a.tile_lines == kSpLinesFew ? kSpLinesFew : kSpLines;
+}
 __host__ __device__ inline int64_t sp_line_tiles(const SpArgs& a) {
-  return (a.lines + kSpLines - 1) / kSpLines;
+  return (a.lines + sp_tl(a) - 1) / sp_tl(a);
 }
 // The GPU hands workgroup i to XCD i % kXcds, and each XCD has its own L2.
 // Workgroup bid takes logical tile xcd_order(bid, n), which numbers the

@@ -24,26 +24,26 @@ __device__ __forceinline__ void sp_store(void* p, int t, int64_t i, float v) {
   }
 }
 
-template <int MAXB, int SIDE>
+template <int MAXB, int SIDE, int LINES>
 __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   // one tile buffer: the outputs wait in registers until every input is read
-  __shared__ __align__(16) float buf[SIDE ? kSpBufFloats : kSpLines * kSpLineFloats];
+  __shared__ __align__(16) float buf[SIDE ? kSpBufFloats : LINES * kSpLineFloats];
   __shared__ int spos[kSpLineFloats];   // left side: position of tile member q (-1: none)
   __shared__ int sslot[kSpLineFloats];  // left side: its LDS slot at line 0 (+ l for line l)
   const int u = threadIdx.x;
   int64_t gt, lt;
   sp_tile_of_block(a, blockIdx.x, gt, lt);
   const int64_t g0 = gt * a.gw;
-  const int64_t l0 = lt * kSpLines;
+  const int64_t l0 = lt * LINES;
   const int ng = (int)(a.ngroups - g0 < a.gw ? a.ngroups - g0 : a.gw);
-  const int nl = (int)(a.lines - l0 < kSpLines ? a.lines - l0 : kSpLines);
+  const int nl = (int)(a.lines - l0 < LINES ? a.lines - l0 : LINES);
   const int gb = a.gw * a.b;
-  constexpr int kStep = kSpThreads / kSpLines;  // left side: members per pass over the lines
+  constexpr int kStep = kSpThreads / LINES;  // left side: members per pass over the lines
 
   // ---- tile in.  Right side: thread u owns member u and walks the lines.
   // Left side: thread u owns line u % 32 and members u / 32 + 8 it, whose
   // positions come from a table built once per tile.
-  float v[kSpLines];
+  float v[LINES];
   int mg = 0, mk = 0;
   int64_t mpos = 0;
   if (a.side == 0) {
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
       if (mg < ng) {
         mpos = sp_pos(a, g0 + mg, mk);
 #pragma unroll
-        for (int l = 0; l < kSpLines; ++l)
+        for (int l = 0; l < LINES; ++l)
           if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, mpos, a.ld_src));
       }
     }
@@ -64,10 +64,10 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
       sslot[u] = sp_lds(a, 0, gg, k);
     }
     __syncthreads();
-    const int l = u % kSpLines;
+    const int l = u % LINES;
 #pragma unroll
-    for (int it = 0; it < kSpLines; ++it) {
-      const int q = u / kSpLines + kStep * it;
+    for (int it = 0; it < LINES; ++it) {
+      const int q = u / LINES + kStep * it;
       const int pos = q < gb ? spos[q] : -1;
       if (pos >= 0 && l < nl) v[it] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, pos, a.ld_src));
     }
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   }
 
   // zero the padding members, then write the tile (signs first, forward)
-  for (int e = u; e < kSpLines * a.gw; e += kSpThreads) {
+  for (int e = u; e < LINES * a.gw; e += kSpThreads) {
     const int l = e / a.gw, gg = e - l * a.gw;
     for (int k = a.b; k < a.bs; ++k) buf[sp_lds(a, l, gg, k)] = 0.f;
   }
@@ -115,14 +115,14 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     if (u < gb && mg < ng) {
       const float sg = a.sign_in ? a.sign_in[(uint32_t)mpos % (uint32_t)a.d] : 1.f;
 #pragma unroll
-      for (int l = 0; l < kSpLines; ++l)
+      for (int l = 0; l < LINES; ++l)
         if (l < nl) buf[sp_lds(a, l, mg, mk)] = sg * v[l];
     }
   } else {
-    const int l = u % kSpLines;
+    const int l = u % LINES;
 #pragma unroll
-    for (int it = 0; it < kSpLines; ++it) {
-      const int q = u / kSpLines + kStep * it;
+    for (int it = 0; it < LINES; ++it) {
+      const int q = u / LINES + kStep * it;
       const int pos = q < gb ? spos[q] : -1;
       if (pos >= 0 && l < nl) {  // left side: one chunk, so the position is the sign index
         const float sg = a.sign_in ? a.sign_in[pos] : 1.f;
@@ -133,10 +133,10 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   __syncthreads();
 
   // ---- y_j = sum_k B[j][k] x_k for every line of the tile, into registers
-  float acc[kSpLines];
+  float acc[LINES];
   if (act && SIDE == 0) {  // members consecutive: four members per float4
 #pragma unroll
-    for (int l = 0; l < kSpLines; ++l) {
+    for (int l = 0; l < LINES; ++l) {
       if (l < nl) {
         const float* xr = buf + sp_lds(a, l, g, 0);
         float s = 0.f;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     }
   } else if (act) {  // lines consecutive: four lines per float4
 #pragma unroll
-    for (int l4 = 0; l4 < kSpLines / 4; ++l4) {
+    for (int l4 = 0; l4 < LINES / 4; ++l4) {
       if (4 * l4 < nl) {
         float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   if (act) {  // a pair's first stage leaves its outputs in position order
     const bool swap = a.b2 && !a.inv2;
 #pragma unroll
-    for (int l = 0; l < kSpLines; ++l)
+    for (int l = 0; l < LINES; ++l)
       if (l < nl) buf[swap ? sp_lds(a, l, j, g) : sp_lds(a, l, g, j)] = acc[l];
   }
   __syncthreads();
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     }
     if (a.inv2) {  // members of column g2: slots (k2, g2)
 #pragma unroll
-      for (int l = 0; l < kSpLines; ++l) {
+      for (int l = 0; l < LINES; ++l) {
         if (l < nl) {
           const float* xr = buf + sp_lds(a, l, 0, g2);
           float s2 = 0.f;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
       }
     } else {
 #pragma unroll
-      for (int l = 0; l < kSpLines; ++l) {
+      for (int l = 0; l < LINES; ++l) {
         if (l < nl) {
           const float* xr = buf + sp_lds(a, l, g2, 0);
           float s2 = 0.f;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     }
     __syncthreads();  // every first-stage output read
 #pragma unroll
-    for (int l = 0; l < kSpLines; ++l)
+    for (int l = 0; l < LINES; ++l)
       if (l < nl) buf[sp_lds(a, l, j2, g2)] = acc[l];
     __syncthreads();
   }
@@ -244,15 +244,15 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     if (u < gb && mg < ng) {
       const float sg = a.sign_out ? a.sign_out[(uint32_t)mpos % (uint32_t)a.d] : 1.f;
 #pragma unroll
-      for (int l = 0; l < kSpLines; ++l)
+      for (int l = 0; l < LINES; ++l)
         if (l < nl)
           sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, mpos, a.ld_dst), sg * buf[sp_lds(a, l, mg, mk)]);
     }
   } else {
-    const int l = u % kSpLines;
+    const int l = u % LINES;
 #pragma unroll
-    for (int it = 0; it < kSpLines; ++it) {
-      const int q = u / kSpLines + kStep * it;
+    for (int it = 0; it < LINES; ++it) {
+      const int q = u / LINES + kStep * it;
       const int pos = q < gb ? spos[q] : -1;
       if (pos >= 0 && l < nl) {
         const float sg = a.sign_out ? a.sign_out[pos] : 1.f;
@@ -266,9 +266,11 @@ template <int MAXB>
 hipError_t launch_t(const SpArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)sp_blocks(a));
   if (a.side)
-    hipLaunchKernelGGL((stage_kernel<MAXB, 1>), grid, dim3(kSpThreads), 0, s, a);
+    hipLaunchKernelGGL((stage_kernel<MAXB, 1, kSpLines>), grid, dim3(kSpThreads), 0, s, a);
+  else if (sp_tl(a) == kSpLinesFew)
+    hipLaunchKernelGGL((stage_kernel<MAXB, 0, kSpLinesFew>), grid, dim3(kSpThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((stage_kernel<MAXB, 0>), grid, dim3(kSpThreads), 0, s, a);
+    hipLaunchKernelGGL((stage_kernel<MAXB, 0, kSpLines>), grid, dim3(kSpThreads), 0, s, a);
   return hipGetLastError();
 }
 
