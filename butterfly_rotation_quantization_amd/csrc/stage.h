@@ -66,8 +66,8 @@ struct SpArgs {
   // writes output j2 at slot (j2, g2), again that position's slot.
   int b2;             // 16, or 0 for a single stage
   int inv2;           // the pair is the inverse one
-  // right side: lines per tile, kSpLines or kSpLinesFew (few rows: more
-  // workgroups); the left side always takes kSpLines
+  // right side: lines per tile, kSpLines or kSpLinesFew (more workgroups,
+  // each lighter); the left side always takes kSpLines
   int tile_lines;
   const float* blk2;  // its blocks ([group][j][k] over the chunk's d / b2 groups, or one)
 };
