@@ -433,7 +433,7 @@ def test_requant_walk(dl, d, m, n, bits_in, bits_out, g_out, fused):
 @pytest.mark.parametrize("radix,mode,rows,chunks,lanes", [
     ((7, 16, 16, 16), "per_group", 4096, 1, 2),   # the 70B right schedule: stages 0, 1
     ((7, 16, 16, 16), "per_group", 1, 1, 0),      # decode T = 1: the tile kernel
-    ((7, 16, 16, 16), "per_group", 16, 1, 2),     # decode T = 16
+    ((7, 16, 16, 16), "per_group", 16, 1, 0),     # decode T = 16: the tile kernel up to 32 rows
     ((7, 16, 16), "shared", 37, 2, 1),            # block-diagonal, shared block
     ((8, 8, 8, 5, 2), "per_group", 40, 1, 1),     # S = 640 at stage 0; 80 and 10 are not
     ((2, 4, 64), "per_group", 33, 3, 2),          # S = 256 and 64
@@ -441,7 +441,8 @@ def test_requant_walk(dl, d, m, n, bits_in, bits_out, g_out, fused):
     ((7, 16, 16, 16), "shared", 64, 1, 1),        # radix 7 (radix 16: block rows not 16-byte aligned)
     ((7, 16, 16, 16), "per_group", 256, 1, 1),    # radix 16 only for <= 32 or >= 4096 rows
     ((2, 16, 64), "shared", 5, 2, 0),             # below 8 rows: (2, 16) as one pair launch
-    ((2, 16, 64), "shared", 17, 2, 2),            # radix 2 (S = 1024) and 16 (S = 64)
+    ((2, 16, 64), "shared", 17, 2, 0),            # 17 rows: the tile kernel
+    ((2, 4, 16, 64), "shared", 33, 1, 2),         # radix 2 (S = 4096) and 4 (S = 1024)
 ])
 def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
     side = S.random_plan(np.random.default_rng(rows), radix, mode)
