@@ -856,7 +856,7 @@ hipError_t launch_stage_pair2(const P2Args& a, hipStream_t) {
   ++g_pair2_launches;
   const int n = a.bo * a.bi;
   if (a.bo < 2 || a.bi < 2 || a.bo > 16 || a.bi > 16 || n > 256 || a.sets != 256 / n || a.sets < 1 ||
-      a.lines < 1 || a.lines > kP2Lines || a.Si < 1 || a.d % (n * a.Si))
+      a.lines < 1 || a.lines > kP2MaxLines || a.Si < 1 || a.d % (n * a.Si))
     return violation("stage pair geometry (bo %lld, bi %lld)", a.bo, a.bi), hipErrorInvalidValue;
   const int64_t per_chunk = a.d / (n * a.Si) * a.Si;
   if (a.nsets % per_chunk || a.ld_src < a.nsets / per_chunk * a.d || a.ld_dst < a.nsets / per_chunk * a.d)
@@ -864,19 +864,23 @@ hipError_t launch_stage_pair2(const P2Args& a, hipStream_t) {
   const int64_t cols = a.nsets / per_chunk * a.d;
   const int64_t blk_o = a.per_group ? a.d / a.bo * a.bo * a.bo : a.bo * a.bo;
   const int64_t blk_i = a.per_group ? a.d / a.bi * a.bi * a.bi : a.bi * a.bi;
-  std::vector<uint8_t> seen((size_t)cols, 0);
-  const int64_t nb = p2_blocks(a);
+  std::vector<uint8_t> seen((size_t)(cols * a.lines), 0);
+  const int64_t nb = p2_blocks(a), nsb = p2_set_blocks(a);
   if (nb >= ((int64_t)1 << 31)) return violation("stage pair grid %lld", nb, 0), hipErrorInvalidValue;
   for (int64_t blk = 0; blk < nb; ++blk)
     for (int u = 0; u < 256; ++u) {
       const int sl = u / n, e = u - sl * n;
-      const int64_t s = blk * a.sets + sl;
+      const int64_t s = (blk % nsb) * a.sets + sl, l0 = (blk / nsb) * kP2Lines;
+      const int nl = (int)std::min<int64_t>(a.lines - l0, kP2Lines);
       if (sl >= a.sets || s >= a.nsets) continue;
+      if (nl < 1) return violation("stage pair line tile at %lld", l0, 0), hipErrorInvalidValue;
       int64_t c, hi, lo;
       p2_set(a, s, c, hi, lo);
       const int ea = e / a.bi, eb = e - ea * a.bi, og = e / a.bo, oj = e - og * a.bo;
       const int64_t pos = p2_pos(a, c, hi, lo, ea, eb);
-      if (pos < 0 || pos >= cols || seen[(size_t)pos]++) return violation("stage pair position %lld", pos, 0), hipErrorInvalidValue;
+      if (pos < 0 || pos >= cols) return violation("stage pair position %lld", pos, 0), hipErrorInvalidValue;
+      for (int l = 0; l < nl; ++l)
+        if (seen[(size_t)((l0 + l) * cols + pos)]++) return violation("stage pair element (%lld, %lld)", l0 + l, pos), hipErrorInvalidValue;
       if (pos / a.d != c) return violation("stage pair chunk of %lld", pos, 0), hipErrorInvalidValue;
       const int64_t ro = p2_row_o(a, hi, lo, og, oj), ri = p2_row_i(a, hi, lo, ea, eb);
       if (ro < 0 || ro + a.bo > blk_o || ri < 0 || ri + a.bi > blk_i)

@@ -247,13 +247,15 @@ brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt
 // S_o = b_i S_i, so position hi (b_o b_i S_i) + a S_o + b S_i + lo of a chunk
 // is element (a, b) of the closed set (hi, lo): the outer stage mixes a for
 // each b, the inner one b for each a.  A workgroup takes sets = 256 / (b_o
-// b_i) consecutive lo of one hi for up to kP2Lines rows; thread (set, g, j)
+// b_i) consecutive lo of one hi; thread (set, g, j)
 // makes output j of group g of each stage, its block rows loaded up front,
-// the set's elements in LDS between the two stages.  Forward runs the outer
-// stage first, inverse (transposed blocks) the inner one.  Used below 8 rows,
-// where the groups-in-lanes kernel does not apply (at 16 rows its two
-// launches beat this one, measured 23 against 30 us on the 70B decode).
-constexpr int kP2Lines = 7;
+// the set's elements in LDS between the two stages, kP2Lines rows per
+// workgroup (more rows: more workgroups).  Forward runs the outer
+// stage first, inverse (transposed blocks) the inner one.  Used up to
+// kP2MaxLines rows, where the two stages would otherwise be two tile-kernel
+// launches.
+constexpr int kP2Lines = 4;
+constexpr int kP2MaxLines = 32;
 struct P2Args {
   int bo, bi;              // radices of the outer and inner stage (bo * bi <= 256, each <= 16)
   int64_t Si;              // inner stride (outer: bo's stride bi * Si)
@@ -272,7 +274,7 @@ struct P2Args {
   void* dst;
   int dst_t;
   int64_t ld_dst;
-  int64_t lines;           // rows, at most kP2Lines
+  int64_t lines;           // rows, at most kP2MaxLines
 };
 // Set s (of the row) -> chunk c, hi, lo.
 __host__ __device__ inline void p2_set(const P2Args& a, int64_t s, int64_t& c, int64_t& hi, int64_t& lo) {
@@ -295,8 +297,12 @@ __host__ __device__ inline int64_t p2_row_i(const P2Args& a, int64_t hi, int64_t
   const int64_t g = a.per_group ? (hi * a.bo + ao) * a.Si + lo : 0;
   return (g * a.bi + j) * a.bi;
 }
-__host__ __device__ inline int64_t p2_blocks(const P2Args& a) {
+__host__ __device__ inline int64_t p2_set_blocks(const P2Args& a) {
   return (a.nsets + a.sets - 1) / a.sets;
+}
+// Workgroup bid: set block bid % set blocks, rows kP2Lines * (bid / set blocks) ..
+__host__ __device__ inline int64_t p2_blocks(const P2Args& a) {
+  return p2_set_blocks(a) * ((a.lines + kP2Lines - 1) / kP2Lines);
 }
 hipError_t launch_stage_pair2(const P2Args& a, hipStream_t s);
 

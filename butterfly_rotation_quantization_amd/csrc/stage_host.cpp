@@ -163,9 +163,9 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
   for (int i = 0; i < L.n; ++i) {
     const int si = inverse ? L.n - 1 - i : i;
     // two consecutive right-side stages of radix <= 16 (product <= 256) for
-    // fewer than 8 rows: one launch (a trailing forward or leading inverse (16, 16)
+    // up to 32 rows: one launch (a trailing forward or leading inverse (16, 16)
     // at strides 16 and 1 keeps its own pair kernel)
-    if (side == 0 && lines <= kP2Lines && p->mode != BRQ_HADAMARD && i + 1 < L.n) {
+    if (side == 0 && lines <= kP2MaxLines && p->mode != BRQ_HADAMARD && i + 1 < L.n) {
       const int sn = inverse ? si - 1 : si + 1;
       const int to = si < sn ? si : sn, ti = si < sn ? sn : si;  // outer (larger stride), inner
       const bool pair16 = L.b[to] == 16 && L.b[ti] == 16 && L.S[to] == 16 && L.S[ti] == 1;

@@ -23,9 +23,11 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
   const int n = a.bo * a.bi;
   const int u = threadIdx.x;
   const int sl = u / n, e = u - sl * n;
-  const int64_t s = (int64_t)blockIdx.x * a.sets + sl;
+  const int64_t nsb = p2_set_blocks(a);
+  const int64_t sbk = blockIdx.x % nsb, l0 = (int64_t)(blockIdx.x / nsb) * kP2Lines;
+  const int64_t s = sbk * a.sets + sl;
   const bool act = sl < a.sets && s < a.nsets;
-  const int nl = (int)a.lines;
+  const int nl = (int)(a.lines - l0 < kP2Lines ? a.lines - l0 : kP2Lines);
   int64_t c = 0, hi = 0, lo = 0;
   if (act) p2_set(a, s, c, hi, lo);
   float* sb = buf + sl * (kP2Lines * n);
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
     pos = p2_pos(a, c, hi, lo, ea, eb);
 #pragma unroll
     for (int l = 0; l < kP2Lines; ++l)
-      if (l < nl) v[l] = p2_load(a.src, a.src_t, l * a.ld_src + pos);
+      if (l < nl) v[l] = p2_load(a.src, a.src_t, (l0 + l) * a.ld_src + pos);
     const float* ro = a.blk_o + p2_row_o(a, hi, lo, og, oj);
     const float* ri = a.blk_i + p2_row_i(a, hi, lo, ig, ij);
 #pragma unroll
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
     const float sg = a.sign_out ? a.sign_out[(uint32_t)(pos % a.d)] : 1.f;
 #pragma unroll
     for (int l = 0; l < kP2Lines; ++l)
-      if (l < nl) p2_store(a.dst, a.dst_t, l * a.ld_dst + pos, sg * sb[l * n + ea * a.bi + eb]);
+      if (l < nl) p2_store(a.dst, a.dst_t, (l0 + l) * a.ld_dst + pos, sg * sb[l * n + ea * a.bi + eb]);
   }
 }
 

@@ -190,10 +190,11 @@ def test_right_stages_in_place(radix, mode, rows):
 @pytest.mark.parametrize("radix,mode,rows,chunks", [
     ((7, 16, 16, 16), "per_group", 1, 1), ((8, 8, 8, 5, 2), "per_group", 3, 1),
     ((2, 16, 64), "shared", 7, 2), ((3, 5, 7), "per_group", 4, 3), ((16, 4, 16), "per_group", 2, 1),
+    ((7, 16, 16, 16), "per_group", 13, 1), ((8, 8, 8, 5, 2), "shared", 32, 1),
 ])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_right_stage_pairs_few_rows(radix, mode, rows, chunks, dt):
-    """Below 8 rows two consecutive stages of radix <= 16 run as one launch
+    """Up to 32 rows two consecutive stages of radix <= 16 run as one launch
     (outer stage first forward, inner first inverse, with the signs at the
     plan's stage 0): forward and inverse against the oracle."""
     import butterfly_rotation_quantization_amd as brq

@@ -189,8 +189,8 @@ def test_rowhad_launches(dl, l2d, rows, cpr):
 
 def _right_launches(radices, lines, mode, inverse):
     """Launches of a right-side stage pass: in application order, a
-    forward (16, 16) at strides 16, 1 (or its inverse) is one launch; below
-    8 rows of a dense plan, so are two consecutive stages of radix <= 16
+    forward (16, 16) at strides 16, 1 (or its inverse) is one launch; up to
+    32 rows of a dense plan, so are two consecutive stages of radix <= 16
     with a product <= 256; every other stage is a launch of its own."""
     n = len(radices)
     S = [int(np.prod(radices[t + 1:])) for t in range(n)]
@@ -200,7 +200,7 @@ def _right_launches(radices, lines, mode, inverse):
         if i + 1 < n:
             to, ti = sorted((order[i], order[i + 1]))
             pair16 = radices[to] == 16 and radices[ti] == 16 and S[to] == 16 and S[ti] == 1
-            pair2 = (lines < 8 and mode != "hadamard" and not pair16 and radices[to] <= 16 and
+            pair2 = (lines <= 32 and mode != "hadamard" and not pair16 and radices[to] <= 16 and
                      radices[ti] <= 16 and radices[to] * radices[ti] <= 256)
             if pair16 or pair2:
                 launches += 1
