@@ -13,6 +13,10 @@ Sources (cited in every function by short key and section):
 * [PolarQuant] "PolarQuant: Optimal Gaussian Weight Quantization via Hadamard
   Rotation for LLM Compression", gist.science explainer, technical overview
   (section 1 "background", section 2 "method").
+* [ORPQuant] "ORPQuant: geometric orthogonal residual projection for
+  multiplier-free power-of-two transformer quantization", gist.science
+  explainer, technical summary (section 2: the two-basis search and the GEO
+  scales).
 
 Modules:
 
@@ -27,9 +31,12 @@ Modules:
   ([PolarQuant] section 3).
 * ``linear`` -- the quantized linear layer at decode: rotate the activations,
   multiply by the quantized rotated weight, unrotate the output ([HARP] 2).
+* ``orp`` -- ORP's GEO mode: a power-of-two primary basis, an orthogonal
+  secondary basis by stride exchange and sign flips, least-squares scales
+  ([ORPQuant] section 2).
 
 Readings of points the pages leave open are stated where they are used and
 listed together in the design notes of the repository.
 """
 
-from . import transform, quant, lloydmax, harp, chain, linear  # noqa: F401
+from . import transform, quant, lloydmax, harp, chain, linear, orp  # noqa: F401
