@@ -33,6 +33,10 @@ same kind of line; "all" prints one line per workload):
                    f16 activations rotated (7,16,16,16), times the 2-bit g64
                    weight 8192 x 28672, the output rotated back (32,16,16):
                    latency per call
+  orp_geo          ORP GEO quantization of the 7B weight 4096 x 4096 bf16: 3-bit
+                   power-of-two basis, stride-4 orthogonal residual basis,
+                   least-squares scales per group of 128
+  orp_geo_dequant  its dequantization back to bf16
   harp_build       HARP blocks built on the device from int8 parameters for
                    the 70B schedules (left (32,16,16) d=8192, right
                    (7,16,16,16) d=28672): latency of the seven launches
@@ -199,6 +203,29 @@ def quant_bytes(m, n, bits, group, scale_bytes):
     return m * n * bits // 8 + m * (n // group) * scale_bytes
 
 
+def _two_sided_parity(self):
+    """The GPU's codes on the oracle's sampled rows against the oracle's codes
+    of the same rows: mismatches, the decision band's population (elements
+    within 1e-6 relative of a threshold), and mismatches outside the band."""
+    import numpy as np
+    from oracle import quant as Q
+    if getattr(self, "_oracle_sample", None) is None:
+        return None
+    rows, y, codes = self._oracle_sample
+    out = {"rows": int(len(rows)), "elements": 0, "mismatches": 0, "band": 0,
+           "mismatches_outside_band": 0}
+    for b in self.bits_list:
+        got = Q.unpack(self.out[b][0].cpu().numpy()[rows], b, self.N)
+        band = Q.absmax_band(y, b, self.group)
+        mism = got != codes[b]
+        out["elements"] += int(got.size)
+        out["mismatches"] += int(mism.sum())
+        out["band"] += int(band.sum())
+        out["mismatches_outside_band"] += int((mism & ~band).sum())
+    out["band_frac"] = out["band"] / max(out["elements"], 1)
+    return out
+
+
 class TwoSidedWeight(Workload):
     """Two-sided rotate + quantize + pack of one weight matrix."""
     kind = "absmax"
@@ -286,6 +313,8 @@ class TwoSidedWeight(Workload):
                 "right": {"d": R.d, "radix": list(R.radix), "mode": R.mode},
                 "input_copies": len(self.bufs)}
 
+    parity_sample = _two_sided_parity
+
     def cpu_baseline(self, budget_s):
         """The oracle on seeded rows: rows of M_U (factor by factor), times W,
         then M_V^T (dense from its stages when d <= 11008, else factor by
@@ -304,10 +333,13 @@ class TwoSidedWeight(Workload):
             t0 = time.perf_counter()
             y = T.left_rows(U, rows) @ w64
             y = T.apply_right(V, y, method=method)
+            codes = {}
             for b in self.bits_list:
-                codes, _alpha = Q.absmax_quantize(y, b, self.group)
-                Q.pack(codes, b)
-            return time.perf_counter() - t0
+                codes[b], _alpha = Q.absmax_quantize(y, b, self.group)
+                Q.pack(codes[b], b)
+            dt = time.perf_counter() - t0
+            self._oracle_sample = (rows, y, codes)
+            return dt
 
         k = self._cpu_rows
         dt = run(k)
@@ -355,6 +387,15 @@ class RightRotate(Workload):
     def step(self, i):
         self.brq.rotate(self.plans[i % len(self.plans)], self.bufs[i % len(self.bufs)], self.y,
                         side="right", ws=self.ws, stream=self.stream)
+
+    @property
+    def step_warm(self):
+        """Latency runs also time the same call with one plan, whose blocks
+        then stay in the caches (warm), beside the plan rotation (cold)."""
+        if not self.latency:
+            return None
+        return lambda i: self.brq.rotate(self.plans[0], self.bufs[0], self.y, side="right",
+                                         ws=self.ws, stream=self.stream)
 
     def elements(self):
         return self.T * self.N
@@ -624,6 +665,12 @@ class DecodeLinear(Workload):
         self.brq.qlinear(self.U, self.V, self.x, codes, alpha, self.m, self.n, self.bits,
                          self.group, y=self.y, ws=self.ws, stream=self.stream)
 
+    def step_warm(self, i):
+        """The same call on one weight copy (as far as the caches hold it)."""
+        codes, alpha = self.ws_copies[0]
+        self.brq.qlinear(self.U, self.V, self.x, codes, alpha, self.m, self.n, self.bits,
+                         self.group, y=self.y, ws=self.ws, stream=self.stream)
+
     def value(self, ms):
         return ms * 1e3
 
@@ -671,6 +718,73 @@ class DecodeLinear(Workload):
                 "kind": "oracle",
                 "sample": (f"rotation of the {self.T} tokens and {rows} of the {self.m} weight rows "
                            f"(scaled by {1 / share:.0f}); the output rotation left out; {dt:.2f} s")}
+
+
+class OrpGeo(Workload):
+    """ORP GEO quantization (or dequantization) of the 7B-shaped weight,
+    4096 x 4096 bf16 (0.02 * Student-t(3), 0.5% outlier input channels x30):
+    power-of-two primary basis, stride-4 exchange secondary basis,
+    least-squares scales per group of 128, 3 bits (one step = one call)."""
+    bits, group, stride = 3, 128, 4
+
+    def __init__(self, name, metric, dequant):
+        self.name, self.metric, self.dequant = name, metric, dequant
+
+    def setup(self, brq, dev, stream):
+        import torch
+        import synthetic as S
+        self.brq, self.stream = brq, stream
+        self.cfg = S.llama7b(act_tokens=1)
+        self.w_h = self.cfg["w"]
+        self.M, self.N = self.w_h.shape
+        w = storage_tensor(self.w_h, "bf16", dev)
+        self.bufs = [w] + [w.clone() for _ in range(copies_for(w.numel() * 2) - 1)]
+        self.codes, self.signs, self.coef = brq.orp_geo_quantize(w, self.bits, self.group,
+                                                                 self.stride, stream=stream)
+        if self.dequant:
+            n_out = copies_for(w.numel() * 2)
+            self.outs = [torch.empty_like(w) for _ in range(n_out)]
+
+    def step(self, i):
+        if self.dequant:
+            self.brq.orp_geo_dequant(self.codes, self.signs, self.coef, self.M, self.N, self.bits,
+                                     self.group, self.stride, out=self.outs[i % len(self.outs)],
+                                     stream=self.stream)
+        else:
+            self.brq.orp_geo_quantize(self.bufs[i % len(self.bufs)], self.bits, self.group,
+                                      self.stride, codes=self.codes, signs=self.signs,
+                                      coef=self.coef, stream=self.stream)
+
+    def elements(self):
+        return self.M * self.N
+
+    def alg_bytes(self):
+        E = self.M * self.N
+        return 2 * E + E * self.bits // 8 + E // 16 + 8 * E // self.group
+
+    def kernel_cost(self, name):
+        return self.alg_bytes(), 0, "alu"
+
+    def config(self):
+        return {"m": self.M, "n": self.N, "bits": self.bits, "group": self.group,
+                "stride": self.stride, "io_dtype": "bf16",
+                "copies": len(self.outs) if self.dequant else len(self.bufs)}
+
+    def cpu_baseline(self, budget_s):
+        import synthetic as S
+        from oracle import orp as O
+        k = self._cpu_rows
+        w64 = S.storage_to_f64(self.w_h[:k], "bf16")
+        t0 = time.perf_counter()
+        codes, sigma, coef, b1, b2, _ = O.geo_quantize(w64, self.bits, self.group, self.stride)
+        if self.dequant:
+            O.geo_dequant(codes, sigma, coef, self.bits, self.group, self.stride)
+        dt = time.perf_counter() - t0
+        share = k / self.M
+        return {"value": round(self.alg_bytes() * share / dt / 1e9, 6), "unit": "GB/s",
+                "cores": cpu_threads(), "kind": "oracle",
+                "sample": (f"{k} of {self.M} rows ({'quantize + dequantize' if self.dequant else 'quantize'} "
+                           f"in the oracle); {dt:.2f} s")}
 
 
 class HarpBuild(Workload):
@@ -810,6 +924,14 @@ def make_workload(name):
                       "d=28672", [(8192, (32, 16, 16)), (28672, (7, 16, 16, 16))])
         w.workload = "harp_build_70b_U(32,16,16)_d8192_V(7,16,16,16)_d28672_int8"
         return w
+    if name in ("orp_geo", "orp_geo_dequant"):
+        dq = name == "orp_geo_dequant"
+        w = OrpGeo(name, "HBM GB/s: ORP GEO " + ("dequantize" if dq else "quantize") +
+                   " (power-of-two + orthogonal residual basis, 3-bit, g128, stride 4), "
+                   "4096x4096 bf16", dq)
+        w.workload = f"{name}_7b_4096x4096_bf16_b3_g128_s4"
+        w._cpu_rows = 1024
+        return w
     if name in ("polar_quant", "polar_dequant"):
         dq = name == "polar_dequant"
         w = PolarBlock(name, ("HBM GB/s: PolarQuant dequant+unrotate" if dq else
@@ -824,10 +946,77 @@ def make_workload(name):
 
 WORKLOADS = ("harp_mlp", "llama7b_weight", "llama7b_act", "polar_quant", "polar_dequant",
              "llama70b_weight", "decode_t1", "decode_t16", "decode_t256", "harp_build",
-             "polar_requant", "qlinear_t1", "qlinear_t16", "qlinear_t256")
+             "polar_requant", "qlinear_t1", "qlinear_t16", "qlinear_t256", "orp_geo",
+             "orp_geo_dequant")
 
 
-def run_workload(wl, a, brq, torch, dev, stream):
+def _pct(vals, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(vals, dtype=float), q)), 5)
+
+
+def time_steps(wl, steps, torch, stream, step=None):
+    """Per-step durations (ms) of `steps` consecutive steps, from HIP events
+    recorded between the steps on the launch stream; no per-launch events."""
+    step = step or wl.step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def stream_copy_gbs(torch, dev, mib=1024, reps=10):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel):
+    bytes read + written per second, the practical HBM ceiling."""
+    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)
+
+
+def host_description():
+    """CPU model, logical CPUs in the affinity mask, and numpy's BLAS with the
+    threads its pool runs (what the oracle's matrix products use)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+        for info in threadpool_info():
+            if info.get("user_api") == "blas":
+                blas = f"{info.get('internal_api')} {info.get('version')}"
+                threads = info.get("num_threads")
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "cpus_in_mask": len(os.sched_getaffinity(0)), "blas": blas,
+            "blas_threads": threads}
+
+
+def run_workload(wl, a, brq, torch, dev, stream, copy_gbs=None):
     wl.setup(brq, dev, stream)
     if a.copy_calibration:
         nel = a.copy_calibration * (1 << 20) // 4
@@ -840,31 +1029,27 @@ def run_workload(wl, a, brq, torch, dev, stream):
     for i in range(a.warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    # Per-kernel durations come from HIP events recorded around each launch on
-    # its stream.  Latency workloads (a few microseconds per kernel) time the
-    # step without them and take the kernel durations from a second run of
-    # the same steps; the others record them inside the timed region.
-    separate = getattr(wl, "latency", False)
+    # The timed region runs with per-launch profiling off; each step is
+    # bracketed by events on the launch stream, which give the median and
+    # p10/p90.  Per-kernel durations come from a second run of the same steps
+    # with an event pair around every launch.
+    brq.profile_enable(False)
+    ms, per = time_steps(wl, a.steps, torch, stream)
     brq.profile_reset()
-    brq.profile_enable(not separate)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
+    brq.profile_enable(True)
     for i in range(a.steps):
         wl.step(i)
-    end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / a.steps
-    if separate:
-        brq.profile_enable(True)
-        for i in range(a.steps):
-            wl.step(i)
-        torch.cuda.synchronize()
     brq.profile_enable(False)
     kernels = brq.profile_read()
     names = list(kernels)
     wl._first_kernel, wl._last_kernel = names[0], names[-1]
+    warm = None
+    if getattr(wl, "step_warm", None) is not None:
+        for i in range(a.warmup):
+            wl.step_warm(i)
+        _, wper = time_steps(wl, a.steps, torch, stream, wl.step_warm)
+        warm = {"median": _pct(wper, 50), "p10": _pct(wper, 10), "p90": _pct(wper, 90)}
 
     value = wl.value(ms)
     alg = wl.alg_bytes()
@@ -879,9 +1064,17 @@ def run_workload(wl, a, brq, torch, dev, stream):
         "algorithmic_bytes": alg,
         "hbm_gbs": round(alg / (ms * 1e-3) / 1e9, 3),
         "hbm_peak_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+        "step_ms": {"mean": round(ms, 5), "median": _pct(per, 50), "p10": _pct(per, 10),
+                    "p90": _pct(per, 90)},
         "kernels_ms_per_step": {k: round(v[0] / a.steps, 5) for k, v in kernels.items()},
         "launches_per_step": {k: v[1] / a.steps for k, v in kernels.items()},
     })
+    if warm is not None:
+        cfg["step_ms_warm"] = warm
+        cfg["step_ms_cold"] = cfg["step_ms"]
+    if copy_gbs is not None:
+        cfg["stream_copy_gbs"] = copy_gbs
+        cfg["hbm_frac_of_copy"] = round(alg / (ms * 1e-3) / 1e9 / copy_gbs, 5)
     cfg["elements_per_s"] = round(wl.elements() / (ms * 1e-3), 1)
     line = {
         "metric": wl.metric,
@@ -911,7 +1104,13 @@ def run_workload(wl, a, brq, torch, dev, stream):
         },
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = wl.cpu_baseline(None)
+        cb = wl.cpu_baseline(None)
+        if cb is not None:
+            cb.update(host_description())
+        line["cpu_baseline"] = cb
+        par = getattr(wl, "parity_sample", None)
+        if par is not None:
+            line["parity"] = par()
     print(json.dumps(line), flush=True)
 
 
@@ -941,11 +1140,12 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
     names = WORKLOADS if a.workload == "all" else (a.workload,)
+    copy_gbs = stream_copy_gbs(torch, dev)
     for name in names:
         wl = make_workload(name)
         if a.cpu_rows:
             wl._cpu_rows = a.cpu_rows
-        run_workload(wl, a, brq, torch, dev, stream)
+        run_workload(wl, a, brq, torch, dev, stream, copy_gbs)
         del wl
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

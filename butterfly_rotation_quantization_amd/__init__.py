@@ -37,7 +37,7 @@ EXPORTED = (
     "brq_lloyd_max_gaussian", "brq_profile_enable", "brq_profile_reset", "brq_profile_count",
     "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_harp_blocks_batch", "brq_plan_create_harp",
     "brq_plan_serialize", "brq_plan_deserialize", "brq_requant_workspace_bytes", "brq_requant",
-    "brq_qlinear_workspace_bytes", "brq_qlinear",
+    "brq_qlinear_workspace_bytes", "brq_qlinear", "brq_orp_geo_quantize", "brq_orp_geo_dequant",
 )
 
 
@@ -46,6 +46,10 @@ class BrqError(RuntimeError):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
         self.status = status
         self.detail = detail
+
+
+class Orp(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("stride", ctypes.c_int32)]
 
 
 class Quant(ctypes.Structure):
@@ -139,6 +143,13 @@ def bind(lib):
         lib.brq_qlinear.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, ctypes.POINTER(Quant), i64,
                                     i64, vp, i32, i64, vp, sz, vp]
         lib.brq_qlinear.restype = i32
+    if hasattr(lib, "brq_orp_geo_quantize"):
+        lib.brq_orp_geo_quantize.argtypes = [vp, i32, i64, i64, i64, vp, ctypes.POINTER(Orp), vp, vp,
+                                             vp, vp]
+        lib.brq_orp_geo_quantize.restype = i32
+        lib.brq_orp_geo_dequant.argtypes = [vp, vp, vp, ctypes.POINTER(Orp), i64, i64, vp, i32, i64,
+                                            vp]
+        lib.brq_orp_geo_dequant.restype = i32
     if hasattr(lib, "brq_plan_serialize"):
         lib.brq_plan_serialize.argtypes = [vp, vp, sz, ctypes.POINTER(sz)]
         lib.brq_plan_serialize.restype = i32
@@ -425,6 +436,14 @@ def requant(right: Optional[Plan], codes, scales, m: int, n: int, bits_in: int, 
     return codes_out, scales_out
 
 
+def qlinear_workspace_bytes(left: Optional[Plan], right: Optional[Plan], bits: int, group: int,
+                            T: int, m: int, n: int) -> int:
+    """Bytes of device workspace brq_qlinear needs for T tokens."""
+    q = make_quant(bits, group, "absmax")
+    return int(lib().brq_qlinear_workspace_bytes(_h(left), _h(right), ctypes.byref(q), int(T),
+                                                 int(m), int(n)))
+
+
 def qlinear(left: Optional[Plan], right: Optional[Plan], x, codes, scales, m: int, n: int,
             bits: int, group: int, y=None, out_dtype=None, ws=None, stream=None):
     """Y = X W^T for the weight W = M_U^T W' M_V stored as the absmax codes and
@@ -444,6 +463,39 @@ def qlinear(left: Optional[Plan], right: Optional[Plan], x, codes, scales, m: in
                         _ptr(scales), ctypes.byref(q), int(m), int(n), _ptr(y), dtype_code(y),
                         _ld(y), wp, wb, _stream(stream)))
     return y
+
+
+def orp_geo_quantize(w, bits: int, group: int, stride: int, smooth=None, codes=None, signs=None,
+                     coef=None, stream=None):
+    """ORP GEO quantizer (brq_orp_geo_quantize): w [m, n] f32/bf16/f16 on the
+    device, optional float32 smoothing vector [n].  Returns (codes [m, n*bits/8]
+    uint8, signs [m, n/16] uint8, coef [m, n/group, 2] float32)."""
+    import torch
+    m, n = int(w.shape[0]), int(w.shape[1])
+    dev = w.device
+    if codes is None:
+        codes = torch.empty((m, n * bits // 8), dtype=torch.uint8, device=dev)
+    if signs is None:
+        signs = torch.empty((m, n // 16), dtype=torch.uint8, device=dev)
+    if coef is None:
+        coef = torch.empty((m, n // group, 2), dtype=torch.float32, device=dev)
+    q = Orp(bits, group, stride)
+    check(lib().brq_orp_geo_quantize(_ptr(w), dtype_code(w), m, n, _ld(w), _ptr(smooth),
+                                     ctypes.byref(q), _ptr(codes), _ptr(signs), _ptr(coef),
+                                     _stream(stream)))
+    return codes, signs, coef
+
+
+def orp_geo_dequant(codes, signs, coef, m: int, n: int, bits: int, group: int, stride: int,
+                    out=None, out_dtype=None, stream=None):
+    """w_p^ = c1 b1 + c2 b2 (brq_orp_geo_dequant).  Returns out [m, n]."""
+    import torch
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=codes.device)
+    q = Orp(bits, group, stride)
+    check(lib().brq_orp_geo_dequant(_ptr(codes), _ptr(signs), _ptr(coef), ctypes.byref(q), int(m),
+                                    int(n), _ptr(out), dtype_code(out), _ld(out), _stream(stream)))
+    return out
 
 
 def profile_enable(on: bool = True):

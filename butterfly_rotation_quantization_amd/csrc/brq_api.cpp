@@ -15,6 +15,7 @@
 #include "fused.h"
 #include "rowhad.h"
 #include "harp.h"
+#include "orp.h"
 #include "qlinear.h"
 #include "stage.h"
 
@@ -1408,6 +1409,109 @@ brq_status brq_lloyd_max_gaussian(int32_t bits, float* centroids) {
     centroids[h + k] = (float)c[k];
     centroids[h - 1 - k] = (float)-c[k];
   }
+  return BRQ_OK;
+}
+
+// ---- ORP GEO quantizer ----------------------------------------------------------
+
+namespace {
+
+brq_status check_orp(const brq_orp* q, int64_t n) {
+  if (!q) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL quantizer");
+  if (q->bits < 2 || q->bits > 5) return fail(BRQ_ERR_UNSUPPORTED, "bits must be 2..5");
+  if (q->group != 64 && q->group != 128 && q->group != 256 && q->group != 512)
+    return fail(BRQ_ERR_UNSUPPORTED, "group must be 64, 128, 256 or 512");
+  if (!is_pow2(q->stride) || 2 * q->stride > q->group)
+    return fail(BRQ_ERR_INVALID_ARGUMENT, "stride must be a power of two with 2*stride <= group");
+  if (n % q->group) return fail(BRQ_ERR_INVALID_ARGUMENT, "group %d does not divide n", q->group);
+  return BRQ_OK;
+}
+
+brq_status orp_outputs_ok(const uint8_t* codes, const uint8_t* signs, const float* coef) {
+  if (!codes || !signs || !coef) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 4 || reinterpret_cast<uintptr_t>(coef) % 8)
+    return fail(BRQ_ERR_ALIGNMENT, "codes must be 4-byte and coef 8-byte aligned");
+  return BRQ_OK;
+}
+
+size_t dtype_bytes(int t) { return t == BRQ_F32 ? 4 : 2; }
+
+}  // namespace
+
+brq_status brq_orp_geo_quantize(const void* w, int32_t wt, int64_t m, int64_t n, int64_t ldw,
+                                const float* smooth, const brq_orp* q, uint8_t* codes,
+                                uint8_t* signs, float* coef, void* stream) {
+  g_last_error.clear();
+  if (!valid_dtype(wt)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad input dtype");
+  if (m < 0 || n < 0 || ldw < n) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape or leading dimension");
+  brq_status st = check_orp(q, n);
+  if (st != BRQ_OK) return st;
+  if (m == 0 || n == 0) return BRQ_OK;
+  if (!w) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if ((st = orp_outputs_ok(codes, signs, coef)) != BRQ_OK) return st;
+  if (reinterpret_cast<uintptr_t>(w) % 16 || (ldw * dtype_bytes(wt)) % 16)
+    return fail(BRQ_ERR_ALIGNMENT, "input rows must be 16-byte aligned");
+  if (smooth && reinterpret_cast<uintptr_t>(smooth) % 16)
+    return fail(BRQ_ERR_ALIGNMENT, "the smoothing vector must be 16-byte aligned");
+  OrpArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.w = w;
+  a.wt = wt;
+  a.ldw = ldw;
+  a.smooth = smooth;
+  a.m = m;
+  a.n = n;
+  a.bits = q->bits;
+  a.group = q->group;
+  a.stride = q->stride;
+  a.chunks = (n + kOrpChunk - 1) / kOrpChunk;
+  a.codes = codes;
+  a.signs = signs;
+  a.coef = coef;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char name[48];
+  snprintf(name, sizeof name, "orp geo quant b%d g%d S%d", q->bits, q->group, q->stride);
+  const int tok = prof_begin(name, s);
+  const hipError_t e = launch_orp_quant(a, s);
+  prof_end(tok, s);
+  if (e != hipSuccess) return hip_fail(e, "ORP quantizer launch");
+  return BRQ_OK;
+}
+
+brq_status brq_orp_geo_dequant(const uint8_t* codes, const uint8_t* signs, const float* coef,
+                               const brq_orp* q, int64_t m, int64_t n, void* out, int32_t ot,
+                               int64_t ldo, void* stream) {
+  g_last_error.clear();
+  if (!valid_dtype(ot)) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad output dtype");
+  if (m < 0 || n < 0 || ldo < n) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape or leading dimension");
+  brq_status st = check_orp(q, n);
+  if (st != BRQ_OK) return st;
+  if (m == 0 || n == 0) return BRQ_OK;
+  if (!out) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
+  if ((st = orp_outputs_ok(codes, signs, coef)) != BRQ_OK) return st;
+  if (reinterpret_cast<uintptr_t>(out) % 16 || (ldo * dtype_bytes(ot)) % 16)
+    return fail(BRQ_ERR_ALIGNMENT, "output rows must be 16-byte aligned");
+  OrpArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.m = m;
+  a.n = n;
+  a.bits = q->bits;
+  a.group = q->group;
+  a.stride = q->stride;
+  a.chunks = (n + kOrpChunk - 1) / kOrpChunk;
+  a.codes = const_cast<uint8_t*>(codes);
+  a.signs = const_cast<uint8_t*>(signs);
+  a.coef = const_cast<float*>(coef);
+  a.out = out;
+  a.ot = ot;
+  a.ldo = ldo;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char name[48];
+  snprintf(name, sizeof name, "orp geo dequant b%d g%d S%d", q->bits, q->group, q->stride);
+  const int tok = prof_begin(name, s);
+  const hipError_t e = launch_orp_dequant(a, s);
+  prof_end(tok, s);
+  if (e != hipSuccess) return hip_fail(e, "ORP dequantizer launch");
   return BRQ_OK;
 }
 

@@ -12,6 +12,7 @@
 
 #include "brq_internal.h"
 #include "harp.h"
+#include "orp.h"
 #include "qlinear.h"
 
 namespace brq {
@@ -1053,5 +1054,87 @@ hipError_t launch_ql_reduce(const float*, int splits, int64_t T, int64_t m, void
     return violation("reduce geometry (splits %lld, ld %lld)", splits, ldo), hipErrorInvalidValue;
   return hipSuccess;
 }
+
+// ---------------------------------------------------------------- ORP GEO
+
+static hipError_t walk_orp(const OrpArgs& a, bool quant) {
+  ++g_launches;
+  const int bits = a.bits, g = a.group, S = a.stride;
+  if (bits < 2 || bits > 5 || g % kOrpPerLane || g > kOrpChunk || (g & (g - 1)) || S < 1 ||
+      (S & (S - 1)) || 2 * S > g || a.n % g)
+    return violation("ORP geometry (group %lld, stride %lld)", g, S), hipErrorInvalidValue;
+  if (a.chunks != (a.n + kOrpChunk - 1) / kOrpChunk)
+    return violation("ORP chunks per row %lld for n %lld", a.chunks, a.n), hipErrorInvalidValue;
+  const int lpg = g / kOrpPerLane;
+  const int64_t cb = a.n * bits / 8, sb = a.n / 16, ng = a.n / g;
+  std::vector<uint8_t> code_cov((size_t)(a.m * cb), 0), sign_cov((size_t)(a.m * sb), 0);
+  std::vector<uint8_t> coef_cov((size_t)(a.m * ng), 0), elem_cov((size_t)(a.m * a.n), 0);
+  const int64_t waves = orp_waves(a);
+  if (orp_blocks(a) * (kOrpThreads / 64) < waves)
+    return violation("ORP grid of %lld blocks for %lld waves", orp_blocks(a), waves), hipErrorInvalidValue;
+  for (int64_t wv = 0; wv < waves; ++wv) {
+    int64_t row, c0;
+    orp_wave(a, wv, &row, &c0);
+    if (row < 0 || row >= a.m || c0 % g) return violation("ORP wave %lld at row %lld", wv, row), hipErrorInvalidValue;
+    for (int lane = 0; lane < 64; ++lane) {
+      const int64_t col = c0 + kOrpPerLane * lane;
+      const bool valid = col < a.n;
+      // a group's lanes are all valid or all not
+      const int lead = lane & ~(lpg - 1);
+      if (valid != (c0 + kOrpPerLane * lead < a.n))
+        return violation("ORP group straddles the row end at column %lld (n %lld)", col, a.n), hipErrorInvalidValue;
+      if (S >= kOrpPerLane) {
+        const int xm = S / kOrpPerLane, partner = lane ^ xm;
+        if ((partner & ~(lpg - 1)) != lead)
+          return violation("ORP pair partner lane %lld outside the group of lane %lld", partner, lane), hipErrorInvalidValue;
+        if (valid && ((lane & (lpg - 1)) & xm) == 0 && (col + S) / (2 * S) != col / (2 * S))
+          return violation("ORP pair at column %lld leaves its micro-block", col, S), hipErrorInvalidValue;
+      }
+      if (!valid) continue;
+      if (col + kOrpPerLane > a.n) return violation("ORP lane reads past the row (%lld, n %lld)", col, a.n), hipErrorInvalidValue;
+      for (int j = 0; j < kOrpPerLane; ++j) elem_cov[(size_t)(row * a.n + col + j)]++;
+      // codes
+      const int64_t cbyte = col * bits / 8;
+      for (int b = 0; b < bits; ++b) {
+        if (cbyte + b >= cb) return violation("ORP code byte %lld of a %lld-byte row", cbyte + b, cb), hipErrorInvalidValue;
+        if (quant) code_cov[(size_t)(row * cb + cbyte + b)]++;
+      }
+      // sign bytes
+      if (S < kOrpPerLane) {
+        if (col / 16 >= sb) return violation("ORP sign byte %lld of %lld", col / 16, sb), hipErrorInvalidValue;
+        if (quant && (lane & 1) == 0) sign_cov[(size_t)(row * sb + col / 16)]++;
+      } else {
+        const bool first = ((lane & (lpg - 1)) & (S / kOrpPerLane)) == 0;
+        const int64_t fc = first ? col : col - S;
+        const int64_t byte = orp_pair(fc, S) / 8;
+        if (fc < 0 || orp_pair(fc, S) % 8 || byte >= sb)
+          return violation("ORP sign byte %lld for column %lld", byte, col), hipErrorInvalidValue;
+        if (quant && first) sign_cov[(size_t)(row * sb + byte)]++;
+      }
+      // coefficients
+      const int64_t ci = row * ng + col / g;
+      if (2 * ci + 1 >= 2 * a.m * ng) return violation("ORP coefficient %lld of %lld", ci, a.m * ng), hipErrorInvalidValue;
+      if (quant && (lane & (lpg - 1)) == 0) coef_cov[(size_t)ci]++;
+      // input / output rows
+      const int64_t ld = quant ? a.ldw : a.ldo;
+      if (ld < a.n || row * ld + col + kOrpPerLane > a.m * ld)
+        return violation("ORP element %lld outside %lld", row * ld + col, a.m * ld), hipErrorInvalidValue;
+    }
+  }
+  for (size_t i = 0; i < elem_cov.size(); ++i)
+    if (elem_cov[i] != 1) return violation("ORP element %lld handled %lld times", (int64_t)i, elem_cov[i]), hipErrorInvalidValue;
+  if (quant) {
+    for (size_t i = 0; i < code_cov.size(); ++i)
+      if (code_cov[i] != 1) return violation("ORP code byte %lld written %lld times", (int64_t)i, code_cov[i]), hipErrorInvalidValue;
+    for (size_t i = 0; i < sign_cov.size(); ++i)
+      if (sign_cov[i] != 1) return violation("ORP sign byte %lld written %lld times", (int64_t)i, sign_cov[i]), hipErrorInvalidValue;
+    for (size_t i = 0; i < coef_cov.size(); ++i)
+      if (coef_cov[i] != 1) return violation("ORP coefficients %lld written %lld times", (int64_t)i, coef_cov[i]), hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_orp_quant(const OrpArgs& a, hipStream_t) { return walk_orp(a, true); }
+hipError_t launch_orp_dequant(const OrpArgs& a, hipStream_t) { return walk_orp(a, false); }
 
 }  // namespace brq

@@ -15,6 +15,9 @@
  *         Extreme LLM Quantization", technical summary sections 1, 2.1, 2.2, 2.4.
  *  [PolarQuant] "PolarQuant: Optimal Gaussian Weight Quantization via Hadamard
  *         Rotation for LLM Compression", technical overview sections 1 and 2.
+ *  [ORPQuant] "ORPQuant: geometric orthogonal residual projection for
+ *         multiplier-free power-of-two transformer quantization", technical
+ *         summary section 2.
  */
 #ifndef BRQ_H
 #define BRQ_H
@@ -281,7 +284,9 @@ brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* 
  *           otherwise a slower kernel reads it directly (same results to
  *           the float32 rounding of the group sums).
  *   y:      device [T][ldy] of type yt.
- *   ws:     device workspace of brq_qlinear_workspace_bytes(...) bytes.
+ *   ws:     device workspace of brq_qlinear_workspace_bytes(...) bytes.  On
+ *           return, when right is not NULL, its first T*n*2 bytes hold X~ as
+ *           a row-major [T][n] array of the activation type.
  * m must be a multiple of 256 for T <= 16 and of 128 above.  Asynchronous
  * on `stream`.  Errors: INVALID_ARGUMENT (dtypes, shapes, NULLs, q not
  * ABSMAX), UNSUPPORTED (m, group), ALIGNMENT, WORKSPACE, HIP. */
@@ -291,6 +296,57 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
                        int64_t ldx, int64_t T, const uint8_t* codes, const void* scales,
                        const brq_quant* q, int64_t m, int64_t n, void* y, int32_t yt, int64_t ldy,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ORP GEO quantizer ([ORPQuant] technical summary, section 2: the geometric
+ * discrete basis search and the GEO scales).  Per group of `group`
+ * consecutive inputs w of a row, after the optional preconditioning
+ * w_p = w * smooth (one float32 product per element):
+ *   b1: the nearest level to u = w_p * fl(1/alpha), alpha = max |w_p|, of the
+ *       asymmetric power-of-two lattice with zero: 2^(bits-1) negative levels
+ *       -1, -1/2, ..., -2^-(2^(bits-1)-1), zero, and 2^(bits-1)-1 positive
+ *       levels 1, 1/2, ..., 2^-(2^(bits-1)-2) (3 bits: -1 -1/2 -1/4 -1/8 0
+ *       1/4 1/2 1); codes index the levels in ascending order; a tie goes to
+ *       the lower code; decided in float32.
+ *   b2: inside micro-blocks of 2*stride entries, entry i of the first half
+ *       pairs with i + stride and b2 takes (b1[i], b1[i+stride]) to
+ *       sigma * (-b1[i+stride], b1[i]), sigma = +1 when
+ *       d = w_p[i+stride] b1[i] - w_p[i] b1[i+stride] >= 0 (b2 follows the
+ *       Gram-Schmidt residual of w_p against b1), else -1.  b2 is orthogonal
+ *       to b1 and ||b2|| = ||b1||.
+ *   c1 = <w_p, b1> / ||b1||^2, c2 = <w_p, b2> / ||b1||^2 (the least-squares
+ *       scales for orthogonal bases); a group with alpha = 0 gets the zero
+ *       code everywhere and c1 = c2 = 0.
+ * Outputs (device, caller-owned):
+ *   codes [m][n*bits/8]: LSB-first bit stream of b1 codes per row (as for
+ *         brq_quant), 4-byte aligned;
+ *   signs [m][n/16]: one bit per pair, 1 for sigma = -1; the pair whose first
+ *         entry is i has number (i / (2*stride))*stride + i % (2*stride) and
+ *         sits at bit (number mod 8) of byte number/8 of its row;
+ *   coef  [m][n/group][2] float32 (c1, c2), 8-byte aligned.
+ * w: device [m][ldw] of type wt (F32/BF16/F16), 16-byte aligned rows;
+ * smooth: device float32 [n] (16-byte aligned) or NULL.  bits 2..5, group
+ * 64/128/256/512 dividing n, stride a power of two with 2*stride <= group.
+ * Asynchronous on `stream`.  Errors: INVALID_ARGUMENT (dtype, shape, NULLs,
+ * stride, group not dividing n), UNSUPPORTED (bits, group), ALIGNMENT, HIP. */
+typedef struct {
+  int32_t bits;   /* 2..5                          */
+  int32_t group;  /* 64, 128, 256 or 512           */
+  int32_t stride; /* pair stride S: power of two   */
+} brq_orp;
+
+brq_status brq_orp_geo_quantize(const void* w, int32_t wt, int64_t m, int64_t n, int64_t ldw,
+                                const float* smooth, const brq_orp* q, uint8_t* codes,
+                                uint8_t* signs, float* coef, void* stream);
+
+/*
+ * The ORP dequantizer: w_p^ = c1 b1 + c2 b2 per group (in the preconditioned
+ * domain; rounded once from float32, c1 b1 being exact), from the outputs of
+ * brq_orp_geo_quantize.  out: device [m][ldo] of type ot, 16-byte aligned
+ * rows.  Errors as brq_orp_geo_quantize. */
+brq_status brq_orp_geo_dequant(const uint8_t* codes, const uint8_t* signs, const float* coef,
+                               const brq_orp* q, int64_t m, int64_t n, void* out, int32_t ot,
+                               int64_t ldo, void* stream);
 
 /*
  * Host helper: the 2^bits Lloyd-Max centroids for N(0,1), ascending, rounded

@@ -62,13 +62,6 @@ def digits(i: int, radix: Sequence[int]) -> List[int]:
     return out
 
 
-def group_index(i: int, t: int, radix: Sequence[int]) -> int:
-    """Group c of coordinate i at stage t: c = hi*S_t + lo (index reading)."""
-    s = strides(radix)[t]
-    b = radix[t]
-    return (i // (b * s)) * s + (i % s)
-
-
 def sylvester(n: int) -> np.ndarray:
     """The +-1 Sylvester Hadamard matrix H_n (n a power of two), natural order:
     H_1 = [1], H_{2k} = [[H_k, H_k], [H_k, -H_k]]."""
@@ -176,12 +169,6 @@ def dense(plan: Plan) -> np.ndarray:
             m = stage_matrix(plan, t) @ m
         plan._dense = np.asarray(m)
     return plan._dense
-
-
-def rht_matrix(d: int, signs: Optional[np.ndarray] = None) -> np.ndarray:
-    """Randomized Hadamard transform H_d D / sqrt(d) ([HARP] section 1)."""
-    s = np.ones(d) if signs is None else np.asarray(signs, dtype=np.float64)
-    return sylvester(d) * s[None, :] / np.sqrt(d)
 
 
 def apply_factored(plan: Plan, x: np.ndarray, inverse: bool = False) -> np.ndarray:

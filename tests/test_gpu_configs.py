@@ -59,7 +59,7 @@ def check_quantized_rows(codes, scales, y_rows, rows, bits, group, what, kind="a
         ref, r, z = Q.codebook_norm_quantize(y_rows, cb, group)
         band = Q.codebook_band(z, cb)
         check_f16_norms(sc, r, what)
-    info = check_codes(got, ref, band, what)
+    info = check_codes(got, ref, band, what, bits)
     assert np.array_equal(Q.pack(got, bits), codes.cpu().numpy()[rows])
     print(what, info, flush=True)
     return got, sc
@@ -127,6 +127,9 @@ def test_harp_mlp_two_sided():
 
 @pytest.mark.parametrize("name", list(S.POLAR_SHAPES))
 def test_polar_projection(name):
+    """Every row of the projection: the block-128 oracle is cheap, so codes,
+    norms and packing are compared over the whole matrix and the decision
+    band's population is that of the whole matrix."""
     import butterfly_rotation_quantization_amd as brq
     announce(f"PolarQuant {name} {S.POLAR_SHAPES[name]}")
     cfg = polar_mats()
@@ -136,31 +139,55 @@ def test_polar_projection(name):
     w = to_dev(ws, "bf16")
     V = lib_plan(cfg["right"])
     codes, scales = brq.rotate_quantize_pack(None, V, w, 4, 128, "codebook_norm", cb)
-    rows = sampled_rows(m, 512, 13)
-    Vo = orc_plan(cfg["right"])
-    y = T.apply_right(Vo, S.storage_to_f64(ws, "bf16")[rows])
-    got, sc = check_quantized_rows(codes, scales, y, rows, 4, 128, f"polar {name}",
-                                   "codebook_norm", cb)
     out = brq.dequant_unrotate(None, V, codes, scales, m, n, 4, 128, "codebook_norm", cb,
                                out_dtype=w.dtype)
-    v = Q.codebook_dequant(got, sc, cb, 128)
-    back = T.apply_right(Vo, v, inverse=True)
-    check_rotation(from_dev(out)[rows], back, "bf16", f"polar {name} dequant")
+    codes_h, sc_h, out_h = codes.cpu().numpy(), scales.cpu().numpy(), from_dev(out)
+    Vo = orc_plan(cfg["right"])
+    gots, refs, bands = [], [], []
+    worst = 0.0
+    for r0 in range(0, m, 2048):
+        rows = slice(r0, min(m, r0 + 2048))
+        y = T.apply_right(Vo, S.storage_to_f64(ws[rows], "bf16"))
+        ref, r, z = Q.codebook_norm_quantize(y, cb, 128)
+        got = Q.unpack(codes_h[rows], 4, n)
+        check_f16_norms(sc_h[rows], r, f"polar {name}")
+        assert np.array_equal(Q.pack(got, 4), codes_h[rows])
+        gots.append(got)
+        refs.append(ref)
+        bands.append(Q.codebook_band(z, cb))
+        back = T.apply_right(Vo, Q.codebook_dequant(got, sc_h[rows], cb, 128), inverse=True)
+        info = check_rotation(out_h[rows], back, "bf16", f"polar {name} dequant")
+        worst = max(worst, info["max_rel_err"])
+    info = check_codes(np.concatenate(gots), np.concatenate(refs), np.concatenate(bands),
+                       f"polar {name} (all rows)", 4)
+    print(f"polar {name}", info, "dequant max rel err", worst, flush=True)
 
 
 def test_llama70b_two_sided():
     import butterfly_rotation_quantization_amd as brq
+    import torch
     announce("70B 8192x28672 two-sided 2-bit g64")
     cfg = S.llama70b()
     w = to_dev(cfg["w"], "bf16")
     U, V = lib_plan(cfg["left"]), lib_plan(cfg["right"])
     codes, scales = brq.rotate_quantize_pack(U, V, w, 2, 64)
     Uo, Vo = orc_plan(cfg["left"]), orc_plan(cfg["right"])
-    rows = sampled_rows(8192, 96, 17)
+    rows = sampled_rows(8192, 256, 17)
     w64 = S.storage_to_f64(cfg["w"], "bf16")
     y = oracle_rows(Uo, Vo, w64, rows)
-    del w64
+    del w64, w
     check_quantized_rows(codes, scales, y, rows, 2, 64, "70B")
+    del y
+    # dequant + unrotate at the same shape, on the same sampled rows
+    out = brq.dequant_unrotate(U, V, codes, scales, 8192, 28672, 2, 64)
+    out_rows = from_dev(out[torch.from_numpy(rows).cuda()])
+    del out
+    allc = Q.unpack(codes.cpu().numpy(), 2, 28672)
+    v = Q.absmax_dequant(allc, scales.cpu().numpy().astype(np.float64), 2, 64)
+    del allc
+    back = T.apply_right(Vo, unit_rows_of_transpose(Uo, rows) @ v, inverse=True,
+                         method="factored")
+    check_rotation(out_rows, back, "f32", "70B dequant")
 
 
 @pytest.mark.parametrize("tokens", [1, 16, 256])

@@ -60,7 +60,7 @@ def test_fused_two_sided(bv, mode, chunks, bits, group, dt, kind):
         ref, r, z = Q.codebook_norm_quantize(y, cb, group)
         band = Q.codebook_band(z, cb)
         check_f16_norms(sc, r, "fused")
-    info = check_codes(got, ref, band, "fused")
+    info = check_codes(got, ref, band, "fused", bits)
     assert np.array_equal(Q.pack(got, bits), codes.cpu().numpy()[rows])
     print(info, flush=True)
 

@@ -45,7 +45,7 @@ def run_case(w_store, dtype, left, right, bits, group, kind="absmax", codebook=N
         ref, r, z = Q.codebook_norm_quantize(y, codebook, group)
         band = Q.codebook_band(z, codebook)
         check_f16_norms(scales.cpu().numpy(), r, what)
-    info = check_codes(got, ref, band, what)
+    info = check_codes(got, ref, band, what, bits)
     # packed stream: identical bytes to the oracle's packing of the same codes
     assert np.array_equal(Q.pack(got, bits), codes_np), f"{what}: packing layout differs"
     # inverse: both sides dequantize the GPU's codes and scales

@@ -57,7 +57,7 @@ def test_requant_parity(m, n, d, bits_in, bits_out, g_out, signs):
     got = Q.unpack(c_out.cpu().numpy(), bits_out, n)
     what = f"requant d={d} b{bits_in}->b{bits_out} g{g_out}"
     check_absmax_scales(a_out.cpu().numpy(), alpha, w, what)
-    info = check_codes(got, ref, Q.absmax_band(w, bits_out, g_out), what)
+    info = check_codes(got, ref, Q.absmax_band(w, bits_out, g_out), what, bits_out)
     assert np.array_equal(Q.pack(got, bits_out), c_out.cpu().numpy())
     print(info, flush=True)
 
@@ -74,7 +74,7 @@ def test_requant_equals_the_two_calls():
     c2, a2 = brq.rotate_quantize_pack(None, None, restored, 4, 128)
     w = restored.cpu().numpy().astype(np.float64)
     band = Q.absmax_band(w, 4, 128)
-    check_codes(Q.unpack(c1.cpu().numpy(), 4, n), Q.unpack(c2.cpu().numpy(), 4, n), band, "fused vs two calls")
+    check_codes(Q.unpack(c1.cpu().numpy(), 4, n), Q.unpack(c2.cpu().numpy(), 4, n), band, "fused vs two calls", 4)
     assert np.abs(a1.cpu().numpy() - a2.cpu().numpy()).max() <= 1e-6 * np.abs(a2.cpu().numpy()).max()
 
 
@@ -92,4 +92,4 @@ def test_requant_polar_projection_full_size():
     ref, alpha, w = C.requant(ci, norms[rows].cpu().numpy(), cb, d, plan_o, 4, 128)
     got = Q.unpack(c_out[rows].cpu().numpy(), 4, n)
     check_absmax_scales(a_out[rows].cpu().numpy(), alpha, w, "full projection")
-    check_codes(got, ref, Q.absmax_band(w, 4, 128), "full projection")
+    check_codes(got, ref, Q.absmax_band(w, 4, 128), "full projection", 4)

@@ -120,7 +120,7 @@ def test_rowhad_quant_dequant(l2d, rows, cpr, bits, group, kind, dt):
         ref, r, z = Q.codebook_norm_quantize(y, cb, group)
         band = Q.codebook_band(z, cb)
         check_f16_norms(scales.cpu().numpy(), r, what)
-    info = check_codes(got, ref, band, what)
+    info = check_codes(got, ref, band, what, bits)
     assert np.array_equal(Q.pack(got, bits), codes.cpu().numpy())
     _profile_on()
     out = brq.dequant_unrotate(None, p, codes, scales, rows, n, bits, group, kind, cb)

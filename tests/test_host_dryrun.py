@@ -480,3 +480,32 @@ def test_qlinear_walk(dl, T, m, n, bits, group, sides):
                           nb, None) == 1
     assert dl.brq_qlinear(lh, rh, X, 0, n, T, CODES, SCALES, ctypes.byref(q), m, n, Y, 2, m, WS,
                           nb, None) == 1
+
+
+# The ORP GEO quantizer and dequantizer: every lane's element run, code
+# bytes, sign bytes and coefficient pairs, each written exactly once; pair
+# partners inside their group and micro-block; ragged last chunks.
+@pytest.mark.parametrize("m,n,bits,group,stride", [
+    (3, 1024, 3, 128, 1), (2, 11008, 3, 128, 4), (4, 1536, 2, 64, 32), (2, 3072, 5, 512, 256),
+    (5, 640, 4, 64, 8), (1, 4096, 4, 256, 2), (2, 1152, 3, 128, 64), (7, 64, 2, 64, 16),
+])
+def test_orp_walk(dl, m, n, bits, group, stride):
+    q = brq.Orp(bits, group, stride)
+    SIGNS, COEF = 0x60000000, 0x70000000
+    for wt in (0, 1):
+        dl.brq_dryrun_reset()
+        st = dl.brq_orp_geo_quantize(X, wt, m, n, n, None, ctypes.byref(q), CODES, SIGNS, COEF, None)
+        _ok(dl, st, f"orp quant {m}x{n} b{bits} g{group} S{stride}")
+        assert dl.brq_dryrun_launches() == 1
+    dl.brq_dryrun_reset()
+    st = dl.brq_orp_geo_dequant(CODES, SIGNS, COEF, ctypes.byref(q), m, n, Y, 1, n, None)
+    _ok(dl, st, f"orp dequant {m}x{n}")
+    # validation: a stride that does not fit the group, a group not dividing n,
+    # misaligned rows
+    bad = brq.Orp(bits, group, group)
+    assert dl.brq_orp_geo_quantize(X, 0, m, n, n, None, ctypes.byref(bad), CODES, SIGNS, COEF,
+                                   None) == 1
+    assert dl.brq_orp_geo_quantize(X, 0, m, n + 8, n + 8, None, ctypes.byref(q), CODES, SIGNS,
+                                   COEF, None) == 1
+    assert dl.brq_orp_geo_quantize(X + 4, 0, m, n, n, None, ctypes.byref(q), CODES, SIGNS, COEF,
+                                   None) == 3

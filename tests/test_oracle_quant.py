@@ -100,6 +100,67 @@ def test_codebook_threshold_search_equals_nearest_centroid():
     assert np.array_equal(by_search, Q.nearest_centroid(z, cb))
 
 
+def _switch_points(cb):
+    """Where the brute-force nearest-centroid search changes its answer,
+    found by bisection on nearest_centroid alone (no threshold formula)."""
+    c = np.asarray(cb, dtype=np.float32).astype(np.float64)
+    pts = []
+    for k in range(len(c) - 1):
+        lo, hi = c[k], c[k + 1]
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if Q.nearest_centroid(np.array([mid]), cb)[0] <= k:
+                lo = mid
+            else:
+                hi = mid
+        pts.append(lo)
+    return np.array(pts)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_codebook_band_sits_on_the_decision_points(bits):
+    """The band of the codebook search lies on the points where the nearest
+    centroid changes: points 0.5 band widths from each switching point are in
+    it, points 3 widths away are not; the width is 1e-6 relative, floored at
+    1e-6 of the smallest centroid gap, so it is not empty at the threshold 0."""
+    cb = LM.lloyd_max_gaussian(bits)[0].astype(np.float32)
+    sw = _switch_points(cb)
+    assert len(sw) == (1 << bits) - 1
+    gap = float(np.diff(cb.astype(np.float64)).min())
+    width = Q.BAND_REL * np.maximum(np.abs(sw), gap)
+    mid = (1 << bits) // 2 - 1
+    assert abs(sw[mid]) < 1e-15 and width[mid] > 0  # the middle threshold is 0
+    for f in (-0.5, 0.5):
+        assert Q.codebook_band(sw + f * width, cb).all()
+    for f in (-3.0, 3.0):
+        assert not Q.codebook_band(sw + f * width, cb).any()
+    # far from every switching point: never in the band
+    far = 0.5 * (sw[:-1] + sw[1:])
+    assert not Q.codebook_band(far, cb).any()
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5])
+@pytest.mark.parametrize("decide_f32", [True, False])
+def test_codebook_codes_equal_brute_force_outside_band(bits, decide_f32):
+    """codebook_norm_quantize's codes equal the brute-force nearest centroid
+    of z = sqrt(g) v / ||v|| (computed in float64) everywhere outside the
+    band, on Gaussian and heavy-tailed blocks, scaled over decades."""
+    cb = LM.lloyd_max_gaussian(bits)[0].astype(np.float32)
+    rng = np.random.default_rng(40 + bits)
+    g = 128
+    v = rng.standard_normal((400, 4 * g))
+    v[:200] *= np.where(rng.random((200, 4 * g)) < 0.01, 10.0, 1.0)
+    v *= 10.0 ** rng.uniform(-3, 2, size=(400, 1))
+    v = v.astype(np.float32).astype(np.float64)
+    codes, r, z = Q.codebook_norm_quantize(v, cb, g, decide_f32=decide_f32)
+    vg = v.reshape(400, 4, g)
+    z_bf = (np.sqrt(g) * vg / np.linalg.norm(vg, axis=2, keepdims=True)).reshape(400, -1)
+    ref = Q.nearest_centroid(z_bf, cb)
+    band = Q.codebook_band(z_bf, cb)
+    assert np.array_equal(codes[~band], ref[~band])
+    assert band.mean() < 1e-4
+
+
 def test_polar_block_identities():
     """PolarQuant section 2: normalise the block onto the unit sphere, rotate
     by the Walsh-Hadamard matrix, scale by sqrt(d): sum z^2 = d; H/sqrt(d) is
