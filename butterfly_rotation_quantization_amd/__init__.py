@@ -38,6 +38,7 @@ EXPORTED = (
     "brq_profile_read", "brq_set_path", "brq_harp_blocks", "brq_harp_blocks_batch", "brq_plan_create_harp",
     "brq_plan_serialize", "brq_plan_deserialize", "brq_requant_workspace_bytes", "brq_requant",
     "brq_qlinear_workspace_bytes", "brq_qlinear", "brq_orp_geo_quantize", "brq_orp_geo_dequant",
+    "brq_qlinear_noalloc_limit", "brq_qlinear_noalloc",
 )
 
 
@@ -143,6 +144,12 @@ def bind(lib):
         lib.brq_qlinear.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, ctypes.POINTER(Quant), i64,
                                     i64, vp, i32, i64, vp, sz, vp]
         lib.brq_qlinear.restype = i32
+    if hasattr(lib, "brq_qlinear_noalloc"):
+        lib.brq_qlinear_noalloc_limit.argtypes = []
+        lib.brq_qlinear_noalloc_limit.restype = sz
+        lib.brq_qlinear_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, ctypes.POINTER(Quant),
+                                            i64, i64, vp, i32, i64, vp]
+        lib.brq_qlinear_noalloc.restype = i32
     if hasattr(lib, "brq_orp_geo_quantize"):
         lib.brq_orp_geo_quantize.argtypes = [vp, i32, i64, i64, i64, vp, ctypes.POINTER(Orp), vp, vp,
                                              vp, vp]
@@ -462,6 +469,21 @@ def qlinear(left: Optional[Plan], right: Optional[Plan], x, codes, scales, m: in
     check(L.brq_qlinear(_h(left), _h(right), _ptr(x), dtype_code(x), _ld(x), T, _ptr(codes),
                         _ptr(scales), ctypes.byref(q), int(m), int(n), _ptr(y), dtype_code(y),
                         _ld(y), wp, wb, _stream(stream)))
+    return y
+
+
+def qlinear_noalloc(left: Optional[Plan], right: Optional[Plan], x, codes, scales, m: int, n: int,
+                    bits: int, group: int, y=None, out_dtype=None, stream=None):
+    """brq_qlinear without a workspace (brq_qlinear_noalloc): the library's
+    per-device scratch array is used; returns y [T, m]."""
+    import torch
+    T = int(x.shape[0])
+    q = make_quant(bits, group, "absmax")
+    if y is None:
+        y = torch.empty((T, m), dtype=out_dtype or x.dtype, device=x.device)
+    check(lib().brq_qlinear_noalloc(_h(left), _h(right), _ptr(x), dtype_code(x), _ld(x), T,
+                                    _ptr(codes), _ptr(scales), ctypes.byref(q), int(m), int(n),
+                                    _ptr(y), dtype_code(y), _ld(y), _stream(stream)))
     return y
 
 

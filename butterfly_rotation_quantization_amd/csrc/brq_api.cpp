@@ -47,6 +47,12 @@ brq_status hip_fail(hipError_t e, const char* what) {
   return fail(BRQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+brq_status report_error(brq_status s, const char* msg) { return fail(s, "%s", msg); }
+
+namespace {
+
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 std::atomic<int> g_path{BRQ_PATH_AUTO};

@@ -107,6 +107,10 @@ hipError_t rt_copy_to_host(void* dst, const void* src, size_t bytes);
 hipError_t rt_cu_count(int dev, int* cus);
 void rt_free(void* p);
 
+// Set this thread's brq_last_error text and return `s` (for entry points
+// defined outside the host layer's file).
+brq_status report_error(brq_status s, const char* msg);
+
 // Kernel timing (brq_profile_*): bracket a launch with events on its stream
 // when profiling is enabled; both calls are no-ops otherwise.
 int prof_begin(const char* name, hipStream_t s);

@@ -298,6 +298,26 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * brq_qlinear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, kernels and results as brq_qlinear, without the `ws`
+ * argument.  Its scratch is a device array of brq_qlinear_noalloc_limit()
+ * bytes (64 MiB) inside the library, one per GPU, held until the process
+ * ends; the call allocates nothing.  A call whose brq_qlinear_workspace_bytes
+ * exceeds the limit returns BRQ_ERR_WORKSPACE (at the 70B down projection,
+ * 8192 x 28672 with 2-bit groups of 64, up to 128 tokens fit).  Every call on
+ * one GPU uses that GPU's array: calls that overlap on one GPU (other streams
+ * or threads) race and must be serialised by the caller.  Nothing in the
+ * array needs to start at zero; it keeps the last call's contents.  Errors:
+ * as brq_qlinear, plus WORKSPACE for a call beyond the limit.
+ */
+size_t brq_qlinear_noalloc_limit(void);
+brq_status brq_qlinear_noalloc(const brq_plan* left, const brq_plan* right, const void* x,
+                               int32_t xt, int64_t ldx, int64_t T, const uint8_t* codes,
+                               const void* scales, const brq_quant* q, int64_t m, int64_t n,
+                               void* y, int32_t yt, int64_t ldy, void* stream);
+
+/*
  * ORP GEO quantizer ([ORPQuant] technical summary, section 2: the geometric
  * discrete basis search and the GEO scales).  Per group of `group`
  * consecutive inputs w of a row, after the optional preconditioning
