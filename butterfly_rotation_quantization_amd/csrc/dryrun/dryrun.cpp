@@ -342,12 +342,22 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
       if (t.r0 < 0 || t.r0 >= a.nrb || a.nrb * 256 != a.m || t.c0 < 0 || t.c0 >= a.bv || t.chunk < 0 ||
           t.chunk >= a.nchunk)
         return violation("pass B tile %lld of %lld", tile, ntiles), hipErrorInvalidValue;
+      {  // each staged block's quads are a permutation of its 64 slots
+        std::vector<int> seen(256, 0);
+        for (int qd = 0; qd < 64; ++qd) {
+          const int o = fb_vslot(qd >> 2, qd & 3);
+          if (o < 0 || o + 4 > 256 || o % 4) return violation("V block slot %lld of quad %lld", o, qd), hipErrorInvalidValue;
+          for (int j = 0; j < 4; ++j) seen[o + j]++;
+        }
+        for (int i = 0; i < 256; ++i)
+          if (seen[i] != 1) return violation("V block float %lld staged %lld times", i, seen[i]), hipErrorInvalidValue;
+      }
       // block staging into LDS
       for (int k = 0; k < 2 * 16 * 64; ++k) {
         const int which = k >> 10, rem = k & 1023, f = rem >> 6, qd = rem & 63;
         const int64_t src = (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs) + 4 * qd;
         if (!in_range(src, 4, which ? a.v2_n : a.v1_n)) return violation("V block staging %lld", src, which), hipErrorInvalidValue;
-        const int dst = (which ? kFbV2Off : kFbV1Off) + f * 256 + 4 * qd;
+        const int dst = (which ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(qd >> 2, qd & 3);
         if (!in_range(dst, 4, kFbLdsFloats) || (which == 0 && dst + 4 > kFbXchFloats))
           return violation("V block LDS slot %lld", dst, which), hipErrorInvalidValue;
       }
@@ -369,8 +379,8 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
               !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg, 4, a.u2_n))
             return violation("U_1/U_2 block read wave %lld lane %lld", w, l), hipErrorInvalidValue;
           for (int c = 0; c < 16; ++c) {
-            if (!in_range(kFbV1Off + c * 256 + fb_sigma(lr) * 16 + 4 * lg, 4, kFbXchFloats) ||
-                !in_range(kFbV2Off + c * 256 + lr * 16 + 4 * lg, 4, kFbLdsFloats))
+            if (!in_range(kFbV1Off + c * 256 + fb_vslot(fb_sigma(lr), lg), 4, kFbXchFloats) ||
+                !in_range(kFbV2Off + c * 256 + fb_vslot(lr, lg), 4, kFbLdsFloats))
               return violation("V block LDS read %lld lane %lld", c, l), hipErrorInvalidValue;
           }
         }

@@ -228,14 +228,25 @@ __host__ __device__ inline FbTile fb_tile(const FusedBArgs& a, int64_t b) {
 
 // Exchange slot of element (r1, c1h, r2, c2), c1h = c1 - 8 h.  Each float4
 // holds four consecutive c2; within every 16 float4s (r1, c1h and r2 / 4
-// fixed) the quad index (r2 % 4, c2 / 4) is XORed with r1 and r2 / 4.  The 16
-// lanes of a row group then hit 16 different bank groups both on the phase-1
+// fixed) the quad index takes r2 % 4 XOR r1 % 4 in its low two bits and
+// c2 / 4 XOR r2 / 4 XOR r1 / 4 in its high two.  Every 8 and every 16
+// consecutive lanes then hit distinct bank groups both on the phase-1
 // writes (lanes over r1 at fixed c1h, r2, c2 / 4) and on the phase-2 reads
-// (lanes over r2 at fixed r1, c1h, c2 / 4).
+// and write-backs (lanes over r2 at fixed r1, c1h, c2 / 4).
 __host__ __device__ inline int fb_xch(int r1, int c1h, int r2, int c2) {
   const int hi = (r1 * 8 + c1h) * 4 + (r2 >> 2);
-  const int lo = (((r2 & 3) * 4 + (c2 >> 2)) ^ (r2 >> 2) ^ r1) & 15;
+  const int lo = ((r2 & 3) ^ (r1 & 3)) | ((((c2 >> 2) ^ (r2 >> 2) ^ (r1 >> 2)) & 3) << 2);
   return (hi * 16 + lo) * 4 + (c2 & 3);
+}
+
+// Float offset of quad q (columns 4q .. 4q + 3) of row j of a 16 x 16 V block
+// staged in LDS.  The quad index is XORed with ((j >> 1) & 3) ^ ((j >> 3) & 1),
+// so that the 16-byte reads of V_1 (lanes lr over rows fb_sigma(lr)) and of
+// V_2 (lanes over rows lr), at a fixed quad, fall on distinct bank groups
+// for every 8 and every 16 consecutive lanes; unswizzled, the 64-byte row
+// stride put the lanes of a read on two bank groups.
+__host__ __device__ inline int fb_vslot(int j, int q) {
+  return (j * 4 + (q ^ (((j >> 1) & 3) ^ ((j >> 3) & 1)))) * 4;
 }
 
 // Row order of the V_1 products: output tile row n holds c1' = fb_sigma(n),

@@ -371,13 +371,14 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
     for (int k = tid; k < 2 * 16 * 64; k += kFbWaves * 64) {
       const int which = k >> 10, rem = k & 1023, f = rem >> 6, qd = rem & 63;
       const float* src = (which ? a.v2 : a.v1) + (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs);
-      *reinterpret_cast<f4*>(&lds[(which ? kFbV2Off : kFbV1Off) + f * 256 + 4 * qd]) = ld4(src + 4 * qd);
+      *reinterpret_cast<f4*>(&lds[(which ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(qd >> 2, qd & 3)]) =
+          ld4(src + 4 * qd);
     }
     __syncthreads();
 
     // ---- phase 1: this wave owns r2 = w; fragments over (r1, c1), one per c2.
     lanes();
-    const int v1_lane = kFbV1Off + fb_sigma(lr) * 16 + 4 * lg;
+    const int v1_lane = kFbV1Off + fb_vslot(fb_sigma(lr), lg);
 #pragma unroll
     for (int c2q = 0; c2q < 16; c2q += FB_IL) {
       f4 d[FB_IL];
@@ -399,9 +400,8 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
 
     // ---- phase 2: this wave owns r1 = w; fragments over (r2, c2), one per c1.
     const int64_t next = tile + gridDim.x;
-    // past the last tile, prefetch tile 0: every workgroup ending there reads
-    // the same block, which then comes from cache instead of HBM
-    const FbTile tn = fb_tile(a, next < ntiles ? next : 0);
+    const bool more = next < ntiles;  // uniform over the workgroup
+    const FbTile tn = fb_tile(a, more ? next : tile);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       lanes();
@@ -418,9 +418,8 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
           *reinterpret_cast<f4*>(&xch[fb_xch(lro, lgo + 4 * e, w, 4 * qd)]) = q4;
         }
       // after the second half every tile register is free: load the whole
-      // next tile (past the last one, tile 0, which keeps this code free of
-      // branches)
-      if (h == 1) {
+      // next tile
+      if (h == 1 && more) {
         fb_load_half<0>(a, tn, w, lro, lgo, x);
         fb_load_half<1>(a, tn, w, lro, lgo, x);
       }
@@ -437,7 +436,7 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
 #pragma unroll
         for (int f = 0; f < FB_IL2; ++f) {
           const f4 av = ld4(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]);  // c2 = 4lg + i, r2 = lr
-          const f4 bv2 = ld4(&lds[kFbV2Off + (8 * h + c1q + f) * 256 + lr * 16 + 4 * lg]);
+          const f4 bv2 = ld4(&lds[kFbV2Off + (8 * h + c1q + f) * 256 + fb_vslot(lr, lg)]);
           d[f] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) d[f] = mfma4(av[i], bv2[i], d[f]);  // V_2: c2
@@ -457,7 +456,7 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
       lanes();
       fb_quantize<BITS, QK, G>(a, t, w, h, xch, stat, lr, lg);
     }
-    if (next >= ntiles) break;
+    if (!more) break;
     lanes();
     bu1 = ld4(a.u1 + (int64_t)(tn.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg);
     bu2 = ld4(a.u2 + (int64_t)(tn.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg);
