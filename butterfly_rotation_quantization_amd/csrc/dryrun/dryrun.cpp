@@ -866,7 +866,7 @@ hipError_t launch_stage_pair2(const P2Args& a, hipStream_t) {
   ++g_launches;
   ++g_pair2_launches;
   const int n = a.bo * a.bi;
-  if (a.bo < 2 || a.bi < 2 || a.bo > 16 || a.bi > 16 || n > 256 || a.sets != 256 / n || a.sets < 1 ||
+  if (a.bo < 2 || a.bi < 2 || a.bo > 16 || a.bi > 16 || n > 256 || a.sets > 256 / n || a.sets < 1 ||
       a.lines < 1 || a.lines > kP2MaxLines || a.Si < 1 || a.d % (n * a.Si))
     return violation("stage pair geometry (bo %lld, bi %lld)", a.bo, a.bi), hipErrorInvalidValue;
   const int64_t per_chunk = a.d / (n * a.Si) * a.Si;

@@ -261,7 +261,7 @@ struct P2Args {
   int64_t Si;              // inner stride (outer: bo's stride bi * Si)
   int64_t d;               // plan dimension
   int64_t nsets;           // sets per row: (cols / d) * (d / (bo bi Si)) * Si
-  int sets;                // sets per workgroup
+  int sets;                // sets per workgroup (at most 256 / (bo bi))
   int inner_first;         // inverse order
   int per_group;           // blocks per group (else one shared block per stage)
   const float* blk_o;      // outer stage blocks [group][j][k] (groups hi Si bi... as in the plan)

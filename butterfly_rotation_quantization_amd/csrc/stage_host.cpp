@@ -178,6 +178,8 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
         q.d = p->d;
         q.nsets = (cols / p->d) * (p->d / (q.bo * q.bi * q.Si)) * q.Si;
         q.sets = 256 / (q.bo * q.bi);
+        // fewer workgroups than compute units: one set per workgroup
+        if (p2_blocks(q) < 256) q.sets = 1;
         q.inner_first = inverse ? 1 : 0;
         q.per_group = p->mode == BRQ_PER_GROUP ? 1 : 0;
         const float* base = inverse ? p->blkT : p->blk;
