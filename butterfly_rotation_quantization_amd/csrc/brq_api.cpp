@@ -1442,6 +1442,16 @@ brq_status orp_outputs_ok(const uint8_t* codes, const uint8_t* signs, const floa
 
 size_t dtype_bytes(int t) { return t == BRQ_F32 ? 4 : 2; }
 
+void orp_strides(OrpArgs& a) {
+  a.lg_group = 0;
+  while ((1 << a.lg_group) < a.group) ++a.lg_group;
+  a.lg_stride = 0;
+  while ((1 << a.lg_stride) < a.stride) ++a.lg_stride;
+  a.codes_ld = a.n * a.bits / 8;
+  a.signs_ld = a.n / 16;
+  a.coef_ld = 2 * (a.n / a.group);
+}
+
 }  // namespace
 
 brq_status brq_orp_geo_quantize(const void* w, int32_t wt, int64_t m, int64_t n, int64_t ldw,
@@ -1452,6 +1462,7 @@ brq_status brq_orp_geo_quantize(const void* w, int32_t wt, int64_t m, int64_t n,
   if (m < 0 || n < 0 || ldw < n) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape or leading dimension");
   brq_status st = check_orp(q, n);
   if (st != BRQ_OK) return st;
+  if (n >= ((int64_t)1 << 31)) return fail(BRQ_ERR_UNSUPPORTED, "rows longer than 2^31 elements");
   if (m == 0 || n == 0) return BRQ_OK;
   if (!w) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
   if ((st = orp_outputs_ok(codes, signs, coef)) != BRQ_OK) return st;
@@ -1471,6 +1482,7 @@ brq_status brq_orp_geo_quantize(const void* w, int32_t wt, int64_t m, int64_t n,
   a.group = q->group;
   a.stride = q->stride;
   a.chunks = (n + kOrpChunk - 1) / kOrpChunk;
+  orp_strides(a);
   a.codes = codes;
   a.signs = signs;
   a.coef = coef;
@@ -1492,6 +1504,7 @@ brq_status brq_orp_geo_dequant(const uint8_t* codes, const uint8_t* signs, const
   if (m < 0 || n < 0 || ldo < n) return fail(BRQ_ERR_INVALID_ARGUMENT, "bad shape or leading dimension");
   brq_status st = check_orp(q, n);
   if (st != BRQ_OK) return st;
+  if (n >= ((int64_t)1 << 31)) return fail(BRQ_ERR_UNSUPPORTED, "rows longer than 2^31 elements");
   if (m == 0 || n == 0) return BRQ_OK;
   if (!out) return fail(BRQ_ERR_INVALID_ARGUMENT, "NULL data pointer");
   if ((st = orp_outputs_ok(codes, signs, coef)) != BRQ_OK) return st;
@@ -1505,6 +1518,7 @@ brq_status brq_orp_geo_dequant(const uint8_t* codes, const uint8_t* signs, const
   a.group = q->group;
   a.stride = q->stride;
   a.chunks = (n + kOrpChunk - 1) / kOrpChunk;
+  orp_strides(a);
   a.codes = const_cast<uint8_t*>(codes);
   a.signs = const_cast<uint8_t*>(signs);
   a.coef = const_cast<float*>(coef);

@@ -1075,17 +1075,26 @@ static hipError_t walk_orp(const OrpArgs& a, bool quant) {
     return violation("ORP geometry (group %lld, stride %lld)", g, S), hipErrorInvalidValue;
   if (a.chunks != (a.n + kOrpChunk - 1) / kOrpChunk)
     return violation("ORP chunks per row %lld for n %lld", a.chunks, a.n), hipErrorInvalidValue;
+  if ((1 << a.lg_group) != g || (1 << a.lg_stride) != S || a.codes_ld != a.n * bits / 8 ||
+      a.signs_ld != a.n / 16 || a.coef_ld != 2 * (a.n / g) || a.n >= ((int64_t)1 << 31))
+    return violation("ORP strides (log2 group %lld, log2 stride %lld)", a.lg_group, a.lg_stride), hipErrorInvalidValue;
+  for (int64_t i = 0; i < 4 * S + 64; ++i)  // the shift form of the pair number
+    if (orp_pair(i, S) % (2 * S) < S && (int64_t)orp_pair_lg((uint32_t)i, a.lg_stride) != orp_pair(i, S))
+      return violation("ORP pair number of %lld", i, S), hipErrorInvalidValue;
   const int lpg = g / kOrpPerLane;
   const int64_t cb = a.n * bits / 8, sb = a.n / 16, ng = a.n / g;
   std::vector<uint8_t> code_cov((size_t)(a.m * cb), 0), sign_cov((size_t)(a.m * sb), 0);
   std::vector<uint8_t> coef_cov((size_t)(a.m * ng), 0), elem_cov((size_t)(a.m * a.n), 0);
-  const int64_t waves = orp_waves(a);
-  if (orp_blocks(a) * (kOrpThreads / 64) < waves)
-    return violation("ORP grid of %lld blocks for %lld waves", orp_blocks(a), waves), hipErrorInvalidValue;
-  for (int64_t wv = 0; wv < waves; ++wv) {
+  const int64_t waves = orp_waves(a), total = orp_total_chunks(a);
+  if (orp_blocks(a) * (kOrpThreads / 64) < waves || waves * kOrpChunksPerWave < total)
+    return violation("ORP grid of %lld blocks for %lld chunks", orp_blocks(a), total), hipErrorInvalidValue;
+  for (int64_t wv = 0; wv < waves; ++wv)
+  for (int jc = 0; jc < kOrpChunksPerWave; ++jc) {
+    const int64_t ci = wv * kOrpChunksPerWave + jc;
+    if (ci >= total) break;
     int64_t row, c0;
-    orp_wave(a, wv, &row, &c0);
-    if (row < 0 || row >= a.m || c0 % g) return violation("ORP wave %lld at row %lld", wv, row), hipErrorInvalidValue;
+    orp_chunk(a, ci, &row, &c0);
+    if (row < 0 || row >= a.m || c0 % g) return violation("ORP chunk %lld at row %lld", ci, row), hipErrorInvalidValue;
     for (int lane = 0; lane < 64; ++lane) {
       const int64_t col = c0 + kOrpPerLane * lane;
       const bool valid = col < a.n;

@@ -18,6 +18,7 @@ namespace brq {
 constexpr int kOrpThreads = 256;  // four wavefronts per workgroup
 constexpr int kOrpPerLane = 8;
 constexpr int kOrpChunk = 64 * kOrpPerLane;
+constexpr int kOrpChunksPerWave = 4;  // consecutive chunks, all loads issued first
 
 struct OrpArgs {
   // quantize input
@@ -29,6 +30,8 @@ struct OrpArgs {
   int64_t m, n;
   int bits, group, stride;
   int64_t chunks;       // kOrpChunk-element chunks per row: ceil(n / kOrpChunk)
+  int lg_group, lg_stride;  // log2 of group and stride
+  int64_t codes_ld, signs_ld, coef_ld;  // per row: n*bits/8 bytes, n/16 bytes, 2*n/group floats
   // quantize outputs / dequant inputs
   uint8_t* codes;       // [m][n*bits/8]
   uint8_t* signs;       // [m][n/16]: one bit per pair
@@ -44,14 +47,22 @@ struct OrpArgs {
 __host__ __device__ inline int64_t orp_pair(int64_t i, int S) {
   return (i / (2 * S)) * S + (i % (2 * S));
 }
-
-// Wavefront w of the grid: its row and the first column of its chunk.
-__host__ __device__ inline void orp_wave(const OrpArgs& a, int64_t w, int64_t* row, int64_t* c0) {
-  *row = w / a.chunks;
-  *c0 = (w - *row * a.chunks) * kOrpChunk;
+// The same for S = 2^lg (32-bit column indices).
+__host__ __device__ inline uint32_t orp_pair_lg(uint32_t i, int lg) {
+  return ((i >> (lg + 1)) << lg) + (i & ((2u << lg) - 1));
 }
 
-inline int64_t orp_waves(const OrpArgs& a) { return a.m * a.chunks; }
+// Chunk ci (0 <= ci < m * chunks, row-major): its row and first column.
+// Wavefront w takes chunks w * kOrpChunksPerWave .. + kOrpChunksPerWave - 1.
+__host__ __device__ inline void orp_chunk(const OrpArgs& a, int64_t ci, int64_t* row, int64_t* c0) {
+  *row = ci / a.chunks;
+  *c0 = (ci - *row * a.chunks) * kOrpChunk;
+}
+
+__host__ __device__ inline int64_t orp_total_chunks(const OrpArgs& a) { return a.m * a.chunks; }
+inline int64_t orp_waves(const OrpArgs& a) {
+  return (orp_total_chunks(a) + kOrpChunksPerWave - 1) / kOrpChunksPerWave;
+}
 inline int64_t orp_blocks(const OrpArgs& a) {
   return (orp_waves(a) + kOrpThreads / 64 - 1) / (kOrpThreads / 64);
 }
