@@ -26,20 +26,23 @@ struct Plan {
   float* blkT = nullptr;             // the same blocks transposed, for the inverse
   float* signs = nullptr;            // +-1 as float, or nullptr
   // Fast-path data (fused_prepare), for plans of the shape (b0, 16, 16):
-  // stage-0 blocks zero-padded to [groups][16*fz_nb][16*fz_nb], block
-  // pointers of stages 1 and 2, and float strides between groups (0 = one
-  // block shared by all groups).
+  // stage-0 blocks zero-padded to [groups][16*fz_nb][16*fz_nb] and the float
+  // stride between groups (0 = one block shared by all groups).
   int fz_ok = 0;
   int fz_b0 = 0;                     // radix of the fast path's stage 0 (d = fz_b0 * 256)
   int fz_nb = 0;
   float* fz0 = nullptr;
   float* fz0f = nullptr;             // the same blocks in MFMA fragment order (fused.h)
   int64_t fz_gs0 = 0;
-  const float* fz1 = nullptr;
-  int64_t fz_gs1 = 0;
-  const float* fz2 = nullptr;
-  int64_t fz_gs2 = 0;
-  float* fz_had = nullptr;           // Hadamard blocks materialised for stages 1 and 2
+  // Pass B's blocks (the last two stages when both are radix 16) split into
+  // f16 pairs, laid out as fused.h describes: stage nst-2 first, stage nst-1
+  // at fzh_off2 halves; fzh_gs halves between groups (0 = shared).  Only
+  // set when every block row has norm at most 1 + 1e-3.
+  uint16_t* fzh = nullptr;
+  int64_t fzh_off2 = 0;
+  int64_t fzh_gs = 0;
+  int64_t fzh_n = 0;                 // halves per stage
+  int fzh_exact = 0;                 // every entry exact in f16
 };
 
 // One stage applied inside a pass, along one axis of the tile.

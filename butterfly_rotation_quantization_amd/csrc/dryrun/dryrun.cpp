@@ -330,6 +330,15 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
   const int bits = a.bits, g = a.group;
   const int fpg = g / 16, nw = fpg * 16 * bits / 32;
   std::vector<int> tiles_seen((size_t)ntiles, 0);
+  for (int e = 0; e < 255; ++e) {  // the tile scale puts every maximum in [64, 128), or scales by 2^127
+    const float mlo = e ? std::ldexp(1.0f, e - 127) : 0.0f;
+    uint32_t bits;
+    std::memcpy(&bits, &mlo, 4);
+    const int ks = fb_scale_shift(bits), ks2 = fb_scale_shift(bits | 0x7fffffu);
+    if (ks != ks2 || ks > 127 || ks < -126) return violation("tile scale of exponent %lld: %lld", e, ks), hipErrorInvalidValue;
+    if (e >= 6 && (std::ldexp((double)mlo, ks) != 64.0)) return violation("tile scale of exponent %lld", e, ks), hipErrorInvalidValue;
+    if (e < 6 && ks != 127) return violation("tile scale of small exponent %lld", e, ks), hipErrorInvalidValue;
+  }
   {  // the V_1 row order is a permutation of the 16 rows
     int seen = 0;
     for (int n = 0; n < 16; ++n) seen |= 1 << fb_sigma(n);
@@ -352,14 +361,24 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
         for (int i = 0; i < 256; ++i)
           if (seen[i] != 1) return violation("V block float %lld staged %lld times", i, seen[i]), hipErrorInvalidValue;
       }
-      // block staging into LDS
+      // block staging into LDS: (bh, bh) entries, and (bl, bl) unless exact;
+      // the maxima between the V_1 blocks and the end of the exchange buffer
+      if (kFbV1LOff + 16 * 256 > kFbMaxOff || kFbMaxOff + 16 > kFbXchFloats || kFbV2Off != kFbXchFloats ||
+          kFbV2LOff != kFbV2Off + 16 * 256 || kFbLdsFloats != kFbV2LOff + 16 * 256 ||
+          kFbLdsFloats * 4 > 160 * 1024)
+        return violation("pass B LDS layout", 0, 0), hipErrorInvalidValue;
       for (int k = 0; k < 2 * 16 * 64; ++k) {
         const int which = k >> 10, rem = k & 1023, f = rem >> 6, qd = rem & 63;
-        const int64_t src = (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs) + 4 * qd;
-        if (!in_range(src, 4, which ? a.v2_n : a.v1_n)) return violation("V block staging %lld", src, which), hipErrorInvalidValue;
+        const int64_t src = (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs) + fb_hentry(qd >> 2, qd & 3);
+        if (!in_range(src, 8, which ? a.v2_n : a.v1_n) || src % 8)
+          return violation("V block staging %lld", src, which), hipErrorInvalidValue;
         const int dst = (which ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(qd >> 2, qd & 3);
-        if (!in_range(dst, 4, kFbLdsFloats) || (which == 0 && dst + 4 > kFbXchFloats))
+        if (!in_range(dst, 4, kFbLdsFloats) || (which == 0 && dst + 4 > kFbV1LOff) ||
+            (which == 1 && dst + 4 > kFbV2LOff) || dst % 4)
           return violation("V block LDS slot %lld", dst, which), hipErrorInvalidValue;
+        const int dl = (which ? kFbV2LOff : kFbV1LOff) + f * 256 + fb_vslot(qd >> 2, qd & 3);
+        if (!in_range(dl, 4, kFbLdsFloats) || (which == 0 && dl + 4 > kFbMaxOff) || dl % 4)
+          return violation("V bl LDS slot %lld", dl, which), hipErrorInvalidValue;
       }
       for (int w = 0; w < kFbWaves; ++w)
         for (int l = 0; l < 64; ++l) {
@@ -375,12 +394,14 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
                   return violation("pass B load (%lld, %lld)", row, col), hipErrorInvalidValue;
                 for (int j = 0; j < 4; ++j) cover[(size_t)(off + j)]++;
               }
-          if (!in_range((int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg, 4, a.u1_n) ||
-              !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg, 4, a.u2_n))
+          if (!in_range((int64_t)(t.r0 * 16 + w) * a.u1_gs + fb_hentry(lr, lg), 8, a.u1_n) ||
+              !in_range((int64_t)(t.r0 * 16 + w) * a.u2_gs + fb_hentry(lr, lg), 8, a.u2_n))
             return violation("U_1/U_2 block read wave %lld lane %lld", w, l), hipErrorInvalidValue;
           for (int c = 0; c < 16; ++c) {
-            if (!in_range(kFbV1Off + c * 256 + fb_vslot(fb_sigma(lr), lg), 4, kFbXchFloats) ||
-                !in_range(kFbV2Off + c * 256 + fb_vslot(lr, lg), 4, kFbLdsFloats))
+            if (!in_range(kFbV1Off + c * 256 + fb_vslot(fb_sigma(lr), lg), 4, kFbV1LOff) ||
+                !in_range(kFbV2Off + c * 256 + fb_vslot(lr, lg), 4, kFbV2LOff) ||
+                !in_range(kFbV1LOff + c * 256 + fb_vslot(fb_sigma(lr), lg), 4, kFbMaxOff) ||
+                !in_range(kFbV2LOff + c * 256 + fb_vslot(lr, lg), 4, kFbLdsFloats))
               return violation("V block LDS read %lld lane %lld", c, l), hipErrorInvalidValue;
           }
         }

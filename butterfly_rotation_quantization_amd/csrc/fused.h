@@ -10,7 +10,13 @@
 //  pass B: the remaining radix-16 stages U_1, U_2, V_1, V_2 on a 256 x 256
 //          block (rows r0*256 + [0,256), columns c0*256 + [0,256)) held in
 //          registers, with one LDS exchange, then the group quantizer and
-//          LSB-first packing.
+//          LSB-first packing.  Its products run on f16 MFMA with split
+//          operands: the tile is scaled by a power of two so that its
+//          largest magnitude lies in [64, 128); every stage splits its
+//          float32 data x into hi = f16(x) and lo = f16(x - hi) and uses the
+//          blocks split the same way (bh, bl, prepared with the plan), and
+//          sums (hi + lo)*bh + (hi + lo)*bl in float32.  Blocks whose
+//          entries are all exact in f16 (Hadamard) need (hi + lo)*bh only.
 //
 // The index arithmetic both kernels use lives here as __host__ __device__
 // functions so the host dry run checks exactly what the GPU executes.
@@ -24,12 +30,24 @@ constexpr int kFaWaves = 8;            // pass A: waves per workgroup
 constexpr int kFaQC = 8;               // pass A: q values per workgroup (looped)
 constexpr int kFbWaves = 16;           // pass B: waves per workgroup
 // pass B LDS: the exchange buffer [r1 16][c1h 8][r2 16][c2 16] (swizzled),
-// whose first 16 KB hold the tile's 16 V_1 blocks during phase 1, then the
-// tile's 16 V_2 blocks.
+// whose first 32 KB hold the tile's 16 V_1 blocks during phase 1, then the
+// tile's 16 V_2 blocks.  A staged block is 64 entries of (bh, bh) and, for
+// blocks that are not exact in f16, 64 entries of (bl, bl), 16 bytes each at
+// fb_vslot.  The 16 waves' tile maxima pass through the exchange buffer
+// after the V_1 blocks (free until phase 2).  160 KB in all.
 constexpr int kFbXchFloats = 16 * 8 * 16 * 16;
 constexpr int kFbV1Off = 0;
+constexpr int kFbV1LOff = kFbV1Off + 16 * 256;
+constexpr int kFbMaxOff = kFbV1LOff + 16 * 256;
 constexpr int kFbV2Off = kFbXchFloats;
-constexpr int kFbLdsFloats = kFbV2Off + 16 * 256;
+constexpr int kFbV2LOff = kFbV2Off + 16 * 256;
+constexpr int kFbLdsFloats = kFbV2LOff + 16 * 256;
+
+// Split-f16 blocks of pass B's four stages: block c of a stage is 16 rows x
+// 4 quads of 8 halves, entry (j, q) = (bh[j][4q .. 4q+3], bl[j][4q .. 4q+3])
+// at halves offset c * kFbBlockHalves + fb_hentry(j, q).
+constexpr int kFbBlockHalves = 512;
+__host__ __device__ constexpr int fb_hentry(int j, int q) { return (j * 4 + q) * 8; }
 
 struct FusedAArgs {
   const void* w;      // input [m][n], type wt, leading dimension ldw
@@ -55,10 +73,13 @@ struct FusedBArgs {
   int nrb;            // 256-row blocks r0: m / 256
   int bv;             // 256-column blocks c0 per d_V (the radix of V_0 after pass A)
   int nchunk, dv;
-  const float* u1; int64_t u1_gs;  // U_1 blocks [256][16][16], group r0*16 + r2
-  const float* u2; int64_t u2_gs;  // U_2 blocks, group r0*16 + r1
-  const float* v1; int64_t v1_gs;  // V_1 blocks, group c0*16 + c2
-  const float* v2; int64_t v2_gs;  // V_2 blocks, group c0*16 + c1
+  // split-f16 blocks (entries as above); strides between groups in halves
+  // (0 = one block shared by all groups)
+  const uint16_t* u1; int64_t u1_gs;  // U_1, group r0*16 + r2
+  const uint16_t* u2; int64_t u2_gs;  // U_2, group r0*16 + r1
+  const uint16_t* v1; int64_t v1_gs;  // V_1, group c0*16 + c2
+  const uint16_t* v2; int64_t v2_gs;  // V_2, group c0*16 + c1
+  int exact;          // every block entry is exact in f16 (bl = 0)
   // quantizer
   int qkind, bits, group, nlev;
   float h, sqrt_g;
@@ -66,7 +87,7 @@ struct FusedBArgs {
   uint8_t* codes;
   void* scales;
   int64_t codes_ld, scales_ld;
-  int64_t u1_n, u2_n, v1_n, v2_n;  // float extents of the block arrays (host checks)
+  int64_t u1_n, u2_n, v1_n, v2_n;  // extents of the block arrays in halves (host checks)
 };
 
 // ---- pass A geometry --------------------------------------------------------
@@ -265,6 +286,16 @@ __host__ __device__ inline int64_t fb_col(const FusedBArgs& a, const FbTile& t, 
 // ---- entry points -------------------------------------------------------------
 
 hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_signs);
+
+// Tile scale of pass B: 2^k with k = fb_scale_shift(M) puts the largest
+// magnitude M of a tile in [64, 128) (k = 127 for M below 2^-121 or zero).
+// The blocks' rows have norm at most 1 + 1e-3 (the host checks), so no value
+// of the four stages exceeds 4^4 * 1.004 * 128 < 65504.
+__host__ __device__ inline int fb_scale_shift(uint32_t mbits) {
+  const int e = (int)((mbits >> 23) & 0xff);
+  const int s = 260 - e;
+  return (s > 254 ? 254 : s) - 127;
+}
 void fused_release(Plan& p);
 
 bool fused_rotate_supported(const Plan* U, const Plan* V, int xt, int yt, int64_t rows,

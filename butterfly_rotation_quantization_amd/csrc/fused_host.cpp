@@ -35,6 +35,58 @@ void hadamard_block(int b, float* out) {
     for (int k = 0; k < b; ++k) out[j * b + k] = (__builtin_popcount(j & k) & 1) ? -s : s;
 }
 
+// Split-f16 copies of pass B's blocks: the last two stages of a plan whose
+// last two radices are 16 (Hadamard plans of the fast path: H_16 / 4, shared).
+// Each entry x becomes hi = f16(x) and lo = f16(x - hi), both rounded to
+// nearest even.  Returns hipSuccess with p.fzh unset when the plan does not
+// qualify or a block row has norm above 1 + 1e-3 (pass B's range bound).
+hipError_t prepare_split16(Plan& p, const float* host_blocks) {
+  std::vector<float> had;
+  int64_t groups = 0;
+  const float* st[2] = {nullptr, nullptr};
+  if (p.mode == BRQ_HADAMARD) {
+    if (!fused_b0(p)) return hipSuccess;
+    had.resize(256);
+    hadamard_block(16, had.data());
+    st[0] = st[1] = had.data();
+    groups = 1;
+  } else {
+    if (p.nst < 3 || p.radix[p.nst - 2] != 16 || p.radix[p.nst - 1] != 16 || p.d % 256) return hipSuccess;
+    groups = p.mode == BRQ_PER_GROUP ? p.d / 16 : 1;
+    st[0] = host_blocks + p.blk_off[p.nst - 2];
+    st[1] = host_blocks + p.blk_off[p.nst - 1];
+  }
+  const int64_t per = groups * kFbBlockHalves;
+  std::vector<uint16_t> out((size_t)(2 * per));
+  bool exact = true;
+  for (int s = 0; s < 2; ++s)
+    for (int64_t g = 0; g < groups; ++g) {
+      const float* blk = st[s] + g * 256;
+      for (int j = 0; j < 16; ++j) {
+        double nrm = 0;
+        for (int k = 0; k < 16; ++k) nrm += (double)blk[j * 16 + k] * blk[j * 16 + k];
+        if (!(nrm <= 1.002)) return hipSuccess;  // (1 + 1e-3)^2, and not NaN
+        for (int k = 0; k < 16; ++k) {
+          const float x = blk[j * 16 + k];
+          const _Float16 hi = (_Float16)x;
+          const _Float16 lo = (_Float16)(x - (float)hi);
+          if ((float)lo != 0.0f) exact = false;
+          uint16_t* e = out.data() + s * per + g * kFbBlockHalves + fb_hentry(j, k / 4);
+          e[k % 4] = __builtin_bit_cast(uint16_t, hi);
+          e[4 + k % 4] = __builtin_bit_cast(uint16_t, lo);
+        }
+      }
+    }
+  hipError_t e = rt_malloc((void**)&p.fzh, out.size() * sizeof(uint16_t));
+  if (e == hipSuccess) e = rt_copy_to_device(p.fzh, out.data(), out.size() * sizeof(uint16_t));
+  if (e != hipSuccess) return e;
+  p.fzh_off2 = per;
+  p.fzh_gs = groups > 1 ? kFbBlockHalves : 0;
+  p.fzh_n = per;
+  p.fzh_exact = exact ? 1 : 0;
+  return hipSuccess;
+}
+
 }  // namespace
 
 // Stage-0 blocks for the fast path: zero-padded to 16*nb, with the plan's
@@ -42,8 +94,10 @@ void hadamard_block(int b, float* out) {
 // i = k*S_0 + c (S_0 = 256), so (B_0 D) restricted to group c is
 // B_{0,c} diag(s[k*256 + c]): column k of the block times that sign.
 hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_signs) {
+  const hipError_t es = prepare_split16(p, host_blocks);
+  if (es != hipSuccess) return es;
   const int b0 = fused_b0(p);
-  if (!b0) return hipSuccess;
+  if (!b0 || !p.fzh) return hipSuccess;
   const int nb = (b0 + 15) / 16;
   const int np = 16 * nb;
   const int S0 = 256;  // stride of stage 0 in the (b0, 16, 16) schedule
@@ -83,20 +137,6 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
   p.fz_b0 = b0;
   p.fz_nb = nb;
   p.fz_gs0 = per_group ? (int64_t)np * np : 0;
-  if (p.mode == BRQ_HADAMARD) {
-    std::vector<float> h16(256);
-    hadamard_block(16, h16.data());
-    e = rt_malloc((void**)&p.fz_had, 256 * sizeof(float));
-    if (e == hipSuccess) e = rt_copy_to_device(p.fz_had, h16.data(), 256 * sizeof(float));
-    if (e != hipSuccess) return e;
-    p.fz1 = p.fz_had;
-    p.fz2 = p.fz_had;
-    p.fz_gs1 = p.fz_gs2 = 0;
-  } else {
-    p.fz1 = p.blk + p.blk_off[1];
-    p.fz2 = p.blk + p.blk_off[2];
-    p.fz_gs1 = p.fz_gs2 = shared_src ? 0 : 256;
-  }
   p.fz_ok = 1;
   return hipSuccess;
 }
@@ -147,15 +187,31 @@ const char* check_b(const FusedBArgs& b) {
     return "pass B shape";
   if ((int64_t)b.m * b.n * 4 >= (int64_t(1) << 40)) return "pass B extent";
   if (!b.ws || !b.u1 || !b.u2 || !b.v1 || !b.v2 || !b.codes || !b.scales) return "pass B pointers";
-  if (b.u1_gs && b.u1_n < (int64_t)b.nrb * 16 * b.u1_gs) return "U_1 extent";
-  if (b.u2_gs && b.u2_n < (int64_t)b.nrb * 16 * b.u2_gs) return "U_2 extent";
-  if (b.v1_gs && b.v1_n < (int64_t)b.bv * 16 * b.v1_gs) return "V_1 extent";
-  if (b.v2_gs && b.v2_n < (int64_t)b.bv * 16 * b.v2_gs) return "V_2 extent";
+  if (b.u1_n < (b.u1_gs ? (int64_t)b.nrb * 16 * b.u1_gs : kFbBlockHalves)) return "U_1 extent";
+  if (b.u2_n < (b.u2_gs ? (int64_t)b.nrb * 16 * b.u2_gs : kFbBlockHalves)) return "U_2 extent";
+  if (b.v1_n < (b.v1_gs ? (int64_t)b.bv * 16 * b.v1_gs : kFbBlockHalves)) return "V_1 extent";
+  if (b.v2_n < (b.v2_gs ? (int64_t)b.bv * 16 * b.v2_gs : kFbBlockHalves)) return "V_2 extent";
+  if ((b.u1_gs && b.u1_gs < kFbBlockHalves) || (b.v1_gs && b.v1_gs < kFbBlockHalves) ||
+      b.u1_gs % 8 || b.v1_gs % 8 || b.u2_gs != b.u1_gs || b.v2_gs != b.v1_gs)
+    return "block strides";
   if (b.group != 64 && b.group != 128) return "group";
   if (b.bits < 2 || b.bits > 5 || b.nlev != (1 << b.bits)) return "bits";
   if (b.codes_ld * 8 != b.n * b.bits || b.codes_ld % 4 || b.scales_ld * b.group != b.n)
     return "code layout";
   return nullptr;
+}
+
+// Pass B's split blocks of both sides.
+void set_split_blocks(FusedBArgs& b, const Plan* U, const Plan* V) {
+  b.u1 = U->fzh;
+  b.u2 = U->fzh + U->fzh_off2;
+  b.u1_gs = b.u2_gs = U->fzh_gs;
+  b.u1_n = b.u2_n = U->fzh_n;
+  b.v1 = V->fzh;
+  b.v2 = V->fzh + V->fzh_off2;
+  b.v1_gs = b.v2_gs = V->fzh_gs;
+  b.v1_n = b.v2_n = V->fzh_n;
+  b.exact = U->fzh_exact && V->fzh_exact ? 1 : 0;
 }
 
 void fill_quant_b(FusedBArgs& b, const brq_quant* q, int64_t n) {
@@ -176,8 +232,9 @@ void fill_quant_b(FusedBArgs& b, const brq_quant* q, int64_t n) {
 void fused_release(Plan& p) {
   rt_free(p.fz0);
   rt_free(p.fz0f);
-  rt_free(p.fz_had);
-  p.fz0 = p.fz0f = p.fz_had = nullptr;
+  rt_free(p.fzh);
+  p.fz0 = p.fz0f = nullptr;
+  p.fzh = nullptr;
   p.fz_ok = 0;
   p.fz_b0 = 0;
 }
@@ -197,7 +254,7 @@ hipError_t fused_rotate(const Plan*, const Plan*, const void*, int, int64_t, voi
 // whole 32-bit code words per group and per row.
 bool fused_rqp_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_t n, int64_t ldw,
                          const void* w, const brq_quant* q) {
-  if (!U || !V || !U->fz_ok || !V->fz_ok) return false;
+  if (!U || !V || !U->fz_ok || !V->fz_ok || !U->fzh || !V->fzh) return false;
   if (U->fz_b0 != 16 || U->d != m || n % V->d) return false;
   if (q->group != 64 && q->group != 128) return false;
   if ((n * q->bits) % 32) return false;
@@ -241,23 +298,12 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   b.bv = a.bv;
   b.nchunk = a.nchunk;
   b.dv = a.dv;
-  b.u1 = U->fz1;
-  b.u1_gs = U->fz_gs1;
-  b.u2 = U->fz2;
-  b.u2_gs = U->fz_gs2;
-  b.v1 = V->fz1;
-  b.v1_gs = V->fz_gs1;
-  b.v2 = V->fz2;
-  b.v2_gs = V->fz_gs2;
+  set_split_blocks(b, U, V);
   fill_quant_b(b, q, n);
   b.codes = codes;
   b.scales = scales;
-  const int64_t u16 = U->mode == BRQ_PER_GROUP ? (int64_t)(U->d / 16) * 256 : 256;
-  const int64_t v16 = V->mode == BRQ_PER_GROUP ? (int64_t)(V->d / 16) * 256 : 256;
   a.u0_n = (U->fz_gs0 ? 256 : 1) * 256;
   a.v0_n = (V->fz_gs0 ? 256 : 1) * 256 * a.nb * a.nb;
-  b.u1_n = b.u2_n = u16;
-  b.v1_n = b.v2_n = v16;
   if (check_fused(a, b)) return BRQ_ERR_UNSUPPORTED;
 
   char name[96];
@@ -282,7 +328,7 @@ bool dense_tail16(const Plan* p) {
 }  // namespace
 
 bool fused_tail_supported(const Plan* U, const Plan* V, int64_t m, int64_t n, const brq_quant* q) {
-  if (!dense_tail16(U) || !dense_tail16(V) || U->d != m || n % V->d) return false;
+  if (!dense_tail16(U) || !dense_tail16(V) || !U->fzh || !V->fzh || U->d != m || n % V->d) return false;
   if (q->group != 64 && q->group != 128) return false;
   return (n * q->bits) % 32 == 0;
 }
@@ -301,16 +347,7 @@ brq_status fused_tail_rqp(const Plan* U, const Plan* V, const float* ws, int64_t
   b.bv = V->d / 256;
   b.dv = V->d;
   b.nchunk = (int)(n / V->d);
-  // stage t's per-group blocks: group c at c * 256 floats (shared: one block)
-  const bool ug = U->mode == BRQ_PER_GROUP, vg = V->mode == BRQ_PER_GROUP;
-  b.u1 = U->blk + U->blk_off[U->nst - 2];
-  b.u2 = U->blk + U->blk_off[U->nst - 1];
-  b.v1 = V->blk + V->blk_off[V->nst - 2];
-  b.v2 = V->blk + V->blk_off[V->nst - 1];
-  b.u1_gs = b.u2_gs = ug ? 256 : 0;
-  b.v1_gs = b.v2_gs = vg ? 256 : 0;
-  b.u1_n = b.u2_n = ug ? (int64_t)(U->d / 16) * 256 : 256;
-  b.v1_n = b.v2_n = vg ? (int64_t)(V->d / 16) * 256 : 256;
+  set_split_blocks(b, U, V);
   fill_quant_b(b, q, n);
   b.codes = codes;
   b.scales = scales;

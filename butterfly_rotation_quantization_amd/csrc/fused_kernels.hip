@@ -7,6 +7,14 @@
 // operand of the next product, D is the transpose: a stage that mixes the
 // other index of the same 16 x 16 tile needs no data movement.
 //
+// v_mfma_f32_16x16x32_f16 (pass B): lane l holds A[m = lr][k = 8 lg + s] and
+// B[k = 8 lg + s][n = lr] in slot s = 0..7, and the result in the same layout
+// as above (checked on gfx950, which also keeps f16 subnormal inputs).  Only
+// the pairing of slots matters to the sum, so slot s < 4 carries k' = 4 lg + s
+// of the 16-wide contraction and slot s >= 4 carries k' = 4 lg + s - 4 again,
+// with the other half of a split operand: the lane's four accumulator values
+// are still its A operand, and one instruction adds two split products.
+//
 // Stage arithmetic ([HARP] technical summary 2.1): every group of a stage is
 // multiplied by its own b x b block, y_j = sum_k B[j][k] x_k; here the group
 // index is fixed per tile and the batch of the product runs over the other
@@ -19,12 +27,16 @@ namespace brq {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));  // 16-byte aligned, as f4
 
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ void st4(float* p, const f4& v) { *reinterpret_cast<f4*>(p) = v; }
 
 // The value itself, hidden from the optimizer: addresses derived from it are
 // rebuilt where they are used instead of being hoisted out of a loop, where
@@ -233,10 +245,13 @@ __device__ __forceinline__ float fb_stat(float acc, const f4& v) {
 // slot (r1, c1h, r2, 4 lg) holds row r2's four consecutive columns
 // c1 = 8h + c1h, c2 = 4 lg .. 4 lg + 3; stat[gi] holds this lane's part of
 // group gi's statistic.  Each fragment is read back, coded and packed in turn.
+// The values carry the tile scale 2^ks: the codes depend only on v / stat,
+// which the power of two leaves exact, and the stored statistic is scaled
+// back by 2^-ks (exact as well).
 template <int BITS, int QK, int G>
 __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t, int r1, int h,
                                             const float* xch, const float (&stat_in)[128 / G], int lr,
-                                            int lg) {
+                                            int lg, int ks) {
   constexpr int NG = 128 / G;      // groups in this half
   constexpr int FPG = 8 / NG;      // 16-column fragments per group
   constexpr int LV = (1 << BITS) - 1;
@@ -271,8 +286,9 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
         int c = 0;
         if (stat > 0.f) {
           if (QK == BRQ_ABSMAX) {
+            // |v| <= stat and k = RN(h / stat) keep v k + h within
+            // [-h 2^-24, 2h (1 + 2^-24)], which rounds into [0, LV]: no clamp
             c = (int)__builtin_rintf(fmaf(v[i], k, a.h));
-            c = c < 0 ? 0 : (c > LV ? LV : c);
           } else {
             const float z = v[i] * k;
 #pragma unroll
@@ -300,10 +316,11 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
     const int64_t col0 = fb_col(a, t, 8 * h + gi * FPG, 0);
     const int64_t gcol = col0 / G;
     if (lg == 0) {
+      const float st = __builtin_ldexpf(stat, -ks);
       if (QK == BRQ_ABSMAX)
-        static_cast<float*>(a.scales)[row * a.scales_ld + gcol] = stat;
+        static_cast<float*>(a.scales)[row * a.scales_ld + gcol] = st;
       else
-        static_cast<_Float16*>(a.scales)[row * a.scales_ld + gcol] = (_Float16)stat;
+        static_cast<_Float16*>(a.scales)[row * a.scales_ld + gcol] = (_Float16)st;
     }
     if (SPLIT || lg == 0) {
       uint32_t* out = reinterpret_cast<uint32_t*>(a.codes + row * a.codes_ld + col0 * BITS / 8) +
@@ -316,6 +333,44 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
 
 constexpr int FB_IL = 2;   // pass B phase 1: fragments whose MFMA chains interleave
 constexpr int FB_IL2 = 2;  // pass B phase 2 (its registers are shared with the prefetched tile)
+
+// One stage of pass B for one 16 x 16 fragment: the lane's four float32
+// values a[i] (contraction index k = 4 lg + i) times the block entries for the
+// same k, bhh = (bh, bh) and bll = (bl, bl).  The data split is hi = f16(a),
+// lo = f16(a - hi), both rounded to nearest (a - hi is exact in float32, so
+// hi + lo holds a to 2^-22 relative); products of f16 values are exact in
+// float32.  m1 is -1 from a scalar register: a constant -1 would let the
+// compiler turn the multiply-add into a subtraction, which costs a conversion
+// of hi back to float32 where v_fma_mix_f32 reads the f16 directly.
+//   (hi, lo) . (bh, bh), then (hi, lo) . (bl, bl) into the same accumulator
+//   (not for blocks exact in f16, EX).
+// The second product uses the same K = 32 instruction as the first: chained
+// through the accumulator after a K = 32 product, v_mfma_f32_16x16x16_f16
+// read a stale accumulator on gfx950 (the compiler issued them back to back).
+template <bool EX>
+__device__ __forceinline__ f4 fb_prod(const f4& a, const u4& bhh, const u4& bll, float m1) {
+  const h4 hi = __builtin_convertvector(a, h4);
+  f4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, a[i]);
+  const h4 lo = __builtin_convertvector(r, h4);
+  const h8 A = __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bhh), z, 0, 0, 0);
+  if constexpr (EX) return d;
+  else return __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bll), d, 0, 0, 0);
+}
+
+// -1 in a scalar register, hidden from constant folding.
+__device__ __forceinline__ float fb_minus_one() {
+  float v = -1.0f;
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// (bh, bh) and (bl, bl) of a block entry (bh, bl).
+__device__ __forceinline__ u4 fb_hh(const u4& e) { return u4{e.x, e.y, e.x, e.y}; }
+__device__ __forceinline__ u4 fb_ll(const u4& e) { return u4{e.z, e.w, e.z, e.w}; }
 
 // Load half H of the tile's float32 block for phase 1: x[c2][i] = element
 // (r1 = lr, c1 = 4 lg + i, r2 = w, c2) for i = 2H, 2H + 1, which is 128
@@ -334,11 +389,11 @@ __device__ __forceinline__ void fb_load_half(const FusedBArgs& a, const FbTile& 
     }
 }
 
-// Persistent: workgroup b handles tiles b, b + gridDim.x, ...  Each half of
-// the exchange frees half of every lane's tile registers, and the next
-// tile's matching half is loaded into them at once, so the loads run under
-// the second phase and the quantizer of the current tile.
-template <int BITS, int QK, int G>
+// Persistent: workgroup b handles tiles b, b + gridDim.x, ...  Once the
+// second half of the exchange has been written, every tile register is free
+// and the next tile is loaded into them, so the loads run under the second
+// half of phase 2 and its quantizer.
+template <int BITS, int QK, int G, bool EX>
 __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   extern __shared__ float lds[];
   float* xch = lds;
@@ -362,40 +417,70 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   FbTile t = fb_tile(a, tile);
   fb_load_half<0>(a, t, w, lr, lg, x);
   fb_load_half<1>(a, t, w, lr, lg, x);
-  f4 bu1 = ld4(a.u1 + (int64_t)(t.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg);
-  f4 bu2 = ld4(a.u2 + (int64_t)(t.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg);
+  auto load_u = [&](const uint16_t* blk, int64_t gs, const FbTile& tt) {
+    return *reinterpret_cast<const u4*>(blk + (int64_t)(tt.r0 * 16 + w) * gs + fb_hentry(lr, lg));
+  };
+  u4 e1 = load_u(a.u1, a.u1_gs, t), e2 = load_u(a.u2, a.u2_gs, t);
+  const float m1 = fb_minus_one();
 
   for (;;) {
+    // the wave's largest magnitude (waits for the tile's loads)
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(x[c][i]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     __syncthreads();  // the previous tile is done with LDS
+    if ((tid & 63) == 0) lds[kFbMaxOff + w] = mx;
     // stage the tile's V_1 and V_2 blocks (16 each, groups c0*16 + f)
     for (int k = tid; k < 2 * 16 * 64; k += kFbWaves * 64) {
       const int which = k >> 10, rem = k & 1023, f = rem >> 6, qd = rem & 63;
-      const float* src = (which ? a.v2 : a.v1) + (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs);
-      *reinterpret_cast<f4*>(&lds[(which ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(qd >> 2, qd & 3)]) =
-          ld4(src + 4 * qd);
+      const int j = qd >> 2, q = qd & 3;
+      const uint16_t* src = (which ? a.v2 : a.v1) + (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs) +
+                            fb_hentry(j, q);
+      const u4 e = *reinterpret_cast<const u4*>(src);
+      st4(&lds[(which ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(j, q)], __builtin_bit_cast(f4, fb_hh(e)));
+      if (!EX)
+        st4(&lds[(which ? kFbV2LOff : kFbV1LOff) + f * 256 + fb_vslot(j, q)], __builtin_bit_cast(f4, fb_ll(e)));
     }
     __syncthreads();
+    // the tile scale 2^ks (uniform over the workgroup)
+    int ks;
+    {
+      const f4 m0 = ld4(&lds[kFbMaxOff]), m1 = ld4(&lds[kFbMaxOff + 4]);
+      const f4 m2 = ld4(&lds[kFbMaxOff + 8]), m3 = ld4(&lds[kFbMaxOff + 12]);
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fmaxf(m0[i], m1[i]), fmaxf(m2[i], m3[i])));
+      ks = __builtin_amdgcn_readfirstlane(fb_scale_shift(__float_as_uint(m)));
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[c][i] = __builtin_ldexpf(x[c][i], ks);
 
     // ---- phase 1: this wave owns r2 = w; fragments over (r1, c1), one per c2.
     lanes();
-    const int v1_lane = kFbV1Off + fb_vslot(fb_sigma(lr), lg);
+    {
+      const u4 bu1 = fb_hh(e1), bl1 = fb_ll(e1);
+      const int v1_lane = kFbV1Off + fb_vslot(fb_sigma(lr), lg);
 #pragma unroll
-    for (int c2q = 0; c2q < 16; c2q += FB_IL) {
-      f4 d[FB_IL];
+      for (int c2q = 0; c2q < 16; c2q += FB_IL) {
+        f4 d[FB_IL];
 #pragma unroll
-      for (int f = 0; f < FB_IL; ++f) {
-        // B[k = c1][n] = V_1[c1' = sigma(n)][c1]
-        const f4 bv1 = ld4(&lds[v1_lane + (c2q + f) * 256]);
-        d[f] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int f = 0; f < FB_IL; ++f) {
+          // B[k = c1][n] = V_1[c1' = sigma(n)][c1]
+          const u4 bv = __builtin_bit_cast(u4, ld4(&lds[v1_lane + (c2q + f) * 256]));
+          const u4 bl = EX ? u4{0u, 0u, 0u, 0u}
+                           : __builtin_bit_cast(u4, ld4(&lds[v1_lane + kFbV1LOff + (c2q + f) * 256]));
+          d[f] = fb_prod<EX>(x[c2q + f], bv, bl, m1);  // V_1: c1
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[f] = mfma4(x[c2q + f][i], bv1[i], d[f]);  // V_1: c1
-        x[c2q + f] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int f = 0; f < FB_IL; ++f) x[c2q + f] = fb_prod<EX>(d[f], bu1, bl1, m1);  // U_1: r1
+        // x[c2][j]: element (c1' = lg + 4 j, r1' = lr)
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int f = 0; f < FB_IL; ++f) x[c2q + f] = mfma4(d[f][i], bu1[i], x[c2q + f]);  // U_1: r1
-      // x[c2][j]: element (c1' = lg + 4 j, r1' = lr)
     }
 
     // ---- phase 2: this wave owns r1 = w; fragments over (r2, c2), one per c1.
@@ -430,36 +515,34 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
       float stat[128 / G];
 #pragma unroll
       for (int gi = 0; gi < 128 / G; ++gi) stat[gi] = 0.f;
+      const u4 bu2 = fb_hh(e2), bl2 = fb_ll(e2);
 #pragma unroll
       for (int c1q = 0; c1q < 8; c1q += FB_IL2) {
-        f4 d[FB_IL2], v[FB_IL2];
+        f4 d[FB_IL2];
 #pragma unroll
         for (int f = 0; f < FB_IL2; ++f) {
           const f4 av = ld4(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]);  // c2 = 4lg + i, r2 = lr
-          const f4 bv2 = ld4(&lds[kFbV2Off + (8 * h + c1q + f) * 256 + fb_vslot(lr, lg)]);
-          d[f] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d[f] = mfma4(av[i], bv2[i], d[f]);  // V_2: c2
-          v[f] = f4{0.f, 0.f, 0.f, 0.f};
+          const int c1 = 8 * h + c1q + f;
+          const u4 bv = __builtin_bit_cast(u4, ld4(&lds[kFbV2Off + c1 * 256 + fb_vslot(lr, lg)]));
+          const u4 bl = EX ? u4{0u, 0u, 0u, 0u}
+                           : __builtin_bit_cast(u4, ld4(&lds[kFbV2LOff + c1 * 256 + fb_vslot(lr, lg)]));
+          d[f] = fb_prod<EX>(av, bv, bl, m1);  // V_2: c2
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int f = 0; f < FB_IL2; ++f) v[f] = mfma4(d[f][i], bu2[i], v[f]);  // U_2: r2
-        // v[f]: element (row r2' = lr, column c1 = 8h + c1q + f, c2' = 4lg + i)
-#pragma unroll
         for (int f = 0; f < FB_IL2; ++f) {
-          *reinterpret_cast<f4*>(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]) = v[f];
-          stat[(c1q + f) / (G / 16)] = fb_stat<QK>(stat[(c1q + f) / (G / 16)], v[f]);
+          const f4 v = fb_prod<EX>(d[f], bu2, bl2, m1);  // U_2: r2
+          // v: element (row r2' = lr, column c1 = 8h + c1q + f, c2' = 4lg + i)
+          *reinterpret_cast<f4*>(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]) = v;
+          stat[(c1q + f) / (G / 16)] = fb_stat<QK>(stat[(c1q + f) / (G / 16)], v);
         }
       }
       lanes();
-      fb_quantize<BITS, QK, G>(a, t, w, h, xch, stat, lr, lg);
+      fb_quantize<BITS, QK, G>(a, t, w, h, xch, stat, lr, lg, ks);
     }
     if (!more) break;
     lanes();
-    bu1 = ld4(a.u1 + (int64_t)(tn.r0 * 16 + w) * a.u1_gs + lr * 16 + 4 * lg);
-    bu2 = ld4(a.u2 + (int64_t)(tn.r0 * 16 + w) * a.u2_gs + lr * 16 + 4 * lg);
+    e1 = load_u(a.u1, a.u1_gs, tn);
+    e2 = load_u(a.u2, a.u2_gs, tn);
     tile = next;
     t = tn;
   }
@@ -500,25 +583,30 @@ hipError_t launch_a_steps(const FusedAArgs& a, hipStream_t s, std::integer_seque
   return e;
 }
 
-template <int BITS, int QK, int G>
+template <int BITS, int QK, int G, bool EX>
 hipError_t launch_b_t(const FusedBArgs& a, int grid, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_b_kernel<BITS, QK, G>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_b_kernel<BITS, QK, G, EX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        kFbLdsFloats * (int)sizeof(float));
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((fused_b_kernel<BITS, QK, G>), dim3((unsigned)grid), dim3(kFbWaves * 64),
+  hipLaunchKernelGGL((fused_b_kernel<BITS, QK, G, EX>), dim3((unsigned)grid), dim3(kFbWaves * 64),
                      (size_t)kFbLdsFloats * sizeof(float), s, a);
   return hipGetLastError();
 }
 
+template <int BITS, int QK, int G>
+hipError_t launch_b_x(const FusedBArgs& a, int grid, hipStream_t s) {
+  return a.exact ? launch_b_t<BITS, QK, G, true>(a, grid, s) : launch_b_t<BITS, QK, G, false>(a, grid, s);
+}
+
 template <int BITS, int QK>
 hipError_t launch_b_g(const FusedBArgs& a, int grid, hipStream_t s) {
-  return a.group == 64 ? launch_b_t<BITS, QK, 64>(a, grid, s)
-                       : launch_b_t<BITS, QK, 128>(a, grid, s);
+  return a.group == 64 ? launch_b_x<BITS, QK, 64>(a, grid, s)
+                       : launch_b_x<BITS, QK, 128>(a, grid, s);
 }
 
 template <int BITS>
