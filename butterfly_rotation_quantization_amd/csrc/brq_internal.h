@@ -26,14 +26,18 @@ struct Plan {
   float* blkT = nullptr;             // the same blocks transposed, for the inverse
   float* signs = nullptr;            // +-1 as float, or nullptr
   // Fast-path data (fused_prepare), for plans of the shape (b0, 16, 16):
-  // stage-0 blocks zero-padded to [groups][16*fz_nb][16*fz_nb] and the float
-  // stride between groups (0 = one block shared by all groups).
+  // stage-0 blocks with the signs folded in, zero-padded to 16*fz_nb and
+  // split into f16 (bh, bl) entries: as pass A's U_0 (fz0u, b0 = 16 only) and
+  // in pass A's V_0 fragment order (fz0v); halves between groups (0 = one
+  // block shared by all groups).
   int fz_ok = 0;
   int fz_b0 = 0;                     // radix of the fast path's stage 0 (d = fz_b0 * 256)
   int fz_nb = 0;
-  float* fz0 = nullptr;
-  float* fz0f = nullptr;             // the same blocks in MFMA fragment order (fused.h)
-  int64_t fz_gs0 = 0;
+  uint16_t* fz0u = nullptr;
+  uint16_t* fz0v = nullptr;
+  int64_t fz_gs0u = 0, fz_gs0v = 0;
+  int64_t fz_n0u = 0, fz_n0v = 0;    // extents in halves
+  int fz0_exact = 0;                 // every stage-0 entry exact in f16
   // Pass B's blocks (the last two stages when both are radix 16) split into
   // f16 pairs, laid out as fused.h describes: stage nst-2 first, stage nst-1
   // at fzh_off2 halves; fzh_gs halves between groups (0 = shared).  Only

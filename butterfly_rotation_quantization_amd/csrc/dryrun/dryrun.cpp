@@ -199,8 +199,18 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   const int P = g.P, ppw = g.ppw, esz = g.esz, epi = 16 / esz, ipr = g.ipr;
   if (64 % ipr || 256 % P || 8 * ki < 16 * fa_ncb(64 / ipr, st) || 8 * kq * (256 / P) < 256)
     return violation("pass A loop counts %lld / %lld", ki, kq), hipErrorInvalidValue;
-  if (fa_lds_bytes(g) > 160 * 1024 || g.slab_bytes % 16)
+  if (fa_lds_bytes(g) > 160 * 1024 || g.slab_bytes % 16 || g.max_off < g.slab_bytes + g.out_floats * 4 ||
+      g.max_off % 4 || fa_lds_bytes(g) < g.max_off + 4 * kFaWaves)
     return violation("pass A LDS %lld bytes", fa_lds_bytes(g), 0), hipErrorInvalidValue;
+  for (int e = 0; e < 255; ++e) {  // the slab scale puts every maximum in [2^11, 2^12)
+    const float mlo = e ? std::ldexp(1.0f, e - 127) : 0.0f;
+    uint32_t bits;
+    std::memcpy(&bits, &mlo, 4);
+    const int ks = fa_scale_shift(bits);
+    if (ks != fa_scale_shift(bits | 0x7fffffu)) return violation("slab scale of exponent %lld", e, ks), hipErrorInvalidValue;
+    if (e > 0 && std::ldexp((double)mlo, ks) != 2048.0) return violation("slab scale of exponent %lld", e, ks), hipErrorInvalidValue;
+    if (e == 0 && std::ldexp(std::ldexp(1.0, -126), ks) > 4096.0) return violation("slab scale of subnormals", 0, ks), hipErrorInvalidValue;
+  }
   // which input element (r0, c0, p_local) each slab byte holds, and which
   // output (r0', c0', p_local) each float of the output area holds
   auto code = [&](int r0, int c0, int pl) { return ((int64_t)r0 * 64 + c0) * 256 + pl; };
@@ -215,9 +225,9 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
       for (int j = 0; j < ppw; ++j)
         for (int l = 0; l < 64; ++l)
           for (int nt = 0; nt < nb; ++nt)
-            for (int sq = 0; 4 * sq < fa_steps(bv); ++sq) {
-              const int64_t i = (int64_t)(t.p0 + ppw * w + j) * a.v0_gs + fa_vfrag(nb, nt, l & 15, l >> 4, 4 * sq);
-              if (!in_range(i, 4, a.v0_n) || i % 4)
+            for (int ch = 0; ch < nb; ++ch) {
+              const int64_t i = (int64_t)(t.p0 + ppw * w + j) * a.v0_gs + fa_vhentry(nb, nt, l & 15, l >> 4, ch);
+              if (!in_range(i, 8, a.v0_n) || i % 8)
                 return violation("V_0 block read (p %lld, lane %lld)", t.p0 + ppw * w + j, l), hipErrorInvalidValue;
             }
     for (int q = t.q0; q < t.q0 + kFaQC; ++q) {
@@ -256,10 +266,11 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
       for (int w = 0; w < kFaWaves; ++w)
         for (int l = 0; l < 64; ++l) {
           const int lr = l & 15, lg = l >> 4;
-          if (!in_range((int64_t)q * a.u0_gs + lr * 16 + 4 * lg, 4, a.u0_n))
+          if (!in_range((int64_t)q * a.u0_gs + fb_hentry(lr, lg), 8, a.u0_n))
             return violation("U_0 block read q %lld lane %lld", q, l), hipErrorInvalidValue;
-          for (int st = 0; st < fa_steps(bv); ++st) {
-            const int c0 = std::min(4 * st + lg, bv - 1);
+          for (int ci = 0; ci < 16 * nb; ++ci) {  // chunk ci / 16, element (ci / 4) % 4 == lg, i = ci % 4
+            if (((ci / 4) & 3) != lg) continue;
+            const int c0 = std::min(ci, bv - 1);
             const int off = fa_slab_read(g, lr, c0, w);
             if (!in_range(off, ppw * esz, g.slab_bytes) || off % (ppw * esz))
               return violation("pass A slab read at byte %lld", off, 0), hipErrorInvalidValue;

@@ -6,7 +6,12 @@
 //  pass A: the stride-256 stages U_0 and V_0.  Rows r0*256 + q (r0 < 16) and
 //          columns c0*256 + p (c0 < bV) of one (q, p) pair form a 16 x bV
 //          matrix X_qp; the pass computes B^U0_q X_qp (B^V0_p)^T for every
-//          (q, p) and writes the float32 intermediate.
+//          (q, p) and writes the float32 intermediate.  Its products run on
+//          f16 MFMA too: the slab of a q is scaled by a power of two that
+//          puts its largest magnitude in [2^11, 2^12); 16-bit inputs are then
+//          f16 values (hi) and float32 inputs split into hi and lo; V_0's
+//          blocks split into (bh, bl); U_0 splits its float32 input like a
+//          pass B stage; the output is scaled back.
 //  pass B: the remaining radix-16 stages U_1, U_2, V_1, V_2 on a 256 x 256
 //          block (rows r0*256 + [0,256), columns c0*256 + [0,256)) held in
 //          registers, with one LDS exchange, then the group quantizer and
@@ -59,12 +64,17 @@ struct FusedAArgs {
   int nb;             // 16-blocks spanned by bv
   int nchunk;         // n / d_V (block-diagonal right side)
   int dv;             // d_V = bv * 256
-  const float* u0;    // U_0 blocks [256][16][16] (or one shared block), signs folded in
-  int64_t u0_gs;      // float stride between groups (0 = shared)
-  const float* v0f;   // V_0 blocks in fragment order [256][nb][16][4][4nb] (or one), signs folded in
+  // U_0 blocks split into f16 (bh, bl) entries as pass B's (fb_hentry),
+  // signs folded in; halves between groups (0 = one shared block)
+  const uint16_t* u0;
+  int64_t u0_gs;
+  int u0_exact;       // every U_0 entry exact in f16
+  // V_0 blocks split into (bh, bl) entries in fragment order (fa_vhentry),
+  // zero-padded to 16 nb, signs folded in
+  const uint16_t* v0;
   int64_t v0_gs;
   uint32_t bv_magic;  // floor(2^32 / bv) + 1: i / bv = (i * bv_magic) >> 32 for the i used
-  int64_t u0_n, v0_n; // float extents of the block arrays (host checks)
+  int64_t u0_n, v0_n; // extents of the block arrays in halves (host checks)
 };
 
 struct FusedBArgs {
@@ -99,13 +109,19 @@ struct FusedBArgs {
 // registers, then r0 with the U_0 block of q, and the results leave through a
 // second LDS area as runs of P floats.
 //
-// V_0 as MFMA steps: step s contracts c0 = 4s + lg (lane group lg), so
-// ceil(bv / 4) steps cover the radix and the block fragment of step s and
-// output tile nt is V[16 nt + lr][4 s + lg].
+// V_0 as MFMA steps: chunk ch of 16 columns c0 is one K = 32 product, lane
+// (lr, lg) holding x[r0 = lr][c0 = 16 ch + 4 lg + i] (i < 4) as (hi, hi) and
+// the block entry (bh, bl) of V[16 nt + lr][16 ch + 4 lg + i] for output tile
+// nt; nb = ceil(bv / 16) chunks cover the radix.  (The kernels are
+// instantiated per st = ceil(bv / 4), the f32 layout's step count.)
 
 __host__ __device__ constexpr int fa_esz(int wt) { return wt == BRQ_F32 ? 4 : 2; }
-// p per wave: 4, or 2 where the blocks (nb = 4) or the float32 slab would not fit.
-__host__ __device__ constexpr int fa_ppw(int wt, int nb) { return (wt == BRQ_F32 || nb == 4) ? 2 : 4; }
+// p per wave, as many as the V_0 entries (nb^2 16-byte entries per p and
+// lane) leave registers for: 4 for 16-bit input up to nb = 3, else 2;
+// float32 input 2, or 1 at nb = 4.
+__host__ __device__ constexpr int fa_ppw(int wt, int nb) {
+  return wt == BRQ_F32 ? (nb >= 4 ? 1 : 2) : (nb >= 4 ? 2 : 4);
+}
 __host__ __device__ constexpr int fa_p(int wt, int nb) { return 8 * fa_ppw(wt, nb); }
 // 16-byte input items per run of P elements
 __host__ __device__ constexpr int fa_ipr(int wt, int nb) { return fa_p(wt, nb) * fa_esz(wt) / 16; }
@@ -144,6 +160,7 @@ __host__ __device__ inline FaSlot fa_slot(int lpr, int w, int k, int lane, int b
 
 struct FaGeom {
   int P, ppw, esz, ipr;
+  int max_off;     // byte offset of the 8 waves' slab maxima (after the output area)
   int rsb;         // slab: bytes between runs (c0), P*esz + 8
   int rowb;        // slab: bytes between r0 rows; rowb / 8 odd
   int rowo;        // output area: floats between r0 rows; rowo / 4 odd
@@ -170,12 +187,18 @@ __host__ __device__ inline FaGeom fa_geom(int wt, int nb, int bv) {
   g.out_floats = 16 * g.rowo;
   g.items = 16 * bv * g.ipr;
   g.quads = 16 * bv * g.P / 4;
+  g.max_off = g.slab_bytes + g.out_floats * (int)sizeof(float);
   return g;
 }
 
-__host__ __device__ inline int fa_lds_bytes(const FaGeom& g) {
-  return g.slab_bytes + g.out_floats * (int)sizeof(float);
-}
+__host__ __device__ inline int fa_lds_bytes(const FaGeom& g) { return g.max_off + kFaWaves * 4; }
+
+// Slab scale of pass A: 2^k with k = fa_scale_shift(M) puts the largest
+// magnitude M of the slab in [2^11, 2^12) (M below 2^-126 or zero: k = 138,
+// which keeps every value below 2^12).  A V_0 block row has norm at most
+// 1 + 1e-3 (the host checks), so V_0's outputs, which U_0 splits into f16,
+// stay below 8 * 1.001 * 2^12 < 65504 for radices up to 64.
+__host__ __device__ inline int fa_scale_shift(uint32_t mbits) { return 138 - (int)((mbits >> 23) & 0xff); }
 
 // Workgroup b -> (p range, q chunk, column chunk).  Workgroups are dealt to
 // the 8 XCDs round robin (b % 8); consecutive slots of one XCD walk the p
@@ -222,10 +245,10 @@ __host__ __device__ inline int64_t fa_row(int r0, int q) { return (int64_t)r0 * 
 __host__ __device__ inline int64_t fa_col(const FusedAArgs& a, int chunk, int c0, int p) {
   return (int64_t)chunk * a.dv + (int64_t)c0 * 256 + p;
 }
-// Fragment-order V_0 block index of (group, nt, lr, lg, s): the 4 nb steps of
-// one (nt, lane) are contiguous.
-__host__ __device__ inline int64_t fa_vfrag(int nb, int nt, int lr, int lg, int s) {
-  return (((int64_t)nt * 16 + lr) * 4 + lg) * (4 * nb) + s;
+// Halves offset of the fragment-order V_0 entry (nt, lr, lg, ch) within a
+// group (512 nb^2 halves): the nb chunks of one (nt, lane) are contiguous.
+__host__ __device__ inline int64_t fa_vhentry(int nb, int nt, int lr, int lg, int ch) {
+  return ((((int64_t)nt * 16 + lr) * 4 + lg) * nb + ch) * 8;
 }
 
 // ---- pass B geometry --------------------------------------------------------

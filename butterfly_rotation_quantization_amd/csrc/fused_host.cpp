@@ -92,7 +92,10 @@ hipError_t prepare_split16(Plan& p, const float* host_blocks) {
 // Stage-0 blocks for the fast path: zero-padded to 16*nb, with the plan's
 // signs folded in.  M = ... B_0 D, and the members of stage-0 group c are
 // i = k*S_0 + c (S_0 = 256), so (B_0 D) restricted to group c is
-// B_{0,c} diag(s[k*256 + c]): column k of the block times that sign.
+// B_{0,c} diag(s[k*256 + c]): column k of the block times that sign.  Each
+// entry x is split into hi = f16(x), lo = f16(x - hi) (nearest even), laid out
+// for pass A's U_0 (radix 16: fb_hentry) and V_0 (fa_vhentry).  The fast path
+// is refused (fz_ok stays 0) when a block row has norm above 1 + 1e-3.
 hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_signs) {
   const hipError_t es = prepare_split16(p, host_blocks);
   if (es != hipSuccess) return es;
@@ -113,30 +116,62 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
   std::vector<float> pad((size_t)ng0 * np * np, 0.f);
   for (int g = 0; g < ng0; ++g) {
     const float* blk = g0 + (shared_src ? 0 : (size_t)g * b0 * b0);
-    for (int j = 0; j < b0; ++j)
+    for (int j = 0; j < b0; ++j) {
+      double nrm = 0;
       for (int k = 0; k < b0; ++k) {
         const float sg = host_signs ? (float)host_signs[(size_t)k * S0 + g] : 1.0f;
-        pad[((size_t)g * np + j) * np + k] = blk[j * b0 + k] * sg;
+        const float x = blk[j * b0 + k] * sg;
+        pad[((size_t)g * np + j) * np + k] = x;
+        nrm += (double)x * x;
       }
+      if (!(nrm <= 1.002)) return hipSuccess;  // (1 + 1e-3)^2, and not NaN
+    }
   }
-  // the same blocks in pass A's fragment order: lane (lr, lg) of output tile
-  // nt reads the 4 nb steps V[16 nt + lr][4 s + lg] as consecutive floats
-  std::vector<float> frag(pad.size());
+  bool exact = true;
+  auto split = [&](float x, uint16_t* hi_out, uint16_t* lo_out) {
+    const _Float16 hi = (_Float16)x;
+    const _Float16 lo = (_Float16)(x - (float)hi);
+    if ((float)lo != 0.0f) exact = false;
+    *hi_out = __builtin_bit_cast(uint16_t, hi);
+    *lo_out = __builtin_bit_cast(uint16_t, lo);
+  };
+  // V_0 order: entry (nt, lr, lg, ch) holds V[16 nt + lr][16 ch + 4 lg + i]
+  const int64_t gv = (int64_t)kFbBlockHalves * nb * nb;
+  std::vector<uint16_t> v0((size_t)(ng0 * gv));
   for (int g = 0; g < ng0; ++g)
     for (int nt = 0; nt < nb; ++nt)
       for (int lr = 0; lr < 16; ++lr)
         for (int lg = 0; lg < 4; ++lg)
-          for (int st = 0; st < 4 * nb; ++st)
-            frag[(size_t)g * np * np + fa_vfrag(nb, nt, lr, lg, st)] =
-                pad[((size_t)g * np + 16 * nt + lr) * np + 4 * st + lg];
-  hipError_t e = rt_malloc((void**)&p.fz0, pad.size() * sizeof(float));
-  if (e == hipSuccess) e = rt_copy_to_device(p.fz0, pad.data(), pad.size() * sizeof(float));
-  if (e == hipSuccess) e = rt_malloc((void**)&p.fz0f, frag.size() * sizeof(float));
-  if (e == hipSuccess) e = rt_copy_to_device(p.fz0f, frag.data(), frag.size() * sizeof(float));
+          for (int ch = 0; ch < nb; ++ch) {
+            uint16_t* e = v0.data() + g * gv + fa_vhentry(nb, nt, lr, lg, ch);
+            for (int i = 0; i < 4; ++i)
+              split(pad[((size_t)g * np + 16 * nt + lr) * np + 16 * ch + 4 * lg + i], e + i, e + 4 + i);
+          }
+  // U_0 order (radix 16 only): entry (j, q) holds U[j][4 q + i]
+  std::vector<uint16_t> u0;
+  if (np == 16) {
+    u0.resize((size_t)ng0 * kFbBlockHalves);
+    for (int g = 0; g < ng0; ++g)
+      for (int j = 0; j < 16; ++j)
+        for (int k = 0; k < 16; ++k) {
+          uint16_t* e = u0.data() + (size_t)g * kFbBlockHalves + fb_hentry(j, k / 4);
+          split(pad[((size_t)g * np + j) * np + k], e + k % 4, e + 4 + k % 4);
+        }
+  }
+  hipError_t e = rt_malloc((void**)&p.fz0v, v0.size() * sizeof(uint16_t));
+  if (e == hipSuccess) e = rt_copy_to_device(p.fz0v, v0.data(), v0.size() * sizeof(uint16_t));
+  if (e == hipSuccess && !u0.empty()) {
+    e = rt_malloc((void**)&p.fz0u, u0.size() * sizeof(uint16_t));
+    if (e == hipSuccess) e = rt_copy_to_device(p.fz0u, u0.data(), u0.size() * sizeof(uint16_t));
+  }
   if (e != hipSuccess) return e;
   p.fz_b0 = b0;
   p.fz_nb = nb;
-  p.fz_gs0 = per_group ? (int64_t)np * np : 0;
+  p.fz_gs0v = per_group ? gv : 0;
+  p.fz_gs0u = per_group ? kFbBlockHalves : 0;
+  p.fz_n0v = (int64_t)v0.size();
+  p.fz_n0u = (int64_t)u0.size();
+  p.fz0_exact = exact ? 1 : 0;
   p.fz_ok = 1;
   return hipSuccess;
 }
@@ -171,10 +206,12 @@ const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if ((int64_t)a.m * a.ldw * fa_esz(a.wt) >= (int64_t(1) << 31) ||
       (int64_t)a.m * a.n * 4 >= (int64_t(1) << 31))
     return "32-bit offsets";
-  if (!a.w || !a.ws || !a.u0 || !a.v0f) return "pass A pointers";
-  if (a.u0_gs && a.u0_n < 256 * a.u0_gs) return "U_0 extent";
-  if (a.v0_gs && a.v0_n < 256 * a.v0_gs) return "V_0 extent";
-  if (a.u0_n < 256 || a.v0_n < 256 * a.nb * a.nb) return "block extent";
+  if (!a.w || !a.ws || !a.u0 || !a.v0) return "pass A pointers";
+  if (a.u0_n < (a.u0_gs ? 256 * a.u0_gs : kFbBlockHalves)) return "U_0 extent";
+  if (a.v0_n < (a.v0_gs ? 256 * a.v0_gs : (int64_t)kFbBlockHalves * a.nb * a.nb)) return "V_0 extent";
+  if ((a.u0_gs && a.u0_gs < kFbBlockHalves) || (a.v0_gs && a.v0_gs < (int64_t)kFbBlockHalves * a.nb * a.nb) ||
+      a.u0_gs % 8 || a.v0_gs % 8)
+    return "block strides";
   if (b.bv != a.bv || b.nchunk != a.nchunk || b.dv != a.dv || b.m != a.m || b.n != a.n)
     return "pass B shape";
   return check_b(b);
@@ -230,10 +267,10 @@ void fill_quant_b(FusedBArgs& b, const brq_quant* q, int64_t n) {
 }  // namespace
 
 void fused_release(Plan& p) {
-  rt_free(p.fz0);
-  rt_free(p.fz0f);
+  rt_free(p.fz0u);
+  rt_free(p.fz0v);
   rt_free(p.fzh);
-  p.fz0 = p.fz0f = nullptr;
+  p.fz0u = p.fz0v = nullptr;
   p.fzh = nullptr;
   p.fz_ok = 0;
   p.fz_b0 = 0;
@@ -283,10 +320,11 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.nb = V->fz_nb;
   a.dv = V->d;
   a.nchunk = (int)(n / V->d);
-  a.u0 = U->fz0;  // radix 16: the padded layout is the 16 x 16 block itself
-  a.u0_gs = U->fz_gs0;
-  a.v0f = V->fz0f;
-  a.v0_gs = V->fz_gs0;
+  a.u0 = U->fz0u;
+  a.u0_gs = U->fz_gs0u;
+  a.u0_exact = U->fz0_exact;
+  a.v0 = V->fz0v;
+  a.v0_gs = V->fz_gs0v;
   a.bv_magic = (uint32_t)((1ull << 32) / (uint64_t)a.bv + 1);
 
   FusedBArgs b;
@@ -302,8 +340,8 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   fill_quant_b(b, q, n);
   b.codes = codes;
   b.scales = scales;
-  a.u0_n = (U->fz_gs0 ? 256 : 1) * 256;
-  a.v0_n = (V->fz_gs0 ? 256 : 1) * 256 * a.nb * a.nb;
+  a.u0_n = U->fz_n0u;
+  a.v0_n = V->fz_n0v;
   if (check_fused(a, b)) return BRQ_ERR_UNSUPPORTED;
 
   char name[96];

@@ -55,6 +55,46 @@ __device__ __forceinline__ float cvt_f16(uint32_t w, int hi) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// ------------------------------------------------------------------ split-f16 products
+
+// One stage for one 16 x 16 fragment: the lane's four float32
+// values a[i] (contraction index k = 4 lg + i) times the block entries for the
+// same k, bhh = (bh, bh) and bll = (bl, bl).  The data split is hi = f16(a),
+// lo = f16(a - hi), both rounded to nearest (a - hi is exact in float32, so
+// hi + lo holds a to 2^-22 relative); products of f16 values are exact in
+// float32.  m1 is -1 from a scalar register: a constant -1 would let the
+// compiler turn the multiply-add into a subtraction, which costs a conversion
+// of hi back to float32 where v_fma_mix_f32 reads the f16 directly.
+//   (hi, lo) . (bh, bh), then (hi, lo) . (bl, bl) into the same accumulator
+//   (not for blocks exact in f16, EX).
+// The second product uses the same K = 32 instruction as the first: chained
+// through the accumulator after a K = 32 product, v_mfma_f32_16x16x16_f16
+// read a stale accumulator on gfx950 (the compiler issued them back to back).
+template <bool EX>
+__device__ __forceinline__ f4 fb_prod(const f4& a, const u4& bhh, const u4& bll, float m1) {
+  const h4 hi = __builtin_convertvector(a, h4);
+  f4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, a[i]);
+  const h4 lo = __builtin_convertvector(r, h4);
+  const h8 A = __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bhh), z, 0, 0, 0);
+  if constexpr (EX) return d;
+  else return __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bll), d, 0, 0, 0);
+}
+
+// -1 in a scalar register, hidden from constant folding.
+__device__ __forceinline__ float fb_minus_one() {
+  float v = -1.0f;
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// (bh, bh) and (bl, bl) of a block entry (bh, bl).
+__device__ __forceinline__ u4 fb_hh(const u4& e) { return u4{e.x, e.y, e.x, e.y}; }
+__device__ __forceinline__ u4 fb_ll(const u4& e) { return u4{e.z, e.w, e.z, e.w}; }
+
 // ------------------------------------------------------------------ pass A
 
 // The ppw consecutive slab elements one lane reads per V_0 step: 8 bytes, or
@@ -68,9 +108,9 @@ __device__ __forceinline__ uint2 fa_aread(const uint8_t* src) {
 template <int WT, int PPW>
 __device__ __forceinline__ void fa_unpack(uint2 x, float (&v)[PPW]) {
   if constexpr (WT == BRQ_F32) {
-    static_assert(PPW == 2, "float32 slabs hold two p per wave");
+    static_assert(PPW <= 2, "float32 slabs hold one or two p per wave");
     v[0] = __uint_as_float(x.x);
-    v[1] = __uint_as_float(x.y);
+    if constexpr (PPW == 2) v[1] = __uint_as_float(x.y);
   } else if constexpr (PPW == 4) {
     if constexpr (WT == BRQ_BF16) {
       v[0] = cvt_bf16(x.x, 0); v[1] = cvt_bf16(x.x, 1);
@@ -88,13 +128,39 @@ __device__ __forceinline__ void fa_unpack(uint2 x, float (&v)[PPW]) {
   }
 }
 
+// Largest magnitude among the thread's slab items, as the bit pattern of a
+// float32 (integer order equals magnitude order for finite values).
+template <int WT, int KI>
+__device__ __forceinline__ uint32_t fa_items_absmax(const uint4 (&raw)[KI]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < KI; ++k) {
+    const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (WT == BRQ_F32) {
+        const uint32_t v = wd[e] & 0x7fffffffu;
+        m = v > m ? v : m;
+      } else {
+        const uint32_t lo = wd[e] & 0x7fffu, hi = (wd[e] >> 16) & 0x7fffu;
+        const uint32_t v = lo > hi ? lo : hi;
+        m = v > m ? v : m;
+      }
+    }
+  }
+  if constexpr (WT == BRQ_BF16) return m << 16;
+  if constexpr (WT == BRQ_F16) return __float_as_uint((float)__builtin_bit_cast(_Float16, (uint16_t)m));
+  return m;
+}
+
 // The signs of both sides are folded into the stage-0 blocks at plan time, so
-// the input is used as stored.  Per q: slab in (barrier), V_0 and U_0 on
-// MFMA per 16-column output tile with the results into the output area
-// (barrier), output area to global; the next slab is loaded into registers
-// while the products run.  Loads and stores
-// take one column c0 per wave instruction, so a lane's address is one
-// loop-invariant register plus wave-uniform terms.
+// the input is used as stored.  Per q: slab in (barrier), V_0 on MFMA for all
+// output tiles at once (chunk by chunk of 16 columns c0, each slab value read
+// and converted once), U_0 per output tile with the results into the output
+// area (barrier), output area to global; the next slab is loaded into
+// registers while the products run.  Loads and stores take one column c0 per
+// wave instruction, so a lane's address is one loop-invariant register plus
+// wave-uniform terms.
 template <int ST, int WT>
 __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a) {
   constexpr int NB = fa_nb_of_steps(ST);
@@ -113,6 +179,8 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
   const FaGeom g = fa_geom(WT, NB, bv);
   uint8_t* slab = smem;
   float* outa = reinterpret_cast<float*>(smem + g.slab_bytes);
+  uint32_t* smax = reinterpret_cast<uint32_t*>(smem + g.max_off);
+  const float m1 = fb_minus_one();
 
   // The per-instruction lane offsets are rebuilt from an opaque copy of the
   // lane index on every use: hoisted out of the q loop they would hold some
@@ -129,30 +197,40 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
       raw[k] = *reinterpret_cast<const uint4*>(base + off);
     }
   };
+  auto load_u = [&](int q) {
+    return *reinterpret_cast<const u4*>(a.u0 + (int64_t)q * a.u0_gs + fb_hentry(lr, lg));
+  };
 
-  // V_0 blocks of this wave's p: bvf[j][nt][s] = V[16 nt + lr][4 s + lg]
-  float bvf[PPW][NB][ST];
+  // V_0 entries of this wave's p: vb[j][nt][ch] = (bh, bl) of
+  // V[16 nt + lr][16 ch + 4 lg + i]
+  u4 vb[PPW][NB][NB];
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
-    const float* vb = a.v0f + (int64_t)(t.p0 + PPW * w + j) * a.v0_gs;
+    const uint16_t* vp = a.v0 + (int64_t)(t.p0 + PPW * w + j) * a.v0_gs;
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
-      for (int sq = 0; 4 * sq < ST; ++sq) {
-        const f4 v = ld4(vb + fa_vfrag(NB, nt, lr, lg, 4 * sq));
-#pragma unroll
-        for (int e = 0; e < 4 && 4 * sq + e < ST; ++e) bvf[j][nt][4 * sq + e] = v[e];
-      }
+      for (int ch = 0; ch < NB; ++ch)
+        vb[j][nt][ch] = *reinterpret_cast<const u4*>(vp + fa_vhentry(NB, nt, lr, lg, ch));
   }
   int q = t.q0;
   load_slab(q);
-  f4 bu = ld4(a.u0 + (int64_t)q * a.u0_gs + lr * 16 + 4 * lg);
+  u4 eu = load_u(q);
   // nothing loaded before the loop is outstanding inside it, so the products
   // never wait on the prefetch of the next slab
   __builtin_amdgcn_s_waitcnt(0);
 
   for (int qi = 0; qi < kFaQC; ++qi, ++q) {
     // the previous slab's reads ended before the previous second barrier
+    {
+      uint32_t mx = fa_items_absmax<WT, KI>(raw);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)mx, o, 64);
+        mx = y > mx ? y : mx;
+      }
+      if (lane == 0) smax[w] = mx;
+    }
     const int ls = opaque(lane);
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
@@ -161,47 +239,71 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
       *reinterpret_cast<uint2*>(d) = make_uint2(raw[k].x, raw[k].y);
       *reinterpret_cast<uint2*>(d + 8) = make_uint2(raw[k].z, raw[k].w);
     }
-    __syncthreads();  // slab complete
-    const f4 bq = bu;
+    __syncthreads();  // slab and maxima complete
+    int ks;
+    {
+      uint32_t m = smax[0];
+#pragma unroll
+      for (int i = 1; i < kFaWaves; ++i) m = smax[i] > m ? smax[i] : m;
+      ks = __builtin_amdgcn_readfirstlane(fa_scale_shift(m));
+    }
+    const u4 bhh = fb_hh(eu), bll = fb_ll(eu);
     uint8_t* obase = reinterpret_cast<uint8_t*>(a.ws) + ((int64_t)q * a.n + fa_col(a, t.chunk, 0, t.p0)) * 4;
 
     const uint8_t* arow = slab + fa_slab_read(g, lr, 0, w);
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt) {
-      // V_0: D[j][m = r0][n = c0'] = sum_c0 X_j[r0][c0] V_j[c0'][c0], c0' = 16 nt + n.
-      // The slab read of step s + 1 is issued before the products of step s.
+      // V_0: D[j][m = r0][n = c0'] = sum_c0 X_j[r0][c0] V_j[c0'][c0], c0' = 16 nt + n,
+      // one K = 32 product per 16 columns c0: (hi, hi) . (bh, bl), and for
+      // float32 input also (lo, lo) . (bh, bl).  The lane's slab values
+      // x[r0 = lr][c0 = 16 ch + 4 lg + i] are read, scaled and split per
+      // output tile (kept for all tiles they would need the registers of the
+      // V_0 entries).
       f4 d[PPW];
 #pragma unroll
       for (int j = 0; j < PPW; ++j) d[j] = f4{0.f, 0.f, 0.f, 0.f};
-      uint2 nxt = fa_aread<WT, PPW>(arow + lg * g.rsb);
 #pragma unroll
-      for (int s = 0; s < ST; ++s) {
-        const uint2 cur = nxt;
-        if (s + 1 < ST) {
-          const int c1 = 4 * (s + 1) + lg;  // only the last step can pass the radix
-          nxt = fa_aread<WT, PPW>(arow + (s + 2 < ST || c1 < bv ? c1 : bv - 1) * g.rsb);
+      for (int ch = 0; ch < NB; ++ch) {
+        float xv[4][PPW];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c0 = 16 * ch + 4 * lg + i;
+          const bool live = ch + 1 < NB || c0 < bv;  // only the last chunk can pass the radix
+          const uint2 rd = fa_aread<WT, PPW>(arow + (live ? c0 : bv - 1) * g.rsb);
+          fa_unpack<WT, PPW>(rd, xv[i]);
+#pragma unroll
+          for (int j = 0; j < PPW; ++j) xv[i][j] = live ? __builtin_ldexpf(xv[i][j], ks) : 0.f;
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep that read ahead of this step's products
-        const bool live = s + 1 < ST || 4 * s + lg < bv;
-        float av[PPW];
-        fa_unpack<WT, PPW>(cur, av);
 #pragma unroll
-        for (int j = 0; j < PPW; ++j) d[j] = mfma4(live ? av[j] : 0.f, bvf[j][nt][s], d[j]);
+        for (int j = 0; j < PPW; ++j) {
+          const f4 xs = {xv[0][j], xv[1][j], xv[2][j], xv[3][j]};
+          const h4 hi = __builtin_convertvector(xs, h4);
+          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(hi, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                        __builtin_bit_cast(h8, vb[j][nt][ch]), d[j], 0, 0, 0);
+          if constexpr (WT == BRQ_F32) {
+            f4 r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, xs[i]);
+            const h4 lo = __builtin_convertvector(r, h4);
+            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(lo, lo, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                          __builtin_bit_cast(h8, vb[j][nt][ch]), d[j], 0, 0, 0);
+          }
+        }
       }
       // the next slab's loads queue behind the previous stores: issued after
-      // the first tile's products they no longer hold up the MFMA phase
-      if (nt == 0 && qi + 1 < kFaQC) {
+      // the last V_0 products they no longer hold up the MFMA phase
+      if (nt == NB - 1 && qi + 1 < kFaQC) {
         load_slab(q + 1);
-        bu = ld4(a.u0 + (int64_t)(q + 1) * a.u0_gs + lr * 16 + 4 * lg);
+        eu = load_u(q + 1);
       }
       // U_0 on the transpose: E[j][m = c0'][n = r0'] = sum_r0 U[r0'][r0] D[j][r0][c0']
       f4 e[PPW];
 #pragma unroll
-      for (int j = 0; j < PPW; ++j) e[j] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < PPW; ++j) {
+        e[j] = a.u0_exact ? fb_prod<true>(d[j], bhh, bll, m1) : fb_prod<false>(d[j], bhh, bll, m1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) e[j] = mfma4(d[j][i], bq[i], e[j]);
+        for (int i = 0; i < 4; ++i) e[j][i] = __builtin_ldexpf(e[j][i], -ks);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c0 = 16 * nt + 4 * lg + i;
@@ -209,8 +311,10 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
           float* o = outa + fa_out(g, lr, c0, PPW * w);
           if constexpr (PPW == 4)
             *reinterpret_cast<f4*>(o) = f4{e[0][i], e[1][i], e[2][i], e[3][i]};
-          else
+          else if constexpr (PPW == 2)
             *reinterpret_cast<float2*>(o) = make_float2(e[0][i], e[1][i]);
+          else
+            *o = e[0][i];
         }
       }
     }
@@ -333,44 +437,6 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
 
 constexpr int FB_IL = 2;   // pass B phase 1: fragments whose MFMA chains interleave
 constexpr int FB_IL2 = 2;  // pass B phase 2 (its registers are shared with the prefetched tile)
-
-// One stage of pass B for one 16 x 16 fragment: the lane's four float32
-// values a[i] (contraction index k = 4 lg + i) times the block entries for the
-// same k, bhh = (bh, bh) and bll = (bl, bl).  The data split is hi = f16(a),
-// lo = f16(a - hi), both rounded to nearest (a - hi is exact in float32, so
-// hi + lo holds a to 2^-22 relative); products of f16 values are exact in
-// float32.  m1 is -1 from a scalar register: a constant -1 would let the
-// compiler turn the multiply-add into a subtraction, which costs a conversion
-// of hi back to float32 where v_fma_mix_f32 reads the f16 directly.
-//   (hi, lo) . (bh, bh), then (hi, lo) . (bl, bl) into the same accumulator
-//   (not for blocks exact in f16, EX).
-// The second product uses the same K = 32 instruction as the first: chained
-// through the accumulator after a K = 32 product, v_mfma_f32_16x16x16_f16
-// read a stale accumulator on gfx950 (the compiler issued them back to back).
-template <bool EX>
-__device__ __forceinline__ f4 fb_prod(const f4& a, const u4& bhh, const u4& bll, float m1) {
-  const h4 hi = __builtin_convertvector(a, h4);
-  f4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, a[i]);
-  const h4 lo = __builtin_convertvector(r, h4);
-  const h8 A = __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
-  const f4 z = {0.f, 0.f, 0.f, 0.f};
-  const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bhh), z, 0, 0, 0);
-  if constexpr (EX) return d;
-  else return __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(h8, bll), d, 0, 0, 0);
-}
-
-// -1 in a scalar register, hidden from constant folding.
-__device__ __forceinline__ float fb_minus_one() {
-  float v = -1.0f;
-  asm volatile("" : "+s"(v));
-  return v;
-}
-
-// (bh, bh) and (bl, bl) of a block entry (bh, bl).
-__device__ __forceinline__ u4 fb_hh(const u4& e) { return u4{e.x, e.y, e.x, e.y}; }
-__device__ __forceinline__ u4 fb_ll(const u4& e) { return u4{e.z, e.w, e.z, e.w}; }
 
 // Load half H of the tile's float32 block for phase 1: x[c2][i] = element
 // (r1 = lr, c1 = 4 lg + i, r2 = w, c2) for i = 2H, 2H + 1, which is 128
