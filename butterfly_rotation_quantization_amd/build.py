@@ -23,6 +23,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libbrq.so")
 DRYRUN_LIB = os.path.join(LIBDIR, "libbrq_dryrun.so")
+DRYRUN_ASAN_LIB = os.path.join(LIBDIR, "libbrq_dryrun_asan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -47,9 +48,28 @@ def dryrun_sources():
     return sorted(host + glob.glob(os.path.join(CSRC, "dryrun", "*.cpp")))
 
 
-def _compile(src: str, verbose: bool, objdir: str = OBJ) -> str:
+# AddressSanitizer for the host code of the dry-run build (it holds no device
+# code; the instrumentation is asked for the host side only).  The library
+# leaves the sanitizer runtime unresolved: a process loads it first
+# (LD_PRELOAD of asan_runtime()).
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's AddressSanitizer runtime for x86-64 in the ROCm LLVM."""
+    r = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang"),
+                        "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        matches = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        path = matches[-1] if matches else ""
+    return path
+
+
+def _compile(src: str, verbose: bool, objdir: str = OBJ, extra=()) -> str:
     obj = os.path.join(objdir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -72,15 +92,19 @@ def _link(objs, out, verbose):
 
 
 def build(jobs: int = 8, verbose: bool = False) -> str:
+    """libbrq.so, its dry-run build and the dry-run build under AddressSanitizer."""
     dry_obj = os.path.join(OBJ, "dryrun")
-    os.makedirs(dry_obj, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    jobs_list = [(s, OBJ) for s in sources()] + [(s, dry_obj) for s in dryrun_sources()]
+    asan_obj = os.path.join(OBJ, "dryrun_asan")
+    for d in (dry_obj, asan_obj, LIBDIR):
+        os.makedirs(d, exist_ok=True)
+    jobs_list = ([(s, OBJ, ()) for s in sources()] + [(s, dry_obj, ()) for s in dryrun_sources()] +
+                 [(s, asan_obj, tuple(ASAN_FLAGS)) for s in dryrun_sources()])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda sj: _compile(sj[0], verbose, sj[1]), jobs_list))
-    n = len(sources())
+        objs = list(ex.map(lambda sj: _compile(sj[0], verbose, sj[1], sj[2]), jobs_list))
+    n, k = len(sources()), len(dryrun_sources())
     _link(objs[:n], LIB, verbose)
-    _link(objs[n:], DRYRUN_LIB, verbose)
+    _link(objs[n:n + k], DRYRUN_LIB, verbose)
+    _link(objs[n + k:], DRYRUN_ASAN_LIB, verbose)
     return LIB
 
 

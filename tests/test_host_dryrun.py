@@ -22,9 +22,12 @@ X, Y, WS, CODES, SCALES = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x5000
 @pytest.fixture(scope="module")
 def dl():
     import os
-    if not os.path.exists(brq.DRYRUN_LIB_PATH):
-        pytest.fail("libbrq_dryrun.so is not built")
-    lib = brq.load_library(brq.DRYRUN_LIB_PATH)
+    # BRQ_DRYRUN_LIB selects another build of the same library (the
+    # AddressSanitizer one, from test_host_asan.py)
+    path = os.environ.get("BRQ_DRYRUN_LIB", brq.DRYRUN_LIB_PATH)
+    if not os.path.exists(path):
+        pytest.fail(f"{os.path.basename(path)} is not built")
+    lib = brq.load_library(path)
     lib.brq_dryrun_violation.restype = ctypes.c_char_p
     lib.brq_dryrun_launches.restype = ctypes.c_longlong
     lib.brq_dryrun_rows_launches.restype = ctypes.c_longlong
