@@ -284,12 +284,13 @@ class TwoSidedWeight(Workload):
             fl = (stage_flops((16,), True, E) * 2 if had
                   else stage_flops((L.radix[0], R.radix[0]), False, E))
             blk = 0 if had else 4 * (M * L.radix[0] + N * R.radix[0])
-            return E * 2 + E * 4 + blk + 4 * (M + N), fl, "mfma"
+            # products on split-f16 MFMA: the f16 peak applies
+            return E * 2 + E * 4 + blk + 4 * (M + N), fl, "mfma16"
         if name.startswith("fusedB"):
             fl = (stage_flops((16, 16), True, E) * 2 if had
                   else stage_flops(L.radix[1:] + R.radix[1:], False, E))
             blk = 0 if had else 4 * (M * sum(L.radix[1:]) + N * sum(R.radix[1:]))
-            return E * 4 + q_out + blk, fl, "mfma"
+            return E * 4 + q_out + blk, fl, "mfma16"
         if name.startswith("rowhad quant"):  # quantizer pass over the float32 intermediate
             return E * 4 + q_out, 0, "alu"
         # stage pass ("stage L(b) S..") or generic tile pass ("pass L(..) R(..) [quant]")

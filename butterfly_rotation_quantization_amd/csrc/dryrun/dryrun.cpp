@@ -337,9 +337,9 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
   const int64_t ntiles = fb_nwg(a);
   if (grid < 1 || grid > ntiles) return violation("pass B grid %lld of %lld tiles", grid, ntiles), hipErrorInvalidValue;
   std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
-  std::vector<int> slot(kFbXchFloats);
+  std::vector<int> slot(kFbXchFloats), qread(kFbXchFloats);
   const int bits = a.bits, g = a.group;
-  const int fpg = g / 16, nw = fpg * 16 * bits / 32;
+  std::vector<uint8_t> code_bytes((size_t)(a.m * a.codes_ld), 0), scale_seen((size_t)(a.m * a.scales_ld), 0);
   std::vector<int> tiles_seen((size_t)ntiles, 0);
   for (int e = 0; e < 255; ++e) {  // the tile scale puts every maximum in [64, 128), or scales by 2^127
     const float mlo = e ? std::ldexp(1.0f, e - 127) : 0.0f;
@@ -418,6 +418,7 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
         }
       for (int h = 0; h < 2; ++h) {
         std::fill(slot.begin(), slot.end(), 0);
+        std::fill(qread.begin(), qread.end(), 0);
         for (int w = 0; w < kFbWaves; ++w)
           for (int l = 0; l < 64; ++l) {
             const int lr = l & 15, lg = l >> 4;
@@ -446,20 +447,40 @@ hipError_t launch_fused_b(const FusedBArgs& a, int grid, hipStream_t) {
               for (int i = 0; i < 4; ++i)
                 if (fb_xch(w, c1h, lr, 4 * lg + i) != s + i) return violation("exchange quad %lld", s, i), hipErrorInvalidValue;
             }
-            if (lg != 0) continue;
+            // the quantizer: lane (lr, lg) reads row r2 = lr, c1h = 2 lg + e, all c2
+            for (int e = 0; e < 2; ++e)
+              for (int q = 0; q < 4; ++q) {
+                const int sq = fb_xch(w, 2 * lg + e, lr, 4 * q);
+                if (!in_range(sq, 4, kFbXchFloats) || sq % 4)
+                  return violation("quantizer read %lld", sq, 0), hipErrorInvalidValue;
+                for (int i = 0; i < 4; ++i) {
+                  if (fb_xch(w, 2 * lg + e, lr, 4 * q + i) != sq + i)
+                    return violation("quantizer quad %lld", sq, i), hipErrorInvalidValue;
+                  qread[sq + i]++;
+                }
+              }
             const int64_t row = fb_row(t, w, lr);
-            for (int gi = 0; gi < 128 / g; ++gi) {
-              const int64_t col0 = fb_col(a, t, 8 * h + gi * fpg, 0);
-              if (col0 % g) return violation("group start %lld", col0, g), hipErrorInvalidValue;
-              const int64_t off = row * a.codes_ld + col0 * bits / 8;
-              if (!in_range(off, 4 * nw, a.m * a.codes_ld) || off % 4)
-                return violation("codes [%lld, +%lld)", off, 4 * nw), hipErrorInvalidValue;
-              if (!in_range(row * a.scales_ld + col0 / g, 1, a.m * a.scales_ld))
-                return violation("scale %lld", row * a.scales_ld + col0 / g, 0), hipErrorInvalidValue;
+            const int64_t col0 = fb_col(a, t, 8 * h + 2 * lg, 0);
+            if (col0 % 32) return violation("quantizer columns start %lld", col0, 0), hipErrorInvalidValue;
+            const int64_t off = row * a.codes_ld + col0 * bits / 8;
+            if (!in_range(off, 4 * bits, a.m * a.codes_ld) || off % 4)
+              return violation("codes [%lld, +%lld)", off, 4 * bits), hipErrorInvalidValue;
+            for (int64_t b = off; b < off + 4 * bits; ++b) code_bytes[(size_t)b]++;
+            if (fb_scale_lane(lg, g)) {
+              const int64_t si = row * a.scales_ld + col0 / g;
+              if (!in_range(si, 1, a.m * a.scales_ld))
+                return violation("scale %lld", si, 0), hipErrorInvalidValue;
+              scale_seen[(size_t)si]++;
             }
           }
+        for (int sq = 0; sq < kFbXchFloats; ++sq)  // each half's slots are read exactly once
+          if (qread[sq] != 1) return violation("quantizer read slot %lld %lld times", sq, qread[sq]), hipErrorInvalidValue;
       }
     }
+  for (size_t b = 0; b < code_bytes.size(); ++b)
+    if (code_bytes[b] != 1) return violation("code byte %lld written %lld times", (int64_t)b, code_bytes[b]), hipErrorInvalidValue;
+  for (size_t i = 0; i < scale_seen.size(); ++i)
+    if (scale_seen[i] != 1) return violation("scale %lld written %lld times", (int64_t)i, scale_seen[i]), hipErrorInvalidValue;
   for (int64_t i = 0; i < ntiles; ++i)
     if (tiles_seen[(size_t)i] != 1) return violation("pass B tile %lld visited %lld times", i, tiles_seen[(size_t)i]), hipErrorInvalidValue;
   for (int64_t i = 0; i < a.m * a.n; ++i)

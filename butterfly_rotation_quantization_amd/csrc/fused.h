@@ -293,6 +293,11 @@ __host__ __device__ inline int fb_vslot(int j, int q) {
   return (j * 4 + (q ^ (((j >> 1) & 3) ^ ((j >> 3) & 1)))) * 4;
 }
 
+// Pass B's quantizer: lane (lr, lg) codes 32 consecutive columns of one row,
+// so a group of g columns spans g / 32 lanes of consecutive lg; the first of
+// them stores the group's statistic.
+__host__ __device__ constexpr bool fb_scale_lane(int lg, int g) { return (lg & (g / 32 - 1)) == 0; }
+
 // Row order of the V_1 products: output tile row n holds c1' = fb_sigma(n),
 // so MFMA result register j of lane group lg holds c1' = lg + 4 j and the
 // exchange half h (c1' in [8h, 8h + 8)) is registers 2h and 2h + 1 of every

@@ -335,103 +335,76 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
 
 // ------------------------------------------------------------------ pass B
 
-// Group statistic of one lane's four values: absmax, or sum of squares for
-// the norm quantizer (reduced over the four lane groups and rooted later).
-template <int QK>
-__device__ __forceinline__ float fb_stat(float acc, const f4& v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = QK == BRQ_ABSMAX ? fmaxf(acc, fabsf(v[i])) : fmaf(v[i], v[i], acc);
-  return acc;
-}
-
 // Quantize and pack half h of the tile rows of r1.  The phase-2 results were
-// written back in place into this wave's part of the exchange buffer, where
-// slot (r1, c1h, r2, 4 lg) holds row r2's four consecutive columns
-// c1 = 8h + c1h, c2 = 4 lg .. 4 lg + 3; stat[gi] holds this lane's part of
-// group gi's statistic.  Each fragment is read back, coded and packed in turn.
-// The values carry the tile scale 2^ks: the codes depend only on v / stat,
-// which the power of two leaves exact, and the stored statistic is scaled
-// back by 2^-ks (exact as well).
+// written back in place into this wave's part of the exchange buffer, slot
+// (r1, c1h, r2, c2) holding row r2, column c1 = 8h + c1h, c2.  Lane (lr, lg)
+// takes row r2 = lr and the 32 consecutive columns c1h = 2 lg, 2 lg + 1, all
+// c2: it reduces their statistic, then with the lanes of the same row that
+// share its quantizer group (lg ^ 1 for g = 64, all four lg for g = 128),
+// codes the 32 values and writes them as BITS whole 32-bit words.  The values
+// carry the tile scale 2^ks: the codes depend only on v / stat, which the
+// power of two leaves exact, and the stored statistic is scaled back by
+// 2^-ks (exact as well).
 template <int BITS, int QK, int G>
 __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t, int r1, int h,
-                                            const float* xch, const float (&stat_in)[128 / G], int lr,
-                                            int lg, int ks) {
-  constexpr int NG = 128 / G;      // groups in this half
-  constexpr int FPG = 8 / NG;      // 16-column fragments per group
+                                            const float* xch, int lr, int lg, int ks) {
   constexpr int LV = (1 << BITS) - 1;
-  constexpr int NW = FPG * 16 * BITS / 32;  // 32-bit code words per row and group
+  f4 v[8];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[4 * e + q] = ld4(&xch[fb_xch(r1, 2 * lg + e, lr, 4 * q)]);
+  float stat = 0.f;
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      stat = QK == BRQ_ABSMAX ? fmaxf(stat, fabsf(v[f][i])) : fmaf(v[f][i], v[f][i], stat);
+  if (QK == BRQ_ABSMAX) {
+    stat = fmaxf(stat, __shfl_xor(stat, 16, 64));
+    if (G == 128) stat = fmaxf(stat, __shfl_xor(stat, 32, 64));
+  } else {
+    stat += __shfl_xor(stat, 16, 64);
+    if (G == 128) stat += __shfl_xor(stat, 32, 64);
+    stat = sqrtf(stat);
+  }
+  const bool live = stat > 0.f;  // a zero group codes as all zeros
+  const float k = live ? (QK == BRQ_ABSMAX ? a.h / stat : a.sqrt_g / stat) : 0.f;
+  uint32_t words[BITS];
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) words[j] = 0u;
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c;
+      if (QK == BRQ_ABSMAX) {
+        // |v| <= stat and k = RN(h / stat) keep v k + h within
+        // [-h 2^-24, 2h (1 + 2^-24)], which rounds into [0, LV]: no clamp
+        c = (int)__builtin_rintf(fmaf(v[f][i], k, a.h));
+      } else {
+        const float z = v[f][i] * k;
+        c = 0;
+#pragma unroll
+        for (int q = 0; q < LV; ++q) c += (z > a.tau[q]) ? 1 : 0;
+      }
+      c = live ? c : 0;
+      const int bit = (4 * f + i) * BITS, wi = bit >> 5, sh = bit & 31;
+      words[wi] |= (uint32_t)c << sh;
+      if (sh + BITS > 32) words[wi + 1] |= (uint32_t)c >> (32 - sh);
+    }
   const int64_t row = fb_row(t, r1, lr);
+  const int64_t col0 = fb_col(a, t, 8 * h + 2 * lg, 0);
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.codes + row * a.codes_ld + col0 * BITS / 8);
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    float stat = stat_in[gi];
-    if (QK == BRQ_ABSMAX) {
-      stat = fmaxf(stat, __shfl_xor(stat, 16, 64));
-      stat = fmaxf(stat, __shfl_xor(stat, 32, 64));
-    } else {
-      stat += __shfl_xor(stat, 16, 64);
-      stat += __shfl_xor(stat, 32, 64);
-      stat = sqrtf(stat);
-    }
-    const float k = stat > 0.f ? (QK == BRQ_ABSMAX ? a.h / stat : a.sqrt_g / stat) : 0.f;
-    // Packing: lane group lg assembles the words of fragments
-    // [lg * FPG / 4, (lg + 1) * FPG / 4) when they end on a word boundary
-    // (NW divisible by 4), else lane group 0 assembles all NW words.
-    constexpr bool SPLIT = NW % 4 == 0;
-    constexpr int NWL = SPLIT ? NW / 4 : NW;  // words per assembling lane
-    uint32_t words[NWL];
-#pragma unroll
-    for (int j = 0; j < NWL; ++j) words[j] = 0u;
-#pragma unroll
-    for (int f = 0; f < FPG; ++f) {
-      const f4 v = ld4(&xch[fb_xch(r1, gi * FPG + f, lr, 4 * lg)]);
-      uint32_t c4 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int c = 0;
-        if (stat > 0.f) {
-          if (QK == BRQ_ABSMAX) {
-            // |v| <= stat and k = RN(h / stat) keep v k + h within
-            // [-h 2^-24, 2h (1 + 2^-24)], which rounds into [0, LV]: no clamp
-            c = (int)__builtin_rintf(fmaf(v[i], k, a.h));
-          } else {
-            const float z = v[i] * k;
-#pragma unroll
-            for (int q = 0; q < LV; ++q) c += (z > a.tau[q]) ? 1 : 0;
-          }
-        }
-        c4 |= (uint32_t)c << (BITS * i);
-      }
-      // the row's four chunks of this fragment (4 codes each)
-      const bool mine = SPLIT ? lg == f / (FPG / 4) : lg == 0;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t ch = (uint32_t)__shfl((int)c4, lr + 16 * q4, 64);
-        const int bit = (SPLIT ? (f % (FPG / 4)) * 4 + q4 : f * 4 + q4) * 4 * BITS;
-        const int wi = bit >> 5, sh = bit & 31;
-        if (mine) {
-          words[wi] |= ch << sh;
-          if (sh + 4 * BITS > 32) words[wi + 1] |= ch >> (32 - sh);
-        }
-      }
-      // one fragment at a time: read-ahead of the others would hold registers
-      // that the prefetched tile needs
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const int64_t col0 = fb_col(a, t, 8 * h + gi * FPG, 0);
-    const int64_t gcol = col0 / G;
-    if (lg == 0) {
-      const float st = __builtin_ldexpf(stat, -ks);
-      if (QK == BRQ_ABSMAX)
-        static_cast<float*>(a.scales)[row * a.scales_ld + gcol] = st;
-      else
-        static_cast<_Float16*>(a.scales)[row * a.scales_ld + gcol] = (_Float16)st;
-    }
-    if (SPLIT || lg == 0) {
-      uint32_t* out = reinterpret_cast<uint32_t*>(a.codes + row * a.codes_ld + col0 * BITS / 8) +
-                      (SPLIT ? lg * NWL : 0);
-#pragma unroll
-      for (int j = 0; j < NWL; ++j) out[j] = words[j];
-    }
+  for (int j = 0; j < BITS; ++j) out[j] = words[j];
+  if (fb_scale_lane(lg, G)) {
+    const int64_t gi = row * a.scales_ld + col0 / G;
+    const float st = __builtin_ldexpf(stat, -ks);
+    if (QK == BRQ_ABSMAX)
+      static_cast<float*>(a.scales)[gi] = st;
+    else
+      static_cast<_Float16*>(a.scales)[gi] = (_Float16)st;
   }
 }
 
@@ -578,9 +551,6 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
       lanes();
       // only this wave reads the slots of r1 = w, so each result goes back
       // into the slot its input came from
-      float stat[128 / G];
-#pragma unroll
-      for (int gi = 0; gi < 128 / G; ++gi) stat[gi] = 0.f;
       const u4 bu2 = fb_hh(e2), bl2 = fb_ll(e2);
 #pragma unroll
       for (int c1q = 0; c1q < 8; c1q += FB_IL2) {
@@ -599,11 +569,14 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
           const f4 v = fb_prod<EX>(d[f], bu2, bl2, m1);  // U_2: r2
           // v: element (row r2' = lr, column c1 = 8h + c1q + f, c2' = 4lg + i)
           *reinterpret_cast<f4*>(&xch[fb_xch(w, c1q + f, lr, 4 * lg)]) = v;
-          stat[(c1q + f) / (G / 16)] = fb_stat<QK>(stat[(c1q + f) / (G / 16)], v);
         }
       }
+      // the quantizer reads what other lanes of this wave wrote: a wave's LDS
+      // accesses complete in order, and the fence keeps the compiler from
+      // moving the reads above the writes
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       lanes();
-      fb_quantize<BITS, QK, G>(a, t, w, h, xch, stat, lr, lg, ks);
+      fb_quantize<BITS, QK, G>(a, t, w, h, xch, lr, lg, ks);
     }
     if (!more) break;
     lanes();
