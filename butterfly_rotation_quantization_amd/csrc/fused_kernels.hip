@@ -349,17 +349,16 @@ template <int BITS, int QK, int G>
 __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t, int r1, int h,
                                             const float* xch, int lr, int lg, int ks) {
   constexpr int LV = (1 << BITS) - 1;
-  f4 v[8];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[4 * e + q] = ld4(&xch[fb_xch(r1, 2 * lg + e, lr, 4 * q)]);
+  // The values are read twice, for the statistic and for the codes: held
+  // between the two they would take 32 registers next to the prefetched tile.
   float stat = 0.f;
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int f = 0; f < 8; ++f) {
+    const f4 v = ld4(&xch[fb_xch(r1, 2 * lg + (f >> 2), lr, 4 * (f & 3))]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      stat = QK == BRQ_ABSMAX ? fmaxf(stat, fabsf(v[f][i])) : fmaf(v[f][i], v[f][i], stat);
+    for (int i = 0; i < 4; ++i) stat = QK == BRQ_ABSMAX ? fmaxf(stat, fabsf(v[i])) : fmaf(v[i], v[i], stat);
+  }
+  asm volatile("" ::: "memory");
   if (QK == BRQ_ABSMAX) {
     stat = fmaxf(stat, __shfl_xor(stat, 16, 64));
     if (G == 128) stat = fmaxf(stat, __shfl_xor(stat, 32, 64));
@@ -374,16 +373,17 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
 #pragma unroll
   for (int j = 0; j < BITS; ++j) words[j] = 0u;
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int f = 0; f < 8; ++f) {
+    const f4 v = ld4(&xch[fb_xch(r1, 2 * lg + (f >> 2), lr, 4 * (f & 3))]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int c;
       if (QK == BRQ_ABSMAX) {
         // |v| <= stat and k = RN(h / stat) keep v k + h within
         // [-h 2^-24, 2h (1 + 2^-24)], which rounds into [0, LV]: no clamp
-        c = (int)__builtin_rintf(fmaf(v[f][i], k, a.h));
+        c = (int)__builtin_rintf(fmaf(v[i], k, a.h));
       } else {
-        const float z = v[f][i] * k;
+        const float z = v[i] * k;
         c = 0;
 #pragma unroll
         for (int q = 0; q < LV; ++q) c += (z > a.tau[q]) ? 1 : 0;
@@ -393,6 +393,7 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
       words[wi] |= (uint32_t)c << sh;
       if (sh + BITS > 32) words[wi + 1] |= (uint32_t)c >> (32 - sh);
     }
+  }
   const int64_t row = fb_row(t, r1, lr);
   const int64_t col0 = fb_col(a, t, 8 * h + 2 * lg, 0);
   uint32_t* out = reinterpret_cast<uint32_t*>(a.codes + row * a.codes_ld + col0 * BITS / 8);
@@ -411,12 +412,14 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
 constexpr int FB_IL = 2;   // pass B phase 1: fragments whose MFMA chains interleave
 constexpr int FB_IL2 = 2;  // pass B phase 2 (its registers are shared with the prefetched tile)
 
-// Load half H of the tile's float32 block for phase 1: x[c2][i] = element
-// (r1 = lr, c1 = 4 lg + i, r2 = w, c2) for i = 2H, 2H + 1, which is 128
-// contiguous bytes of one row per lane.
+// Load half H of the tile's float32 block for phase 1: x[c2] = elements
+// (r1 = lr, c1 = 4 lg + 2H + e, r2 = w, c2) for e = 0, 1, which is 128
+// contiguous bytes of one row per lane.  The tile is held as two arrays of
+// float2 (c1 = 4 lg + {0, 1} and 4 lg + {2, 3}), so that each half's
+// registers are free on their own once the exchange has taken them.
 template <int H>
 __device__ __forceinline__ void fb_load_half(const FusedBArgs& a, const FbTile& t, int w, int lr,
-                                             int lg, f4 (&x)[16]) {
+                                             int lg, float2 (&x)[16]) {
   const float* src = a.ws + fb_row(t, lr, w) * a.n + fb_col(a, t, 4 * lg + 2 * H, 0);
 #pragma unroll
   for (int e = 0; e < 2; ++e)
@@ -424,7 +427,7 @@ __device__ __forceinline__ void fb_load_half(const FusedBArgs& a, const FbTile& 
     for (int qd = 0; qd < 4; ++qd) {
       const f4 v = ld4(src + e * 16 + 4 * qd);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[4 * qd + j][2 * H + e] = v[j];
+      for (int j = 0; j < 4; ++j) (e ? x[4 * qd + j].y : x[4 * qd + j].x) = v[j];
     }
 }
 
@@ -452,10 +455,10 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   int64_t tile = blockIdx.x;
   if (tile >= ntiles) return;
 
-  f4 x[16];
+  float2 xa[16], xb[16];
   FbTile t = fb_tile(a, tile);
-  fb_load_half<0>(a, t, w, lr, lg, x);
-  fb_load_half<1>(a, t, w, lr, lg, x);
+  fb_load_half<0>(a, t, w, lr, lg, xa);
+  fb_load_half<1>(a, t, w, lr, lg, xb);
   auto load_u = [&](const uint16_t* blk, int64_t gs, const FbTile& tt) {
     return *reinterpret_cast<const u4*>(blk + (int64_t)(tt.r0 * 16 + w) * gs + fb_hentry(lr, lg));
   };
@@ -467,8 +470,7 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
     float mx = 0.f;
 #pragma unroll
     for (int c = 0; c < 16; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(x[c][i]));
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xa[c].x), fabsf(xa[c].y)), fmaxf(fabsf(xb[c].x), fabsf(xb[c].y))));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     __syncthreads();  // the previous tile is done with LDS
@@ -496,9 +498,10 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
       ks = __builtin_amdgcn_readfirstlane(fb_scale_shift(__float_as_uint(m)));
     }
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[c][i] = __builtin_ldexpf(x[c][i], ks);
+    for (int c = 0; c < 16; ++c) {
+      xa[c] = make_float2(__builtin_ldexpf(xa[c].x, ks), __builtin_ldexpf(xa[c].y, ks));
+      xb[c] = make_float2(__builtin_ldexpf(xb[c].x, ks), __builtin_ldexpf(xb[c].y, ks));
+    }
 
     // ---- phase 1: this wave owns r2 = w; fragments over (r1, c1), one per c2.
     lanes();
@@ -514,11 +517,17 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
           const u4 bv = __builtin_bit_cast(u4, ld4(&lds[v1_lane + (c2q + f) * 256]));
           const u4 bl = EX ? u4{0u, 0u, 0u, 0u}
                            : __builtin_bit_cast(u4, ld4(&lds[v1_lane + kFbV1LOff + (c2q + f) * 256]));
-          d[f] = fb_prod<EX>(x[c2q + f], bv, bl, m1);  // V_1: c1
+          const int c = c2q + f;
+          d[f] = fb_prod<EX>(f4{xa[c].x, xa[c].y, xb[c].x, xb[c].y}, bv, bl, m1);  // V_1: c1
         }
 #pragma unroll
-        for (int f = 0; f < FB_IL; ++f) x[c2q + f] = fb_prod<EX>(d[f], bu1, bl1, m1);  // U_1: r1
-        // x[c2][j]: element (c1' = lg + 4 j, r1' = lr)
+        for (int f = 0; f < FB_IL; ++f) {
+          const f4 r = fb_prod<EX>(d[f], bu1, bl1, m1);  // U_1: r1
+          xa[c2q + f] = make_float2(r[0], r[1]);
+          xb[c2q + f] = make_float2(r[2], r[3]);
+        }
+        // register j of fragment c2 (xa: j = 0, 1; xb: j = 2, 3): element
+        // (c1' = lg + 4 j, r1' = lr)
       }
     }
 
@@ -537,15 +546,16 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
       for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const int j = 2 * h + e;
-          const f4 q4 = {x[4 * qd][j], x[4 * qd + 1][j], x[4 * qd + 2][j], x[4 * qd + 3][j]};
+          const float2* xh = h ? xb : xa;
+          const f4 q4 = e ? f4{xh[4 * qd].y, xh[4 * qd + 1].y, xh[4 * qd + 2].y, xh[4 * qd + 3].y}
+                          : f4{xh[4 * qd].x, xh[4 * qd + 1].x, xh[4 * qd + 2].x, xh[4 * qd + 3].x};
           *reinterpret_cast<f4*>(&xch[fb_xch(lro, lgo + 4 * e, w, 4 * qd)]) = q4;
         }
-      // after the second half every tile register is free: load the whole
-      // next tile
-      if (h == 1 && more) {
-        fb_load_half<0>(a, tn, w, lro, lgo, x);
-        fb_load_half<1>(a, tn, w, lro, lgo, x);
+      // registers 2h and 2h + 1 are free now: load the next tile's half h
+      // into them
+      if (more) {
+        if (h == 0) fb_load_half<0>(a, tn, w, lro, lgo, xa);
+        else fb_load_half<1>(a, tn, w, lro, lgo, xb);
       }
       __syncthreads();
       lanes();
