@@ -437,6 +437,7 @@ __device__ __forceinline__ void fb_load_half(const FusedBArgs& a, const FbTile& 
 // half of phase 2 and its quantizer.
 template <int BITS, int QK, int G, bool EX>
 __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
+  static_assert(kFbWaves * 64 == 16 * 64, "one thread per entry of the 16 staged blocks of a stage");
   extern __shared__ float lds[];
   float* xch = lds;
   const int tid = threadIdx.x;
@@ -466,6 +467,15 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   const float m1 = fb_minus_one();
 
   for (;;) {
+    // the tile's V_1 and V_2 block entries (16 blocks each, groups c0*16 + f):
+    // thread tid stages entry tid of each, loaded before the wait for the tile
+    u4 ve[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int f = tid >> 6, qd = tid & 63;
+      ve[r] = *reinterpret_cast<const u4*>((r ? a.v2 : a.v1) + (int64_t)(t.c0 * 16 + f) * (r ? a.v2_gs : a.v1_gs) +
+                                           fb_hentry(qd >> 2, qd & 3));
+    }
     // the wave's largest magnitude (waits for the tile's loads)
     float mx = 0.f;
 #pragma unroll
@@ -475,16 +485,12 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     __syncthreads();  // the previous tile is done with LDS
     if ((tid & 63) == 0) lds[kFbMaxOff + w] = mx;
-    // stage the tile's V_1 and V_2 blocks (16 each, groups c0*16 + f)
-    for (int k = tid; k < 2 * 16 * 64; k += kFbWaves * 64) {
-      const int which = k >> 10, rem = k & 1023, f = rem >> 6, qd = rem & 63;
-      const int j = qd >> 2, q = qd & 3;
-      const uint16_t* src = (which ? a.v2 : a.v1) + (int64_t)(t.c0 * 16 + f) * (which ? a.v2_gs : a.v1_gs) +
-                            fb_hentry(j, q);
-      const u4 e = *reinterpret_cast<const u4*>(src);
-      st4(&lds[(which ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(j, q)], __builtin_bit_cast(f4, fb_hh(e)));
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int f = tid >> 6, j = (tid & 63) >> 2, q = tid & 3;
+      st4(&lds[(r ? kFbV2Off : kFbV1Off) + f * 256 + fb_vslot(j, q)], __builtin_bit_cast(f4, fb_hh(ve[r])));
       if (!EX)
-        st4(&lds[(which ? kFbV2LOff : kFbV1LOff) + f * 256 + fb_vslot(j, q)], __builtin_bit_cast(f4, fb_ll(e)));
+        st4(&lds[(r ? kFbV2LOff : kFbV1LOff) + f * 256 + fb_vslot(j, q)], __builtin_bit_cast(f4, fb_ll(ve[r])));
     }
     __syncthreads();
     // the tile scale 2^ks (uniform over the workgroup)
