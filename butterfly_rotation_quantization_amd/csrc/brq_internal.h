@@ -25,13 +25,15 @@ struct Plan {
   float* blk = nullptr;              // blocks as given, [group][j][k] (or [j][k] shared)
   float* blkT = nullptr;             // the same blocks transposed, for the inverse
   float* signs = nullptr;            // +-1 as float, or nullptr
-  // Fast-path data (fused_prepare), for plans of the shape (b0, 16, 16):
-  // stage-0 blocks with the signs folded in, zero-padded to 16*fz_nb and
-  // split into f16 (bh, bl) entries: as pass A's U_0 (fz0u, b0 = 16 only) and
-  // in pass A's V_0 fragment order (fz0v); halves between groups (0 = one
-  // block shared by all groups).
+  // Fast-path data (fused_prepare), for plans whose stage 0 has radix
+  // <= 64 and whose last two stages are radix 16 (Hadamard plans as
+  // (d / 256, 16, 16)): stage-0 blocks with the signs folded in, zero-padded
+  // to 16*fz_nb and split into f16 (bh, bl) entries: as pass A's U_0 (fz0u,
+  // radix 16 or 32 only) and in pass A's V_0 fragment order (fz0v); halves
+  // between groups (0 = one block shared by all groups).
   int fz_ok = 0;
-  int fz_b0 = 0;                     // radix of the fast path's stage 0 (d = fz_b0 * 256)
+  int fz_b0 = 0;                     // radix of the fast path's stage 0
+  int fz_s0 = 0;                     // its stride (d / fz_b0; 256 for Hadamard plans)
   int fz_nb = 0;
   uint16_t* fz0u = nullptr;
   uint16_t* fz0v = nullptr;

@@ -193,11 +193,13 @@ static bool in_range(int64_t lo, int64_t n, int64_t extent) { return lo >= 0 && 
 hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   ++g_launches;
   const int64_t nwg = fa_nwg(a);
-  const int nb = a.nb, bv = a.bv;
-  const FaGeom g = fa_geom(a.wt, nb, bv);
-  const int st = fa_steps(bv), ki = fa_ki(a.wt, st), kq = fa_kq_nt(a.wt, st);
+  const int nb = a.nb, bv = a.bv, ru = a.ru;
+  if (ru != 16 && ru != 32) return violation("pass A U_0 radix %lld", ru, 0), hipErrorInvalidValue;
+  const FaGeom g = fa_geom(a.wt, nb, bv, ru);
+  const int st = fa_steps(bv), ki = fa_ki(a.wt, st, ru), kq = fa_kq_nt(a.wt, st, ru);
   const int P = g.P, ppw = g.ppw, esz = g.esz, epi = 16 / esz, ipr = g.ipr;
-  if (64 % ipr || 256 % P || 8 * ki < 16 * fa_ncb(64 / ipr, st) || 8 * kq * (256 / P) < 256)
+  if (64 % ipr || a.sv % P || a.su % kFaQC || 8 * ki < ru * fa_ncb(64 / ipr, st) ||
+      8 * kq * (64 / (P / 4)) < ru * 16)
     return violation("pass A loop counts %lld / %lld", ki, kq), hipErrorInvalidValue;
   if (fa_lds_bytes(g) > 160 * 1024 || g.slab_bytes % 16 || g.max_off < g.slab_bytes + g.out_floats * 4 ||
       g.max_off % 4 || fa_lds_bytes(g) < g.max_off + 4 * kFaWaves)
@@ -218,7 +220,7 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
   for (int64_t b = 0; b < nwg; ++b) {
     const FaTile t = fa_tile(a, b, nwg);
-    if (t.p0 < 0 || t.p0 + P > 256 || t.p0 % P || t.q0 < 0 || t.q0 + kFaQC > 256 || t.chunk < 0 ||
+    if (t.p0 < 0 || t.p0 + P > a.sv || t.p0 % P || t.q0 < 0 || t.q0 + kFaQC > a.su || t.chunk < 0 ||
         t.chunk >= a.nchunk)
       return violation("pass A tile %lld of %lld", b, nwg), hipErrorInvalidValue;
     for (int w = 0; w < kFaWaves; ++w)
@@ -238,15 +240,15 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
         for (int l = 0; l < 64; ++l) {
           const int o = l % ipr;
           for (int k = 0; k < ki; ++k) {
-            const FaSlot x = fa_slot(ipr, w, k, l, bv, 0);
+            const FaSlot x = fa_slot(ipr, w, k, l, bv, 0, ru);
             const int r0 = x.r0, c0 = x.c0;
-            if (c0 < 0 || c0 >= bv) return violation("pass A load column %lld", c0, 0), hipErrorInvalidValue;
+            if (c0 < 0 || c0 >= bv || r0 >= ru) return violation("pass A load column %lld", c0, 0), hipErrorInvalidValue;
             loaded[(size_t)((r0 * bv + c0) * ipr + o)] = 1;
-            const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + o * epi);
+            const int64_t row = fa_row(a, r0, q), col = fa_col(a, t.chunk, c0, t.p0 + o * epi);
             if (row >= a.m || !in_range(col, epi, a.n) || col + epi > a.ldw || ((row * a.ldw + col) * esz) % 16)
               return violation("pass A input (%lld, %lld)", row, col), hipErrorInvalidValue;
-            // the kernel's 32-bit lane offset: (r0 * 256 * ldw + o * epi + c0 * 256) * esz
-            if ((r0 * 256 * a.ldw + o * epi + c0 * 256) * esz >= (int64_t(1) << 32))
+            // the kernel's 32-bit lane offset: (r0 * su * ldw + c0 * sv + o * epi) * esz
+            if (((int64_t)r0 * a.su * a.ldw + (int64_t)c0 * a.sv + o * epi) * esz >= (int64_t(1) << 32))
               return violation("pass A 32-bit input offset (%lld, %lld)", r0, c0), hipErrorInvalidValue;
             const int off = fa_slab_item(g, r0, c0, o);
             if (!in_range(off, 16, g.slab_bytes) || off % 8)
@@ -266,55 +268,59 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
       for (int w = 0; w < kFaWaves; ++w)
         for (int l = 0; l < 64; ++l) {
           const int lr = l & 15, lg = l >> 4;
-          if (!in_range((int64_t)q * a.u0_gs + fb_hentry(lr, lg), 8, a.u0_n))
-            return violation("U_0 block read q %lld lane %lld", q, l), hipErrorInvalidValue;
-          for (int ci = 0; ci < 16 * nb; ++ci) {  // chunk ci / 16, element (ci / 4) % 4 == lg, i = ci % 4
-            if (((ci / 4) & 3) != lg) continue;
-            const int c0 = std::min(ci, bv - 1);
-            const int off = fa_slab_read(g, lr, c0, w);
-            if (!in_range(off, ppw * esz, g.slab_bytes) || off % (ppw * esz))
-              return violation("pass A slab read at byte %lld", off, 0), hipErrorInvalidValue;
-            for (int e = 0; e < ppw; ++e)
-              for (int bb = 0; bb < esz; ++bb)
-                if (slab[(size_t)(off + e * esz + bb)] != code(lr, c0, ppw * w + e))
-                  return violation("pass A slab read of the wrong element at byte %lld", off + e * esz + bb, 0), hipErrorInvalidValue;
-          }
-          for (int nt = 0; nt < nb; ++nt)
-            for (int i = 0; i < 4; ++i) {
-              const int c0 = 16 * nt + 4 * lg + i;
-              if (c0 >= bv) continue;
-              const int off = fa_out(g, lr, c0, ppw * w);
-              if (!in_range(off, ppw, g.out_floats) || (off * 4) % (ppw * 4))
-                return violation("pass A output-area write %lld", off, 0), hipErrorInvalidValue;
-              for (int e = 0; e < ppw; ++e) {
-                int64_t& s = outa[(size_t)(off + e)];
-                if (s != -1) return violation("pass A output float %lld written twice", off + e, 0), hipErrorInvalidValue;
-                s = code(lr, c0, ppw * w + e);
-              }
+          for (int ot = 0; ot < ru / 16; ++ot)
+            for (int kt = 0; kt < ru / 16; ++kt)
+              if (!in_range((int64_t)q * a.u0_gs + fa_uhentry(ru, 16 * ot + lr, 4 * kt + lg), 8, a.u0_n))
+                return violation("U_0 block read q %lld lane %lld", q, l), hipErrorInvalidValue;
+          for (int mt = 0; mt < ru / 16; ++mt)
+            for (int ci = 0; ci < 16 * nb; ++ci) {  // chunk ci / 16, (ci / 4) % 4 == lg, i = ci % 4
+              if (((ci / 4) & 3) != lg) continue;
+              const int c0 = std::min(ci, bv - 1);
+              const int off = fa_slab_read(g, 16 * mt + lr, c0, w);
+              if (!in_range(off, ppw * esz, g.slab_bytes) || off % (ppw * esz))
+                return violation("pass A slab read at byte %lld", off, 0), hipErrorInvalidValue;
+              for (int e = 0; e < ppw; ++e)
+                for (int bb = 0; bb < esz; ++bb)
+                  if (slab[(size_t)(off + e * esz + bb)] != code(16 * mt + lr, c0, ppw * w + e))
+                    return violation("pass A slab read of the wrong element at byte %lld", off + e * esz + bb, 0), hipErrorInvalidValue;
             }
+          for (int nt = 0; nt < nb; ++nt)
+            for (int ot = 0; ot < ru / 16; ++ot)
+              for (int i = 0; i < 4; ++i) {
+                const int c0 = 16 * nt + 4 * lg + i;
+                if (c0 >= bv) continue;
+                const int off = fa_out(g, 16 * ot + lr, c0, ppw * w);
+                if (!in_range(off, ppw, g.out_floats) || (off * 4) % (ppw * 4))
+                  return violation("pass A output-area write %lld", off, 0), hipErrorInvalidValue;
+                for (int e = 0; e < ppw; ++e) {
+                  int64_t& s = outa[(size_t)(off + e)];
+                  if (s != -1) return violation("pass A output float %lld written twice", off + e, 0), hipErrorInvalidValue;
+                  s = code(16 * ot + lr, c0, ppw * w + e);
+                }
+              }
         }
-      std::vector<uint8_t> stored((size_t)16 * bv * (P / 4), 0);
+      std::vector<uint8_t> stored((size_t)ru * bv * (P / 4), 0);
       for (int w = 0; w < kFaWaves; ++w)
         for (int l = 0; l < 64; ++l) {
           const int pq = l % (P / 4);
           for (int k = 0; k < kq * nb; ++k) {
             const int nt = k / kq;
-            const FaSlot x = fa_slot(P / 4, w, k % kq, l, bv, 16 * nt);
+            const FaSlot x = fa_slot(P / 4, w, k % kq, l, bv, 16 * nt, ru);
             const int r0 = x.r0, c0 = x.c0;
             if (c0 < 16 * nt || c0 >= 16 * nt + 16)
               return violation("pass A store column %lld outside tile %lld", c0, nt), hipErrorInvalidValue;
             {
-              if (r0 >= 16 || c0 < 0 || c0 >= bv) return violation("pass A store row %lld col %lld", r0, c0), hipErrorInvalidValue;
+              if (r0 >= ru || c0 < 0 || c0 >= bv) return violation("pass A store row %lld col %lld", r0, c0), hipErrorInvalidValue;
               const int off = fa_out(g, r0, c0, 4 * pq);
               if (!in_range(off, 4, g.out_floats) || off % 4)
                 return violation("pass A output-area read %lld", off, 0), hipErrorInvalidValue;
               for (int e = 0; e < 4; ++e)
                 if (outa[(size_t)(off + e)] != code(r0, c0, 4 * pq + e))
                   return violation("pass A output-area read of the wrong value at %lld", off + e, 0), hipErrorInvalidValue;
-              const int64_t row = fa_row(r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * pq);
+              const int64_t row = fa_row(a, r0, q), col = fa_col(a, t.chunk, c0, t.p0 + 4 * pq);
               if (row >= a.m || !in_range(col, 4, a.n) || (row * a.n + col) % 4)
                 return violation("pass A store (%lld, %lld)", row, col), hipErrorInvalidValue;
-              if ((r0 * 256 * a.n + c0 * 256 + 4 * pq) * 4 >= (int64_t(1) << 32))
+              if (((int64_t)r0 * a.su * a.n + (int64_t)c0 * a.sv + 4 * pq) * 4 >= (int64_t(1) << 32))
                 return violation("pass A 32-bit output offset (%lld, %lld)", r0, c0), hipErrorInvalidValue;
               uint8_t& sd = stored[(size_t)((r0 * bv + c0) * (P / 4) + pq)];
               if (!sd)  // a repeated last column stores the same value again

@@ -3,10 +3,12 @@
 // serves as the tail of longer dense schedules ending in (16, 16) on both
 // sides, after stage passes have applied the earlier stages.
 //
-//  pass A: the stride-256 stages U_0 and V_0.  Rows r0*256 + q (r0 < 16) and
-//          columns c0*256 + p (c0 < bV) of one (q, p) pair form a 16 x bV
-//          matrix X_qp; the pass computes B^U0_q X_qp (B^V0_p)^T for every
-//          (q, p) and writes the float32 intermediate.  Its products run on
+//  pass A: the first stages U_0 and V_0.  Rows r0*S_U + q (r0 < bU, S_U =
+//          256) and columns c0*S_V + p (c0 < bV, S_V the stride of V_0) of
+//          one (q, p) pair form a bU x bV matrix X_qp; the pass computes
+//          B^U0_q X_qp (B^V0_p)^T for every (q, p) and writes the float32
+//          intermediate.  bU is 16 or 32; V may have stages between V_0 and
+//          its last two (stage passes apply them in between).  Its products run on
 //          f16 MFMA too: the slab of a q is scaled by a power of two that
 //          puts its largest magnitude in [2^11, 2^12); 16-bit inputs are then
 //          f16 values (hi) and float32 inputs split into hi and lo; V_0's
@@ -62,10 +64,12 @@ struct FusedAArgs {
   int64_t m, n;
   int bv;             // radix of V_0 (columns)
   int nb;             // 16-blocks spanned by bv
+  int ru;             // radix of U_0 (rows): 16 or 32
+  int su, sv;         // strides of U_0 (256) and V_0 (d_V / bv)
   int nchunk;         // n / d_V (block-diagonal right side)
-  int dv;             // d_V = bv * 256
-  // U_0 blocks split into f16 (bh, bl) entries as pass B's (fb_hentry),
-  // signs folded in; halves between groups (0 = one shared block)
+  int dv;             // d_V = bv * sv
+  // U_0 blocks split into f16 (bh, bl) entries (fa_uhentry), signs folded
+  // in; halves between groups (0 = one shared block)
   const uint16_t* u0;
   int64_t u0_gs;
   int u0_exact;       // every U_0 entry exact in f16
@@ -73,7 +77,6 @@ struct FusedAArgs {
   // zero-padded to 16 nb, signs folded in
   const uint16_t* v0;
   int64_t v0_gs;
-  uint32_t bv_magic;  // floor(2^32 / bv) + 1: i / bv = (i * bv_magic) >> 32 for the i used
   int64_t u0_n, v0_n; // extents of the block arrays in halves (host checks)
 };
 
@@ -104,10 +107,10 @@ struct FusedBArgs {
 //
 // A workgroup owns P = 8 * ppw consecutive p (ppw per wave) of one column
 // chunk and kFaQC consecutive q.  For each q it stages the input slab
-// X[r0 < 16][c0 < bv][P] through LDS (runs of P input elements, at least 64
+// X[r0 < ru][c0 < bv][P] through LDS (runs of P input elements, at least 64
 // bytes), each wave contracts c0 with the V_0 blocks of its own ppw p held in
-// registers, then r0 with the U_0 block of q, and the results leave through a
-// second LDS area as runs of P floats.
+// registers (ru / 16 row tiles), then r0 with the U_0 block of q, and the
+// results leave through a second LDS area as runs of P floats.
 //
 // V_0 as MFMA steps: chunk ch of 16 columns c0 is one K = 32 product, lane
 // (lr, lg) holding x[r0 = lr][c0 = 16 ch + 4 lg + i] (i < 4) as (hi, hi) and
@@ -133,27 +136,29 @@ __host__ __device__ constexpr int fa_nb_of_steps(int st) { return (st + 3) / 4; 
 // columns c0 per wave instruction (lpr lanes per run of P elements: ipr for
 // loads, P / 4 for stores): lane l holds part l % lpr of column
 // cb * (64 / lpr) + l / lpr.  Instruction k of wave w is slot j = w + 8 k:
-// row (j % 16), column block cb = j / 16.  Columns past the radix repeat the
+// row (j % ru), column block cb = j / ru.  Columns past the radix repeat the
 // last one, so every wave issues the same fixed number of instructions.
 __host__ __device__ constexpr int fa_ncb(int runs_per_inst, int st) {
   return (4 * st + runs_per_inst - 1) / runs_per_inst;
 }
-__host__ __device__ constexpr int fa_ki(int wt, int st) {
-  return 2 * fa_ncb(64 / fa_ipr(wt, fa_nb_of_steps(st)), st);
+__host__ __device__ constexpr int fa_ki(int wt, int st, int ru) {
+  return ru / 8 * fa_ncb(64 / fa_ipr(wt, fa_nb_of_steps(st)), st);
 }
-// Output stores of one 16-column tile nt: 16 rows x 16 columns of P / 4
+// Output stores of one 16-column tile nt: ru rows x 16 columns of P / 4
 // float4s, lpr = P / 4 lanes per run, as kq_nt instructions per wave.
-__host__ __device__ constexpr int fa_kq_nt(int wt, int st) { return fa_p(wt, fa_nb_of_steps(st)) / 8; }
+__host__ __device__ constexpr int fa_kq_nt(int wt, int st, int ru) {
+  return ru * fa_p(wt, fa_nb_of_steps(st)) / 128;
+}
 struct FaSlot {
   int r0, c0;
 };
 // c_first: first column of the range (0 for slab loads, 16 nt for the
 // stores of output tile nt).
-__host__ __device__ inline FaSlot fa_slot(int lpr, int w, int k, int lane, int bv, int c_first) {
+__host__ __device__ inline FaSlot fa_slot(int lpr, int w, int k, int lane, int bv, int c_first, int ru) {
   const int j = w + 8 * k;
   FaSlot x;
-  x.r0 = j % 16;
-  const int c0 = c_first + (j / 16) * (64 / lpr) + lane / lpr;
+  x.r0 = j % ru;
+  const int c0 = c_first + (j / ru) * (64 / lpr) + lane / lpr;
   x.c0 = c0 < bv ? c0 : bv - 1;
   return x;
 }
@@ -164,15 +169,15 @@ struct FaGeom {
   int rsb;         // slab: bytes between runs (c0), P*esz + 8
   int rowb;        // slab: bytes between r0 rows; rowb / 8 odd
   int rowo;        // output area: floats between r0 rows; rowo / 4 odd
-  int slab_bytes;  // 16 * rowb, rounded up to 16
-  int out_floats;  // 16 * rowo
-  int items;       // 16-byte input items per q: 16 * bv * ipr
-  int quads;       // float4 outputs per q: 16 * bv * P / 4
+  int slab_bytes;  // ru * rowb, rounded up to 16
+  int out_floats;  // ru * rowo
+  int items;       // 16-byte input items per q: ru * bv * ipr
+  int quads;       // float4 outputs per q: ru * bv * P / 4
 };
 
 // The pads make the 16 lanes of a row group (16 different r0, same c0) hit
 // distinct LDS banks on the 8-byte slab reads and the 16-byte output writes.
-__host__ __device__ inline FaGeom fa_geom(int wt, int nb, int bv) {
+__host__ __device__ inline FaGeom fa_geom(int wt, int nb, int bv, int ru) {
   FaGeom g;
   g.ppw = fa_ppw(wt, nb);
   g.esz = fa_esz(wt);
@@ -183,10 +188,10 @@ __host__ __device__ inline FaGeom fa_geom(int wt, int nb, int bv) {
   if (((g.rowb / 8) & 1) == 0) g.rowb += 8;
   g.rowo = bv * g.P;
   if (((g.rowo / 4) & 1) == 0) g.rowo += 4;
-  g.slab_bytes = (16 * g.rowb + 15) / 16 * 16;
-  g.out_floats = 16 * g.rowo;
-  g.items = 16 * bv * g.ipr;
-  g.quads = 16 * bv * g.P / 4;
+  g.slab_bytes = (ru * g.rowb + 15) / 16 * 16;
+  g.out_floats = ru * g.rowo;
+  g.items = ru * bv * g.ipr;
+  g.quads = ru * bv * g.P / 4;
   g.max_off = g.slab_bytes + g.out_floats * (int)sizeof(float);
   return g;
 }
@@ -208,7 +213,7 @@ struct FaTile {
 };
 
 __host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
-  return (int64_t)(256 / fa_p(a.wt, a.nb)) * (256 / kFaQC) * a.nchunk;
+  return (int64_t)(a.sv / fa_p(a.wt, a.nb)) * (a.su / kFaQC) * a.nchunk;
 }
 
 __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_t nwg) {
@@ -216,16 +221,11 @@ __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_
   const int64_t per_xcd = nwg / 8;
   const int64_t lin = (b % 8) * per_xcd + b / 8;
   FaTile t;
-  t.p0 = (int)(lin % (256 / P)) * P;
-  const int64_t rest = lin / (256 / P);
-  t.q0 = (int)(rest % (256 / kFaQC)) * kFaQC;
-  t.chunk = (int)(rest / (256 / kFaQC));
+  t.p0 = (int)(lin % (a.sv / P)) * P;
+  const int64_t rest = lin / (a.sv / P);
+  t.q0 = (int)(rest % (a.su / kFaQC)) * kFaQC;
+  t.chunk = (int)(rest / (a.su / kFaQC));
   return t;
-}
-
-// i / bv without a division instruction (exact for the ranges the host checks).
-__host__ __device__ inline int fa_div_bv(const FusedAArgs& a, int i) {
-  return (int)(((uint64_t)(uint32_t)i * a.bv_magic) >> 32);
 }
 
 // Byte offset of input item (r0, c0, o) in the slab (8-byte aligned).
@@ -241,10 +241,13 @@ __host__ __device__ inline int fa_out(const FaGeom& g, int r0, int c0, int pl) {
   return r0 * g.rowo + c0 * g.P + pl;
 }
 // Global element (row, col) of (r0, q) x (chunk, c0, p).
-__host__ __device__ inline int64_t fa_row(int r0, int q) { return (int64_t)r0 * 256 + q; }
+__host__ __device__ inline int64_t fa_row(const FusedAArgs& a, int r0, int q) { return (int64_t)r0 * a.su + q; }
 __host__ __device__ inline int64_t fa_col(const FusedAArgs& a, int chunk, int c0, int p) {
-  return (int64_t)chunk * a.dv + (int64_t)c0 * 256 + p;
+  return (int64_t)chunk * a.dv + (int64_t)c0 * a.sv + p;
 }
+// Halves offset of the U_0 entry (row j, quad q) within a ru x ru block
+// (2 ru^2 halves): (bh, bl) of U[j][4 q .. 4 q + 3].
+__host__ __device__ constexpr int fa_uhentry(int ru, int j, int q) { return (j * (ru / 4) + q) * 8; }
 // Halves offset of the fragment-order V_0 entry (nt, lr, lg, ch) within a
 // group (512 nb^2 halves): the nb chunks of one (nt, lane) are contiguous.
 __host__ __device__ inline int64_t fa_vhentry(int nb, int nt, int lr, int lg, int ch) {

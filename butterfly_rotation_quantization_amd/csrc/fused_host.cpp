@@ -6,6 +6,7 @@
 #include <vector>
 
 #include "fused.h"
+#include "stage.h"
 
 namespace brq {
 
@@ -14,19 +15,28 @@ void prof_end(int token, hipStream_t s);
 
 namespace {
 
-// Radix of stage 0 when the plan fits the fast path as (b0, 16, 16), else 0.
-// A Hadamard plan of any power-of-two radix schedule is the Sylvester matrix
-// H_d / sqrt(d) = (H_b0 / sqrt(b0)) x (H_16 / 4) x (H_16 / 4) in natural order,
-// so for d = 256 b0 it is taken as that three-stage schedule.
+// Radix of stage 0 when the plan fits pass A and pass B, else 0: stage 0 of
+// radix at most 64, then any stages (stage passes apply them between the two
+// passes), then two of radix 16.  A Hadamard plan of any power-of-two radix
+// schedule is the Sylvester matrix H_d / sqrt(d) = (H_b0 / sqrt(b0)) x
+// (H_16 / 4) x (H_16 / 4) in natural order, so for d = 256 b0 it is taken as
+// that three-stage schedule.
 int fused_b0(const Plan& p) {
   if (p.mode == BRQ_HADAMARD) {
     const int b0 = p.d / 256;
     return p.d % 256 == 0 && b0 >= 2 && b0 <= 64 && (b0 & (b0 - 1)) == 0 ? b0 : 0;
   }
-  const bool fits = p.nst == 3 && p.radix[1] == 16 && p.radix[2] == 16 && p.radix[0] >= 2 &&
-                    p.radix[0] <= 64;
+  const bool fits = p.nst >= 3 && p.radix[p.nst - 2] == 16 && p.radix[p.nst - 1] == 16 &&
+                    p.radix[0] >= 2 && p.radix[0] <= 64 && p.stride[0] % 256 == 0;
   return fits ? p.radix[0] : 0;
 }
+
+// Stride of that stage 0.
+int fused_s0(const Plan& p) { return p.mode == BRQ_HADAMARD ? 256 : p.stride[0]; }
+
+// Stages between stage 0 and the last two (none for Hadamard plans, which
+// run as (b0, 16, 16)).
+int mid_stages(const Plan& p) { return p.mode == BRQ_HADAMARD ? 0 : p.nst - 3; }
 
 // Sylvester Hadamard block H_b / sqrt(b), row-major, H[j][k] = (-1)^popcount(j & k).
 void hadamard_block(int b, float* out) {
@@ -103,7 +113,7 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
   if (!b0 || !p.fzh) return hipSuccess;
   const int nb = (b0 + 15) / 16;
   const int np = 16 * nb;
-  const int S0 = 256;  // stride of stage 0 in the (b0, 16, 16) schedule
+  const int S0 = fused_s0(p);
   const bool shared_src = p.mode != BRQ_PER_GROUP;
   const bool per_group = !shared_src || host_signs;
   const int ng0 = per_group ? S0 : 1;
@@ -147,14 +157,15 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
             for (int i = 0; i < 4; ++i)
               split(pad[((size_t)g * np + 16 * nt + lr) * np + 16 * ch + 4 * lg + i], e + i, e + 4 + i);
           }
-  // U_0 order (radix 16 only): entry (j, q) holds U[j][4 q + i]
+  // U_0 order (radix 16 or 32 only): entry (j, q) holds U[j][4 q + i]
   std::vector<uint16_t> u0;
-  if (np == 16) {
-    u0.resize((size_t)ng0 * kFbBlockHalves);
+  const int64_t gu = 2 * (int64_t)b0 * b0;  // halves per U_0 block
+  if (b0 == 16 || b0 == 32) {
+    u0.resize((size_t)(ng0 * gu));
     for (int g = 0; g < ng0; ++g)
-      for (int j = 0; j < 16; ++j)
-        for (int k = 0; k < 16; ++k) {
-          uint16_t* e = u0.data() + (size_t)g * kFbBlockHalves + fb_hentry(j, k / 4);
+      for (int j = 0; j < b0; ++j)
+        for (int k = 0; k < b0; ++k) {
+          uint16_t* e = u0.data() + g * gu + fa_uhentry(b0, j, k / 4);
           split(pad[((size_t)g * np + j) * np + k], e + k % 4, e + 4 + k % 4);
         }
   }
@@ -166,9 +177,10 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
   }
   if (e != hipSuccess) return e;
   p.fz_b0 = b0;
+  p.fz_s0 = S0;
   p.fz_nb = nb;
   p.fz_gs0v = per_group ? gv : 0;
-  p.fz_gs0u = per_group ? kFbBlockHalves : 0;
+  p.fz_gs0u = per_group ? gu : 0;
   p.fz_n0v = (int64_t)v0.size();
   p.fz_n0u = (int64_t)u0.size();
   p.fz0_exact = exact ? 1 : 0;
@@ -196,24 +208,26 @@ const char* check_b(const FusedBArgs& b);
 // Host check of what the two kernels' index arithmetic relies on.
 const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (a.bv < 2 || a.bv > 64 || a.nb != (a.bv + 15) / 16) return "V_0 radix";
-  if (a.m != 4096 || a.dv != a.bv * 256 || (int64_t)a.nchunk * a.dv != a.n) return "shape";
+  if ((a.ru != 16 && a.ru != 32) || (a.ru == 32 && a.nb > 2)) return "U_0 radix";
+  const int P = fa_p(a.wt, a.nb);
+  if (a.su % kFaQC || a.sv % P || (int64_t)a.ru * a.su != a.m || a.dv != a.bv * a.sv ||
+      (int64_t)a.nchunk * a.dv != a.n)
+    return "shape";
   if (fa_nwg(a) % 8) return "pass A grid";
-  for (int i = 0; i < 16 * a.bv; ++i)  // the multiply-shift quotient is exact where used
-    if (fa_div_bv(a, i) != i / a.bv) return "division multiplier";
-  if (fa_lds_bytes(fa_geom(a.wt, a.nb, a.bv)) > 160 * 1024) return "pass A LDS";
+  if (fa_lds_bytes(fa_geom(a.wt, a.nb, a.bv, a.ru)) > 160 * 1024) return "pass A LDS";
   // pass A addresses a lane's input and output as 32-bit byte offsets from a
   // per-chunk base
   if ((int64_t)a.m * a.ldw * fa_esz(a.wt) >= (int64_t(1) << 31) ||
       (int64_t)a.m * a.n * 4 >= (int64_t(1) << 31))
     return "32-bit offsets";
   if (!a.w || !a.ws || !a.u0 || !a.v0) return "pass A pointers";
-  if (a.u0_n < (a.u0_gs ? 256 * a.u0_gs : kFbBlockHalves)) return "U_0 extent";
-  if (a.v0_n < (a.v0_gs ? 256 * a.v0_gs : (int64_t)kFbBlockHalves * a.nb * a.nb)) return "V_0 extent";
-  if ((a.u0_gs && a.u0_gs < kFbBlockHalves) || (a.v0_gs && a.v0_gs < (int64_t)kFbBlockHalves * a.nb * a.nb) ||
+  const int64_t gu = 2 * (int64_t)a.ru * a.ru;
+  if (a.u0_n < (a.u0_gs ? a.su * a.u0_gs : gu)) return "U_0 extent";
+  if (a.v0_n < (a.v0_gs ? a.sv * a.v0_gs : (int64_t)kFbBlockHalves * a.nb * a.nb)) return "V_0 extent";
+  if ((a.u0_gs && a.u0_gs < gu) || (a.v0_gs && a.v0_gs < (int64_t)kFbBlockHalves * a.nb * a.nb) ||
       a.u0_gs % 8 || a.v0_gs % 8)
     return "block strides";
-  if (b.bv != a.bv || b.nchunk != a.nchunk || b.dv != a.dv || b.m != a.m || b.n != a.n)
-    return "pass B shape";
+  if (b.m != a.m || b.n != a.n) return "pass B shape";
   return check_b(b);
 }
 
@@ -292,11 +306,15 @@ hipError_t fused_rotate(const Plan*, const Plan*, const void*, int, int64_t, voi
 bool fused_rqp_supported(const Plan* U, const Plan* V, int wt, int64_t m, int64_t n, int64_t ldw,
                          const void* w, const brq_quant* q) {
   if (!U || !V || !U->fz_ok || !V->fz_ok || !U->fzh || !V->fzh) return false;
-  if (U->fz_b0 != 16 || U->d != m || n % V->d) return false;
+  if ((U->fz_b0 != 16 && U->fz_b0 != 32) || U->d != m || n % V->d) return false;
+  if (U->fz_b0 == 32 && V->fz_nb > 2) return false;
   if (q->group != 64 && q->group != 128) return false;
   if ((n * q->bits) % 32) return false;
   const int elem = wt == BRQ_F32 ? 4 : 2;
   if ((ldw * elem) % 16 || reinterpret_cast<uintptr_t>(w) % 16) return false;
+  // stages between stage 0 and the last two run as stage passes in place
+  if ((mid_stages(*U) && !sp_shape_ok(U, 1, m, n)) || (mid_stages(*V) && !sp_shape_ok(V, 0, m, n)))
+    return false;
   return true;
 }
 
@@ -318,6 +336,9 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.n = n;
   a.bv = V->fz_b0;
   a.nb = V->fz_nb;
+  a.ru = U->fz_b0;
+  a.su = U->fz_s0;
+  a.sv = V->fz_s0;
   a.dv = V->d;
   a.nchunk = (int)(n / V->d);
   a.u0 = U->fz0u;
@@ -325,7 +346,6 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.u0_exact = U->fz0_exact;
   a.v0 = V->fz0v;
   a.v0_gs = V->fz_gs0v;
-  a.bv_magic = (uint32_t)((1ull << 32) / (uint64_t)a.bv + 1);
 
   FusedBArgs b;
   std::memset(&b, 0, sizeof b);
@@ -333,7 +353,7 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   b.m = m;
   b.n = n;
   b.nrb = (int)(m / 256);
-  b.bv = a.bv;
+  b.bv = V->d / 256;
   b.nchunk = a.nchunk;
   b.dv = a.dv;
   set_split_blocks(b, U, V);
@@ -345,11 +365,20 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   if (check_fused(a, b)) return BRQ_ERR_UNSUPPORTED;
 
   char name[96];
-  snprintf(name, sizeof name, "fusedA U0(16) V0(%d)", a.bv);
+  snprintf(name, sizeof name, "fusedA U0(%d) V0(%d)", a.ru, a.bv);
   int tok = prof_begin(name, s);
   hipError_t e = launch_fused_a(a, s);
   prof_end(tok, s);
   if (e != hipSuccess) return BRQ_ERR_HIP;
+  // the stages between stage 0 and the last two, in place on the intermediate
+  for (int side = 1; side >= 0; --side) {
+    const Plan* p = side ? U : V;
+    if (!mid_stages(*p)) continue;
+    hipError_t he = hipSuccess;
+    const brq_status st = sp_rotate_stages(p, side, 0, 1, p->nst - 2, ws, BRQ_F32, n, ws, BRQ_F32, n, m, n,
+                                           nullptr, 0, s, &he);
+    if (st != BRQ_OK) return st == BRQ_ERR_HIP ? BRQ_ERR_HIP : BRQ_ERR_UNSUPPORTED;
+  }
   snprintf(name, sizeof name, "fusedB U(16,16) V(16,16) quant b%d g%d", q->bits, q->group);
   tok = prof_begin(name, s);
   e = launch_fused_b(b, fused_b_grid(b), s);

@@ -161,26 +161,29 @@ __device__ __forceinline__ uint32_t fa_items_absmax(const uint4 (&raw)[KI]) {
 // registers while the products run.  Loads and stores take one column c0 per
 // wave instruction, so a lane's address is one loop-invariant register plus
 // wave-uniform terms.
-template <int ST, int WT>
+template <int ST, int WT, int RU>
 __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a) {
   constexpr int NB = fa_nb_of_steps(ST);
+  constexpr int MT = RU / 16;  // row tiles of the slab (r0 = 16 mt + lr)
   constexpr int PPW = fa_ppw(WT, NB);
   constexpr int ESZ = fa_esz(WT);
   constexpr int P = 8 * PPW;
   constexpr int IPR = P * ESZ / 16;
-  constexpr int KI = fa_ki(WT, ST);  // slab load instructions per wave
-  constexpr int KQ = fa_kq_nt(WT, ST);  // output store instructions per wave and 16 columns
+  constexpr int KI = fa_ki(WT, ST, RU);  // slab load instructions per wave
+  constexpr int KQ = fa_kq_nt(WT, ST, RU);  // output store instructions per wave and 16 columns
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int w = tid >> 6;
   const FaTile t = fa_tile(a, blockIdx.x, fa_nwg(a));
   const int bv = a.bv;
-  const FaGeom g = fa_geom(WT, NB, bv);
+  const FaGeom g = fa_geom(WT, NB, bv, RU);
   uint8_t* slab = smem;
   float* outa = reinterpret_cast<float*>(smem + g.slab_bytes);
   uint32_t* smax = reinterpret_cast<uint32_t*>(smem + g.max_off);
   const float m1 = fb_minus_one();
+  const int64_t ru_ld = (int64_t)a.su * a.ldw;  // input elements between rows r0 and r0 + 1
+  const int64_t ru_n = (int64_t)a.su * a.n;     // output elements between rows r0 and r0 + 1
 
   // The per-instruction lane offsets are rebuilt from an opaque copy of the
   // lane index on every use: hoisted out of the q loop they would hold some
@@ -192,13 +195,20 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
     const int ln = opaque(lane);
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
-      const FaSlot x = fa_slot(IPR, w, k, ln, bv, 0);
-      const uint32_t off = (uint32_t)((x.r0 * 256 * a.ldw + x.c0 * 256 + (ln % IPR) * (16 / ESZ)) * ESZ);
+      const FaSlot x = fa_slot(IPR, w, k, ln, bv, 0, RU);
+      const uint32_t off = (uint32_t)((x.r0 * ru_ld + x.c0 * a.sv + (ln % IPR) * (16 / ESZ)) * ESZ);
       raw[k] = *reinterpret_cast<const uint4*>(base + off);
     }
   };
+  // U_0 entries of q: eu[ot][kt] = (bh, bl) of U[16 ot + lr][16 kt + 4 lg + i]
+  u4 eu[MT][MT];
   auto load_u = [&](int q) {
-    return *reinterpret_cast<const u4*>(a.u0 + (int64_t)q * a.u0_gs + fb_hentry(lr, lg));
+#pragma unroll
+    for (int ot = 0; ot < MT; ++ot)
+#pragma unroll
+      for (int kt = 0; kt < MT; ++kt)
+        eu[ot][kt] = *reinterpret_cast<const u4*>(a.u0 + (int64_t)q * a.u0_gs +
+                                                  fa_uhentry(RU, 16 * ot + lr, 4 * kt + lg));
   };
 
   // V_0 entries of this wave's p: vb[j][nt][ch] = (bh, bl) of
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
   }
   int q = t.q0;
   load_slab(q);
-  u4 eu = load_u(q);
+  load_u(q);
   // nothing loaded before the loop is outstanding inside it, so the products
   // never wait on the prefetch of the next slab
   __builtin_amdgcn_s_waitcnt(0);
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
     const int ls = opaque(lane);
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
-      const FaSlot x = fa_slot(IPR, w, k, ls, bv, 0);
+      const FaSlot x = fa_slot(IPR, w, k, ls, bv, 0, RU);
       uint8_t* d = slab + fa_slab_item(g, x.r0, x.c0, ls % IPR);
       *reinterpret_cast<uint2*>(d) = make_uint2(raw[k].x, raw[k].y);
       *reinterpret_cast<uint2*>(d + 8) = make_uint2(raw[k].z, raw[k].w);
@@ -247,46 +257,58 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
       for (int i = 1; i < kFaWaves; ++i) m = smax[i] > m ? smax[i] : m;
       ks = __builtin_amdgcn_readfirstlane(fa_scale_shift(m));
     }
-    const u4 bhh = fb_hh(eu), bll = fb_ll(eu);
+    u4 bhh[MT][MT], bll[MT][MT];
+#pragma unroll
+    for (int ot = 0; ot < MT; ++ot)
+#pragma unroll
+      for (int kt = 0; kt < MT; ++kt) {
+        bhh[ot][kt] = fb_hh(eu[ot][kt]);
+        bll[ot][kt] = fb_ll(eu[ot][kt]);
+      }
     uint8_t* obase = reinterpret_cast<uint8_t*>(a.ws) + ((int64_t)q * a.n + fa_col(a, t.chunk, 0, t.p0)) * 4;
 
-    const uint8_t* arow = slab + fa_slab_read(g, lr, 0, w);
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt) {
       // V_0: D[j][m = r0][n = c0'] = sum_c0 X_j[r0][c0] V_j[c0'][c0], c0' = 16 nt + n,
-      // one K = 32 product per 16 columns c0: (hi, hi) . (bh, bl), and for
-      // float32 input also (lo, lo) . (bh, bl).  The lane's slab values
-      // x[r0 = lr][c0 = 16 ch + 4 lg + i] are read, scaled and split per
-      // output tile (kept for all tiles they would need the registers of the
-      // V_0 entries).
-      f4 d[PPW];
+      // per row tile mt (r0 = 16 mt + m), one K = 32 product per 16 columns
+      // c0: (hi, hi) . (bh, bl), and for float32 input also (lo, lo) . (bh, bl).
+      // The lane's slab values x[r0][c0 = 16 ch + 4 lg + i] are read, scaled
+      // and split per output tile (kept for all tiles they would need the
+      // registers of the V_0 entries).
+      f4 d[PPW][MT];
 #pragma unroll
-      for (int j = 0; j < PPW; ++j) d[j] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < PPW; ++j)
 #pragma unroll
-      for (int ch = 0; ch < NB; ++ch) {
-        float xv[4][PPW];
+        for (int mt = 0; mt < MT; ++mt) d[j][mt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c0 = 16 * ch + 4 * lg + i;
-          const bool live = ch + 1 < NB || c0 < bv;  // only the last chunk can pass the radix
-          const uint2 rd = fa_aread<WT, PPW>(arow + (live ? c0 : bv - 1) * g.rsb);
-          fa_unpack<WT, PPW>(rd, xv[i]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint8_t* arow = slab + fa_slab_read(g, 16 * mt + lr, 0, w);
 #pragma unroll
-          for (int j = 0; j < PPW; ++j) xv[i][j] = live ? __builtin_ldexpf(xv[i][j], ks) : 0.f;
-        }
+        for (int ch = 0; ch < NB; ++ch) {
+          float xv[4][PPW];
 #pragma unroll
-        for (int j = 0; j < PPW; ++j) {
-          const f4 xs = {xv[0][j], xv[1][j], xv[2][j], xv[3][j]};
-          const h4 hi = __builtin_convertvector(xs, h4);
-          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(hi, hi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                        __builtin_bit_cast(h8, vb[j][nt][ch]), d[j], 0, 0, 0);
-          if constexpr (WT == BRQ_F32) {
-            f4 r;
+          for (int i = 0; i < 4; ++i) {
+            const int c0 = 16 * ch + 4 * lg + i;
+            const bool live = ch + 1 < NB || c0 < bv;  // only the last chunk can pass the radix
+            const uint2 rd = fa_aread<WT, PPW>(arow + (live ? c0 : bv - 1) * g.rsb);
+            fa_unpack<WT, PPW>(rd, xv[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, xs[i]);
-            const h4 lo = __builtin_convertvector(r, h4);
-            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(lo, lo, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                          __builtin_bit_cast(h8, vb[j][nt][ch]), d[j], 0, 0, 0);
+            for (int j = 0; j < PPW; ++j) xv[i][j] = live ? __builtin_ldexpf(xv[i][j], ks) : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < PPW; ++j) {
+            const f4 xs = {xv[0][j], xv[1][j], xv[2][j], xv[3][j]};
+            const h4 hi = __builtin_convertvector(xs, h4);
+            d[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(hi, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                              __builtin_bit_cast(h8, vb[j][nt][ch]), d[j][mt], 0, 0, 0);
+            if constexpr (WT == BRQ_F32) {
+              f4 r;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, xs[i]);
+              const h4 lo = __builtin_convertvector(r, h4);
+              d[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(lo, lo, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                                __builtin_bit_cast(h8, vb[j][nt][ch]), d[j][mt], 0, 0, 0);
+            }
           }
         }
       }
@@ -294,29 +316,53 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
       // the last V_0 products they no longer hold up the MFMA phase
       if (nt == NB - 1 && qi + 1 < kFaQC) {
         load_slab(q + 1);
-        eu = load_u(q + 1);
+        load_u(q + 1);
       }
-      // U_0 on the transpose: E[j][m = c0'][n = r0'] = sum_r0 U[r0'][r0] D[j][r0][c0']
-      f4 e[PPW];
+      // U_0 on the transpose: E[j][m = c0'][n = r0'] = sum_r0 U[r0'][r0] D[j][r0][c0'],
+      // r0' = 16 ot + n; each row tile kt of D is split once into (hi, lo)
+      f4 e[PPW][MT];
 #pragma unroll
       for (int j = 0; j < PPW; ++j) {
-        e[j] = a.u0_exact ? fb_prod<true>(d[j], bhh, bll, m1) : fb_prod<false>(d[j], bhh, bll, m1);
+        h8 ad[MT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[j][i] = __builtin_ldexpf(e[j][i], -ks);
-      }
+        for (int kt = 0; kt < MT; ++kt) {
+          const h4 hi = __builtin_convertvector(d[j][kt], h4);
+          f4 r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c0 = 16 * nt + 4 * lg + i;
-        if (c0 < bv) {
-          float* o = outa + fa_out(g, lr, c0, PPW * w);
-          if constexpr (PPW == 4)
-            *reinterpret_cast<f4*>(o) = f4{e[0][i], e[1][i], e[2][i], e[3][i]};
-          else if constexpr (PPW == 2)
-            *reinterpret_cast<float2*>(o) = make_float2(e[0][i], e[1][i]);
-          else
-            *o = e[0][i];
+          for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf((float)hi[i], m1, d[j][kt][i]);
+          ad[kt] = __builtin_shufflevector(hi, __builtin_convertvector(r, h4), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int ot = 0; ot < MT; ++ot) {
+          e[j][ot] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kt = 0; kt < MT; ++kt) {
+            e[j][ot] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ad[kt], __builtin_bit_cast(h8, bhh[ot][kt]), e[j][ot],
+                                                              0, 0, 0);
+            if (!a.u0_exact)
+              e[j][ot] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ad[kt], __builtin_bit_cast(h8, bll[ot][kt]),
+                                                                e[j][ot], 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[j][ot][i] = __builtin_ldexpf(e[j][ot][i], -ks);
         }
       }
+      // e[j][ot][i]: element (c0' = 16 nt + 4 lg + i, r0' = 16 ot + lr) of p j
+#pragma unroll
+      for (int ot = 0; ot < MT; ++ot)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c0 = 16 * nt + 4 * lg + i;
+          if (c0 < bv) {
+            float* o = outa + fa_out(g, 16 * ot + lr, c0, PPW * w);
+            if constexpr (PPW == 4)
+              *reinterpret_cast<f4*>(o) = f4{e[0][ot][i], e[1][ot][i], e[2][ot][i], e[3][ot][i]};
+            else if constexpr (PPW == 2)
+              *reinterpret_cast<float2*>(o) = make_float2(e[0][ot][i], e[1][ot][i]);
+            else
+              *o = e[0][ot][i];
+          }
+        }
     }
     __syncthreads();  // output area complete; the slab may be overwritten
 
@@ -325,10 +371,10 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
     for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
       for (int k = 0; k < KQ; ++k) {
-        const FaSlot x = fa_slot(P / 4, w, k, lo, bv, 16 * nt);
+        const FaSlot x = fa_slot(P / 4, w, k, lo, bv, 16 * nt, RU);
         const int pq = lo % (P / 4);
         const f4 v = ld4(outa + fa_out(g, x.r0, x.c0, 4 * pq));
-        *reinterpret_cast<f4*>(obase + (uint32_t)((x.r0 * 256 * a.n + x.c0 * 256 + 4 * pq) * 4)) = v;
+        *reinterpret_cast<f4*>(obase + (uint32_t)((x.r0 * ru_n + x.c0 * a.sv + 4 * pq) * 4)) = v;
       }
   }
 }
@@ -603,31 +649,41 @@ __global__ __launch_bounds__(kFbWaves * 64) void fused_b_kernel(FusedBArgs a) {
   }
 }
 
-template <int ST, int WT>
+template <int ST, int WT, int RU>
 hipError_t launch_a_t(const FusedAArgs& a, hipStream_t s) {
   static bool attr = false;  // output areas above 64 KiB of LDS need the opt-in
   if (!attr) {
     int most = 0;
     for (int bv = 4 * ST - 3; bv <= 4 * ST; ++bv) {
-      const int b = fa_lds_bytes(fa_geom(WT, fa_nb_of_steps(ST), bv));
+      const int b = fa_lds_bytes(fa_geom(WT, fa_nb_of_steps(ST), bv, RU));
       most = b > most ? b : most;
     }
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_a_kernel<ST, WT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_a_kernel<ST, WT, RU>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, most);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const size_t lds = (size_t)fa_lds_bytes(fa_geom(WT, a.nb, a.bv));
-  hipLaunchKernelGGL((fused_a_kernel<ST, WT>), dim3((unsigned)fa_nwg(a)), dim3(kFaWaves * 64), lds,
+  const size_t lds = (size_t)fa_lds_bytes(fa_geom(WT, a.nb, a.bv, RU));
+  hipLaunchKernelGGL((fused_a_kernel<ST, WT, RU>), dim3((unsigned)fa_nwg(a)), dim3(kFaWaves * 64), lds,
                      s, a);
   return hipGetLastError();
 }
 
+template <int ST, int RU>
+hipError_t launch_a_wt(const FusedAArgs& a, hipStream_t s) {
+  if (a.wt == BRQ_F32) return launch_a_t<ST, BRQ_F32, RU>(a, s);
+  if (a.wt == BRQ_BF16) return launch_a_t<ST, BRQ_BF16, RU>(a, s);
+  return launch_a_t<ST, BRQ_F16, RU>(a, s);
+}
+
+// U_0 of radix 32 is built for V_0 radices up to 32 (two column chunks).
 template <int ST>
 hipError_t launch_a_st(const FusedAArgs& a, hipStream_t s) {
-  if (a.wt == BRQ_F32) return launch_a_t<ST, BRQ_F32>(a, s);
-  if (a.wt == BRQ_BF16) return launch_a_t<ST, BRQ_BF16>(a, s);
-  return launch_a_t<ST, BRQ_F16>(a, s);
+  if (a.ru == 16) return launch_a_wt<ST, 16>(a, s);
+  if constexpr (ST <= 8) {
+    if (a.ru == 32) return launch_a_wt<ST, 32>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int... STs>

@@ -102,3 +102,45 @@ def test_fused_deterministic_and_matches_generic():
         assert diff.mean() < 1e-5, (route, diff.sum())
         rel = (s1 - s3).abs().max().item() / s1.abs().max().item()
         assert rel < 1e-5, (route, rel)
+
+
+LONGER = [
+    ((32, 16, 16), (7, 16, 16), 3, 128, "bf16"),
+    ((32, 16, 16), (3, 2, 16, 16), 4, 64, "f16"),
+    ((16, 2, 16, 16), (16, 16, 16), 2, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("uradix,vradix,bits,group,dt", LONGER)
+def test_fused_longer_schedules(uradix, vradix, bits, group, dt):
+    """Stage 0 of radix 32 on the left, stages between stage 0 and the last
+    two (run as stage passes between pass A and pass B): sampled rows against
+    the oracle."""
+    import butterfly_rotation_quantization_amd as brq
+    announce(f"fused longer {uradix} x {vradix} b{bits} g{group} {dt}")
+    rng = np.random.default_rng(7 + bits)
+    left = S.random_plan(rng, uradix, "per_group")
+    right = S.random_plan(rng, vradix, "per_group")
+    m, n = left.d, right.d
+    x = 0.02 * rng.standard_t(3, size=(m, n))
+    x[:, rng.choice(n, size=max(1, n // 200), replace=False)] *= 30.0
+    ws = S.to_storage(x, dt)
+    w = to_dev(ws, dt)
+    U, V = lib_plan(left), lib_plan(right)
+    brq.profile_reset()
+    brq.profile_enable(True)
+    codes, scales = brq.rotate_quantize_pack(U, V, w, bits, group)
+    brq.profile_enable(False)
+    names = list(brq.profile_read())
+    assert names[0].startswith("fusedA") and names[-1].startswith("fusedB"), names
+    assert len(names) == 2 + (len(uradix) - 3) + (len(vradix) - 3), names
+    Uo, Vo = orc_plan(left), orc_plan(right)
+    rows = np.sort(rng.choice(m, size=96, replace=False))
+    y = T.left_rows(Uo, rows) @ S.storage_to_f64(ws, dt)
+    y = T.apply_right(Vo, y, method="factored")
+    got = Q.unpack(codes.cpu().numpy()[rows], bits, n)
+    ref, _ = Q.absmax_quantize(y, bits, group)
+    band = Q.absmax_band(y, bits, group)
+    check_absmax_scales(scales.cpu().numpy()[rows], Q.absmax_scales(y, group), y, "fused longer")
+    info = check_codes(got, ref, band, "fused longer", bits)
+    print(info, flush=True)

@@ -164,6 +164,29 @@ def test_fused_two_sided_launches(dl, bv, mode, chunks, bits, group, wt):
     assert dl.brq_dryrun_launches() == 2
 
 
+@pytest.mark.parametrize("uradix,vradix,m,n,bits,group,wt", [
+    ((32, 16, 16), (7, 16, 16, 16), 8192, 28672, 2, 64, 1),   # the 70B weight
+    ((32, 16, 16), (7, 16, 16), 8192, 1792, 3, 128, 0),
+    ((32, 16, 16), (3, 2, 16, 16), 8192, 3072, 4, 128, 2),
+    ((16, 2, 16, 16), (16, 16, 16), 8192, 4096, 3, 64, 1),
+])
+def test_fused_longer_schedules_launches(dl, uradix, vradix, m, n, bits, group, wt):
+    """Stage 0 of radix 16 or 32 on the left and up to 64 on the right at any
+    stride, stages between stage 0 and the last two as stage passes in place,
+    then pass B: every index of the passes stays in bounds and every output
+    element is written once."""
+    rng = np.random.default_rng(m + n)
+    u = DPlan(dl, S.random_plan(rng, uradix, "per_group"))
+    v = DPlan(dl, S.random_plan(rng, vradix, "per_group"))
+    q = brq.make_quant(bits, group)
+    ws = dl.brq_workspace_bytes(u.h, v.h, m, n)
+    dl.brq_dryrun_reset()
+    st = dl.brq_rotate_quantize_pack(u.h, v.h, X, wt, m, n, n, ctypes.byref(q), CODES, SCALES,
+                                     WS, ws, None)
+    _ok(dl, st, f"fused {uradix} x {vradix}")
+    assert dl.brq_dryrun_launches() == 2 + (len(uradix) - 3) + (len(vradix) - 3)
+
+
 # The row Hadamard path: one launch per call, for every chunk length it
 # takes, with partial last workgroups, every dtype pair and group size.
 @pytest.mark.parametrize("l2d,rows,cpr", [(4, 33, 2), (5, 129, 3), (7, 50, 4), (8, 17, 2),
