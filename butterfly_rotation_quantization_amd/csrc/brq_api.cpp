@@ -701,6 +701,12 @@ brq_status brq_plan_create(brq_plan** out, int32_t d, int32_t n_stages, const in
     for (int i = 0; i < d; ++i) sf[i] = (float)signs[i];
     e = rt_malloc((void**)&p.signs, d * sizeof(float));
     if (e == hipSuccess) e = rt_copy_to_device(p.signs, sf.data(), d * sizeof(float));
+    if (e == hipSuccess && mode == BRQ_HADAMARD) {
+      const float sc = 1.0f / std::sqrt((float)d);
+      for (int i = 0; i < d; ++i) sf[i] *= sc;
+      e = rt_malloc((void**)&p.signs_s, d * sizeof(float));
+      if (e == hipSuccess) e = rt_copy_to_device(p.signs_s, sf.data(), d * sizeof(float));
+    }
   }
   if (signs) h->signs.assign(signs, signs + d);
   if (e == hipSuccess) e = fused_prepare(p, blocks, signs);
@@ -1040,6 +1046,7 @@ brq_status brq_plan_destroy(brq_plan* plan) {
   rt_free(p.blk);
   rt_free(p.blkT);
   rt_free(p.signs);
+  rt_free(p.signs_s);
   fused_release(p);
   delete plan;
   return BRQ_OK;

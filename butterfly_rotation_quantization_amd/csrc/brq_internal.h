@@ -25,6 +25,7 @@ struct Plan {
   float* blk = nullptr;              // blocks as given, [group][j][k] (or [j][k] shared)
   float* blkT = nullptr;             // the same blocks transposed, for the inverse
   float* signs = nullptr;            // +-1 as float, or nullptr
+  float* signs_s = nullptr;          // Hadamard plans: the signs times 1 / sqrt(d)
   // Fast-path data (fused_prepare), for plans whose stage 0 has radix
   // <= 64 and whose last two stages are radix 16 (Hadamard plans as
   // (d / 256, 16, 16)): stage-0 blocks with the signs folded in, zero-padded

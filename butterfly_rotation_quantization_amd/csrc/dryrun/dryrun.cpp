@@ -576,7 +576,7 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
       if (b <= prev || b >= kRhBins - 1)
         return violation("codebook threshold %lld in bin %lld", k, b), hipErrorInvalidValue;
       if (a.tbin[k] != b) return violation("threshold %lld recorded in bin %lld", k, a.tbin[k]), hipErrorInvalidValue;
-      if (a.bintab[b].x != a.tau[k] || (int)a.bintab[b].y != k)
+      if (a.bintab[b].x != std::fma(a.tau[k], a.bin_s, a.bin_off) || (int)a.bintab[b].y != k)
         return violation("bin table entry %lld (threshold %lld)", b, k), hipErrorInvalidValue;
       prev = b;
     }

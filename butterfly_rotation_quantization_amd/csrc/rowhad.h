@@ -43,6 +43,7 @@ struct RhArgs {
   int yt;
   int64_t ldy;
   const float* signs; // d signs (+-1) of the plan, or null
+  const float* signs_s;  // the same times scale (with signs)
   int inverse;        // apply M^T: signs after the transform instead of before
   int identity;       // no transform (quantize only): d = 16, no signs, scale 1
   float scale;        // 1 / sqrt(d)
@@ -59,8 +60,9 @@ struct RhArgs {
   // when no such scaling exists.
   float bin_s, bin_off;
   int tbin[kMaxLevels];
-  // The bin table itself, built on the host: bin b holds {its threshold or
-  // +inf, the number of thresholds in lower bins}.
+  // The bin table itself, built on the host: bin b holds {its threshold's u
+  // (fma(tau, bin_s, bin_off)) or +inf, the number of thresholds in lower
+  // bins}; the kernel compares u = fma(v, k bin_s, bin_off) against it.
   float2 bintab[kRhBins];
   uint8_t* codes;
   const uint8_t* in_codes;

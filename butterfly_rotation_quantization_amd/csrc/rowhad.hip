@@ -185,9 +185,9 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   // they are in flight.
   auto build_tables = [&]() {
     if (MODE == RH_QUANT && bins) tab[threadIdx.x] = a.bintab[threadIdx.x];  // built on the host
-    if (DEQ && threadIdx.x <= LV) {
+    if (DEQ && threadIdx.x <= LV) {  // the levels carry the transform's 1 / sqrt(d)
       const int c = threadIdx.x;
-      tab[c].x = a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g;
+      tab[c].x = (a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g) * a.scale;
     }
   };
   float v[16];
@@ -215,9 +215,14 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = scale * tab[c[j]].x;
   }
-  if (!a.inverse && a.signs)
+  // The transform's 1 / sqrt(d): folded into the signs (rotate), into the
+  // level table (dequantize), or left out (quantize: the codes depend only on
+  // v / stat, and the stored statistic is scaled instead).
+  if (!a.inverse && a.signs) {
+    const float* sg = MODE == RH_ROTATE ? a.signs_s : a.signs;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] *= a.signs[16 * p.cu + j];
+    for (int j = 0; j < 16; ++j) v[j] *= sg[16 * p.cu + j];
+  }
 
   // ---- transform: per round, butterflies on its new bits, then an LDS
   // transpose to the next round's layout (the last one back to natural order)
@@ -236,11 +241,18 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
       if (r + 1 < R) __syncthreads();  // every read is done before the next round's writes
     }
   }
+  if (MODE == RH_ROTATE) {
+    if (a.inverse && a.signs) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] *= a.scale;  // 1 for the identity
-  if (a.inverse && a.signs)
+      for (int j = 0; j < 16; ++j) v[j] *= a.signs_s[16 * p.cu + j];
+    } else if (!a.signs) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] *= a.scale;
+    }
+  } else if (a.inverse && a.signs) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] *= a.signs[16 * p.cu + j];
+  }
 
   // ---- epilogue
   if (!QOUT) {
@@ -281,11 +293,14 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     // one branch for the whole thread: inside it the 16 table reads are
     // independent and pipeline
     if (bins) {
+      // the decision in the bins' coordinate u = v k s + off, where the
+      // table holds each threshold's own u
+      const float ku = k * a.bin_s;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float z = v[j] * k;
-        const float2 e = tab[rh_bin(fmaf(z, a.bin_s, a.bin_off))];
-        c[j] = (uint32_t)((int)e.y + (z > e.x ? 1 : 0));
+        const float u = fmaf(v[j], ku, a.bin_off);
+        const float2 e = tab[rh_bin(u)];
+        c[j] = (uint32_t)((int)e.y + (u > e.x ? 1 : 0));
       }
     } else {
 #pragma unroll
@@ -303,8 +318,10 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     for (int j = 0; j < 16; ++j) c[j] = 0u;
   store_codes<QB>(qcodes, c);
   if ((threadIdx.x & (lpg - 1)) == 0) {
-    if (qkind == BRQ_ABSMAX) static_cast<float*>(a.scales)[qsidx] = stat;
-    else static_cast<_Float16*>(a.scales)[qsidx] = (_Float16)stat;
+    // quantize: v left out the transform's scale, so its statistic takes it
+    const float st = MODE == RH_QUANT ? stat * a.scale : stat;
+    if (qkind == BRQ_ABSMAX) static_cast<float*>(a.scales)[qsidx] = st;
+    else static_cast<_Float16*>(a.scales)[qsidx] = (_Float16)st;
   }
 }
 

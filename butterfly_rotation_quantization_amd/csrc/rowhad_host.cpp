@@ -35,6 +35,7 @@ void fill_common(RhArgs& a, const Plan* p, int64_t rows, int64_t n) {
   a.cpr = n / p->d;
   a.nchunks = rows * a.cpr;
   a.signs = p->signs;
+  a.signs_s = p->signs_s;
   a.scale = 1.0f / std::sqrt((float)p->d);
 }
 
@@ -84,7 +85,8 @@ void fill_quant(RhArgs& a, const brq_quant* q, int64_t n) {
           cnt += a.tbin[i] < b ? 1 : 0;
           if (a.tbin[i] == b) tin = a.tau[i];
         }
-        a.bintab[b] = make_float2(tin, (float)cnt);
+        // the threshold in the bins' coordinate, as the kernel compares it
+        a.bintab[b] = make_float2(tin == INFINITY ? INFINITY : std::fma(tin, s, off), (float)cnt);
       }
       return;
     }
