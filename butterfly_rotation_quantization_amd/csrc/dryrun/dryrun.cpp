@@ -576,7 +576,9 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
       if (b <= prev || b >= kRhBins - 1)
         return violation("codebook threshold %lld in bin %lld", k, b), hipErrorInvalidValue;
       if (a.tbin[k] != b) return violation("threshold %lld recorded in bin %lld", k, a.tbin[k]), hipErrorInvalidValue;
-      if (a.bintab[b].x != std::fma(a.tau[k], a.bin_s, a.bin_off) || (int)a.bintab[b].y != k)
+      int cnt;
+      std::memcpy(&cnt, &a.bintab[b].y, sizeof cnt);
+      if (a.bintab[b].x != std::fma(a.tau[k], a.bin_s, a.bin_off) || cnt != k)
         return violation("bin table entry %lld (threshold %lld)", b, k), hipErrorInvalidValue;
       prev = b;
     }
@@ -606,7 +608,10 @@ hipError_t launch_rowhad(const RhArgs& a, hipStream_t) {
   for (int64_t b = 0; b < nwg; ++b)
     for (int u = 0; u < kRhThreads; ++u) {
       const RhPos p = rh_pos(a, b, u);
-      if (!p.live) continue;
+      if (!p.live) {  // dead threads read the first 16 elements of row 0
+        if (p.row != 0 || p.col0 != 0) return violation("dead thread %lld reads (%lld)", u, p.row), hipErrorInvalidValue;
+        continue;
+      }
       if (p.row >= a.rows || p.col0 < 0 || p.col0 + 16 > a.n || p.col0 % 16)
         return violation("row Hadamard element (%lld, %lld)", p.row, p.col0), hipErrorInvalidValue;
       if (p.col0 % d != 16 * p.cu) return violation("chunk position of thread %lld", u, 0), hipErrorInvalidValue;

@@ -62,7 +62,8 @@ struct RhArgs {
   int tbin[kMaxLevels];
   // The bin table itself, built on the host: bin b holds {its threshold's u
   // (fma(tau, bin_s, bin_off)) or +inf, the number of thresholds in lower
-  // bins}; the kernel compares u = fma(v, k bin_s, bin_off) against it.
+  // bins as the bits of a 32-bit integer}; the kernel compares
+  // u = fma(v, k bin_s, bin_off) against it.
   float2 bintab[kRhBins];
   uint8_t* codes;
   const uint8_t* in_codes;
@@ -135,10 +136,16 @@ __host__ __device__ inline int rh_lds_base(int l2d, int r, int cw, int cu) {
   return b + (b >> 4);
 }
 
-// Bin of a scaled value (the kernel's arithmetic, shared with the host check).
+// Bin of a scaled value (the kernel's arithmetic, shared with the host check):
+// u clamped to [0, kRhBins - 1], then truncated.  The GPU clamps with one
+// median-of-three.
 __host__ __device__ inline int rh_bin(float u) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kRhBins - 1));
+#else
   const float c = u < 0.f ? 0.f : (u > (float)(kRhBins - 1) ? (float)(kRhBins - 1) : u);
   return (int)c;
+#endif
 }
 
 __host__ __device__ inline int64_t rh_nwg(const RhArgs& a) {
@@ -162,7 +169,7 @@ __host__ __device__ inline RhPos rh_pos(const RhArgs& a, int64_t b, int u) {
   p.cw = u >> (a.log2d - 4);
   p.cu = u - p.cw * tpc;
   p.c = b * (kRhTile >> a.log2d) + p.cw;
-  p.live = p.c < a.nchunks;
+  p.live = p.c < a.nchunks;  // a dead thread reads row 0, columns 0..15 and stores nothing
   const uint32_t c32 = p.live ? (uint32_t)p.c : 0u, cpr = (uint32_t)a.cpr;
   const uint32_t row = c32 / cpr;
   p.row = row;

@@ -20,6 +20,9 @@ namespace brq {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef _Float16 hf2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -29,11 +32,13 @@ __device__ __forceinline__ float f16_lo(uint32_t w) {
 __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
-__device__ __forceinline__ uint32_t to_bf16(float f) {  // nearest, ties to even
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+// Two floats to two 16-bit values in one word (lo first), nearest, ties to
+// even: one packed conversion.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v{lo, hi}), bf2v));
 }
-__device__ __forceinline__ uint32_t to_f16(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v{lo, hi}), hf2v));
 }
 
 // 16 consecutive elements (16-byte aligned) as float.
@@ -79,7 +84,7 @@ __device__ __forceinline__ void store16(void* base, int t, int64_t off, const fl
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = v[8 * q + 2 * e], hi = v[8 * q + 2 * e + 1];
-        w[e] = t == BRQ_BF16 ? (to_bf16(lo) | (to_bf16(hi) << 16)) : (to_f16(lo) | (to_f16(hi) << 16));
+        w[e] = t == BRQ_BF16 ? pack_bf16(lo, hi) : pack_f16(lo, hi);
       }
       p[q] = make_uint4(w[0], w[1], w[2], w[3]);
     }
@@ -144,8 +149,10 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[16])
   }
 }
 
+// The 16 codes of one thread as byte offsets into a float table (4 c): each
+// is a shift and a mask of its word, or of the two words it straddles.
 template <int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&c)[16]) {
+__device__ __forceinline__ void load_code_offsets(const uint8_t* p, uint32_t (&o)[16]) {
   uint32_t w[3] = {0u, 0u, 0u};
   if constexpr ((BITS & 1) == 0) {
     const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
@@ -156,13 +163,17 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&c)[16]) 
 #pragma unroll
     for (int k = 0; k < BITS; ++k) w[k >> 1] |= (uint32_t)q[k] << (16 * (k & 1));
   }
-  constexpr uint32_t mask = (1u << BITS) - 1u;
+  constexpr uint32_t mask4 = ((1u << BITS) - 1u) << 2;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int bit = j * BITS, wi = bit >> 5, sh = bit & 31;
-    uint32_t x = w[wi] >> sh;
-    if (sh + BITS > 32) x |= w[wi + 1] << (32 - sh);
-    c[j] = x & mask;
+    if (sh + BITS > 32) {
+      o[j] = (((w[wi] >> sh) | (w[wi + 1] << (32 - sh))) << 2) & mask4;
+    } else if (sh >= 2) {
+      o[j] = (w[wi] >> (sh - 2)) & mask4;
+    } else {
+      o[j] = (w[wi] << (2 - sh)) & mask4;
+    }
   }
 }
 
@@ -175,7 +186,8 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   // dequantize: the level values (centroid / sqrt(g), or code / h - 1)
   constexpr bool DEQ = MODE == RH_DEQUANT || MODE == RH_REQUANT;  // codes in
   constexpr bool QOUT = MODE == RH_QUANT || MODE == RH_REQUANT;    // codes out
-  __shared__ float2 tab[MODE == RH_QUANT ? kRhBins : (DEQ ? kMaxLevels : 1)];
+  __shared__ float2 tab[MODE == RH_QUANT ? kRhBins : 1];
+  __shared__ float lev[DEQ ? kMaxLevels : 1];
   constexpr int R = rh_rounds(L2D);
   constexpr int LV = (1 << BITS) - 1;
   const RhPos p = rh_pos(a, blockIdx.x, threadIdx.x);
@@ -187,33 +199,28 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
     if (MODE == RH_QUANT && bins) tab[threadIdx.x] = a.bintab[threadIdx.x];  // built on the host
     if (DEQ && threadIdx.x <= LV) {  // the levels carry the transform's 1 / sqrt(d)
       const int c = threadIdx.x;
-      tab[c].x = (a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g) * a.scale;
+      lev[c] = (a.qkind == BRQ_ABSMAX ? (float)c / a.h - 1.0f : a.cent[c] / a.sqrt_g) * a.scale;
     }
   };
   float v[16];
 
   // ---- prologue: load or unpack + dequantize, then the signs (forward)
+  // A dead thread (past the last chunk) reads valid memory, transforms it in
+  // its own chunk's LDS area and stores nothing; its quantizer groups hold no
+  // live lane.
   if (!DEQ) {
-    if (p.live) load16(a.x, a.xt, p.row * a.ldx + p.col0, v);
-    else
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    load16(a.x, a.xt, p.row * a.ldx + p.col0, v);
     build_tables();
   } else {
-    uint32_t c[16];
-    float scale = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) c[j] = 0u;
-    if (p.live) {
-      load_codes<BITS>(a.in_codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
-      const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
-      scale = a.qkind == BRQ_ABSMAX ? static_cast<const float*>(a.in_scales)[sidx]
-                                    : (float)static_cast<const _Float16*>(a.in_scales)[sidx];
-    }
+    uint32_t c[16];  // byte offsets into lev
+    load_code_offsets<BITS>(a.in_codes + p.row * a.codes_ld + p.col0 * BITS / 8, c);
+    const int64_t sidx = p.row * a.scales_ld + p.col0 / a.group;
+    const float scale = a.qkind == BRQ_ABSMAX ? static_cast<const float*>(a.in_scales)[sidx]
+                                              : (float)static_cast<const _Float16*>(a.in_scales)[sidx];
     build_tables();
     __syncthreads();  // the level table
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = scale * tab[c[j]].x;
+    for (int j = 0; j < 16; ++j) v[j] = scale * *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(lev) + c[j]);
   }
   // The transform's 1 / sqrt(d): folded into the signs (rotate), into the
   // level table (dequantize), or left out (quantize: the codes depend only on
@@ -280,27 +287,30 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
   }
   if (R == 1 && bins) __syncthreads();  // the bin table (R > 1 passed barriers since)
   if (!p.live) return;
+  // A zero group (stat 0, or not a number) codes as all zeros: its scale k is 0
+  // and its offset puts every value on code 0.
+  const bool nz = stat > 0.f;
   uint32_t c[16];
   if (qkind == BRQ_ABSMAX) {
-    const float k = stat > 0.f ? qh / stat : 0.f;
+    const float k = nz ? qh / stat : 0.f, off = nz ? qh : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int q = (int)rintf(fmaf(v[j], k, qh));
+      const int q = (int)rintf(fmaf(v[j], k, off));
       c[j] = (uint32_t)(q < 0 ? 0 : (q > LVQ ? LVQ : q));
     }
   } else if (MODE == RH_QUANT) {
-    const float k = stat > 0.f ? a.sqrt_g / stat : 0.f;
+    const float k = nz ? a.sqrt_g / stat : 0.f;
     // one branch for the whole thread: inside it the 16 table reads are
     // independent and pipeline
     if (bins) {
       // the decision in the bins' coordinate u = v k s + off, where the
-      // table holds each threshold's own u
-      const float ku = k * a.bin_s;
+      // table holds each threshold's own u; bin 0 holds no threshold
+      const float ku = k * a.bin_s, off = nz ? a.bin_off : -1.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float u = fmaf(v[j], ku, a.bin_off);
+        const float u = fmaf(v[j], ku, off);
         const float2 e = tab[rh_bin(u)];
-        c[j] = (uint32_t)((int)e.y + (u > e.x ? 1 : 0));
+        c[j] = __float_as_uint(e.y) + (u > e.x ? 1u : 0u);
       }
     } else {
 #pragma unroll
@@ -309,13 +319,10 @@ __global__ __launch_bounds__(kRhThreads) void rowhad_kernel(RhArgs a) {
         int q = 0;
 #pragma unroll
         for (int t = 0; t < LV; ++t) q += (z > a.tau[t]) ? 1 : 0;
-        c[j] = (uint32_t)q;
+        c[j] = nz ? (uint32_t)q : 0u;
       }
     }
   }
-  if (!(stat > 0.f))  // a zero group codes as all zeros
-#pragma unroll
-    for (int j = 0; j < 16; ++j) c[j] = 0u;
   store_codes<QB>(qcodes, c);
   if ((threadIdx.x & (lpg - 1)) == 0) {
     // quantize: v left out the transform's scale, so its statistic takes it

@@ -86,7 +86,9 @@ void fill_quant(RhArgs& a, const brq_quant* q, int64_t n) {
           if (a.tbin[i] == b) tin = a.tau[i];
         }
         // the threshold in the bins' coordinate, as the kernel compares it
-        a.bintab[b] = make_float2(tin == INFINITY ? INFINITY : std::fma(tin, s, off), (float)cnt);
+        float cbits;
+        std::memcpy(&cbits, &cnt, sizeof cbits);
+        a.bintab[b] = make_float2(tin == INFINITY ? INFINITY : std::fma(tin, s, off), cbits);
       }
       return;
     }
