@@ -198,7 +198,7 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   const FaGeom g = fa_geom(a.wt, nb, bv, ru);
   const int st = fa_steps(bv), ki = fa_ki(a.wt, st, ru), kq = fa_kq_nt(a.wt, st, ru);
   const int P = g.P, ppw = g.ppw, esz = g.esz, epi = 16 / esz, ipr = g.ipr;
-  if (64 % ipr || a.sv % P || a.su % kFaQC || 8 * ki < ru * fa_ncb(64 / ipr, st) ||
+  if (64 % ipr || a.sv % P || (a.qc != 8 && a.qc != 16 && a.qc != 32) || a.su % a.qc || 8 * ki < ru * fa_ncb(64 / ipr, st) ||
       8 * kq * (64 / (P / 4)) < ru * 16)
     return violation("pass A loop counts %lld / %lld", ki, kq), hipErrorInvalidValue;
   if (fa_lds_bytes(g) > 160 * 1024 || g.slab_bytes % 16 || g.max_off < g.slab_bytes + g.out_floats * 4 ||
@@ -220,7 +220,7 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
   std::vector<uint8_t> cover((size_t)(a.m * a.n), 0);
   for (int64_t b = 0; b < nwg; ++b) {
     const FaTile t = fa_tile(a, b, nwg);
-    if (t.p0 < 0 || t.p0 + P > a.sv || t.p0 % P || t.q0 < 0 || t.q0 + kFaQC > a.su || t.chunk < 0 ||
+    if (t.p0 < 0 || t.p0 + P > a.sv || t.p0 % P || t.q0 < 0 || t.q0 + a.qc > a.su || t.chunk < 0 ||
         t.chunk >= a.nchunk)
       return violation("pass A tile %lld of %lld", b, nwg), hipErrorInvalidValue;
     for (int w = 0; w < kFaWaves; ++w)
@@ -232,7 +232,7 @@ hipError_t launch_fused_a(const FusedAArgs& a, hipStream_t) {
               if (!in_range(i, 8, a.v0_n) || i % 8)
                 return violation("V_0 block read (p %lld, lane %lld)", t.p0 + ppw * w + j, l), hipErrorInvalidValue;
             }
-    for (int q = t.q0; q < t.q0 + kFaQC; ++q) {
+    for (int q = t.q0; q < t.q0 + a.qc; ++q) {
       std::fill(slab.begin(), slab.end(), -1);
       std::fill(outa.begin(), outa.end(), -1);
       std::vector<uint8_t> loaded(g.items, 0);

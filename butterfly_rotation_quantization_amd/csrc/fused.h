@@ -34,7 +34,7 @@
 namespace brq {
 
 constexpr int kFaWaves = 8;            // pass A: waves per workgroup
-constexpr int kFaQC = 8;               // pass A: q values per workgroup (looped)
+constexpr int kFaQC = 8;               // pass A: fewest q values per workgroup (looped; fa_qc)
 constexpr int kFbWaves = 16;           // pass B: waves per workgroup
 // pass B LDS: the exchange buffer [r1 16][c1h 8][r2 16][c2 16] (swizzled),
 // whose first 32 KB hold the tile's 16 V_1 blocks during phase 1, then the
@@ -78,6 +78,7 @@ struct FusedAArgs {
   const uint16_t* v0;
   int64_t v0_gs;
   int64_t u0_n, v0_n; // extents of the block arrays in halves (host checks)
+  int qc;             // q values per workgroup (fa_qc)
 };
 
 struct FusedBArgs {
@@ -106,7 +107,7 @@ struct FusedBArgs {
 // ---- pass A geometry --------------------------------------------------------
 //
 // A workgroup owns P = 8 * ppw consecutive p (ppw per wave) of one column
-// chunk and kFaQC consecutive q.  For each q it stages the input slab
+// chunk and qc consecutive q (fa_qc).  For each q it stages the input slab
 // X[r0 < ru][c0 < bv][P] through LDS (runs of P input elements, at least 64
 // bytes), each wave contracts c0 with the V_0 blocks of its own ppw p held in
 // registers (ru / 16 row tiles), then r0 with the U_0 block of q, and the
@@ -208,12 +209,25 @@ __host__ __device__ inline int fa_scale_shift(uint32_t mbits) { return 138 - (in
 // Workgroup b -> (p range, q chunk, column chunk).  Workgroups are dealt to
 // the 8 XCDs round robin (b % 8); consecutive slots of one XCD walk the p
 // ranges first, so workgroups sharing input rows share that XCD's L2.
+// q values per workgroup: 32 or 16 when su allows it and the grid still
+// gives each of the cus CUs a workgroup and splits into 8 equal XCD shares,
+// else kFaQC.  A workgroup loads its V_0 entries and pays its start-up
+// latency once for all its q, and with fewer q groups each XCD reads the V_0
+// entries of fewer of them.
+inline int fa_qc(int64_t nwg8, int su, int cus) {
+  for (int qc = 32; qc > kFaQC; qc /= 2) {
+    const int64_t n = nwg8 * kFaQC / qc;
+    if (su % qc == 0 && n >= cus && n % 8 == 0) return qc;
+  }
+  return kFaQC;
+}
+
 struct FaTile {
   int p0, q0, chunk;
 };
 
 __host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
-  return (int64_t)(a.sv / fa_p(a.wt, a.nb)) * (a.su / kFaQC) * a.nchunk;
+  return (int64_t)(a.sv / fa_p(a.wt, a.nb)) * (a.su / a.qc) * a.nchunk;
 }
 
 __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_t nwg) {
@@ -223,8 +237,8 @@ __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_
   FaTile t;
   t.p0 = (int)(lin % (a.sv / P)) * P;
   const int64_t rest = lin / (a.sv / P);
-  t.q0 = (int)(rest % (a.su / kFaQC)) * kFaQC;
-  t.chunk = (int)(rest / (a.su / kFaQC));
+  t.q0 = (int)(rest % (a.su / a.qc)) * a.qc;
+  t.chunk = (int)(rest / (a.su / a.qc));
   return t;
 }
 

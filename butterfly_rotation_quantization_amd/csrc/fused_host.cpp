@@ -210,7 +210,8 @@ const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
   if (a.bv < 2 || a.bv > 64 || a.nb != (a.bv + 15) / 16) return "V_0 radix";
   if ((a.ru != 16 && a.ru != 32) || (a.ru == 32 && a.nb > 2)) return "U_0 radix";
   const int P = fa_p(a.wt, a.nb);
-  if (a.su % kFaQC || a.sv % P || (int64_t)a.ru * a.su != a.m || a.dv != a.bv * a.sv ||
+  if ((a.qc != 8 && a.qc != 16 && a.qc != 32) || a.su % a.qc || a.sv % P ||
+      (int64_t)a.ru * a.su != a.m || a.dv != a.bv * a.sv ||
       (int64_t)a.nchunk * a.dv != a.n)
     return "shape";
   if (fa_nwg(a) % 8) return "pass A grid";
@@ -346,6 +347,12 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
   a.u0_exact = U->fz0_exact;
   a.v0 = V->fz0v;
   a.v0_gs = V->fz_gs0v;
+  {
+    int dev = 0, cus = 0;
+    if (rt_get_device(&dev) != hipSuccess || rt_cu_count(dev, &cus) != hipSuccess || cus < 1) return BRQ_ERR_HIP;
+    a.qc = kFaQC;
+    a.qc = fa_qc(a.su % kFaQC ? 0 : fa_nwg(a), a.su, cus);
+  }
 
   FusedBArgs b;
   std::memset(&b, 0, sizeof b);

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
   // never wait on the prefetch of the next slab
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int qi = 0; qi < kFaQC; ++qi, ++q) {
+  for (int qi = 0; qi < a.qc; ++qi, ++q) {
     // the previous slab's reads ended before the previous second barrier
     {
       uint32_t mx = fa_items_absmax<WT, KI>(raw);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
       }
       // the next slab's loads queue behind the previous stores: issued after
       // the last V_0 products they no longer hold up the MFMA phase
-      if (nt == NB - 1 && qi + 1 < kFaQC) {
+      if (nt == NB - 1 && qi + 1 < a.qc) {
         load_slab(q + 1);
         load_u(q + 1);
       }
