@@ -945,7 +945,11 @@ hipError_t launch_stage_pair2(const P2Args& a, hipStream_t) {
   for (int64_t blk = 0; blk < nb; ++blk)
     for (int u = 0; u < 256; ++u) {
       const int sl = u / n, e = u - sl * n;
-      const int64_t s = (blk % nsb) * a.sets + sl, l0 = (blk / nsb) * kP2Lines;
+      int64_t sbk, lb;
+      p2_tile(a, blk, sbk, lb);
+      if (sbk < 0 || sbk >= nsb || lb < 0 || lb * nsb + sbk >= nb)
+        return violation("stage pair workgroup %lld maps to (%lld, ...)", blk, sbk), hipErrorInvalidValue;
+      const int64_t s = sbk * a.sets + sl, l0 = lb * kP2Lines;
       const int nl = (int)std::min<int64_t>(a.lines - l0, kP2Lines);
       if (sl >= a.sets || s >= a.nsets) continue;
       if (nl < 1) return violation("stage pair line tile at %lld", l0, 0), hipErrorInvalidValue;

@@ -300,9 +300,18 @@ __host__ __device__ inline int64_t p2_row_i(const P2Args& a, int64_t hi, int64_t
 __host__ __device__ inline int64_t p2_set_blocks(const P2Args& a) {
   return (a.nsets + a.sets - 1) / a.sets;
 }
-// Workgroup bid: set block bid % set blocks, rows kP2Lines * (bid / set blocks) ..
 __host__ __device__ inline int64_t p2_blocks(const P2Args& a) {
   return p2_set_blocks(a) * ((a.lines + kP2Lines - 1) / kP2Lines);
+}
+// Workgroup blk -> set block sbk and rows kP2Lines * lb ..  Workgroups go to
+// the XCDs in turn (blk mod 8); with the grid a multiple of 8, the workgroups
+// of one XCD take consecutive set blocks, so block rows that neighbouring
+// sets share in a cache line come into that XCD's L2 once.
+__host__ __device__ inline void p2_tile(const P2Args& a, int64_t blk, int64_t& sbk, int64_t& lb) {
+  const int64_t nb = p2_blocks(a), nsb = p2_set_blocks(a);
+  const int64_t lin = nb % 8 ? blk : (blk % 8) * (nb / 8) + blk / 8;
+  sbk = lin % nsb;
+  lb = lin / nsb;
 }
 hipError_t launch_stage_pair2(const P2Args& a, hipStream_t s);
 

@@ -23,8 +23,9 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
   const int n = a.bo * a.bi;
   const int u = threadIdx.x;
   const int sl = u / n, e = u - sl * n;
-  const int64_t nsb = p2_set_blocks(a);
-  const int64_t sbk = blockIdx.x % nsb, l0 = (int64_t)(blockIdx.x / nsb) * kP2Lines;
+  int64_t sbk, lb;
+  p2_tile(a, blockIdx.x, sbk, lb);
+  const int64_t l0 = lb * kP2Lines;
   const int64_t s = sbk * a.sets + sl;
   const bool act = sl < a.sets && s < a.nsets;
   const int nl = (int)(a.lines - l0 < kP2Lines ? a.lines - l0 : kP2Lines);
