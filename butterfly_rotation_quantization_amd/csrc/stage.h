@@ -305,13 +305,14 @@ __host__ __device__ inline int64_t p2_blocks(const P2Args& a) {
 }
 // Workgroup blk -> set block sbk and rows kP2Lines * lb ..  Workgroups go to
 // the XCDs in turn (blk mod 8); with the grid a multiple of 8, the workgroups
-// of one XCD take consecutive set blocks, so block rows that neighbouring
+// of one XCD take consecutive (set block, line block) pairs, line blocks
+// fastest, so the line blocks of a set and the block rows that neighbouring
 // sets share in a cache line come into that XCD's L2 once.
 __host__ __device__ inline void p2_tile(const P2Args& a, int64_t blk, int64_t& sbk, int64_t& lb) {
-  const int64_t nb = p2_blocks(a), nsb = p2_set_blocks(a);
+  const int64_t nb = p2_blocks(a), nlb = nb / p2_set_blocks(a);
   const int64_t lin = nb % 8 ? blk : (blk % 8) * (nb / 8) + blk / 8;
-  sbk = lin % nsb;
-  lb = lin / nsb;
+  sbk = lin / nlb;
+  lb = lin % nlb;
 }
 hipError_t launch_stage_pair2(const P2Args& a, hipStream_t s);
 
