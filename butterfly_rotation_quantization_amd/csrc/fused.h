@@ -79,6 +79,7 @@ struct FusedAArgs {
   int64_t v0_gs;
   int64_t u0_n, v0_n; // extents of the block arrays in halves (host checks)
   int qc;             // q values per workgroup (fa_qc)
+  int pt;             // p tiles per block of the workgroup order (fa_pt)
 };
 
 struct FusedBArgs {
@@ -230,15 +231,36 @@ __host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
   return (int64_t)(a.sv / fa_p(a.wt, a.nb)) * (a.su / a.qc) * a.nchunk;
 }
 
+// Workgroup b goes to XCD b mod 8 and takes position lin of that XCD's
+// share (the grid is a multiple of 8).  In lin order the p tiles run in
+// blocks of a.pt (fa_pt), then the q groups, then the blocks, then the
+// chunks: an XCD's workgroups share every input line they touch in its L2,
+// and each XCD reads the V_0 entries of only its own p tiles.
+//
+// p tiles per block: grids of at least four workgroups per CU take the
+// tiles that share 128-byte input lines (two 64-byte runs), so an XCD holds
+// few p tiles' V_0 entries at a time; smaller grids take 512 contiguous
+// bytes of a row per q.  Measured on the 16-bit weights: the 8192-row weight
+// with radix 7 (1024 workgroups) ran pass A in 487 us with pairs against 499
+// with 512-byte blocks; the 256-workgroup grids (4096 and 11008 columns)
+// were 4% slower with pairs.
+inline int fa_pt(const FusedAArgs& a, int64_t nwg, int cus) {
+  const int P = fa_p(a.wt, a.nb), run = P * fa_esz(a.wt), npt = a.sv / P;
+  const int bytes = nwg >= 4 * (int64_t)cus ? 128 : 512;
+  const int pt = run >= bytes ? 1 : bytes / run;
+  return pt < npt ? pt : npt;
+}
 __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_t nwg) {
-  const int P = fa_p(a.wt, a.nb);
+  const int P = fa_p(a.wt, a.nb), pt = a.pt, nqg = a.su / a.qc;
   const int64_t per_xcd = nwg / 8;
   const int64_t lin = (b % 8) * per_xcd + b / 8;
+  const int64_t per_pair = (int64_t)pt * nqg, per_chunk = (int64_t)(a.sv / P) * nqg;
+  const int64_t in_chunk = lin % per_chunk;
+  const int64_t pair = in_chunk / per_pair, r = in_chunk % per_pair;
   FaTile t;
-  t.p0 = (int)(lin % (a.sv / P)) * P;
-  const int64_t rest = lin / (a.sv / P);
-  t.q0 = (int)(rest % (a.su / a.qc)) * a.qc;
-  t.chunk = (int)(rest / (a.su / a.qc));
+  t.p0 = (int)(pair * pt + r % pt) * P;
+  t.q0 = (int)(r / pt) * a.qc;
+  t.chunk = (int)(lin / per_chunk);
   return t;
 }
 

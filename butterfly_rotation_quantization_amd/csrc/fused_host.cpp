@@ -214,7 +214,7 @@ const char* check_fused(const FusedAArgs& a, const FusedBArgs& b) {
       (int64_t)a.ru * a.su != a.m || a.dv != a.bv * a.sv ||
       (int64_t)a.nchunk * a.dv != a.n)
     return "shape";
-  if (fa_nwg(a) % 8) return "pass A grid";
+  if (fa_nwg(a) % 8 || a.pt < 1 || (a.sv / fa_p(a.wt, a.nb)) % a.pt) return "pass A grid";
   if (fa_lds_bytes(fa_geom(a.wt, a.nb, a.bv, a.ru)) > 160 * 1024) return "pass A LDS";
   // pass A addresses a lane's input and output as 32-bit byte offsets from a
   // per-chunk base
@@ -352,6 +352,7 @@ brq_status fused_rqp(const Plan* U, const Plan* V, const void* w, int wt, int64_
     if (rt_get_device(&dev) != hipSuccess || rt_cu_count(dev, &cus) != hipSuccess || cus < 1) return BRQ_ERR_HIP;
     a.qc = kFaQC;
     a.qc = fa_qc(a.su % kFaQC ? 0 : fa_nwg(a), a.su, cus);
+    a.pt = a.su % a.qc ? 1 : fa_pt(a, fa_nwg(a), cus);
   }
 
   FusedBArgs b;
