@@ -207,9 +207,6 @@ __host__ __device__ inline int fa_lds_bytes(const FaGeom& g) { return g.max_off 
 // stay below 8 * 1.001 * 2^12 < 65504 for radices up to 64.
 __host__ __device__ inline int fa_scale_shift(uint32_t mbits) { return 138 - (int)((mbits >> 23) & 0xff); }
 
-// Workgroup b -> (p range, q chunk, column chunk).  Workgroups are dealt to
-// the 8 XCDs round robin (b % 8); consecutive slots of one XCD walk the p
-// ranges first, so workgroups sharing input rows share that XCD's L2.
 // q values per workgroup: 32 or 16 when su allows it and the grid still
 // gives each of the cus CUs a workgroup and splits into 8 equal XCD shares,
 // else kFaQC.  A workgroup loads its V_0 entries and pays its start-up
@@ -231,11 +228,12 @@ __host__ __device__ inline int64_t fa_nwg(const FusedAArgs& a) {
   return (int64_t)(a.sv / fa_p(a.wt, a.nb)) * (a.su / a.qc) * a.nchunk;
 }
 
-// Workgroup b goes to XCD b mod 8 and takes position lin of that XCD's
-// share (the grid is a multiple of 8).  In lin order the p tiles run in
-// blocks of a.pt (fa_pt), then the q groups, then the blocks, then the
-// chunks: an XCD's workgroups share every input line they touch in its L2,
-// and each XCD reads the V_0 entries of only its own p tiles.
+// Workgroup b -> (p range, q range, column chunk).  Workgroup b goes to XCD
+// b mod 8 and takes position lin of that XCD's share (the grid is a multiple
+// of 8).  In lin order the p tiles run in blocks of a.pt (fa_pt), then the q
+// groups, then the blocks, then the chunks: an XCD's workgroups share every
+// input line they touch in its L2, and each XCD reads the V_0 entries of
+// only its own p tiles.
 //
 // p tiles per block: grids of at least four workgroups per CU take the
 // tiles that share 128-byte input lines (two 64-byte runs), so an XCD holds
@@ -254,11 +252,11 @@ __host__ __device__ inline FaTile fa_tile(const FusedAArgs& a, int64_t b, int64_
   const int P = fa_p(a.wt, a.nb), pt = a.pt, nqg = a.su / a.qc;
   const int64_t per_xcd = nwg / 8;
   const int64_t lin = (b % 8) * per_xcd + b / 8;
-  const int64_t per_pair = (int64_t)pt * nqg, per_chunk = (int64_t)(a.sv / P) * nqg;
+  const int64_t per_block = (int64_t)pt * nqg, per_chunk = (int64_t)(a.sv / P) * nqg;
   const int64_t in_chunk = lin % per_chunk;
-  const int64_t pair = in_chunk / per_pair, r = in_chunk % per_pair;
+  const int64_t blk = in_chunk / per_block, r = in_chunk % per_block;
   FaTile t;
-  t.p0 = (int)(pair * pt + r % pt) * P;
+  t.p0 = (int)(blk * pt + r % pt) * P;
   t.q0 = (int)(r / pt) * a.qc;
   t.chunk = (int)(lin / per_chunk);
   return t;
