@@ -783,7 +783,7 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
         }
       }
       if (a.b2) {  // the second stage: reads (g2, k2) (forward) or (k2, g2) (inverse), writes (j2, g2)
-        if (a.side != 0 || a.gw != 16 || a.S != (a.inv2 ? 1 : 16) || a.b != 16 || a.b2 != 16 || a.bs != 16 ||
+        if (a.side != 0 || a.gw != 16 || a.S != (a.inv2 ? 1 : 16) || a.b != 16 || a.b2 != 16 || a.bs != 16 || a.bp != 16 ||
             ng != a.gw || (a.mode != BRQ_HADAMARD && (!a.blk2 || reinterpret_cast<uintptr_t>(a.blk2) % 16)))
           return violation("stage pair geometry (b %lld, b2 %lld)", a.b, a.b2), hipErrorInvalidValue;
         const int64_t blk2_floats = a.mode == BRQ_PER_GROUP ? (a.d / a.b2) * a.b2 * a.b2 : (int64_t)a.b2 * a.b2;

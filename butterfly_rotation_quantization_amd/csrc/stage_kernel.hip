@@ -106,6 +106,30 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
     }
   }
 
+  // The optional second stage's block row (pairs run only at radix 16 on the
+  // right side, the launcher checks), loaded with the first one so that no
+  // global load waits between the two stages.
+  const int g2 = u >> 4, j2 = u & 15;
+  float w2[16];
+  if constexpr (MAXB == 16 && SIDE == 0) {
+    if (a.b2) {
+      if (a.mode == BRQ_HADAMARD) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w2[k] = (__popc(j2 & k) & 1) ? -0.25f : 0.25f;
+      } else {
+        const float* row = a.blk2 + sp_block_row2(a, g0, g2, j2);
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const float4 q = *reinterpret_cast<const float4*>(row + 4 * k4);
+          w2[4 * k4] = q.x;
+          w2[4 * k4 + 1] = q.y;
+          w2[4 * k4 + 2] = q.z;
+          w2[4 * k4 + 3] = q.w;
+        }
+      }
+    }
+  }
+
   // zero the padding members, then write the tile (signs first, forward)
   for (int e = u; e < LINES * a.gw; e += kSpThreads) {
     const int l = e / a.gw, gg = e - l * a.gw;
@@ -186,23 +210,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
 
   // ---- the optional second stage (radix 16, stride 1) on the same tile: its
   // group g2 is positions 16 g2 .. 16 g2 + 15, consecutive slots (g2, k2)
-  if (a.b2) {
-    const int g2 = u >> 4, j2 = u & 15;
-    float w2[16];
-    if (a.mode == BRQ_HADAMARD) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) w2[k] = (__popc(j2 & k) & 1) ? -0.25f : 0.25f;
-    } else {
-      const float* row = a.blk2 + sp_block_row2(a, g0, g2, j2);
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const float4 q = *reinterpret_cast<const float4*>(row + 4 * k4);
-        w2[4 * k4] = q.x;
-        w2[4 * k4 + 1] = q.y;
-        w2[4 * k4 + 2] = q.z;
-        w2[4 * k4 + 3] = q.w;
-      }
-    }
+  if (MAXB == 16 && SIDE == 0 && a.b2) {
     if (a.inv2) {  // members of column g2: slots (k2, g2)
 #pragma unroll
       for (int l = 0; l < LINES; ++l) {
@@ -277,6 +285,7 @@ hipError_t launch_t(const SpArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_stage(const SpArgs& a, hipStream_t s) {
+  if (a.b2 && (a.bp != 16 || a.side != 0)) return hipErrorInvalidValue;  // pairs: radix 16, right side
   if (a.bp <= 8) return launch_t<8>(a, s);
   if (a.bp <= 16) return launch_t<16>(a, s);
   if (a.bp <= 32) return launch_t<32>(a, s);
