@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   float v[LINES];
   int mg = 0, mk = 0;
   int64_t mpos = 0;
+  float sg_out = 1.f;  // right side: the member's output sign, loaded with its inputs
   if (a.side == 0) {
     if (u < gb) {
       sp_member(a, u, mg, mk);
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
 #pragma unroll
         for (int l = 0; l < LINES; ++l)
           if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, mpos, a.ld_src));
+        if (a.sign_out) sg_out = a.sign_out[(uint32_t)mpos % (uint32_t)a.d];
       }
     }
   } else {
@@ -250,11 +252,10 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
   // ---- tile out
   if (a.side == 0) {
     if (u < gb && mg < ng) {
-      const float sg = a.sign_out ? a.sign_out[(uint32_t)mpos % (uint32_t)a.d] : 1.f;
 #pragma unroll
       for (int l = 0; l < LINES; ++l)
         if (l < nl)
-          sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, mpos, a.ld_dst), sg * buf[sp_lds(a, l, mg, mk)]);
+          sp_store(a.dst, a.dst_t, sp_off(a, l0 + l, mpos, a.ld_dst), sg_out * buf[sp_lds(a, l, mg, mk)]);
     }
   } else {
     const int l = u % LINES;

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
   const int ig = ea, ij = eb;
   int64_t pos = 0;
   float wo[BO], wi[BI], v[kP2Lines];
+  float sg_out = 1.f;
 #pragma unroll
   for (int k = 0; k < BO; ++k) wo[k] = 0.f;
 #pragma unroll
@@ -57,6 +58,7 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
     for (int k = 0; k < BI; ++k)
       if (k < a.bi) wi[k] = ri[k];
     const float sg = a.sign_in ? a.sign_in[(uint32_t)(pos % a.d)] : 1.f;
+    if (a.sign_out) sg_out = a.sign_out[(uint32_t)(pos % a.d)];  // loaded with the inputs
 #pragma unroll
     for (int l = 0; l < kP2Lines; ++l)
       if (l < nl) sb[l * n + ea * a.bi + eb] = sg * v[l];
@@ -93,10 +95,9 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
     __syncthreads();
   }
   if (act) {
-    const float sg = a.sign_out ? a.sign_out[(uint32_t)(pos % a.d)] : 1.f;
 #pragma unroll
     for (int l = 0; l < kP2Lines; ++l)
-      if (l < nl) p2_store(a.dst, a.dst_t, (l0 + l) * a.ld_dst + pos, sg * sb[l * n + ea * a.bi + eb]);
+      if (l < nl) p2_store(a.dst, a.dst_t, (l0 + l) * a.ld_dst + pos, sg_out * sb[l * n + ea * a.bi + eb]);
   }
 }
 
