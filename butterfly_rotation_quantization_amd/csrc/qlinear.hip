@@ -461,14 +461,18 @@ __global__ void ql_reduce_kernel(const float* part, int splits, int64_t T, int64
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * m) return;
   const int64_t t = i / m, o = i - t * m;
-  // four running sums in a fixed order (the loads of a round are independent)
+  // four running sums in a fixed order: part p goes to sum p mod 4.  The
+  // parts are read 32 at a time, all loads of a batch in flight together
+  // (a batch is one memory round trip; past the last part a slot adds 0).
   const int64_t st = T * m;
   float s4[4] = {0.f, 0.f, 0.f, 0.f};
-  int p = 0;
-  for (; p + 4 <= splits; p += 4)
+  for (int p = 0; p < splits; p += 32) {
+    float v[32];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s4[j] += part[(int64_t)(p + j) * st + i];
-  for (; p < splits; ++p) s4[0] += part[(int64_t)p * st + i];
+    for (int j = 0; j < 32; ++j) v[j] = p + j < splits ? part[(int64_t)(p + j) * st + i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) s4[j & 3] += v[j];
+  }
   const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   const int64_t j = t * ldo + o;
   if (ot == BRQ_F32) {
