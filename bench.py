@@ -395,8 +395,9 @@ class RightRotate(Workload):
         then stay in the caches (warm), beside the plan rotation (cold)."""
         if not self.latency:
             return None
-        return lambda i: self.brq.rotate(self.plans[0], self.bufs[0], self.y, side="right",
-                                         ws=self.ws, stream=self.stream)
+        return lambda i, stream=None: self.brq.rotate(self.plans[0], self.bufs[0], self.y,
+                                                      side="right", ws=self.ws,
+                                                      stream=stream or self.stream)
 
     def elements(self):
         return self.T * self.N
@@ -666,11 +667,11 @@ class DecodeLinear(Workload):
         self.brq.qlinear(self.U, self.V, self.x, codes, alpha, self.m, self.n, self.bits,
                          self.group, y=self.y, ws=self.ws, stream=self.stream)
 
-    def step_warm(self, i):
+    def step_warm(self, i, stream=None):
         """The same call on one weight copy (as far as the caches hold it)."""
         codes, alpha = self.ws_copies[0]
         self.brq.qlinear(self.U, self.V, self.x, codes, alpha, self.m, self.n, self.bits,
-                         self.group, y=self.y, ws=self.ws, stream=self.stream)
+                         self.group, y=self.y, ws=self.ws, stream=stream or self.stream)
 
     def value(self, ms):
         return ms * 1e3
@@ -971,6 +972,38 @@ def time_steps(wl, steps, torch, stream, step=None):
     return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
+def graph_latency(wl, steps, warmup, torch):
+    """Per-call latency of the warm call replayed from a graph captured once
+    (the call's kernels and arguments; a replay saves the host launch path
+    and the gaps between dependent launches).  The hot calls only launch
+    kernels on the given stream, which makes them capturable."""
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            wl.step_warm(0, stream=s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            wl.step_warm(0, stream=s)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(cur)
+        for i in range(steps):
+            g.replay()
+            evs[i + 1].record(cur)
+        torch.cuda.synchronize()
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        del g
+        return {"median": _pct(per, 50), "p10": _pct(per, 10), "p90": _pct(per, 90)}
+    except Exception as e:  # a failed capture leaves the line without the figure
+        return {"error": str(e)[:160]}
+
+
 def stream_copy_gbs(torch, dev, mib=1024, reps=10):
     """A plain device-to-device copy of `mib` MiB (torch's copy kernel):
     bytes read + written per second, the practical HBM ceiling."""
@@ -1045,12 +1078,13 @@ def run_workload(wl, a, brq, torch, dev, stream, copy_gbs=None):
     kernels = brq.profile_read()
     names = list(kernels)
     wl._first_kernel, wl._last_kernel = names[0], names[-1]
-    warm = None
+    warm = graph = None
     if getattr(wl, "step_warm", None) is not None:
         for i in range(a.warmup):
             wl.step_warm(i)
         _, wper = time_steps(wl, a.steps, torch, stream, wl.step_warm)
         warm = {"median": _pct(wper, 50), "p10": _pct(wper, 10), "p90": _pct(wper, 90)}
+        graph = graph_latency(wl, a.steps, a.warmup, torch)
 
     value = wl.value(ms)
     alg = wl.alg_bytes()
@@ -1073,6 +1107,7 @@ def run_workload(wl, a, brq, torch, dev, stream, copy_gbs=None):
     if warm is not None:
         cfg["step_ms_warm"] = warm
         cfg["step_ms_cold"] = cfg["step_ms"]
+        cfg["step_ms_graph"] = graph
     if copy_gbs is not None:
         cfg["stream_copy_gbs"] = copy_gbs
         cfg["hbm_frac_of_copy"] = round(alg / (ms * 1e-3) / 1e9 / copy_gbs, 5)
