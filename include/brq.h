@@ -3,10 +3,14 @@
  *
  * C ABI of libbrq.so.  Every data pointer passed to a hot call is a DEVICE
  * pointer owned by the caller; the library never frees or keeps it.  Hot calls
- * (brq_rotate*, brq_rotate_quantize_pack, brq_dequant_unrotate) are
- * asynchronous on the caller's HIP stream (`stream` is a hipStream_t, NULL =
- * the default stream), never allocate and never synchronise; a fault inside a
- * kernel shows up at the caller's next synchronisation.  Launch failures are
+ * (brq_rotate*, brq_rotate_quantize_pack, brq_dequant_unrotate, brq_requant,
+ * brq_qlinear, brq_orp_geo_*) are asynchronous on the caller's HIP stream
+ * (`stream` is a hipStream_t, NULL = the default stream), never allocate and
+ * never synchronise; a fault inside a kernel shows up at the caller's next
+ * synchronisation.  A hot call issues nothing but kernel launches on
+ * `stream`, so it can be captured into a HIP graph (once called outside the
+ * capture: the first call of a kernel may set its attributes); the
+ * pointers and workspace captured are then those of every replay.  Launch failures are
  * returned as BRQ_ERR_HIP.  Errors are returned, never thrown; the last
  * error's detail text is kept per thread (brq_last_error).
  *
