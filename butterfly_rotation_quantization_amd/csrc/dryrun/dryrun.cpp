@@ -664,7 +664,7 @@ namespace brq {
 hipError_t launch_stage(const SpArgs& a, hipStream_t) {
   ++g_launches;
   const int b = a.b;
-  if ((a.tile_lines != 0 && (a.side != 0 || a.tile_lines != kSpLinesFew)) ||
+  if ((a.tile_lines != 0 && (a.side != 0 || (a.tile_lines != kSpLinesFew && a.tile_lines != kSpLinesTiny))) ||
       b < 2 || b > 64 || a.bp < b || (a.bp & (a.bp - 1)) || a.bp > 64 || a.bs < b || a.bs % 4 ||
       a.bs - b >= 4 || a.gw < 1 || a.gw * a.bp > kSpThreads || a.gw * a.bs > kSpLineFloats)
     return violation("stage pass geometry (b %lld, gw %lld)", b, a.gw), hipErrorInvalidValue;

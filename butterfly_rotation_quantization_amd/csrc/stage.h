@@ -66,8 +66,8 @@ struct SpArgs {
   // writes output j2 at slot (j2, g2), again that position's slot.
   int b2;             // 16, or 0 for a single stage
   int inv2;           // the pair is the inverse one
-  // right side: lines per tile, kSpLines or kSpLinesFew (more workgroups,
-  // each lighter); the left side always takes kSpLines
+  // right side: lines per tile, kSpLines, kSpLinesFew or kSpLinesTiny (more
+  // workgroups, each lighter); the left side always takes kSpLines
   int tile_lines;
   const float* blk2;  // its blocks ([group][j][k] over the chunk's d / b2 groups, or one)
 };
@@ -86,8 +86,11 @@ __host__ __device__ inline int64_t sp_group_tiles(const SpArgs& a) {
   return (a.ngroups + a.gw - 1) / a.gw;
 }
 constexpr int kSpLinesFew = 8;
+constexpr int kSpLinesTiny = 4;       // right side, up to kSpTinyRows rows
+constexpr int kSpTinyRows = 16;
 __host__ __device__ inline int sp_tl(const SpArgs& a) {
-  return a.side == 0 && a.tile_lines == kSpLinesFew ? kSpLinesFew : kSpLines;
+  if (a.side != 0) return kSpLines;
+  return a.tile_lines == kSpLinesTiny ? kSpLinesTiny : (a.tile_lines == kSpLinesFew ? kSpLinesFew : kSpLines);
 }
 __host__ __device__ inline int64_t sp_line_tiles(const SpArgs& a) {
   return (a.lines + sp_tl(a) - 1) / sp_tl(a);

@@ -73,7 +73,9 @@ bool sp_shape_ok(const Plan* p, int side, int64_t rows, int64_t cols) {
   const int64_t lines = side == 0 ? rows : cols;
   const int64_t axis = side == 0 ? cols : rows;  // positions fit sp_pos's 32 bits
   if (axis % p->d || axis > (int64_t)1 << 30) return false;
-  if (((lines + kSpLines - 1) / kSpLines) * (axis / 2) >= ((int64_t)1 << 31)) return false;  // grid
+  // grid: line tiles of the size the launch will use times at most axis / 2 group tiles
+  const int64_t tl = side != 0 ? kSpLines : (lines <= kSpTinyRows ? kSpLinesTiny : kSpLinesFew);
+  if (((lines + tl - 1) / tl) * (axis / 2) >= ((int64_t)1 << 31)) return false;
   for (int i = 0; i < p->nst; ++i)
     if (p->radix[i] > 64) return false;
   return true;
@@ -214,8 +216,11 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     std::memset(&a, 0, sizeof a);
     a.side = side;
     // right side: 8-row tiles (measured faster than 32-row ones from 1 row
-    // to 8192: more workgroups, fewer registers and less LDS each)
-    a.tile_lines = side == 0 ? kSpLinesFew : 0;
+    // to 8192: more workgroups, fewer registers and less LDS each), 4-row
+    // tiles up to 16 rows (the decode rotations at 16 tokens: the (16, 16)
+    // pair 10.8 -> 9.8 us, the decode linear's output rotation 22 -> 17 us;
+    // at 256 rows 4-row tiles were slower)
+    a.tile_lines = side == 0 ? (lines <= kSpTinyRows ? kSpLinesTiny : kSpLinesFew) : 0;
     a.b = L.b[si];
     a.bp = pow2_at_least(a.b);
     a.bs = (a.b + 3) & ~3;

@@ -276,6 +276,8 @@ hipError_t launch_t(const SpArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)sp_blocks(a));
   if (a.side)
     hipLaunchKernelGGL((stage_kernel<MAXB, 1, kSpLines>), grid, dim3(kSpThreads), 0, s, a);
+  else if (sp_tl(a) == kSpLinesTiny)
+    hipLaunchKernelGGL((stage_kernel<MAXB, 0, kSpLinesTiny>), grid, dim3(kSpThreads), 0, s, a);
   else if (sp_tl(a) == kSpLinesFew)
     hipLaunchKernelGGL((stage_kernel<MAXB, 0, kSpLinesFew>), grid, dim3(kSpThreads), 0, s, a);
   else
