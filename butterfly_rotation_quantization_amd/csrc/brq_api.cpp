@@ -1208,7 +1208,8 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // beat fewer with longer load pipelines).  The split count does not depend
 // on the pointers, so the workspace size is known before the call.
 int ql_splits(int64_t T, int64_t m, int64_t n, int bits, int group) {
-  const int kind = ql_kind(T, n, bits, group, true);
+  const int kind = ql_kind(T, m, n, bits, group, true);
+  if (kind == kQlGemm) return ql_gemm_splits(T, n);
   const int tm = ql_kind_tm(kind, T, bits, group);
   const int64_t tt = kQlTok * tm;
   const int64_t base = (m / (kQlOut * ql_kind_tn(kind, tm))) * ((T + tt - 1) / tt);
@@ -1229,8 +1230,10 @@ QlLayout ql_layout(const Plan* U, const Plan* V, const brq_quant* q, int64_t T, 
                    int64_t n) {
   QlLayout L;
   L.splits = ql_splits(T, m, n, q->bits, q->group);
-  // the streaming kernel's splits hold whole chunks
-  const int unit = n % kQlChunk == 0 ? kQlChunk : q->group;
+  // the staged kernels' splits hold whole chunks
+  const int unit = ql_kind(T, m, n, q->bits, q->group, true) == kQlGemm ? kQlGemmChunk
+                   : n % kQlChunk == 0                                  ? kQlChunk
+                                                                        : q->group;
   const int64_t nu = n / unit;
   if (L.splits > nu) L.splits = (int)nu;
   L.kc = ((nu + L.splits - 1) / L.splits) * unit;
@@ -1320,7 +1323,7 @@ brq_status brq_qlinear(const brq_plan* left, const brq_plan* right, const void* 
   a.scales_ld = n / q->group;
   a.splits = L.splits;
   a.kc = L.kc;
-  a.kind = ql_kind(T, n, q->bits, q->group, reinterpret_cast<uintptr_t>(codes) % 16 == 0);
+  a.kind = ql_kind(T, m, n, q->bits, q->group, reinterpret_cast<uintptr_t>(codes) % 16 == 0);
   a.tm = ql_kind_tm(a.kind, T, q->bits, q->group);
   a.tn = ql_kind_tn(a.kind, a.tm);
   a.tv = (int)(T < kQlTok * a.tm ? T : kQlTok * a.tm);

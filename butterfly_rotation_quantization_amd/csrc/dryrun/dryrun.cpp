@@ -1036,7 +1036,7 @@ hipError_t launch_stage_lanes(const SpArgs& a, int rows_per, hipStream_t) {
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   ++g_launches;
   const int TN = a.tn;
-  if (a.kind != ql_kind(a.T, a.n, a.bits, a.group, reinterpret_cast<uintptr_t>(a.codes) % 16 == 0) ||
+  if (a.kind != ql_kind(a.T, a.m, a.n, a.bits, a.group, reinterpret_cast<uintptr_t>(a.codes) % 16 == 0) ||
       TN != ql_kind_tn(a.kind, a.tm) || a.tv != (int)std::min<int64_t>(a.T, (int64_t)kQlTok * a.tm))
     return violation("quantized linear kernel choice (kind %lld, tn %lld)", a.kind, TN), hipErrorInvalidValue;
   if (a.bits < 2 || a.bits > 5 || (a.group != 64 && a.group != 128) || a.n % a.group || a.m % (kQlOut * TN) ||
@@ -1051,31 +1051,56 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
   if (nb >= ((int64_t)1 << 31)) return violation("quantized linear grid %lld", nb, 0), hipErrorInvalidValue;
   const int NC = a.group / 4, NB = NC * a.bits / 8;
   if (a.kind != kQlDirect) {  // whole chunks per split, 16-byte rows, and the LDS the launch asks for
-    const int R = kQlOut * TN, CB = kQlChunk * a.bits / 8, PB = ql_code_pitch(a.bits);
+    const bool gemm = a.kind == kQlGemm;
+    const int CK = gemm ? kQlGemmChunk : kQlChunk;
+    const int R = kQlOut * TN, CB = CK * a.bits / 8, PB = ql_code_pitch_ck(a.bits, CK);
     const int tv = a.tv;
-    if (a.n % kQlChunk || a.kc % kQlChunk || reinterpret_cast<uintptr_t>(a.codes) % 16 || a.codes_ld % 16 ||
-        ql_lds_bytes(a.bits, a.group, R, tv) > 64 * 1024 || (a.kind == kQlStream && a.tm != 1 && a.tm != 2))
+    const size_t lds_cap = gemm ? 160 * 1024 : 64 * 1024;
+    if (a.n % CK || a.kc % CK || reinterpret_cast<uintptr_t>(a.codes) % 16 || a.codes_ld % 16 ||
+        ql_lds_bytes_ck(a.bits, a.group, R, tv, CK) > lds_cap || (a.kind == kQlStream && a.tm != 1 && a.tm != 2) ||
+        (gemm && (a.tm != kQlGemmTm || TN != kQlGemmTn || a.splits != ql_gemm_splits(a.T, a.n))))
       return violation("staged product geometry (kc %lld, ld %lld)", a.kc, a.codes_ld), hipErrorInvalidValue;
-    if (a.kind == kQlStream) {
+    if (gemm) {
+      // paired activation units: the two natural pieces and the two stored
+      // operands of each unit lie inside the chunk, and the stored operands
+      // of all units tile the chunk exactly once
+      const bool bf = a.xt == BRQ_BF16;
+      const int NC2 = a.group / 4, UT = CK / 16;
+      std::vector<int> seen(CK / 8, 0);
+      for (int u = 0; u < UT; ++u) {
+        const int n0 = ql_gemm_nat0(u, NC2, bf), n1 = ql_gemm_nat1(u, NC2, bf), o0 = ql_gemm_op0(u, NC2);
+        if (n0 < 0 || n1 + 8 > CK || o0 + 16 > CK || n0 % 8 || n1 % 8 || o0 % 8)
+          return violation("activation unit %lld at %lld", u, n0), hipErrorInvalidValue;
+        ++seen[o0 / 8];
+        ++seen[o0 / 8 + 1];
+      }
+      for (int q = 0; q < CK / 8; ++q)
+        if (seen[q] != 1) return violation("activation operand slot %lld stored %lld times", q, seen[q]), hipErrorInvalidValue;
+      if (ql_gemm_lds_bytes(a.bits, a.group, tv) > 160 * 1024)
+        return violation("gemm LDS %lld bytes", (int64_t)ql_gemm_lds_bytes(a.bits, a.group, tv), 0), hipErrorInvalidValue;
+    }
+    {
       // staged pieces per thread divide exactly; activation reads stay inside a token's chunk row
-      const int NG = kQlChunk / a.group;
-      if ((R * (CB / 16)) % kQlThreads || (R * NG) % kQlThreads || (kQlTok * a.tm * (kQlChunk / 8)) % kQlThreads)
-        return violation("stream staging pieces (rows %lld)", R, 0), hipErrorInvalidValue;
+      const int NG = CK / a.group;
+      const int NT = gemm ? kQlGemmThreads : kQlThreads;
+      if ((R * (CB / 16)) % NT || (R * NG) % NT || (kQlTok * a.tm * (CK / 8)) % NT)
+        return violation("staging pieces (rows %lld)", R, 0), hipErrorInvalidValue;
       const bool bf = a.xt == BRQ_BF16;
       for (int gi = 0; gi < NG; ++gi)
         for (int lg = 0; lg < 4; ++lg)
           for (int sp = 0; sp < NC / 16; ++sp) {
             const int64_t lo = gi * a.group + lg * NC + (bf ? 16 * sp : 8 * sp);
             const int64_t hi = lo + (bf ? 8 : NC / 2) + 8;
-            if (lo < 0 || 2 * hi > 2 * kQlChunk || (2 * lo) % 16)
+            if (lo < 0 || 2 * hi > 2 * CK || (2 * lo) % 16)
               return violation("LDS activation read at %lld (group %lld)", 2 * lo, gi), hipErrorInvalidValue;
           }
-      if ((int64_t)tv * kQlXPitch % 16 || kQlXPitch < 2 * kQlChunk)
-        return violation("LDS activation pitch %lld", kQlXPitch, 0), hipErrorInvalidValue;
+      const int XP = ql_xpitch(CK);
+      if ((int64_t)tv * XP % 16 || XP < 2 * CK)
+        return violation("LDS activation pitch %lld", XP, 0), hipErrorInvalidValue;
     }
     if (PB % 16 || ((int64_t)R * PB) % 16) return violation("LDS code pitch %lld", PB, 0), hipErrorInvalidValue;
     for (int r = 0; r < R; ++r)
-      for (int gi = 0; gi < kQlChunk / a.group; ++gi)
+      for (int gi = 0; gi < CK / a.group; ++gi)
         for (int lg = 0; lg < 4; ++lg) {
           const int off = r * PB + gi * (a.group * a.bits / 8) + lg * NB;
           if (off + NB > r * PB + CB || off % (NB % 4 == 0 ? 4 : 2))

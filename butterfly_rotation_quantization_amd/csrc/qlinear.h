@@ -59,8 +59,25 @@ struct QlArgs {
 //   most re-reads hit the caches).  The decode work per code is the limit;
 //   two tiles per workgroup (above 16 tokens, where the staging fits) halve
 //   it per token, four tiles cost too many registers.
-enum QlKind { kQlDirect = 0, kQlStream = 1 };
+// kQlGemm (64 tokens and more): 128 tokens (eight 16-token tiles) x 256
+//   weight rows per workgroup of eight waves, two per SIMD; wave w owns rows
+//   32 w .. 32 w + 31 for all 128 tokens, so each code is decoded once for
+//   128 tokens instead of 16 or 32.  Chunks of 256 inputs are staged in LDS
+//   (codes, scales, activations) with the f16 activations already paired the
+//   way the MFMA operands take them.  (tn = 4 keeps the row count per
+//   workgroup as kQlOut tn.)  Workgroups are numbered so that the eight
+//   (token tile, split) pairs of a weight row block go one to each XCD: an
+//   XCD reads one slice of X~ from memory and serves it to every row block
+//   from its L2.
+enum QlKind { kQlDirect = 0, kQlStream = 1, kQlGemm = 2 };
 constexpr int kQlStreamTn = 2;
+constexpr int kQlGemmTm = 8;
+constexpr int kQlGemmTn = 4;
+constexpr int kQlGemmChunk = 256;
+constexpr int kQlGemmMinT = 64;
+constexpr int kQlGemmThreads = 512;  // eight waves
+constexpr int kQlGemmTnw = 2;        // 16-row tiles per wave
+constexpr int kQlGemmXcds = 8;  // (token tile, split) pairs per weight row block
 
 struct QlTile {
   int64_t ct, tt, split;
@@ -75,9 +92,19 @@ __host__ __device__ inline int64_t ql_blocks(const QlArgs& a) {
   return ql_ctiles(a) * ql_ttiles(a) * a.splits;
 }
 // Output tiles run fastest: consecutive workgroups read consecutive weight rows.
+// kQlGemm: the (token tile, split) pairs run fastest, so consecutive
+// workgroups (which the dispatcher deals to the XCDs in turn) share a row
+// block and each XCD keeps one (token tile, split) pair.
 __host__ __device__ inline QlTile ql_tile(const QlArgs& a, int64_t bid) {
   QlTile t;
   const int64_t nc = ql_ctiles(a), nt = ql_ttiles(a);
+  if (a.kind == kQlGemm) {
+    const int64_t nts = nt * a.splits, r = bid % nts;
+    t.ct = bid / nts;
+    t.tt = r % nt;
+    t.split = r / nt;
+    return t;
+  }
   t.ct = bid % nc;
   const int64_t r = bid / nc;
   t.tt = r % nt;
@@ -90,22 +117,34 @@ __host__ __device__ inline int64_t ql_code_off(const QlArgs& a, int64_t o, int64
 }
 // The streaming kernel needs n a multiple of kQlChunk and 16-byte aligned codes.
 constexpr int kQlChunk = 512;
-// LDS row pitches: the chunk's code bytes plus 16 (keeps 16-byte alignment
-// and moves successive rows by four banks); a token's activations plus 16.
-__host__ __device__ inline int ql_code_pitch(int bits) { return kQlChunk * bits / 8 + 16; }
-constexpr int kQlXPitch = 2 * kQlChunk + 16;
-// LDS of a streaming launch: rows x (codes + scales of the chunk's groups), and
+// LDS row pitches for a chunk of ck inputs: the chunk's code bytes plus 16
+// (keeps 16-byte alignment and moves successive rows by four banks); a
+// token's activations plus 16.
+__host__ __device__ constexpr int ql_code_pitch_ck(int bits, int ck) { return ck * bits / 8 + 16; }
+__host__ __device__ constexpr int ql_xpitch(int ck) { return 2 * ck + 16; }
+__host__ __device__ inline int ql_code_pitch(int bits) { return ql_code_pitch_ck(bits, kQlChunk); }
+constexpr int kQlXPitch = ql_xpitch(kQlChunk);
+// LDS of a staged launch: rows x (codes + scales of the chunk's groups), and
 // tv activation rows.
+__host__ __device__ inline size_t ql_lds_bytes_ck(int bits, int group, int rows, int tv, int ck) {
+  return (size_t)rows * ql_code_pitch_ck(bits, ck) + (size_t)rows * (ck / group + 1) * 4 +
+         (size_t)tv * ql_xpitch(ck);
+}
 __host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int rows, int tv) {
-  return (size_t)rows * ql_code_pitch(bits) + (size_t)rows * (kQlChunk / group + 1) * 4 +
-         (size_t)tv * kQlXPitch;
+  return ql_lds_bytes_ck(bits, group, rows, tv, kQlChunk);
+}
+// The LDS of a kQlGemm launch (at most 115 KiB, b <= 5).
+__host__ __device__ inline size_t ql_gemm_lds_bytes(int bits, int group, int tv) {
+  return ql_lds_bytes_ck(bits, group, kQlOut * kQlGemmTn, tv, kQlGemmChunk);
 }
 // 16-token tiles per workgroup for T tokens.
 __host__ __device__ inline int ql_tm(int64_t T) { return T > kQlTok ? 4 : 1; }
 // The kernel for a shape (codes_aligned: 16-byte aligned codes), staying
 // within the 64 KiB of LDS a launch takes without an attribute (the
 // streaming kernel's staging is at most 62.75 KiB for b <= 5).
-__host__ __device__ inline int ql_kind(int64_t T, int64_t n, int bits, int group, bool codes_aligned) {
+__host__ __device__ inline int ql_kind(int64_t T, int64_t m, int64_t n, int bits, int group, bool codes_aligned) {
+  if (codes_aligned && T >= kQlGemmMinT && n % kQlGemmChunk == 0 && m % (kQlOut * kQlGemmTn) == 0)
+    return kQlGemm;
   if (n % kQlChunk || !codes_aligned) return kQlDirect;
   if (ql_lds_bytes(bits, group, kQlOut * kQlStreamTn, (int)(T < kQlTok ? T : kQlTok)) <= 64 * 1024)
     return kQlStream;
@@ -118,9 +157,49 @@ __host__ __device__ inline int ql_stream_tm(int64_t T, int bits, int group) {
              ? 2 : 1;
 }
 __host__ __device__ inline int ql_kind_tm(int kind, int64_t T, int bits, int group) {
-  return kind == kQlStream ? ql_stream_tm(T, bits, group) : ql_tm(T);
+  return kind == kQlGemm ? kQlGemmTm : kind == kQlStream ? ql_stream_tm(T, bits, group) : ql_tm(T);
 }
-__host__ __device__ inline int ql_kind_tn(int kind, int tm) { return kind == kQlStream ? kQlStreamTn : ql_tn(tm); }
+__host__ __device__ inline int ql_kind_tn(int kind, int tm) {
+  return kind == kQlGemm ? kQlGemmTn : kind == kQlStream ? kQlStreamTn : ql_tn(tm);
+}
+// Splits of a kQlGemm launch: one per XCD for each token tile (at least one),
+// at most one per chunk of inputs.
+__host__ __device__ inline int ql_gemm_splits(int64_t T, int64_t n) {
+  const int64_t tt = (T + kQlTok * kQlGemmTm - 1) / (kQlTok * kQlGemmTm);
+  int64_t s = tt >= kQlGemmXcds ? 1 : kQlGemmXcds / tt;
+  if (s > n / kQlGemmChunk) s = n / kQlGemmChunk;
+  return (int)(s < 1 ? 1 : s);
+}
+
+// kQlGemm staging.  Per chunk of CK inputs: R rows of codes (16-byte pieces)
+// and scales (times 1/L), and the activations of up to 128 tokens in 16-byte
+// pieces taken two at a time: the pieces whose inputs ql_group_tile's MFMA
+// operands pair up are loaded by one thread and stored in operand order, so
+// that each operand is one 16-byte LDS read.  A lane's NC inputs of a group
+// form a block; within it, slot pair sp covers 16 inputs, stored as operand
+// s2 = 0 then s2 = 1.  f16: operand s2 word i holds inputs (8 sp + 4 s2 + i',
+// 8 sp + 4 s2 + i' + NC/2) for i' = 2i, 2i + 1 (as ql_group_tile's perms make
+// them); bf16: inputs 16 sp .. 16 sp + 15 in order.
+// Input offsets (within the chunk) of unit u's two natural pieces, and of
+// its two stored operands (nc = G/4 inputs per lane block).
+__host__ __device__ constexpr int ql_gemm_nat0(int u, int nc, bool bf) {
+  return (u / (nc / 16)) * nc + (bf ? 16 : 8) * (u % (nc / 16));
+}
+__host__ __device__ constexpr int ql_gemm_nat1(int u, int nc, bool bf) { return ql_gemm_nat0(u, nc, bf) + (bf ? 8 : nc / 2); }
+__host__ __device__ constexpr int ql_gemm_op0(int u, int nc) { return (u / (nc / 16)) * nc + 16 * (u % (nc / 16)); }
+template <int BITS, int G, bool BF>
+struct QlGemmPieces {
+  static constexpr int R = kQlOut * kQlGemmTn, CK = kQlGemmChunk, NT = kQlGemmThreads;
+  static constexpr int CB = CK * BITS / 8, NG = CK / G, NC = G / 4;
+  static constexpr int UT = CK / 16;  // 16-input units per token
+  static constexpr int NCP = R * (CB / 16) / NT, NSP = R * NG / NT;
+  static constexpr int NXU = kQlTok * kQlGemmTm * UT / NT;  // units per thread
+  static_assert(NCP * NT == R * (CB / 16) && NSP * NT == R * NG && NXU * NT == kQlTok * kQlGemmTm * UT,
+                "staging pieces must divide among the threads");
+  __host__ __device__ static constexpr int nat0(int u) { return ql_gemm_nat0(u, NC, BF); }
+  __host__ __device__ static constexpr int nat1(int u) { return ql_gemm_nat1(u, NC, BF); }
+  __host__ __device__ static constexpr int op0(int u) { return ql_gemm_op0(u, NC); }
+};
 
 hipError_t launch_qlinear(const QlArgs& a, hipStream_t s);
 // Z[t][o] = sum over splits of part[s][t][o], into out (type ot, leading dimension ldo).

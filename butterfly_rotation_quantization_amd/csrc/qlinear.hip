@@ -300,18 +300,18 @@ struct QlStage {
   int64_t ldx;
   int tv;
 };
-template <int BITS, int G, int R, int TM>
+template <int BITS, int G, int R, int TM, int CK = kQlChunk>
 struct QlPieces {
-  static constexpr int CB = kQlChunk * BITS / 8, NG = kQlChunk / G, XQ = kQlChunk / 8;
+  static constexpr int CB = CK * BITS / 8, NG = CK / G, XQ = CK / 8;
   static constexpr int NCP = R * (CB / 16) / kQlThreads, NSP = R * NG / kQlThreads;
   static constexpr int NXP = kQlTok * TM * XQ / kQlThreads;
 };
 
-template <int BITS, int G, int R, int TM>
-__device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pcod)[QlPieces<BITS, G, R, TM>::NCP],
-                                         float (&psc)[QlPieces<BITS, G, R, TM>::NSP],
-                                         u4v (&px)[QlPieces<BITS, G, R, TM>::NXP]) {
-  using P = QlPieces<BITS, G, R, TM>;
+template <int BITS, int G, int R, int TM, int CK = kQlChunk>
+__device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pcod)[QlPieces<BITS, G, R, TM, CK>::NCP],
+                                         float (&psc)[QlPieces<BITS, G, R, TM, CK>::NSP],
+                                         u4v (&px)[QlPieces<BITS, G, R, TM, CK>::NXP]) {
+  using P = QlPieces<BITS, G, R, TM, CK>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < P::NCP; ++i) {
@@ -330,12 +330,12 @@ __device__ __forceinline__ void ql_fetch(const QlStage& st, int64_t k0, u4v (&pc
   }
 }
 
-template <int BITS, int G, int R, int TM>
+template <int BITS, int G, int R, int TM, int CK = kQlChunk>
 __device__ __forceinline__ void ql_stash(int tv, float invL, uint8_t* lcodes, float* lscales, uint8_t* lx,
-                                         const u4v (&pcod)[QlPieces<BITS, G, R, TM>::NCP],
-                                         const float (&psc)[QlPieces<BITS, G, R, TM>::NSP],
-                                         const u4v (&px)[QlPieces<BITS, G, R, TM>::NXP]) {
-  using P = QlPieces<BITS, G, R, TM>;
+                                         const u4v (&pcod)[QlPieces<BITS, G, R, TM, CK>::NCP],
+                                         const float (&psc)[QlPieces<BITS, G, R, TM, CK>::NSP],
+                                         const u4v (&px)[QlPieces<BITS, G, R, TM, CK>::NXP]) {
+  using P = QlPieces<BITS, G, R, TM, CK>;
   constexpr int PB = P::CB + 16, PS = P::NG + 1;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -351,7 +351,7 @@ __device__ __forceinline__ void ql_stash(int tv, float invL, uint8_t* lcodes, fl
 #pragma unroll
   for (int i = 0; i < P::NXP; ++i) {
     const int e = tid + i * kQlThreads, tk = e / P::XQ, q = e - tk * P::XQ;
-    if (tk < tv) *reinterpret_cast<u4v*>(lx + tk * kQlXPitch + 16 * q) = px[i];
+    if (tk < tv) *reinterpret_cast<u4v*>(lx + tk * ql_xpitch(CK) + 16 * q) = px[i];
   }
 }
 
@@ -456,6 +456,187 @@ __global__ __launch_bounds__(kQlThreads) void qlinear_stream_kernel(QlArgs a) {
     }
 }
 
+template <int BITS, int G, bool BF>
+__device__ __forceinline__ void ql_gemm_fetch(const QlStage& st, int64_t k0,
+                                              u4v (&pcod)[QlGemmPieces<BITS, G, BF>::NCP],
+                                              float (&psc)[QlGemmPieces<BITS, G, BF>::NSP],
+                                              u4v (&px)[2 * QlGemmPieces<BITS, G, BF>::NXU]) {
+  using P = QlGemmPieces<BITS, G, BF>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < P::NCP; ++i) {
+    const int e = tid + i * P::NT, r = e / (P::CB / 16), q = e - r * (P::CB / 16);
+    pcod[i] = *reinterpret_cast<const u4v*>(st.codes + r * st.codes_ld + k0 * BITS / 8 + 16 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < P::NSP; ++i) {
+    const int e = tid + i * P::NT, r = e / P::NG, gq = e - r * P::NG;
+    psc[i] = st.scales[r * st.scales_ld + k0 / G + gq];
+  }
+#pragma unroll
+  for (int i = 0; i < P::NXU; ++i) {
+    const int e = tid + i * P::NT, tk = e / P::UT, u = e - tk * P::UT;
+    const uint16_t* xr = st.x + tk * st.ldx + k0;
+    px[2 * i] = tk < st.tv ? *reinterpret_cast<const u4v*>(xr + P::nat0(u)) : u4v{0u, 0u, 0u, 0u};
+    px[2 * i + 1] = tk < st.tv ? *reinterpret_cast<const u4v*>(xr + P::nat1(u)) : u4v{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int BITS, int G, bool BF>
+__device__ __forceinline__ void ql_gemm_stash(int tv, float invL, uint8_t* lcodes, float* lscales, uint8_t* lx,
+                                              const u4v (&pcod)[QlGemmPieces<BITS, G, BF>::NCP],
+                                              const float (&psc)[QlGemmPieces<BITS, G, BF>::NSP],
+                                              const u4v (&px)[2 * QlGemmPieces<BITS, G, BF>::NXU]) {
+  using P = QlGemmPieces<BITS, G, BF>;
+  constexpr int PB = P::CB + 16, PS = P::NG + 1, XP = ql_xpitch(P::CK);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < P::NCP; ++i) {
+    const int e = tid + i * P::NT, r = e / (P::CB / 16), q = e - r * (P::CB / 16);
+    *reinterpret_cast<u4v*>(lcodes + r * PB + 16 * q) = pcod[i];
+  }
+#pragma unroll
+  for (int i = 0; i < P::NSP; ++i) {
+    const int e = tid + i * P::NT, r = e / P::NG, gq = e - r * P::NG;
+    lscales[r * PS + gq] = psc[i] * invL;
+  }
+#pragma unroll
+  for (int i = 0; i < P::NXU; ++i) {
+    const int e = tid + i * P::NT, tk = e / P::UT, u = e - tk * P::UT;
+    if (tk < tv) {
+      uint16_t* xr = reinterpret_cast<uint16_t*>(lx + tk * XP) + P::op0(u);
+      const u4v a = px[2 * i], c = px[2 * i + 1];
+      if constexpr (BF) {
+        *reinterpret_cast<u4v*>(xr) = a;
+        *reinterpret_cast<u4v*>(xr + 8) = c;
+      } else {
+        *reinterpret_cast<u4v*>(xr) =
+            u4v{__builtin_amdgcn_perm(c.x, a.x, 0x05040100u), __builtin_amdgcn_perm(c.x, a.x, 0x07060302u),
+                __builtin_amdgcn_perm(c.y, a.y, 0x05040100u), __builtin_amdgcn_perm(c.y, a.y, 0x07060302u)};
+        *reinterpret_cast<u4v*>(xr + 8) =
+            u4v{__builtin_amdgcn_perm(c.z, a.z, 0x05040100u), __builtin_amdgcn_perm(c.z, a.z, 0x07060302u),
+                __builtin_amdgcn_perm(c.w, a.w, 0x05040100u), __builtin_amdgcn_perm(c.w, a.w, 0x07060302u)};
+      }
+    }
+  }
+}
+
+// The products of one group for one 16-token tile from the paired operands
+// in LDS and weight operands already decoded (pr, as ql_group makes them):
+// d[tn] = sum over the group's inputs of the activations times 2q - L.
+template <bool BF, int G, int TN>
+__device__ __forceinline__ void ql_gemm_tile(f4v (&d)[TN], const uint32_t (&pr)[TN][G / 8], const uint16_t* xrow,
+                                             bool tok_ok) {
+  constexpr int NC = G / 4;
+  using V8 = typename std::conditional<BF, b8v, h8v>::type;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) d[tn] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < NC / 16; ++sp) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint4 r = tok_ok ? *reinterpret_cast<const uint4*>(xrow + 16 * sp + 8 * s2) : make_uint4(0u, 0u, 0u, 0u);
+      const V8 av = __builtin_bit_cast(V8, r);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int p0 = 8 * sp + 4 * s2;
+        const V8 bv = __builtin_bit_cast(V8, make_uint4(pr[tn][p0], pr[tn][p0 + 1], pr[tn][p0 + 2], pr[tn][p0 + 3]));
+        if constexpr (BF) d[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, d[tn], 0, 0, 0);
+        else d[tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, d[tn], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// kQlGemm kernel.  Per group a wave decodes its two weight operands once and
+// runs them against the eight token tiles; the next chunk is loaded into
+// registers while the current one is multiplied.  The arithmetic per output
+// is the streaming kernel's: each group's MFMA sum times alpha / L, added in
+// group order.
+template <int BITS, bool BF, int G>
+__global__ __launch_bounds__(kQlGemmThreads, 1) void qlinear_gemm_kernel(QlArgs a) {
+  using P = QlGemmPieces<BITS, G, BF>;
+  constexpr int TM = kQlGemmTm, TN = kQlGemmTnw, CK = kQlGemmChunk, R = P::R;
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int NC = G / 4;
+  constexpr int NW = (NC * BITS + 31) / 32;
+  constexpr int PB = P::CB + 16, PS = P::NG + 1, XP = ql_xpitch(CK);
+  extern __shared__ __align__(16) uint8_t ql_lds[];
+  uint8_t* lcodes = ql_lds;
+  float* lscales = reinterpret_cast<float*>(ql_lds + R * PB);
+  uint8_t* lx = ql_lds + R * PB + R * PS * 4;
+  const QlTile t = ql_tile(a, blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t row0 = t.ct * (int64_t)R;
+  const int lrow0 = 16 * TN * w + lr;  // + 16 tn
+  const int64_t tok0 = t.tt * (int64_t)(kQlTok * TM);
+  const int tv = (int)(a.T - tok0 < kQlTok * TM ? a.T - tok0 : kQlTok * TM);
+  const int64_t k_beg = t.split * a.kc;
+  const int64_t k_end = k_beg + a.kc < a.n ? k_beg + a.kc : a.n;
+  const float invL = 1.0f / (float)L;
+  u4v pcod[P::NCP];
+  float psc[P::NSP];
+  u4v px[2 * P::NXU];
+  const QlStage st{a.codes + row0 * a.codes_ld, a.codes_ld, a.scales + row0 * a.scales_ld, a.scales_ld,
+                   static_cast<const uint16_t*>(a.x) + tok0 * a.ldx, a.ldx, tv};
+  f4v acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f4v{0.f, 0.f, 0.f, 0.f};
+  ql_gemm_fetch<BITS, G, BF>(st, k_beg, pcod, psc, px);  // k_end - k_beg is a positive multiple of CK
+  for (int64_t k0 = k_beg; k0 < k_end; k0 += CK) {
+    __syncthreads();  // the previous chunk's reads are done
+    ql_gemm_stash<BITS, G, BF>(tv, invL, lcodes, lscales, lx, pcod, psc, px);
+    __syncthreads();
+    if (k0 + CK < k_end) ql_gemm_fetch<BITS, G, BF>(st, k0 + CK, pcod, psc, px);
+#pragma unroll 1
+    for (int gi = 0; gi < P::NG; ++gi) {
+      uint32_t pr[TN][NC / 2];
+      float sc[TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        uint32_t wds[NW];
+        const uint8_t* cp = lcodes + (lrow0 + 16 * tn) * PB + gi * (G * BITS / 8) + lg * (NC * BITS / 8);
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          if constexpr ((NC * BITS / 8) % 4 == 0) {
+            wds[q] = reinterpret_cast<const uint32_t*>(cp)[q];
+          } else {  // 2-byte aligned pieces
+            const uint16_t* hp = reinterpret_cast<const uint16_t*>(cp);
+            const int h0 = 2 * q;
+            wds[q] = (uint32_t)hp[h0] | (h0 + 1 < NC * BITS / 16 ? (uint32_t)hp[h0 + 1] << 16 : 0u);
+          }
+        }
+        if constexpr (BF) ql_bf16_pairs<BITS, NC, true>(wds, pr[tn], std::make_integer_sequence<int, NC / 2>{});
+        else ql_f16_pairs<BITS, NC, true>(wds, pr[tn], std::make_integer_sequence<int, NC / 2>{});
+        sc[tn] = lscales[(lrow0 + 16 * tn) * PS + gi];
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const uint16_t* xrow = reinterpret_cast<const uint16_t*>(lx + (16 * tm + lr) * XP) + gi * G + lg * NC;
+        f4v d[TN];
+        ql_gemm_tile<BF, G, TN>(d, pr, xrow, 16 * tm + lr < tv);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tm][tn][i] = fmaf(d[tn][i], sc[tn], acc[tm][tn][i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 16 * tm + 4 * lg + i;
+      if (tk < tv)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          a.part[((int64_t)t.split * a.T + tok0 + tk) * a.m + row0 + lrow0 + 16 * tn] = acc[tm][tn][i];
+    }
+}
+
 __global__ void ql_reduce_kernel(const float* part, int splits, int64_t T, int64_t m, void* out,
                                  int ot, int64_t ldo) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -490,7 +671,18 @@ __global__ void ql_reduce_kernel(const float* part, int splits, int64_t T, int64
 template <int BITS, bool BF, int G>
 hipError_t launch_g(const QlArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)ql_blocks(a));
-  if (a.kind == kQlStream) {
+  if (a.kind == kQlGemm) {
+    static bool attr = false;  // more than 64 KiB of LDS needs the opt-in
+    if (!attr) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlinear_gemm_kernel<BITS, BF, G>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)ql_gemm_lds_bytes(BITS, G, kQlTok * kQlGemmTm));
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL((qlinear_gemm_kernel<BITS, BF, G>), grid, dim3(kQlGemmThreads), ql_gemm_lds_bytes(BITS, G, a.tv),
+                       s, a);
+  } else if (a.kind == kQlStream) {
     const size_t lds = ql_lds_bytes(BITS, G, kQlOut * kQlStreamTn, a.tv);
     if (a.tm == 2)
       hipLaunchKernelGGL((qlinear_stream_kernel<BITS, BF, G, 2, kQlStreamTn, false>), grid, dim3(kQlThreads), lds, s, a);
