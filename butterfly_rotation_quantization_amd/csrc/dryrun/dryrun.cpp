@@ -1076,8 +1076,9 @@ hipError_t launch_qlinear(const QlArgs& a, hipStream_t) {
       }
       for (int q = 0; q < CK / 8; ++q)
         if (seen[q] != 1) return violation("activation operand slot %lld stored %lld times", q, seen[q]), hipErrorInvalidValue;
-      if (ql_gemm_lds_bytes(a.bits, a.group, tv) > 160 * 1024)
-        return violation("gemm LDS %lld bytes", (int64_t)ql_gemm_lds_bytes(a.bits, a.group, tv), 0), hipErrorInvalidValue;
+      if (ql_gemm_lds_bytes(a.bits, a.group, kQlTok * kQlGemmTm) > 160 * 1024)
+        return violation("gemm LDS %lld bytes", (int64_t)ql_gemm_lds_bytes(a.bits, a.group, kQlTok * kQlGemmTm), 0),
+               hipErrorInvalidValue;
     }
     {
       // staged pieces per thread divide exactly; activation reads stay inside a token's chunk row

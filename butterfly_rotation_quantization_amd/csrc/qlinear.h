@@ -133,7 +133,8 @@ __host__ __device__ inline size_t ql_lds_bytes_ck(int bits, int group, int rows,
 __host__ __device__ inline size_t ql_lds_bytes(int bits, int group, int rows, int tv) {
   return ql_lds_bytes_ck(bits, group, rows, tv, kQlChunk);
 }
-// The LDS of a kQlGemm launch (at most 115 KiB, b <= 5).
+// The LDS of a kQlGemm launch (at most 115 KiB, b <= 5); the launch takes
+// all 128 token rows (rows past the last token hold zeros).
 __host__ __device__ inline size_t ql_gemm_lds_bytes(int bits, int group, int tv) {
   return ql_lds_bytes_ck(bits, group, kQlOut * kQlGemmTn, tv, kQlGemmChunk);
 }

@@ -502,8 +502,10 @@ __device__ __forceinline__ void ql_gemm_stash(int tv, float invL, uint8_t* lcode
   }
 #pragma unroll
   for (int i = 0; i < P::NXU; ++i) {
+    // every token row is written (rows past the last token with the zeros
+    // the fetch left there), so the products read them unguarded
     const int e = tid + i * P::NT, tk = e / P::UT, u = e - tk * P::UT;
-    if (tk < tv) {
+    {
       uint16_t* xr = reinterpret_cast<uint16_t*>(lx + tk * XP) + P::op0(u);
       const u4v a = px[2 * i], c = px[2 * i + 1];
       if constexpr (BF) {
@@ -521,12 +523,11 @@ __device__ __forceinline__ void ql_gemm_stash(int tv, float invL, uint8_t* lcode
   }
 }
 
-// The products of one group for one 16-token tile from the paired operands
-// in LDS and weight operands already decoded (pr, as ql_group makes them):
-// d[tn] = sum over the group's inputs of the activations times 2q - L.
+// The products of one group for one 16-token tile: d[tn] = sum over the
+// group's inputs of the activations (the tile's paired operands xo, two per
+// 16 inputs) times the decoded weight operands pr (as ql_group makes them).
 template <bool BF, int G, int TN>
-__device__ __forceinline__ void ql_gemm_tile(f4v (&d)[TN], const uint32_t (&pr)[TN][G / 8], const uint16_t* xrow,
-                                             bool tok_ok) {
+__device__ __forceinline__ void ql_gemm_tile(f4v (&d)[TN], const uint32_t (&pr)[TN][G / 8], const uint4 (&xo)[G / 32]) {
   constexpr int NC = G / 4;
   using V8 = typename std::conditional<BF, b8v, h8v>::type;
 #pragma unroll
@@ -535,8 +536,7 @@ __device__ __forceinline__ void ql_gemm_tile(f4v (&d)[TN], const uint32_t (&pr)[
   for (int sp = 0; sp < NC / 16; ++sp) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const uint4 r = tok_ok ? *reinterpret_cast<const uint4*>(xrow + 16 * sp + 8 * s2) : make_uint4(0u, 0u, 0u, 0u);
-      const V8 av = __builtin_bit_cast(V8, r);
+      const V8 av = __builtin_bit_cast(V8, xo[2 * sp + s2]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const int p0 = 8 * sp + 4 * s2;
@@ -546,6 +546,13 @@ __device__ __forceinline__ void ql_gemm_tile(f4v (&d)[TN], const uint32_t (&pr)[
       }
     }
   }
+}
+
+// A token tile's paired operands of one group: G/32 16-byte LDS reads.
+template <int G>
+__device__ __forceinline__ void ql_gemm_operands(uint4 (&xo)[G / 32], const uint16_t* xrow) {
+#pragma unroll
+  for (int j = 0; j < G / 32; ++j) xo[j] = *reinterpret_cast<const uint4*>(xrow + 8 * j);
 }
 
 // kQlGemm kernel.  Per group a wave decodes its two weight operands once and
@@ -613,16 +620,34 @@ __global__ __launch_bounds__(kQlGemmThreads, 1) void qlinear_gemm_kernel(QlArgs 
         else ql_f16_pairs<BITS, NC, true>(wds, pr[tn], std::make_integer_sequence<int, NC / 2>{});
         sc[tn] = lscales[(lrow0 + 16 * tn) * PS + gi];
       }
+      // token tile tm's operands are read while tile tm - 1 is multiplied,
+      // and tile tm - 1's sums are scaled after tile tm's products are
+      // issued; the scheduling fences keep that order (left to itself the
+      // compiler reuses one operand register for every read and waits on each)
+      const uint16_t* xrow0 = reinterpret_cast<const uint16_t*>(lx + lr * XP) + gi * G + lg * NC;
+      uint4 xo[G / 32], xn[G / 32];
+      ql_gemm_operands<G>(xo, xrow0);
+      f4v dp[TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        const uint16_t* xrow = reinterpret_cast<const uint16_t*>(lx + (16 * tm + lr) * XP) + gi * G + lg * NC;
+        if (tm + 1 < TM) ql_gemm_operands<G>(xn, xrow0 + (tm + 1) * (16 * XP / 2));
         f4v d[TN];
-        ql_gemm_tile<BF, G, TN>(d, pr, xrow, 16 * tm + lr < tv);
+        ql_gemm_tile<BF, G, TN>(d, pr, xo);
+        if (tm > 0)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
+          for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tm][tn][i] = fmaf(d[tn][i], sc[tn], acc[tm][tn][i]);
+            for (int i = 0; i < 4; ++i) acc[tm - 1][tn][i] = fmaf(dp[tn][i], sc[tn], acc[tm - 1][tn][i]);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) dp[tn] = d[tn];
+#pragma unroll
+        for (int j = 0; j < G / 32; ++j) xo[j] = xn[j];
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[TM - 1][tn][i] = fmaf(dp[tn][i], sc[tn], acc[TM - 1][tn][i]);
     }
   }
 #pragma unroll
@@ -680,7 +705,8 @@ hipError_t launch_g(const QlArgs& a, hipStream_t s) {
       if (e != hipSuccess) return e;
       attr = true;
     }
-    hipLaunchKernelGGL((qlinear_gemm_kernel<BITS, BF, G>), grid, dim3(kQlGemmThreads), ql_gemm_lds_bytes(BITS, G, a.tv),
+    hipLaunchKernelGGL((qlinear_gemm_kernel<BITS, BF, G>), grid, dim3(kQlGemmThreads),
+                       ql_gemm_lds_bytes(BITS, G, kQlTok * kQlGemmTm),
                        s, a);
   } else if (a.kind == kQlStream) {
     const size_t lds = ql_lds_bytes(BITS, G, kQlOut * kQlStreamTn, a.tv);
