@@ -190,8 +190,10 @@ hipError_t fused_prepare(Plan& p, const float* host_blocks, const int8_t* host_s
 
 namespace {
 
-// Persistent pass B: one workgroup per compute unit (its LDS use allows no
-// more), capped by the tile count.
+// Persistent pass B: at most one workgroup per compute unit (its LDS use
+// allows no more), and as few as take the tiles in the same number of rounds
+// (688 tiles: 230 workgroups of three tiles, not 256 of which 176 take a
+// third), so the rounds run with fewer workgroups competing for memory.
 int fused_b_grid(const FusedBArgs& b) {
   static int cus = 0;
   if (!cus) {
@@ -200,7 +202,8 @@ int fused_b_grid(const FusedBArgs& b) {
       cus = 256;
   }
   const int64_t nt = fb_nwg(b);
-  return (int)(nt < cus ? nt : cus);
+  const int64_t rounds = (nt + cus - 1) / cus;
+  return (int)((nt + rounds - 1) / rounds);
 }
 
 const char* check_b(const FusedBArgs& b);

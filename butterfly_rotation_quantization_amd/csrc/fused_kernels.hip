@@ -415,6 +415,9 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
   }
   const bool live = stat > 0.f;  // a zero group codes as all zeros
   const float k = live ? (QK == BRQ_ABSMAX ? a.h / stat : a.sqrt_g / stat) : 0.f;
+  // absmax: a zero group takes k = 0 and offset 0, so its codes come out 0
+  // without a select per code
+  const float off = live ? a.h : 0.f;
   uint32_t words[BITS];
 #pragma unroll
   for (int j = 0; j < BITS; ++j) words[j] = 0u;
@@ -427,14 +430,14 @@ __device__ __forceinline__ void fb_quantize(const FusedBArgs& a, const FbTile& t
       if (QK == BRQ_ABSMAX) {
         // |v| <= stat and k = RN(h / stat) keep v k + h within
         // [-h 2^-24, 2h (1 + 2^-24)], which rounds into [0, LV]: no clamp
-        c = (int)__builtin_rintf(fmaf(v[i], k, a.h));
+        c = (int)__builtin_rintf(fmaf(v[i], k, off));
       } else {
         const float z = v[i] * k;
         c = 0;
 #pragma unroll
         for (int q = 0; q < LV; ++q) c += (z > a.tau[q]) ? 1 : 0;
       }
-      c = live ? c : 0;
+      if (QK != BRQ_ABSMAX) c = live ? c : 0;
       const int bit = (4 * f + i) * BITS, wi = bit >> 5, sh = bit & 31;
       words[wi] |= (uint32_t)c << sh;
       if (sh + BITS > 32) words[wi + 1] |= (uint32_t)c >> (32 - sh);
