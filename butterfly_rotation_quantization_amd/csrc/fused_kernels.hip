@@ -128,6 +128,19 @@ __device__ __forceinline__ void fa_unpack(uint2 x, float (&v)[PPW]) {
   }
 }
 
+// The two 16-bit inputs of word w times 2^ks, as an f16 pair (the slab scale
+// makes 16-bit inputs exact f16 values, so this is the operand the products
+// take).
+template <int WT>
+__device__ __forceinline__ uint32_t fa_scaled_pair(uint32_t w, int ks) {
+  const float a = WT == BRQ_BF16 ? cvt_bf16(w, 0) : cvt_f16(w, 0);
+  const float b = WT == BRQ_BF16 ? cvt_bf16(w, 1) : cvt_f16(w, 1);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const h2 r = __builtin_convertvector((f2{__builtin_ldexpf(a, ks), __builtin_ldexpf(b, ks)}), h2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Largest magnitude among the thread's slab items, as the bit pattern of a
 // float32 (integer order equals magnitude order for finite values).
 template <int WT, int KI>
@@ -154,11 +167,13 @@ __device__ __forceinline__ uint32_t fa_items_absmax(const uint4 (&raw)[KI]) {
 }
 
 // The signs of both sides are folded into the stage-0 blocks at plan time, so
-// the input is used as stored.  Per q: slab in (barrier), V_0 on MFMA for all
-// output tiles at once (chunk by chunk of 16 columns c0, each slab value read
-// and converted once), U_0 per output tile with the results into the output
-// area (barrier), output area to global; the next slab is loaded into
-// registers while the products run.  Loads and stores take one column c0 per
+// the input is used as stored.  Per q: slab in (barrier; with 16-bit inputs
+// and more than one V_0 output tile, first the maxima (barrier), then the
+// slab scaled and converted to f16 on its way into LDS), V_0 on MFMA output
+// tile by output tile (chunk by chunk of 16 columns c0, the slab values read
+// for each), U_0 per output tile with the results into the output area
+// (barrier), output area to global; the next slab is loaded into registers
+// while the products run.  Loads and stores take one column c0 per
 // wave instruction, so a lane's address is one loop-invariant register plus
 // wave-uniform terms.
 template <int ST, int WT, int RU>
@@ -171,6 +186,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
   constexpr int IPR = P * ESZ / 16;
   constexpr int KI = fa_ki(WT, ST, RU);  // slab load instructions per wave
   constexpr int KQ = fa_kq_nt(WT, ST, RU);  // output store instructions per wave and 16 columns
+  constexpr bool PRE = WT != BRQ_F32 && NB > 1;  // the slab holds scaled f16 operands
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -241,22 +257,35 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
       }
       if (lane == 0) smax[w] = mx;
     }
+    auto slab_scale = [&]() {
+      uint32_t m = smax[0];
+#pragma unroll
+      for (int i = 1; i < kFaWaves; ++i) m = smax[i] > m ? smax[i] : m;
+      return __builtin_amdgcn_readfirstlane(fa_scale_shift(m));
+    };
+    int ks = 0;
     const int ls = opaque(lane);
+    // With several V_0 output tiles (radix above 16), 16-bit inputs go into
+    // the slab already scaled and converted to f16, once, at the cost of a
+    // barrier (the products read them for every output tile); otherwise, and
+    // for float32 inputs, as loaded (converted, or split, where read)
+    if constexpr (PRE) {
+      __syncthreads();  // maxima complete
+      ks = slab_scale();
+    }
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
       const FaSlot x = fa_slot(IPR, w, k, ls, bv, 0, RU);
       uint8_t* d = slab + fa_slab_item(g, x.r0, x.c0, ls % IPR);
-      *reinterpret_cast<uint2*>(d) = make_uint2(raw[k].x, raw[k].y);
-      *reinterpret_cast<uint2*>(d + 8) = make_uint2(raw[k].z, raw[k].w);
+      uint4 v = raw[k];
+      if constexpr (PRE)
+        v = make_uint4(fa_scaled_pair<WT>(v.x, ks), fa_scaled_pair<WT>(v.y, ks), fa_scaled_pair<WT>(v.z, ks),
+                       fa_scaled_pair<WT>(v.w, ks));
+      *reinterpret_cast<uint2*>(d) = make_uint2(v.x, v.y);
+      *reinterpret_cast<uint2*>(d + 8) = make_uint2(v.z, v.w);
     }
-    __syncthreads();  // slab and maxima complete
-    int ks;
-    {
-      uint32_t m = smax[0];
-#pragma unroll
-      for (int i = 1; i < kFaWaves; ++i) m = smax[i] > m ? smax[i] : m;
-      ks = __builtin_amdgcn_readfirstlane(fa_scale_shift(m));
-    }
+    __syncthreads();  // slab (and, unless converted on the way in, maxima) complete
+    if constexpr (!PRE) ks = slab_scale();
     u4 bhh[MT][MT], bll[MT][MT];
 #pragma unroll
     for (int ot = 0; ot < MT; ++ot)
@@ -285,6 +314,28 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void fused_a_kernel(FusedAArgs a)
         const uint8_t* arow = slab + fa_slab_read(g, 16 * mt + lr, 0, w);
 #pragma unroll
         for (int ch = 0; ch < NB; ++ch) {
+          if constexpr (PRE) {
+            // the lane's f16 operands x[r0][c0 = 16 ch + 4 lg + i] of its PPW
+            // p: word j / 2 of read i holds p j in half j % 2
+            uint2 rd[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c0 = 16 * ch + 4 * lg + i;
+              const bool live = ch + 1 < NB || c0 < bv;
+              rd[i] = fa_aread<WT, PPW>(arow + (live ? c0 : bv - 1) * g.rsb);
+              if (!live) rd[i] = make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int j = 0; j < PPW; ++j) {
+              const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+              const uint32_t w0 = __builtin_amdgcn_perm(j < 2 ? rd[1].x : rd[1].y, j < 2 ? rd[0].x : rd[0].y, sel);
+              const uint32_t w1 = __builtin_amdgcn_perm(j < 2 ? rd[3].x : rd[3].y, j < 2 ? rd[2].x : rd[2].y, sel);
+              const h4 hi = __builtin_bit_cast(h4, make_uint2(w0, w1));
+              d[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(hi, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                                __builtin_bit_cast(h8, vb[j][nt][ch]), d[j][mt], 0, 0, 0);
+            }
+            continue;
+          }
           float xv[4][PPW];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
