@@ -681,6 +681,10 @@ hipError_t launch_stage(const SpArgs& a, hipStream_t) {
     return violation("stage pass leading dimension (%lld < %lld)", std::min(a.ld_src, a.ld_dst), cols), hipErrorInvalidValue;
   const int64_t nblocks = sp_blocks(a);
   if (nblocks >= ((int64_t)1 << 31)) return violation("stage pass grid (%lld blocks)", nblocks, 0), hipErrorInvalidValue;
+  // a source of several parts: right side, float32, parts no closer than one
+  // whole source apart (every read of part p is the part-0 read plus p strides)
+  if (a.nparts > 1 && (a.side != 0 || a.src_t != BRQ_F32 || a.part_stride < rows * a.ld_src))
+    return violation("stage pass parts (%lld parts, stride %lld)", a.nparts, a.part_stride), hipErrorInvalidValue;
   const int64_t blk_floats = a.mode == BRQ_PER_GROUP ? a.ngc * b * b : (int64_t)b * b;
   const int TL = sp_tl(a);
   const int kLds = a.side ? kSpBufFloats : TL * kSpLineFloats;

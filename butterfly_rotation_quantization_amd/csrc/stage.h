@@ -70,6 +70,12 @@ struct SpArgs {
   // workgroups, each lighter); the left side always takes kSpLines
   int tile_lines;
   const float* blk2;  // its blocks ([group][j][k] over the chunk's d / b2 groups, or one)
+  // right side, float32 source: the source is the sum of nparts arrays
+  // part_stride elements apart (split partial sums of a product), added part
+  // by part into four running sums, part p into sum p mod 4, then (s0 + s1) +
+  // (s2 + s3); nparts 0 or 1: one array
+  int nparts;
+  int64_t part_stride;
 };
 
 // Float offset of row j2 of the second stage's block for local group g2 of
@@ -322,9 +328,12 @@ hipError_t launch_stage_pair2(const P2Args& a, hipStream_t s);
 // Stages [t_begin, t_end) of the plan only (t_end = -1: to the last), in
 // forward order (inverse: the same range, transposed, last stage first); the
 // signs go with stage 0, so a range that starts later applies none.
+// nparts > 1 (right side, float32 x): x is nparts arrays part_stride elements
+// apart whose sum is the input (SpArgs::nparts); only when the first launch
+// is the tile kernel, else BRQ_ERR_UNSUPPORTED before anything is launched.
 brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, int t_end,
                             const void* x, int xt, int64_t ldx, void* y, int yt, int64_t ldy,
                             int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t s,
-                            hipError_t* herr);
+                            hipError_t* herr, int nparts = 1, int64_t part_stride = 0);
 
 }  // namespace brq

@@ -137,8 +137,10 @@ brq_status sp_rotate(const Plan* p, int side, int inverse, const void* x, int xt
 brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, int t_end,
                             const void* x, int xt, int64_t ldx, void* y, int yt, int64_t ldy,
                             int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t s,
-                            hipError_t* herr) {
+                            hipError_t* herr, int nparts, int64_t part_stride) {
   *herr = hipSuccess;
+  const bool parts = nparts > 1;
+  if (parts && (side != 0 || xt != BRQ_F32 || part_stride < rows * ldx)) return BRQ_ERR_UNSUPPORTED;
   StageList L = stages_of(p);
   if (t_end < 0) t_end = L.n;
   if (t_begin < 0 || t_end > L.n || t_begin >= t_end) return BRQ_ERR_UNSUPPORTED;
@@ -172,6 +174,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
       const int to = si < sn ? si : sn, ti = si < sn ? sn : si;  // outer (larger stride), inner
       const bool pair16 = L.b[to] == 16 && L.b[ti] == 16 && L.S[to] == 16 && L.S[ti] == 1;
       if (!pair16 && L.b[to] <= 16 && L.b[ti] <= 16 && L.b[to] * L.b[ti] <= 256) {
+        if (parts && i == 0) return BRQ_ERR_UNSUPPORTED;  // the pair kernel reads one array
         P2Args q;
         std::memset(&q, 0, sizeof q);
         q.bo = L.b[to];
@@ -260,8 +263,13 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
     a.dst = last ? y : mid;
     a.dst_t = last ? yt : BRQ_F32;
     a.ld_dst = last ? ldy : ldm;
-    const bool rows_kernel = sr_supported(a);
-    const bool lanes_kernel = !rows_kernel && sl_supported(a);
+    if (parts && i == 0) {
+      a.nparts = nparts;
+      a.part_stride = part_stride;
+    }
+    const bool rows_kernel = !a.nparts && sr_supported(a);
+    const bool lanes_kernel = !a.nparts && !rows_kernel && sl_supported(a);
+    if (parts && i == 0 && (rows_kernel || lanes_kernel)) return BRQ_ERR_UNSUPPORTED;
     if (!rows_kernel && !lanes_kernel && sp_blocks(a) >= ((int64_t)1 << 31)) return BRQ_ERR_UNSUPPORTED;  // grid
     char name[64];
     if (pair)

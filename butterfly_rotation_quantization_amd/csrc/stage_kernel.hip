@@ -52,9 +52,29 @@ __global__ __launch_bounds__(kSpThreads) void stage_kernel(SpArgs a) {
       sp_member(a, u, mg, mk);
       if (mg < ng) {
         mpos = sp_pos(a, g0 + mg, mk);
+        if (a.nparts > 1) {  // the sum of the parts, in their fixed order
 #pragma unroll
-        for (int l = 0; l < LINES; ++l)
-          if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, mpos, a.ld_src));
+          for (int l = 0; l < LINES; ++l) {
+            if (l < nl) {
+              const float* src = static_cast<const float*>(a.src) + sp_off(a, l0 + l, mpos, a.ld_src);
+              // eight parts at a time, all eight loads in flight (past the
+              // last part a slot adds 0)
+              float s4[4] = {0.f, 0.f, 0.f, 0.f};
+              for (int p0 = 0; p0 < a.nparts; p0 += 8) {
+                float v8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v8[j] = p0 + j < a.nparts ? src[(int64_t)(p0 + j) * a.part_stride] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s4[j & 3] += v8[j];
+              }
+              v[l] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int l = 0; l < LINES; ++l)
+            if (l < nl) v[l] = sp_load(a.src, a.src_t, sp_off(a, l0 + l, mpos, a.ld_src));
+        }
         if (a.sign_out) sg_out = a.sign_out[(uint32_t)mpos % (uint32_t)a.d];
       }
     }

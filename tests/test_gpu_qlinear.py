@@ -129,12 +129,13 @@ def test_qlinear_bf16_in(out_dt):
                    f"bf16 in {out_dt} out")
 
 
-@pytest.mark.parametrize("T_", [64, 130, 256])
+@pytest.mark.parametrize("T_", [64, 130, 256, 1030])
 @pytest.mark.parametrize("bits,group,dt", [(2, 64, "f16"), (3, 128, "f16"), (4, 64, "bf16"), (5, 64, "f16")])
 def test_qlinear_gemm_kernel(T_, bits, group, dt):
     """64 tokens and more with a multiple of 256 weight rows: the GEMM-shaped
     kernel (128 tokens x 256 rows per workgroup, 256-input chunks, one split
-    per XCD and token tile), including a ragged last token tile."""
+    per XCD and token tile, a single split from nine token tiles), including
+    a ragged last token tile."""
     rng = np.random.default_rng(T_ * 7 + bits * 3 + group)
     m, n = 512, 2048
     codes, alpha, x = _case(rng, T_, m, n, bits, group)

@@ -488,6 +488,7 @@ def test_right_lanes_kernel(dl, radix, mode, rows, chunks, lanes):
     (64, 256, 1024, 2, 64, "both"), (130, 512, 2048, 3, 128, "right"), (256, 256, 768, 5, 64, "none"),
     (300, 512, 1280, 4, 64, "left"),
     (128, 384, 1024, 2, 64, "none"),  # m not a multiple of 256: the direct kernel
+    (1100, 256, 512, 2, 64, "none"),  # nine token tiles: a single split
 ])
 def test_qlinear_walk(dl, T, m, n, bits, group, sides):
     left = DPlan(dl, S.random_plan(np.random.default_rng(m), (m // 16, 16), "per_group")) \
