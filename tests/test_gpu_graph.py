@@ -57,25 +57,27 @@ def test_graph_decode_rotation():
                    lambda: brq.rotate(V, x2, yo, side="right", ws=ws), yg, ref)
 
 
-def test_graph_decode_linear():
-    """The quantized linear layer at one token: input rotation, product,
-    reduction, output rotation."""
+@pytest.mark.parametrize("T_", [1, 130])
+def test_graph_decode_linear(T_):
+    """The quantized linear layer at one token (input rotation, streaming
+    product, reduction, output rotation) and at 130 tokens (the GEMM-shaped
+    product, the reduction folded into the first output stage)."""
     import butterfly_rotation_quantization_amd as brq
     import torch
-    announce("graph: decode linear T=1 m=256 n=1792")
-    rng = np.random.default_rng(12)
+    announce(f"graph: decode linear T={T_} m=256 n=1792")
+    rng = np.random.default_rng(12 + T_)
     m, n, bits, group = 256, 1792, 2, 64
     codes = rng.integers(0, 256, size=(m, n * bits // 8), dtype=np.int64).astype(np.uint8)
     alpha = (0.5 + rng.random((m, n // group))).astype(np.float32) * 0.05
     U = lib_plan(S.random_plan(rng, (16, 16), "per_group"))
     V = lib_plan(S.random_plan(rng, (7, 16, 16), "per_group"))
-    x = to_dev(S.to_storage(rng.standard_normal((1, n)), "f16"), "f16")
-    x2 = to_dev(S.to_storage(rng.standard_normal((1, n)), "f16"), "f16")
+    x = to_dev(S.to_storage(rng.standard_normal((T_, n)), "f16"), "f16")
+    x2 = to_dev(S.to_storage(rng.standard_normal((T_, n)), "f16"), "f16")
     cd, sd = to_dev(codes, "u8"), to_dev(alpha, "f32")
-    nb = brq.qlinear_workspace_bytes(U, V, bits, group, 1, m, n)
+    nb = brq.qlinear_workspace_bytes(U, V, bits, group, T_, m, n)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     ws2 = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    ref = torch.empty((1, m), dtype=torch.float16, device="cuda")
+    ref = torch.empty((T_, m), dtype=torch.float16, device="cuda")
     brq.qlinear(U, V, x, cd, sd, m, n, bits, group, y=ref, ws=ws)
     torch.cuda.synchronize()
     yg, yo = torch.empty_like(ref), torch.empty_like(ref)
