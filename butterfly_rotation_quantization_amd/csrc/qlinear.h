@@ -140,9 +140,11 @@ __host__ __device__ inline size_t ql_gemm_lds_bytes(int bits, int group, int tv)
 }
 // 16-token tiles per workgroup for T tokens.
 __host__ __device__ inline int ql_tm(int64_t T) { return T > kQlTok ? 4 : 1; }
-// The kernel for a shape (codes_aligned: 16-byte aligned codes), staying
-// within the 64 KiB of LDS a launch takes without an attribute (the
-// streaming kernel's staging is at most 62.75 KiB for b <= 5).
+// The kernel for a shape (codes_aligned: 16-byte aligned codes): the GEMM-
+// shaped kernel from 64 tokens when the rows come in blocks of 256 and the
+// inputs in chunks of 256 (its launch opts in to up to 115 KiB of LDS); else
+// the streaming kernel when its staging fits the 64 KiB a launch takes
+// without an attribute (at most 62.75 KiB for b <= 5); else the direct one.
 __host__ __device__ inline int ql_kind(int64_t T, int64_t m, int64_t n, int bits, int group, bool codes_aligned) {
   if (codes_aligned && T >= kQlGemmMinT && n % kQlGemmChunk == 0 && m % (kQlOut * kQlGemmTn) == 0)
     return kQlGemm;

@@ -283,10 +283,11 @@ brq_status brq_requant(const brq_plan* right, const uint8_t* codes, const void* 
  *           when right is NULL).
  *   codes, scales: device, as brq_rotate_quantize_pack wrote them for an
  *           [m][n] weight (4-byte aligned); q: that call's quantizer (ABSMAX,
- *           groups of 64 or 128).  With 16-byte aligned codes and n a
- *           multiple of 512 the product streams the weight through LDS;
- *           otherwise a slower kernel reads it directly (same results to
- *           the float32 rounding of the group sums).
+ *           groups of 64 or 128).  With 16-byte aligned codes the product
+ *           stages the weight through LDS: from 64 tokens with n a multiple
+ *           of 256 and m of 256 (a GEMM-shaped kernel), else with n a
+ *           multiple of 512; otherwise a slower kernel reads it directly
+ *           (same results to the float32 rounding of the group sums).
  *   y:      device [T][ldy] of type yt.
  *   ws:     device workspace of brq_qlinear_workspace_bytes(...) bytes.  On
  *           return, when right is not NULL, its first T*n*2 bytes hold X~ as
