@@ -968,6 +968,8 @@ hipError_t launch_stage_pair2(const P2Args& a, hipStream_t) {
       const int64_t ro = p2_row_o(a, hi, lo, og, oj), ri = p2_row_i(a, hi, lo, ea, eb);
       if (ro < 0 || ro + a.bo > blk_o || ri < 0 || ri + a.bi > blk_i)
         return violation("stage pair block rows %lld, %lld", ro, ri), hipErrorInvalidValue;
+      if (a.vec_i && (a.bi % 4 || ri % 4 || reinterpret_cast<uintptr_t>(a.blk_i) % 16))
+        return violation("stage pair vector block row at %lld (bi %lld)", ri, a.bi), hipErrorInvalidValue;
       // the outer group og mixes positions (k, og), the inner group ea positions (ea, k): same chunk, hi, lo
       for (int k = 0; k < a.bo; ++k)
         if (p2_pos(a, c, hi, lo, k, og) / (n * a.Si) != pos / (n * a.Si)) return violation("stage pair set %lld", s, 0), hipErrorInvalidValue;

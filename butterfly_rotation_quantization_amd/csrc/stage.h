@@ -275,6 +275,7 @@ struct P2Args {
   int per_group;           // blocks per group (else one shared block per stage)
   const float* blk_o;      // outer stage blocks [group][j][k] (groups hi Si bi... as in the plan)
   const float* blk_i;
+  int vec_i;               // blk_i 16-byte aligned and bi a multiple of 4: its rows load as float4
   const float* sign_in;    // applied at load (forward, first stage of the plan), or null
   const float* sign_out;   // applied at store (inverse, first stage of the plan), or null
   const void* src;

@@ -190,6 +190,7 @@ brq_status sp_rotate_stages(const Plan* p, int side, int inverse, int t_begin, i
         const float* base = inverse ? p->blkT : p->blk;
         q.blk_o = base + p->blk_off[L.t[to]];
         q.blk_i = base + p->blk_off[L.t[ti]];
+        q.vec_i = q.bi % 4 == 0 && reinterpret_cast<uintptr_t>(q.blk_i) % 16 == 0 ? 1 : 0;
         const bool last = i + 1 == L.n - 1;
         q.sign_in = (!inverse && i == 0 && signs_here) ? p->signs : nullptr;
         q.sign_out = (inverse && last && signs_here) ? p->signs : nullptr;

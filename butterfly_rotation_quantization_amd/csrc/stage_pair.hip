@@ -54,9 +54,21 @@ __global__ __launch_bounds__(256) void stage_pair2_kernel(P2Args a) {
 #pragma unroll
     for (int k = 0; k < BO; ++k)
       if (k < a.bo) wo[k] = ro[k];
+    if (a.vec_i) {
 #pragma unroll
-    for (int k = 0; k < BI; ++k)
-      if (k < a.bi) wi[k] = ri[k];
+      for (int k4 = 0; k4 < BI / 4; ++k4)
+        if (4 * k4 < a.bi) {
+          const float4 q = *reinterpret_cast<const float4*>(ri + 4 * k4);
+          wi[4 * k4] = q.x;
+          wi[4 * k4 + 1] = q.y;
+          wi[4 * k4 + 2] = q.z;
+          wi[4 * k4 + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+      for (int k = 0; k < BI; ++k)
+        if (k < a.bi) wi[k] = ri[k];
+    }
     const float sg = a.sign_in ? a.sign_in[(uint32_t)(pos % a.d)] : 1.f;
     if (a.sign_out) sg_out = a.sign_out[(uint32_t)(pos % a.d)];  // loaded with the inputs
 #pragma unroll
